@@ -1,0 +1,180 @@
+"""CPU oracle for the MoT token-routed projection (ctypes over mot_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product library never does.
+
+Every function takes and returns numpy arrays.  bf16 tensors travel as raw
+uint16 bit patterns.  The C source cites, per function, the passage of the
+pages it follows.  Pins against things other than itself live in
+tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mot_oracle.c")
+_LIB = os.path.join(_HERE, "libmot_oracle.so")
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (fp64, no fast math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call([
+            "gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+            "-std=c11", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        L.mot_oracle_bf16_round.argtypes = [ctypes.c_double]
+        L.mot_oracle_bf16_round.restype = ctypes.c_uint16
+        L.mot_oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        L.mot_oracle_bf16_value.restype = ctypes.c_double
+        L.mot_oracle_max_threads.restype = ctypes.c_int
+        L.mot_oracle_routing_plan.argtypes = [P, I64, P, P, P]
+        L.mot_oracle_routing_plan.restype = ctypes.c_int
+        L.mot_oracle_routed_gemm.argtypes = [P, I64, P, P, P, I64, I64, I64, P, P, ctypes.c_int]
+        L.mot_oracle_routed_gemm.restype = None
+        L.mot_oracle_routed_gemm_swiglu.argtypes = [P, I64, P, P, P, I64, I64, I64, P, P, ctypes.c_int]
+        L.mot_oracle_routed_gemm_swiglu.restype = None
+        L.mot_oracle_fused_add_rmsnorm.argtypes = [P, P, P, P, P, ctypes.c_float, I64, I64,
+                                                   P, P, P, P, ctypes.c_int]
+        L.mot_oracle_fused_add_rmsnorm.restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a, shape=None):
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    if shape is not None:
+        assert a.shape == shape, (a.shape, shape)
+    return a
+
+
+def max_threads() -> int:
+    return int(lib().mot_oracle_max_threads())
+
+
+def bf16_round(v: float) -> int:
+    return int(lib().mot_oracle_bf16_round(float(v)))
+
+
+def bf16_value(b: int) -> float:
+    return float(lib().mot_oracle_bf16_value(int(b)))
+
+
+def bf16_to_f64(a: np.ndarray) -> np.ndarray:
+    """Exact decode of bf16 bit patterns (uint16) to float64."""
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def routing_plan(modality: np.ndarray):
+    """Returns (perm int32 [T], n_und, n_gen), or None for a bad modality byte."""
+    m = np.ascontiguousarray(modality, dtype=np.uint8)
+    perm = np.zeros(m.size, np.int32)
+    nu = np.zeros(1, np.int32)
+    ng = np.zeros(1, np.int32)
+    rc = lib().mot_oracle_routing_plan(_p(m), m.size, _p(perm), _p(nu), _p(ng))
+    if rc != 0:
+        return None
+    return perm, int(nu[0]), int(ng[0])
+
+
+def routed_gemm(x, w_und, w_gen, modality, want_ref=True, want_out=True, threads=0):
+    """x [T,K] uint16, w_* [N,K] uint16, modality [T] uint8 -> (ref f64 [T,N], out u16 [T,N])."""
+    x = _u16(x)
+    T, K = x.shape
+    N = w_und.shape[0]
+    wu = _u16(w_und, (N, K))
+    wg = _u16(w_gen, (N, K))
+    m = np.ascontiguousarray(modality, dtype=np.uint8)
+    assert m.shape == (T,)
+    ref = np.empty((T, N), np.float64) if want_ref else None
+    out = np.empty((T, N), np.uint16) if want_out else None
+    lib().mot_oracle_routed_gemm(_p(x), K, _p(wu), _p(wg), _p(m), T, K, N, _p(ref), _p(out), threads)
+    return ref, out
+
+
+def routed_gemm_swiglu(x, w_und, w_gen, modality, want_ref=True, want_out=True, threads=0):
+    """w_* [2F,K] (gate rows then up rows) -> (ref f64 [T,F], out u16 [T,F])."""
+    x = _u16(x)
+    T, K = x.shape
+    F2 = w_und.shape[0]
+    assert F2 % 2 == 0
+    F = F2 // 2
+    wu = _u16(w_und, (F2, K))
+    wg = _u16(w_gen, (F2, K))
+    m = np.ascontiguousarray(modality, dtype=np.uint8)
+    assert m.shape == (T,)
+    ref = np.empty((T, F), np.float64) if want_ref else None
+    out = np.empty((T, F), np.uint16) if want_out else None
+    lib().mot_oracle_routed_gemm_swiglu(_p(x), K, _p(wu), _p(wg), _p(m), T, K, F, _p(ref), _p(out), threads)
+    return ref, out
+
+
+def fused_add_rmsnorm(x, r, w_und, w_gen, modality, eps=1e-6, threads=0):
+    """x, r [T,H] uint16 (r may be None) -> dict(h u16, rstd f64, ref f64, out u16)."""
+    x = _u16(x)
+    T, H = x.shape
+    rr = None if r is None else _u16(r, (T, H))
+    wu = _u16(w_und, (H,))
+    wg = _u16(w_gen, (H,))
+    m = np.ascontiguousarray(modality, dtype=np.uint8)
+    assert m.shape == (T,)
+    h = np.empty((T, H), np.uint16)
+    rstd = np.empty(T, np.float64)
+    ref = np.empty((T, H), np.float64)
+    out = np.empty((T, H), np.uint16)
+    lib().mot_oracle_fused_add_rmsnorm(_p(x), _p(rr), _p(wu), _p(wg), _p(m), float(eps), T, H,
+                                       _p(h), _p(rstd), _p(ref), _p(out), threads)
+    return {"h": h, "rstd": rstd, "ref": ref, "out": out}
+
+
+def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in bf16 steps between two arrays of finite bf16 bit patterns."""
+    def key(v):
+        v = np.asarray(v, np.uint16).astype(np.int32)
+        mag = v & 0x7FFF
+        return np.where(v & 0x8000, -mag, mag)
+    return np.abs(key(a) - key(b))
+
+
+def gate_metrics(got_bits: np.ndarray, ref: np.ndarray) -> dict:
+    """Tolerance metrics of a bf16 result against the unrounded fp64 oracle:
+    max-abs error, relative Frobenius error, elementwise excess over the
+    bf16 row of the tolerance contract (|d| <= 2e-2 + 1.6e-2*|ref|), and the
+    largest bf16-step distance to the correctly rounded oracle."""
+    got = bf16_to_f64(got_bits)
+    d = got - ref
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(d)) / nref if nref > 0 else float(np.linalg.norm(d))
+    excess = float(np.max(np.abs(d) - (2e-2 + 1.6e-2 * np.abs(ref)))) if d.size else 0.0
+    rne = np.vectorize(bf16_round, otypes=[np.uint16])(ref) if ref.size <= 4096 else None
+    return {
+        "max_abs": float(np.max(np.abs(d))) if d.size else 0.0,
+        "rel_fro": rel,
+        "elem_excess": excess,
+        "max_ref": float(np.max(np.abs(ref))) if ref.size else 0.0,
+        "max_ulp_to_rne": int(np.max(ulp_distance(got_bits, rne))) if rne is not None and rne.size else None,
+    }

@@ -1,0 +1,236 @@
+/*
+ * CPU oracle for the Mixture-of-Transformers (MoT) token-routed projection.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP library, and the HIP library never
+ * calls it.
+ *
+ * What it computes (plain definitions, fp64 accumulation, ascending k):
+ *
+ *  - Routing.  The RL-Kernel RFC page "[RFC][BAGEL-7B-MoT][CUDA/ROCm] WS1/WS2
+ *    kernel roadmap and integration plan", section 1 (Motivation, item 1):
+ *    one decoder holds two weight sets; every GEMM and norm picks its weight
+ *    set per token by a fixed index set, with no learned router.  Here the
+ *    index set is a byte per row: 0 = understanding set, 1 = generation set.
+ *  - Routed GEMM (the "mot_routed_gemm" work item, same page, section 5):
+ *    out[t,n] = bf16_rne( sum_k x[t,k] * W_{m(t)}[n,k] ), W stored [N,K].
+ *  - Routed gate/up + SwiGLU (the "mot_swiglu_mlp" work item, section 5; the
+ *    RL-Kernel MoE route/combine PR page gives the SwiGLU contract as gate_up
+ *    GEMM, SwiGLU in fp32, one bf16 cast):  g and u are the routed GEMMs with
+ *    the gate rows [0,F) and the up rows [F,2F) of the set's [2F,K] weight;
+ *    act = g / (1 + exp(-g)) * u, then one bf16 rounding.
+ *  - Routed fused add-RMSNorm (the "mot_fused_add_rmsnorm" work item,
+ *    section 5; the MoE PR page's RMSNorm commits fix the convention: every
+ *    multiply in fp32, one trailing cast, fixed reduction per row):
+ *    h = bf16_rne(x + r) (the new residual), rstd = 1/sqrt(mean_k(h^2)+eps),
+ *    y = bf16_rne(h * rstd * w_{m(t)}).
+ *
+ * Every floating-point step is done in fp64 and rounded to bf16 exactly once,
+ * directly from fp64 (no fp32 step), so the oracle is the exact result up to
+ * fp64 rounding.  The GPU path computes in fp32 and is compared within a
+ * tolerance; bitwise claims are only made GPU-against-GPU.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- bf16 encode / decode, written from the format's definition ---------- */
+
+/* bf16 is the upper half of an IEEE binary32: 1 sign, 8 exponent, 7 fraction
+ * bits.  Decoding is exact. */
+static double bf16_value(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bf16, ties to even, directly (no binary32
+ * intermediate).  bf16 has 8 significant bits; the smallest subnormal is
+ * 2^-133 and the largest finite value is (2 - 2^-7) * 2^127. */
+static uint16_t bf16_round(double v)
+{
+    if (isnan(v))
+        return 0x7fc0;
+    double a = fabs(v);
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return sign | 0x7f80;
+    int e;
+    frexp(a, &e);                 /* a = f * 2^e, 0.5 <= f < 1 */
+    int q = e - 8;                /* spacing of 8-significant-bit numbers */
+    if (q < -133)
+        q = -133;                 /* subnormal spacing */
+    double scaled = ldexp(a, -q); /* exact: power-of-two scaling */
+    double n = nearbyint(scaled); /* default mode: round half to even */
+    double r = ldexp(n, q);
+    if (r >= ldexp(1.0, 128))     /* rounded past the largest finite value */
+        return sign | 0x7f80;
+    float rf = (float)r;          /* exact: r has <= 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &rf, sizeof u);
+    return sign | (uint16_t)(u >> 16);
+}
+
+uint16_t mot_oracle_bf16_round(double v) { return bf16_round(v); }
+double mot_oracle_bf16_value(uint16_t b) { return bf16_value(b); }
+
+static void set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+int mot_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---- routing plan -------------------------------------------------------- */
+
+/* Stable partition of the rows by modality: perm[0..n_und) lists the rows
+ * with modality 0 in ascending order, perm[n_und..T) the rows with modality 1
+ * in ascending order.  Returns 0, or -1 if a byte is neither 0 nor 1 (then
+ * nothing is written). */
+int mot_oracle_routing_plan(const uint8_t *modality, int64_t T, int32_t *perm,
+                            int32_t *n_und, int32_t *n_gen)
+{
+    int64_t nu = 0, ng = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        if (modality[t] == 0)
+            ++nu;
+        else if (modality[t] == 1)
+            ++ng;
+        else
+            return -1;
+    }
+    int64_t iu = 0, ig = nu;
+    for (int64_t t = 0; t < T; ++t) {
+        if (modality[t] == 0)
+            perm[iu++] = (int32_t)t;
+        else
+            perm[ig++] = (int32_t)t;
+    }
+    *n_und = (int32_t)nu;
+    *n_gen = (int32_t)ng;
+    return 0;
+}
+
+/* ---- routed GEMM ----------------------------------------------------------- */
+
+/* x: [T, ldx] bf16 (first K columns used); w_und, w_gen: [N, K] bf16.
+ * ref (may be NULL): [T, N] fp64 exact-ish sums; out (may be NULL): [T, N]
+ * bf16 = bf16_round(ref). */
+void mot_oracle_routed_gemm(const uint16_t *x, int64_t ldx,
+                            const uint16_t *w_und, const uint16_t *w_gen,
+                            const uint8_t *modality,
+                            int64_t T, int64_t K, int64_t N,
+                            double *ref, uint16_t *out, int nthreads)
+{
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *w = modality[t] ? w_gen : w_und;
+        const uint16_t *xr = x + t * ldx;
+        for (int64_t n = 0; n < N; ++n) {
+            const uint16_t *wr = w + n * K;
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s += bf16_value(xr[k]) * bf16_value(wr[k]);
+            if (ref)
+                ref[t * N + n] = s;
+            if (out)
+                out[t * N + n] = bf16_round(s);
+        }
+    }
+}
+
+/* ---- routed gate/up GEMM + SwiGLU ------------------------------------------ */
+
+/* w_und, w_gen: [2F, K] bf16, rows [0,F) gate and [F,2F) up.
+ * ref (may be NULL): [T, F] fp64 silu(g)*u; out (may be NULL): [T, F] bf16. */
+void mot_oracle_routed_gemm_swiglu(const uint16_t *x, int64_t ldx,
+                                   const uint16_t *w_und, const uint16_t *w_gen,
+                                   const uint8_t *modality,
+                                   int64_t T, int64_t K, int64_t F,
+                                   double *ref, uint16_t *out, int nthreads)
+{
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *w = modality[t] ? w_gen : w_und;
+        const uint16_t *xr = x + t * ldx;
+        for (int64_t j = 0; j < F; ++j) {
+            const uint16_t *wg = w + j * K;
+            const uint16_t *wu = w + (F + j) * K;
+            double g = 0.0, u = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double xv = bf16_value(xr[k]);
+                g += xv * bf16_value(wg[k]);
+                u += xv * bf16_value(wu[k]);
+            }
+            double a = g / (1.0 + exp(-g)) * u;
+            if (ref)
+                ref[t * F + j] = a;
+            if (out)
+                out[t * F + j] = bf16_round(a);
+        }
+    }
+}
+
+/* ---- routed fused add-RMSNorm ------------------------------------------------ */
+
+/* x: [T, H] bf16; r: [T, H] bf16 residual or NULL (then h = x).
+ * h_out (may be NULL): [T, H] bf16 new residual; rstd (may be NULL): [T] fp64;
+ * ref (may be NULL): [T, H] fp64; out (may be NULL): [T, H] bf16. */
+void mot_oracle_fused_add_rmsnorm(const uint16_t *x, const uint16_t *r,
+                                  const uint16_t *w_und, const uint16_t *w_gen,
+                                  const uint8_t *modality, float eps,
+                                  int64_t T, int64_t H,
+                                  uint16_t *h_out, double *rstd,
+                                  double *ref, uint16_t *out, int nthreads)
+{
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *w = modality[t] ? w_gen : w_und;
+        double ss = 0.0;
+        for (int64_t k = 0; k < H; ++k) {
+            double hv = bf16_value(x[t * H + k]);
+            if (r)
+                hv = bf16_value(bf16_round(hv + bf16_value(r[t * H + k])));
+            ss += hv * hv;
+        }
+        double rs = 1.0 / sqrt(ss / (double)H + (double)eps);
+        if (rstd)
+            rstd[t] = rs;
+        for (int64_t k = 0; k < H; ++k) {
+            uint16_t hb = x[t * H + k];
+            if (r)
+                hb = bf16_round(bf16_value(hb) + bf16_value(r[t * H + k]));
+            if (h_out)
+                h_out[t * H + k] = hb;
+            double y = bf16_value(hb) * rs * bf16_value(w[k]);
+            if (ref)
+                ref[t * H + k] = y;
+            if (out)
+                out[t * H + k] = bf16_round(y);
+        }
+    }
+}

@@ -1,0 +1,379 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Every check here is independent of the oracle's own code: exact integer /
+rational arithmetic written in this file, library routines (torch fp64
+matmul, torch silu), closed forms, brute force on tiny shapes, and structural
+invariants of the routing definition (RL-Kernel RFC page "[RFC][BAGEL-7B-MoT]
+WS1/WS2 kernel roadmap", section 1: a row picks its weight set by a fixed
+index set, and a row's bytes must not depend on the modality mix of the pack).
+
+The mutation tests at the end plant typical mistakes (swapped weight sets, a
+dropped k term, a transposed operand, a wrong SiLU sign, a norm without the
+mean) on the CPU and show that the pins catch them.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---- an independent bf16 rounding, by exact rational arithmetic ---------------
+
+def rne_bf16_exact(v) -> int:
+    """Nearest bf16 (ties to even) of an exact rational or float, computed with
+    integers only: find the binade, scale to an integer significand grid and
+    round half to even by comparing remainders."""
+    q = Fraction(v)
+    if q == 0:
+        return 0x8000 if (isinstance(v, float) and math.copysign(1.0, v) < 0) else 0
+    sign = 0x8000 if q < 0 else 0
+    a = abs(q)
+    # exponent e with 2^e <= a < 2^(e+1)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    step_exp = max(e - 7, -133)           # spacing of the bf16 grid at a
+    scaled = a / (Fraction(2) ** step_exp)
+    n, rem = divmod(scaled.numerator, scaled.denominator)
+    twice = 2 * rem
+    if twice > scaled.denominator or (twice == scaled.denominator and n % 2 == 1):
+        n += 1
+    val = Fraction(n) * Fraction(2) ** step_exp
+    if val >= Fraction(2) ** 128:
+        return sign | 0x7F80
+    f = np.float32(float(val))             # exact: val has <= 8 significant bits
+    return sign | int(f.view(np.uint32) >> 16)
+
+
+def test_rounding_helper_against_torch_on_fp32_exact_values():
+    # For values exactly representable in fp32, torch's fp32->bf16 cast is RNE:
+    # a library special case that pins the helper above.
+    g = torch.Generator().manual_seed(5)
+    v = torch.randn(4000, generator=g) * torch.exp2(torch.randint(-140, 120, (4000,), generator=g).float())
+    v = torch.cat([v, torch.tensor([1.0 + 2**-8, 1.0 + 3 * 2**-8, -(1.0 + 2**-8), 2.0**-133, 2.0**-134,
+                                    3 * 2.0**-135, 3.3895313892515355e38, 3.3961775292304957e38, 0.0])])
+    want = v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for x, wv in zip(v.tolist(), want.tolist()):
+        assert rne_bf16_exact(float(np.float32(x))) == wv, x
+
+
+def test_oracle_bf16_round_matches_exact_rounding():
+    rng = np.random.default_rng(1)
+    vals = list(rng.standard_normal(3000) * np.exp2(rng.integers(-140, 127, 3000)))
+    # ties and near-ties at several binades, subnormals, overflow boundary
+    for e in (-133, -130, -126, -20, 0, 7, 100, 126):
+        for k in range(0, 40):
+            base = 2.0 ** e
+            vals += [base * (1 + k / 256), base * (1 + k / 256) + base * 2**-30,
+                     base * (1 + k / 256) - base * 2**-30]
+    vals += [2.0**-134, 2.0**-134 * 1.0000001, 2.0**-135, 3.3961775292304957e38, 3.3961775292304955e38,
+             1e300, -1e300, 0.0, -0.0]
+    for v in vals:
+        assert oracle.bf16_round(v) == rne_bf16_exact(v), v
+
+
+def test_bf16_decode_is_exact():
+    b = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = (b & 0x7F80) != 0x7F80
+    got = oracle.bf16_to_f64(b[finite])
+    want = torch.from_numpy(b[finite].view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(got, want)
+    # the C decoder agrees with the numpy decoder on a spread of patterns
+    for v in (0x0000, 0x0001, 0x3F80, 0xBF80, 0x7F7F, 0x8001, 0x4049):
+        assert oracle.bf16_value(v) == oracle.bf16_to_f64(np.array([v], np.uint16))[0]
+
+
+# ---- routed GEMM -------------------------------------------------------------
+
+def _dense(x, w):
+    return (torch.from_numpy(oracle.bf16_to_f64(x)) @ torch.from_numpy(oracle.bf16_to_f64(w)).T).numpy()
+
+
+def test_tiny_brute_force_every_element():
+    """Tiny case (T=64, K=256, N=384, 24 und + 40 gen rows): every fp64 sum is
+    within the sequential-summation bound of the exact sum (math.fsum of the
+    exact bf16 x bf16 products), and every bf16 output is the exactly rounded
+    exact sum."""
+    x, wu, wg, m = W.tiny()
+    X, WU, WG = W.bits(x), W.bits(wu), W.bits(wg)
+    ref, out = oracle.routed_gemm(X, WU, WG, m)
+    xd = oracle.bf16_to_f64(X)
+    wud, wgd = oracle.bf16_to_f64(WU), oracle.bf16_to_f64(WG)
+    K = X.shape[1]
+    for t in range(X.shape[0]):
+        w = wgd if m[t] else wud
+        P = xd[t][None, :] * w            # exact: 8x8-bit significands
+        for n in range(w.shape[0]):
+            p = P[n]
+            s = math.fsum(p)
+            bound = K * 2.0**-53 * float(np.abs(p).sum())
+            assert abs(ref[t, n] - s) <= bound
+            exact = sum((Fraction(v) for v in p), Fraction(0)) if _near_tie(s) else s
+            assert out[t, n] == rne_bf16_exact(exact), (t, n)
+
+
+def _near_tie(s: float) -> bool:
+    if s == 0.0:
+        return False
+    e = math.frexp(abs(s))[1] - 1
+    step = 2.0 ** max(e - 7, -133)
+    r = abs(s) / step
+    return abs(r - math.floor(r) - 0.5) < 1e-6
+
+
+@pytest.mark.parametrize("which", [W.UND, W.GEN])
+def test_single_set_pack_is_plain_gemm(which):
+    """All-und pack == torch fp64 matmul with W_und (and gen with W_gen)."""
+    T, K, N = 96, 320, 192
+    x, wu, wg, _ = W.gemm_case(T, K, N, np.zeros(T, np.uint8), base=3)
+    m = np.full(T, which, np.uint8)
+    ref, out = oracle.routed_gemm(W.bits(x), W.bits(wu), W.bits(wg), m)
+    want = _dense(W.bits(x), W.bits(wg if which else wu))
+    assert np.max(np.abs(ref - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+
+
+def test_mixed_pack_is_per_row_gemm():
+    """A mixed pack equals the per-set dense GEMMs of the gathered rows,
+    scattered back to their positions."""
+    T, K, N = 200, 256, 128
+    m = np.random.default_rng(7).integers(0, 2, T).astype(np.uint8)
+    x, wu, wg, _ = W.gemm_case(T, K, N, m, base=4)
+    X = W.bits(x)
+    ref, _ = oracle.routed_gemm(X, W.bits(wu), W.bits(wg), m)
+    want = np.empty_like(ref)
+    for s, w in ((0, wu), (1, wg)):
+        rows = np.nonzero(m == s)[0]
+        want[rows] = _dense(X[rows], W.bits(w))
+    assert np.max(np.abs(ref - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+def test_permutation_equivariance_and_relabel():
+    T, K, N = 150, 192, 64
+    m = W.pattern(T)
+    x, wu, wg, _ = W.gemm_case(T, K, N, m, base=5)
+    X, WU, WG = W.bits(x), W.bits(wu), W.bits(wg)
+    _, out = oracle.routed_gemm(X, WU, WG, m)
+    p = np.random.default_rng(2).permutation(T)
+    _, outp = oracle.routed_gemm(X[p], WU, WG, m[p])
+    assert np.array_equal(outp, out[p])
+    _, outr = oracle.routed_gemm(X, WG, WU, (1 - m).astype(np.uint8))
+    assert np.array_equal(outr, out)
+    # a row computed alone equals the row inside the pack
+    _, one = oracle.routed_gemm(X[7:8], WU, WG, m[7:8])
+    assert np.array_equal(one[0], out[7])
+
+
+def test_leading_dimension():
+    T, K, N = 40, 128, 64
+    m = W.pattern(T)
+    x, wu, wg, _ = W.gemm_case(T, 2 * K, N, m, base=6)
+    X = W.bits(x)
+    wu2, wg2 = W.bits(wu)[:, :K].copy(), W.bits(wg)[:, :K].copy()
+    ref_slice, _ = oracle.routed_gemm(X[:, :K].copy(), wu2, wg2, m)
+    # strided view through the C entry point: x rows of length 2K, first K used
+    L = oracle.lib()
+    ref = np.empty((T, N))
+    L.mot_oracle_routed_gemm(oracle._p(X), 2 * K, oracle._p(wu2), oracle._p(wg2), oracle._p(m),
+                             T, K, N, oracle._p(ref), None, 0)
+    assert np.array_equal(ref, ref_slice)
+
+
+# ---- SwiGLU ------------------------------------------------------------------
+
+def test_swiglu_matches_torch_silu_fp64():
+    T, K, F = 48, 256, 96
+    m = W.pattern(T)
+    x, _, _, _ = W.gemm_case(T, K, 8, m, base=7)
+    wu = W.normal_bf16((2 * F, K), 71, 0.05)
+    wg = W.normal_bf16((2 * F, K), 72, 0.05)
+    X, WU, WG = W.bits(x), W.bits(wu), W.bits(wg)
+    ref, out = oracle.routed_gemm_swiglu(X, WU, WG, m)
+    want = np.empty((T, F))
+    for s, w in ((0, WU), (1, WG)):
+        rows = np.nonzero(m == s)[0]
+        gu = torch.from_numpy(_dense(X[rows], w))
+        want[rows] = (torch.nn.functional.silu(gu[:, :F]) * gu[:, F:]).numpy()
+    assert np.max(np.abs(ref - want)) <= 1e-12 * np.max(np.abs(want))
+    assert all(out[i, j] == rne_bf16_exact(float(ref[i, j])) for i in range(0, T, 5) for j in range(F))
+
+
+def test_swiglu_closed_forms():
+    K, F = 64, 4
+    # g = 0 exactly (gate rows zero) -> act = 0 for any u
+    x = np.full((2, K), 0x3F80, np.uint16)                      # x = 1
+    w = np.zeros((2 * F, K), np.uint16)
+    w[F:] = 0x3F80                                              # u = K
+    ref, out = oracle.routed_gemm_swiglu(x, w, w, np.array([0, 1], np.uint8))
+    assert np.all(ref == 0.0) and np.all((out & 0x7FFF) == 0)
+    # g large: silu(g) = g up to exp(-g); g = 64 (all ones), u = 2 -> act = 128
+    w2 = np.full((2 * F, K), 0x3F80, np.uint16)
+    w2[F:] = 0x0000
+    w2[F:, 0] = 0x4000                                          # u = 2*x0 = 2
+    ref, out = oracle.routed_gemm_swiglu(x, w2, w2, np.array([1, 0], np.uint8))
+    assert np.allclose(ref, 128.0, rtol=1e-20, atol=128 * 64 * math.exp(-64))
+    assert np.all(out == 0x4300)                                # bf16(128)
+    # g very negative: silu -> -0-ish tiny, act finite and ~0
+    w3 = np.full((2 * F, K), 0xBF80, np.uint16)                 # g = -64
+    ref, _ = oracle.routed_gemm_swiglu(x, w3, w3, np.array([0, 0], np.uint8))
+    assert np.all(np.abs(ref) < 1e-20)
+
+
+# ---- fused add-RMSNorm -------------------------------------------------------
+
+def test_rmsnorm_textbook_special_case():
+    """w = 1 and no residual: the textbook x / sqrt(mean(x^2) + eps), by torch
+    fp64; the routing then cannot matter."""
+    T, H = 33, 3584
+    x = W.normal_bf16((T, H), 81)
+    ones = np.full(H, 0x3F80, np.uint16)
+    m = W.pattern(T)
+    r = oracle.fused_add_rmsnorm(W.bits(x), None, ones, ones, m, eps=1e-6)
+    xd = x.double()
+    want = (xd / torch.sqrt((xd * xd).mean(-1, keepdim=True) + float(np.float32(1e-6)))).numpy()
+    assert np.max(np.abs(r["ref"] - want)) <= 1e-14
+    assert np.array_equal(r["h"], W.bits(x))
+
+
+def test_rmsnorm_constant_row_closed_form():
+    H = 256
+    c = 0x4040                                                  # 3.0
+    x = np.full((2, H), c, np.uint16)
+    wu = np.full(H, 0x3F80, np.uint16)                          # 1.0
+    wg = np.full(H, 0x4000, np.uint16)                          # 2.0
+    eps = 0.5
+    r = oracle.fused_add_rmsnorm(x, None, wu, wg, np.array([0, 1], np.uint8), eps=eps)
+    y0 = 3.0 / math.sqrt(9.0 + eps)
+    assert np.allclose(r["ref"][0], y0, rtol=1e-15) and np.allclose(r["ref"][1], 2 * y0, rtol=1e-15)
+    assert np.allclose(r["rstd"], 1 / math.sqrt(9.5), rtol=1e-15)
+
+
+def test_fused_add_residual_is_exactly_rounded_sum():
+    T, H = 16, 512
+    x, res = W.residual_inputs(T, H, base=9)
+    wu, wg = W.norm_weights(H, base=9)
+    m = W.pattern(T)
+    r = oracle.fused_add_rmsnorm(W.bits(x), W.bits(res), W.bits(wu), W.bits(wg), m)
+    xd, rd = oracle.bf16_to_f64(W.bits(x)), oracle.bf16_to_f64(W.bits(res))
+    for t in range(T):
+        for k in range(0, H, 7):
+            assert r["h"][t, k] == rne_bf16_exact(Fraction(float(xd[t, k])) + Fraction(float(rd[t, k])))
+    # normalising the rounded sum equals the fused result (fused == add, store, norm)
+    r2 = oracle.fused_add_rmsnorm(r["h"], None, W.bits(wu), W.bits(wg), m)
+    assert np.array_equal(r2["out"], r["out"]) and np.array_equal(r2["ref"], r["ref"])
+
+
+def test_rmsnorm_routing_rows_independent():
+    T, H = 20, 384
+    x = W.normal_bf16((T, H), 91)
+    wu, wg = W.norm_weights(H, base=10)
+    m = W.pattern(T)
+    full = oracle.fused_add_rmsnorm(W.bits(x), None, W.bits(wu), W.bits(wg), m)["out"]
+    for t in (0, 5, 19):
+        one = oracle.fused_add_rmsnorm(W.bits(x)[t:t + 1], None, W.bits(wu), W.bits(wg), m[t:t + 1])["out"]
+        assert np.array_equal(one[0], full[t])
+    # the weight applied is the row's own set
+    xd = oracle.bf16_to_f64(W.bits(x))
+    for t in range(T):
+        wv = oracle.bf16_to_f64(W.bits(wg if m[t] else wu))
+        rs = 1 / math.sqrt(float(np.mean(xd[t] ** 2)) + float(np.float32(1e-6)))
+        assert np.allclose(oracle.bf16_to_f64(full[t]), xd[t] * rs * wv, rtol=2**-8, atol=0)
+
+
+# ---- routing plan ------------------------------------------------------------
+
+def test_routing_plan_is_stable_partition():
+    for T, seed in ((0, 0), (1, 1), (77, 2), (4096, 3)):
+        m = np.random.default_rng(seed).integers(0, 2, T).astype(np.uint8)
+        perm, nu, ng = oracle.routing_plan(m)
+        want = np.argsort(m, kind="stable")
+        assert np.array_equal(perm, want) and nu == int((m == 0).sum()) and ng == T - nu
+    bad = np.array([0, 1, 2, 0], np.uint8)
+    assert oracle.routing_plan(bad) is None
+
+
+# ---- the hand-worked examples in tests/golden ---------------------------------
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_golden_hand_worked_gemm():
+    g = _load("routed_gemm_worked_example.json")
+    x = np.array(g["x_bits"], np.uint16)
+    ref, out = oracle.routed_gemm(x, np.array(g["w_und_bits"], np.uint16),
+                                  np.array(g["w_gen_bits"], np.uint16), np.array(g["modality"], np.uint8))
+    assert ref.tolist() == g["expected_sum"]
+    assert out.tolist() == g["expected_bits"]
+
+
+def test_golden_hand_worked_norm():
+    g = _load("rmsnorm_worked_example.json")
+    r = oracle.fused_add_rmsnorm(np.array(g["x_bits"], np.uint16), np.array(g["r_bits"], np.uint16),
+                                 np.array(g["w_und_bits"], np.uint16), np.array(g["w_gen_bits"], np.uint16),
+                                 np.array(g["modality"], np.uint8), eps=g["eps"])
+    assert r["h"].tolist() == g["expected_h_bits"]
+    assert r["out"].tolist() == g["expected_bits"]
+
+
+# ---- planted mistakes: the pins must catch them ---------------------------------
+
+def _pin_dense(out_ref, X, WU, WG, m):
+    want = np.empty_like(out_ref)
+    for s, w in ((0, WU), (1, WG)):
+        rows = np.nonzero(m == s)[0]
+        if rows.size:
+            want[rows] = _dense(X[rows], w)
+    return np.max(np.abs(out_ref - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+
+
+def test_pins_catch_planted_gemm_mistakes():
+    T, K, N = 64, 128, 128
+    m = W.tiny_modality()
+    x, wu, wg, _ = W.gemm_case(T, K, N, m, base=11)
+    X, WU, WG = W.bits(x), W.bits(wu), W.bits(wg)
+    good, _ = oracle.routed_gemm(X, WU, WG, m)
+    assert _pin_dense(good, X, WU, WG, m)
+    swapped, _ = oracle.routed_gemm(X, WG, WU, m)               # sets swapped
+    assert not _pin_dense(swapped, X, WU, WG, m)
+    dropped, _ = oracle.routed_gemm(X[:, :K - 1].copy(), WU[:, :K - 1].copy(), WG[:, :K - 1].copy(), m)
+    assert not _pin_dense(dropped, X, WU, WG, m)                 # last k term dropped
+    transposed, _ = oracle.routed_gemm(X, WU.reshape(K, N).T.copy(), WG.reshape(K, N).T.copy(), m)
+    assert not _pin_dense(transposed, X, WU, WG, m)              # operand read transposed
+    one_set, _ = oracle.routed_gemm(X, WU, WU, m)               # routing ignored
+    assert not _pin_dense(one_set, X, WU, WG, m)
+
+
+def test_pins_catch_planted_swiglu_and_norm_mistakes():
+    T, K, F = 16, 64, 32
+    m = W.pattern(T)
+    x = W.normal_bf16((T, K), 12)
+    w = W.normal_bf16((2 * F, K), 13, 0.1)
+    X, Wb = W.bits(x), W.bits(w)
+    ref, _ = oracle.routed_gemm_swiglu(X, Wb, Wb, m)
+    gu = torch.from_numpy(_dense(X, Wb))
+    g, u = gu[:, :F], gu[:, F:]
+    good = (torch.nn.functional.silu(g) * u).numpy()
+    assert np.allclose(ref, good, rtol=1e-12, atol=1e-14)
+    for wrong in ((g * torch.sigmoid(-g) * u), (torch.nn.functional.silu(u) * g), (g * u)):
+        assert not np.allclose(ref, wrong.numpy(), rtol=1e-6, atol=1e-9)
+    H = 128
+    xn = W.normal_bf16((4, H), 14)
+    ones = np.full(H, 0x3F80, np.uint16)
+    r = oracle.fused_add_rmsnorm(W.bits(xn), None, ones, ones, W.pattern(4))
+    xd = xn.double()
+    sum_not_mean = (xd / torch.sqrt((xd * xd).sum(-1, keepdim=True) + 1e-6)).numpy()
+    no_eps_sqrt = (xd / (xd * xd).mean(-1, keepdim=True)).numpy()
+    assert not np.allclose(r["ref"], sum_not_mean, rtol=1e-6)
+    assert not np.allclose(r["ref"], no_eps_sqrt, rtol=1e-6)
