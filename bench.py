@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoT token-routed projection on one MI355X.
+
+Headline: routed-GEMM TFLOP/s (and % of the bf16 MFMA peak) of the BAGEL
+fused QKV projection, T=4096 packed rows (77 und + 1024 gen rows cycled:
+308 und / 3788 gen), K=3584 -> N=4608 (3584 q + 512 k + 512 v).  One step is
+one mot_routed_gemm call on inputs already resident in HBM: the routing plan
+(segment list) and the routed GEMM with its bf16 epilogue.  FLOPs count real
+rows only: 2*T*K*N.
+
+Beside it, on the same line:
+  roofline      dominant kernel (the routed GEMM) against the bf16 MFMA peak,
+                its average duration from HIP events on the launch stream;
+  cpu_baseline  the CPU oracle timed on a bounded row sample on this host;
+  components    the other hot-path steps: routed fused add-RMSNorm (GB/s),
+                the routed-RMSNorm prologue variant, the MLP gate/up+SwiGLU and
+                down projections, a small-pack HBM-bound case.
+
+Inputs are synthetic and seeded (CPU generators, then copied to the GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-GEMM TFLOP/s and % bf16 MFMA peak at T=4096, 3584->4608 QKV"
+# MI355X: 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU (published 2.5 PFLOP/s).
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-components", action="store_true")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="run one 1 GiB device copy first (HBM counter calibration under rocprofv3)")
+    p.add_argument("--cpu-rows", type=int, default=96, help="oracle row sample for cpu_baseline")
+    return p.parse_args()
+
+
+def git_rev():
+    try:
+        rev = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                             text=True).stdout.strip()
+        dirty = subprocess.run(["git", "status", "--porcelain"], cwd=ROOT, capture_output=True,
+                               text=True).stdout.strip() != ""
+        return rev or "unknown", dirty if rev else None
+    except Exception:
+        return "unknown", None
+
+
+def time_calls(fn, iters, stream):
+    """Average duration of `fn` launches, HIP events on the launch stream."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters * 1e-3  # seconds
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
+              "routed projection is row-local and would shard by rows, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_transformers_token_amd as mot
+    import workloads as W
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    if args.copy_probe:
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # ---- headline workload: BAGEL fused QKV, T=4096 --------------------------
+    T, K, N = 4096, W.HIDDEN, W.QKV_DIM
+    x, wu, wg, m = W.qkv(T)
+    xd, wud, wgd = x.to(dev), wu.to(dev), wg.to(dev)
+    md = torch.from_numpy(m).to(dev)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    ws = mot.new_workspace(T, dev)
+    flops = 2.0 * T * K * N
+
+    def step():
+        mot.routed_gemm(xd, wud, wgd, md, out=y, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    value = flops * args.steps / elapsed / 1e12
+    if mot.read_device_error(ws) != 0:
+        raise RuntimeError("device error word set during the benchmark")
+
+    # dominant kernel alone: the routed GEMM launch with the plan already built
+    def gemm_only():
+        mot.routed_gemm(xd, wud, wgd, md, out=y, workspace=ws, plan_ready=True)
+    gemm_s = time_calls(gemm_only, max(args.steps, 50), stream)
+    plan_s = time_calls(lambda: mot.routing_plan(md, ws), 50, stream)
+    achieved = flops / gemm_s / 1e12
+    n_und, n_gen = int((m == 0).sum()), int((m == 1).sum())
+    roofline = {
+        "kernel": "gemm_kernel<256,256> (routed QKV GEMM)",
+        "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        "avg_kernel_us": round(gemm_s * 1e6, 2), "plan_kernel_us": round(plan_s * 1e6, 2),
+        "flop_per_launch": flops,
+        "alg_bytes_per_launch": 2 * (2 * N * K + T * K + T * N) + T,
+    }
+
+    # ---- other hot-path steps ------------------------------------------------
+    components = {}
+    if not args.no_components:
+        iters = 30
+        # routed fused add-RMSNorm, T=4096, H=3584 (x, residual in; residual, y out)
+        xs, rs = W.residual_inputs(T, K)
+        nwu, nwg = (t.to(dev) for t in W.norm_weights(K))
+        xsd, rsd = xs.to(dev), rs.to(dev)
+        yn = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+        rstd = torch.empty(T, dtype=torch.float32, device=dev)
+        s_norm = time_calls(lambda: mot.fused_add_rmsnorm(xsd, rsd, nwu, nwg, md, out=yn, rstd=rstd),
+                            iters, stream)
+        nbytes = 4 * T * K * 2 + T * 4 + T
+        components["fused_add_rmsnorm_T4096_H3584"] = {
+            "us": round(s_norm * 1e6, 2), "GB/s": round(nbytes / s_norm / 1e9, 1),
+            "frac_hbm": round(nbytes / s_norm / 1e9 / PEAK_HBM_GBS, 3)}
+        # QKV with the routed-RMSNorm prologue (reads h + rstd instead of y)
+        s_pro = time_calls(lambda: mot.routed_gemm(rsd, wud, wgd, md, out=y, workspace=ws,
+                                                   norm=(rstd, nwu, nwg)), iters, stream)
+        components["qkv_prologue_T4096"] = {"us": round(s_pro * 1e6, 2),
+                                            "TFLOP/s": round(flops / s_pro / 1e12, 1)}
+        # small, weight-bound packs (HBM roofline): weights rotated over 8 copies
+        for Ts in (1, 64, 256):
+            ms = W.pattern(Ts)
+            xs_s = W.normal_bf16((Ts, K), 9).to(dev)
+            mds = torch.from_numpy(ms).to(dev)
+            copies = [(W.normal_bf16((N, K), 90 + i, 0.02).to(dev), W.normal_bf16((N, K), 190 + i, 0.02).to(dev))
+                      for i in range(4)]
+            ys = torch.empty((Ts, N), dtype=torch.bfloat16, device=dev)
+            wss = mot.new_workspace(Ts, dev)
+            ctr = [0]
+
+            def small():
+                a, b = copies[ctr[0] % 4]
+                ctr[0] += 1
+                mot.routed_gemm(xs_s, a, b, mds, out=ys, workspace=wss)
+            s_small = time_calls(small, 40, stream)
+            sets = int((ms == 0).any()) + int((ms == 1).any())
+            nb = sets * N * K * 2 + Ts * K * 2 + Ts * N * 2 + Ts
+            components[f"qkv_small_T{Ts}"] = {"us": round(s_small * 1e6, 2),
+                                              "GB/s": round(nb / s_small / 1e9, 1),
+                                              "frac_hbm": round(nb / s_small / 1e9 / PEAK_HBM_GBS, 3),
+                                              "sets": sets}
+            del copies
+        # MLP: gate/up+SwiGLU 3584 -> 2x18944, down 18944 -> 3584
+        gu_u, gu_g, dn_u, dn_g = (t.to(dev) for t in W.mlp_weights())
+        act = torch.empty((T, W.FFN), dtype=torch.bfloat16, device=dev)
+        yd = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+        s_gu = time_calls(lambda: mot.routed_gemm_swiglu(xd, gu_u, gu_g, md, out=act, workspace=ws),
+                          10, stream)
+        s_dn = time_calls(lambda: mot.routed_gemm(act, dn_u, dn_g, md, out=yd, workspace=ws), 10, stream)
+        f_gu = 2.0 * T * K * 2 * W.FFN
+        f_dn = 2.0 * T * W.FFN * K
+        components["gate_up_swiglu_T4096"] = {"us": round(s_gu * 1e6, 1),
+                                              "TFLOP/s": round(f_gu / s_gu / 1e12, 1)}
+        components["down_T4096"] = {"us": round(s_dn * 1e6, 1), "TFLOP/s": round(f_dn / s_dn / 1e12, 1)}
+        del gu_u, gu_g, dn_u, dn_g
+
+    # ---- CPU oracle baseline on a bounded row sample -------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = W.sample_rows(m, args.cpu_rows, seed=7)
+        xb, wub, wgb = W.bits(x)[rows], W.bits(wu), W.bits(wg)
+        threads = oracle.max_threads()
+        t0 = time.perf_counter()
+        oracle.routed_gemm(xb, wub, wgb, m[rows], want_ref=True, want_out=True)
+        cs = time.perf_counter() - t0
+        cpu = {"value": round(2.0 * rows.size * K * N / cs / 1e12, 6), "unit": "TFLOP/s",
+               "cores": threads, "kind": "oracle",
+               "sample": f"{rows.size} of {T} QKV rows (stratified by modality, every segment "
+                         f"boundary), full K={K}, N={N}, fp64; {cs:.1f} s"}
+
+    rev, dirty = git_rev()
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "BAGEL fused QKV routed GEMM: T=4096 packed rows (77 und + 1024 gen "
+                               "cycled; 308 und, 3788 gen), K=3584, N=4608, two bf16 weight sets, "
+                               "fp32 accumulate, bf16 out",
+                   "T": T, "K": K, "N": N, "n_und": n_und, "n_gen": n_gen,
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "components": components,
+        "provenance": {"commit": rev, "dirty": dirty, "torch": torch.__version__,
+                       "hip": torch.version.hip, "device": torch.cuda.get_device_name(dev)},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

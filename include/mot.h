@@ -1,0 +1,170 @@
+/*
+ * mot.h -- C ABI of libmot, the MI355X (gfx950) Mixture-of-Transformers
+ * token-routed projection.
+ *
+ * The method: BAGEL-7B-MoT's Qwen2.5-7B-shaped decoder holds two full weight
+ * sets, "understanding" (und) and "generation" (gen), that share attention;
+ * every GEMM and every norm picks the weight set of each packed token row by a
+ * fixed per-row index set, not by a learned router, and a row's output bytes
+ * must not depend on the modality mix of the pack (RL-Kernel RFC page
+ * "[RFC][BAGEL-7B-MoT][CUDA/ROCm] WS1/WS2 kernel roadmap and integration plan",
+ * section 1, item 1).  The numerical contract of the same page (section 3)
+ * applies to every call: fixed fp32 accumulator and fixed reduction order, no
+ * Split-K / Stream-K / atomics, no fast math, casts only at declared
+ * boundaries, fail closed on unsupported geometry.  The three operations are
+ * the page's "mot_routed_gemm", "mot_swiglu_mlp" (its gate/up + SwiGLU half)
+ * and "mot_fused_add_rmsnorm" work items (section 5).
+ *
+ * Conventions shared by every call
+ *  - bf16 tensors are passed as uint16_t bit patterns; all tensors are
+ *    row-major.  Weights use the nn.Linear layout W[n][k]: y = x * W^T.
+ *  - modality[t] is one byte per row: 0 = und, 1 = gen.  Any other value is a
+ *    data error detected on the device (see mot_read_device_error).
+ *  - Every pointer except `stream` is a DEVICE pointer owned by the caller.
+ *    The library allocates nothing and keeps no state between calls.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued on
+ *    it and runs on the stream's device; no call synchronises except
+ *    mot_read_device_error.
+ *  - Every host-checkable error is returned before anything is enqueued, and
+ *    the outputs are then untouched.  T == 0 is a no-op returning MOT_OK.
+ *  - Calls that share a workspace must be ordered (same stream, or events).
+ *
+ * Result bytes are batch-invariant: each output row depends only on its own
+ * input row, its modality byte and the weights, bit for bit, whatever the
+ * pack's size, order or mix.
+ */
+#ifndef MOT_H
+#define MOT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOT_ABI_VERSION 1
+
+typedef enum mot_status {
+    MOT_OK = 0,
+    MOT_ERR_INVALID_ARG = 1,       /* null pointer, negative size, bad leading dimension, aliasing, eps */
+    MOT_ERR_UNSUPPORTED_SHAPE = 2, /* K, N or F not a positive multiple of 64, or above the limits below */
+    MOT_ERR_MISALIGNED = 3,        /* a tensor pointer not 16-byte aligned, or a leading dimension not a multiple of 8 */
+    MOT_ERR_WORKSPACE = 4,         /* workspace missing or smaller than mot_workspace_bytes(T) */
+    MOT_ERR_DEVICE = 5,            /* a HIP runtime call or a kernel launch failed */
+    MOT_ERR_MODALITY = 6           /* a modality byte was neither 0 nor 1 (reported by mot_read_device_error) */
+} mot_status;
+
+/* Limits checked on the host. */
+#define MOT_MAX_T (1 << 24)
+#define MOT_MAX_DIM (1 << 20)
+
+/* Workspace layout (device memory, 256-byte aligned, caller-owned):
+ *   bytes [0, 16)      int32 header[4] = { error, n_und, n_gen, T }
+ *                      error is MOT_OK or MOT_ERR_MODALITY; on error n_und = n_gen = 0.
+ *   bytes [256, 256+4T) int32 perm[T]: the rows with modality 0 in ascending
+ *                      order, then the rows with modality 1 in ascending order.
+ * This stable partition is the pack's segment list: routed kernels cut it into
+ * per-set row tiles, so no tile mixes weight sets. */
+#define MOT_WS_HEADER_BYTES 256
+
+/* ABI version of the loaded library (compare with MOT_ABI_VERSION; a Python
+ * binding refuses to run on a mismatch). */
+int mot_abi_version(void);
+
+/* Static, human-readable name of a mot_status value. */
+const char *mot_status_string(int status);
+
+/* Bytes of workspace the routed calls need for a pack of T rows (T >= 0). */
+size_t mot_workspace_bytes(int64_t T);
+
+/* Routing plan (the segment list): from modality[T] build the header and perm
+ * described above in `workspace`.  The routed GEMM calls run this step
+ * themselves unless MOT_FLAG_PLAN_READY is given.
+ * Errors: MOT_ERR_INVALID_ARG (T < 0, null pointers with T > 0),
+ * MOT_ERR_UNSUPPORTED_SHAPE (T > MOT_MAX_T), MOT_ERR_WORKSPACE, MOT_ERR_DEVICE. */
+int mot_routing_plan(const uint8_t *modality, int64_t T,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Flags of the routed GEMM calls. */
+#define MOT_FLAG_PLAN_READY 1u /* workspace already holds the plan of this `modality`,
+                                  built earlier in stream order; skip rebuilding it */
+
+/* Routed GEMM (QKV, O and down projections):
+ *   y[t][n] = bf16_rne( sum_k A[t][k] * W_{modality[t]}[n][k] ),  0 <= n < N,
+ * fp32 accumulation over k in one fixed ascending order, one writer per
+ * element.  A = x, or with the routed-RMSNorm prologue (rstd, nw_und and
+ * nw_gen all non-NULL) A[t][k] = bf16_rne((x[t][k] * rstd[t]) * nw_{modality[t]}[k])
+ * computed in fp32 -- bit-identical to feeding the output of
+ * mot_fused_add_rmsnorm to the plain GEMM.
+ *   x      [T][ldx] bf16, first K columns read; ldx >= K, ldx % 8 == 0.
+ *   w_und, w_gen [N][K] bf16 each; both required.
+ *   modality [T] uint8.
+ *   y      [T][ldy] bf16, columns [0, N) written; ldy >= N, ldy % 8 == 0;
+ *          must not overlap x.
+ *   rstd [T] fp32, nw_und / nw_gen [K] bf16: all three NULL (no prologue)
+ *          or all three non-NULL.
+ *   K % 64 == 0, N % 64 == 0, 0 < K, N <= MOT_MAX_DIM, 0 <= T <= MOT_MAX_T.
+ *   workspace: >= mot_workspace_bytes(T) bytes, 256-byte aligned.
+ * Rows whose modality byte is invalid make the whole call write nothing; the
+ * error is reported by mot_read_device_error. */
+int mot_routed_gemm(const uint16_t *x, int64_t ldx,
+                    const uint16_t *w_und, const uint16_t *w_gen,
+                    const uint8_t *modality,
+                    uint16_t *y, int64_t ldy,
+                    int64_t T, int64_t K, int64_t N,
+                    const float *rstd, const uint16_t *nw_und, const uint16_t *nw_gen,
+                    void *workspace, size_t workspace_bytes,
+                    unsigned flags, void *stream);
+
+/* Routed gate/up GEMM with the SwiGLU epilogue (the gate/up half of the MLP):
+ *   g = sum_k A[t][k] * W_m[j][k],  u = sum_k A[t][k] * W_m[F + j][k]  (fp32),
+ *   act[t][j] = bf16_rne( (g / (1 + expf(-g))) * u ),  0 <= j < F,
+ * with accurate expf (no fast intrinsic) and one bf16 cast (RL-Kernel MoE
+ * route/combine PR page: gate_up GEMM, SwiGLU in fp32, then bf16).
+ *   wgu_und, wgu_gen [2F][K] bf16: rows [0, F) gate, rows [F, 2F) up.
+ *   act [T][ldact] bf16, ldact >= F, ldact % 8 == 0.  F % 64 == 0.
+ * Other arguments, the prologue and the errors as mot_routed_gemm. */
+int mot_routed_gemm_swiglu(const uint16_t *x, int64_t ldx,
+                           const uint16_t *wgu_und, const uint16_t *wgu_gen,
+                           const uint8_t *modality,
+                           uint16_t *act, int64_t ldact,
+                           int64_t T, int64_t K, int64_t F,
+                           const float *rstd, const uint16_t *nw_und, const uint16_t *nw_gen,
+                           void *workspace, size_t workspace_bytes,
+                           unsigned flags, void *stream);
+
+/* Routed fused add-RMSNorm, per row t with m = modality[t]:
+ *   h = bf16_rne(x[t] + residual[t])   (fp32 add; h = x[t] when residual is NULL)
+ *   residual[t] = h                    (in place, when residual is non-NULL)
+ *   rstd = 1 / sqrtf(sum_k(h_k^2) / H + eps)   fp32, correctly rounded divide
+ *          and sqrt, one fixed reduction tree per row that does not depend on T
+ *   out[t][k] = bf16_rne((h_k * rstd) * w_m[k])   fp32, one cast
+ *   rstd_out[t] = rstd
+ * (RMSNorm convention of the RL-Kernel MoE route/combine PR page: fp32
+ * weight multiply, single trailing cast, row reduction fixed for a fixed H.)
+ *   x, residual, out: [T][H] bf16, contiguous; out may be NULL (prologue mode:
+ *   the routed GEMMs then read h and rstd); rstd_out [T] fp32 or NULL; at least
+ *   one of out / rstd_out non-NULL.  w_und, w_gen [H] bf16.
+ *   H % 64 == 0, 0 < H <= 16384; eps > 0 and finite.
+ *   workspace: NULL, or a routed workspace whose header error word is SET to
+ *   MOT_ERR_MODALITY if a byte is invalid (rows with an invalid byte are not
+ *   written).  This call never clears the error word.
+ * Errors: MOT_ERR_INVALID_ARG, MOT_ERR_UNSUPPORTED_SHAPE, MOT_ERR_MISALIGNED,
+ * MOT_ERR_DEVICE. */
+int mot_fused_add_rmsnorm(const uint16_t *x, uint16_t *residual,
+                          const uint16_t *w_und, const uint16_t *w_gen,
+                          const uint8_t *modality, float eps,
+                          uint16_t *out, float *rstd_out,
+                          int64_t T, int64_t H,
+                          void *workspace, void *stream);
+
+/* Synchronises `stream` and returns the workspace's device error word:
+ * MOT_OK, MOT_ERR_MODALITY, or MOT_ERR_DEVICE if the copy fails. */
+int mot_read_device_error(const void *workspace, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOT_H */

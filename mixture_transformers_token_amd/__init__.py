@@ -1,0 +1,248 @@
+"""MI355X-native Mixture-of-Transformers token-routed projection.
+
+Thin ctypes binding of libmot (include/mot.h): argument checking and
+marshalling only.  Every step of the path runs in the HIP library; PyTorch
+provides device memory and the current stream.  There is no fallback: if
+libmot.so is missing or stale, every call raises.
+
+Functions mirror the C ABI:
+  routing_plan, routed_gemm, routed_gemm_swiglu, fused_add_rmsnorm,
+  read_device_error, workspace_bytes, abi_version.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MotError", "ABI_VERSION", "lib", "abi_version", "workspace_bytes", "new_workspace",
+    "routing_plan", "plan_view", "routed_gemm", "routed_gemm_swiglu", "fused_add_rmsnorm",
+    "read_device_error", "status_string", "LIB_PATH",
+]
+
+ABI_VERSION = 1
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
+WS_HEADER_BYTES = 256
+FLAG_PLAN_READY = 1
+
+# exported symbols, as declared in include/mot.h
+EXPORTS = (
+    "mot_abi_version", "mot_status_string", "mot_workspace_bytes", "mot_routing_plan",
+    "mot_routed_gemm", "mot_routed_gemm_swiglu", "mot_fused_add_rmsnorm", "mot_read_device_error",
+)
+
+STATUS = {
+    0: "MOT_OK", 1: "MOT_ERR_INVALID_ARG", 2: "MOT_ERR_UNSUPPORTED_SHAPE", 3: "MOT_ERR_MISALIGNED",
+    4: "MOT_ERR_WORKSPACE", 5: "MOT_ERR_DEVICE", 6: "MOT_ERR_MODALITY",
+}
+
+
+class MotError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = int(status)
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def lib():
+    """Load libmot.so (once) and check its ABI version; raise if unavailable."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libmot.so not built at {LIB_PATH}: run __graft_entry__.build() "
+                           "or python mixture_transformers_token_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, SZ, U = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint
+    L.mot_abi_version.restype = ctypes.c_int
+    L.mot_abi_version.argtypes = []
+    L.mot_status_string.restype = ctypes.c_char_p
+    L.mot_status_string.argtypes = [ctypes.c_int]
+    L.mot_workspace_bytes.restype = SZ
+    L.mot_workspace_bytes.argtypes = [I64]
+    L.mot_routing_plan.restype = ctypes.c_int
+    L.mot_routing_plan.argtypes = [P, I64, P, SZ, P]
+    L.mot_routed_gemm.restype = ctypes.c_int
+    L.mot_routed_gemm.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64, P, P, P, P, SZ, U, P]
+    L.mot_routed_gemm_swiglu.restype = ctypes.c_int
+    L.mot_routed_gemm_swiglu.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64, P, P, P, P, SZ, U, P]
+    L.mot_fused_add_rmsnorm.restype = ctypes.c_int
+    L.mot_fused_add_rmsnorm.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, I64, I64, P, P]
+    L.mot_read_device_error.restype = ctypes.c_int
+    L.mot_read_device_error.argtypes = [P, P]
+    v = L.mot_abi_version()
+    if v != ABI_VERSION:
+        raise RuntimeError(f"stale libmot.so: ABI {v}, binding expects {ABI_VERSION}; rebuild it")
+    _lib = L
+    return L
+
+
+def abi_version() -> int:
+    return int(lib().mot_abi_version())
+
+
+def status_string(status: int) -> str:
+    try:
+        return lib().mot_status_string(int(status)).decode()
+    except Exception:
+        return STATUS.get(int(status), "unknown")
+
+
+def workspace_bytes(T: int) -> int:
+    return int(lib().mot_workspace_bytes(int(T)))
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MotError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _req(t, name, dtype, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _rows(t, name):
+    """Leading dimension of a row-major 2-D tensor (unit column stride)."""
+    if t.shape[0] > 0 and t.shape[1] > 0 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+
+
+def new_workspace(T: int, device) -> torch.Tensor:
+    return torch.empty(workspace_bytes(T), dtype=torch.uint8, device=device)
+
+
+def routing_plan(modality: torch.Tensor, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Build the segment list of a pack in a workspace (returned)."""
+    _req(modality, "modality", torch.uint8, 1)
+    T = modality.shape[0]
+    if workspace is None:
+        workspace = new_workspace(T, modality.device)
+    _check(lib().mot_routing_plan(_ptr(modality.contiguous()), T, _ptr(workspace),
+                                  workspace.numel(), _stream(modality.device)), "mot_routing_plan")
+    return workspace
+
+
+def plan_view(workspace: torch.Tensor, T: int):
+    """(header int32[4], perm int32[T]) views of a workspace (documented layout)."""
+    hdr = workspace[:16].view(torch.int32)
+    perm = workspace[WS_HEADER_BYTES:WS_HEADER_BYTES + 4 * T].view(torch.int32)
+    return hdr, perm
+
+
+def _routed(fn, name, x, w_und, w_gen, modality, out, norm, workspace, plan_ready, swiglu):
+    _req(x, "x", torch.bfloat16, 2)
+    _req(w_und, "w_und", torch.bfloat16, 2)
+    _req(w_gen, "w_gen", torch.bfloat16, 2)
+    _req(modality, "modality", torch.uint8, 1)
+    if w_und.shape != w_gen.shape:
+        raise ValueError("w_und and w_gen must have the same shape (both weight sets are required)")
+    if not (w_und.is_contiguous() and w_gen.is_contiguous()):
+        raise ValueError("weights must be contiguous [rows, K]")
+    T, K = x.shape
+    rows = w_und.shape[0]
+    if w_und.shape[1] != K:
+        raise ValueError(f"weights have K={w_und.shape[1]}, x has K={K}")
+    if modality.shape[0] != T:
+        raise ValueError("modality must have one byte per row")
+    if swiglu and rows % 2:
+        raise ValueError("gate/up weights need an even number of rows")
+    N = rows // 2 if swiglu else rows
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _req(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (T, N):
+        raise ValueError(f"out must be [{T}, {N}]")
+    if workspace is None:
+        if plan_ready:
+            raise ValueError("plan_ready needs the workspace that holds the plan")
+        workspace = new_workspace(T, x.device)
+    rstd = nw_u = nw_g = None
+    if norm is not None:
+        rstd, nw_u, nw_g = norm
+        _req(rstd, "rstd", torch.float32, 1)
+        _req(nw_u, "norm w_und", torch.bfloat16, 1)
+        _req(nw_g, "norm w_gen", torch.bfloat16, 1)
+        if rstd.shape[0] != T or nw_u.shape[0] != K or nw_g.shape[0] != K:
+            raise ValueError("prologue shapes: rstd [T], norm weights [K]")
+    mod = modality.contiguous()
+    st = fn(_ptr(x), _rows(x, "x"), _ptr(w_und), _ptr(w_gen), _ptr(mod), _ptr(out), _rows(out, "out"),
+            T, K, N, _ptr(rstd), _ptr(nw_u), _ptr(nw_g), _ptr(workspace), workspace.numel(),
+            FLAG_PLAN_READY if plan_ready else 0, _stream(x.device))
+    _check(st, name)
+    return out
+
+
+def routed_gemm(x, w_und, w_gen, modality, out=None, norm=None, workspace=None, plan_ready=False):
+    """y[t] = x[t] @ W_{modality[t]}^T in bf16 (fp32 accumulate).  W_* are [N, K].
+    norm=(rstd [T] fp32, nw_und [K], nw_gen [K]) applies the routed-RMSNorm prologue."""
+    return _routed(lib().mot_routed_gemm, "mot_routed_gemm", x, w_und, w_gen, modality, out, norm,
+                   workspace, plan_ready, swiglu=False)
+
+
+def routed_gemm_swiglu(x, wgu_und, wgu_gen, modality, out=None, norm=None, workspace=None,
+                       plan_ready=False):
+    """act[t] = silu(g) * u with [g | u] = x[t] @ Wgu_{modality[t]}^T; Wgu_* are [2F, K]."""
+    return _routed(lib().mot_routed_gemm_swiglu, "mot_routed_gemm_swiglu", x, wgu_und, wgu_gen,
+                   modality, out, norm, workspace, plan_ready, swiglu=True)
+
+
+def fused_add_rmsnorm(x, residual, w_und, w_gen, modality, eps=1e-6, out=True, rstd=True,
+                      workspace=None):
+    """Routed fused add-RMSNorm.  residual (or None) is updated in place with h.
+    out / rstd: True to allocate, a tensor to fill, or None to skip.
+    Returns (out, rstd)."""
+    _req(x, "x", torch.bfloat16, 2)
+    _req(modality, "modality", torch.uint8, 1)
+    _req(w_und, "w_und", torch.bfloat16, 1)
+    _req(w_gen, "w_gen", torch.bfloat16, 1)
+    T, H = x.shape
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if residual is not None:
+        _req(residual, "residual", torch.bfloat16, 2)
+        if tuple(residual.shape) != (T, H) or not residual.is_contiguous():
+            raise ValueError("residual must be contiguous [T, H]")
+    if out is True:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if rstd is True:
+        rstd = torch.empty(T, dtype=torch.float32, device=x.device)
+    if out is not None:
+        _req(out, "out", torch.bfloat16, 2)
+        if tuple(out.shape) != (T, H) or not out.is_contiguous():
+            raise ValueError("out must be contiguous [T, H]")
+    if rstd is not None:
+        _req(rstd, "rstd", torch.float32, 1)
+        if rstd.shape[0] != T:
+            raise ValueError("rstd must be [T]")
+    if modality.shape[0] != T or w_und.shape[0] != H or w_gen.shape[0] != H:
+        raise ValueError("shapes: modality [T], weights [H]")
+    st = lib().mot_fused_add_rmsnorm(_ptr(x), _ptr(residual), _ptr(w_und), _ptr(w_gen),
+                                     _ptr(modality.contiguous()), float(eps), _ptr(out), _ptr(rstd),
+                                     T, H, _ptr(workspace), _stream(x.device))
+    _check(st, "mot_fused_add_rmsnorm")
+    return out, rstd
+
+
+def read_device_error(workspace: torch.Tensor) -> int:
+    """Synchronises the current stream; returns the workspace's error status."""
+    return int(lib().mot_read_device_error(_ptr(workspace), _stream(workspace.device)))

@@ -1,0 +1,242 @@
+// C-ABI layer of libmot: argument validation (fail closed, before anything is
+// enqueued), device selection from the caller's stream, and kernel dispatch.
+// The layer allocates nothing and keeps no state between calls.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/mot.h"
+#include "mot_internal.h"
+
+namespace {
+
+constexpr int64_t kWsAlign = 256;
+
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
+}
+
+// Makes the stream's device current for the duration of a call (launches go to
+// the device that owns the caller's stream, not to whatever device is current).
+class DeviceGuard {
+  public:
+    explicit DeviceGuard(hipStream_t s) {
+        if (hipGetDevice(&prev_) != hipSuccess) {
+            ok_ = false;
+            return;
+        }
+        int dev = prev_;
+        if (s != nullptr && hipStreamGetDevice(s, &dev) != hipSuccess) {
+            ok_ = false;
+            return;
+        }
+        if (dev != prev_) {
+            if (hipSetDevice(dev) != hipSuccess) {
+                ok_ = false;
+                return;
+            }
+            switched_ = true;
+        }
+    }
+    ~DeviceGuard() {
+        if (switched_) (void)hipSetDevice(prev_);
+    }
+    bool ok() const { return ok_; }
+
+  private:
+    int prev_ = 0;
+    bool ok_ = true;
+    bool switched_ = false;
+};
+
+size_t ws_bytes(int64_t T) {
+    return (size_t)(MOT_WS_HEADER_BYTES + round_up(4 * (T > 0 ? T : 0), kWsAlign));
+}
+
+struct RoutedCall {
+    const uint16_t *x;
+    int64_t ldx;
+    const uint16_t *w_und, *w_gen;
+    const uint8_t *modality;
+    uint16_t *y;
+    int64_t ldy;
+    int64_t T, K, N;       // N: output columns (F for SwiGLU)
+    int64_t w_rows;        // rows of each weight matrix (N, or 2F)
+    const float *rstd;
+    const uint16_t *nw_und, *nw_gen;
+    void *workspace;
+    size_t workspace_bytes;
+    unsigned flags;
+};
+
+int validate_routed(const RoutedCall &c) {
+    if (c.T < 0 || c.K < 0 || c.N < 0) return MOT_ERR_INVALID_ARG;
+    if (c.T == 0) return MOT_OK;
+    if (!c.x || !c.w_und || !c.w_gen || !c.modality || !c.y) return MOT_ERR_INVALID_ARG;
+    if (c.T > MOT_MAX_T) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (c.K == 0 || c.N == 0 || c.K % 64 || c.N % 64 || c.K > MOT_MAX_DIM || c.N > MOT_MAX_DIM)
+        return MOT_ERR_UNSUPPORTED_SHAPE;
+    if ((c.flags & ~MOT_FLAG_PLAN_READY) != 0) return MOT_ERR_INVALID_ARG;
+    if (c.ldx < c.K || c.ldy < c.N || c.ldx > (int64_t(1) << 32) || c.ldy > (int64_t(1) << 32))
+        return MOT_ERR_INVALID_ARG;
+    if (c.ldx % 8 || c.ldy % 8) return MOT_ERR_MISALIGNED;
+    const int npro = (c.rstd != nullptr) + (c.nw_und != nullptr) + (c.nw_gen != nullptr);
+    if (npro != 0 && npro != 3) return MOT_ERR_INVALID_ARG;
+    if (!aligned16(c.x) || !aligned16(c.w_und) || !aligned16(c.w_gen) || !aligned16(c.y))
+        return MOT_ERR_MISALIGNED;
+    if (npro == 3 && (!aligned16(c.nw_und) || !aligned16(c.nw_gen) ||
+                      (reinterpret_cast<uintptr_t>(c.rstd) & 3u)))
+        return MOT_ERR_MISALIGNED;
+    if (!c.workspace || c.workspace_bytes < ws_bytes(c.T)) return MOT_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(c.workspace) & (kWsAlign - 1)) != 0) return MOT_ERR_MISALIGNED;
+    const int64_t x_bytes = ((c.T - 1) * c.ldx + c.K) * 2;
+    const int64_t y_bytes = ((c.T - 1) * c.ldy + c.N) * 2;
+    if (overlaps(c.x, x_bytes, c.y, y_bytes)) return MOT_ERR_INVALID_ARG;
+    const int64_t w_bytes = c.w_rows * c.K * 2;
+    if (overlaps(c.w_und, w_bytes, c.y, y_bytes) || overlaps(c.w_gen, w_bytes, c.y, y_bytes))
+        return MOT_ERR_INVALID_ARG;
+    if (overlaps(c.workspace, (int64_t)ws_bytes(c.T), c.y, y_bytes)) return MOT_ERR_INVALID_ARG;
+    // the kernels address each operand with 32-bit byte offsets
+    if (x_bytes >= (int64_t(1) << 32) || w_bytes >= (int64_t(1) << 32) ||
+        y_bytes >= (int64_t(1) << 32))
+        return MOT_ERR_UNSUPPORTED_SHAPE;
+    return MOT_OK;
+}
+
+int run_routed(const RoutedCall &c, bool swiglu, void *stream) {
+    const int v = validate_routed(c);
+    if (v != MOT_OK || c.T == 0) return v;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(s);
+    if (!guard.ok()) return MOT_ERR_DEVICE;
+    int32_t *hdr = static_cast<int32_t *>(c.workspace);
+    int32_t *perm = reinterpret_cast<int32_t *>(static_cast<char *>(c.workspace) + MOT_WS_HEADER_BYTES);
+    if (!(c.flags & MOT_FLAG_PLAN_READY)) {
+        if (mot::launch_plan(c.modality, c.T, hdr, perm, s) != hipSuccess) return MOT_ERR_DEVICE;
+    }
+    mot::GemmArgs a;
+    a.x = c.x;
+    a.ldx = c.ldx;
+    a.w_und = c.w_und;
+    a.w_gen = c.w_gen;
+    a.y = c.y;
+    a.ldy = c.ldy;
+    a.hdr = hdr;
+    a.perm = perm;
+    a.rstd = c.rstd;
+    a.nw_und = c.nw_und;
+    a.nw_gen = c.nw_gen;
+    a.T = c.T;
+    a.K = (int)c.K;
+    a.N = (int)c.N;
+    a.x_bytes = (uint32_t)(((c.T - 1) * c.ldx + c.K) * 2);
+    a.w_bytes = (uint32_t)(c.w_rows * c.K * 2);
+    if (mot::launch_gemm(a, swiglu, s) != hipSuccess) return MOT_ERR_DEVICE;
+    return MOT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mot_abi_version(void) { return MOT_ABI_VERSION; }
+
+const char *mot_status_string(int status) {
+    switch (status) {
+    case MOT_OK: return "MOT_OK";
+    case MOT_ERR_INVALID_ARG: return "MOT_ERR_INVALID_ARG: invalid argument";
+    case MOT_ERR_UNSUPPORTED_SHAPE: return "MOT_ERR_UNSUPPORTED_SHAPE: unsupported shape";
+    case MOT_ERR_MISALIGNED: return "MOT_ERR_MISALIGNED: pointer or leading dimension misaligned";
+    case MOT_ERR_WORKSPACE: return "MOT_ERR_WORKSPACE: workspace missing or too small";
+    case MOT_ERR_DEVICE: return "MOT_ERR_DEVICE: HIP runtime or launch failure";
+    case MOT_ERR_MODALITY: return "MOT_ERR_MODALITY: modality byte not 0 or 1";
+    default: return "unknown mot_status";
+    }
+}
+
+size_t mot_workspace_bytes(int64_t T) { return ws_bytes(T); }
+
+int mot_routing_plan(const uint8_t *modality, int64_t T, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    if (T < 0) return MOT_ERR_INVALID_ARG;
+    if (T == 0) return MOT_OK;
+    if (!modality) return MOT_ERR_INVALID_ARG;
+    if (T > MOT_MAX_T) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (!workspace || workspace_bytes < ws_bytes(T)) return MOT_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kWsAlign - 1)) != 0) return MOT_ERR_MISALIGNED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(s);
+    if (!guard.ok()) return MOT_ERR_DEVICE;
+    int32_t *hdr = static_cast<int32_t *>(workspace);
+    int32_t *perm = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + MOT_WS_HEADER_BYTES);
+    return mot::launch_plan(modality, T, hdr, perm, s) == hipSuccess ? MOT_OK : MOT_ERR_DEVICE;
+}
+
+int mot_routed_gemm(const uint16_t *x, int64_t ldx, const uint16_t *w_und, const uint16_t *w_gen,
+                    const uint8_t *modality, uint16_t *y, int64_t ldy, int64_t T, int64_t K,
+                    int64_t N, const float *rstd, const uint16_t *nw_und, const uint16_t *nw_gen,
+                    void *workspace, size_t workspace_bytes, unsigned flags, void *stream) {
+    RoutedCall c{x, ldx, w_und, w_gen, modality, y, ldy, T, K, N, N,
+                 rstd, nw_und, nw_gen, workspace, workspace_bytes, flags};
+    return run_routed(c, false, stream);
+}
+
+int mot_routed_gemm_swiglu(const uint16_t *x, int64_t ldx, const uint16_t *wgu_und,
+                           const uint16_t *wgu_gen, const uint8_t *modality, uint16_t *act,
+                           int64_t ldact, int64_t T, int64_t K, int64_t F, const float *rstd,
+                           const uint16_t *nw_und, const uint16_t *nw_gen, void *workspace,
+                           size_t workspace_bytes, unsigned flags, void *stream) {
+    RoutedCall c{x, ldx, wgu_und, wgu_gen, modality, act, ldact, T, K, F, 2 * F,
+                 rstd, nw_und, nw_gen, workspace, workspace_bytes, flags};
+    return run_routed(c, true, stream);
+}
+
+int mot_fused_add_rmsnorm(const uint16_t *x, uint16_t *residual, const uint16_t *w_und,
+                          const uint16_t *w_gen, const uint8_t *modality, float eps,
+                          uint16_t *out, float *rstd_out, int64_t T, int64_t H, void *workspace,
+                          void *stream) {
+    if (T < 0 || H < 0) return MOT_ERR_INVALID_ARG;
+    if (!(eps > 0.0f) || !isfinite(eps)) return MOT_ERR_INVALID_ARG;
+    if (T == 0) return MOT_OK;
+    if (!x || !w_und || !w_gen || !modality) return MOT_ERR_INVALID_ARG;
+    if (!out && !rstd_out) return MOT_ERR_INVALID_ARG;
+    if (T > MOT_MAX_T) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (H == 0 || H % 64 || H > 16384) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(x) || !aligned16(w_und) || !aligned16(w_gen) ||
+        (residual && !aligned16(residual)) || (out && !aligned16(out)) ||
+        (rstd_out && (reinterpret_cast<uintptr_t>(rstd_out) & 3u)) ||
+        (workspace && (reinterpret_cast<uintptr_t>(workspace) & (kWsAlign - 1))))
+        return MOT_ERR_MISALIGNED;
+    const int64_t bytes = T * H * 2;
+    if (out && (overlaps(out, bytes, x, bytes) || (residual && overlaps(out, bytes, residual, bytes))))
+        return MOT_ERR_INVALID_ARG;
+    if (residual && overlaps(residual, bytes, x, bytes)) return MOT_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(s);
+    if (!guard.ok()) return MOT_ERR_DEVICE;
+    int32_t *err = workspace ? static_cast<int32_t *>(workspace) : nullptr;
+    return mot::launch_norm(x, residual, w_und, w_gen, modality, eps, out, rstd_out, T, (int)H, err,
+                            s) == hipSuccess
+               ? MOT_OK
+               : MOT_ERR_DEVICE;
+}
+
+int mot_read_device_error(const void *workspace, void *stream) {
+    if (!workspace) return MOT_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(s);
+    if (!guard.ok()) return MOT_ERR_DEVICE;
+    int32_t host = 0;
+    if (hipMemcpyAsync(&host, workspace, sizeof host, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return MOT_ERR_DEVICE;
+    if (hipStreamSynchronize(s) != hipSuccess) return MOT_ERR_DEVICE;
+    return host == 0 ? MOT_OK : host;
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Internal interface between the C-ABI layer (mot_api.cpp) and the HIP
+// kernels (mot_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mot {
+
+// Arguments of one routed GEMM launch.  Sizes are validated by the caller.
+struct GemmArgs {
+    const uint16_t *x;
+    int64_t ldx;
+    const uint16_t *w_und;
+    const uint16_t *w_gen;
+    uint16_t *y;
+    int64_t ldy;
+    const int32_t *hdr;   // workspace header: error, n_und, n_gen, T
+    const int32_t *perm;  // workspace segment list
+    const float *rstd;    // prologue (nullptr: none)
+    const uint16_t *nw_und;
+    const uint16_t *nw_gen;
+    int64_t T;
+    int K;
+    int N;                // output columns (F for SwiGLU)
+    uint32_t x_bytes;     // extent of x from its base (bytes, < 4 GiB)
+    uint32_t w_bytes;     // extent of one weight matrix (bytes, < 4 GiB)
+};
+
+hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t *perm,
+                       hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs &a, bool swiglu, hipStream_t stream);
+hipError_t launch_norm(const uint16_t *x, uint16_t *residual, const uint16_t *w_und,
+                       const uint16_t *w_gen, const uint8_t *modality, float eps,
+                       uint16_t *out, float *rstd_out, int64_t T, int H, int32_t *err_word,
+                       hipStream_t stream);
+
+}  // namespace mot

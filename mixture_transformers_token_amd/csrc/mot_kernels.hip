@@ -1,0 +1,626 @@
+// HIP kernels of the MoT token-routed projection for gfx950 (MI355X).
+//
+//  * plan_kernel   -- the routing plan: stable partition of the pack's rows by
+//                     modality byte (the per-set segment list).
+//  * gemm_kernel   -- routed GEMM  y = A * W_set^T on bf16 MFMA with fp32
+//                     accumulation; optional routed-RMSNorm prologue on the A
+//                     operand; optional SwiGLU epilogue (gate/up pairs).
+//  * norm_kernel   -- routed fused add-RMSNorm.
+//
+// Numerical contract (RL-Kernel RFC page "[RFC][BAGEL-7B-MoT] WS1/WS2 kernel
+// roadmap", section 3): one fixed fp32 accumulation order per output element,
+// no split-K, no atomics, no fast math, casts only where declared.  A row's
+// bytes depend only on its own data: the GEMM's per-element k order is fixed
+// (one MFMA instruction, k ascending in 16-wide steps) whatever the tile shape,
+// the tile's position in the grid or the pack's composition.
+//
+// Built with -ffp-contract=off: every fp32 multiply and add in the epilogues
+// and the norm rounds where the source says so.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mot_internal.h"
+
+namespace mot {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kErrModality = 6;  // MOT_ERR_MODALITY
+
+// ---- bf16 helpers (format definition: upper 16 bits of an IEEE binary32) ----
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round to nearest, ties to even.  NaN stays NaN (quiet bit set).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// ============================================================================
+// Routing plan
+// ============================================================================
+
+// One workgroup of 1024 threads walks the pack in chunks of 16 rows per
+// thread.  Pass 1 counts the und rows and checks the bytes; pass 2 writes
+// each row's position: und rows at [0, n_und) and gen rows at [n_und, T), both
+// in ascending row order (an exclusive scan of per-thread counts).
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanPerThread = 16;
+
+__device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave, int &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += o;
+    }
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    int wave_base = 0, sum = 0;
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+        int t = s_wave[w];
+        if (w < wave) wave_base += t;
+        sum += t;
+    }
+    __syncthreads();
+    total = sum;
+    return wave_base + inc - v;
+}
+
+__global__ void __launch_bounds__(kPlanThreads)
+plan_kernel(const uint8_t *__restrict__ modality, int T, int32_t *__restrict__ hdr,
+            int32_t *__restrict__ perm) {
+    __shared__ int s_wave[kPlanThreads / 64];
+    const int chunk = kPlanThreads * kPlanPerThread;
+    // pass 1: count und rows, detect invalid bytes
+    int n_und = 0, bad = 0;
+    for (int base = 0; base < T; base += chunk) {
+        const int r0 = base + threadIdx.x * kPlanPerThread;
+        int cu = 0;
+        for (int i = 0; i < kPlanPerThread; ++i) {
+            const int r = r0 + i;
+            if (r < T) {
+                const uint8_t m = modality[r];
+                cu += (m == 0);
+                bad |= (m > 1);
+            }
+        }
+        int tot;
+        (void)block_exclusive_scan(cu, s_wave, tot);
+        n_und += tot;
+    }
+    bad = __syncthreads_or(bad);
+    if (bad) {
+        if (threadIdx.x == 0) {
+            hdr[0] = kErrModality;
+            hdr[1] = 0;
+            hdr[2] = 0;
+            hdr[3] = T;
+        }
+        return;
+    }
+    // pass 2: positions
+    int und_base = 0, gen_base = n_und;
+    for (int base = 0; base < T; base += chunk) {
+        const int r0 = base + threadIdx.x * kPlanPerThread;
+        uint32_t mask = 0;  // bit i: row r0+i is gen
+        int cu = 0, cnt = 0;
+        for (int i = 0; i < kPlanPerThread; ++i) {
+            const int r = r0 + i;
+            if (r < T) {
+                const uint8_t m = modality[r];
+                mask |= uint32_t(m) << i;
+                cu += (m == 0);
+                ++cnt;
+            }
+        }
+        int tot_u, tot_all;
+        const int pu = block_exclusive_scan(cu, s_wave, tot_u);
+        const int pa = block_exclusive_scan(cnt, s_wave, tot_all);
+        int iu = und_base + pu;
+        int ig = gen_base + (pa - pu);
+        for (int i = 0; i < cnt; ++i) {
+            if ((mask >> i) & 1u)
+                perm[ig++] = r0 + i;
+            else
+                perm[iu++] = r0 + i;
+        }
+        und_base += tot_u;
+        gen_base += tot_all - tot_u;
+    }
+    if (threadIdx.x == 0) {
+        hdr[0] = 0;
+        hdr[1] = n_und;
+        hdr[2] = T - n_und;
+        hdr[3] = T;
+    }
+}
+
+// ============================================================================
+// Routed GEMM
+// ============================================================================
+//
+// Orientation: the MFMA computes D[n][m] = sum_k W[n][k] * A[m][k] over a
+// 32 (weight rows) x 32 (token rows) block with v_mfma_f32_32x32x16_bf16 --
+// the only MFMA instruction used anywhere, so every output element sees the
+// same k-step sequence (ascending, 16 per step) in every launch shape.
+//
+// Workgroup: 256 threads = 4 waves in a 2 (tokens) x 2 (weights) grid; a
+// tile is BM token rows of ONE weight set (a slice of that set's segment
+// list) by BN weight rows.  Each stage stages 64 k-columns of both operands
+// in LDS with direct global->LDS 16-byte loads (global_load_lds_dwordx4).
+// LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
+// position c ^ (r & 7) so that MFMA fragment reads of 32 different rows at
+// the same k hit distinct banks.
+//
+// Gathered rows: the A-operand row of tile slot i is perm[first + i]; slots
+// past the segment's end load a valid row and are never stored.
+
+constexpr int kBK = 64;          // k per stage
+constexpr int kRowBytes = 128;   // kBK bf16
+constexpr int kThreads = 256;
+constexpr int kGroupM = 4;       // tile-order grouping (L2 reuse of W columns)
+
+struct TileInfo {
+    int set, first, count, mt, nt;
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
+// that each XCD receives a contiguous range of tile ids (tiles that share
+// operands share that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+    const int per = total >> 3, rem = total & 7;
+    const int xcd = bid & 7, local = bid >> 3;
+    return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
+}
+
+template <int BM>
+__device__ __forceinline__ bool decode_tile(const int32_t *hdr, int T, int mtiles_max, int ntiles,
+                                            TileInfo &ti) {
+    const int n_und = hdr[1], n_gen = hdr[2];
+    // a plan that does not describe exactly T rows (error, or a stale plan
+    // passed with MOT_FLAG_PLAN_READY) makes every tile exit
+    if (hdr[0] != 0 || hdr[3] != T || n_und < 0 || n_gen < 0 || n_und + n_gen != T) return false;
+    const int tu = (n_und + BM - 1) / BM;
+    const int tg = (n_gen + BM - 1) / BM;
+    const int r = xcd_remap(blockIdx.x, gridDim.x);
+    const int width = kGroupM * ntiles;
+    const int g = r / width;
+    const int first_m = g * kGroupM;
+    const int gm = min(mtiles_max - first_m, kGroupM);
+    const int in = r - g * width;
+    ti.mt = first_m + in % gm;
+    ti.nt = in / gm;
+    if (ti.mt >= tu + tg) return false;
+    if (ti.mt < tu) {
+        ti.set = 0;
+        ti.first = ti.mt * BM;
+        ti.count = min(BM, n_und - ti.first);
+    } else {
+        const int j = ti.mt - tu;
+        ti.set = 1;
+        ti.first = n_und + j * BM;
+        ti.count = min(BM, n_gen - j * BM);
+    }
+    return ti.count > 0;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global->LDS 16-byte buffer load: lane L's 16 bytes land at
+// lds + 16*L.  The buffer resource covers exactly one operand, so an offset
+// past its end reads zeros instead of faulting; `voff` is the lane's byte
+// offset, `soff` the wave-uniform k offset.  Operands are limited to 4 GiB.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer, gfx9 data format word
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcFlags);
+}
+
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint8_t *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, (int)voff, (int)soff, 0, 0);
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
+// vmcnt[5:4] at bits 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One LDS array per pipeline stage (lds0/lds1/lds2 below): the compiler's
+// alias analysis can then tell a stage being filled by DMA from the stage
+// being read, and does not make the reads wait for the in-flight loads.
+template <int BM, int BN, int STAGES, bool SWIGLU, bool PRO>
+__global__ void __launch_bounds__(kThreads)
+gemm_kernel(GemmArgs a, int mtiles_max, int ntiles) {
+    constexpr int WM = BM / 2, WN = BN / 2;   // wave tile: tokens x weight rows
+    constexpr int MJ = WM / 32, MI = WN / 32; // MFMA blocks per wave
+    constexpr int XL = BM / 32;               // A-tile DMA instructions per wave per stage
+    constexpr int WL = BN / 32;               // W-tile DMA instructions per wave per stage
+    constexpr int STAGE_BYTES = (BM + BN) * kRowBytes;
+    static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
+    static_assert(STAGES == 2 || STAGES == 3, "stages");
+    static_assert(!SWIGLU || MI % 2 == 0, "SwiGLU pairs gate and up blocks");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[STAGES > 2 ? STAGE_BYTES : 16];
+    __shared__ int32_t s_rows[BM];
+
+    TileInfo ti;
+    if (!decode_tile<BM>(a.hdr, (int)a.T, mtiles_max, ntiles, ti)) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    for (int i = tid; i < BM; i += kThreads)
+        s_rows[i] = min(max(a.perm[ti.first + min(i, ti.count - 1)], 0), (int)a.T - 1);
+    __syncthreads();
+
+    const int K = a.K;
+    const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+    const rsrc_t wr = make_rsrc(ti.set ? a.w_gen : a.w_und, a.w_bytes);
+
+    // Per-lane byte offsets of this wave's DMA instructions.  LDS position
+    // lane&7 of tile row lane>>3 receives the global 16-byte chunk
+    // (lane&7) ^ (lane>>3) (the swizzle described above).
+    const uint32_t swz = (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+    uint32_t xoff[XL], woff[WL];
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+        const int r = wave * (BM / 4) + j * 8 + (lane >> 3);
+        xoff[j] = (uint32_t)s_rows[r] * (uint32_t)(a.ldx * 2) + swz;
+    }
+#pragma unroll
+    for (int j = 0; j < WL; ++j) {
+        const int r = wave * (BN / 4) + j * 8 + (lane >> 3);
+        int wrow;
+        if constexpr (SWIGLU) {
+            const int half = r / (BN / 2), q = r % (BN / 2);
+            int col = ti.nt * (BN / 2) + half * (BN / 4) + (q % (BN / 4));
+            col = min(col, a.N - 1);
+            wrow = (q < BN / 4) ? col : a.N + col;
+        } else {
+            wrow = min(ti.nt * BN + r, a.N - 1);
+        }
+        woff[j] = (uint32_t)wrow * (uint32_t)(K * 2) + swz;
+    }
+
+    auto issue = [&](int kt, uint8_t *st) {
+        const uint32_t soff = (uint32_t)kt * kRowBytes;
+#pragma unroll
+        for (int j = 0; j < XL; ++j)
+            dma16(xr, xoff[j], soff, st + (wave * (BM / 4) + j * 8) * kRowBytes);
+#pragma unroll
+        for (int j = 0; j < WL; ++j)
+            dma16(wr, woff[j], soff, st + BM * kRowBytes + (wave * (BN / 4) + j * 8) * kRowBytes);
+    };
+
+    // Prologue operands: rstd of this lane's token rows, norm weights of the set.
+    float rs[MJ];
+    const uint16_t *nw = nullptr;
+    if constexpr (PRO) {
+#pragma unroll
+        for (int j = 0; j < MJ; ++j) rs[j] = a.rstd[s_rows[wm * WM + j * 32 + (lane & 31)]];
+        nw = ti.set ? a.nw_gen : a.nw_und;
+    }
+
+    f32x16_t acc[MI][MJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < MJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    const int nk = K / kBK;
+    const int rsel = lane & 31;   // row within a 32-row fragment
+    const int khalf = lane >> 5;  // which 8-wide half of a 16-wide k step
+    const int xrow0 = (wm * WM + rsel) * kRowBytes;
+    const int wrow0 = BM * kRowBytes + (wn * WN + rsel) * kRowBytes;
+
+    // Fragment loads of k-step s (16 k) of a staged tile.
+    auto load_frags = [&](const uint8_t *st, int s, bf16x8_t (&fa)[MI], bf16x8_t (&fb)[MJ],
+                          const uint4 &nwv) {
+        const int pos = ((2 * s + khalf) ^ (lane & 7)) * 16;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+            fa[i] = *(const bf16x8_t *)(st + wrow0 + i * 32 * kRowBytes + pos);
+#pragma unroll
+        for (int j = 0; j < MJ; ++j) {
+            if constexpr (PRO) {
+                const uint4 v = *(const uint4 *)(st + xrow0 + j * 32 * kRowBytes + pos);
+                const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+                const uint32_t wv[4] = {nwv.x, nwv.y, nwv.z, nwv.w};
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = (bf16_to_f32(in[e] & 0xffffu) * rs[j]) * bf16_to_f32(wv[e] & 0xffffu);
+                    const float hi = (bf16_to_f32(in[e] >> 16) * rs[j]) * bf16_to_f32(wv[e] >> 16);
+                    o[e] = pack2(lo, hi);
+                }
+                const uint4 ov = {o[0], o[1], o[2], o[3]};
+                fb[j] = __builtin_bit_cast(bf16x8_t, ov);
+            } else {
+                fb[j] = *(const bf16x8_t *)(st + xrow0 + j * 32 * kRowBytes + pos);
+            }
+        }
+    };
+
+    // One pipeline step: wait for stage kt, refill the oldest stage with
+    // kt + STAGES - 1, then run the 4 k-steps of stage kt.
+    auto step = [&](int kt, const uint8_t *cur, uint8_t *refill) {
+        uint4 nwv[4];
+        if constexpr (PRO) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                nwv[s] = *(const uint4 *)(nw + kt * kBK + s * 16 + khalf * 8);
+        }
+        if (STAGES > 2 && kt + 1 < nk)
+            wait_vmcnt<(STAGES > 2 ? (STAGES - 2) * (XL + WL) : 0)>();
+        else
+            wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, refill);
+        // keep the refill ahead of this stage's math (the scheduler would
+        // otherwise sink the independent loads below it)
+        __builtin_amdgcn_sched_barrier(0);
+
+        bf16x8_t fa[2][MI], fb[2][MJ];
+        load_frags(cur, 0, fa[0], fb[0], nwv[0]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3) load_frags(cur, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1], nwv[(s + 1) & 3]);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < MJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
+                                                                        acc[i][j], 0, 0, 0);
+        }
+    };
+
+    issue(0, lds0);
+    if (STAGES > 2 && nk > 1) issue(1, lds1);
+    // The k loop is unrolled by the stage count so that every LDS access names
+    // one stage array; the steps left over run after the loop (no step is
+    // conditional inside the loop, which keeps the accumulators in place).
+    int kt = 0;
+    if constexpr (STAGES == 2) {
+        for (; kt + 1 < nk; kt += 2) {
+            step(kt, lds0, lds1);
+            step(kt + 1, lds1, lds0);
+        }
+        if (kt < nk) step(kt, lds0, lds1);
+    } else {
+        for (; kt + 2 < nk; kt += 3) {
+            step(kt, lds0, lds2);
+            step(kt + 1, lds1, lds0);
+            step(kt + 2, lds2, lds1);
+        }
+        if (kt < nk) step(kt, lds0, lds2);
+        if (kt + 1 < nk) step(kt + 1, lds1, lds0);
+    }
+
+    // Epilogue.  Lane holds, for token column m = lane&31 of each block, the
+    // weight rows 8*(e/4) + 4*(lane>>5) + (e&3), e = 0..15.
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) {
+        const int mloc = wm * WM + j * 32 + rsel;
+        if (mloc >= ti.count) continue;
+        const int64_t t = s_rows[mloc];
+        uint16_t *yrow = a.y + t * a.ldy;
+        if constexpr (SWIGLU) {
+#pragma unroll
+            for (int i = 0; i < MI / 2; ++i) {
+                const int c0 = ti.nt * (BN / 2) + wn * (BN / 4) + i * 32;
+                if (c0 >= a.N) continue;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float g = acc[i][j][4 * q + e];
+                        const float u = acc[i + MI / 2][j][4 * q + e];
+                        v[e] = (g / (1.0f + expf(-g))) * u;
+                    }
+                    const uint2 pk = {pack2(v[0], v[1]), pack2(v[2], v[3])};
+                    *(uint2 *)(yrow + c0 + q * 8 + khalf * 4) = pk;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const int n0 = ti.nt * BN + wn * WN + i * 32;
+                if (n0 >= a.N) continue;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint2 pk = {pack2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]),
+                                      pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+                    *(uint2 *)(yrow + n0 + q * 8 + khalf * 4) = pk;
+                }
+            }
+        }
+    }
+}
+
+// ============================================================================
+// Routed fused add-RMSNorm
+// ============================================================================
+//
+// One wave per row, four rows per workgroup.  Lane L owns the 8-element
+// chunks L, L+64, L+128, ... of the row.  The sum of squares is taken per lane
+// over its chunks in ascending order (elements ascending within a chunk), then
+// combined across the wave with a fixed xor-butterfly -- a tree fixed by H
+// alone, so a row's rstd and outputs do not depend on T or on the row's
+// position in the pack.
+
+template <int CPL>  // chunks per lane; 0 = generic (re-reads h from memory)
+__global__ void __launch_bounds__(256)
+norm_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ residual,
+            const uint16_t *__restrict__ w_und, const uint16_t *__restrict__ w_gen,
+            const uint8_t *__restrict__ modality, float eps, uint16_t *__restrict__ out,
+            float *__restrict__ rstd_out, int T, int H, int32_t *__restrict__ err_word) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const uint8_t m = modality[t];
+    if (m > 1) {
+        if (err_word != nullptr && lane == 0) *err_word = kErrModality;
+        return;
+    }
+    const int nchunk = H >> 3;
+    const uint16_t *xr = x + (int64_t)t * H;
+    uint16_t *rr = residual ? residual + (int64_t)t * H : nullptr;
+    const uint16_t *w = m ? w_gen : w_und;
+
+    constexpr int NC = CPL > 0 ? CPL : 1;
+    uint4 hv[NC];
+    float ss = 0.0f;
+    auto make_h = [&](int c) -> uint4 {
+        uint4 xv = *(const uint4 *)(xr + c * 8);
+        if (rr == nullptr) return xv;
+        uint4 rv = *(const uint4 *)(rr + c * 8);
+        uint32_t xa[4] = {xv.x, xv.y, xv.z, xv.w}, ra[4] = {rv.x, rv.y, rv.z, rv.w}, o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo = bf16_to_f32(xa[e] & 0xffffu) + bf16_to_f32(ra[e] & 0xffffu);
+            const float hi = bf16_to_f32(xa[e] >> 16) + bf16_to_f32(ra[e] >> 16);
+            o[e] = pack2(lo, hi);
+        }
+        return uint4{o[0], o[1], o[2], o[3]};
+    };
+    auto sumsq = [&](uint4 v) {
+        uint32_t va[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo = bf16_to_f32(va[e] & 0xffffu);
+            const float hi = bf16_to_f32(va[e] >> 16);
+            ss = ss + lo * lo;
+            ss = ss + hi * hi;
+        }
+    };
+
+    if constexpr (CPL > 0) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nchunk) {
+                hv[i] = make_h(c);
+                sumsq(hv[i]);
+            }
+        }
+    } else {
+        for (int c = lane; c < nchunk; c += 64) sumsq(make_h(c));
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) ss = ss + __shfl_xor(ss, d, 64);
+
+    const float rstd = 1.0f / sqrtf(ss / (float)H + eps);
+    if (rstd_out != nullptr && lane == 0) rstd_out[t] = rstd;
+
+    auto emit = [&](int c, uint4 h) {
+        if (rr != nullptr) *(uint4 *)(rr + c * 8) = h;
+        if (out != nullptr) {
+            uint4 wv = *(const uint4 *)(w + c * 8);
+            uint32_t ha[4] = {h.x, h.y, h.z, h.w}, wa[4] = {wv.x, wv.y, wv.z, wv.w}, o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = (bf16_to_f32(ha[e] & 0xffffu) * rstd) * bf16_to_f32(wa[e] & 0xffffu);
+                const float hi = (bf16_to_f32(ha[e] >> 16) * rstd) * bf16_to_f32(wa[e] >> 16);
+                o[e] = pack2(lo, hi);
+            }
+            *(uint4 *)(out + (int64_t)t * H + c * 8) = uint4{o[0], o[1], o[2], o[3]};
+        }
+    };
+    if constexpr (CPL > 0) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane + 64 * i;
+            if (c < nchunk) emit(c, hv[i]);
+        }
+    } else {
+        // generic path: h must be recomputed before the residual is overwritten
+        for (int c = lane; c < nchunk; c += 64) emit(c, make_h(c));
+    }
+}
+
+}  // namespace
+
+// ============================================================================
+// Launchers
+// ============================================================================
+
+hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t *perm,
+                       hipStream_t stream) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, modality, (int)T,
+                       hdr, perm);
+    return hipGetLastError();
+}
+
+namespace {
+template <int BM, int BN, int STAGES, bool SWIGLU>
+hipError_t launch_gemm_t(const GemmArgs &a, hipStream_t stream) {
+    const int mtiles_max = (int)((a.T + BM - 1) / BM) + 1;
+    const int cols_per_tile = SWIGLU ? BN / 2 : BN;
+    const int ntiles = (a.N + cols_per_tile - 1) / cols_per_tile;
+    const dim3 grid(mtiles_max * ntiles);
+    if (a.rstd != nullptr)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, STAGES, SWIGLU, true>), grid, dim3(kThreads), 0,
+                           stream, a, mtiles_max, ntiles);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, STAGES, SWIGLU, false>), grid, dim3(kThreads), 0,
+                           stream, a, mtiles_max, ntiles);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs &a, bool swiglu, hipStream_t stream) {
+    if (swiglu) return launch_gemm_t<256, 256, 2, true>(a, stream);
+    return launch_gemm_t<256, 256, 2, false>(a, stream);
+}
+
+hipError_t launch_norm(const uint16_t *x, uint16_t *residual, const uint16_t *w_und,
+                       const uint16_t *w_gen, const uint8_t *modality, float eps, uint16_t *out,
+                       float *rstd_out, int64_t T, int H, int32_t *err_word,
+                       hipStream_t stream) {
+    const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+    const int cpl = (H / 8 + 63) / 64;
+#define MOT_NORM_CASE(C)                                                                       \
+    case C:                                                                                    \
+        hipLaunchKernelGGL(norm_kernel<C>, grid, block, 0, stream, x, residual, w_und, w_gen,  \
+                           modality, eps, out, rstd_out, (int)T, H, err_word);                 \
+        break;
+    switch (cpl) {
+        MOT_NORM_CASE(1)
+        MOT_NORM_CASE(2)
+        MOT_NORM_CASE(3)
+        MOT_NORM_CASE(4)
+        MOT_NORM_CASE(5)
+        MOT_NORM_CASE(6)
+        MOT_NORM_CASE(7)
+        MOT_NORM_CASE(8)
+    default:
+        hipLaunchKernelGGL(norm_kernel<0>, grid, block, 0, stream, x, residual, w_und, w_gen,
+                           modality, eps, out, rstd_out, (int)T, H, err_word);
+    }
+#undef MOT_NORM_CASE
+    return hipGetLastError();
+}
+
+}  // namespace mot

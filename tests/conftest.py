@@ -24,3 +24,12 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on stdout before it runs (a GPU fault can end the
+    process without pytest's report)."""
+    if "gpu" in request.keywords:
+        print(f"\n[gpu case] {request.node.nodeid}", flush=True)
+    yield

@@ -1,0 +1,142 @@
+"""The C-ABI library loads, exports every declared symbol, and fails closed on
+host-checkable errors before touching the GPU (no compute here)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_transformers_token_amd as mot
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mot.h")
+
+# error codes of include/mot.h
+OK, INVALID, SHAPE, MISALIGNED, WORKSPACE, DEVICE, MODALITY = range(7)
+
+A = 1 << 20  # fake, 256-byte aligned device addresses: never dereferenced
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(mot_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = mot.lib()
+    declared = _header_functions()
+    assert set(declared) == set(mot.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    nm = os.popen(f"nm -D --defined-only {mot.LIB_PATH}").read()
+    for name in declared:
+        assert re.search(rf"\bT {name}\b", nm), name
+
+
+def test_abi_version_matches_header():
+    text = open(HEADER).read()
+    v = int(re.search(r"#define MOT_ABI_VERSION (\d+)", text).group(1))
+    assert mot.abi_version() == v == mot.ABI_VERSION
+
+
+def test_status_strings():
+    for code, name in mot.STATUS.items():
+        assert mot.status_string(code).startswith(name)
+    assert "unknown" in mot.status_string(99)
+
+
+def test_workspace_bytes():
+    assert mot.workspace_bytes(0) == 256
+    assert mot.workspace_bytes(1) == 512
+    assert mot.workspace_bytes(64) == 512
+    assert mot.workspace_bytes(65) == 768
+    assert mot.workspace_bytes(4096) == 256 + 4 * 4096
+
+
+def _gemm(**kw):
+    args = dict(x=A, ldx=256, wu=2 * A, wg=3 * A, m=4 * A, y=5 * A, ldy=384, T=64, K=256, N=384,
+                rstd=None, nwu=None, nwg=None, ws=6 * A, wsb=1 << 20, flags=0)
+    args.update(kw)
+    return mot.lib().mot_routed_gemm(args["x"], args["ldx"], args["wu"], args["wg"], args["m"],
+                                     args["y"], args["ldy"], args["T"], args["K"], args["N"],
+                                     args["rstd"], args["nwu"], args["nwg"], args["ws"], args["wsb"],
+                                     args["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID),
+    (dict(T=0, x=None), OK),                  # T == 0 is a no-op
+    (dict(x=None), INVALID),
+    (dict(wg=None), INVALID),                 # both weight sets are required
+    (dict(m=None), INVALID),
+    (dict(y=None), INVALID),
+    (dict(K=100), SHAPE),
+    (dict(N=100, ldy=128), SHAPE),
+    (dict(K=0), SHAPE),
+    (dict(T=(1 << 24) + 1), SHAPE),
+    (dict(ldx=128), INVALID),                 # ldx < K
+    (dict(ldy=256), INVALID),                 # ldy < N
+    (dict(ldx=260), MISALIGNED),
+    (dict(x=A + 2), MISALIGNED),
+    (dict(y=5 * A + 8), MISALIGNED),
+    (dict(ws=None), WORKSPACE),
+    (dict(wsb=300), WORKSPACE),
+    (dict(ws=6 * A + 16), MISALIGNED),
+    (dict(rstd=7 * A), INVALID),              # prologue pointers all or none
+    (dict(rstd=7 * A, nwu=8 * A), INVALID),
+    (dict(flags=4), INVALID),
+    (dict(y=A + 1024), INVALID),              # y overlaps x
+    (dict(y=2 * A), INVALID),                 # y overlaps a weight set
+    (dict(K=(1 << 20) + 64, ldx=(1 << 20) + 64), SHAPE),
+])
+def test_gemm_fails_closed(kw, code):
+    assert _gemm(**kw) == code
+
+
+def test_swiglu_fails_closed():
+    L = mot.lib()
+    # F not a multiple of 64
+    assert L.mot_routed_gemm_swiglu(A, 256, 2 * A, 3 * A, 4 * A, 5 * A, 96, 64, 256, 96,
+                                    None, None, None, 6 * A, 1 << 20, 0, None) == SHAPE
+    assert L.mot_routed_gemm_swiglu(A, 256, 2 * A, None, 4 * A, 5 * A, 128, 64, 256, 128,
+                                    None, None, None, 6 * A, 1 << 20, 0, None) == INVALID
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID),
+    (dict(eps=0.0), INVALID),
+    (dict(eps=float("inf")), INVALID),
+    (dict(eps=float("nan")), INVALID),
+    (dict(x=None), INVALID),
+    (dict(out=None, rstd=None), INVALID),
+    (dict(H=100), SHAPE),
+    (dict(H=16384 + 64), SHAPE),
+    (dict(x=A + 4), MISALIGNED),
+    (dict(out=A), INVALID),                   # out aliases x
+    (dict(res=A + 64), INVALID),              # residual overlaps x
+    (dict(T=0, x=None), OK),
+])
+def test_norm_fails_closed(kw, code):
+    a = dict(x=A, res=2 * A, wu=3 * A, wg=4 * A, m=5 * A, eps=1e-6, out=6 * A, rstd=7 * A, T=64, H=3584,
+             ws=None)
+    a.update(kw)
+    L = mot.lib()
+    st = L.mot_fused_add_rmsnorm(a["x"], a["res"], a["wu"], a["wg"], a["m"], a["eps"], a["out"],
+                                 a["rstd"], a["T"], a["H"], a["ws"], None)
+    assert st == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID), (dict(m=None), INVALID), (dict(ws=None), WORKSPACE),
+    (dict(wsb=100), WORKSPACE), (dict(T=0, m=None), OK), (dict(ws=A + 8), MISALIGNED),
+])
+def test_plan_fails_closed(kw, code):
+    a = dict(m=A, T=100, ws=2 * A, wsb=4096)
+    a.update(kw)
+    assert mot.lib().mot_routing_plan(a["m"], a["T"], a["ws"], a["wsb"], None) == code
+
+
+def test_read_device_error_needs_workspace():
+    assert mot.lib().mot_read_device_error(None, None) == INVALID
