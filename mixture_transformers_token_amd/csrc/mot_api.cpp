@@ -88,6 +88,7 @@ int validate_routed(const RoutedCall &c) {
     if (c.ldx % 8 || c.ldy % 8) return MOT_ERR_MISALIGNED;
     const int npro = (c.rstd != nullptr) + (c.nw_und != nullptr) + (c.nw_gen != nullptr);
     if (npro != 0 && npro != 3) return MOT_ERR_INVALID_ARG;
+    if (npro == 3 && c.K > mot::kMaxPrologueK) return MOT_ERR_UNSUPPORTED_SHAPE;
     if (!aligned16(c.x) || !aligned16(c.w_und) || !aligned16(c.w_gen) || !aligned16(c.y))
         return MOT_ERR_MISALIGNED;
     if (npro == 3 && (!aligned16(c.nw_und) || !aligned16(c.nw_gen) ||

@@ -7,6 +7,10 @@
 
 namespace mot {
 
+// Largest K the routed-RMSNorm prologue supports (its norm weights are
+// staged in LDS).
+constexpr int kMaxPrologueK = 8192;
+
 // Arguments of one routed GEMM launch.  Sizes are validated by the caller.
 struct GemmArgs {
     const uint16_t *x;

@@ -154,66 +154,99 @@ plan_kernel(const uint8_t *__restrict__ modality, int T, int32_t *__restrict__ h
 // Orientation: the MFMA computes D[n][m] = sum_k W[n][k] * A[m][k] over a
 // 32 (weight rows) x 32 (token rows) block with v_mfma_f32_32x32x16_bf16 --
 // the only MFMA instruction used anywhere, so every output element sees the
-// same k-step sequence (ascending, 16 per step) in every launch shape.
+// same k-step sequence (ascending, 16 per step) whatever the tile shape, the
+// tile's place in the schedule or the pack's composition.
 //
-// Workgroup: 256 threads = 4 waves in a 2 (tokens) x 2 (weights) grid; a
+// Workgroup: 256 threads = 4 waves in a 2 (tokens) x 2 (weights) grid.  A
 // tile is BM token rows of ONE weight set (a slice of that set's segment
-// list) by BN weight rows.  Each stage stages 64 k-columns of both operands
-// in LDS with direct global->LDS 16-byte loads (global_load_lds_dwordx4).
-// LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-// position c ^ (r & 7) so that MFMA fragment reads of 32 different rows at
-// the same k hit distinct banks.
+// list) by BN weight rows.  Two tile shapes share one launch: 256x256 "big"
+// tiles fill whole rounds of the machine, and 128x128 "small" tiles cover
+// what is left (partial row blocks and the big tiles that would start a
+// mostly idle extra round).  No tile splits K: each output element has one
+// writer and one accumulation order.
+//
+// Pipeline: 4 LDS stages of 32 k-columns, filled with direct global->LDS
+// 16-byte buffer loads; the refill of a stage is issued right after the
+// barrier that frees it, three stages ahead of its use.  The first k-step's
+// fragments of the next stage are read across that barrier, so the MFMA pipe
+// has work while the barrier drains.
+//
+// LDS rows are 64 bytes (32 bf16).  The 16-byte chunk c of staged row r is
+// stored at chunk position c ^ swz(r), swz(r) = ((r >> 1) ^ ((r >> 3) & 1)) & 3,
+// which keeps any 8 or 16 consecutive rows read at one k-chunk on distinct
+// LDS banks.
 //
 // Gathered rows: the A-operand row of tile slot i is perm[first + i]; slots
 // past the segment's end load a valid row and are never stored.
 
-constexpr int kBK = 64;          // k per stage
-constexpr int kRowBytes = 128;   // kBK bf16
+constexpr int kBK = 32;          // k per stage
+constexpr int kRowBytes = 64;    // kBK bf16
+constexpr int kStages = 4;
 constexpr int kThreads = 256;
-constexpr int kGroupM = 4;       // tile-order grouping (L2 reuse of W columns)
+constexpr int kBigM = 256, kBigN = 256, kSmallM = 128, kSmallN = 128;
+constexpr int kStageBytes = (kBigM + kBigN) * kRowBytes;  // 32 KiB
 
-struct TileInfo {
-    int set, first, count, mt, nt;
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r >> 3) & 1)) & 3; }
+
+struct Tile {
+    int set;    // 0 = und, 1 = gen
+    int first;  // offset of the tile's first row in perm
+    int count;  // valid token rows
+    int wrow0;  // first weight row of the tile (tile-local W row space)
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
 // that each XCD receives a contiguous range of tile ids (tiles that share
 // operands share that XCD's L2).
-__device__ __forceinline__ int xcd_remap(int bid, int total) {
+__device__ __forceinline__ int xcd_remap(int id, int total) {
     const int per = total >> 3, rem = total & 7;
-    const int xcd = bid & 7, local = bid >> 3;
+    const int xcd = id & 7, local = id >> 3;
     return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
 }
 
-template <int BM>
-__device__ __forceinline__ bool decode_tile(const int32_t *hdr, int T, int mtiles_max, int ntiles,
-                                            TileInfo &ti) {
-    const int n_und = hdr[1], n_gen = hdr[2];
-    // a plan that does not describe exactly T rows (error, or a stale plan
-    // passed with MOT_FLAG_PLAN_READY) makes every tile exit
-    if (hdr[0] != 0 || hdr[3] != T || n_und < 0 || n_gen < 0 || n_und + n_gen != T) return false;
-    const int tu = (n_und + BM - 1) / BM;
-    const int tg = (n_gen + BM - 1) / BM;
-    const int r = xcd_remap(blockIdx.x, gridDim.x);
-    const int width = kGroupM * ntiles;
-    const int g = r / width;
-    const int first_m = g * kGroupM;
-    const int gm = min(mtiles_max - first_m, kGroupM);
-    const int in = r - g * width;
-    ti.mt = first_m + in % gm;
-    ti.nt = in / gm;
-    if (ti.mt >= tu + tg) return false;
-    if (ti.mt < tu) {
-        ti.set = 0;
-        ti.first = ti.mt * BM;
-        ti.count = min(BM, n_und - ti.first);
+// The schedule, computed identically by every workgroup from the plan's
+// counts.  nwt = number of 256-row weight tiles (ceil(weight rows / 256)).
+struct Schedule {
+    int U, G, bu, bg, nbig, nkeep, nleft, su, sg, nsmall;
+};
+
+__device__ __forceinline__ Schedule make_schedule(int U, int G, int nwt, int ncu) {
+    Schedule s;
+    s.U = U;
+    s.G = G;
+    s.bu = U / kBigM;
+    s.bg = G / kBigM;
+    s.nbig = (s.bu + s.bg) * nwt;
+    s.nkeep = s.nbig >= ncu ? (s.nbig / ncu) * ncu : s.nbig;
+    s.nleft = s.nbig - s.nkeep;
+    s.su = (U - s.bu * kBigM + kSmallM - 1) / kSmallM;
+    s.sg = (G - s.bg * kBigM + kSmallM - 1) / kSmallM;
+    s.nsmall = 4 * s.nleft + (s.su + s.sg) * 2 * nwt;
+    return s;
+}
+
+// Big tile b (0 <= b < nbig): 256-row block mb of the concatenated full
+// blocks [und..., gen...], weight tile nb; ordered in groups of 4 row blocks.
+__device__ __forceinline__ void big_tile(const Schedule &s, int b, int nwt, int &mb, int &nb) {
+    constexpr int GM = 4;
+    const int nmb = s.bu + s.bg;
+    const int width = GM * nwt;
+    const int g = b / width;
+    const int first_m = g * GM;
+    const int gm = min(nmb - first_m, GM);
+    const int in = b - g * width;
+    mb = first_m + in % gm;
+    nb = in / gm;
+}
+
+__device__ __forceinline__ void block_rows(const Schedule &s, int mb, int &set, int &first) {
+    if (mb < s.bu) {
+        set = 0;
+        first = mb * kBigM;
     } else {
-        const int j = ti.mt - tu;
-        ti.set = 1;
-        ti.first = n_und + j * BM;
-        ti.count = min(BM, n_gen - j * BM);
+        set = 1;
+        first = s.U + (mb - s.bu) * kBigM;
     }
-    return ti.count > 0;
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -234,90 +267,84 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, ui
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, (int)voff, (int)soff, 0, 0);
 }
 
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
-// vmcnt[5:4] at bits 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
+// s_waitcnt: vmcnt <= N and lgkmcnt == 0 (gfx9 encoding: vmcnt[3:0] and
+// vmcnt[5:4] at bits 15:14, expcnt 6:4 = 7 (no wait), lgkmcnt 11:8).
 template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
+__device__ __forceinline__ void wait_vm_lgkm0() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
-// One LDS array per pipeline stage (lds0/lds1/lds2 below): the compiler's
-// alias analysis can then tell a stage being filled by DMA from the stage
-// being read, and does not make the reads wait for the in-flight loads.
-template <int BM, int BN, int STAGES, bool SWIGLU, bool PRO>
-__global__ void __launch_bounds__(kThreads)
-gemm_kernel(GemmArgs a, int mtiles_max, int ntiles) {
+// One tile of BM x BN.  The four stage arrays are distinct LDS objects so
+// that the compiler can tell the stage being filled by DMA from the stages
+// being read and does not make the reads wait for the in-flight loads.
+template <int BM, int BN, bool SWIGLU, bool PRO>
+__device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint8_t *lds0,
+                                         uint8_t *lds1, uint8_t *lds2, uint8_t *lds3,
+                                         int32_t *s_rows, uint16_t *s_nw) {
     constexpr int WM = BM / 2, WN = BN / 2;   // wave tile: tokens x weight rows
     constexpr int MJ = WM / 32, MI = WN / 32; // MFMA blocks per wave
-    constexpr int XL = BM / 32;               // A-tile DMA instructions per wave per stage
-    constexpr int WL = BN / 32;               // W-tile DMA instructions per wave per stage
-    constexpr int STAGE_BYTES = (BM + BN) * kRowBytes;
+    constexpr int XL = BM / 64;               // A-tile DMA instructions per wave per stage
+    constexpr int WL = BN / 64;               // W-tile DMA instructions per wave per stage
+    constexpr int PER_STAGE = XL + WL;
     static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
-    static_assert(STAGES == 2 || STAGES == 3, "stages");
     static_assert(!SWIGLU || MI % 2 == 0, "SwiGLU pairs gate and up blocks");
-
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds2[STAGES > 2 ? STAGE_BYTES : 16];
-    __shared__ int32_t s_rows[BM];
-
-    TileInfo ti;
-    if (!decode_tile<BM>(a.hdr, (int)a.T, mtiles_max, ntiles, ti)) return;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    const int K = a.K;
+    const int nk = K / kBK;
 
     for (int i = tid; i < BM; i += kThreads)
         s_rows[i] = min(max(a.perm[ti.first + min(i, ti.count - 1)], 0), (int)a.T - 1);
+    if constexpr (PRO) {
+        const uint16_t *nw = ti.set ? a.nw_gen : a.nw_und;
+        for (int i = tid * 8; i < K; i += kThreads * 8)
+            *(uint4 *)(s_nw + i) = *(const uint4 *)(nw + i);
+    }
     __syncthreads();
 
-    const int K = a.K;
     const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
     const rsrc_t wr = make_rsrc(ti.set ? a.w_gen : a.w_und, a.w_bytes);
 
-    // Per-lane byte offsets of this wave's DMA instructions.  LDS position
-    // lane&7 of tile row lane>>3 receives the global 16-byte chunk
-    // (lane&7) ^ (lane>>3) (the swizzle described above).
-    const uint32_t swz = (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+    // Per-lane byte offsets of this wave's DMA instructions: LDS position
+    // lane&3 of staged row lane>>2 receives global chunk (lane&3) ^ swz(lane>>2).
+    const uint32_t cbyte = (uint32_t)(((lane & 3) ^ swz(lane >> 2)) * 16);
     uint32_t xoff[XL], woff[WL];
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
-        const int r = wave * (BM / 4) + j * 8 + (lane >> 3);
-        xoff[j] = (uint32_t)s_rows[r] * (uint32_t)(a.ldx * 2) + swz;
+        const int r = wave * (BM / 4) + j * 16 + (lane >> 2);
+        xoff[j] = (uint32_t)s_rows[r] * (uint32_t)(a.ldx * 2) + cbyte;
     }
 #pragma unroll
     for (int j = 0; j < WL; ++j) {
-        const int r = wave * (BN / 4) + j * 8 + (lane >> 3);
+        const int r = wave * (BN / 4) + j * 16 + (lane >> 2);
         int wrow;
         if constexpr (SWIGLU) {
             const int half = r / (BN / 2), q = r % (BN / 2);
-            int col = ti.nt * (BN / 2) + half * (BN / 4) + (q % (BN / 4));
+            int col = ti.wrow0 / 2 + half * (BN / 4) + (q % (BN / 4));
             col = min(col, a.N - 1);
             wrow = (q < BN / 4) ? col : a.N + col;
         } else {
-            wrow = min(ti.nt * BN + r, a.N - 1);
+            wrow = min(ti.wrow0 + r, a.N - 1);
         }
-        woff[j] = (uint32_t)wrow * (uint32_t)(K * 2) + swz;
+        woff[j] = (uint32_t)wrow * (uint32_t)(K * 2) + cbyte;
     }
 
     auto issue = [&](int kt, uint8_t *st) {
         const uint32_t soff = (uint32_t)kt * kRowBytes;
 #pragma unroll
         for (int j = 0; j < XL; ++j)
-            dma16(xr, xoff[j], soff, st + (wave * (BM / 4) + j * 8) * kRowBytes);
+            dma16(xr, xoff[j], soff, st + (wave * (BM / 4) + j * 16) * kRowBytes);
 #pragma unroll
         for (int j = 0; j < WL; ++j)
-            dma16(wr, woff[j], soff, st + BM * kRowBytes + (wave * (BN / 4) + j * 8) * kRowBytes);
+            dma16(wr, woff[j], soff, st + BM * kRowBytes + (wave * (BN / 4) + j * 16) * kRowBytes);
     };
 
-    // Prologue operands: rstd of this lane's token rows, norm weights of the set.
     float rs[MJ];
-    const uint16_t *nw = nullptr;
     if constexpr (PRO) {
 #pragma unroll
         for (int j = 0; j < MJ; ++j) rs[j] = a.rstd[s_rows[wm * WM + j * 32 + (lane & 31)]];
-        nw = ti.set ? a.nw_gen : a.nw_und;
     }
 
     f32x16_t acc[MI][MJ];
@@ -328,16 +355,15 @@ gemm_kernel(GemmArgs a, int mtiles_max, int ntiles) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    const int nk = K / kBK;
     const int rsel = lane & 31;   // row within a 32-row fragment
     const int khalf = lane >> 5;  // which 8-wide half of a 16-wide k step
+    const int lsw = swz(lane & 15);
     const int xrow0 = (wm * WM + rsel) * kRowBytes;
     const int wrow0 = BM * kRowBytes + (wn * WN + rsel) * kRowBytes;
 
-    // Fragment loads of k-step s (16 k) of a staged tile.
-    auto load_frags = [&](const uint8_t *st, int s, bf16x8_t (&fa)[MI], bf16x8_t (&fb)[MJ],
-                          const uint4 &nwv) {
-        const int pos = ((2 * s + khalf) ^ (lane & 7)) * 16;
+    // Fragments of k-step s (16 k) of staged k-block kt.
+    auto load_frags = [&](const uint8_t *st, int kt, int s, bf16x8_t (&fa)[MI], bf16x8_t (&fb)[MJ]) {
+        const int pos = ((2 * s + khalf) ^ lsw) * 16;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
             fa[i] = *(const bf16x8_t *)(st + wrow0 + i * 32 * kRowBytes + pos);
@@ -345,6 +371,7 @@ gemm_kernel(GemmArgs a, int mtiles_max, int ntiles) {
         for (int j = 0; j < MJ; ++j) {
             if constexpr (PRO) {
                 const uint4 v = *(const uint4 *)(st + xrow0 + j * 32 * kRowBytes + pos);
+                const uint4 nwv = *(const uint4 *)(s_nw + kt * kBK + s * 16 + khalf * 8);
                 const uint32_t in[4] = {v.x, v.y, v.z, v.w};
                 const uint32_t wv[4] = {nwv.x, nwv.y, nwv.z, nwv.w};
                 uint32_t o[4];
@@ -361,61 +388,82 @@ gemm_kernel(GemmArgs a, int mtiles_max, int ntiles) {
             }
         }
     };
+    auto mfmas = [&](const bf16x8_t (&fa)[MI], const bf16x8_t (&fb)[MJ]) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < MJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
 
-    // One pipeline step: wait for stage kt, refill the oldest stage with
-    // kt + STAGES - 1, then run the 4 k-steps of stage kt.
-    auto step = [&](int kt, const uint8_t *cur, uint8_t *refill) {
-        uint4 nwv[4];
-        if constexpr (PRO) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                nwv[s] = *(const uint4 *)(nw + kt * kBK + s * 16 + khalf * 8);
-        }
-        if (STAGES > 2 && kt + 1 < nk)
-            wait_vmcnt<(STAGES > 2 ? (STAGES - 2) * (XL + WL) : 0)>();
-        else
-            wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, refill);
-        // keep the refill ahead of this stage's math (the scheduler would
-        // otherwise sink the independent loads below it)
-        __builtin_amdgcn_sched_barrier(0);
+    bf16x8_t fa0[MI], fb0[MJ], fa1[MI], fb1[MJ];
 
-        bf16x8_t fa[2][MI], fb[2][MJ];
-        load_frags(cur, 0, fa[0], fb[0], nwv[0]);
+    // One pipeline step over staged k-block kt (slot `cur`): the fragments of
+    // its first k-step are already in fa0/fb0.
+    // Interleave the fragment reads of the next k-step with this k-step's
+    // MFMAs: one 16-byte LDS read, then two MFMAs, and so on.
+    auto interleave = [&]() {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if (s < 3) load_frags(cur, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1], nwv[(s + 1) & 3]);
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < MJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
-                                                                        acc[i][j], 0, 0, 0);
+        for (int i = 0; i < MI + MJ; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, (MI * MJ) / (MI + MJ), 0);  // MFMA
         }
     };
 
+    // One pipeline step over staged k-block kt (slot `cur`): the fragments of
+    // its first k-step are already in fa0/fb0.  The reads of the next
+    // stage's first k-step are unconditional (on the last step they read a
+    // stale, in-bounds stage whose values are never used).
+    auto step = [&](int kt, uint8_t *cur, const uint8_t *nxt) {
+        load_frags(cur, kt, 1, fa1, fb1);
+        mfmas(fa0, fb0);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        // stage kt+1 must have landed; kt+2 and kt+3 may still be in flight
+        if (kt + 3 < nk)
+            wait_vm_lgkm0<2 * PER_STAGE>();
+        else if (kt + 2 < nk)
+            wait_vm_lgkm0<PER_STAGE>();
+        else
+            wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        // every wave is past its reads of `cur`: refill it four k-blocks ahead
+        if (kt + kStages < nk) issue(kt + kStages, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(nxt, min(kt + 1, nk - 1), 0, fa0, fb0);
+        mfmas(fa1, fb1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
     issue(0, lds0);
-    if (STAGES > 2 && nk > 1) issue(1, lds1);
-    // The k loop is unrolled by the stage count so that every LDS access names
-    // one stage array; the steps left over run after the loop (no step is
-    // conditional inside the loop, which keeps the accumulators in place).
+    if (nk > 1) issue(1, lds1);
+    if (nk > 2) issue(2, lds2);
+    if (nk > 3) issue(3, lds3);
+    if (nk > 3)
+        wait_vm_lgkm0<3 * PER_STAGE>();
+    else if (nk > 2)
+        wait_vm_lgkm0<2 * PER_STAGE>();
+    else if (nk > 1)
+        wait_vm_lgkm0<PER_STAGE>();
+    else
+        wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    load_frags(lds0, 0, 0, fa0, fb0);
+
+    // The k loop is unrolled by the stage count so that every LDS access
+    // names one stage array; the steps left over run after the loop (no step
+    // is conditional inside the loop, which keeps the accumulators in place).
     int kt = 0;
-    if constexpr (STAGES == 2) {
-        for (; kt + 1 < nk; kt += 2) {
-            step(kt, lds0, lds1);
-            step(kt + 1, lds1, lds0);
-        }
-        if (kt < nk) step(kt, lds0, lds1);
-    } else {
-        for (; kt + 2 < nk; kt += 3) {
-            step(kt, lds0, lds2);
-            step(kt + 1, lds1, lds0);
-            step(kt + 2, lds2, lds1);
-        }
-        if (kt < nk) step(kt, lds0, lds2);
-        if (kt + 1 < nk) step(kt + 1, lds1, lds0);
+    for (; kt + 3 < nk; kt += 4) {
+        step(kt, lds0, lds1);
+        step(kt + 1, lds1, lds2);
+        step(kt + 2, lds2, lds3);
+        step(kt + 3, lds3, lds0);
     }
+    if (kt < nk) step(kt, lds0, lds1);
+    if (kt + 1 < nk) step(kt + 1, lds1, lds2);
+    if (kt + 2 < nk) step(kt + 2, lds2, lds3);
 
     // Epilogue.  Lane holds, for token column m = lane&31 of each block, the
     // weight rows 8*(e/4) + 4*(lane>>5) + (e&3), e = 0..15.
@@ -428,7 +476,7 @@ gemm_kernel(GemmArgs a, int mtiles_max, int ntiles) {
         if constexpr (SWIGLU) {
 #pragma unroll
             for (int i = 0; i < MI / 2; ++i) {
-                const int c0 = ti.nt * (BN / 2) + wn * (BN / 4) + i * 32;
+                const int c0 = ti.wrow0 / 2 + wn * (BN / 4) + i * 32;
                 if (c0 >= a.N) continue;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -446,7 +494,7 @@ gemm_kernel(GemmArgs a, int mtiles_max, int ntiles) {
         } else {
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
-                const int n0 = ti.nt * BN + wn * WN + i * 32;
+                const int n0 = ti.wrow0 + wn * WN + i * 32;
                 if (n0 >= a.N) continue;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -457,6 +505,67 @@ gemm_kernel(GemmArgs a, int mtiles_max, int ntiles) {
             }
         }
     }
+}
+
+// nwt: number of 256-row weight tiles; ncu: compute units of the device.
+template <bool SWIGLU, bool PRO>
+__global__ void __launch_bounds__(kThreads)
+gemm_kernel(GemmArgs a, int nwt, int ncu) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[kStageBytes];
+    __shared__ int32_t s_rows[kBigM];
+    __shared__ __attribute__((aligned(16))) uint16_t s_nw[PRO ? kMaxPrologueK : 8];
+
+    const int32_t *hdr = a.hdr;
+    const int U = hdr[1], G = hdr[2];
+    // a plan that does not describe exactly T rows (error, or a stale plan
+    // passed with MOT_FLAG_PLAN_READY) makes every tile exit
+    if (hdr[0] != 0 || hdr[3] != (int)a.T || U < 0 || G < 0 || U + G != (int)a.T) return;
+    const Schedule s = make_schedule(U, G, nwt, ncu);
+    const int bid = blockIdx.x;
+    Tile ti;
+    if (bid < s.nkeep) {
+        int mb, nb;
+        big_tile(s, xcd_remap(bid, s.nkeep), nwt, mb, nb);
+        block_rows(s, mb, ti.set, ti.first);
+        ti.count = kBigM;
+        ti.wrow0 = nb * kBigN;
+        run_tile<kBigM, kBigN, SWIGLU, PRO>(a, ti, lds0, lds1, lds2, lds3, s_rows, s_nw);
+        return;
+    }
+    const int sid = bid - s.nkeep;
+    if (sid >= s.nsmall) return;
+    const int q = xcd_remap(sid, s.nsmall);
+    if (q < 4 * s.nleft) {
+        // quarter (q & 3) of a big tile that would have opened an extra round
+        int mb, nb;
+        big_tile(s, s.nkeep + (q >> 2), nwt, mb, nb);
+        block_rows(s, mb, ti.set, ti.first);
+        ti.first += ((q >> 1) & 1) * kSmallM;
+        ti.count = kSmallM;
+        ti.wrow0 = nb * kBigN + (q & 1) * kSmallN;
+    } else {
+        // 128-row slices of the partial row blocks of each set
+        const int nws = 2 * nwt;
+        const int q2 = q - 4 * s.nleft;
+        const int sm = q2 / nws, n = q2 % nws;
+        if (sm < s.su) {
+            const int r0 = s.bu * kBigM + sm * kSmallM;
+            ti.set = 0;
+            ti.first = r0;
+            ti.count = min(kSmallM, U - r0);
+        } else {
+            const int r0 = s.bg * kBigM + (sm - s.su) * kSmallM;
+            ti.set = 1;
+            ti.first = U + r0;
+            ti.count = min(kSmallM, G - r0);
+        }
+        ti.wrow0 = n * kSmallN;
+    }
+    if (ti.count <= 0) return;
+    run_tile<kSmallM, kSmallN, SWIGLU, PRO>(a, ti, lds0, lds1, lds2, lds3, s_rows, s_nw);
 }
 
 // ============================================================================
@@ -574,25 +683,30 @@ hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t
 }
 
 namespace {
-template <int BM, int BN, int STAGES, bool SWIGLU>
-hipError_t launch_gemm_t(const GemmArgs &a, hipStream_t stream) {
-    const int mtiles_max = (int)((a.T + BM - 1) / BM) + 1;
-    const int cols_per_tile = SWIGLU ? BN / 2 : BN;
-    const int ntiles = (a.N + cols_per_tile - 1) / cols_per_tile;
-    const dim3 grid(mtiles_max * ntiles);
+template <bool SWIGLU>
+hipError_t launch_gemm_t(const GemmArgs &a, int ncu, hipStream_t stream) {
+    const int wrows = SWIGLU ? 2 * a.N : a.N;
+    const int nwt = (wrows + kBigN - 1) / kBigN;
+    // upper bound of the schedule's tile count for any split of T rows
+    const int64_t nbig_max = (a.T / kBigM) * (int64_t)nwt;
+    const int64_t nsmall_max = 4 * (int64_t)ncu + 4 * 2 * (int64_t)nwt;
+    const dim3 grid((unsigned)(nbig_max + nsmall_max));
     if (a.rstd != nullptr)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, STAGES, SWIGLU, true>), grid, dim3(kThreads), 0,
-                           stream, a, mtiles_max, ntiles);
+        hipLaunchKernelGGL((gemm_kernel<SWIGLU, true>), grid, dim3(kThreads), 0, stream, a, nwt, ncu);
     else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, STAGES, SWIGLU, false>), grid, dim3(kThreads), 0,
-                           stream, a, mtiles_max, ntiles);
+        hipLaunchKernelGGL((gemm_kernel<SWIGLU, false>), grid, dim3(kThreads), 0, stream, a, nwt, ncu);
     return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs &a, bool swiglu, hipStream_t stream) {
-    if (swiglu) return launch_gemm_t<256, 256, 2, true>(a, stream);
-    return launch_gemm_t<256, 256, 2, false>(a, stream);
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (ncu <= 0) ncu = 1;
+    return swiglu ? launch_gemm_t<true>(a, ncu, stream) : launch_gemm_t<false>(a, ncu, stream);
 }
 
 hipError_t launch_norm(const uint16_t *x, uint16_t *residual, const uint16_t *w_und,
