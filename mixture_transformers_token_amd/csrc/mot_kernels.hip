@@ -165,28 +165,30 @@ plan_kernel(const uint8_t *__restrict__ modality, int T, int32_t *__restrict__ h
 // mostly idle extra round).  No tile splits K: each output element has one
 // writer and one accumulation order.
 //
-// Pipeline: 4 LDS stages of 32 k-columns, filled with direct global->LDS
-// 16-byte buffer loads; the refill of a stage is issued right after the
-// barrier that frees it, three stages ahead of its use.  The first k-step's
-// fragments of the next stage are read across that barrier, so the MFMA pipe
-// has work while the barrier drains.
+// Pipeline: two LDS stages of 64 k-columns (one 128-byte row piece per
+// operand row, so every direct global->LDS 16-byte buffer load moves whole
+// cache lines).  A stage is consumed in four 16-wide k-steps; each k-step's
+// MFMAs run while the next k-step's fragments are read.  One barrier per
+// stage, placed before its last k-step: there the next stage must have
+// landed, the stage just read is free, and the last k-step's MFMAs cover both
+// the first fragment reads of the next stage and the refill of the freed
+// stage two stages ahead.
 //
-// LDS rows are 64 bytes (32 bf16).  The 16-byte chunk c of staged row r is
-// stored at chunk position c ^ swz(r), swz(r) = ((r >> 1) ^ ((r >> 3) & 1)) & 3,
+// LDS rows are 128 bytes (64 bf16).  The 16-byte chunk c of staged row r is
+// stored at chunk position c ^ swz(r), swz(r) = ((r >> 1) ^ ((r & 1) << 2)) & 7,
 // which keeps any 8 or 16 consecutive rows read at one k-chunk on distinct
 // LDS banks.
 //
 // Gathered rows: the A-operand row of tile slot i is perm[first + i]; slots
 // past the segment's end load a valid row and are never stored.
 
-constexpr int kBK = 32;          // k per stage
-constexpr int kRowBytes = 64;    // kBK bf16
-constexpr int kStages = 4;
+constexpr int kBK = 64;          // k per stage
+constexpr int kRowBytes = 128;   // kBK bf16
 constexpr int kThreads = 256;
 constexpr int kBigM = 256, kBigN = 256, kSmallM = 128, kSmallN = 128;
-constexpr int kStageBytes = (kBigM + kBigN) * kRowBytes;  // 32 KiB
+constexpr int kStageBytes = (kBigM + kBigN) * kRowBytes;  // 64 KiB
 
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r >> 3) & 1)) & 3; }
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
 struct Tile {
     int set;    // 0 = und, 1 = gen
@@ -275,22 +277,22 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
-// One tile of BM x BN.  The four stage arrays are distinct LDS objects so
-// that the compiler can tell the stage being filled by DMA from the stages
-// being read and does not make the reads wait for the in-flight loads.
+// One tile of BM x BN.  The two stage arrays are distinct LDS objects so that
+// the compiler can tell the stage being filled by DMA from the stage being
+// read, and does not make the reads wait for the in-flight loads.
 template <int BM, int BN, bool SWIGLU, bool PRO>
 __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint8_t *lds0,
-                                         uint8_t *lds1, uint8_t *lds2, uint8_t *lds3,
-                                         int32_t *s_rows, uint16_t *s_nw) {
+                                         uint8_t *lds1, int32_t *s_rows, uint16_t *s_nw) {
     constexpr int WM = BM / 2, WN = BN / 2;   // wave tile: tokens x weight rows
     constexpr int MJ = WM / 32, MI = WN / 32; // MFMA blocks per wave
-    constexpr int XL = BM / 64;               // A-tile DMA instructions per wave per stage
-    constexpr int WL = BN / 64;               // W-tile DMA instructions per wave per stage
+    constexpr int XL = BM / 32;               // A-tile DMA instructions per wave per stage
+    constexpr int WL = BN / 32;               // W-tile DMA instructions per wave per stage
     constexpr int PER_STAGE = XL + WL;
     static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
     static_assert(!SWIGLU || MI % 2 == 0, "SwiGLU pairs gate and up blocks");
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int K = a.K;
     const int nk = K / kBK;
@@ -307,18 +309,18 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
     const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
     const rsrc_t wr = make_rsrc(ti.set ? a.w_gen : a.w_und, a.w_bytes);
 
-    // Per-lane byte offsets of this wave's DMA instructions: LDS position
-    // lane&3 of staged row lane>>2 receives global chunk (lane&3) ^ swz(lane>>2).
-    const uint32_t cbyte = (uint32_t)(((lane & 3) ^ swz(lane >> 2)) * 16);
+    // Per-lane byte offsets of this wave's DMA instructions: instruction j
+    // fills staged rows R0 .. R0+7 (R0 = wave*(rows/4) + 8j); LDS position
+    // lane&7 of row R0 + (lane>>3) receives global chunk (lane&7) ^ swz(row).
     uint32_t xoff[XL], woff[WL];
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
-        const int r = wave * (BM / 4) + j * 16 + (lane >> 2);
-        xoff[j] = (uint32_t)s_rows[r] * (uint32_t)(a.ldx * 2) + cbyte;
+        const int r = wave * (BM / 4) + j * 8 + (lane >> 3);
+        xoff[j] = (uint32_t)s_rows[r] * (uint32_t)(a.ldx * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
     }
 #pragma unroll
     for (int j = 0; j < WL; ++j) {
-        const int r = wave * (BN / 4) + j * 16 + (lane >> 2);
+        const int r = wave * (BN / 4) + j * 8 + (lane >> 3);
         int wrow;
         if constexpr (SWIGLU) {
             const int half = r / (BN / 2), q = r % (BN / 2);
@@ -328,17 +330,21 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
         } else {
             wrow = min(ti.wrow0 + r, a.N - 1);
         }
-        woff[j] = (uint32_t)wrow * (uint32_t)(K * 2) + cbyte;
+        woff[j] = (uint32_t)wrow * (uint32_t)(K * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
     }
 
-    auto issue = [&](int kt, uint8_t *st) {
-        const uint32_t soff = (uint32_t)kt * kRowBytes;
+    auto issue_x = [&](int kt, uint8_t *st, int j) {
+        dma16(xr, xoff[j], (uint32_t)kt * kRowBytes, st + (wave * (BM / 4) + j * 8) * kRowBytes);
+    };
+    auto issue_w = [&](int kt, uint8_t *st, int j) {
+        dma16(wr, woff[j], (uint32_t)kt * kRowBytes,
+              st + BM * kRowBytes + (wave * (BN / 4) + j * 8) * kRowBytes);
+    };
+    auto issue_all = [&](int kt, uint8_t *st) {
 #pragma unroll
-        for (int j = 0; j < XL; ++j)
-            dma16(xr, xoff[j], soff, st + (wave * (BM / 4) + j * 16) * kRowBytes);
+        for (int j = 0; j < XL; ++j) issue_x(kt, st, j);
 #pragma unroll
-        for (int j = 0; j < WL; ++j)
-            dma16(wr, woff[j], soff, st + BM * kRowBytes + (wave * (BN / 4) + j * 16) * kRowBytes);
+        for (int j = 0; j < WL; ++j) issue_w(kt, st, j);
     };
 
     float rs[MJ];
@@ -358,20 +364,26 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
     const int rsel = lane & 31;   // row within a 32-row fragment
     const int khalf = lane >> 5;  // which 8-wide half of a 16-wide k step
     const int lsw = swz(lane & 15);
-    const int xrow0 = (wm * WM + rsel) * kRowBytes;
-    const int wrow0 = BM * kRowBytes + (wn * WN + rsel) * kRowBytes;
+    // LDS byte offsets (within a stage) of this lane's fragment row at each of
+    // the four k-steps; blocks of 32 rows are immediate offsets from these.
+    uint32_t xq[4], wq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t pos = (uint32_t)(((2 * q + khalf) ^ lsw) * 16);
+        xq[q] = (uint32_t)((wm * WM + rsel) * kRowBytes) + pos;
+        wq[q] = (uint32_t)(BM * kRowBytes + (wn * WN + rsel) * kRowBytes) + pos;
+    }
 
-    // Fragments of k-step s (16 k) of staged k-block kt.
-    auto load_frags = [&](const uint8_t *st, int kt, int s, bf16x8_t (&fa)[MI], bf16x8_t (&fb)[MJ]) {
-        const int pos = ((2 * s + khalf) ^ lsw) * 16;
+    // Fragments of k-step q (16 k) of staged k-block kt.
+    auto load_frags = [&](const uint8_t *st, int kt, int q, bf16x8_t (&fa)[MI], bf16x8_t (&fb)[MJ]) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
-            fa[i] = *(const bf16x8_t *)(st + wrow0 + i * 32 * kRowBytes + pos);
+            fa[i] = *(const bf16x8_t *)(st + wq[q] + i * 32 * kRowBytes);
 #pragma unroll
         for (int j = 0; j < MJ; ++j) {
             if constexpr (PRO) {
-                const uint4 v = *(const uint4 *)(st + xrow0 + j * 32 * kRowBytes + pos);
-                const uint4 nwv = *(const uint4 *)(s_nw + kt * kBK + s * 16 + khalf * 8);
+                const uint4 v = *(const uint4 *)(st + xq[q] + j * 32 * kRowBytes);
+                const uint4 nwv = *(const uint4 *)(s_nw + kt * kBK + q * 16 + khalf * 8);
                 const uint32_t in[4] = {v.x, v.y, v.z, v.w};
                 const uint32_t wv[4] = {nwv.x, nwv.y, nwv.z, nwv.w};
                 uint32_t o[4];
@@ -384,7 +396,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
                 const uint4 ov = {o[0], o[1], o[2], o[3]};
                 fb[j] = __builtin_bit_cast(bf16x8_t, ov);
             } else {
-                fb[j] = *(const bf16x8_t *)(st + xrow0 + j * 32 * kRowBytes + pos);
+                fb[j] = *(const bf16x8_t *)(st + xq[q] + j * 32 * kRowBytes);
             }
         }
     };
@@ -395,75 +407,77 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
             for (int j = 0; j < MJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     };
-
-    bf16x8_t fa0[MI], fb0[MJ], fa1[MI], fb1[MJ];
-
-    // One pipeline step over staged k-block kt (slot `cur`): the fragments of
-    // its first k-step are already in fa0/fb0.
-    // Interleave the fragment reads of the next k-step with this k-step's
-    // MFMAs: one 16-byte LDS read, then two MFMAs, and so on.
-    auto interleave = [&]() {
+    // Spread the next k-step's fragment reads over this k-step's MFMAs.
+    auto interleave_reads = [&]() {
 #pragma unroll
         for (int i = 0; i < MI + MJ; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, (MI * MJ) / (MI + MJ), 0);  // MFMA
+        }
+    };
+    // Last k-step of a stage: fragment reads of the next stage and the refill
+    // DMA of the freed stage, both spread over the MFMAs.
+    auto interleave_reads_dma = [&]() {
+#pragma unroll
+        for (int i = 0; i < MI + MJ; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      // DS read
+            __builtin_amdgcn_sched_group_barrier(0x020, PER_STAGE / (MI + MJ), 0);  // VMEM (DMA)
             __builtin_amdgcn_sched_group_barrier(0x008, (MI * MJ) / (MI + MJ), 0);  // MFMA
         }
     };
 
-    // One pipeline step over staged k-block kt (slot `cur`): the fragments of
-    // its first k-step are already in fa0/fb0.  The reads of the next
-    // stage's first k-step are unconditional (on the last step they read a
-    // stale, in-bounds stage whose values are never used).
-    auto step = [&](int kt, uint8_t *cur, const uint8_t *nxt) {
+    bf16x8_t fa0[MI], fb0[MJ], fa1[MI], fb1[MJ];
+
+    // Stage kt is staged in `cur`; stage kt+1 is in flight into `oth`.  Once
+    // every wave has finished reading `cur` it is refilled with stage kt+2.
+    // On entry fa0/fb0 hold the fragments of k-step 0 of stage kt.
+    auto stage = [&](int kt, uint8_t *cur, const uint8_t *oth) {
         load_frags(cur, kt, 1, fa1, fb1);
         mfmas(fa0, fb0);
-        interleave();
+        interleave_reads();
         __builtin_amdgcn_sched_barrier(0);
-        // stage kt+1 must have landed; kt+2 and kt+3 may still be in flight
-        if (kt + 3 < nk)
-            wait_vm_lgkm0<2 * PER_STAGE>();
-        else if (kt + 2 < nk)
-            wait_vm_lgkm0<PER_STAGE>();
-        else
-            wait_vm_lgkm0<0>();
-        __builtin_amdgcn_s_barrier();
-        // every wave is past its reads of `cur`: refill it four k-blocks ahead
-        if (kt + kStages < nk) issue(kt + kStages, cur);
-        __builtin_amdgcn_sched_barrier(0);
-        load_frags(nxt, min(kt + 1, nk - 1), 0, fa0, fb0);
+        load_frags(cur, kt, 2, fa0, fb0);
         mfmas(fa1, fb1);
-        interleave();
+        interleave_reads();
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(cur, kt, 3, fa1, fb1);
+        mfmas(fa0, fb0);
+        interleave_reads();
+        __builtin_amdgcn_sched_barrier(0);
+        // all reads of `cur` are issued; stage kt+1 (the only DMA in flight)
+        // must have landed before anyone reads it
+        wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // No branch around MFMAs (it would make the accumulators change
+        // registers): on the last two stages the refill re-reads the final
+        // k-block (in bounds) into a stage nobody reads again, and the next
+        // stage's first fragments are read from a stale, in-bounds stage.
+        load_frags(oth, min(kt + 1, nk - 1), 0, fa0, fb0);
+        issue_all(min(kt + 2, nk - 1), cur);
+        mfmas(fa1, fb1);
+        interleave_reads_dma();
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    issue(0, lds0);
-    if (nk > 1) issue(1, lds1);
-    if (nk > 2) issue(2, lds2);
-    if (nk > 3) issue(3, lds3);
-    if (nk > 3)
-        wait_vm_lgkm0<3 * PER_STAGE>();
-    else if (nk > 2)
-        wait_vm_lgkm0<2 * PER_STAGE>();
-    else if (nk > 1)
+    issue_all(0, lds0);
+    if (nk > 1) issue_all(1, lds1);
+    if (nk > 1)
         wait_vm_lgkm0<PER_STAGE>();
     else
         wait_vm_lgkm0<0>();
     __builtin_amdgcn_s_barrier();
     load_frags(lds0, 0, 0, fa0, fb0);
 
-    // The k loop is unrolled by the stage count so that every LDS access
-    // names one stage array; the steps left over run after the loop (no step
-    // is conditional inside the loop, which keeps the accumulators in place).
+    // The k loop is unrolled by two so that every LDS access names one stage
+    // array; a last odd stage runs after the loop.
     int kt = 0;
-    for (; kt + 3 < nk; kt += 4) {
-        step(kt, lds0, lds1);
-        step(kt + 1, lds1, lds2);
-        step(kt + 2, lds2, lds3);
-        step(kt + 3, lds3, lds0);
+    for (; kt + 1 < nk; kt += 2) {
+        stage(kt, lds0, lds1);
+        stage(kt + 1, lds1, lds0);
     }
-    if (kt < nk) step(kt, lds0, lds1);
-    if (kt + 1 < nk) step(kt + 1, lds1, lds2);
-    if (kt + 2 < nk) step(kt + 2, lds2, lds3);
+    if (kt < nk) stage(kt, lds0, lds1);
+    wait_vm_lgkm0<0>();  // no DMA may still be writing LDS when the tile ends
 
     // Epilogue.  Lane holds, for token column m = lane&31 of each block, the
     // weight rows 8*(e/4) + 4*(lane>>5) + (e&3), e = 0..15.
@@ -513,8 +527,6 @@ __global__ void __launch_bounds__(kThreads)
 gemm_kernel(GemmArgs a, int nwt, int ncu) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds2[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds3[kStageBytes];
     __shared__ int32_t s_rows[kBigM];
     __shared__ __attribute__((aligned(16))) uint16_t s_nw[PRO ? kMaxPrologueK : 8];
 
@@ -532,7 +544,7 @@ gemm_kernel(GemmArgs a, int nwt, int ncu) {
         block_rows(s, mb, ti.set, ti.first);
         ti.count = kBigM;
         ti.wrow0 = nb * kBigN;
-        run_tile<kBigM, kBigN, SWIGLU, PRO>(a, ti, lds0, lds1, lds2, lds3, s_rows, s_nw);
+        run_tile<kBigM, kBigN, SWIGLU, PRO>(a, ti, lds0, lds1, s_rows, s_nw);
         return;
     }
     const int sid = bid - s.nkeep;
@@ -565,7 +577,7 @@ gemm_kernel(GemmArgs a, int nwt, int ncu) {
         ti.wrow0 = n * kSmallN;
     }
     if (ti.count <= 0) return;
-    run_tile<kSmallM, kSmallN, SWIGLU, PRO>(a, ti, lds0, lds1, lds2, lds3, s_rows, s_nw);
+    run_tile<kSmallM, kSmallN, SWIGLU, PRO>(a, ti, lds0, lds1, s_rows, s_nw);
 }
 
 // ============================================================================
