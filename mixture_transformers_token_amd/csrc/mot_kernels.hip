@@ -186,7 +186,7 @@ constexpr int kBK = 64;          // k per stage
 constexpr int kRowBytes = 128;   // kBK bf16
 constexpr int kThreads = 256;
 constexpr int kBigM = 256, kBigN = 256, kSmallM = 128, kSmallN = 128;
-constexpr int kStageBytes = (kBigM + kBigN) * kRowBytes;  // 64 KiB
+constexpr int kArrayBytes = kBigM * kRowBytes;  // 32 KiB: one big operand tile or one small stage
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
@@ -280,9 +280,14 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // One tile of BM x BN.  The two stage arrays are distinct LDS objects so that
 // the compiler can tell the stage being filled by DMA from the stage being
 // read, and does not make the reads wait for the in-flight loads.
-template <int BM, int BN, bool SWIGLU, bool PRO>
-__device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint8_t *lds0,
-                                         uint8_t *lds1, int32_t *s_rows, uint16_t *s_nw) {
+//
+// NS pipeline stages; stage s stages its A rows at xb[s] and its W rows at
+// wb[s] (BM and BN rows of 128 bytes).  Every stage issues exactly one
+// refill (re-reading the final k-block when it runs past the end), so the
+// number of DMA instructions in flight is a compile-time constant.
+template <int BM, int BN, int NS, bool SWIGLU, bool PRO>
+__device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint8_t *const (&xb)[NS],
+                                         uint8_t *const (&wb)[NS], int32_t *s_rows, uint16_t *s_nw) {
     constexpr int WM = BM / 2, WN = BN / 2;   // wave tile: tokens x weight rows
     constexpr int MJ = WM / 32, MI = WN / 32; // MFMA blocks per wave
     constexpr int XL = BM / 32;               // A-tile DMA instructions per wave per stage
@@ -333,18 +338,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
         woff[j] = (uint32_t)wrow * (uint32_t)(K * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
     }
 
-    auto issue_x = [&](int kt, uint8_t *st, int j) {
-        dma16(xr, xoff[j], (uint32_t)kt * kRowBytes, st + (wave * (BM / 4) + j * 8) * kRowBytes);
-    };
-    auto issue_w = [&](int kt, uint8_t *st, int j) {
-        dma16(wr, woff[j], (uint32_t)kt * kRowBytes,
-              st + BM * kRowBytes + (wave * (BN / 4) + j * 8) * kRowBytes);
-    };
-    auto issue_all = [&](int kt, uint8_t *st) {
+    // DMA of k-block kt into stage slot s.
+    auto issue_all = [&](int kt, int s) {
 #pragma unroll
-        for (int j = 0; j < XL; ++j) issue_x(kt, st, j);
+        for (int j = 0; j < XL; ++j)
+            dma16(xr, xoff[j], (uint32_t)kt * kRowBytes, xb[s] + (wave * (BM / 4) + j * 8) * kRowBytes);
 #pragma unroll
-        for (int j = 0; j < WL; ++j) issue_w(kt, st, j);
+        for (int j = 0; j < WL; ++j)
+            dma16(wr, woff[j], (uint32_t)kt * kRowBytes, wb[s] + (wave * (BN / 4) + j * 8) * kRowBytes);
     };
 
     float rs[MJ];
@@ -371,18 +372,19 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
     for (int q = 0; q < 4; ++q) {
         const uint32_t pos = (uint32_t)(((2 * q + khalf) ^ lsw) * 16);
         xq[q] = (uint32_t)((wm * WM + rsel) * kRowBytes) + pos;
-        wq[q] = (uint32_t)(BM * kRowBytes + (wn * WN + rsel) * kRowBytes) + pos;
+        wq[q] = (uint32_t)((wn * WN + rsel) * kRowBytes) + pos;
     }
 
     // Fragments of k-step q (16 k) of staged k-block kt.
-    auto load_frags = [&](const uint8_t *st, int kt, int q, bf16x8_t (&fa)[MI], bf16x8_t (&fb)[MJ]) {
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-            fa[i] = *(const bf16x8_t *)(st + wq[q] + i * 32 * kRowBytes);
+    // Reads are emitted in the order the MFMAs (i-major) first need them:
+    // fa[0], fb[0..MJ), then fa[1..MI).
+    auto load_frags = [&](int s, int kt, int q, bf16x8_t (&fa)[MI], bf16x8_t (&fb)[MJ]) {
+        const uint8_t *xs = xb[s], *ws = wb[s];
+        fa[0] = *(const bf16x8_t *)(ws + wq[q]);
 #pragma unroll
         for (int j = 0; j < MJ; ++j) {
             if constexpr (PRO) {
-                const uint4 v = *(const uint4 *)(st + xq[q] + j * 32 * kRowBytes);
+                const uint4 v = *(const uint4 *)(xs + xq[q] + j * 32 * kRowBytes);
                 const uint4 nwv = *(const uint4 *)(s_nw + kt * kBK + q * 16 + khalf * 8);
                 const uint32_t in[4] = {v.x, v.y, v.z, v.w};
                 const uint32_t wv[4] = {nwv.x, nwv.y, nwv.z, nwv.w};
@@ -396,9 +398,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
                 const uint4 ov = {o[0], o[1], o[2], o[3]};
                 fb[j] = __builtin_bit_cast(bf16x8_t, ov);
             } else {
-                fb[j] = *(const bf16x8_t *)(st + xq[q] + j * 32 * kRowBytes);
+                fb[j] = *(const bf16x8_t *)(xs + xq[q] + j * 32 * kRowBytes);
             }
         }
+#pragma unroll
+        for (int i = 1; i < MI; ++i)
+            fa[i] = *(const bf16x8_t *)(ws + wq[q] + i * 32 * kRowBytes);
     };
     auto mfmas = [&](const bf16x8_t (&fa)[MI], const bf16x8_t (&fb)[MJ]) {
 #pragma unroll
@@ -407,76 +412,82 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
             for (int j = 0; j < MJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     };
-    // Spread the next k-step's fragment reads over this k-step's MFMAs.
+    // Issue the next k-step's fragment reads over the first MFMAs of this
+    // k-step (one read per MFMA), leaving the rest of the k-step to cover
+    // their latency.
+    static_assert(MI * MJ >= MI + MJ, "more MFMAs than reads per k-step");
     auto interleave_reads = [&]() {
 #pragma unroll
         for (int i = 0; i < MI + MJ; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      // DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, (MI * MJ) / (MI + MJ), 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         }
+        if constexpr (MI * MJ > MI + MJ)
+            __builtin_amdgcn_sched_group_barrier(0x008, MI * MJ - (MI + MJ), 0);
     };
-    // Last k-step of a stage: fragment reads of the next stage and the refill
-    // DMA of the freed stage, both spread over the MFMAs.
+    // Last k-step of a stage: the next stage's fragment reads as above, and
+    // the refill DMA of the freed stage spread evenly over all the MFMAs.
+    static_assert(PER_STAGE % (MI * MJ) == 0, "DMA per MFMA");
     auto interleave_reads_dma = [&]() {
 #pragma unroll
-        for (int i = 0; i < MI + MJ; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      // DS read
-            __builtin_amdgcn_sched_group_barrier(0x020, PER_STAGE / (MI + MJ), 0);  // VMEM (DMA)
-            __builtin_amdgcn_sched_group_barrier(0x008, (MI * MJ) / (MI + MJ), 0);  // MFMA
+        for (int i = 0; i < MI * MJ; ++i) {
+            if (i < MI + MJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            __builtin_amdgcn_sched_group_barrier(0x020, PER_STAGE / (MI * MJ), 0); // VMEM (DMA)
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
         }
     };
 
     bf16x8_t fa0[MI], fb0[MJ], fa1[MI], fb1[MJ];
 
-    // Stage kt is staged in `cur`; stage kt+1 is in flight into `oth`.  Once
-    // every wave has finished reading `cur` it is refilled with stage kt+2.
-    // On entry fa0/fb0 hold the fragments of k-step 0 of stage kt.
-    auto stage = [&](int kt, uint8_t *cur, const uint8_t *oth) {
-        load_frags(cur, kt, 1, fa1, fb1);
+    // Stage kt sits in slot s = kt % NS; stages kt+1 .. kt+NS-1 are in flight.
+    // Once every wave has finished reading slot s it is refilled with k-block
+    // kt+NS.  On entry fa0/fb0 hold the fragments of k-step 0 of stage kt.
+    auto stage = [&](int kt, int s) {
+        const int nxt = (s + 1) % NS;
+        load_frags(s, kt, 1, fa1, fb1);
         mfmas(fa0, fb0);
         interleave_reads();
         __builtin_amdgcn_sched_barrier(0);
-        load_frags(cur, kt, 2, fa0, fb0);
+        load_frags(s, kt, 2, fa0, fb0);
         mfmas(fa1, fb1);
         interleave_reads();
         __builtin_amdgcn_sched_barrier(0);
-        load_frags(cur, kt, 3, fa1, fb1);
+        load_frags(s, kt, 3, fa1, fb1);
         mfmas(fa0, fb0);
         interleave_reads();
         __builtin_amdgcn_sched_barrier(0);
-        // all reads of `cur` are issued; stage kt+1 (the only DMA in flight)
-        // must have landed before anyone reads it
-        wait_vm_lgkm0<0>();
+        // all reads of slot s are issued; stage kt+1 must have landed (the
+        // NS-2 younger stages may still be in flight)
+        wait_vm_lgkm0<PER_STAGE * (NS - 2)>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         // No branch around MFMAs (it would make the accumulators change
-        // registers): on the last two stages the refill re-reads the final
-        // k-block (in bounds) into a stage nobody reads again, and the next
-        // stage's first fragments are read from a stale, in-bounds stage.
-        load_frags(oth, min(kt + 1, nk - 1), 0, fa0, fb0);
-        issue_all(min(kt + 2, nk - 1), cur);
+        // registers): past the end the refill re-reads the final k-block (in
+        // bounds) into a slot nobody reads again, and the first fragments of
+        // a stage that does not exist are read from a stale, in-bounds slot.
+        load_frags(nxt, min(kt + 1, nk - 1), 0, fa0, fb0);
+        issue_all(min(kt + NS, nk - 1), s);
         mfmas(fa1, fb1);
         interleave_reads_dma();
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    issue_all(0, lds0);
-    if (nk > 1) issue_all(1, lds1);
-    if (nk > 1)
-        wait_vm_lgkm0<PER_STAGE>();
-    else
-        wait_vm_lgkm0<0>();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) issue_all(min(s, nk - 1), s);
+    wait_vm_lgkm0<PER_STAGE * (NS - 1)>();
     __builtin_amdgcn_s_barrier();
-    load_frags(lds0, 0, 0, fa0, fb0);
+    load_frags(0, 0, 0, fa0, fb0);
 
-    // The k loop is unrolled by two so that every LDS access names one stage
-    // array; a last odd stage runs after the loop.
+    // The k loop is unrolled by NS so that every LDS access names one stage
+    // array; the stages left over run after the loop.
     int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        stage(kt, lds0, lds1);
-        stage(kt + 1, lds1, lds0);
+    for (; kt + NS - 1 < nk; kt += NS) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) stage(kt + s, s);
     }
-    if (kt < nk) stage(kt, lds0, lds1);
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (kt + s < nk) stage(kt + s, s);
     wait_vm_lgkm0<0>();  // no DMA may still be writing LDS when the tile ends
 
     // Epilogue.  Lane holds, for token column m = lane&31 of each block, the
@@ -525,8 +536,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
 template <bool SWIGLU, bool PRO>
 __global__ void __launch_bounds__(kThreads)
 gemm_kernel(GemmArgs a, int nwt, int ncu) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStageBytes];
+    // four 32 KiB LDS arrays: big tiles use two stages of (A in one array,
+    // W in the next), small tiles four stages of one array each
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kArrayBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kArrayBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[kArrayBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[kArrayBytes];
     __shared__ int32_t s_rows[kBigM];
     __shared__ __attribute__((aligned(16))) uint16_t s_nw[PRO ? kMaxPrologueK : 8];
 
@@ -544,7 +559,8 @@ gemm_kernel(GemmArgs a, int nwt, int ncu) {
         block_rows(s, mb, ti.set, ti.first);
         ti.count = kBigM;
         ti.wrow0 = nb * kBigN;
-        run_tile<kBigM, kBigN, SWIGLU, PRO>(a, ti, lds0, lds1, s_rows, s_nw);
+        uint8_t *const xb[2] = {lds0, lds2}, *const wb[2] = {lds1, lds3};
+        run_tile<kBigM, kBigN, 2, SWIGLU, PRO>(a, ti, xb, wb, s_rows, s_nw);
         return;
     }
     const int sid = bid - s.nkeep;
@@ -577,7 +593,10 @@ gemm_kernel(GemmArgs a, int nwt, int ncu) {
         ti.wrow0 = n * kSmallN;
     }
     if (ti.count <= 0) return;
-    run_tile<kSmallM, kSmallN, SWIGLU, PRO>(a, ti, lds0, lds1, s_rows, s_nw);
+    constexpr int kHalf = kSmallM * kRowBytes;
+    uint8_t *const xb[4] = {lds0, lds1, lds2, lds3};
+    uint8_t *const wb[4] = {lds0 + kHalf, lds1 + kHalf, lds2 + kHalf, lds3 + kHalf};
+    run_tile<kSmallM, kSmallN, 4, SWIGLU, PRO>(a, ti, xb, wb, s_rows, s_nw);
 }
 
 // ============================================================================
