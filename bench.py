@@ -45,11 +45,17 @@ def parse():
     p.add_argument("--no-components", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="run one 1 GiB device copy first (HBM counter calibration under rocprofv3)")
-    p.add_argument("--cpu-rows", type=int, default=96, help="oracle row sample for cpu_baseline")
+    p.add_argument("--cpu-rows", type=int, default=4096,
+                   help="oracle row sample for cpu_baseline (stratified, with every segment boundary)")
     return p.parse_args()
 
 
 def git_rev():
+    info = os.path.join(ROOT, "mixture_transformers_token_amd", "BUILD_INFO.json")
+    if os.path.exists(info):
+        with open(info) as f:
+            d = json.load(f)
+        return d.get("commit", "unknown"), d.get("dirty")
     try:
         rev = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
                              text=True).stdout.strip()
@@ -199,16 +205,20 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        rows = W.sample_rows(m, args.cpu_rows, seed=7)
+        rows = W.sample_rows(m, args.cpu_rows, seed=7) if args.cpu_rows < T else np.arange(T)
         xb, wub, wgb = W.bits(x)[rows], W.bits(wu), W.bits(wg)
         threads = oracle.max_threads()
-        t0 = time.perf_counter()
-        oracle.routed_gemm(xb, wub, wgb, m[rows], want_ref=True, want_out=True)
-        cs = time.perf_counter() - t0
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.routed_gemm(xb, wub, wgb, m[rows], want_ref=True, want_out=True)
+            times.append(time.perf_counter() - t0)
+        cs = sorted(times)[1]
+        what = "all" if rows.size == T else f"{rows.size} of"
         cpu = {"value": round(2.0 * rows.size * K * N / cs / 1e12, 6), "unit": "TFLOP/s",
                "cores": threads, "kind": "oracle",
-               "sample": f"{rows.size} of {T} QKV rows (stratified by modality, every segment "
-                         f"boundary), full K={K}, N={N}, fp64; {cs:.1f} s"}
+               "sample": f"{what} {T} QKV rows (K={K}, N={N}), fp64 oracle, median of 3 runs "
+                         f"of {cs:.2f} s each"}
 
     rev, dirty = git_rev()
     line = {

@@ -40,7 +40,24 @@ def build(force: bool = True, verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
     os.replace(tmp, LIB)
+    _write_build_info()
     return LIB
+
+
+def _write_build_info():
+    """Record the source revision the library was built from (the GPU run
+    has no git history)."""
+    import json
+    root = os.path.dirname(HERE)
+    try:
+        rev = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=root, capture_output=True,
+                             text=True).stdout.strip() or "unknown"
+        dirty = subprocess.run(["git", "status", "--porcelain", "--", "mixture_transformers_token_amd",
+                                "include"], cwd=root, capture_output=True, text=True).stdout.strip() != ""
+    except Exception:
+        rev, dirty = "unknown", None
+    with open(os.path.join(HERE, "BUILD_INFO.json"), "w") as f:
+        json.dump({"commit": rev, "dirty": dirty}, f)
 
 
 if __name__ == "__main__":
