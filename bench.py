@@ -66,6 +66,26 @@ def git_rev():
         return "unknown", None
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "qkv_routed_gemm_T4096_hbm_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "mixture_transformers_token_amd", "csrc", "mot_kernels.hip")
+
+
+def measured_traffic():
+    """HBM-side bytes per launch of the QKV routed GEMM from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary -- only while the kernel source
+    is the one those counters were taken on (else None)."""
+    import hashlib
+    try:
+        kv = dict(line.strip().split("=", 1) for line in open(TRAFFIC_SUMMARY) if "=" in line
+                  and not line.startswith(("|", "-", "`", "#")) and " " not in line.strip())
+        h = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+        if kv.get("kernel_source_sha256_16") != h:
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def time_calls(fn, iters, stream):
     """Average duration of `fn` launches, HIP events on the launch stream."""
     import torch
@@ -134,10 +154,11 @@ def main():
     plan_s = time_calls(lambda: mot.routing_plan(md, ws), 50, stream)
     achieved = flops / gemm_s / 1e12
     n_und, n_gen = int((m == 0).sum()), int((m == 1).sum())
+    traffic = measured_traffic()
     roofline = {
         "kernel": "gemm_kernel<256,256> (routed QKV GEMM)",
         "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
         "avg_kernel_us": round(gemm_s * 1e6, 2), "plan_kernel_us": round(plan_s * 1e6, 2),
         "flop_per_launch": flops,
         "alg_bytes_per_launch": 2 * (2 * N * K + T * K + T * N) + T,
