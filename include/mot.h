@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 1
+#define MOT_ABI_VERSION 2
 
 typedef enum mot_status {
     MOT_OK = 0,
@@ -80,7 +80,8 @@ size_t mot_workspace_bytes(int64_t T);
 
 /* Routing plan (the segment list): from modality[T] build the header and perm
  * described above in `workspace`.  The routed GEMM calls run this step
- * themselves unless MOT_FLAG_PLAN_READY is given.
+ * themselves unless MOT_FLAG_PLAN_READY is given (for packs of up to 8192
+ * rows inside the GEMM kernel, which also writes the header and perm).
  * Errors: MOT_ERR_INVALID_ARG (T < 0, null pointers with T > 0),
  * MOT_ERR_UNSUPPORTED_SHAPE (T > MOT_MAX_T), MOT_ERR_WORKSPACE, MOT_ERR_DEVICE. */
 int mot_routing_plan(const uint8_t *modality, int64_t T,
@@ -89,6 +90,16 @@ int mot_routing_plan(const uint8_t *modality, int64_t T,
 /* Flags of the routed GEMM calls. */
 #define MOT_FLAG_PLAN_READY 1u /* workspace already holds the plan of this `modality`,
                                   built earlier in stream order; skip rebuilding it */
+/* Tile shapes (token rows x weight rows per workgroup).  By default the
+ * kernel runs 256x256 tiles for whole rounds of the GPU and 128x128 tiles for
+ * the rest, chosen on the device from the pack's set sizes; these flags force
+ * one shape, for tuning and tests.  Every shape runs the same per-element k
+ * order, so the output bytes do not depend on the shape.  Setting both bits
+ * is MOT_ERR_INVALID_ARG. */
+#define MOT_FLAG_TILE_AUTO    0x00u
+#define MOT_FLAG_TILE_256x256 0x10u
+#define MOT_FLAG_TILE_128x128 0x20u
+#define MOT_FLAG_TILE_MASK    0x30u
 
 /* Routed GEMM (QKV, O and down projections):
  *   y[t][n] = bf16_rne( sum_k A[t][k] * W_{modality[t]}[n][k] ),  0 <= n < N,

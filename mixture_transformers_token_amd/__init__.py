@@ -22,10 +22,13 @@ __all__ = [
     "read_device_error", "status_string", "LIB_PATH",
 ]
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
 WS_HEADER_BYTES = 256
 FLAG_PLAN_READY = 1
+# tile-shape overrides (the library picks the shape by default; every shape
+# gives the same bytes)
+TILE_FLAGS = {None: 0x00, "auto": 0x00, "256x256": 0x10, "128x128": 0x20}
 
 # exported symbols, as declared in include/mot.h
 EXPORTS = (
@@ -149,7 +152,7 @@ def plan_view(workspace: torch.Tensor, T: int):
     return hdr, perm
 
 
-def _routed(fn, name, x, w_und, w_gen, modality, out, norm, workspace, plan_ready, swiglu):
+def _routed(fn, name, x, w_und, w_gen, modality, out, norm, workspace, plan_ready, swiglu, tile):
     _req(x, "x", torch.bfloat16, 2)
     _req(w_und, "w_und", torch.bfloat16, 2)
     _req(w_gen, "w_gen", torch.bfloat16, 2)
@@ -184,26 +187,30 @@ def _routed(fn, name, x, w_und, w_gen, modality, out, norm, workspace, plan_read
         _req(nw_g, "norm w_gen", torch.bfloat16, 1)
         if rstd.shape[0] != T or nw_u.shape[0] != K or nw_g.shape[0] != K:
             raise ValueError("prologue shapes: rstd [T], norm weights [K]")
+    if tile not in TILE_FLAGS:
+        raise ValueError(f"tile must be one of {sorted(k for k in TILE_FLAGS if k)}")
     mod = modality.contiguous()
     st = fn(_ptr(x), _rows(x, "x"), _ptr(w_und), _ptr(w_gen), _ptr(mod), _ptr(out), _rows(out, "out"),
             T, K, N, _ptr(rstd), _ptr(nw_u), _ptr(nw_g), _ptr(workspace), workspace.numel(),
-            FLAG_PLAN_READY if plan_ready else 0, _stream(x.device))
+            (FLAG_PLAN_READY if plan_ready else 0) | TILE_FLAGS[tile], _stream(x.device))
     _check(st, name)
     return out
 
 
-def routed_gemm(x, w_und, w_gen, modality, out=None, norm=None, workspace=None, plan_ready=False):
+def routed_gemm(x, w_und, w_gen, modality, out=None, norm=None, workspace=None, plan_ready=False,
+                tile=None):
     """y[t] = x[t] @ W_{modality[t]}^T in bf16 (fp32 accumulate).  W_* are [N, K].
-    norm=(rstd [T] fp32, nw_und [K], nw_gen [K]) applies the routed-RMSNorm prologue."""
+    norm=(rstd [T] fp32, nw_und [K], nw_gen [K]) applies the routed-RMSNorm prologue.
+    tile: None (library's choice) or "256x256" / "128x128" (force one tile shape)."""
     return _routed(lib().mot_routed_gemm, "mot_routed_gemm", x, w_und, w_gen, modality, out, norm,
-                   workspace, plan_ready, swiglu=False)
+                   workspace, plan_ready, swiglu=False, tile=tile)
 
 
 def routed_gemm_swiglu(x, wgu_und, wgu_gen, modality, out=None, norm=None, workspace=None,
-                       plan_ready=False):
+                       plan_ready=False, tile=None):
     """act[t] = silu(g) * u with [g | u] = x[t] @ Wgu_{modality[t]}^T; Wgu_* are [2F, K]."""
     return _routed(lib().mot_routed_gemm_swiglu, "mot_routed_gemm_swiglu", x, wgu_und, wgu_gen,
-                   modality, out, norm, workspace, plan_ready, swiglu=True)
+                   modality, out, norm, workspace, plan_ready, swiglu=True, tile=tile)
 
 
 def fused_add_rmsnorm(x, residual, w_und, w_gen, modality, eps=1e-6, out=True, rstd=True,

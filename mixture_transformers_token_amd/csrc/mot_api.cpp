@@ -82,13 +82,14 @@ int validate_routed(const RoutedCall &c) {
     if (c.T > MOT_MAX_T) return MOT_ERR_UNSUPPORTED_SHAPE;
     if (c.K == 0 || c.N == 0 || c.K % 64 || c.N % 64 || c.K > MOT_MAX_DIM || c.N > MOT_MAX_DIM)
         return MOT_ERR_UNSUPPORTED_SHAPE;
-    if ((c.flags & ~MOT_FLAG_PLAN_READY) != 0) return MOT_ERR_INVALID_ARG;
+    if ((c.flags & ~(MOT_FLAG_PLAN_READY | MOT_FLAG_TILE_MASK)) != 0) return MOT_ERR_INVALID_ARG;
     if (c.ldx < c.K || c.ldy < c.N || c.ldx > (int64_t(1) << 32) || c.ldy > (int64_t(1) << 32))
         return MOT_ERR_INVALID_ARG;
     if (c.ldx % 8 || c.ldy % 8) return MOT_ERR_MISALIGNED;
     const int npro = (c.rstd != nullptr) + (c.nw_und != nullptr) + (c.nw_gen != nullptr);
     if (npro != 0 && npro != 3) return MOT_ERR_INVALID_ARG;
     if (npro == 3 && c.K > mot::kMaxPrologueK) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if ((c.flags & MOT_FLAG_TILE_MASK) == MOT_FLAG_TILE_MASK) return MOT_ERR_INVALID_ARG;
     if (!aligned16(c.x) || !aligned16(c.w_und) || !aligned16(c.w_gen) || !aligned16(c.y))
         return MOT_ERR_MISALIGNED;
     if (npro == 3 && (!aligned16(c.nw_und) || !aligned16(c.nw_gen) ||
@@ -118,10 +119,15 @@ int run_routed(const RoutedCall &c, bool swiglu, void *stream) {
     if (!guard.ok()) return MOT_ERR_DEVICE;
     int32_t *hdr = static_cast<int32_t *>(c.workspace);
     int32_t *perm = reinterpret_cast<int32_t *>(static_cast<char *>(c.workspace) + MOT_WS_HEADER_BYTES);
-    if (!(c.flags & MOT_FLAG_PLAN_READY)) {
+    const bool plan_ready = (c.flags & MOT_FLAG_PLAN_READY) != 0;
+    const bool inline_route = !plan_ready && c.T <= mot::kInlineRouteMaxT;
+    if (!plan_ready && !inline_route) {
         if (mot::launch_plan(c.modality, c.T, hdr, perm, s) != hipSuccess) return MOT_ERR_DEVICE;
     }
     mot::GemmArgs a;
+    a.modality = c.modality;
+    a.hdr_out = hdr;
+    a.perm_out = perm;
     a.x = c.x;
     a.ldx = c.ldx;
     a.w_und = c.w_und;
@@ -136,9 +142,16 @@ int run_routed(const RoutedCall &c, bool swiglu, void *stream) {
     a.T = c.T;
     a.K = (int)c.K;
     a.N = (int)c.N;
+    a.wrows = (int)c.w_rows;
+    switch (c.flags & MOT_FLAG_TILE_MASK) {
+    case MOT_FLAG_TILE_256x256: a.tile_mode = 1; break;
+    case MOT_FLAG_TILE_128x128: a.tile_mode = 2; break;
+    default: a.tile_mode = 0;
+    }
     a.x_bytes = (uint32_t)(((c.T - 1) * c.ldx + c.K) * 2);
     a.w_bytes = (uint32_t)(c.w_rows * c.K * 2);
-    if (mot::launch_gemm(a, swiglu, s) != hipSuccess) return MOT_ERR_DEVICE;
+    a.y_bytes = (uint32_t)(((c.T - 1) * c.ldy + c.N) * 2);
+    if (mot::launch_gemm(a, swiglu, inline_route, s) != hipSuccess) return MOT_ERR_DEVICE;
     return MOT_OK;
 }
 

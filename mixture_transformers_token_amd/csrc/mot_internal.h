@@ -11,6 +11,11 @@ namespace mot {
 // staged in LDS).
 constexpr int kMaxPrologueK = 8192;
 
+// Packs of at most this many rows build their segment list inside the GEMM
+// kernel (every workgroup scans the modality bytes); larger packs run the
+// plan kernel first.
+constexpr int64_t kInlineRouteMaxT = 8192;
+
 // Arguments of one routed GEMM launch.  Sizes are validated by the caller.
 struct GemmArgs {
     const uint16_t *x;
@@ -19,21 +24,30 @@ struct GemmArgs {
     const uint16_t *w_gen;
     uint16_t *y;
     int64_t ldy;
+    const uint8_t *modality;  // [T]; read by the in-kernel segment list
     const int32_t *hdr;   // workspace header: error, n_und, n_gen, T
     const int32_t *perm;  // workspace segment list
+    int32_t *hdr_out;     // same header and list, written by the in-kernel segment list
+    int32_t *perm_out;
     const float *rstd;    // prologue (nullptr: none)
     const uint16_t *nw_und;
     const uint16_t *nw_gen;
     int64_t T;
     int K;
     int N;                // output columns (F for SwiGLU)
+    int wrows;            // weight rows per set (N, or 2F for SwiGLU)
+    int tile_mode;        // 0: big tiles for whole rounds, small for the rest;
+                          // 1: big (256x256) tiles only; 2: small (128x128) only
     uint32_t x_bytes;     // extent of x from its base (bytes, < 4 GiB)
     uint32_t w_bytes;     // extent of one weight matrix (bytes, < 4 GiB)
+    uint32_t y_bytes;     // extent of y from its base (bytes, < 4 GiB)
 };
 
 hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t *perm,
                        hipStream_t stream);
-hipError_t launch_gemm(const GemmArgs &a, bool swiglu, hipStream_t stream);
+// Launches the persistent routed GEMM (one workgroup per CU at most).  With
+// inline_route the kernel builds (and publishes) the segment list itself.
+hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStream_t stream);
 hipError_t launch_norm(const uint16_t *x, uint16_t *residual, const uint16_t *w_und,
                        const uint16_t *w_gen, const uint8_t *modality, float eps,
                        uint16_t *out, float *rstd_out, int64_t T, int H, int32_t *err_word,

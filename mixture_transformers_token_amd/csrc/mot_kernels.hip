@@ -20,12 +20,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mot_internal.h"
 
 namespace mot {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kErrModality = 6;  // MOT_ERR_MODALITY
@@ -160,41 +164,48 @@ plan_kernel(const uint8_t *__restrict__ modality, int T, int32_t *__restrict__ h
 // Workgroup: 256 threads = 4 waves in a 2 (tokens) x 2 (weights) grid.  A
 // tile is BM token rows of ONE weight set (a slice of that set's segment
 // list) by BN weight rows.  Two tile shapes share one launch: 256x256 "big"
-// tiles fill whole rounds of the machine, and 128x128 "small" tiles cover
-// what is left (partial row blocks and the big tiles that would start a
-// mostly idle extra round).  No tile splits K: each output element has one
-// writer and one accumulation order.
+// tiles (two LDS stages of 64 KiB) fill whole rounds of the machine, and
+// 128x128 "small" tiles (four stages of 32 KiB) cover what is left: the
+// partial row blocks of each set and, split in quarters, the big tiles that
+// would open a mostly idle extra round.  No tile splits K: each output
+// element has one writer and one accumulation order.  The kernel is
+// persistent: at most one workgroup per CU walks the tile list in rounds,
+// and every workgroup derives the same list from the pack's set sizes.
 //
-// Pipeline: two LDS stages of 64 k-columns (one 128-byte row piece per
-// operand row, so every direct global->LDS 16-byte buffer load moves whole
-// cache lines).  A stage is consumed in four 16-wide k-steps; each k-step's
-// MFMAs run while the next k-step's fragments are read.  One barrier per
-// stage, placed before its last k-step: there the next stage must have
-// landed, the stage just read is free, and the last k-step's MFMAs cover both
-// the first fragment reads of the next stage and the refill of the freed
-// stage two stages ahead.
+// Pipeline: LDS stages of 64 k-columns (one 128-byte row piece per operand
+// row, so every direct global->LDS 16-byte buffer load moves whole cache
+// lines).  A stage is consumed in four 16-wide k-steps; each k-step's MFMAs
+// run while the next k-step's fragments are read.  One barrier per stage,
+// placed before its last k-step: there the next stage must have landed, the
+// stage just read is free, and the last k-step's MFMAs cover both the first
+// fragment reads of the next stage and the refill of the freed stage NS
+// stages ahead.
 //
 // LDS rows are 128 bytes (64 bf16).  The 16-byte chunk c of staged row r is
 // stored at chunk position c ^ swz(r), swz(r) = ((r >> 1) ^ ((r & 1) << 2)) & 7,
 // which keeps any 8 or 16 consecutive rows read at one k-chunk on distinct
 // LDS banks.
 //
-// Gathered rows: the A-operand row of tile slot i is perm[first + i]; slots
-// past the segment's end load a valid row and are never stored.
+// Gathered rows: the A-operand row of tile slot i is the i-th row of the
+// tile's slice of the segment list; slots past the slice's end load row 0 and
+// are never stored.
 
 constexpr int kBK = 64;          // k per stage
 constexpr int kRowBytes = 128;   // kBK bf16
 constexpr int kThreads = 256;
-constexpr int kBigM = 256, kBigN = 256, kSmallM = 128, kSmallN = 128;
-constexpr int kArrayBytes = kBigM * kRowBytes;  // 32 KiB: one big operand tile or one small stage
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
+constexpr int kBigM = 256, kBigN = 256, kSmallM = 128, kSmallN = 128;
+
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
 struct Tile {
     int set;    // 0 = und, 1 = gen
-    int first;  // offset of the tile's first row in perm
+    int first;  // offset of the tile's first row in the segment list
     int count;  // valid token rows
     int wrow0;  // first weight row of the tile (tile-local W row space)
+    bool big;
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
@@ -206,52 +217,215 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
     return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
 }
 
-// The schedule, computed identically by every workgroup from the plan's
-// counts.  nwt = number of 256-row weight tiles (ceil(weight rows / 256)).
+// The tile list, computed identically by every workgroup from the set sizes:
+// [nkeep big tiles][4*nleft quarter tiles][small tiles of the rows past the
+// big row blocks].  mode 0: big tiles for whole rounds, small for the rest;
+// mode 1: big tiles only; mode 2: small tiles only.
 struct Schedule {
-    int U, G, bu, bg, nbig, nkeep, nleft, su, sg, nsmall;
+    int U, G;
+    int nwt, nws;  // weight tiles of 256 and of 128 rows
+    int bu, nbr;   // big row blocks: und, und + gen
+    int nkeep;     // big tiles run as such
+    int nleft;     // big tiles run as four small tiles each
+    int ru, rg;    // first row (within its set) of the small row blocks
+    int su, sg;    // small row blocks of each set
+    int ntiles;
 };
 
-__device__ __forceinline__ Schedule make_schedule(int U, int G, int nwt, int ncu) {
+__device__ __forceinline__ Schedule make_schedule(int U, int G, int wrows, int grid, int mode) {
     Schedule s;
     s.U = U;
     s.G = G;
-    s.bu = U / kBigM;
-    s.bg = G / kBigM;
-    s.nbig = (s.bu + s.bg) * nwt;
-    s.nkeep = s.nbig >= ncu ? (s.nbig / ncu) * ncu : s.nbig;
-    s.nleft = s.nbig - s.nkeep;
-    s.su = (U - s.bu * kBigM + kSmallM - 1) / kSmallM;
-    s.sg = (G - s.bg * kBigM + kSmallM - 1) / kSmallM;
-    s.nsmall = 4 * s.nleft + (s.su + s.sg) * 2 * nwt;
+    s.nwt = cdiv(wrows, kBigN);
+    s.nws = cdiv(wrows, kSmallN);
+    if (mode == 2) {
+        s.bu = s.nbr = 0;
+    } else if (mode == 1) {
+        s.bu = cdiv(U, kBigM);
+        s.nbr = s.bu + cdiv(G, kBigM);
+    } else {
+        s.bu = U / kBigM;
+        s.nbr = s.bu + G / kBigM;
+    }
+    const int nbig = s.nbr * s.nwt;
+    s.nkeep = (mode == 0 && nbig >= grid) ? (nbig / grid) * grid : nbig;
+    s.nleft = nbig - s.nkeep;
+    s.ru = min(s.bu * kBigM, U);
+    s.rg = min((s.nbr - s.bu) * kBigM, G);
+    s.su = cdiv(U - s.ru, kSmallM);
+    s.sg = cdiv(G - s.rg, kSmallM);
+    s.ntiles = s.nkeep + 4 * s.nleft + (s.su + s.sg) * s.nws;
     return s;
 }
 
-// Big tile b (0 <= b < nbig): 256-row block mb of the concatenated full
-// blocks [und..., gen...], weight tile nb; ordered in groups of 4 row blocks.
-__device__ __forceinline__ void big_tile(const Schedule &s, int b, int nwt, int &mb, int &nb) {
+// Big tile b: 256-row block mb of the concatenated blocks [und..., gen...] by
+// weight tile nb, ordered in groups of 4 row blocks (consecutive tiles share
+// A rows or weight rows).
+__device__ __forceinline__ void big_tile(const Schedule &s, int b, int &mb, int &nb) {
     constexpr int GM = 4;
-    const int nmb = s.bu + s.bg;
-    const int width = GM * nwt;
+    const int width = GM * s.nwt;
     const int g = b / width;
     const int first_m = g * GM;
-    const int gm = min(nmb - first_m, GM);
+    const int gm = min(s.nbr - first_m, GM);
     const int in = b - g * width;
     mb = first_m + in % gm;
     nb = in / gm;
 }
 
-__device__ __forceinline__ void block_rows(const Schedule &s, int mb, int &set, int &first) {
+__device__ __forceinline__ void block_rows(const Schedule &s, int mb, Tile &ti) {
     if (mb < s.bu) {
-        set = 0;
-        first = mb * kBigM;
+        ti.set = 0;
+        ti.first = mb * kBigM;
+        ti.count = min(kBigM, s.U - ti.first);
     } else {
-        set = 1;
-        first = s.U + (mb - s.bu) * kBigM;
+        const int off = (mb - s.bu) * kBigM;
+        ti.set = 1;
+        ti.first = s.U + off;
+        ti.count = min(kBigM, s.G - off);
+    }
+}
+
+__device__ __forceinline__ Tile tile_of(const Schedule &s, int t) {
+    Tile ti;
+    if (t < s.nkeep) {
+        int mb, nb;
+        big_tile(s, t, mb, nb);
+        block_rows(s, mb, ti);
+        ti.wrow0 = nb * kBigN;
+        ti.big = true;
+        return ti;
+    }
+    ti.big = false;
+    const int q = t - s.nkeep;
+    if (q < 4 * s.nleft) {
+        // quarter (q & 3) of a big tile that would have opened an extra round
+        int mb, nb;
+        big_tile(s, s.nkeep + (q >> 2), mb, nb);
+        block_rows(s, mb, ti);
+        const int off = ((q >> 1) & 1) * kSmallM;
+        ti.first += off;
+        ti.count = min(kSmallM, ti.count - off);
+        ti.wrow0 = nb * kBigN + (q & 1) * kSmallN;
+    } else {
+        // 128-row slices of the rows past the big row blocks of each set
+        const int q2 = q - 4 * s.nleft;
+        const int sm = q2 / s.nws, n = q2 % s.nws;
+        if (sm < s.su) {
+            const int r0 = s.ru + sm * kSmallM;
+            ti.set = 0;
+            ti.first = r0;
+            ti.count = min(kSmallM, s.U - r0);
+        } else {
+            const int r0 = s.rg + (sm - s.su) * kSmallM;
+            ti.set = 1;
+            ti.first = s.U + r0;
+            ti.count = min(kSmallM, s.G - r0);
+        }
+        ti.wrow0 = n * kSmallN;
+    }
+    return ti;
+}
+
+// ---- in-kernel segment list ------------------------------------------------
+//
+// For packs of up to kInlineRouteMaxT rows every workgroup reads the modality
+// bytes itself, once: thread i owns rows p*4096 + 16i .. +15 of each pass p
+// and keeps one bit per row (und, gen) in registers.  Per tile, an exclusive
+// scan of the per-thread counts gives the rank of each row among its set's
+// rows (stable partition, ascending row order), and the rows of the tile's
+// slice are written to LDS.  Integer work only.
+
+constexpr int kRouteRows = 16;                     // rows per thread per pass
+constexpr int kRoutePass = kThreads * kRouteRows;  // rows per pass
+constexpr int kRoutePasses = 2;                    // 32 bits per thread and set
+static_assert(kRoutePass * kRoutePasses == kInlineRouteMaxT, "in-kernel segment list size");
+
+// Exclusive scan of v over the workgroup (thread order); total to every thread.
+__device__ __forceinline__ int block_excl_scan(int v, int *s_red, int &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += o;
+    }
+    if (lane == 63) s_red[wave] = inc;
+    __syncthreads();
+    int base = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+        const int t = s_red[w];
+        if (w < wave) base += t;
+        sum += t;
+    }
+    __syncthreads();
+    total = sum;
+    return base + inc - v;
+}
+
+struct RouteBits {
+    uint32_t bits[2];  // [set]: bit 16p + i <=> row p*kRoutePass + 16*tid + i is in the set
+};
+
+// Reads the pack's modality bytes once (all loads issued before any is
+// used); returns true if some byte is neither 0 nor 1.  U = und rows.
+__device__ bool route_count(const uint8_t *__restrict__ mod, int T, int *s_red, int &U, RouteBits &rb) {
+    uint32_t v[kRoutePasses * kRouteRows];
+#pragma unroll
+    for (int p = 0; p < kRoutePasses; ++p)
+#pragma unroll
+        for (int i = 0; i < kRouteRows; ++i) {
+            const int r = p * kRoutePass + (int)threadIdx.x * kRouteRows + i;
+            v[p * kRouteRows + i] = mod[min(r, T - 1)];
+        }
+    uint32_t und = 0, gen = 0, bad = 0;
+#pragma unroll
+    for (int p = 0; p < kRoutePasses; ++p)
+#pragma unroll
+        for (int i = 0; i < kRouteRows; ++i) {
+            const int r = p * kRoutePass + (int)threadIdx.x * kRouteRows + i;
+            const uint32_t m = v[p * kRouteRows + i];
+            if (r < T) {
+                und |= (uint32_t)(m == 0) << (16 * p + i);
+                gen |= (uint32_t)(m == 1) << (16 * p + i);
+                bad |= (m > 1);
+            }
+        }
+    rb.bits[0] = und;
+    rb.bits[1] = gen;
+    int tot;
+    (void)block_excl_scan(__popc(und), s_red, tot);
+    U = tot;
+    return __syncthreads_or((int)bad) != 0;
+}
+
+// s_rows[i] = the row of rank f + i among the pack's rows of `set` (i < count),
+// row 0 for the slots past count.
+__device__ void route_gather(const RouteBits &rb, int set, int f, int count, int bm, int32_t *s_rows,
+                             int *s_red) {
+    for (int i = count + (int)threadIdx.x; i < bm; i += kThreads) s_rows[i] = 0;
+    const uint32_t all = set ? rb.bits[1] : rb.bits[0];
+    int base_rank = 0;
+#pragma unroll
+    for (int p = 0; p < kRoutePasses; ++p) {
+        uint32_t mask = (all >> (16 * p)) & 0xffffu;
+        int tot;
+        int rank = base_rank + block_excl_scan(__popc(mask), s_red, tot);
+        const int r0 = p * kRoutePass + (int)threadIdx.x * kRouteRows;
+        while (mask != 0 && rank < f + count) {
+            const int i = __ffs(mask) - 1;
+            mask &= mask - 1;
+            if (rank >= f) s_rows[rank - f] = r0 + i;
+            ++rank;
+        }
+        base_rank += tot;
     }
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 // Direct global->LDS 16-byte buffer load: lane L's 16 bytes land at
 // lds + 16*L.  The buffer resource covers exactly one operand, so an offset
@@ -277,7 +451,16 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
-// One tile of BM x BN.  The two stage arrays are distinct LDS objects so that
+// Rows per epilogue pass: the largest multiple of 32 that divides the wave's
+// rows and whose padded rows fit one 32 KiB LDS array.
+constexpr int ep_rows(int wm, int rs) {
+    int best = 32;
+    for (int r = 32; r <= wm; r += 32)
+        if (wm % r == 0 && r * rs <= 32768) best = r;
+    return best;
+}
+
+// One tile of BM x BN.  The stage arrays are distinct LDS objects so that
 // the compiler can tell the stage being filled by DMA from the stage being
 // read, and does not make the reads wait for the in-flight loads.
 //
@@ -285,31 +468,33 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // wb[s] (BM and BN rows of 128 bytes).  Every stage issues exactly one
 // refill (re-reading the final k-block when it runs past the end), so the
 // number of DMA instructions in flight is a compile-time constant.
+// s_rows (the tile's A rows) is filled and published by the caller.
 template <int BM, int BN, int NS, bool SWIGLU, bool PRO>
 __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint8_t *const (&xb)[NS],
-                                         uint8_t *const (&wb)[NS], int32_t *s_rows, uint16_t *s_nw) {
+                                         uint8_t *const (&wb)[NS], lds_u8 *const eb,
+                                         const int32_t *s_rows, uint16_t *s_nw, const int tid) {
     constexpr int WM = BM / 2, WN = BN / 2;   // wave tile: tokens x weight rows
     constexpr int MJ = WM / 32, MI = WN / 32; // MFMA blocks per wave
+    constexpr int NM = MI * MJ;               // MFMAs per k-step
     constexpr int XL = BM / 32;               // A-tile DMA instructions per wave per stage
     constexpr int WL = BN / 32;               // W-tile DMA instructions per wave per stage
     constexpr int PER_STAGE = XL + WL;
     static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
     static_assert(!SWIGLU || MI % 2 == 0, "SwiGLU pairs gate and up blocks");
+    static_assert(PER_STAGE * (NS - 1) < 64, "vmcnt range");
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int K = a.K;
     const int nk = K / kBK;
 
-    for (int i = tid; i < BM; i += kThreads)
-        s_rows[i] = min(max(a.perm[ti.first + min(i, ti.count - 1)], 0), (int)a.T - 1);
     if constexpr (PRO) {
         const uint16_t *nw = ti.set ? a.nw_gen : a.nw_und;
         for (int i = tid * 8; i < K; i += kThreads * 8)
             *(uint4 *)(s_nw + i) = *(const uint4 *)(nw + i);
+        __syncthreads();
     }
-    __syncthreads();
 
     const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
     const rsrc_t wr = make_rsrc(ti.set ? a.w_gen : a.w_und, a.w_bytes);
@@ -338,15 +523,20 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
         woff[j] = (uint32_t)wrow * (uint32_t)(K * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
     }
 
-    // DMA of k-block kt into stage slot s.
-    auto issue_all = [&](int kt, int s) {
+    // DMA of k-block kt into stage slot s: instructions [lo, hi) of the
+    // stage's XL A-row and WL W-row instructions.
+    auto issue = [&](int kt, int s, int lo, int hi) {
 #pragma unroll
-        for (int j = 0; j < XL; ++j)
-            dma16(xr, xoff[j], (uint32_t)kt * kRowBytes, xb[s] + (wave * (BM / 4) + j * 8) * kRowBytes);
-#pragma unroll
-        for (int j = 0; j < WL; ++j)
-            dma16(wr, woff[j], (uint32_t)kt * kRowBytes, wb[s] + (wave * (BN / 4) + j * 8) * kRowBytes);
+        for (int j = 0; j < XL + WL; ++j) {
+            if (j < lo || j >= hi) continue;
+            if (j < XL)
+                dma16(xr, xoff[j], (uint32_t)kt * kRowBytes, xb[s] + (wave * (BM / 4) + j * 8) * kRowBytes);
+            else
+                dma16(wr, woff[j - XL], (uint32_t)kt * kRowBytes,
+                      wb[s] + (wave * (BN / 4) + (j - XL) * 8) * kRowBytes);
+        }
     };
+    auto issue_all = [&](int kt, int s) { issue(kt, s, 0, PER_STAGE); };
 
     float rs[MJ];
     if constexpr (PRO) {
@@ -415,25 +605,32 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
     // Issue the next k-step's fragment reads over the first MFMAs of this
     // k-step (one read per MFMA), leaving the rest of the k-step to cover
     // their latency.
-    static_assert(MI * MJ >= MI + MJ, "more MFMAs than reads per k-step");
+    static_assert(NM >= MI + MJ, "more MFMAs than reads per k-step");
     auto interleave_reads = [&]() {
 #pragma unroll
         for (int i = 0; i < MI + MJ; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         }
-        if constexpr (MI * MJ > MI + MJ)
-            __builtin_amdgcn_sched_group_barrier(0x008, MI * MJ - (MI + MJ), 0);
+        if constexpr (NM > MI + MJ)
+            __builtin_amdgcn_sched_group_barrier(0x008, NM - (MI + MJ), 0);
     };
-    // Last k-step of a stage: the next stage's fragment reads as above, and
-    // the refill DMA of the freed stage spread evenly over all the MFMAs.
-    static_assert(PER_STAGE % (MI * MJ) == 0, "DMA per MFMA");
-    auto interleave_reads_dma = [&]() {
+    // The refill of a freed stage is issued in two halves: H instructions
+    // over the last k-step of the stage, the rest over the first k-step of
+    // the next one, each spread evenly over that k-step's MFMAs together with
+    // the fragment reads.
+    constexpr int H = PER_STAGE / 2;
+    auto interleave_reads_dma = [&](auto nd_c) {
+        constexpr int ND = decltype(nd_c)::value;
+        constexpr int DQ = ND / NM, DR = ND % NM;
 #pragma unroll
-        for (int i = 0; i < MI * MJ; ++i) {
+        for (int i = 0; i < NM; ++i) {
             if (i < MI + MJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-            __builtin_amdgcn_sched_group_barrier(0x020, PER_STAGE / (MI * MJ), 0); // VMEM (DMA)
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
+            if (i < DR)
+                __builtin_amdgcn_sched_group_barrier(0x020, DQ + 1, 0);  // VMEM (DMA)
+            else if (DQ > 0)
+                __builtin_amdgcn_sched_group_barrier(0x020, DQ, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         }
     };
 
@@ -443,10 +640,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
     // Once every wave has finished reading slot s it is refilled with k-block
     // kt+NS.  On entry fa0/fb0 hold the fragments of k-step 0 of stage kt.
     auto stage = [&](int kt, int s) {
-        const int nxt = (s + 1) % NS;
+        const int nxt = (s + 1) % NS, prv = (s + NS - 1) % NS;
+        // second half of the refill the previous stage started (slot prv,
+        // k-block kt-1+NS; in the first stage a harmless repeat of the
+        // prologue's load of that slot)
         load_frags(s, kt, 1, fa1, fb1);
+        issue(min(kt - 1 + NS, nk - 1), prv, H, PER_STAGE);
         mfmas(fa0, fb0);
-        interleave_reads();
+        interleave_reads_dma(std::integral_constant<int, PER_STAGE - H>{});
         __builtin_amdgcn_sched_barrier(0);
         load_frags(s, kt, 2, fa0, fb0);
         mfmas(fa1, fb1);
@@ -466,9 +667,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
         // bounds) into a slot nobody reads again, and the first fragments of
         // a stage that does not exist are read from a stale, in-bounds slot.
         load_frags(nxt, min(kt + 1, nk - 1), 0, fa0, fb0);
-        issue_all(min(kt + NS, nk - 1), s);
+        issue(min(kt + NS, nk - 1), s, 0, H);
         mfmas(fa1, fb1);
-        interleave_reads_dma();
+        interleave_reads_dma(std::integral_constant<int, H>{});
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -490,113 +691,163 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
         if (kt + s < nk) stage(kt + s, s);
     wait_vm_lgkm0<0>();  // no DMA may still be writing LDS when the tile ends
 
-    // Epilogue.  Lane holds, for token column m = lane&31 of each block, the
-    // weight rows 8*(e/4) + 4*(lane>>5) + (e&3), e = 0..15.
+    // Epilogue.  Lane holds, for token row m = lane&31 of each block, the
+    // weight rows 8*(e/4) + 4*(lane>>5) + (e&3), e = 0..15: four consecutive
+    // output columns per register quad.  The bf16 results go through a
+    // wave-private LDS region (rows padded by 16 bytes) so that every global
+    // store writes whole 16-byte chunks of contiguous row segments.
+    __syncthreads();  // every wave is done reading the last stage
+    constexpr int OC = SWIGLU ? WN / 2 : WN;  // output columns per wave
+    constexpr int OI = OC / 32;               // output column blocks
+    constexpr int RS = OC * 2 + 16;           // LDS row stride, bytes
+    constexpr int RH = ep_rows(WM, RS);       // rows per pass
+    constexpr int LPR = OC / 8;               // lanes per row (16 bytes each)
+    constexpr int RPI = 64 / LPR;             // rows per store instruction
+    static_assert(RH % 32 == 0 && WM % RH == 0 && 64 % LPR == 0 && RH % RPI == 0, "epilogue");
+    const int col0 = SWIGLU ? ti.wrow0 / 2 + wn * (BN / 4) : ti.wrow0 + wn * WN;
+    // one LDS base per lane for the writes and one for the read-back; the
+    // rest are immediate offsets
+    lds_u8 *const wp = eb + rsel * RS + khalf * 8;
+    lds_u8 *const rp = eb + (lane / LPR) * RS + (lane % LPR) * 16;
+    const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+    const uint32_t ldy_bytes = (uint32_t)a.ldy * 2u;
+    const int col = col0 + (lane % LPR) * 8;
+    const bool col_ok = col < a.N;
 #pragma unroll
-    for (int j = 0; j < MJ; ++j) {
-        const int mloc = wm * WM + j * 32 + rsel;
-        if (mloc >= ti.count) continue;
-        const int64_t t = s_rows[mloc];
-        uint16_t *yrow = a.y + t * a.ldy;
-        if constexpr (SWIGLU) {
+    for (int jp = 0; jp < MJ; jp += RH / 32) {
 #pragma unroll
-            for (int i = 0; i < MI / 2; ++i) {
-                const int c0 = ti.wrow0 / 2 + wn * (BN / 4) + i * 32;
-                if (c0 >= a.N) continue;
+        for (int jj = 0; jj < RH / 32; ++jj) {
+            const int j = jp + jj;
+#pragma unroll
+            for (int i = 0; i < OI; ++i) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float g = acc[i][j][4 * q + e];
-                        const float u = acc[i + MI / 2][j][4 * q + e];
-                        v[e] = (g / (1.0f + expf(-g))) * u;
+                        if constexpr (SWIGLU) {
+                            const float g = acc[i][j][4 * q + e];
+                            const float u = acc[i + MI / 2][j][4 * q + e];
+                            v[e] = (g / (1.0f + expf(-g))) * u;
+                        } else {
+                            v[e] = acc[i][j][4 * q + e];
+                        }
                     }
-                    const uint2 pk = {pack2(v[0], v[1]), pack2(v[2], v[3])};
-                    *(uint2 *)(yrow + c0 + q * 8 + khalf * 4) = pk;
+                    const u32x2_t pk = {pack2(v[0], v[1]), pack2(v[2], v[3])};
+                    *(lds_u32x2 *)(wp + jj * 32 * RS + (i * 32 + q * 8) * 2) = pk;
                 }
             }
-        } else {
+        }
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int n0 = ti.wrow0 + wn * WN + i * 32;
-                if (n0 >= a.N) continue;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint2 pk = {pack2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]),
-                                      pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-                    *(uint2 *)(yrow + n0 + q * 8 + khalf * 4) = pk;
-                }
-            }
+        for (int r = 0; r < RH; r += RPI) {
+            const u32x4_t v = *(const lds_u32x4 *)(rp + r * RS);
+            const int mloc = wm * WM + jp * 32 + r + lane / LPR;
+            if (col_ok && mloc < ti.count)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    v, yr,
+                    (uint32_t)s_rows[mloc] * ldy_bytes + (uint32_t)col * 2u, 0, 0);
         }
     }
 }
 
-// nwt: number of 256-row weight tiles; ncu: compute units of the device.
-template <bool SWIGLU, bool PRO>
-__global__ void __launch_bounds__(kThreads)
-gemm_kernel(GemmArgs a, int nwt, int ncu) {
-    // four 32 KiB LDS arrays: big tiles use two stages of (A in one array,
-    // W in the next), small tiles four stages of one array each
+// INLINE: the workgroups build the segment list from the modality bytes
+// (and publish it to the workspace); otherwise they read the plan that
+// plan_kernel wrote.
+template <bool SWIGLU, bool PRO, bool INLINE>
+__global__ void __launch_bounds__(kThreads, 1)
+gemm_kernel(GemmArgs a) {
+    // four 32 KiB LDS arrays: big tiles use two stages of (A in array 0 or
+    // 2, W in array 1 or 3), small tiles four stages of one array each
+    constexpr int kArrayBytes = kBigM * kRowBytes;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kArrayBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kArrayBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds2[kArrayBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds3[kArrayBytes];
     __shared__ int32_t s_rows[kBigM];
+    __shared__ int s_red[kThreads / 64];
     __shared__ __attribute__((aligned(16))) uint16_t s_nw[PRO ? kMaxPrologueK : 8];
 
-    const int32_t *hdr = a.hdr;
-    const int U = hdr[1], G = hdr[2];
-    // a plan that does not describe exactly T rows (error, or a stale plan
-    // passed with MOT_FLAG_PLAN_READY) makes every tile exit
-    if (hdr[0] != 0 || hdr[3] != (int)a.T || U < 0 || G < 0 || U + G != (int)a.T) return;
-    const Schedule s = make_schedule(U, G, nwt, ncu);
-    const int bid = blockIdx.x;
-    Tile ti;
-    if (bid < s.nkeep) {
-        int mb, nb;
-        big_tile(s, xcd_remap(bid, s.nkeep), nwt, mb, nb);
-        block_rows(s, mb, ti.set, ti.first);
-        ti.count = kBigM;
-        ti.wrow0 = nb * kBigN;
-        uint8_t *const xb[2] = {lds0, lds2}, *const wb[2] = {lds1, lds3};
-        run_tile<kBigM, kBigN, 2, SWIGLU, PRO>(a, ti, xb, wb, s_rows, s_nw);
-        return;
-    }
-    const int sid = bid - s.nkeep;
-    if (sid >= s.nsmall) return;
-    const int q = xcd_remap(sid, s.nsmall);
-    if (q < 4 * s.nleft) {
-        // quarter (q & 3) of a big tile that would have opened an extra round
-        int mb, nb;
-        big_tile(s, s.nkeep + (q >> 2), nwt, mb, nb);
-        block_rows(s, mb, ti.set, ti.first);
-        ti.first += ((q >> 1) & 1) * kSmallM;
-        ti.count = kSmallM;
-        ti.wrow0 = nb * kBigN + (q & 1) * kSmallN;
-    } else {
-        // 128-row slices of the partial row blocks of each set
-        const int nws = 2 * nwt;
-        const int q2 = q - 4 * s.nleft;
-        const int sm = q2 / nws, n = q2 % nws;
-        if (sm < s.su) {
-            const int r0 = s.bu * kBigM + sm * kSmallM;
-            ti.set = 0;
-            ti.first = r0;
-            ti.count = min(kSmallM, U - r0);
-        } else {
-            const int r0 = s.bg * kBigM + (sm - s.su) * kSmallM;
-            ti.set = 1;
-            ti.first = U + r0;
-            ti.count = min(kSmallM, G - r0);
+    const int T = (int)a.T;
+    int U, G;
+    RouteBits rb;
+    if constexpr (INLINE) {
+        const bool bad = route_count(a.modality, T, s_red, U, rb);
+        // the count is the same in every lane (an LDS reduction); say so, so
+        // that everything derived from it (tile, weight set, buffer
+        // resources) stays in scalar registers
+        U = __builtin_amdgcn_readfirstlane(U);
+        G = T - U;
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            a.hdr_out[0] = bad ? kErrModality : 0;
+            a.hdr_out[1] = bad ? 0 : U;
+            a.hdr_out[2] = bad ? 0 : G;
+            a.hdr_out[3] = T;
         }
-        ti.wrow0 = n * kSmallN;
+        if (bad) return;  // the pack holds an invalid byte: write nothing
+    } else {
+        const int32_t *hdr = a.hdr;
+        U = hdr[1];
+        G = hdr[2];
+        // a plan that does not describe exactly T rows (error, or a stale plan
+        // passed with MOT_FLAG_PLAN_READY) makes every workgroup exit
+        if (hdr[0] != 0 || hdr[3] != T || U < 0 || G < 0 || U + G != T) return;
     }
-    if (ti.count <= 0) return;
-    constexpr int kHalf = kSmallM * kRowBytes;
-    uint8_t *const xb[4] = {lds0, lds1, lds2, lds3};
-    uint8_t *const wb[4] = {lds0 + kHalf, lds1 + kHalf, lds2 + kHalf, lds3 + kHalf};
-    run_tile<kSmallM, kSmallN, 4, SWIGLU, PRO>(a, ti, xb, wb, s_rows, s_nw);
+    // per-wave epilogue staging: array `wave` of the four
+    const int wave_id = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    lds_u8 *const eb = (lds_u8 *)(wave_id == 0 ? lds0 : wave_id == 1 ? lds1 : wave_id == 2 ? lds2 : lds3);
+    const int grid = (int)gridDim.x;
+    const Schedule sc = make_schedule(U, G, a.wrows, grid, a.tile_mode);
+    // Static assignment.  Big tiles go round-robin (whole rounds, or one
+    // partial round); small tiles (about a quarter of a big tile's work each)
+    // go first to the workgroups that hold no big tile, up to four each, then
+    // round-robin over all workgroups.
+    const int w = xcd_remap((int)blockIdx.x, grid);
+    const int nsm = sc.ntiles - sc.nkeep;
+    const int idle = sc.nkeep < grid ? grid - sc.nkeep : 0;
+    const int cap = min(nsm, 4 * idle);
+    const int n_big = w < sc.nkeep ? cdiv(sc.nkeep - w, grid) : 0;
+    const int n_idle = (idle > 0 && w >= sc.nkeep && w - sc.nkeep < cap) ? cdiv(cap - (w - sc.nkeep), idle) : 0;
+    const int n_rr = cap + w < nsm ? cdiv(nsm - cap - w, grid) : 0;
+    for (int it = 0; it < n_big + n_idle + n_rr; ++it) {
+        int t;
+        if (it < n_big)
+            t = w + it * grid;
+        else if (it < n_big + n_idle)
+            t = sc.nkeep + (w - sc.nkeep) + (it - n_big) * idle;
+        else
+            t = sc.nkeep + cap + w + (it - n_big - n_idle) * grid;
+        const Tile ti = tile_of(sc, t);
+        if (ti.count <= 0 || ti.wrow0 >= a.wrows) continue;  // uniform: nothing to compute
+        const int bm = ti.big ? kBigM : kSmallM;
+        // The thread index, made opaque per tile: per-lane offsets are then
+        // recomputed in each tile instead of being hoisted out of this loop
+        // and spilled (a spill reload waits on vmcnt, i.e. on in-flight DMA).
+        int tid = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        __syncthreads();  // every wave is done with the previous tile's LDS
+        if constexpr (INLINE) {
+            route_gather(rb, ti.set, ti.first - (ti.set ? U : 0), ti.count, bm, s_rows, s_red);
+        } else {
+            for (int i = threadIdx.x; i < bm; i += kThreads)
+                s_rows[i] = i < ti.count ? min(max(a.perm[ti.first + i], 0), T - 1) : 0;
+        }
+        __syncthreads();
+        if constexpr (INLINE) {
+            // the tiles of weight rows [0, ...) cover every row once: they
+            // publish the segment list
+            if (ti.wrow0 == 0)
+                for (int i = threadIdx.x; i < ti.count; i += kThreads) a.perm_out[ti.first + i] = s_rows[i];
+        }
+        if (ti.big) {
+            uint8_t *const xb[2] = {lds0, lds2}, *const wb[2] = {lds1, lds3};
+            run_tile<kBigM, kBigN, 2, SWIGLU, PRO>(a, ti, xb, wb, eb, s_rows, s_nw, tid);
+        } else {
+            constexpr int kHalf = kSmallM * kRowBytes;
+            uint8_t *const xb[4] = {lds0, lds1, lds2, lds3};
+            uint8_t *const wb[4] = {lds0 + kHalf, lds1 + kHalf, lds2 + kHalf, lds3 + kHalf};
+            run_tile<kSmallM, kSmallN, 4, SWIGLU, PRO>(a, ti, xb, wb, eb, s_rows, s_nw, tid);
+        }
+    }
 }
 
 // ============================================================================
@@ -714,30 +965,42 @@ hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t
 }
 
 namespace {
-template <bool SWIGLU>
-hipError_t launch_gemm_t(const GemmArgs &a, int ncu, hipStream_t stream) {
-    const int wrows = SWIGLU ? 2 * a.N : a.N;
-    const int nwt = (wrows + kBigN - 1) / kBigN;
-    // upper bound of the schedule's tile count for any split of T rows
-    const int64_t nbig_max = (a.T / kBigM) * (int64_t)nwt;
-    const int64_t nsmall_max = 4 * (int64_t)ncu + 4 * 2 * (int64_t)nwt;
-    const dim3 grid((unsigned)(nbig_max + nsmall_max));
-    if (a.rstd != nullptr)
-        hipLaunchKernelGGL((gemm_kernel<SWIGLU, true>), grid, dim3(kThreads), 0, stream, a, nwt, ncu);
+template <bool SWIGLU, bool PRO>
+hipError_t launch_gemm_t(const GemmArgs &a, bool inline_route, int grid, hipStream_t stream) {
+    if (inline_route)
+        hipLaunchKernelGGL((gemm_kernel<SWIGLU, PRO, true>), dim3(grid), dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL((gemm_kernel<SWIGLU, false>), grid, dim3(kThreads), 0, stream, a, nwt, ncu);
+        hipLaunchKernelGGL((gemm_kernel<SWIGLU, PRO, false>), dim3(grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs &a, bool swiglu, hipStream_t stream) {
+// Upper bound of the tile list's length for any split of T rows into the two
+// sets (at most one workgroup per CU is launched; a shorter list leaves the
+// rest of the grid idle).
+int64_t gemm_tile_bound(int64_t T, int64_t wrows, int ncu) {
+    const int64_t nwt = (wrows + kBigN - 1) / kBigN, nws = (wrows + kSmallN - 1) / kSmallN;
+    const int64_t small_only = ((T + kSmallM - 1) / kSmallM + 1) * nws;
+    const int64_t big_first = (T / kBigM) * nwt + 4 * (int64_t)ncu + 4 * nws;
+    return small_only > big_first ? small_only : big_first;
+}
+
+hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStream_t stream) {
     int dev = 0, ncu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     if (ncu <= 0) ncu = 1;
-    return swiglu ? launch_gemm_t<true>(a, ncu, stream) : launch_gemm_t<false>(a, ncu, stream);
+    const bool pro = a.rstd != nullptr;
+    const int64_t bound = gemm_tile_bound(a.T, a.wrows, ncu);
+    const int grid = (int)(bound < ncu ? bound : ncu);
+    if (grid <= 0) return hipSuccess;
+    if (swiglu)
+        return pro ? launch_gemm_t<true, true>(a, inline_route, grid, stream)
+                   : launch_gemm_t<true, false>(a, inline_route, grid, stream);
+    return pro ? launch_gemm_t<false, true>(a, inline_route, grid, stream)
+               : launch_gemm_t<false, false>(a, inline_route, grid, stream);
 }
 
 hipError_t launch_norm(const uint16_t *x, uint16_t *residual, const uint16_t *w_und,

@@ -87,6 +87,8 @@ def _gemm(**kw):
     (dict(rstd=7 * A), INVALID),              # prologue pointers all or none
     (dict(rstd=7 * A, nwu=8 * A), INVALID),
     (dict(flags=4), INVALID),
+    (dict(flags=0x30), INVALID),              # two tile shapes at once
+    (dict(flags=0x40), INVALID),
     (dict(y=A + 1024), INVALID),              # y overlaps x
     (dict(y=2 * A), INVALID),                 # y overlaps a weight set
     (dict(K=(1 << 20) + 64, ldx=(1 << 20) + 64), SHAPE),

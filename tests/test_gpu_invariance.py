@@ -92,6 +92,16 @@ def test_repeatable_and_strided_output(qkv_setup):
     assert raw_equal(big[:, 32:32 + N].contiguous(), s["ref"])
 
 
+@pytest.mark.parametrize("tile", ["256x256", "128x128"])
+def test_tile_shape_does_not_change_bytes(qkv_setup, tile):
+    """Every tile shape runs the same per-element k order: forcing one shape
+    gives the bytes of the library's own choice."""
+    s = qkv_setup
+    md = dev(torch.from_numpy(s["probe_m"]))
+    y = mot.routed_gemm(dev(s["x_probe"]), s["wu"], s["wg"], md, tile=tile)
+    assert raw_equal(y, s["ref"])
+
+
 def test_mixed_equals_per_set_dense(qkv_setup):
     """Mixed pack == each set's rows run as a single-set pack (gathered)."""
     s = qkv_setup

@@ -19,7 +19,7 @@ from helpers import bits, check_parity, dev
 pytestmark = pytest.mark.gpu
 
 
-def _gemm_parity(x, wu, wg, m, rows=None, ldx_pad=0, ldy_pad=0):
+def _gemm_parity(x, wu, wg, m, rows=None, ldx_pad=0, ldy_pad=0, tile=None):
     T, K = x.shape
     N = wu.shape[0]
     if ldx_pad:
@@ -32,7 +32,7 @@ def _gemm_parity(x, wu, wg, m, rows=None, ldx_pad=0, ldy_pad=0):
     if ldy_pad:
         ybig = torch.full((T, N + ldy_pad), 7.0, dtype=torch.bfloat16, device="cuda")
         out = ybig[:, :N]
-    y = mot.routed_gemm(xd, dev(wu), dev(wg), dev(torch.from_numpy(m)), out=out)
+    y = mot.routed_gemm(xd, dev(wu), dev(wg), dev(torch.from_numpy(m)), out=out, tile=tile)
     torch.cuda.synchronize()
     if ldy_pad:
         assert torch.all(ybig[:, N:] == 7.0), "wrote outside columns [0, N)"
@@ -46,12 +46,25 @@ def test_tiny():
     _gemm_parity(x, wu, wg, m)
 
 
-@pytest.mark.parametrize("T", [1, 2, 31, 33, 255, 257, 513, 1025])
+@pytest.mark.parametrize("T", [1, 2, 31, 33, 255, 257, 513, 1025, 8192, 8193, 9001])
 def test_ragged_packs(T):
+    """Ragged set sizes; T > 8192 takes the plan-kernel route, T <= 8192 the
+    in-kernel segment list."""
     m = W.pattern(T)
     m[::7] = 1 - m[::7]  # break runs
     x, wu, wg, _ = W.gemm_case(T, 256, 320, m, base=T)
     _gemm_parity(x, wu, wg, m)
+
+
+@pytest.mark.parametrize("tile", ["256x256", "128x128"])
+@pytest.mark.parametrize("T", [1, 300, 1101])
+def test_forced_tile_shapes(T, tile):
+    """Each tile shape alone (big tiles with ragged row blocks, small tiles
+    everywhere) against the oracle."""
+    m = W.pattern(T)
+    m[::5] = 1 - m[::5]
+    x, wu, wg, _ = W.gemm_case(T, 320, 576, m, base=40 + T)
+    _gemm_parity(x, wu, wg, m, tile=tile)
 
 
 @pytest.mark.parametrize("which", [0, 1])
@@ -87,23 +100,24 @@ def test_empty_pack_is_noop():
 
 # ---- SwiGLU ----------------------------------------------------------------
 
-def _swiglu_parity(x, wu, wg, m, rows=None):
+def _swiglu_parity(x, wu, wg, m, rows=None, tile=None):
     T, K = x.shape
     F = wu.shape[0] // 2
-    act = mot.routed_gemm_swiglu(dev(x), dev(wu), dev(wg), dev(torch.from_numpy(m)))
+    act = mot.routed_gemm_swiglu(dev(x), dev(wu), dev(wg), dev(torch.from_numpy(m)), tile=tile)
     torch.cuda.synchronize()
     sel = np.arange(T) if rows is None else rows
     ref, rne = oracle.routed_gemm_swiglu(W.bits(x)[sel], W.bits(wu), W.bits(wg), m[sel])
     return check_parity(bits(act)[sel], ref, rne, f"swiglu T={T} K={K} F={F}")
 
 
-@pytest.mark.parametrize("T,K,F", [(64, 256, 192), (333, 128, 64), (1, 64, 128)])
-def test_swiglu_small(T, K, F):
+@pytest.mark.parametrize("T,K,F,tile", [(64, 256, 192, None), (333, 128, 64, None), (1, 64, 128, None),
+                                        (600, 192, 320, "256x256"), (600, 192, 320, "128x128")])
+def test_swiglu_small(T, K, F, tile):
     m = W.pattern(T)
     x = W.normal_bf16((T, K), 40 + T)
     wu = W.normal_bf16((2 * F, K), 41, 0.05)
     wg = W.normal_bf16((2 * F, K), 42, 0.05)
-    _swiglu_parity(x, wu, wg, m)
+    _swiglu_parity(x, wu, wg, m, tile=tile)
 
 
 def test_mlp_full_size_sampled():
@@ -170,6 +184,20 @@ def test_routing_plan_bit_exact(T):
     assert np.array_equal(perm, want_perm)
 
 
+@pytest.mark.parametrize("T", [1, 77, 1101, 4096, 8192])
+def test_gemm_publishes_the_plan(T):
+    """The in-kernel segment list (packs of up to 8192 rows) leaves the same
+    header and perm in the workspace as the routing plan, bit for bit."""
+    m = np.random.default_rng(T).integers(0, 2, T).astype(np.uint8) if T % 2 else W.pattern(T)
+    x, wu, wg, _ = W.gemm_case(T, 64, 128, m, base=80)
+    ws = torch.full((mot.workspace_bytes(T),), 0xAB, dtype=torch.uint8, device="cuda")
+    mot.routed_gemm(dev(x), dev(wu), dev(wg), dev(torch.from_numpy(m)), workspace=ws)
+    hdr, perm = mot.plan_view(ws, T)
+    want_perm, nu, ng = oracle.routing_plan(m)
+    assert list(hdr.cpu().numpy()) == [0, nu, ng, T]
+    assert np.array_equal(perm.cpu().numpy(), want_perm)
+
+
 def test_bad_modality_sets_error_and_writes_nothing():
     T, K, N = 100, 128, 128
     m = W.pattern(T)
@@ -193,3 +221,13 @@ def test_bad_modality_sets_error_and_writes_nothing():
                           workspace=ws)
     assert mot.read_device_error(ws) == 6
     assert torch.all(out[57] == 3.0) and not torch.all(out[56] == 3.0)
+    # a pack above the in-kernel segment-list limit takes the plan kernel
+    T2 = 9000
+    m2 = W.pattern(T2)
+    m2[8999] = 2
+    x2, wu2, wg2, _ = W.gemm_case(T2, 64, 64, np.zeros(T2, np.uint8), base=62)
+    ws2 = mot.new_workspace(T2, "cuda")
+    y2 = torch.full((T2, 64), 5.0, dtype=torch.bfloat16, device="cuda")
+    mot.routed_gemm(dev(x2), dev(wu2), dev(wg2), dev(torch.from_numpy(m2)), out=y2, workspace=ws2)
+    assert mot.read_device_error(ws2) == 6
+    assert torch.all(y2 == 5.0)
