@@ -393,10 +393,12 @@ __device__ bool route_count(const uint8_t *__restrict__ mod, int T, int *s_red, 
         }
     rb.bits[0] = und;
     rb.bits[1] = gen;
+    // und count (at most kInlineRouteMaxT < 2^20) and bad-byte flags in one
+    // scan; no other LDS is used (the GEMM's stage arrays fill the LDS)
     int tot;
-    (void)block_excl_scan(__popc(und), s_red, tot);
-    U = tot;
-    return __syncthreads_or((int)bad) != 0;
+    (void)block_excl_scan(__popc(und) | ((int)bad << 20), s_red, tot);
+    U = tot & 0xfffff;
+    return (tot >> 20) != 0;
 }
 
 // s_rows[i] = the row of rank f + i among the pack's rows of `set` (i < count),
@@ -458,6 +460,77 @@ constexpr int ep_rows(int wm, int rs) {
     for (int r = 32; r <= wm; r += 32)
         if (wm % r == 0 && r * rs <= 32768) best = r;
     return best;
+}
+
+// Cache policy of the staged (full-row-segment) output stores: system scope
+// (written through, no dirty lines left in L2 at the end of the kernel);
+// measured faster than the default for the end-of-tile store burst.
+constexpr int kStoreAux = 0x11;
+
+// Staged epilogue of one wave's WM x WN accumulator block.  Lane holds, for
+// token row m = lane&31 of each 32x32 block, the weight rows
+// 8*(e/4) + 4*(lane>>5) + (e&3), e = 0..15: four consecutive output columns
+// per register quad.  The bf16 results (SwiGLU: act of each gate/up pair) go
+// through a wave-private LDS region (rows padded by 16 bytes) so that every
+// global store writes whole 16-byte chunks of contiguous row segments.  The
+// caller has synchronised the workgroup after the main loop.
+template <int WM, int WN, int MI, int MJ, bool SWIGLU>
+__device__ __forceinline__ void epilogue_staged(const GemmArgs &a, const Tile &ti, f32x16_t (&acc)[MI][MJ],
+                                                lds_u8 *const eb, const int32_t *s_rows, int lane, int wm,
+                                                int wn) {
+    constexpr int BN = 2 * WN;
+    const int rsel = lane & 31, khalf = lane >> 5;
+    constexpr int OC = SWIGLU ? WN / 2 : WN;  // output columns per wave
+    constexpr int OI = OC / 32;               // output column blocks
+    constexpr int RS = OC * 2 + 16;           // LDS row stride, bytes
+    constexpr int RH = ep_rows(WM, RS);       // rows per pass
+    constexpr int LPR = OC / 8;               // lanes per row (16 bytes each)
+    constexpr int RPI = 64 / LPR;             // rows per store instruction
+    static_assert(RH % 32 == 0 && WM % RH == 0 && 64 % LPR == 0 && RH % RPI == 0, "epilogue");
+    const int col0 = SWIGLU ? ti.wrow0 / 2 + wn * (BN / 4) : ti.wrow0 + wn * WN;
+    // one LDS base per lane for the writes and one for the read-back; the
+    // rest are immediate offsets
+    lds_u8 *const wp = eb + rsel * RS + khalf * 8;
+    lds_u8 *const rp = eb + (lane / LPR) * RS + (lane % LPR) * 16;
+    const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+    const uint32_t ldy_bytes = (uint32_t)a.ldy * 2u;
+    const int col = col0 + (lane % LPR) * 8;
+    const bool col_ok = col < a.N;
+#pragma unroll
+    for (int jp = 0; jp < MJ; jp += RH / 32) {
+#pragma unroll
+        for (int jj = 0; jj < RH / 32; ++jj) {
+            const int j = jp + jj;
+#pragma unroll
+            for (int i = 0; i < OI; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (SWIGLU) {
+                            const float g = acc[i][j][4 * q + e];
+                            const float u = acc[i + MI / 2][j][4 * q + e];
+                            v[e] = (g / (1.0f + expf(-g))) * u;
+                        } else {
+                            v[e] = acc[i][j][4 * q + e];
+                        }
+                    }
+                    const u32x2_t pk = {pack2(v[0], v[1]), pack2(v[2], v[3])};
+                    *(lds_u32x2 *)(wp + jj * 32 * RS + (i * 32 + q * 8) * 2) = pk;
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RH; r += RPI) {
+            const u32x4_t v = *(const lds_u32x4 *)(rp + r * RS);
+            const int mloc = wm * WM + jp * 32 + r + lane / LPR;
+            if (col_ok && mloc < ti.count)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    v, yr,
+                    (uint32_t)s_rows[mloc] * ldy_bytes + (uint32_t)col * 2u, 0, kStoreAux);
+        }
+    }
 }
 
 // One tile of BM x BN.  The stage arrays are distinct LDS objects so that
@@ -691,35 +764,212 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
         if (kt + s < nk) stage(kt + s, s);
     wait_vm_lgkm0<0>();  // no DMA may still be writing LDS when the tile ends
 
-    // Epilogue.  Lane holds, for token row m = lane&31 of each block, the
-    // weight rows 8*(e/4) + 4*(lane>>5) + (e&3), e = 0..15: four consecutive
-    // output columns per register quad.  The bf16 results go through a
-    // wave-private LDS region (rows padded by 16 bytes) so that every global
-    // store writes whole 16-byte chunks of contiguous row segments.
+    // Epilogue.
     __syncthreads();  // every wave is done reading the last stage
-    constexpr int OC = SWIGLU ? WN / 2 : WN;  // output columns per wave
-    constexpr int OI = OC / 32;               // output column blocks
-    constexpr int RS = OC * 2 + 16;           // LDS row stride, bytes
-    constexpr int RH = ep_rows(WM, RS);       // rows per pass
-    constexpr int LPR = OC / 8;               // lanes per row (16 bytes each)
-    constexpr int RPI = 64 / LPR;             // rows per store instruction
-    static_assert(RH % 32 == 0 && WM % RH == 0 && 64 % LPR == 0 && RH % RPI == 0, "epilogue");
-    const int col0 = SWIGLU ? ti.wrow0 / 2 + wn * (BN / 4) : ti.wrow0 + wn * WN;
-    // one LDS base per lane for the writes and one for the read-back; the
-    // rest are immediate offsets
-    lds_u8 *const wp = eb + rsel * RS + khalf * 8;
-    lds_u8 *const rp = eb + (lane / LPR) * RS + (lane % LPR) * 16;
-    const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
-    const uint32_t ldy_bytes = (uint32_t)a.ldy * 2u;
-    const int col = col0 + (lane % LPR) * 8;
-    const bool col_ok = col < a.N;
+    epilogue_staged<WM, WN, MI, MJ, SWIGLU>(a, ti, acc, eb, s_rows, lane, wm, wn);
+}
+
+// Big tile (256 x 256) without the prologue, on a ring of five 32 KiB LDS
+// slots (all of the LDS).  Each slot holds one operand of one stage (256 rows
+// of a 64-wide k-block): the A rows of stage j sit in slot (2j) % 5 and its
+// W rows in slot (2j+1) % 5.  Once stage j has been read, its two slots take
+// the W rows of stage j+2 and the A rows of stage j+3, so the A rows are
+// requested about five k-steps and the W rows about two and a half k-steps
+// before they are read, and the refill is spread evenly: four DMA
+// instructions per wave in every k-step.
+//   k-step 0: second half of W(j+1)    k-step 1: first half of A(j+2)
+//   k-step 2: second half of A(j+2)    barrier
+//   k-step 3: first half of W(j+2)
+// At the barrier of stage j, A(j+1) and W(j+1) must have landed; only the
+// eight instructions of A(j+2) may still be in flight.
+// The row list lives in slot 4 until the prologue's barrier: each lane
+// takes its DMA offsets and the byte offsets of its four output rows from
+// it first.  The epilogue stores straight from the accumulators (8-byte
+// pieces, default cache policy); measured faster here than staging through
+// LDS, which would need the row list rebuilt.
+template <bool SWIGLU>
+__device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint8_t *const (&hs)[5],
+                                         const int32_t *s_rows, const int tid) {
+    constexpr int BM = kBigM, BN = kBigN;
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int MJ = WM / 32, MI = WN / 32;
+    constexpr int NM = MI * MJ;
+    constexpr int XL = BM / 32, WL = BN / 32;  // DMA instructions per wave per operand and stage
+    constexpr int HX = XL / 2, HW = WL / 2;
+    static_assert(XL == 8 && WL == 8 && NM == 16, "big tile");
+
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int K = a.K;
+    const int nk = K / kBK;
+
+    const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+    const rsrc_t wr = make_rsrc(ti.set ? a.w_gen : a.w_und, a.w_bytes);
+
+    uint32_t xoff[XL], woff[WL];
 #pragma unroll
-    for (int jp = 0; jp < MJ; jp += RH / 32) {
+    for (int j = 0; j < XL; ++j) {
+        const int r = wave * (BM / 4) + j * 8 + (lane >> 3);
+        xoff[j] = (uint32_t)s_rows[r] * (uint32_t)(a.ldx * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+    }
 #pragma unroll
-        for (int jj = 0; jj < RH / 32; ++jj) {
-            const int j = jp + jj;
+    for (int j = 0; j < WL; ++j) {
+        const int r = wave * (BN / 4) + j * 8 + (lane >> 3);
+        int wrow;
+        if constexpr (SWIGLU) {
+            const int half = r / (BN / 2), q = r % (BN / 2);
+            int col = ti.wrow0 / 2 + half * (BN / 4) + (q % (BN / 4));
+            col = min(col, a.N - 1);
+            wrow = (q < BN / 4) ? col : a.N + col;
+        } else {
+            wrow = min(ti.wrow0 + r, a.N - 1);
+        }
+        woff[j] = (uint32_t)wrow * (uint32_t)(K * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+    }
+    // byte offsets of this lane's four output rows, -1 past the tile's rows
+    const int rsel = lane & 31;
+    const int khalf = lane >> 5;
+    int32_t yoff[MJ];
+    {
+#pragma unroll
+        for (int j = 0; j < MJ; ++j) {
+            const int mloc = wm * WM + j * 32 + rsel;
+            yoff[j] = mloc < ti.count ? (int32_t)((uint32_t)s_rows[mloc] * (uint32_t)a.ldy * 2u) : -1;
+        }
+    }
+
+    // operand o (0 = A, 1 = W) of k-block kb into slot s, instructions [lo, hi)
+    auto issue = [&](int o, int kb, int s, int lo, int hi) {
+#pragma unroll
+        for (int j = 0; j < XL; ++j) {
+            if (j < lo || j >= hi) continue;
+            if (o == 0)
+                dma16(xr, xoff[j], (uint32_t)kb * kRowBytes, hs[s] + (wave * (BM / 4) + j * 8) * kRowBytes);
+            else
+                dma16(wr, woff[j], (uint32_t)kb * kRowBytes, hs[s] + (wave * (BN / 4) + j * 8) * kRowBytes);
+        }
+    };
+
+    f32x16_t acc[MI][MJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < MJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    const int lsw = swz(lane & 15);
+    uint32_t xq[4], wq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t pos = (uint32_t)(((2 * q + khalf) ^ lsw) * 16);
+        xq[q] = (uint32_t)((wm * WM + rsel) * kRowBytes) + pos;
+        wq[q] = (uint32_t)((wn * WN + rsel) * kRowBytes) + pos;
+    }
+    // fragments of k-step q of the stage whose A rows are in slot sa and W rows in sw
+    auto load_frags = [&](int sa, int sw, int q, bf16x8_t (&fa)[MI], bf16x8_t (&fb)[MJ]) {
+        const uint8_t *xs = hs[sa], *ws = hs[sw];
+        fa[0] = *(const bf16x8_t *)(ws + wq[q]);
+#pragma unroll
+        for (int j = 0; j < MJ; ++j) fb[j] = *(const bf16x8_t *)(xs + xq[q] + j * 32 * kRowBytes);
+#pragma unroll
+        for (int i = 1; i < MI; ++i) fa[i] = *(const bf16x8_t *)(ws + wq[q] + i * 32 * kRowBytes);
+    };
+    auto mfmas = [&](const bf16x8_t (&fa)[MI], const bf16x8_t (&fb)[MJ]) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < MJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+    // one k-step: the next fragment reads over the first MFMAs, four DMA
+    // instructions spread over all of them
+    auto interleave = [&]() {
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            if (i < MI + MJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            if (i % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (DMA)
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+        }
+    };
+
+    bf16x8_t fa0[MI], fb0[MJ], fa1[MI], fb1[MJ];
+
+    // Stage kt with jm = kt % 5 (a compile-time slot pattern).  On entry
+    // fa0/fb0 hold the fragments of its k-step 0.
+    auto stage = [&](auto jm_c, int kt) {
+        constexpr int jm = decltype(jm_c)::value;
+        constexpr int sa = (2 * jm) % 5, sw = (2 * jm + 1) % 5;            // this stage
+        constexpr int na = (2 * jm + 2) % 5, nw = (2 * jm + 3) % 5;        // next stage
+        constexpr int a2 = (2 * jm + 4) % 5, w2 = (2 * jm + 5) % 5;        // A(j+2), W(j+2)
+        load_frags(sa, sw, 1, fa1, fb1);
+        issue(1, min(kt + 1, nk - 1), nw, HW, WL);  // W(j+1), second half
+        mfmas(fa0, fb0);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(sa, sw, 2, fa0, fb0);
+        issue(0, min(kt + 2, nk - 1), a2, 0, HX);   // A(j+2), first half
+        mfmas(fa1, fb1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(sa, sw, 3, fa1, fb1);
+        issue(0, min(kt + 2, nk - 1), a2, HX, XL);  // A(j+2), second half
+        mfmas(fa0, fb0);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        // slot reads of this stage are done; A(j+1), W(j+1) have landed
+        wait_vm_lgkm0<XL>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // Past the end the refills re-read the final k-block into freed
+        // slots, and the first fragments of a stage that does not exist are
+        // read from a stale, in-bounds slot.
+        load_frags(na, nw, 0, fa0, fb0);
+        issue(1, min(kt + 2, nk - 1), w2, 0, HW);   // W(j+2), first half
+        mfmas(fa1, fb1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // prologue: A0, W0, A1, W1 into slots 0..3 (slot 4 holds the row list
+    // until every wave has passed the barrier below)
+    issue(0, 0, 0, 0, XL);
+    issue(1, 0, 1, 0, WL);
+    issue(0, min(1, nk - 1), 2, 0, XL);
+    issue(1, min(1, nk - 1), 3, 0, WL);
+    wait_vm_lgkm0<XL + WL>();
+    __builtin_amdgcn_s_barrier();
+    load_frags(0, 1, 0, fa0, fb0);
+
+    int kt = 0;
+    for (; kt + 4 < nk; kt += 5) {
+        stage(std::integral_constant<int, 0>{}, kt);
+        stage(std::integral_constant<int, 1>{}, kt + 1);
+        stage(std::integral_constant<int, 2>{}, kt + 2);
+        stage(std::integral_constant<int, 3>{}, kt + 3);
+        stage(std::integral_constant<int, 4>{}, kt + 4);
+    }
+    if (kt < nk) stage(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) stage(std::integral_constant<int, 1>{}, kt + 1);
+    if (kt + 2 < nk) stage(std::integral_constant<int, 2>{}, kt + 2);
+    if (kt + 3 < nk) stage(std::integral_constant<int, 3>{}, kt + 3);
+    wait_vm_lgkm0<0>();  // no DMA may still be writing LDS when the tile ends
+
+    // Epilogue: lane holds, for token row m = lane&31 of each block, four
+    // consecutive output columns per register quad (SwiGLU: the act of each
+    // gate/up pair).
+    {
+        const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+        constexpr int OI = SWIGLU ? MI / 2 : MI;
+        const int col0 = SWIGLU ? ti.wrow0 / 2 + wn * (BN / 4) : ti.wrow0 + wn * WN;
+#pragma unroll
+        for (int j = 0; j < MJ; ++j) {
+            if (yoff[j] < 0) continue;
 #pragma unroll
             for (int i = 0; i < OI; ++i) {
+                const int n0 = col0 + i * 32;
+                if (n0 >= a.N) continue;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     float v[4];
@@ -734,38 +984,49 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
                         }
                     }
                     const u32x2_t pk = {pack2(v[0], v[1]), pack2(v[2], v[3])};
-                    *(lds_u32x2 *)(wp + jj * 32 * RS + (i * 32 + q * 8) * 2) = pk;
+                    __builtin_amdgcn_raw_buffer_store_b64(pk, yr,
+                                                          (uint32_t)yoff[j] + (uint32_t)(n0 + q * 8 + khalf * 4) * 2u,
+                                                          0, 0);
                 }
             }
         }
-#pragma unroll
-        for (int r = 0; r < RH; r += RPI) {
-            const u32x4_t v = *(const lds_u32x4 *)(rp + r * RS);
-            const int mloc = wm * WM + jp * 32 + r + lane / LPR;
-            if (col_ok && mloc < ti.count)
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    v, yr,
-                    (uint32_t)s_rows[mloc] * ldy_bytes + (uint32_t)col * 2u, 0, 0);
-        }
+    }
+}
+
+// Norm weights of the prologue, staged in LDS (only the prologue variants
+// reserve this space).
+template <bool PRO>
+__device__ __forceinline__ uint16_t *prologue_nw_lds() {
+    if constexpr (PRO) {
+        __shared__ __attribute__((aligned(16))) uint16_t s_nw[kMaxPrologueK];
+        return s_nw;
+    } else {
+        return nullptr;
     }
 }
 
 // INLINE: the workgroups build the segment list from the modality bytes
 // (and publish it to the workspace); otherwise they read the plan that
 // plan_kernel wrote.
+//
+// LDS: four 32 KiB arrays and a fifth that is a 32 KiB stage slot without
+// the prologue (the big tiles' five-slot ring; the row list and the scan
+// scratch then live in it outside the main loop) and 2 KiB with it (row
+// list and scan scratch; the prologue's big tiles run two stages of A in
+// array 0 or 2 and W in array 1 or 3, and its norm weights take 16 KiB).
+// Small tiles run four stages, one array each.
 template <bool SWIGLU, bool PRO, bool INLINE>
 __global__ void __launch_bounds__(kThreads, 1)
 gemm_kernel(GemmArgs a) {
-    // four 32 KiB LDS arrays: big tiles use two stages of (A in array 0 or
-    // 2, W in array 1 or 3), small tiles four stages of one array each
     constexpr int kArrayBytes = kBigM * kRowBytes;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kArrayBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kArrayBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds2[kArrayBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds3[kArrayBytes];
-    __shared__ int32_t s_rows[kBigM];
-    __shared__ int s_red[kThreads / 64];
-    __shared__ __attribute__((aligned(16))) uint16_t s_nw[PRO ? kMaxPrologueK : 8];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds4[PRO ? 2048 : kArrayBytes];
+    int32_t *const s_rows = (int32_t *)lds4;            // kBigM entries
+    int *const s_red = (int *)(lds4 + kBigM * 4);       // block-scan scratch
+    uint16_t *const s_nw = prologue_nw_lds<PRO>();
 
     const int T = (int)a.T;
     int U, G;
@@ -792,7 +1053,7 @@ gemm_kernel(GemmArgs a) {
         // passed with MOT_FLAG_PLAN_READY) makes every workgroup exit
         if (hdr[0] != 0 || hdr[3] != T || U < 0 || G < 0 || U + G != T) return;
     }
-    // per-wave epilogue staging: array `wave` of the four
+    // per-wave epilogue staging: array `wave` of the first four
     const int wave_id = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     lds_u8 *const eb = (lds_u8 *)(wave_id == 0 ? lds0 : wave_id == 1 ? lds1 : wave_id == 2 ? lds2 : lds3);
     const int grid = (int)gridDim.x;
@@ -824,14 +1085,18 @@ gemm_kernel(GemmArgs a) {
         // and spilled (a spill reload waits on vmcnt, i.e. on in-flight DMA).
         int tid = (int)threadIdx.x;
         asm volatile("" : "+v"(tid));
+        // the tile's rows into s_rows (ends with a barrier)
+        auto fill_rows = [&]() {
+            if constexpr (INLINE) {
+                route_gather(rb, ti.set, ti.first - (ti.set ? U : 0), ti.count, bm, s_rows, s_red);
+            } else {
+                for (int i = threadIdx.x; i < bm; i += kThreads)
+                    s_rows[i] = i < ti.count ? min(max(a.perm[ti.first + i], 0), T - 1) : 0;
+            }
+            __syncthreads();
+        };
         __syncthreads();  // every wave is done with the previous tile's LDS
-        if constexpr (INLINE) {
-            route_gather(rb, ti.set, ti.first - (ti.set ? U : 0), ti.count, bm, s_rows, s_red);
-        } else {
-            for (int i = threadIdx.x; i < bm; i += kThreads)
-                s_rows[i] = i < ti.count ? min(max(a.perm[ti.first + i], 0), T - 1) : 0;
-        }
-        __syncthreads();
+        fill_rows();
         if constexpr (INLINE) {
             // the tiles of weight rows [0, ...) cover every row once: they
             // publish the segment list
@@ -839,8 +1104,13 @@ gemm_kernel(GemmArgs a) {
                 for (int i = threadIdx.x; i < ti.count; i += kThreads) a.perm_out[ti.first + i] = s_rows[i];
         }
         if (ti.big) {
-            uint8_t *const xb[2] = {lds0, lds2}, *const wb[2] = {lds1, lds3};
-            run_tile<kBigM, kBigN, 2, SWIGLU, PRO>(a, ti, xb, wb, eb, s_rows, s_nw, tid);
+            if constexpr (PRO) {
+                uint8_t *const xb[2] = {lds0, lds2}, *const wb[2] = {lds1, lds3};
+                run_tile<kBigM, kBigN, 2, SWIGLU, PRO>(a, ti, xb, wb, eb, s_rows, s_nw, tid);
+            } else {
+                uint8_t *const hs[5] = {lds0, lds1, lds2, lds3, lds4};
+                run_big5<SWIGLU>(a, ti, hs, s_rows, tid);
+            }
         } else {
             constexpr int kHalf = kSmallM * kRowBytes;
             uint8_t *const xb[4] = {lds0, lds1, lds2, lds3};
