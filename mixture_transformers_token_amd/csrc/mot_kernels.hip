@@ -38,16 +38,14 @@ constexpr int kErrModality = 6;  // MOT_ERR_MODALITY
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Round to nearest, ties to even.  NaN stays NaN (quiet bit set).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+// fp32 -> bf16, round to nearest, ties to even: gfx950's v_cvt_pk_bf16_f32
+// (two values per instruction; a NaN comes out as a quiet NaN).  Every
+// rounding to bf16 in this library goes through it.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // ============================================================================

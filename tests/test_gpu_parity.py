@@ -91,6 +91,44 @@ def test_qkv_full_size_sampled():
     _gemm_parity(x, wu, wg, m, rows=rows)
 
 
+def _bf16_bits(sign, exp, mant):
+    """bf16 bit patterns of (-1)^sign * (1 + mant/128) * 2^exp."""
+    return ((sign.astype(np.uint16) << 15) | ((exp + 127).astype(np.uint16) << 7) |
+            mant.astype(np.uint16)).astype(np.uint16)
+
+
+def test_epilogue_rounding_bit_exact():
+    """Outputs that are exact two-term sums a_t + b_n (bf16 a, b; exponent
+    gap at most 15, so the fp32 accumulation is exact): the GPU's bf16 result
+    must be the correctly rounded value, bit for bit, ties to even included."""
+    rng = np.random.default_rng(11)
+    T, K, N = 96, 64, 128
+    a = _bf16_bits(rng.integers(0, 2, T), rng.integers(0, 4, T), rng.integers(0, 128, T))
+    xb = np.zeros((T, K), np.uint16)
+    xb[:, 0] = a
+    xb[:, 1] = 0x3F80  # 1.0
+    wsets = []
+    for s in range(2):
+        b = _bf16_bits(rng.integers(0, 2, N), rng.integers(-12, 4, N), rng.integers(0, 128, N))
+        wb = np.zeros((N, K), np.uint16)
+        wb[:, 0] = 0x3F80
+        wb[:, 1] = b
+        wsets.append(wb)
+    m = (rng.random(T) < 0.6).astype(np.uint8)
+
+    def t16(b):
+        return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+
+    y = mot.routed_gemm(dev(t16(xb)), dev(t16(wsets[0])), dev(t16(wsets[1])), dev(torch.from_numpy(m)))
+    ref, rne = oracle.routed_gemm(xb, wsets[0], wsets[1], m)
+    got = bits(y)
+    assert np.array_equal(got, rne), f"{int((got != rne).sum())} of {got.size} outputs not correctly rounded"
+    # the case really exercises ties: values exactly halfway between two bf16 numbers
+    e = np.floor(np.log2(np.abs(ref[ref != 0])))
+    frac = np.abs(ref[ref != 0]) * 2.0 ** (7 - e)
+    assert int((frac - np.floor(frac) == 0.5).sum()) > 50
+
+
 def test_empty_pack_is_noop():
     x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
     w = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
