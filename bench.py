@@ -100,6 +100,15 @@ def time_calls(fn, iters, stream):
     return start.elapsed_time(end) / iters * 1e-3  # seconds
 
 
+def time_component(fn, iters, stream, blocks=5, warmup=3):
+    """Median over `blocks` blocks of `iters` launches (after `warmup`
+    untimed launches) of the per-launch duration, HIP events on the stream."""
+    for _ in range(warmup):
+        fn()
+    ts = sorted(time_calls(fn, iters, stream) for _ in range(blocks))
+    return ts[len(ts) // 2]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -172,15 +181,15 @@ def main():
         xsd, rsd = xs.to(dev), rs.to(dev)
         yn = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
         rstd = torch.empty(T, dtype=torch.float32, device=dev)
-        s_norm = time_calls(lambda: mot.fused_add_rmsnorm(xsd, rsd, nwu, nwg, md, out=yn, rstd=rstd),
-                            iters, stream)
+        s_norm = time_component(lambda: mot.fused_add_rmsnorm(xsd, rsd, nwu, nwg, md, out=yn, rstd=rstd),
+                                iters, stream)
         nbytes = 4 * T * K * 2 + T * 4 + T
         components["fused_add_rmsnorm_T4096_H3584"] = {
             "us": round(s_norm * 1e6, 2), "GB/s": round(nbytes / s_norm / 1e9, 1),
             "frac_hbm": round(nbytes / s_norm / 1e9 / PEAK_HBM_GBS, 3)}
         # QKV with the routed-RMSNorm prologue (reads h + rstd instead of y)
-        s_pro = time_calls(lambda: mot.routed_gemm(rsd, wud, wgd, md, out=y, workspace=ws,
-                                                   norm=(rstd, nwu, nwg)), iters, stream)
+        s_pro = time_component(lambda: mot.routed_gemm(rsd, wud, wgd, md, out=y, workspace=ws,
+                                                       norm=(rstd, nwu, nwg)), iters, stream)
         components["qkv_prologue_T4096"] = {"us": round(s_pro * 1e6, 2),
                                             "TFLOP/s": round(flops / s_pro / 1e12, 1)}
         # small, weight-bound packs (HBM roofline): weights rotated over 8 copies
@@ -198,7 +207,7 @@ def main():
                 a, b = copies[ctr[0] % 4]
                 ctr[0] += 1
                 mot.routed_gemm(xs_s, a, b, mds, out=ys, workspace=wss)
-            s_small = time_calls(small, 40, stream)
+            s_small = time_component(small, 40, stream)
             sets = int((ms == 0).any()) + int((ms == 1).any())
             nb = sets * N * K * 2 + Ts * K * 2 + Ts * N * 2 + Ts
             components[f"qkv_small_T{Ts}"] = {"us": round(s_small * 1e6, 2),
@@ -210,9 +219,9 @@ def main():
         gu_u, gu_g, dn_u, dn_g = (t.to(dev) for t in W.mlp_weights())
         act = torch.empty((T, W.FFN), dtype=torch.bfloat16, device=dev)
         yd = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
-        s_gu = time_calls(lambda: mot.routed_gemm_swiglu(xd, gu_u, gu_g, md, out=act, workspace=ws),
-                          10, stream)
-        s_dn = time_calls(lambda: mot.routed_gemm(act, dn_u, dn_g, md, out=yd, workspace=ws), 10, stream)
+        s_gu = time_component(lambda: mot.routed_gemm_swiglu(xd, gu_u, gu_g, md, out=act, workspace=ws),
+                              5, stream)
+        s_dn = time_component(lambda: mot.routed_gemm(act, dn_u, dn_g, md, out=yd, workspace=ws), 5, stream)
         f_gu = 2.0 * T * K * 2 * W.FFN
         f_dn = 2.0 * T * W.FFN * K
         components["gate_up_swiglu_T4096"] = {"us": round(s_gu * 1e6, 1),

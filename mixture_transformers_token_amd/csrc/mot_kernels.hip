@@ -1219,6 +1219,189 @@ norm_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ residual,
     }
 }
 
+// ============================================================================
+// Routed GEMM for small packs (weight-bound)
+// ============================================================================
+//
+// A pack of at most kSkinnyMaxT rows reads far more weight bytes than it
+// computes on, so the work is spread over as many CUs as the weights allow:
+// one wave per workgroup, workgroup b taking weight set b / nblk and the 32
+// output columns (32 weight rows; SwiGLU: 32 gate and the matching 32 up
+// rows) of block b % nblk, for all of that set's rows (MJ = 1 or 2 blocks of
+// 32 token rows).  Weights and the set's A rows stream through a ring of LDS
+// stages of 64 k (distinct arrays, so fragment reads never wait for younger
+// DMA), as deep as the wave's vmcnt allows.  The MFMA chain is the one of the
+// big and small tiles (v_mfma_f32_32x32x16_bf16, D[n][m] = sum_k W[n][k]
+// A[m][k], k ascending), so every output element gets the same bytes.
+
+constexpr int kSkRing = 8;                       // LDS stage arrays
+constexpr int kSkSlotBytes = 128 * kRowBytes;    // up to 64 A rows + 64 W rows
+
+template <int MI, int MJ>
+struct SkinnyCfg {
+    static constexpr int XL = 4 * MJ;                    // A DMA instructions per stage
+    static constexpr int WL = 4 * MI;                    // W DMA instructions per stage
+    static constexpr int PER = XL + WL;
+    static constexpr int S = (63 / PER + 1) < kSkRing ? (63 / PER + 1) : kSkRing;  // stages in the ring
+};
+
+template <bool SWIGLU, int MJ>
+__device__ __forceinline__ void skinny_tile(const GemmArgs &a, int set, int blk, int count,
+                                            uint8_t *const (&sl)[kSkRing], const int32_t *s_rows) {
+    constexpr int MI = SWIGLU ? 2 : 1;
+    using C = SkinnyCfg<MI, MJ>;
+    constexpr int XL = C::XL, WL = C::WL, PER = C::PER, S = C::S;
+    constexpr int AB = MJ * 32 * kRowBytes;  // A rows' bytes in a slot (W rows follow)
+    static_assert(PER * (S - 1) < 64, "vmcnt range");
+    const int lane = threadIdx.x & 63;
+    const int K = a.K;
+    const int nk = K / kBK;
+    const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+    const rsrc_t wr = make_rsrc(set ? a.w_gen : a.w_und, a.w_bytes);
+
+    uint32_t xoff[XL], woff[WL];
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+        const int r = j * 8 + (lane >> 3);
+        xoff[j] = (uint32_t)s_rows[r] * (uint32_t)(a.ldx * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < WL; ++j) {
+        const int r = j * 8 + (lane >> 3);  // staged W row: [0,32) gate (or plain), [32,64) up
+        const int wrow = SWIGLU ? (r < 32 ? blk * 32 + r : a.N + blk * 32 + (r - 32)) : blk * 32 + r;
+        woff[j] = (uint32_t)wrow * (uint32_t)(K * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+    }
+    auto issue = [&](int kt, int s) {
+#pragma unroll
+        for (int j = 0; j < XL; ++j) dma16(xr, xoff[j], (uint32_t)kt * kRowBytes, sl[s] + j * 8 * kRowBytes);
+#pragma unroll
+        for (int j = 0; j < WL; ++j)
+            dma16(wr, woff[j], (uint32_t)kt * kRowBytes, sl[s] + AB + j * 8 * kRowBytes);
+    };
+
+    f32x16_t acc[MI][MJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < MJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    const int rsel = lane & 31, khalf = lane >> 5;
+    const int lsw = swz(lane & 15);
+
+    // stage kt in slot s: wait for it, four k-steps, then refill the slot
+    // with k-block kt + S (the final k-block again past the end)
+    auto stage = [&](int kt, int s) {
+        wait_vm_lgkm0<PER * (S - 1)>();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t pos = (uint32_t)(((2 * q + khalf) ^ lsw) * 16);
+            bf16x8_t fa[MI], fb[MJ];
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                fa[i] = *(const bf16x8_t *)(sl[s] + AB + (i * 32 + rsel) * kRowBytes + pos);
+#pragma unroll
+            for (int j = 0; j < MJ; ++j) fb[j] = *(const bf16x8_t *)(sl[s] + (j * 32 + rsel) * kRowBytes + pos);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < MJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+        wait_vm_lgkm0<PER * (S - 1)>();  // the slot's fragment reads are done
+        issue(min(kt + S, nk - 1), s);
+    };
+#pragma unroll
+    for (int s = 0; s < S; ++s) issue(min(s, nk - 1), s);
+    int kt = 0;
+    for (; kt + S - 1 < nk; kt += S) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) stage(kt + s, s);
+    }
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+        if (kt + s < nk) stage(kt + s, s);
+    wait_vm_lgkm0<0>();
+
+    const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+    const int col0 = blk * 32;
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) {
+        const int mloc = j * 32 + rsel;
+        if (mloc >= count) continue;
+        const uint32_t yrow = (uint32_t)s_rows[mloc] * (uint32_t)a.ldy * 2u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (SWIGLU) {
+                    const float g = acc[0][j][4 * q + e];
+                    const float u = acc[1][j][4 * q + e];
+                    v[e] = (g / (1.0f + expf(-g))) * u;
+                } else {
+                    v[e] = acc[0][j][4 * q + e];
+                }
+            }
+            const u32x2_t pk = {pack2(v[0], v[1]), pack2(v[2], v[3])};
+            __builtin_amdgcn_raw_buffer_store_b64(pk, yr, yrow + (uint32_t)(col0 + q * 8 + khalf * 4) * 2u, 0, 0);
+        }
+    }
+}
+
+// nblk: output column blocks of 32 (N / 32, or F / 32 for SwiGLU).  Builds
+// the pack's segment list itself (a pack fits one wave: lane l owns row l);
+// workgroup 0 publishes it (and the error word) to the workspace unless the
+// caller passed a ready plan.
+template <bool SWIGLU>
+__global__ void __launch_bounds__(64)
+skinny_kernel(GemmArgs a, int nblk, int publish) {
+    __shared__ __attribute__((aligned(1024))) uint8_t sl0[kSkSlotBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sl1[kSkSlotBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sl2[kSkSlotBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sl3[kSkSlotBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sl4[kSkSlotBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sl5[kSkSlotBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sl6[kSkSlotBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t sl7[kSkSlotBytes];
+    __shared__ int32_t s_rows[64];
+    const int lane = threadIdx.x;
+    const int T = (int)a.T;
+    const int set = (int)blockIdx.x / nblk, blk = (int)blockIdx.x % nblk;
+    const uint32_t m = lane < T ? (uint32_t)a.modality[lane] : 0u;
+    const uint64_t valid = lane < T ? 1ull : 0ull;
+    const uint64_t bad = __ballot(valid && m > 1);
+    const uint64_t und = __ballot(valid && m == 0), gen = __ballot(valid && m == 1);
+    const int U = __popcll(und);
+    if (publish && blockIdx.x == 0) {
+        if (lane == 0) {
+            a.hdr_out[0] = bad ? kErrModality : 0;
+            a.hdr_out[1] = bad ? 0 : U;
+            a.hdr_out[2] = bad ? 0 : T - U;
+            a.hdr_out[3] = T;
+        }
+        if (!bad && lane < T) {
+            const uint64_t mine = m ? gen : und;
+            const int rank = __popcll(mine & ((1ull << lane) - 1));
+            a.perm_out[(m ? U : 0) + rank] = lane;
+        }
+    }
+    if (bad) return;  // the pack holds an invalid byte: write nothing
+    const uint64_t mine = set ? gen : und;
+    const int count = __popcll(mine);
+    if (count == 0) return;
+    if (lane < T && ((mine >> lane) & 1ull)) s_rows[__popcll(mine & ((1ull << lane) - 1))] = lane;
+    if (lane >= count) s_rows[lane] = __ffsll((unsigned long long)mine) - 1;  // padding: a row of the set
+    __syncthreads();
+    if (count <= 32) {
+        uint8_t *const sl[kSkRing] = {sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7};
+        skinny_tile<SWIGLU, 1>(a, set, blk, count, sl, s_rows);
+    } else {
+        uint8_t *const sl[kSkRing] = {sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7};
+        skinny_tile<SWIGLU, 2>(a, set, blk, count, sl, s_rows);
+    }
+}
+
 }  // namespace
 
 // ============================================================================
@@ -1254,6 +1437,17 @@ int64_t gemm_tile_bound(int64_t T, int64_t wrows, int ncu) {
 }
 
 hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStream_t stream) {
+    if (a.T <= kSkinnyMaxT && a.rstd == nullptr && a.tile_mode == 0) {
+        // small pack: weight-bound path, one wave per 32 output columns and set
+        const int nblk = a.N / 32;
+        if (swiglu)
+            hipLaunchKernelGGL(skinny_kernel<true>, dim3(2 * nblk), dim3(64), 0, stream, a, nblk,
+                               inline_route ? 1 : 0);
+        else
+            hipLaunchKernelGGL(skinny_kernel<false>, dim3(2 * nblk), dim3(64), 0, stream, a, nblk,
+                               inline_route ? 1 : 0);
+        return hipGetLastError();
+    }
     int dev = 0, ncu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;

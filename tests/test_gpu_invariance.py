@@ -102,6 +102,17 @@ def test_tile_shape_does_not_change_bytes(qkv_setup, tile):
     assert raw_equal(y, s["ref"])
 
 
+@pytest.mark.parametrize("T", [1, 7, 32, 33, 64, 65])
+def test_small_packs_match_large_pack_bytes(qkv_setup, T):
+    """Packs of up to 64 rows run the weight-bound small-pack kernel (65 rows
+    the tiled kernel): each row's bytes equal those of the 1024-row pack."""
+    s = qkv_setup
+    rows = np.random.default_rng(T).permutation(1024)[:T]
+    y = mot.routed_gemm(dev(s["x_probe"][rows]), s["wu"], s["wg"],
+                        dev(torch.from_numpy(s["probe_m"][rows].copy())))
+    assert raw_equal(y, s["ref"][torch.from_numpy(rows).cuda()])
+
+
 def test_mixed_equals_per_set_dense(qkv_setup):
     """Mixed pack == each set's rows run as a single-set pack (gathered)."""
     s = qkv_setup
