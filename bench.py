@@ -227,6 +227,42 @@ def main():
         components["gate_up_swiglu_T4096"] = {"us": round(s_gu * 1e6, 1),
                                               "TFLOP/s": round(f_gu / s_gu / 1e12, 1)}
         components["down_T4096"] = {"us": round(s_dn * 1e6, 1), "TFLOP/s": round(f_dn / s_dn / 1e12, 1)}
+        # per-layer routed linear chain: fused add-RMSNorm -> QKV -> O (q slice
+        # standing in for attention) -> fused add-RMSNorm -> gate/up+SwiGLU ->
+        # down, on the three-branch CFG pack and on a 16384-row pack; FLOPs
+        # count real rows only (the CFG pack's 562 padding rows excluded)
+        ou, og = (t.to(dev) for t in W.o_weights())
+        for name, mc, real in (("cfg_pack_T4096", W.cfg_pack_modality(), 3534),
+                               ("pack_T16384", W.pattern(16384), 16384)):
+            Tc = mc.size
+            mcd = torch.from_numpy(mc).to(dev)
+            xc, rc = (t.to(dev) for t in W.residual_inputs(Tc, K, base=5))
+            res_c = rc.clone()
+            y1 = torch.empty((Tc, K), dtype=torch.bfloat16, device=dev)
+            qkv_c = torch.empty((Tc, N), dtype=torch.bfloat16, device=dev)
+            o_c = torch.empty((Tc, K), dtype=torch.bfloat16, device=dev)
+            act_c = torch.empty((Tc, W.FFN), dtype=torch.bfloat16, device=dev)
+            out_c = torch.empty((Tc, K), dtype=torch.bfloat16, device=dev)
+            wsc = mot.new_workspace(Tc, dev)
+            ops = {
+                "norm1": lambda: mot.fused_add_rmsnorm(xc, res_c, nwu, nwg, mcd, out=y1, rstd=None),
+                "qkv": lambda: mot.routed_gemm(y1, wud, wgd, mcd, out=qkv_c, workspace=wsc),
+                "o": lambda: mot.routed_gemm(qkv_c[:, :W.Q_DIM], ou, og, mcd, out=o_c, workspace=wsc),
+                "norm2": lambda: mot.fused_add_rmsnorm(o_c, res_c, nwu, nwg, mcd, out=y1, rstd=None),
+                "gate_up_swiglu": lambda: mot.routed_gemm_swiglu(y1, gu_u, gu_g, mcd, out=act_c, workspace=wsc),
+                "down": lambda: mot.routed_gemm(act_c, dn_u, dn_g, mcd, out=out_c, workspace=wsc),
+            }
+
+            def layer():
+                for f in ops.values():
+                    f()
+            s_layer = time_component(layer, 2, stream)
+            per_op = {k: round(time_component(f, 3, stream) * 1e6, 1) for k, f in ops.items()}
+            f_layer = 2.0 * real * (K * N + W.Q_DIM * K + K * 2 * W.FFN + W.FFN * K)
+            components[f"layer_chain_{name}"] = {"us": round(s_layer * 1e6, 1),
+                                                 "TFLOP/s": round(f_layer / s_layer / 1e12, 1),
+                                                 "real_rows": real, "per_op_us": per_op}
+            del act_c
         del gu_u, gu_g, dn_u, dn_g
 
     # ---- CPU oracle baseline on a bounded row sample -------------------------

@@ -34,7 +34,14 @@ def bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def check_parity(got_bits: np.ndarray, ref: np.ndarray, rne_bits: np.ndarray, what: str):
+def check_parity(got_bits: np.ndarray, ref: np.ndarray, rne_bits: np.ndarray, what: str,
+                 one_step: bool = True):
+    """The spec gate (max-abs / relative Frobenius, elementwise bf16 row
+    where |ref| >= 8).  one_step additionally requires every output with
+    |ref| >= 1/4 to be within one bf16 step of the correctly rounded oracle
+    value; it applies to single ops, not to a chain where the oracle carries
+    its own bf16 intermediates (a one-step difference in an intermediate
+    propagates)."""
     m = oracle.gate_metrics(got_bits, ref)
     big = np.abs(ref) >= 0.25
     ulp = int(oracle.ulp_distance(got_bits[big], rne_bits[big]).max()) if big.any() else 0
@@ -45,7 +52,8 @@ def check_parity(got_bits: np.ndarray, ref: np.ndarray, rne_bits: np.ndarray, wh
         assert m["max_abs"] <= MAX_ABS, (what, m)
     else:
         assert m["elem_excess"] <= 0.0, (what, m)
-    assert ulp <= 1, (what, m)
+    if one_step:
+        assert ulp <= 1, (what, m)
     return m
 
 
