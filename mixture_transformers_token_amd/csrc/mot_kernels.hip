@@ -1,10 +1,15 @@
 // HIP kernels of the MoT token-routed projection for gfx950 (MI355X).
 //
 //  * plan_kernel   -- the routing plan: stable partition of the pack's rows by
-//                     modality byte (the per-set segment list).
-//  * gemm_kernel   -- routed GEMM  y = A * W_set^T on bf16 MFMA with fp32
-//                     accumulation; optional routed-RMSNorm prologue on the A
+//                     modality byte (the per-set segment list), for packs
+//                     larger than the GEMM kernels build in-kernel.
+//  * gemm_kernel   -- persistent routed GEMM  y = A * W_set^T on bf16 MFMA
+//                     with fp32 accumulation (256x256 tiles on a five-slot
+//                     LDS ring, 128x128 tiles for the rest); in-kernel
+//                     segment list; optional routed-RMSNorm prologue on the A
 //                     operand; optional SwiGLU epilogue (gate/up pairs).
+//  * skinny_kernel -- the same GEMM for packs of at most 64 rows, spread
+//                     over one wave per 32 output columns (weight-bound).
 //  * norm_kernel   -- routed fused add-RMSNorm.
 //
 // Numerical contract (RL-Kernel RFC page "[RFC][BAGEL-7B-MoT] WS1/WS2 kernel
@@ -1083,18 +1088,15 @@ gemm_kernel(GemmArgs a) {
         // and spilled (a spill reload waits on vmcnt, i.e. on in-flight DMA).
         int tid = (int)threadIdx.x;
         asm volatile("" : "+v"(tid));
-        // the tile's rows into s_rows (ends with a barrier)
-        auto fill_rows = [&]() {
-            if constexpr (INLINE) {
-                route_gather(rb, ti.set, ti.first - (ti.set ? U : 0), ti.count, bm, s_rows, s_red);
-            } else {
-                for (int i = threadIdx.x; i < bm; i += kThreads)
-                    s_rows[i] = i < ti.count ? min(max(a.perm[ti.first + i], 0), T - 1) : 0;
-            }
-            __syncthreads();
-        };
         __syncthreads();  // every wave is done with the previous tile's LDS
-        fill_rows();
+        // the tile's rows into s_rows
+        if constexpr (INLINE) {
+            route_gather(rb, ti.set, ti.first - (ti.set ? U : 0), ti.count, bm, s_rows, s_red);
+        } else {
+            for (int i = threadIdx.x; i < bm; i += kThreads)
+                s_rows[i] = i < ti.count ? min(max(a.perm[ti.first + i], 0), T - 1) : 0;
+        }
+        __syncthreads();
         if constexpr (INLINE) {
             // the tiles of weight rows [0, ...) cover every row once: they
             // publish the segment list
