@@ -830,15 +830,17 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
         }
         woff[j] = (uint32_t)wrow * (uint32_t)(K * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
     }
-    // byte offsets of this lane's four output rows, -1 past the tile's rows
+    // byte offsets of this lane's four output rows (below 4 GiB), kNoRow
+    // past the tile's rows (odd, so never a row's offset)
+    constexpr uint32_t kNoRow = 0xffffffffu;
     const int rsel = lane & 31;
     const int khalf = lane >> 5;
-    int32_t yoff[MJ];
+    uint32_t yoff[MJ];
     {
 #pragma unroll
         for (int j = 0; j < MJ; ++j) {
             const int mloc = wm * WM + j * 32 + rsel;
-            yoff[j] = mloc < ti.count ? (int32_t)((uint32_t)s_rows[mloc] * (uint32_t)a.ldy * 2u) : -1;
+            yoff[j] = mloc < ti.count ? (uint32_t)s_rows[mloc] * (uint32_t)a.ldy * 2u : kNoRow;
         }
     }
 
@@ -968,7 +970,7 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
         const int col0 = SWIGLU ? ti.wrow0 / 2 + wn * (BN / 4) : ti.wrow0 + wn * WN;
 #pragma unroll
         for (int j = 0; j < MJ; ++j) {
-            if (yoff[j] < 0) continue;
+            if (yoff[j] == kNoRow) continue;
 #pragma unroll
             for (int i = 0; i < OI; ++i) {
                 const int n0 = col0 + i * 32;
@@ -987,8 +989,7 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
                         }
                     }
                     const u32x2_t pk = {pack2(v[0], v[1]), pack2(v[2], v[3])};
-                    __builtin_amdgcn_raw_buffer_store_b64(pk, yr,
-                                                          (uint32_t)yoff[j] + (uint32_t)(n0 + q * 8 + khalf * 4) * 2u,
+                    __builtin_amdgcn_raw_buffer_store_b64(pk, yr, yoff[j] + (uint32_t)(n0 + q * 8 + khalf * 4) * 2u,
                                                           0, 0);
                 }
             }

@@ -129,6 +129,40 @@ def test_epilogue_rounding_bit_exact():
     assert int((frac - np.floor(frac) == 0.5).sum()) > 50
 
 
+def test_operands_just_under_4gib():
+    """x and y each span just under 4 GiB (leading dimension ~2^20): the
+    kernels' 32-bit byte offsets reach their largest values in the last rows,
+    which the row sample includes."""
+    T, K, N = 2048, 256, 320
+    ld = (1 << 20) - 64
+    m = W.pattern(T)
+    m[::3] = 1 - m[::3]
+    x, wu, wg, _ = W.gemm_case(T, K, N, m, base=50)
+    xbig = torch.empty((T, ld), dtype=torch.bfloat16, device="cuda")
+    xbig[:, :K] = dev(x)
+    ybig = torch.empty((T, ld), dtype=torch.bfloat16, device="cuda")
+    assert (T - 1) * ld * 2 + K * 2 < (1 << 32) and (T - 1) * ld * 2 > (1 << 32) - (1 << 22)
+    mot.routed_gemm(xbig[:, :K], dev(wu), dev(wg), dev(torch.from_numpy(m)), out=ybig[:, :N])
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([W.sample_rows(m, 40, seed=3), np.arange(T - 8, T)]))
+    ref, rne = oracle.routed_gemm(W.bits(x)[rows], W.bits(wu), W.bits(wg), m[rows])
+    check_parity(bits(ybig[torch.from_numpy(rows).cuda(), :N]), ref, rne, "4 GiB operands")
+    del xbig, ybig
+
+
+def test_million_row_pack():
+    """2^20 rows (plan kernel, then 16 rounds of the persistent tile loop)."""
+    T, K, N = 1 << 20, 64, 64
+    m = np.random.default_rng(7).integers(0, 2, T).astype(np.uint8)
+    x, wu, wg, _ = W.gemm_case(T, K, N, m, base=51)
+    y = mot.routed_gemm(dev(x), dev(wu), dev(wg), dev(torch.from_numpy(m)))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(8).choice(T, 200, replace=False),
+                                     np.arange(0, 4), np.arange(T - 4, T)]))
+    ref, rne = oracle.routed_gemm(W.bits(x)[rows], W.bits(wu), W.bits(wg), m[rows])
+    check_parity(bits(y)[rows], ref, rne, "2^20-row pack")
+
+
 def test_empty_pack_is_noop():
     x = torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda")
     w = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
