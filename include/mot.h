@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 2
+#define MOT_ABI_VERSION 3
 
 typedef enum mot_status {
     MOT_OK = 0,
@@ -169,6 +169,29 @@ int mot_fused_add_rmsnorm(const uint16_t *x, uint16_t *residual,
                           uint16_t *out, float *rstd_out,
                           int64_t T, int64_t H,
                           void *workspace, void *stream);
+
+/* bf16 transpose, the operand preparation of the routed backward.  The RFC
+ * page (section 1) trains only the generation expert in Phase A while the
+ * frozen understanding operators still need dX, and the MoE route/combine PR
+ * page folds weight gradients over rows in ascending order in fp32.  With it:
+ *   dX = dY * W_{m(t)}  (per row t): mot_routed_gemm(dY, W_und^T, W_gen^T),
+ *        the same routed kernel and k order, W^T = this call on each [N][K] set;
+ *   dW_gen = sum over gen rows t of dY[t]^T X[t]: mot_routed_gemm(dY^T, Xg^T,
+ *        Xg^T, all rows set 0) over the tokens, where Xg^T is this call on X
+ *        with modality and keep = 1 (und rows zeroed) and both transposes are
+ *        padded to a multiple of 64 rows; the MFMA chain then folds the rows
+ *        in ascending 16-row chunks, in fp32.
+ *   out[c][r] = in[r][c]                  for r < rows, c < cols, except
+ *   out[c][r] = 0  where modality != NULL and modality[r] != keep, and for
+ *                  rows <= r < rows_pad.
+ *   in  [rows][ld_in] bf16, ld_in >= cols;  out [cols][ld_out], ld_out >= rows_pad;
+ *   ld_in % 8 == ld_out % 8 == 0, pointers 16-byte aligned, in and out disjoint,
+ *   keep 0 or 1; rows_pad <= MOT_MAX_T, cols <= MOT_MAX_DIM.
+ * Errors: MOT_ERR_INVALID_ARG, MOT_ERR_UNSUPPORTED_SHAPE, MOT_ERR_MISALIGNED,
+ * MOT_ERR_DEVICE.  rows_pad == 0 or cols == 0 is a no-op. */
+int mot_transpose_bf16(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t cols,
+                       const uint8_t *modality, int keep, uint16_t *out, int64_t ld_out,
+                       int64_t rows_pad, void *stream);
 
 /* Synchronises `stream` and returns the workspace's device error word:
  * MOT_OK, MOT_ERR_MODALITY, or MOT_ERR_DEVICE if the copy fails. */

@@ -19,10 +19,11 @@ import torch
 __all__ = [
     "MotError", "ABI_VERSION", "lib", "abi_version", "workspace_bytes", "new_workspace",
     "routing_plan", "plan_view", "routed_gemm", "routed_gemm_swiglu", "fused_add_rmsnorm",
+    "transpose", "routed_gemm_dx", "grad_w",
     "read_device_error", "status_string", "LIB_PATH",
 ]
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
 WS_HEADER_BYTES = 256
 FLAG_PLAN_READY = 1
@@ -34,6 +35,7 @@ TILE_FLAGS = {None: 0x00, "auto": 0x00, "256x256": 0x10, "128x128": 0x20}
 EXPORTS = (
     "mot_abi_version", "mot_status_string", "mot_workspace_bytes", "mot_routing_plan",
     "mot_routed_gemm", "mot_routed_gemm_swiglu", "mot_fused_add_rmsnorm", "mot_read_device_error",
+    "mot_transpose_bf16",
 )
 
 STATUS = {
@@ -77,6 +79,8 @@ def lib():
     L.mot_fused_add_rmsnorm.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, I64, I64, P, P]
     L.mot_read_device_error.restype = ctypes.c_int
     L.mot_read_device_error.argtypes = [P, P]
+    L.mot_transpose_bf16.restype = ctypes.c_int
+    L.mot_transpose_bf16.argtypes = [P, I64, I64, I64, P, ctypes.c_int, P, I64, I64, P]
     v = L.mot_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"stale libmot.so: ABI {v}, binding expects {ABI_VERSION}; rebuild it")
@@ -253,3 +257,52 @@ def fused_add_rmsnorm(x, residual, w_und, w_gen, modality, eps=1e-6, out=True, r
 def read_device_error(workspace: torch.Tensor) -> int:
     """Synchronises the current stream; returns the workspace's error status."""
     return int(lib().mot_read_device_error(_ptr(workspace), _stream(workspace.device)))
+
+
+def _pad64(n: int) -> int:
+    return (n + 63) // 64 * 64
+
+
+def transpose(x, modality=None, keep=1, rows_pad=None):
+    """out [cols, rows_pad] with out[c][r] = x[r][c]; rows whose modality byte
+    differs from `keep` (if modality is given) and rows past x's are zero."""
+    _req(x, "x", torch.bfloat16, 2)
+    rows, cols = x.shape
+    rows_pad = rows if rows_pad is None else int(rows_pad)
+    ld_out = max(8, (rows_pad + 7) // 8 * 8)  # the library takes 16-byte row pitches
+    out = torch.empty((cols, ld_out), dtype=torch.bfloat16, device=x.device)[:, :rows_pad]
+    if modality is not None:
+        _req(modality, "modality", torch.uint8, 1)
+        if modality.shape[0] != rows:
+            raise ValueError("modality must have one byte per row")
+        modality = modality.contiguous()
+    ld_in = _rows(x, "x") if rows > 0 else max(cols, 8)
+    st = lib().mot_transpose_bf16(_ptr(x) if rows > 0 else None, ld_in, rows, cols, _ptr(modality),
+                                  int(keep), _ptr(out), ld_out, rows_pad, _stream(x.device))
+    _check(st, "mot_transpose_bf16")
+    return out
+
+
+def routed_gemm_dx(dy, w_und, w_gen, modality, wt=None, out=None, workspace=None):
+    """dX[t] = dY[t] @ W_{modality[t]} (the routed backward for the inputs);
+    W_* are the forward's [N, K] weights.  wt = (W_und^T, W_gen^T) from
+    transpose() may be passed to reuse them."""
+    if wt is None:
+        wt = (transpose(w_und), transpose(w_gen))
+    return routed_gemm(dy, wt[0], wt[1], modality, out=out, workspace=workspace)
+
+
+def grad_w(dy, x, modality, keep=1):
+    """dW[n][k] = sum over rows t with modality[t] == keep of dY[t][n] * X[t][k]
+    (fp32, rows folded in ascending order in 16-row chunks), as bf16 [N, K]."""
+    _req(dy, "dy", torch.bfloat16, 2)
+    _req(x, "x", torch.bfloat16, 2)
+    T, N = dy.shape
+    if x.shape[0] != T:
+        raise ValueError("dy and x must have the same rows")
+    Tp = _pad64(max(T, 1))
+    dyt = transpose(dy, rows_pad=Tp)
+    xt = transpose(x, modality=modality, keep=keep, rows_pad=Tp)
+    sets = torch.zeros(N, dtype=torch.uint8, device=dy.device)
+    return routed_gemm(dyt, xt, xt, sets)
+

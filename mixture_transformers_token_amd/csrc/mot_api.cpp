@@ -241,6 +241,28 @@ int mot_fused_add_rmsnorm(const uint16_t *x, uint16_t *residual, const uint16_t 
                : MOT_ERR_DEVICE;
 }
 
+int mot_transpose_bf16(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t cols,
+                       const uint8_t *modality, int keep, uint16_t *out, int64_t ld_out,
+                       int64_t rows_pad, void *stream) {
+    if (rows < 0 || cols < 0 || rows_pad < rows) return MOT_ERR_INVALID_ARG;
+    if (rows_pad == 0 || cols == 0) return MOT_OK;
+    if (!in && rows > 0) return MOT_ERR_INVALID_ARG;
+    if (!out || (modality && keep != 0 && keep != 1)) return MOT_ERR_INVALID_ARG;
+    if (rows_pad > MOT_MAX_T || cols > MOT_MAX_DIM) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (ld_in < cols || ld_out < rows_pad) return MOT_ERR_INVALID_ARG;
+    if (ld_in % 8 || ld_out % 8) return MOT_ERR_MISALIGNED;
+    if ((in && !aligned16(in)) || !aligned16(out)) return MOT_ERR_MISALIGNED;
+    const int64_t in_bytes = rows > 0 ? ((rows - 1) * ld_in + cols) * 2 : 0;
+    const int64_t out_bytes = ((cols - 1) * ld_out + rows_pad) * 2;
+    if (in && overlaps(in, in_bytes, out, out_bytes)) return MOT_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(s);
+    if (!guard.ok()) return MOT_ERR_DEVICE;
+    return mot::launch_transpose(in, ld_in, rows, cols, modality, keep, out, ld_out, rows_pad, s) == hipSuccess
+               ? MOT_OK
+               : MOT_ERR_DEVICE;
+}
+
 int mot_read_device_error(const void *workspace, void *stream) {
     if (!workspace) return MOT_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -52,6 +52,9 @@ hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t
 // Launches the persistent routed GEMM (one workgroup per CU at most).  With
 // inline_route the kernel builds (and publishes) the segment list itself.
 hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStream_t stream);
+hipError_t launch_transpose(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t cols,
+                            const uint8_t *modality, int keep, uint16_t *out, int64_t ld_out,
+                            int64_t rows_pad, hipStream_t stream);
 hipError_t launch_norm(const uint16_t *x, uint16_t *residual, const uint16_t *w_und,
                        const uint16_t *w_gen, const uint8_t *modality, float eps,
                        uint16_t *out, float *rstd_out, int64_t T, int H, int32_t *err_word,

@@ -1405,6 +1405,67 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
     }
 }
 
+// ============================================================================
+// Transpose (backward operands)
+// ============================================================================
+//
+// out[c][r] = in[r][c] for r < rows, c < cols; zero where the row's modality
+// byte differs from `keep` (when a modality array is given) and for
+// rows <= r < rows_pad.  64x64 tiles through LDS: 16-byte row-contiguous reads
+// and writes.  Pure data movement (no arithmetic), so the bytes are exact.
+
+constexpr int kTrTile = 64;
+
+__global__ void __launch_bounds__(256)
+transpose_kernel(const uint16_t *__restrict__ in, int64_t ld_in, int rows, int cols,
+                 const uint8_t *__restrict__ modality, int keep, uint16_t *__restrict__ out,
+                 int64_t ld_out, int rows_pad) {
+    __shared__ uint16_t tile[kTrTile][kTrTile + 8];  // +8: 16-byte aligned rows, fewer bank conflicts
+    const int r0 = blockIdx.x * kTrTile, c0 = blockIdx.y * kTrTile;
+    const int tid = threadIdx.x;
+    // read: thread -> (row r0 + tid/8 + 32*pass, 8 columns at c0 + 8*(tid%8))
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int lr = tid / 8 + 32 * pass, lc = 8 * (tid % 8);
+        const int r = r0 + lr, c = c0 + lc;
+        uint16_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (r < rows && (modality == nullptr || (int)modality[r] == keep)) {
+            if (c + 8 <= cols) {
+                const uint4 q = *(const uint4 *)(in + (int64_t)r * ld_in + c);
+                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[2 * e] = (uint16_t)(w[e] & 0xffffu);
+                    v[2 * e + 1] = (uint16_t)(w[e] >> 16);
+                }
+            } else {
+                for (int e = 0; e < 8 && c + e < cols; ++e) v[e] = in[(int64_t)r * ld_in + c + e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tile[lr][lc + e] = v[e];
+    }
+    __syncthreads();
+    // write: thread -> (out row c0 + tid/8 + 32*pass, 8 out columns r0 + 8*(tid%8))
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int lc = tid / 8 + 32 * pass, lr = 8 * (tid % 8);
+        const int c = c0 + lc, r = r0 + lr;
+        if (c >= cols || r >= rows_pad) continue;
+        uint16_t v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = tile[lr + e][lc];
+        uint16_t *dst = out + (int64_t)c * ld_out + r;
+        if (r + 8 <= rows_pad) {
+            const uint4 q = {v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
+                             v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16)};
+            *(uint4 *)dst = q;
+        } else {
+            for (int e = 0; e < 8 && r + e < rows_pad; ++e) dst[e] = v[e];
+        }
+    }
+}
+
 }  // namespace
 
 // ============================================================================
@@ -1466,6 +1527,15 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
                    : launch_gemm_t<true, false>(a, inline_route, grid, stream);
     return pro ? launch_gemm_t<false, true>(a, inline_route, grid, stream)
                : launch_gemm_t<false, false>(a, inline_route, grid, stream);
+}
+
+hipError_t launch_transpose(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t cols,
+                            const uint8_t *modality, int keep, uint16_t *out, int64_t ld_out,
+                            int64_t rows_pad, hipStream_t stream) {
+    const dim3 grid((unsigned)((rows_pad + kTrTile - 1) / kTrTile), (unsigned)((cols + kTrTile - 1) / kTrTile));
+    hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, stream, in, ld_in, (int)rows, (int)cols, modality,
+                       keep, out, ld_out, (int)rows_pad);
+    return hipGetLastError();
 }
 
 hipError_t launch_norm(const uint16_t *x, uint16_t *residual, const uint16_t *w_und,

@@ -52,6 +52,10 @@ def lib():
         L.mot_oracle_routed_gemm.argtypes = [P, I64, P, P, P, I64, I64, I64, P, P, ctypes.c_int]
         L.mot_oracle_routed_gemm.restype = None
         L.mot_oracle_routed_gemm_swiglu.argtypes = [P, I64, P, P, P, I64, I64, I64, P, P, ctypes.c_int]
+        L.mot_oracle_routed_gemm_dx.argtypes = [P, P, P, P, I64, I64, I64, P, P, ctypes.c_int]
+        L.mot_oracle_routed_gemm_dx.restype = None
+        L.mot_oracle_grad_w.argtypes = [P, P, P, ctypes.c_int, I64, I64, I64, P, P, ctypes.c_int]
+        L.mot_oracle_grad_w.restype = None
         L.mot_oracle_routed_gemm_swiglu.restype = None
         L.mot_oracle_fused_add_rmsnorm.argtypes = [P, P, P, P, P, ctypes.c_float, I64, I64,
                                                    P, P, P, P, ctypes.c_int]
@@ -113,6 +117,37 @@ def routed_gemm(x, w_und, w_gen, modality, want_ref=True, want_out=True, threads
     ref = np.empty((T, N), np.float64) if want_ref else None
     out = np.empty((T, N), np.uint16) if want_out else None
     lib().mot_oracle_routed_gemm(_p(x), K, _p(wu), _p(wg), _p(m), T, K, N, _p(ref), _p(out), threads)
+    return ref, out
+
+
+def routed_gemm_dx(dy, w_und, w_gen, modality, threads=0):
+    """dy [T,N] uint16, w_* [N,K] uint16 (forward weights) -> (ref f64 [T,K], out u16 [T,K]):
+    dX[t] = dY[t] @ W_{modality[t]}."""
+    dy = _u16(dy)
+    T, N = dy.shape
+    K = w_und.shape[1]
+    wu = _u16(w_und, (N, K))
+    wg = _u16(w_gen, (N, K))
+    m = np.ascontiguousarray(modality, dtype=np.uint8)
+    assert m.shape == (T,)
+    ref = np.empty((T, K), np.float64)
+    out = np.empty((T, K), np.uint16)
+    lib().mot_oracle_routed_gemm_dx(_p(dy), _p(wu), _p(wg), _p(m), T, N, K, _p(ref), _p(out), threads)
+    return ref, out
+
+
+def grad_w(dy, x, modality, keep=1, threads=0):
+    """dy [T,N], x [T,K] uint16 -> (ref f64 [N,K], out u16 [N,K]):
+    dW = sum over rows with modality == keep of dY[t]^T X[t], ascending t."""
+    dy = _u16(dy)
+    T, N = dy.shape
+    x = _u16(x, (T, x.shape[1]))
+    K = x.shape[1]
+    m = np.ascontiguousarray(modality, dtype=np.uint8)
+    assert m.shape == (T,)
+    ref = np.empty((N, K), np.float64)
+    out = np.empty((N, K), np.uint16)
+    lib().mot_oracle_grad_w(_p(dy), _p(x), _p(m), int(keep), T, N, K, _p(ref), _p(out), threads)
     return ref, out
 
 

@@ -25,6 +25,13 @@
  *    multiply in fp32, one trailing cast, fixed reduction per row):
  *    h = bf16_rne(x + r) (the new residual), rstd = 1/sqrt(mean_k(h^2)+eps),
  *    y = bf16_rne(h * rstd * w_{m(t)}).
+ *  - Routed backward (the RFC page, section 1: Phase A trains only the
+ *    generation expert, and the frozen understanding operators still need
+ *    dX for their rows):  dX[t,k] = bf16_rne( sum_n dY[t,n] * W_{m(t)}[n,k] )
+ *    and the generation set's weight gradient
+ *    dW[n,k] = bf16_rne( sum over rows t with m(t) = keep of dY[t,n] * X[t,k] ),
+ *    rows in ascending order (the MoE route/combine PR page folds weight
+ *    gradients over rows in ascending order).
  *
  * Every floating-point step is done in fp64 and rounded to bf16 exactly once,
  * directly from fp64 (no fp32 step), so the oracle is the exact result up to
@@ -157,6 +164,52 @@ void mot_oracle_routed_gemm(const uint16_t *x, int64_t ldx,
                 ref[t * N + n] = s;
             if (out)
                 out[t * N + n] = bf16_round(s);
+        }
+    }
+}
+
+/* ---- routed backward ---------------------------------------------------------- */
+
+/* dy [T, N] (row stride N), w_und / w_gen [N, K]: the forward's weights.
+ * ref (may be NULL): [T, K] fp64; out (may be NULL): [T, K] bf16. */
+void mot_oracle_routed_gemm_dx(const uint16_t *dy, const uint16_t *w_und, const uint16_t *w_gen,
+                               const uint8_t *modality, int64_t T, int64_t N, int64_t K,
+                               double *ref, uint16_t *out, int nthreads)
+{
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *w = modality[t] ? w_gen : w_und;
+        const uint16_t *gr = dy + t * N;
+        for (int64_t k = 0; k < K; ++k) {
+            double s = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                s += bf16_value(gr[n]) * bf16_value(w[n * K + k]);
+            if (ref)
+                ref[t * K + k] = s;
+            if (out)
+                out[t * K + k] = bf16_round(s);
+        }
+    }
+}
+
+/* dy [T, N], x [T, K]: dW[n, k] over the rows whose modality byte is `keep`,
+ * ascending t.  ref (may be NULL): [N, K] fp64; out (may be NULL): [N, K] bf16. */
+void mot_oracle_grad_w(const uint16_t *dy, const uint16_t *x, const uint8_t *modality, int keep,
+                       int64_t T, int64_t N, int64_t K, double *ref, uint16_t *out, int nthreads)
+{
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            double s = 0.0;
+            for (int64_t t = 0; t < T; ++t)
+                if (modality[t] == keep)
+                    s += bf16_value(dy[t * N + n]) * bf16_value(x[t * K + k]);
+            if (ref)
+                ref[n * K + k] = s;
+            if (out)
+                out[n * K + k] = bf16_round(s);
         }
     }
 }

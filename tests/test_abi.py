@@ -142,3 +142,28 @@ def test_plan_fails_closed(kw, code):
 
 def test_read_device_error_needs_workspace():
     assert mot.lib().mot_read_device_error(None, None) == INVALID
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), INVALID),
+    (dict(rows_pad=50), INVALID),             # rows_pad < rows
+    (dict(rows=0, rows_pad=0, inp=None), OK), # nothing to write
+    (dict(cols=0), OK),
+    (dict(inp=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(keep=2, m=3 * A), INVALID),       # keep is read only with a modality
+    (dict(ld_in=100), INVALID),               # ld_in < cols
+    (dict(ld_out=64), INVALID),               # ld_out < rows_pad
+    (dict(ld_in=132), MISALIGNED),
+    (dict(ld_out=132, rows_pad=130), MISALIGNED),
+    (dict(inp=A + 2), MISALIGNED),
+    (dict(out=2 * A + 8), MISALIGNED),
+    (dict(out=A + 64), INVALID),              # out overlaps in
+    (dict(rows_pad=(1 << 24) + 8, ld_out=(1 << 24) + 8), SHAPE),
+])
+def test_transpose_fails_closed(kw, code):
+    a = dict(inp=A, ld_in=128, rows=100, cols=128, m=None, keep=1, out=2 * A, ld_out=128, rows_pad=128)
+    a.update(kw)
+    st = mot.lib().mot_transpose_bf16(a["inp"], a["ld_in"], a["rows"], a["cols"], a["m"], a["keep"],
+                                      a["out"], a["ld_out"], a["rows_pad"], None)
+    assert st == code

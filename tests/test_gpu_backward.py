@@ -1,0 +1,112 @@
+"""GPU parity of the routed backward (RFC page "[RFC][BAGEL-7B-MoT] WS1/WS2
+kernel roadmap", section 1: Phase A trains only the generation expert; the
+frozen understanding operators still need dX) against the CPU oracle.
+
+dX = dY W_{m(t)} runs the forward's routed GEMM on transposed weights; the
+generation set's dW = sum over gen rows of dY[t]^T X[t] runs it over the
+tokens on transposed, masked operands (rows folded in ascending 16-row
+chunks).  The transpose itself is pure data movement and is checked bit for
+bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_transformers_token_amd as mot
+import oracle
+import workloads as W
+from helpers import bits, check_parity, dev, raw_equal
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("rows,cols,pad,masked", [(1, 8, 1, False), (77, 200, 128, True),
+                                                  (300, 64, 320, False), (4096, 4608, 4096, True)])
+def test_transpose_is_exact(rows, cols, pad, masked):
+    x = W.normal_bf16((rows, cols), 500 + rows)
+    m = W.pattern(rows)
+    out = mot.transpose(dev(x), modality=dev(torch.from_numpy(m)) if masked else None, keep=1,
+                        rows_pad=pad if pad >= rows else rows)
+    torch.cuda.synchronize()
+    want = x.clone()
+    if masked:
+        want[torch.from_numpy(m != 1)] = 0
+    full = torch.zeros((cols, out.shape[1]), dtype=torch.bfloat16)
+    full[:, :rows] = want.T
+    assert raw_equal(out.cpu(), full)
+
+
+def _dx_parity(T, N, K, m, base, rows=None):
+    dy = W.normal_bf16((T, N), W.seed_of(base, 1))
+    wu = W.normal_bf16((N, K), W.seed_of(base, 2), 0.02)
+    wg = W.normal_bf16((N, K), W.seed_of(base, 3), 0.02)
+    dx = mot.routed_gemm_dx(dev(dy), dev(wu), dev(wg), dev(torch.from_numpy(m)))
+    torch.cuda.synchronize()
+    sel = np.arange(T) if rows is None else rows
+    ref, rne = oracle.routed_gemm_dx(W.bits(dy)[sel], W.bits(wu), W.bits(wg), m[sel])
+    check_parity(bits(dx)[sel], ref, rne, f"dX T={T} N={N} K={K}")
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 64, 64), (77, 128, 192), (333, 320, 256), (1101, 448, 320)])
+def test_dx_small(T, N, K):
+    m = W.pattern(T)
+    m[::5] = 1 - m[::5]
+    _dx_parity(T, N, K, m, base=510 + T)
+
+
+def test_dx_qkv_shape_sampled():
+    """dY [4096, 4608] (the QKV output's gradient) -> dX [4096, 3584]."""
+    m = W.pattern(4096)
+    _dx_parity(4096, W.QKV_DIM, W.HIDDEN, m, base=520, rows=W.sample_rows(m, 48, seed=4))
+
+
+def _grad_parity(T, N, K, m, base, cols=None):
+    dy = W.normal_bf16((T, N), W.seed_of(base, 1))
+    x = W.normal_bf16((T, K), W.seed_of(base, 4))
+    dw = mot.grad_w(dev(dy), dev(x), dev(torch.from_numpy(m)), keep=1)
+    torch.cuda.synchronize()
+    sel = np.arange(N) if cols is None else cols
+    # dW[n] depends on column n of dY only: the oracle on sampled columns is
+    # the exact restriction
+    ref, rne = oracle.grad_w(np.ascontiguousarray(W.bits(dy)[:, sel]), W.bits(x), m, keep=1)
+    check_parity(bits(dw)[sel], ref, rne, f"dW_gen T={T} N={N} K={K}")
+
+
+@pytest.mark.parametrize("T,N,K", [(1, 64, 64), (100, 128, 64), (333, 192, 256), (1101, 256, 128)])
+def test_grad_w_small(T, N, K):
+    m = W.pattern(T)
+    m[::4] = 1 - m[::4]
+    _grad_parity(T, N, K, m, base=530 + T)
+
+
+def test_grad_w_qkv_shape_sampled():
+    """The generation set's QKV weight gradient, dW [4608, 3584] over the
+    3788 gen rows of the 4096-row BAGEL pack, on sampled output rows."""
+    m = W.pattern(4096)
+    cols = np.random.default_rng(6).choice(W.QKV_DIM, 24, replace=False)
+    _grad_parity(4096, W.QKV_DIM, W.HIDDEN, m, base=540, cols=np.sort(cols))
+
+
+def test_dx_rows_batch_invariant():
+    """dX runs the forward's routed GEMM: a row's bytes do not depend on the
+    pack around it (probe rows alone, inside a larger mixed pack, permuted)."""
+    N, K = 512, 384
+    wu = dev(W.normal_bf16((N, K), 550, 0.02))
+    wg = dev(W.normal_bf16((N, K), 551, 0.02))
+    wt = (mot.transpose(wu), mot.transpose(wg))
+    probe = W.normal_bf16((200, N), 552)
+    pm = W.pattern(200)
+    ref = mot.routed_gemm_dx(dev(probe), wu, wg, dev(torch.from_numpy(pm)), wt=wt)
+    fill = W.normal_bf16((900, N), 553)
+    fm = np.random.default_rng(9).integers(0, 2, 900).astype(np.uint8)
+    dy = torch.cat([fill[:450], probe, fill[450:]])
+    m = np.concatenate([fm[:450], pm, fm[450:]])
+    perm = W.permutation(dy.shape[0], 10).numpy()
+    out = mot.routed_gemm_dx(dev(dy[perm]), wu, wg, dev(torch.from_numpy(m[perm])), wt=wt)
+    pos = np.empty(perm.size, np.int64)
+    pos[perm] = np.arange(perm.size)
+    got = out[torch.from_numpy(pos[450:650]).cuda()]
+    torch.cuda.synchronize()
+    assert raw_equal(got, ref)

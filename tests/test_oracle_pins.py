@@ -377,3 +377,86 @@ def test_pins_catch_planted_swiglu_and_norm_mistakes():
     no_eps_sqrt = (xd / (xd * xd).mean(-1, keepdim=True)).numpy()
     assert not np.allclose(r["ref"], sum_not_mean, rtol=1e-6)
     assert not np.allclose(r["ref"], no_eps_sqrt, rtol=1e-6)
+
+
+# ---- routed backward: dX = dY W_{m(t)} and the gen set's dW ------------------
+
+def _bf(shape, seed, std=1.0):
+    return W.bits(W.normal_bf16(shape, seed, std))
+
+
+def test_backward_tiny_brute_force():
+    """Every dX and dW element against math.fsum of the exact products (each
+    bf16 x bf16 product is exact in fp64), and the bf16 outputs against the
+    exactly rounded sum."""
+    T, N, K = 9, 40, 24
+    m = np.array([0, 1, 1, 0, 1, 0, 0, 1, 1], np.uint8)
+    dy, wu, wg, x = _bf((T, N), 701), _bf((N, K), 702, 0.05), _bf((N, K), 703, 0.05), _bf((T, K), 704)
+    d, w_u, w_g, xv = (oracle.bf16_to_f64(a) for a in (dy, wu, wg, x))
+    ref, out = oracle.routed_gemm_dx(dy, wu, wg, m)
+    for t in range(T):
+        w = w_g if m[t] else w_u
+        for k in range(K):
+            exact = math.fsum(float(d[t, n]) * float(w[n, k]) for n in range(N))
+            assert abs(ref[t, k] - exact) <= N * 2.0 ** -52 * math.fsum(abs(d[t, n] * w[n, k]) for n in range(N))
+            assert out[t, k] == rne_bf16_exact(exact)
+    gref, gout = oracle.grad_w(dy, x, m, keep=1)
+    for n in range(N):
+        for k in range(K):
+            exact = math.fsum(float(d[t, n]) * float(xv[t, k]) for t in range(T) if m[t] == 1)
+            assert abs(gref[n, k] - exact) <= T * 2.0 ** -52 * (1 + abs(exact) * 4)
+            assert gout[n, k] == rne_bf16_exact(exact)
+
+
+def test_backward_matches_torch_fp64():
+    """Single-set packs: dX is dY @ W; dW over the gen rows is
+    dY[gen]^T @ X[gen] (torch fp64 matmul)."""
+    T, N, K = 70, 128, 96
+    m = (np.arange(T) % 3 == 0).astype(np.uint8)
+    dy, wu, wg, x = _bf((T, N), 711), _bf((N, K), 712, 0.05), _bf((N, K), 713, 0.05), _bf((T, K), 714)
+    tdy, twu, twg, tx = (torch.from_numpy(oracle.bf16_to_f64(a)) for a in (dy, wu, wg, x))
+    ref, _ = oracle.routed_gemm_dx(dy, wu, wg, m)
+    want = torch.where(torch.from_numpy(m).bool()[:, None], tdy @ twg, tdy @ twu).numpy()
+    assert np.allclose(ref, want, rtol=1e-12, atol=1e-12)
+    gen = torch.from_numpy(m).bool()
+    gref, _ = oracle.grad_w(dy, x, m, keep=1)
+    assert np.allclose(gref, (tdy[gen].T @ tx[gen]).numpy(), rtol=1e-12, atol=1e-12)
+    uref, _ = oracle.grad_w(dy, x, m, keep=0)
+    assert np.allclose(uref, (tdy[~gen].T @ tx[~gen]).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_backward_adjoint_identities():
+    """dX is the adjoint of the forward routed GEMM: <dY, X W^T> = <dY W, X>
+    for each row's own set; and <dW_gen, V> = sum over gen rows of
+    <dY[t], X[t] V^T>, with the forward oracle on the right-hand side."""
+    T, N, K = 33, 64, 80
+    m = np.random.default_rng(5).integers(0, 2, T).astype(np.uint8)
+    dy, wu, wg, x = _bf((T, N), 721), _bf((N, K), 722, 0.05), _bf((N, K), 723, 0.05), _bf((T, K), 724)
+    fwd, _ = oracle.routed_gemm(x, wu, wg, m)           # X W^T per row, [T, N]
+    dx, _ = oracle.routed_gemm_dx(dy, wu, wg, m)         # dY W per row, [T, K]
+    lhs = float(np.sum(oracle.bf16_to_f64(dy) * fwd))
+    rhs = float(np.sum(dx * oracle.bf16_to_f64(x)))
+    assert abs(lhs - rhs) <= 1e-9 * (1 + abs(lhs))
+    v = _bf((N, K), 725, 0.05)
+    gw, _ = oracle.grad_w(dy, x, m, keep=1)
+    xv, _ = oracle.routed_gemm(x, v, v, m)              # X V^T, [T, N]
+    lhs = float(np.sum(gw * oracle.bf16_to_f64(v)))
+    rhs = float(np.sum((oracle.bf16_to_f64(dy) * xv)[m == 1]))
+    assert abs(lhs - rhs) <= 1e-9 * (1 + abs(lhs))
+
+
+def test_pins_catch_planted_backward_mistakes():
+    """Plausible mistakes, planted here on the CPU, fail the torch pin: the
+    other row's set, the transposed weight, und rows in the gen gradient."""
+    T, N, K = 40, 64, 64
+    m = (np.arange(T) % 2).astype(np.uint8)
+    dy, wu, wg, x = _bf((T, N), 731), _bf((N, K), 732, 0.05), _bf((N, K), 733, 0.05), _bf((T, K), 734)
+    tdy, twu, twg, tx = (torch.from_numpy(oracle.bf16_to_f64(a)) for a in (dy, wu, wg, x))
+    good = torch.where(torch.from_numpy(m).bool()[:, None], tdy @ twg, tdy @ twu).numpy()
+    swapped, _ = oracle.routed_gemm_dx(dy, wu, wg, 1 - m)
+    assert not np.allclose(swapped, good, rtol=1e-6)
+    transposed = torch.where(torch.from_numpy(m).bool()[:, None], tdy @ twg.T, tdy @ twu.T).numpy()
+    assert not np.allclose(transposed, good, rtol=1e-6)
+    all_rows = (tdy.T @ tx).numpy()
+    gref, _ = oracle.grad_w(dy, x, m, keep=1)
+    assert not np.allclose(gref, all_rows, rtol=1e-6)
