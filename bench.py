@@ -109,6 +109,10 @@ def time_component(fn, iters, stream, blocks=5, warmup=3):
     return ts[len(ts) // 2]
 
 
+def n_gen_rows(m):
+    return int((m == 1).sum())
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -215,6 +219,23 @@ def main():
                                               "frac_hbm": round(nb / s_small / 1e9 / PEAK_HBM_GBS, 3),
                                               "sets": sets}
             del copies
+        # routed backward of the QKV projection: dX = dY W_m on the
+        # transposed weights (made once per weight update), and the generation
+        # set's dW over its 3788 rows (two transposes + one routed GEMM over T)
+        dyd = W.normal_bf16((T, N), 11).to(dev)
+        wt = (mot.transpose(wud), mot.transpose(wgd))
+        dx = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+        s_dx = time_component(lambda: mot.routed_gemm_dx(dyd, wud, wgd, md, wt=wt, out=dx, workspace=ws),
+                              iters, stream)
+        s_wt = time_component(lambda: mot.transpose(wgd), iters, stream)
+        s_dw = time_component(lambda: mot.grad_w(dyd, xd, md, keep=1), 10, stream)
+        f_dw = 2.0 * n_gen_rows(m) * N * K
+        components["qkv_backward_T4096"] = {
+            "dx_us": round(s_dx * 1e6, 1), "dx_TFLOP/s": round(flops / s_dx / 1e12, 1),
+            "weight_transpose_us": round(s_wt * 1e6, 1),
+            "dw_gen_us": round(s_dw * 1e6, 1), "dw_gen_TFLOP/s": round(f_dw / s_dw / 1e12, 1),
+            "dw_gen_rows": n_gen_rows(m)}
+        del wt, dyd, dx
         # MLP: gate/up+SwiGLU 3584 -> 2x18944, down 18944 -> 3584
         gu_u, gu_g, dn_u, dn_g = (t.to(dev) for t in W.mlp_weights())
         act = torch.empty((T, W.FFN), dtype=torch.bfloat16, device=dev)
