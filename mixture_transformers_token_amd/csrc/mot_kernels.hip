@@ -9,7 +9,8 @@
 //                     segment list; optional routed-RMSNorm prologue on the A
 //                     operand; optional SwiGLU epilogue (gate/up pairs).
 //  * skinny_kernel -- the same GEMM for packs of at most 64 rows, spread
-//                     over one wave per 32 output columns (weight-bound).
+//                     over one workgroup per 32 output columns, all four
+//                     waves streaming weights (weight-bound).
 //  * norm_kernel   -- routed fused add-RMSNorm.
 //
 // Numerical contract (RL-Kernel RFC page "[RFC][BAGEL-7B-MoT] WS1/WS2 kernel
@@ -26,6 +27,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "mot_internal.h"
 
@@ -1228,147 +1230,224 @@ norm_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ residual,
 //
 // A pack of at most kSkinnyMaxT rows reads far more weight bytes than it
 // computes on, so the work is spread over as many CUs as the weights allow:
-// one wave per workgroup, workgroup b taking weight set b / nblk and the 32
-// output columns (32 weight rows; SwiGLU: 32 gate and the matching 32 up
-// rows) of block b % nblk, for all of that set's rows (MJ = 1 or 2 blocks of
-// 32 token rows).  Weights and the set's A rows stream through a ring of LDS
-// stages of 64 k (distinct arrays, so fragment reads never wait for younger
-// DMA), as deep as the wave's vmcnt allows.  The MFMA chain is the one of the
+// workgroup b takes weight set b / nblk and the 32 output columns (32 weight
+// rows; SwiGLU: 32 gate and the matching 32 up rows) of block b % nblk, for
+// all of that set's rows.  Stage j (64 k of the set's XG*8 A rows and of the
+// weight rows) sits in LDS slot j % S; all four waves load a share of every
+// stage, and one barrier per stage both publishes a stage and frees the slot
+// whose fragments were read before it.  Wave i < MJ runs the MFMA chain of
+// token rows [32i, 32i+32), reading each stage's fragments one stage ahead
+// so that the LDS latency hides under the MFMAs.  The chain is the one of the
 // big and small tiles (v_mfma_f32_32x32x16_bf16, D[n][m] = sum_k W[n][k]
-// A[m][k], k ascending), so every output element gets the same bytes.
+// A[m][k], k ascending), so every output element gets the same bytes; its
+// K/16 dependent MFMAs, not the weight loads, set the kernel's time.  Only
+// the pack's A rows are loaded (XG groups of 8); a fragment of an unloaded row
+// reads other bytes of the same slot, which only reach output rows that are
+// never stored.
 
-constexpr int kSkRing = 8;                       // LDS stage arrays
-constexpr int kSkSlotBytes = 128 * kRowBytes;    // up to 64 A rows + 64 W rows
+constexpr int kSkThreads = 256;
+constexpr int kSkLdsBytes = 152 * 1024;  // ring budget
+// Ring depth: measured best at 6 stages.  The loads are not what bounds this
+// kernel (four waves stream the weights at HBM rate with 8 DMA in flight
+// each); the chain is: every output element takes K/16 dependent MFMAs.  A
+// shallower ring leaves LDS for a second workgroup per CU (packs that hold
+// both sets launch more workgroups than there are CUs).
+constexpr int kSkMaxStages = 6;
 
-template <int MI, int MJ>
+template <int MI, int XG>
 struct SkinnyCfg {
-    static constexpr int XL = 4 * MJ;                    // A DMA instructions per stage
-    static constexpr int WL = 4 * MI;                    // W DMA instructions per stage
-    static constexpr int PER = XL + WL;
-    static constexpr int S = (63 / PER + 1) < kSkRing ? (63 / PER + 1) : kSkRing;  // stages in the ring
+    static constexpr int JMAX = XG > 4 ? 2 : 1;                 // row blocks of 32
+    static constexpr int AB = XG * 8 * kRowBytes;               // A rows' bytes in a slot
+    static constexpr int SLOT = AB + MI * 32 * kRowBytes;       // + the weight rows
+    static constexpr int XW = XG >= 4 ? XG / 4 : 1;             // A DMA per stage, waves that load A
+    static constexpr int CMAX = MI + XW;                        // most DMA per wave and stage
+    static constexpr int S0 = kSkLdsBytes / SLOT;
+    static constexpr int S1 = 63 / CMAX + 1;                    // (S - 1) * CMAX <= 63
+    static constexpr int S2 = S0 < S1 ? S0 : S1;
+    static constexpr int S = S2 < kSkMaxStages ? S2 : kSkMaxStages;  // stages in the ring
+    static_assert(SLOT >= JMAX * 32 * kRowBytes, "fragment reads stay in the slot");
+    static_assert(S >= 3, "ring depth");
 };
 
-template <bool SWIGLU, int MJ>
+// Slot I of a ring of SLOT-byte stages: a distinct LDS object per slot, so
+// that the compiler sees that DMA into one slot never aliases reads of
+// another and waits only where the code says so.
+template <int I, int SLOT>
+__device__ __forceinline__ uint8_t *sk_slot() {
+    __shared__ __attribute__((aligned(1024))) uint8_t buf[SLOT];
+    return buf;
+}
+template <int SLOT, int... I>
+__device__ __forceinline__ void sk_slots(uint8_t *(&sl)[sizeof...(I)], std::integer_sequence<int, I...>) {
+    ((sl[I] = sk_slot<I, SLOT>()), ...);
+}
+
+template <bool SWIGLU, int XG>
 __device__ __forceinline__ void skinny_tile(const GemmArgs &a, int set, int blk, int count,
-                                            uint8_t *const (&sl)[kSkRing], const int32_t *s_rows) {
+                                            uint8_t *const (&sl)[SkinnyCfg<SWIGLU ? 2 : 1, XG>::S],
+                                            const int32_t *s_rows, const int wave, const int lane) {
     constexpr int MI = SWIGLU ? 2 : 1;
-    using C = SkinnyCfg<MI, MJ>;
-    constexpr int XL = C::XL, WL = C::WL, PER = C::PER, S = C::S;
-    constexpr int AB = MJ * 32 * kRowBytes;  // A rows' bytes in a slot (W rows follow)
-    static_assert(PER * (S - 1) < 64, "vmcnt range");
-    const int lane = threadIdx.x & 63;
+    using C = SkinnyCfg<MI, XG>;
+    constexpr int S = C::S, AB = C::AB, XW = C::XW;
     const int K = a.K;
     const int nk = K / kBK;
     const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
     const rsrc_t wr = make_rsrc(set ? a.w_gen : a.w_und, a.w_bytes);
-
-    uint32_t xoff[XL], woff[WL];
+    // this wave's DMA of a stage: A groups wave + 4g (g < XW; with XG < 4
+    // only waves 0 .. XG-1 load one), weight groups wave + 4i (i < MI)
+    const bool loads_a = XG >= 4 || wave < XG;
+    uint32_t xoff[XW], woff[MI];
 #pragma unroll
-    for (int j = 0; j < XL; ++j) {
-        const int r = j * 8 + (lane >> 3);
-        xoff[j] = (uint32_t)s_rows[r] * (uint32_t)(a.ldx * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+    for (int g = 0; g < XW; ++g) {
+        const int r = (wave + 4 * g) * 8 + (lane >> 3);
+        xoff[g] = (uint32_t)s_rows[r < 64 ? r : 0] * (uint32_t)(a.ldx * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
     }
 #pragma unroll
-    for (int j = 0; j < WL; ++j) {
-        const int r = j * 8 + (lane >> 3);  // staged W row: [0,32) gate (or plain), [32,64) up
+    for (int i = 0; i < MI; ++i) {
+        const int r = (wave + 4 * i) * 8 + (lane >> 3);  // staged W row: [0,32) gate (or plain), [32,64) up
         const int wrow = SWIGLU ? (r < 32 ? blk * 32 + r : a.N + blk * 32 + (r - 32)) : blk * 32 + r;
-        woff[j] = (uint32_t)wrow * (uint32_t)(K * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+        woff[i] = (uint32_t)wrow * (uint32_t)(K * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
     }
     auto issue = [&](int kt, int s) {
+        if (loads_a) {
 #pragma unroll
-        for (int j = 0; j < XL; ++j) dma16(xr, xoff[j], (uint32_t)kt * kRowBytes, sl[s] + j * 8 * kRowBytes);
+            for (int g = 0; g < XW; ++g)
+                dma16(xr, xoff[g], (uint32_t)kt * kRowBytes, sl[s] + (wave + 4 * g) * 8 * kRowBytes);
+        }
 #pragma unroll
-        for (int j = 0; j < WL; ++j)
-            dma16(wr, woff[j], (uint32_t)kt * kRowBytes, sl[s] + AB + j * 8 * kRowBytes);
+        for (int i = 0; i < MI; ++i)
+            dma16(wr, woff[i], (uint32_t)kt * kRowBytes, sl[s] + AB + (wave + 4 * i) * 8 * kRowBytes);
+    };
+    // a stage has landed for this wave once at most Y younger stages are in
+    // flight (counts differ between waves that load A and those that do
+    // not, each a wave-uniform branch)
+    auto wait_stage = [&](auto y_c) {
+        constexpr int Y = decltype(y_c)::value;
+        if constexpr (XG >= 4) {
+            wait_vm_lgkm0<Y * (MI + XW)>();
+        } else {
+            if (loads_a)
+                wait_vm_lgkm0<Y * (MI + 1)>();
+            else
+                wait_vm_lgkm0<Y * MI>();
+        }
     };
 
-    f32x16_t acc[MI][MJ];
+    const int mj = count > 32 ? 2 : 1;
+    const bool computes = wave < mj;
+    f32x16_t acc[MI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < MJ; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
     const int rsel = lane & 31, khalf = lane >> 5;
     const int lsw = swz(lane & 15);
+    const int arow = (wave & 1) * 32 + rsel;  // this wave's token row of the slot (compute waves)
 
-    // stage kt in slot s: wait for it, four k-steps, then refill the slot
-    // with k-block kt + S (the final k-block again past the end)
-    auto stage = [&](int kt, int s) {
-        wait_vm_lgkm0<PER * (S - 1)>();
+    // Fragments are read one stage ahead, so that the LDS latency hides
+    // under the MFMAs: iteration kt waits for stage kt+1, passes the barrier
+    // (which also tells every wave that stage kt's slot, read in the
+    // previous iteration, is free), refills that slot with k-block kt+S (the
+    // final k-block again past the end, into a slot that is not read again),
+    // reads stage kt+1's fragments and runs stage kt's four k-steps.
+    bf16x8_t fa0[4][MI], fb0[4], fa1[4][MI], fb1[4];
+    auto read_stage = [&](int s, bf16x8_t (&fa)[4][MI], bf16x8_t (&fb)[4]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint32_t pos = (uint32_t)(((2 * q + khalf) ^ lsw) * 16);
-            bf16x8_t fa[MI], fb[MJ];
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-                fa[i] = *(const bf16x8_t *)(sl[s] + AB + (i * 32 + rsel) * kRowBytes + pos);
-#pragma unroll
-            for (int j = 0; j < MJ; ++j) fb[j] = *(const bf16x8_t *)(sl[s] + (j * 32 + rsel) * kRowBytes + pos);
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < MJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                fa[q][i] = *(const bf16x8_t *)(sl[s] + AB + (i * 32 + rsel) * kRowBytes + pos);
+            fb[q] = *(const bf16x8_t *)(sl[s] + arow * kRowBytes + pos);
         }
-        wait_vm_lgkm0<PER * (S - 1)>();  // the slot's fragment reads are done
+    };
+    auto mfma_stage = [&](const bf16x8_t (&fa)[4][MI], const bf16x8_t (&fb)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q][i], fb[q], acc[i], 0, 0, 0);
+    };
+    // stage kt sits in slot s; its fragments are in (fa0, fb0) when the
+    // parity p is 0, else in (fa1, fb1)
+    auto stage = [&](int kt, int s, auto p_c) {
+        wait_stage(std::integral_constant<int, S - 2>{});
+        __builtin_amdgcn_s_barrier();
         issue(min(kt + S, nk - 1), s);
+        if (computes) {
+            if constexpr (decltype(p_c)::value == 0) {
+                read_stage((s + 1) % S, fa1, fb1);
+                mfma_stage(fa0, fb0);
+            } else {
+                read_stage((s + 1) % S, fa0, fb0);
+                mfma_stage(fa1, fb1);
+            }
+        }
     };
 #pragma unroll
     for (int s = 0; s < S; ++s) issue(min(s, nk - 1), s);
+    wait_stage(std::integral_constant<int, S - 1>{});
+    __builtin_amdgcn_s_barrier();
+    if (computes) read_stage(0, fa0, fb0);
+    // unrolled by 2S so that both the slot and the register parity of every
+    // stage are compile-time constants
     int kt = 0;
-    for (; kt + S - 1 < nk; kt += S) {
+    for (; kt + 2 * S - 1 < nk; kt += 2 * S) {
 #pragma unroll
-        for (int s = 0; s < S; ++s) stage(kt + s, s);
+        for (int s = 0; s < 2 * S; ++s) {
+            if (s % 2 == 0)
+                stage(kt + s, s % S, std::integral_constant<int, 0>{});
+            else
+                stage(kt + s, s % S, std::integral_constant<int, 1>{});
+        }
     }
 #pragma unroll
-    for (int s = 0; s < S - 1; ++s)
-        if (kt + s < nk) stage(kt + s, s);
-    wait_vm_lgkm0<0>();
+    for (int s = 0; s < 2 * S - 1; ++s) {
+        if (kt + s < nk) {
+            if (s % 2 == 0)
+                stage(kt + s, s % S, std::integral_constant<int, 0>{});
+            else
+                stage(kt + s, s % S, std::integral_constant<int, 1>{});
+        }
+    }
+    wait_vm_lgkm0<0>();  // no DMA may still be writing LDS when the workgroup ends
+    if (!computes) return;
 
     const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
     const int col0 = blk * 32;
+    const int mloc = wave * 32 + rsel;
+    if (mloc >= count) return;
+    const uint32_t yrow = (uint32_t)s_rows[mloc] * (uint32_t)a.ldy * 2u;
 #pragma unroll
-    for (int j = 0; j < MJ; ++j) {
-        const int mloc = j * 32 + rsel;
-        if (mloc >= count) continue;
-        const uint32_t yrow = (uint32_t)s_rows[mloc] * (uint32_t)a.ldy * 2u;
+    for (int q = 0; q < 4; ++q) {
+        float v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if constexpr (SWIGLU) {
-                    const float g = acc[0][j][4 * q + e];
-                    const float u = acc[1][j][4 * q + e];
-                    v[e] = (g / (1.0f + expf(-g))) * u;
-                } else {
-                    v[e] = acc[0][j][4 * q + e];
-                }
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (SWIGLU) {
+                const float g = acc[0][4 * q + e];
+                const float u = acc[1][4 * q + e];
+                v[e] = (g / (1.0f + expf(-g))) * u;
+            } else {
+                v[e] = acc[0][4 * q + e];
             }
-            const u32x2_t pk = {pack2(v[0], v[1]), pack2(v[2], v[3])};
-            __builtin_amdgcn_raw_buffer_store_b64(pk, yr, yrow + (uint32_t)(col0 + q * 8 + khalf * 4) * 2u, 0, 0);
         }
+        const u32x2_t pk = {pack2(v[0], v[1]), pack2(v[2], v[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(pk, yr, yrow + (uint32_t)(col0 + q * 8 + khalf * 4) * 2u, 0, 0);
     }
 }
 
-// nblk: output column blocks of 32 (N / 32, or F / 32 for SwiGLU).  Builds
-// the pack's segment list itself (a pack fits one wave: lane l owns row l);
-// workgroup 0 publishes it (and the error word) to the workspace unless the
-// caller passed a ready plan.
-template <bool SWIGLU>
-__global__ void __launch_bounds__(64)
+// nblk: output column blocks of 32 (N / 32, or F / 32 for SwiGLU); XG: A row
+// groups of 8 staged per k-block (at least the pack's rows / 8).  Builds the
+// pack's segment list itself (every wave from the same ballots: lane l owns
+// row l); workgroup 0 publishes it (and the error word) to the workspace
+// unless the caller passed a ready plan.
+template <bool SWIGLU, int XG>
+__global__ void __launch_bounds__(kSkThreads)
 skinny_kernel(GemmArgs a, int nblk, int publish) {
-    __shared__ __attribute__((aligned(1024))) uint8_t sl0[kSkSlotBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sl1[kSkSlotBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sl2[kSkSlotBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sl3[kSkSlotBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sl4[kSkSlotBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sl5[kSkSlotBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sl6[kSkSlotBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t sl7[kSkSlotBytes];
+    using C = SkinnyCfg<SWIGLU ? 2 : 1, XG>;
     __shared__ int32_t s_rows[64];
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int T = (int)a.T;
     const int set = (int)blockIdx.x / nblk, blk = (int)blockIdx.x % nblk;
     const uint32_t m = lane < T ? (uint32_t)a.modality[lane] : 0u;
@@ -1376,7 +1455,7 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
     const uint64_t bad = __ballot(valid && m > 1);
     const uint64_t und = __ballot(valid && m == 0), gen = __ballot(valid && m == 1);
     const int U = __popcll(und);
-    if (publish && blockIdx.x == 0) {
+    if (publish && blockIdx.x == 0 && wave == 0) {
         if (lane == 0) {
             a.hdr_out[0] = bad ? kErrModality : 0;
             a.hdr_out[1] = bad ? 0 : U;
@@ -1389,20 +1468,18 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
             a.perm_out[(m ? U : 0) + rank] = lane;
         }
     }
-    if (bad) return;  // the pack holds an invalid byte: write nothing
+    if (bad) return;  // the pack holds an invalid byte: write nothing (all waves)
     const uint64_t mine = set ? gen : und;
     const int count = __popcll(mine);
-    if (count == 0) return;
-    if (lane < T && ((mine >> lane) & 1ull)) s_rows[__popcll(mine & ((1ull << lane) - 1))] = lane;
-    if (lane >= count) s_rows[lane] = __ffsll((unsigned long long)mine) - 1;  // padding: a row of the set
-    __syncthreads();
-    if (count <= 32) {
-        uint8_t *const sl[kSkRing] = {sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7};
-        skinny_tile<SWIGLU, 1>(a, set, blk, count, sl, s_rows);
-    } else {
-        uint8_t *const sl[kSkRing] = {sl0, sl1, sl2, sl3, sl4, sl5, sl6, sl7};
-        skinny_tile<SWIGLU, 2>(a, set, blk, count, sl, s_rows);
+    if (count == 0) return;  // all waves
+    if (wave == 0) {
+        if (lane < T && ((mine >> lane) & 1ull)) s_rows[__popcll(mine & ((1ull << lane) - 1))] = lane;
+        if (lane >= count) s_rows[lane] = __ffsll((unsigned long long)mine) - 1;  // padding: a row of the set
     }
+    __syncthreads();
+    uint8_t *sl[C::S];
+    sk_slots<C::SLOT>(sl, std::make_integer_sequence<int, C::S>{});
+    skinny_tile<SWIGLU, XG>(a, set, blk, count, sl, s_rows, wave, lane);
 }
 
 // ============================================================================
@@ -1502,14 +1579,26 @@ int64_t gemm_tile_bound(int64_t T, int64_t wrows, int ncu) {
 
 hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStream_t stream) {
     if (a.T <= kSkinnyMaxT && a.rstd == nullptr && a.tile_mode == 0) {
-        // small pack: weight-bound path, one wave per 32 output columns and set
+        // small pack: weight-bound path, one workgroup per 32 output columns
+        // and set; XG = A row groups of 8 that cover the pack
         const int nblk = a.N / 32;
-        if (swiglu)
-            hipLaunchKernelGGL(skinny_kernel<true>, dim3(2 * nblk), dim3(64), 0, stream, a, nblk,
-                               inline_route ? 1 : 0);
-        else
-            hipLaunchKernelGGL(skinny_kernel<false>, dim3(2 * nblk), dim3(64), 0, stream, a, nblk,
-                               inline_route ? 1 : 0);
+        const int pub = inline_route ? 1 : 0;
+        const dim3 grid(2 * nblk), block(kSkThreads);
+        if (swiglu) {
+            if (a.T <= 8)
+                hipLaunchKernelGGL((skinny_kernel<true, 1>), grid, block, 0, stream, a, nblk, pub);
+            else if (a.T <= 32)
+                hipLaunchKernelGGL((skinny_kernel<true, 4>), grid, block, 0, stream, a, nblk, pub);
+            else
+                hipLaunchKernelGGL((skinny_kernel<true, 8>), grid, block, 0, stream, a, nblk, pub);
+        } else {
+            if (a.T <= 8)
+                hipLaunchKernelGGL((skinny_kernel<false, 1>), grid, block, 0, stream, a, nblk, pub);
+            else if (a.T <= 32)
+                hipLaunchKernelGGL((skinny_kernel<false, 4>), grid, block, 0, stream, a, nblk, pub);
+            else
+                hipLaunchKernelGGL((skinny_kernel<false, 8>), grid, block, 0, stream, a, nblk, pub);
+        }
         return hipGetLastError();
     }
     int dev = 0, ncu = 0;
