@@ -1247,25 +1247,29 @@ norm_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ residual,
 
 constexpr int kSkThreads = 256;
 constexpr int kSkLdsBytes = 152 * 1024;  // ring budget
-// Ring depth: measured best at 6 stages.  The loads are not what bounds this
+// Ring depth: measured best at 6 stages.  A stage is one 64-wide k-block,
+// or two for packs of up to 8 rows without SwiGLU (measured 10% faster there,
+// slower elsewhere: larger slots leave room for fewer workgroups).  The loads are not what bounds this
 // kernel (four waves stream the weights at HBM rate with 8 DMA in flight
 // each); the chain is: every output element takes K/16 dependent MFMAs.  A
 // shallower ring leaves LDS for a second workgroup per CU (packs that hold
 // both sets launch more workgroups than there are CUs).
 constexpr int kSkMaxStages = 6;
 
-template <int MI, int XG>
+template <int MI, int XG, int KSUB_>
 struct SkinnyCfg {
+    static constexpr int KSUB = KSUB_;                          // 64-wide k-blocks per stage
     static constexpr int JMAX = XG > 4 ? 2 : 1;                 // row blocks of 32
-    static constexpr int AB = XG * 8 * kRowBytes;               // A rows' bytes in a slot
-    static constexpr int SLOT = AB + MI * 32 * kRowBytes;       // + the weight rows
-    static constexpr int XW = XG >= 4 ? XG / 4 : 1;             // A DMA per stage, waves that load A
-    static constexpr int CMAX = MI + XW;                        // most DMA per wave and stage
+    static constexpr int AB = XG * 8 * kRowBytes;               // A rows' bytes of a k-block
+    static constexpr int SUB = AB + MI * 32 * kRowBytes;        // + the weight rows
+    static constexpr int SLOT = KSUB * SUB;
+    static constexpr int XW = XG >= 4 ? XG / 4 : 1;             // A DMA per k-block, waves that load A
+    static constexpr int CMAX = (MI + XW) * KSUB;               // most DMA per wave and stage
     static constexpr int S0 = kSkLdsBytes / SLOT;
     static constexpr int S1 = 63 / CMAX + 1;                    // (S - 1) * CMAX <= 63
     static constexpr int S2 = S0 < S1 ? S0 : S1;
     static constexpr int S = S2 < kSkMaxStages ? S2 : kSkMaxStages;  // stages in the ring
-    static_assert(SLOT >= JMAX * 32 * kRowBytes, "fragment reads stay in the slot");
+    static_assert(SUB >= JMAX * 32 * kRowBytes, "fragment reads stay in the k-block");
     static_assert(S >= 3, "ring depth");
 };
 
@@ -1282,15 +1286,15 @@ __device__ __forceinline__ void sk_slots(uint8_t *(&sl)[sizeof...(I)], std::inte
     ((sl[I] = sk_slot<I, SLOT>()), ...);
 }
 
-template <bool SWIGLU, int XG>
+template <bool SWIGLU, int XG, int KS>
 __device__ __forceinline__ void skinny_tile(const GemmArgs &a, int set, int blk, int count,
-                                            uint8_t *const (&sl)[SkinnyCfg<SWIGLU ? 2 : 1, XG>::S],
+                                            uint8_t *const (&sl)[SkinnyCfg<SWIGLU ? 2 : 1, XG, KS>::S],
                                             const int32_t *s_rows, const int wave, const int lane) {
     constexpr int MI = SWIGLU ? 2 : 1;
-    using C = SkinnyCfg<MI, XG>;
-    constexpr int S = C::S, AB = C::AB, XW = C::XW;
+    using C = SkinnyCfg<MI, XG, KS>;
+    constexpr int S = C::S, AB = C::AB, XW = C::XW, KSUB = C::KSUB, SUB = C::SUB;
     const int K = a.K;
-    const int nk = K / kBK;
+    const int nk = K / kBK / KSUB;  // stages (the launch makes KSUB divide K / 64)
     const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
     const rsrc_t wr = make_rsrc(set ? a.w_gen : a.w_und, a.w_bytes);
     // this wave's DMA of a stage: A groups wave + 4g (g < XW; with XG < 4
@@ -1309,14 +1313,18 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs &a, int set, int blk,
         woff[i] = (uint32_t)wrow * (uint32_t)(K * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
     }
     auto issue = [&](int kt, int s) {
-        if (loads_a) {
 #pragma unroll
-            for (int g = 0; g < XW; ++g)
-                dma16(xr, xoff[g], (uint32_t)kt * kRowBytes, sl[s] + (wave + 4 * g) * 8 * kRowBytes);
+        for (int u = 0; u < KSUB; ++u) {
+            const uint32_t koff = (uint32_t)(kt * KSUB + u) * kRowBytes;
+            if (loads_a) {
+#pragma unroll
+                for (int g = 0; g < XW; ++g)
+                    dma16(xr, xoff[g], koff, sl[s] + u * SUB + (wave + 4 * g) * 8 * kRowBytes);
+            }
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                dma16(wr, woff[i], koff, sl[s] + u * SUB + AB + (wave + 4 * i) * 8 * kRowBytes);
         }
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-            dma16(wr, woff[i], (uint32_t)kt * kRowBytes, sl[s] + AB + (wave + 4 * i) * 8 * kRowBytes);
     };
     // a stage has landed for this wave once at most Y younger stages are in
     // flight (counts differ between waves that load A and those that do
@@ -1324,12 +1332,12 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs &a, int set, int blk,
     auto wait_stage = [&](auto y_c) {
         constexpr int Y = decltype(y_c)::value;
         if constexpr (XG >= 4) {
-            wait_vm_lgkm0<Y * (MI + XW)>();
+            wait_vm_lgkm0<Y * (MI + XW) * KSUB>();
         } else {
             if (loads_a)
-                wait_vm_lgkm0<Y * (MI + 1)>();
+                wait_vm_lgkm0<Y * (MI + 1) * KSUB>();
             else
-                wait_vm_lgkm0<Y * MI>();
+                wait_vm_lgkm0<Y * MI * KSUB>();
         }
     };
 
@@ -1350,23 +1358,25 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs &a, int set, int blk,
     // previous iteration, is free), refills that slot with k-block kt+S (the
     // final k-block again past the end, into a slot that is not read again),
     // reads stage kt+1's fragments and runs stage kt's four k-steps.
-    bf16x8_t fa0[4][MI], fb0[4], fa1[4][MI], fb1[4];
-    auto read_stage = [&](int s, bf16x8_t (&fa)[4][MI], bf16x8_t (&fb)[4]) {
+    constexpr int NQ = 4 * KSUB;  // k-steps of 16 per stage, ascending
+    bf16x8_t fa0[NQ][MI], fb0[NQ], fa1[NQ][MI], fb1[NQ];
+    auto read_stage = [&](int s, bf16x8_t (&fa)[NQ][MI], bf16x8_t (&fb)[NQ]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int t = 0; t < NQ; ++t) {
+            const int u = t / 4, q = t % 4;
             const uint32_t pos = (uint32_t)(((2 * q + khalf) ^ lsw) * 16);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-                fa[q][i] = *(const bf16x8_t *)(sl[s] + AB + (i * 32 + rsel) * kRowBytes + pos);
-            fb[q] = *(const bf16x8_t *)(sl[s] + arow * kRowBytes + pos);
+                fa[t][i] = *(const bf16x8_t *)(sl[s] + u * SUB + AB + (i * 32 + rsel) * kRowBytes + pos);
+            fb[t] = *(const bf16x8_t *)(sl[s] + u * SUB + arow * kRowBytes + pos);
         }
     };
-    auto mfma_stage = [&](const bf16x8_t (&fa)[4][MI], const bf16x8_t (&fb)[4]) {
+    auto mfma_stage = [&](const bf16x8_t (&fa)[NQ][MI], const bf16x8_t (&fb)[NQ]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int t = 0; t < NQ; ++t)
 #pragma unroll
             for (int i = 0; i < MI; ++i)
-                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q][i], fb[q], acc[i], 0, 0, 0);
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[t][i], fb[t], acc[i], 0, 0, 0);
     };
     // stage kt sits in slot s; its fragments are in (fa0, fb0) when the
     // parity p is 0, else in (fa1, fb1)
@@ -1437,14 +1447,15 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs &a, int set, int blk,
 }
 
 // nblk: output column blocks of 32 (N / 32, or F / 32 for SwiGLU); XG: A row
-// groups of 8 staged per k-block (at least the pack's rows / 8).  Builds the
+// groups of 8 staged per k-block (at least the pack's rows / 8); KS: k-blocks
+// of 64 per stage (dividing K / 64).  Builds the
 // pack's segment list itself (every wave from the same ballots: lane l owns
 // row l); workgroup 0 publishes it (and the error word) to the workspace
 // unless the caller passed a ready plan.
-template <bool SWIGLU, int XG>
+template <bool SWIGLU, int XG, int KS>
 __global__ void __launch_bounds__(kSkThreads)
 skinny_kernel(GemmArgs a, int nblk, int publish) {
-    using C = SkinnyCfg<SWIGLU ? 2 : 1, XG>;
+    using C = SkinnyCfg<SWIGLU ? 2 : 1, XG, KS>;
     __shared__ int32_t s_rows[64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -1479,7 +1490,7 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
     __syncthreads();
     uint8_t *sl[C::S];
     sk_slots<C::SLOT>(sl, std::make_integer_sequence<int, C::S>{});
-    skinny_tile<SWIGLU, XG>(a, set, blk, count, sl, s_rows, wave, lane);
+    skinny_tile<SWIGLU, XG, KS>(a, set, blk, count, sl, s_rows, wave, lane);
 }
 
 // ============================================================================
@@ -1586,18 +1597,20 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
         const dim3 grid(2 * nblk), block(kSkThreads);
         if (swiglu) {
             if (a.T <= 8)
-                hipLaunchKernelGGL((skinny_kernel<true, 1>), grid, block, 0, stream, a, nblk, pub);
+                hipLaunchKernelGGL((skinny_kernel<true, 1, 1>), grid, block, 0, stream, a, nblk, pub);
             else if (a.T <= 32)
-                hipLaunchKernelGGL((skinny_kernel<true, 4>), grid, block, 0, stream, a, nblk, pub);
+                hipLaunchKernelGGL((skinny_kernel<true, 4, 1>), grid, block, 0, stream, a, nblk, pub);
             else
-                hipLaunchKernelGGL((skinny_kernel<true, 8>), grid, block, 0, stream, a, nblk, pub);
+                hipLaunchKernelGGL((skinny_kernel<true, 8, 1>), grid, block, 0, stream, a, nblk, pub);
         } else {
-            if (a.T <= 8)
-                hipLaunchKernelGGL((skinny_kernel<false, 1>), grid, block, 0, stream, a, nblk, pub);
+            if (a.T <= 8 && (a.K / kBK) % 2 == 0)
+                hipLaunchKernelGGL((skinny_kernel<false, 1, 2>), grid, block, 0, stream, a, nblk, pub);
+            else if (a.T <= 8)
+                hipLaunchKernelGGL((skinny_kernel<false, 1, 1>), grid, block, 0, stream, a, nblk, pub);
             else if (a.T <= 32)
-                hipLaunchKernelGGL((skinny_kernel<false, 4>), grid, block, 0, stream, a, nblk, pub);
+                hipLaunchKernelGGL((skinny_kernel<false, 4, 1>), grid, block, 0, stream, a, nblk, pub);
             else
-                hipLaunchKernelGGL((skinny_kernel<false, 8>), grid, block, 0, stream, a, nblk, pub);
+                hipLaunchKernelGGL((skinny_kernel<false, 8, 1>), grid, block, 0, stream, a, nblk, pub);
         }
         return hipGetLastError();
     }

@@ -56,6 +56,24 @@ def test_ragged_packs(T):
     _gemm_parity(x, wu, wg, m)
 
 
+@pytest.mark.parametrize("T", [1, 5, 8, 9, 32, 40, 64])
+@pytest.mark.parametrize("K", [64, 128, 192, 320, 448])
+def test_small_pack_stage_sizes(T, K):
+    """Packs of up to 64 rows run the small-pack kernel, whose stages span one
+    or (for up to 8 rows and an even K / 64) two k-blocks: odd and even block
+    counts, parity with the oracle and the bytes of the tiled kernel (forced
+    with a tile flag) for the same rows."""
+    m = W.pattern(T)
+    m[::3] = 1 - m[::3]
+    x, wu, wg, _ = W.gemm_case(T, K, 192, m, base=600 + T + K)
+    _gemm_parity(x, wu, wg, m)
+    md = dev(torch.from_numpy(m))
+    small = mot.routed_gemm(dev(x), dev(wu), dev(wg), md)
+    tiled = mot.routed_gemm(dev(x), dev(wu), dev(wg), md, tile="128x128")
+    torch.cuda.synchronize()
+    assert torch.equal(small.view(torch.int16), tiled.view(torch.int16))
+
+
 @pytest.mark.parametrize("tile", ["256x256", "128x128"])
 @pytest.mark.parametrize("T", [1, 300, 1101])
 def test_forced_tile_shapes(T, tile):
