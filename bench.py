@@ -236,6 +236,14 @@ def main():
             "dw_gen_us": round(s_dw * 1e6, 1), "dw_gen_TFLOP/s": round(f_dw / s_dw / 1e12, 1),
             "dw_gen_rows": n_gen_rows(m)}
         del wt, dyd, dx
+        # context only: the vendor library's dense GEMM of one weight set at
+        # the same shape (hipBLASLt via torch.matmul; not batch-invariant,
+        # not a target)
+        wg_t = wgd.t()
+        s_blas = time_component(lambda: torch.matmul(xd, wg_t), iters, stream)
+        components["context_dense_one_set_torch_matmul_T4096"] = {
+            "us": round(s_blas * 1e6, 1), "TFLOP/s": round(flops / s_blas / 1e12, 1),
+            "note": "hipBLASLt dense x @ W_gen^T, one set, for context; not batch-invariant"}
         # MLP: gate/up+SwiGLU 3584 -> 2x18944, down 18944 -> 3584
         gu_u, gu_g, dn_u, dn_g = (t.to(dev) for t in W.mlp_weights())
         act = torch.empty((T, W.FFN), dtype=torch.bfloat16, device=dev)
