@@ -60,6 +60,9 @@ def lib():
         L.mot_oracle_fused_add_rmsnorm.argtypes = [P, P, P, P, P, ctypes.c_float, I64, I64,
                                                    P, P, P, P, ctypes.c_int]
         L.mot_oracle_fused_add_rmsnorm.restype = None
+        L.mot_oracle_qk_norm_rope.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, P, P, I64,
+                                              ctypes.c_float, P, P, ctypes.c_int]
+        L.mot_oracle_qk_norm_rope.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -184,6 +187,28 @@ def fused_add_rmsnorm(x, r, w_und, w_gen, modality, eps=1e-6, threads=0):
     lib().mot_oracle_fused_add_rmsnorm(_p(x), _p(rr), _p(wu), _p(wg), _p(m), float(eps), T, H,
                                        _p(h), _p(rstd), _p(ref), _p(out), threads)
     return {"h": h, "rstd": rstd, "ref": ref, "out": out}
+
+
+def qk_norm_rope(qkv, n_q_heads, n_k_heads, modality, q_norm, k_norm, positions, cos_t, sin_t,
+                 eps=1e-6, threads=0):
+    """Routed per-head QK RMSNorm, then the bf16 rotary embedding (rotate-half
+    pairs), on a [T, ld] bf16 copy of the QKV rows.  q_norm, k_norm: (und,
+    gen) pairs of [128] bf16 weights; positions [T] int32; cos_t, sin_t
+    [n_pos, 64] bf16.  Returns (ref fp64 [T, ld], out bf16 [T, ld], error)."""
+    qkv = _u16(qkv)
+    T, ld = qkv.shape
+    m = np.ascontiguousarray(modality, dtype=np.uint8)
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    qu, qg, ku, kg = (_u16(a) for a in (q_norm[0], q_norm[1], k_norm[0], k_norm[1]))
+    ct, st = _u16(cos_t), _u16(sin_t)
+    assert m.shape == (T,) and pos.shape == (T,) and ct.shape == st.shape and ct.shape[1] == 64
+    assert 128 * (n_q_heads + n_k_heads) <= ld and all(a.shape == (128,) for a in (qu, qg, ku, kg))
+    out = np.empty((T, ld), np.uint16)
+    ref = np.empty((T, ld), np.float64)
+    err = lib().mot_oracle_qk_norm_rope(_p(qkv), ld, T, n_q_heads, n_k_heads, _p(m), _p(qu), _p(qg), _p(ku),
+                                        _p(kg), _p(pos), _p(ct), _p(st), ct.shape[0], eps, _p(out), _p(ref),
+                                        threads)
+    return ref, out, int(err)
 
 
 def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:

@@ -32,6 +32,10 @@
  *    dW[n,k] = bf16_rne( sum over rows t with m(t) = keep of dY[t,n] * X[t,k] ),
  *    rows in ascending order (the MoE route/combine PR page folds weight
  *    gradients over rows in ascending order).
+ *  - Routed per-head QK RMSNorm and rotary embedding (the "mot_qk_norm_rope"
+ *    work item; the RFC page's reference hazards: QK norm in fp32, then the
+ *    rotation and Q/K in bf16): see mot_oracle_qk_norm_rope.  Its bf16
+ *    roundings are part of the definition, so it rounds where the page does.
  *
  * Every floating-point step is done in fp64 and rounded to bf16 exactly once,
  * directly from fp64 (no fp32 step), so the oracle is the exact result up to
@@ -286,4 +290,78 @@ void mot_oracle_fused_add_rmsnorm(const uint16_t *x, const uint16_t *r,
                 out[t * H + k] = bf16_round(y);
         }
     }
+}
+
+/* ---- routed per-head QK RMSNorm, then rotary position embedding -------------- */
+
+/* The "mot_qk_norm_rope" work item of the RFC page (section 5), with the
+ * order the page's reference hazards fix: the QK norm in fp32, then the
+ * rotation and Q/K in bf16.  Per row t (weight set m = modality[t]) and per
+ * head of 128 columns (q heads at [0, 128*hq), k heads after them):
+ *   rstd = 1/sqrt(mean_j(x_j^2) + eps),  y_j = bf16_rne(x_j * rstd * w_m[j])
+ *   (the set's q or k norm weight, one cast as in the layer norm), then with
+ *   c_i, s_i the bf16 table entries of the row's position (i = j mod 64) and
+ *   the rotate-half pairing (j, j+64):
+ *     out_j    = bf16(bf16(y_j * c_j)      + bf16(-y_{j+64} * s_j))   j < 64
+ *     out_j+64 = bf16(bf16(y_{j+64} * c_j) + bf16( y_j * s_j))
+ *   each bf16() one round-to-nearest-even of the exact value.
+ * qkv, out: [T][ld] bf16 (out starts as a copy: other columns, and rows with
+ * an invalid modality byte or position, keep their input bytes).  ref (may
+ * be NULL): [T][ld] fp64, the exact sum before the last rounding (the input
+ * value where copied).  cos_t, sin_t: [n_pos][64] bf16.  Returns 0, or the
+ * largest error code seen: 6 (modality byte outside {0,1}), 7 (position
+ * outside [0, n_pos)). */
+int mot_oracle_qk_norm_rope(const uint16_t *qkv, int64_t ld, int64_t T, int64_t hq, int64_t hk,
+                            const uint8_t *modality, const uint16_t *qw_und, const uint16_t *qw_gen,
+                            const uint16_t *kw_und, const uint16_t *kw_gen, const int32_t *positions,
+                            const uint16_t *cos_t, const uint16_t *sin_t, int64_t n_pos, float eps,
+                            uint16_t *out, double *ref, int nthreads)
+{
+    int err = 0;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 4) reduction(max : err)
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *row = qkv + t * ld;
+        for (int64_t c = 0; c < ld; ++c) {
+            out[t * ld + c] = row[c];
+            if (ref)
+                ref[t * ld + c] = bf16_value(row[c]);
+        }
+        int e = 0;
+        if (modality[t] > 1)
+            e = 6;
+        if (positions[t] < 0 || positions[t] >= n_pos)
+            e = 7;
+        if (e) {
+            if (e > err)
+                err = e;
+            continue;
+        }
+        const int m = modality[t];
+        const uint16_t *cs = cos_t + (int64_t)positions[t] * 64, *sn = sin_t + (int64_t)positions[t] * 64;
+        for (int64_t h = 0; h < hq + hk; ++h) {
+            const uint16_t *w = h < hq ? (m ? qw_gen : qw_und) : (m ? kw_gen : kw_und);
+            const uint16_t *x = row + h * 128;
+            double ss = 0.0;
+            for (int j = 0; j < 128; ++j)
+                ss += bf16_value(x[j]) * bf16_value(x[j]);
+            const double rs = 1.0 / sqrt(ss / 128.0 + (double)eps);
+            double y[128];
+            for (int j = 0; j < 128; ++j)
+                y[j] = bf16_value(bf16_round(bf16_value(x[j]) * rs * bf16_value(w[j])));
+            for (int j = 0; j < 64; ++j) {
+                const double c = bf16_value(cs[j]), s = bf16_value(sn[j]);
+                const double lo = bf16_value(bf16_round(y[j] * c)) + bf16_value(bf16_round(-y[j + 64] * s));
+                const double hi = bf16_value(bf16_round(y[j + 64] * c)) + bf16_value(bf16_round(y[j] * s));
+                const int64_t o = t * ld + h * 128 + j;
+                out[o] = bf16_round(lo);
+                out[o + 64] = bf16_round(hi);
+                if (ref) {
+                    ref[o] = lo;
+                    ref[o + 64] = hi;
+                }
+            }
+        }
+    }
+    return err;
 }

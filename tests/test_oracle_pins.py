@@ -460,3 +460,124 @@ def test_pins_catch_planted_backward_mistakes():
     all_rows = (tdy.T @ tx).numpy()
     gref, _ = oracle.grad_w(dy, x, m, keep=1)
     assert not np.allclose(gref, all_rows, rtol=1e-6)
+
+
+# ---- routed per-head QK RMSNorm + rotary embedding -----------------------------
+
+def _qk_case(T, hq, hk, ld, base, n_pos=97):
+    qkv = _bf((T, ld), W.seed_of(base, 1), 1.2)
+    m = (np.arange(T) % 3 == 0).astype(np.uint8)
+    qn, kn = W.qk_norm_weights(base)
+    cos_t, sin_t, pos = W.rope_inputs(T, n_pos, base)
+    return qkv, m, qn, kn, cos_t, sin_t, pos.numpy()
+
+
+def _oracle_qk(qkv, hq, hk, m, qn, kn, cos_t, sin_t, pos, eps=1e-6):
+    return oracle.qk_norm_rope(qkv, hq, hk, m, tuple(W.bits(t) for t in qn), tuple(W.bits(t) for t in kn),
+                               pos, W.bits(cos_t), W.bits(sin_t), eps)
+
+
+def _torch_qk(qkv, hq, hk, m, qn, kn, cos_t, sin_t, pos, eps=1e-6, pair=64, weights_of_k=None,
+              swap_tables=False, whole_row=False, cast_first=False):
+    """The op from library routines: torch's fp64 rms_norm with the row's
+    set's weight, rounded to bf16, then the rotate-half rotation in torch's
+    own bf16 arithmetic (each product and the sum rounded).  The keyword
+    arguments plant plausible mistakes."""
+    F = torch.nn.functional
+    x = torch.from_numpy(oracle.bf16_to_f64(qkv))
+    out = W.from_bits(qkv).clone()
+    gen = torch.from_numpy(m.astype(bool))[:, None]
+    c, s = (cos_t, sin_t) if not swap_tables else (sin_t, cos_t)
+    c2 = torch.cat((c[pos], c[pos]), 1)
+    s2 = torch.cat((s[pos], s[pos]), 1)
+    for h in range(hq + hk):
+        xs = x[:, h * 128:(h + 1) * 128]
+        wu, wg = qn if (h < hq or weights_of_k == "q") else kn
+        if whole_row:
+            rs = torch.rsqrt(x[:, :128 * (hq + hk)].pow(2).mean(1, keepdim=True) + eps)
+            yu, yg = xs * rs * wu.double(), xs * rs * wg.double()
+        elif cast_first:
+            n = F.rms_norm(xs, (128,), eps=eps).to(torch.bfloat16)
+            yu, yg = n * wu, n * wg
+        else:
+            yu = F.rms_norm(xs, (128,), weight=wu.double(), eps=eps)
+            yg = F.rms_norm(xs, (128,), weight=wg.double(), eps=eps)
+        y = torch.where(gen, yg, yu).to(torch.bfloat16)
+        rh = torch.cat((-y[:, pair:], y[:, :pair]), 1)
+        out[:, h * 128:(h + 1) * 128] = y * c2 + rh * s2
+    return W.bits(out)
+
+
+def test_qk_norm_rope_matches_torch():
+    """Both sets, 3 q and 2 k heads, extra columns past the heads: the oracle
+    equals the op built from torch's rms_norm and bf16 arithmetic bit for bit,
+    and leaves the other columns alone."""
+    T, hq, hk, ld = 40, 3, 2, 5 * 128 + 64
+    case = _qk_case(T, hq, hk, ld, base=801)
+    ref, out, err = _oracle_qk(*case[:1], hq, hk, *case[1:])
+    assert err == 0
+    want = _torch_qk(case[0], hq, hk, *case[1:])
+    assert np.array_equal(out, want)
+    assert np.array_equal(out[:, 5 * 128:], case[0][:, 5 * 128:])
+    # ref is the exact sum of two bf16 values, rounded once to give out
+    assert np.array_equal(np.array([oracle.bf16_round(v) for v in ref[:3].ravel()], np.uint16).reshape(3, ld),
+                          out[:3])
+
+
+def test_qk_norm_rope_special_angles():
+    """cos 1, sin 0: the per-head RMSNorm alone (torch's fp64 rms_norm, one
+    rounding).  cos 0, sin 1: exactly the rotate-half of that.  cos -1, sin 0:
+    exactly its negation."""
+    T, hq, hk, ld = 12, 2, 1, 3 * 128
+    qkv, m, qn, kn, _, _, pos = _qk_case(T, hq, hk, ld, base=802, n_pos=5)
+    one, zero = torch.ones((5, 64), dtype=torch.bfloat16), torch.zeros((5, 64), dtype=torch.bfloat16)
+    _, y, err = _oracle_qk(qkv, hq, hk, m, qn, kn, one, zero, pos)
+    assert err == 0
+    x = torch.from_numpy(oracle.bf16_to_f64(qkv))
+    for h in range(hq + hk):
+        wu, wg = qn if h < hq else kn
+        xs = x[:, h * 128:(h + 1) * 128]
+        F = torch.nn.functional
+        want = torch.where(torch.from_numpy(m.astype(bool))[:, None],
+                           F.rms_norm(xs, (128,), weight=wg.double(), eps=1e-6),
+                           F.rms_norm(xs, (128,), weight=wu.double(), eps=1e-6)).to(torch.bfloat16)
+        assert np.array_equal(y[:, h * 128:(h + 1) * 128], W.bits(want))
+    _, r, _ = _oracle_qk(qkv, hq, hk, m, qn, kn, zero, one, pos)
+    _, neg, _ = _oracle_qk(qkv, hq, hk, m, qn, kn, -one, zero, pos)
+    for h in range(hq + hk):
+        yh, rh, nh = (a[:, h * 128:(h + 1) * 128] for a in (y, r, neg))
+        assert np.array_equal(rh[:, :64], yh[:, 64:] ^ np.uint16(0x8000))
+        assert np.array_equal(rh[:, 64:], yh[:, :64])
+        assert np.array_equal(nh, yh ^ np.uint16(0x8000))
+
+
+def test_qk_norm_rope_errors_and_relabel():
+    """Rows with a modality byte outside {0,1} or a position outside the
+    table keep their bytes and set the error (7 wins over 6); swapping the
+    sets' weights and flipping the bytes gives the same output."""
+    T, hq, hk, ld = 10, 1, 1, 2 * 128
+    qkv, m, qn, kn, c, s, pos = _qk_case(T, hq, hk, ld, base=803, n_pos=11)
+    _, good, err = _oracle_qk(qkv, hq, hk, m, qn, kn, c, s, pos)
+    assert err == 0
+    _, flip, _ = _oracle_qk(qkv, hq, hk, 1 - m, (qn[1], qn[0]), (kn[1], kn[0]), c, s, pos)
+    assert np.array_equal(flip, good)
+    bm = m.copy()
+    bm[3] = 2
+    _, o, err = _oracle_qk(qkv, hq, hk, bm, qn, kn, c, s, pos)
+    assert err == 6 and np.array_equal(o[3], qkv[3]) and np.array_equal(np.delete(o, 3, 0), np.delete(good, 3, 0))
+    bp = pos.copy()
+    bp[5], bp[6] = 11, -1
+    _, o, err = _oracle_qk(qkv, hq, hk, bm, qn, kn, c, s, bp)
+    assert err == 7 and all(np.array_equal(o[i], qkv[i]) for i in (3, 5, 6))
+
+
+def test_pins_catch_planted_qk_mistakes():
+    """Plausible mistakes, planted in the torch pin on the CPU, change the
+    result: a wrong rotation pair, cos and sin swapped, k heads normalized
+    with the q weights, one norm over all heads, the cast-first norm."""
+    T, hq, hk, ld = 24, 2, 2, 4 * 128
+    case = _qk_case(T, hq, hk, ld, base=804)
+    _, out, _ = _oracle_qk(*case[:1], hq, hk, *case[1:])
+    for kw in (dict(pair=63), dict(swap_tables=True), dict(weights_of_k="q"), dict(whole_row=True),
+               dict(cast_first=True)):
+        assert not np.array_equal(_torch_qk(case[0], hq, hk, *case[1:], **kw), out), kw

@@ -13,6 +13,8 @@ explicit per-sample generator with fixed device, dtype and consumption order).
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 import torch
 
@@ -111,6 +113,21 @@ def norm_weights(H: int, base: int = 0):
     """Per-set RMSNorm weights ~ 1 + N(0, 0.1), bf16."""
     return (normal_bf16((H,), seed_of(base, 4), 0.1, 1.0),
             normal_bf16((H,), seed_of(base, 5), 0.1, 1.0))
+
+
+def qk_norm_weights(base: int = 0, head_dim: int = 128):
+    """Per-set QK norm weights ~ 1 + N(0, 0.1), bf16: ((q_und, q_gen), (k_und, k_gen))."""
+    return ((normal_bf16((head_dim,), seed_of(base, 11), 0.1, 1.0), normal_bf16((head_dim,), seed_of(base, 12), 0.1, 1.0)),
+            (normal_bf16((head_dim,), seed_of(base, 13), 0.1, 1.0), normal_bf16((head_dim,), seed_of(base, 14), 0.1, 1.0)))
+
+
+def rope_inputs(T: int, n_pos: int, base: int = 0, half: int = 64):
+    """Rotary tables and positions as data: cos and sin [n_pos, half] bf16 of
+    seeded phases uniform on [0, 2*pi) (rounded from fp64), and positions
+    [T] int32 uniform on [0, n_pos)."""
+    ph = torch.rand((n_pos, half), generator=_gen(seed_of(base, 15)), dtype=torch.float64) * (2 * math.pi)
+    pos = torch.randint(0, n_pos, (T,), generator=_gen(seed_of(base, 16)), dtype=torch.int64).to(torch.int32)
+    return ph.cos().to(torch.bfloat16), ph.sin().to(torch.bfloat16), pos
 
 
 def residual_inputs(T: int, H: int, base: int = 0):
