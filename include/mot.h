@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 3
+#define MOT_ABI_VERSION 4
 
 typedef enum mot_status {
     MOT_OK = 0,
@@ -52,7 +52,8 @@ typedef enum mot_status {
     MOT_ERR_MISALIGNED = 3,        /* a tensor pointer not 16-byte aligned, or a leading dimension not a multiple of 8 */
     MOT_ERR_WORKSPACE = 4,         /* workspace missing or smaller than mot_workspace_bytes(T) */
     MOT_ERR_DEVICE = 5,            /* a HIP runtime call or a kernel launch failed */
-    MOT_ERR_MODALITY = 6           /* a modality byte was neither 0 nor 1 (reported by mot_read_device_error) */
+    MOT_ERR_MODALITY = 6,          /* a modality byte was neither 0 nor 1 (reported by mot_read_device_error) */
+    MOT_ERR_POSITION = 7           /* a rotary position outside its table (reported by mot_read_device_error) */
 } mot_status;
 
 /* Limits checked on the host. */
@@ -193,8 +194,36 @@ int mot_transpose_bf16(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t 
                        const uint8_t *modality, int keep, uint16_t *out, int64_t ld_out,
                        int64_t rows_pad, void *stream);
 
+/* Routed per-head QK RMSNorm, then the rotary embedding, in place on the
+ * rows of the QKV projection's output: the "mot_qk_norm_rope" work item of
+ * the RL-Kernel RFC page (section 5), in the order its reference hazards fix
+ * (QK norm in fp32, then the rotation with Q/K in bf16).  Row t uses weight
+ * set m = modality[t]; each of its heads of 128 columns (q heads at columns
+ * [0, 128*n_q_heads), k heads right after; other columns untouched) becomes
+ *   rstd = 1/sqrt(mean_j(x_j^2) + eps),  y_j = bf16((x_j * rstd) * w[j])
+ *   with w the set's q or k norm weight, then, with c, s the row of
+ *   cos_table and sin_table at positions[t] (entry j mod 64):
+ *   out_j    = bf16(bf16(y_j * c_j)      + bf16(-y_{j+64} * s_j))   j < 64
+ *   out_j+64 = bf16(bf16(y_{j+64} * c_j) + bf16( y_j * s_j))
+ *   (rotate-half pairs; each bf16() one round-to-nearest-even).
+ *   qkv [T][ld] bf16, ld >= 128*(n_q_heads+n_k_heads), ld % 8 == 0;
+ *   qw_*, kw_* [128] bf16; positions [T] int32; cos_table, sin_table
+ *   [n_pos][64] bf16; device pointers, 16-byte aligned, none overlapping the
+ *   rows; eps > 0 and finite; workspace: at least MOT_WS_HEADER_BYTES, its
+ *   error word is cleared and then raised (MOT_ERR_MODALITY, MOT_ERR_POSITION;
+ *   the larger wins) for rows whose byte or position is invalid, which keep
+ *   their bytes.  The tables are data (cos and sin of the model's angles).
+ * Errors: MOT_ERR_INVALID_ARG, MOT_ERR_UNSUPPORTED_SHAPE, MOT_ERR_MISALIGNED,
+ * MOT_ERR_WORKSPACE, MOT_ERR_DEVICE.  T == 0 is a no-op. */
+int mot_qk_norm_rope(uint16_t *qkv, int64_t ld, int64_t T, int64_t n_q_heads, int64_t n_k_heads,
+                     const uint8_t *modality, const uint16_t *qw_und, const uint16_t *qw_gen,
+                     const uint16_t *kw_und, const uint16_t *kw_gen, const int32_t *positions,
+                     const uint16_t *cos_table, const uint16_t *sin_table, int64_t n_pos, float eps,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* Synchronises `stream` and returns the workspace's device error word:
- * MOT_OK, MOT_ERR_MODALITY, or MOT_ERR_DEVICE if the copy fails. */
+ * MOT_OK, MOT_ERR_MODALITY, MOT_ERR_POSITION, or MOT_ERR_DEVICE if the copy
+ * fails. */
 int mot_read_device_error(const void *workspace, void *stream);
 
 #ifdef __cplusplus

@@ -19,11 +19,11 @@ import torch
 __all__ = [
     "MotError", "ABI_VERSION", "lib", "abi_version", "workspace_bytes", "new_workspace",
     "routing_plan", "plan_view", "routed_gemm", "routed_gemm_swiglu", "fused_add_rmsnorm",
-    "transpose", "routed_gemm_dx", "grad_w",
+    "transpose", "routed_gemm_dx", "grad_w", "qk_norm_rope",
     "read_device_error", "status_string", "LIB_PATH",
 ]
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
 WS_HEADER_BYTES = 256
 FLAG_PLAN_READY = 1
@@ -35,12 +35,12 @@ TILE_FLAGS = {None: 0x00, "auto": 0x00, "256x256": 0x10, "128x128": 0x20}
 EXPORTS = (
     "mot_abi_version", "mot_status_string", "mot_workspace_bytes", "mot_routing_plan",
     "mot_routed_gemm", "mot_routed_gemm_swiglu", "mot_fused_add_rmsnorm", "mot_read_device_error",
-    "mot_transpose_bf16",
+    "mot_transpose_bf16", "mot_qk_norm_rope",
 )
 
 STATUS = {
     0: "MOT_OK", 1: "MOT_ERR_INVALID_ARG", 2: "MOT_ERR_UNSUPPORTED_SHAPE", 3: "MOT_ERR_MISALIGNED",
-    4: "MOT_ERR_WORKSPACE", 5: "MOT_ERR_DEVICE", 6: "MOT_ERR_MODALITY",
+    4: "MOT_ERR_WORKSPACE", 5: "MOT_ERR_DEVICE", 6: "MOT_ERR_MODALITY", 7: "MOT_ERR_POSITION",
 }
 
 
@@ -81,6 +81,8 @@ def lib():
     L.mot_read_device_error.argtypes = [P, P]
     L.mot_transpose_bf16.restype = ctypes.c_int
     L.mot_transpose_bf16.argtypes = [P, I64, I64, I64, P, ctypes.c_int, P, I64, I64, P]
+    L.mot_qk_norm_rope.restype = ctypes.c_int
+    L.mot_qk_norm_rope.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, P, P, I64, ctypes.c_float, P, SZ, P]
     v = L.mot_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"stale libmot.so: ABI {v}, binding expects {ABI_VERSION}; rebuild it")
@@ -306,3 +308,33 @@ def grad_w(dy, x, modality, keep=1):
     sets = torch.zeros(N, dtype=torch.uint8, device=dy.device)
     return routed_gemm(dyt, xt, xt, sets)
 
+
+def qk_norm_rope(qkv, n_q_heads, n_k_heads, modality, q_norm, k_norm, positions, cos_table, sin_table,
+                 eps=1e-6, workspace=None):
+    """In place on qkv [T, ld] bf16: per-head (128 columns) routed RMSNorm of
+    the q heads (columns [0, 128*n_q_heads)) and k heads (the next
+    128*n_k_heads), then the rotate-half rotary embedding in bf16.  q_norm,
+    k_norm: (und, gen) pairs of [128] bf16; positions [T] int32; cos_table,
+    sin_table [n_pos, 64] bf16.  Rows with an invalid modality byte or
+    position keep their bytes and raise the workspace's error word
+    (read_device_error).  Returns qkv."""
+    _req(qkv, "qkv", torch.bfloat16, 2)
+    if qkv.stride(1) != 1:
+        raise ValueError("qkv must have unit column stride")
+    T = qkv.shape[0]
+    _req(modality, "modality", torch.uint8, 1)
+    _req(positions, "positions", torch.int32, 1)
+    for t, name in ((cos_table, "cos_table"), (sin_table, "sin_table")):
+        _req(t, name, torch.bfloat16, 2)
+    if modality.shape[0] != T or positions.shape[0] != T:
+        raise ValueError("modality and positions need one entry per row")
+    if cos_table.shape != sin_table.shape or cos_table.shape[1] != 64:
+        raise ValueError("cos_table and sin_table must both be [n_pos, 64]")
+    ws = workspace if workspace is not None else new_workspace(0, qkv.device)
+    tensors = [modality.contiguous(), *(w.contiguous() for w in (*q_norm, *k_norm)), positions.contiguous(),
+               cos_table.contiguous(), sin_table.contiguous()]
+    st = lib().mot_qk_norm_rope(_ptr(qkv), qkv.stride(0), T, int(n_q_heads), int(n_k_heads),
+                                *(_ptr(t) for t in tensors), cos_table.shape[0], float(eps), _ptr(ws),
+                                ws.numel(), _stream(qkv.device))
+    _check(st, "mot_qk_norm_rope")
+    return qkv

@@ -170,6 +170,7 @@ const char *mot_status_string(int status) {
     case MOT_ERR_WORKSPACE: return "MOT_ERR_WORKSPACE: workspace missing or too small";
     case MOT_ERR_DEVICE: return "MOT_ERR_DEVICE: HIP runtime or launch failure";
     case MOT_ERR_MODALITY: return "MOT_ERR_MODALITY: modality byte not 0 or 1";
+    case MOT_ERR_POSITION: return "MOT_ERR_POSITION: position outside the rotary table";
     default: return "unknown mot_status";
     }
 }
@@ -261,6 +262,57 @@ int mot_transpose_bf16(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t 
     return mot::launch_transpose(in, ld_in, rows, cols, modality, keep, out, ld_out, rows_pad, s) == hipSuccess
                ? MOT_OK
                : MOT_ERR_DEVICE;
+}
+
+int mot_qk_norm_rope(uint16_t *qkv, int64_t ld, int64_t T, int64_t n_q_heads, int64_t n_k_heads,
+                     const uint8_t *modality, const uint16_t *qw_und, const uint16_t *qw_gen,
+                     const uint16_t *kw_und, const uint16_t *kw_gen, const int32_t *positions,
+                     const uint16_t *cos_table, const uint16_t *sin_table, int64_t n_pos, float eps,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    if (T < 0 || n_q_heads < 0 || n_k_heads < 0) return MOT_ERR_INVALID_ARG;
+    if (!(eps > 0.0f) || !isfinite(eps)) return MOT_ERR_INVALID_ARG;
+    if (T == 0) return MOT_OK;
+    if (!qkv || !modality || !qw_und || !qw_gen || !kw_und || !kw_gen || !positions || !cos_table ||
+        !sin_table)
+        return MOT_ERR_INVALID_ARG;
+    if (n_q_heads + n_k_heads == 0 || n_pos <= 0) return MOT_ERR_INVALID_ARG;
+    if (T > MOT_MAX_T || n_pos > MOT_MAX_T || 128 * (n_q_heads + n_k_heads) > MOT_MAX_DIM)
+        return MOT_ERR_UNSUPPORTED_SHAPE;
+    const int64_t cols = 128 * (n_q_heads + n_k_heads);
+    if (ld < cols) return MOT_ERR_INVALID_ARG;
+    if (ld % 8) return MOT_ERR_MISALIGNED;
+    if (!aligned16(qkv) || !aligned16(qw_und) || !aligned16(qw_gen) || !aligned16(kw_und) ||
+        !aligned16(kw_gen) || !aligned16(positions) || !aligned16(cos_table) || !aligned16(sin_table))
+        return MOT_ERR_MISALIGNED;
+    if (!workspace || workspace_bytes < MOT_WS_HEADER_BYTES) return MOT_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MOT_ERR_MISALIGNED;
+    // the rows are rewritten in place: no input may overlap them
+    const int64_t qkv_bytes = ((T - 1) * ld + cols) * 2;
+    const void *ins[] = {modality, qw_und, qw_gen, kw_und, kw_gen, positions, cos_table, sin_table, workspace};
+    const int64_t in_bytes[] = {T, 256, 256, 256, 256, 4 * T, 128 * n_pos, 128 * n_pos, 16};
+    for (int i = 0; i < 9; ++i)
+        if (overlaps(qkv, qkv_bytes, ins[i], in_bytes[i])) return MOT_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(s);
+    if (!guard.ok()) return MOT_ERR_DEVICE;
+    mot::QkArgs a;
+    a.qkv = qkv;
+    a.ld = ld;
+    a.T = T;
+    a.hq = (int)n_q_heads;
+    a.hk = (int)n_k_heads;
+    a.modality = modality;
+    a.qw_und = qw_und;
+    a.qw_gen = qw_gen;
+    a.kw_und = kw_und;
+    a.kw_gen = kw_gen;
+    a.positions = positions;
+    a.cos_t = cos_table;
+    a.sin_t = sin_table;
+    a.n_pos = (int)n_pos;
+    a.eps = eps;
+    a.err = static_cast<int32_t *>(workspace);
+    return mot::launch_qk_norm_rope(a, s) == hipSuccess ? MOT_OK : MOT_ERR_DEVICE;
 }
 
 int mot_read_device_error(const void *workspace, void *stream) {

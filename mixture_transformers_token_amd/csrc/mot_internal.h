@@ -47,11 +47,27 @@ struct GemmArgs {
     uint32_t y_bytes;     // extent of y from its base (bytes, < 4 GiB)
 };
 
+// Routed per-head QK RMSNorm + rotary embedding, in place on QKV rows.
+struct QkArgs {
+    uint16_t *qkv;        // [T][ld] bf16: q heads, then k heads, 128 columns each
+    int64_t ld;
+    int64_t T;
+    int hq, hk;           // q and k heads
+    const uint8_t *modality;
+    const uint16_t *qw_und, *qw_gen, *kw_und, *kw_gen;  // [128] bf16 norm weights
+    const int32_t *positions;                           // [T]
+    const uint16_t *cos_t, *sin_t;                      // [n_pos][64] bf16
+    int n_pos;
+    float eps;
+    int32_t *err;         // error word (cleared by the launch)
+};
+
 hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t *perm,
                        hipStream_t stream);
 // Launches the persistent routed GEMM (one workgroup per CU at most).  With
 // inline_route the kernel builds (and publishes) the segment list itself.
 hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStream_t stream);
+hipError_t launch_qk_norm_rope(const QkArgs &a, hipStream_t stream);
 hipError_t launch_transpose(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t cols,
                             const uint8_t *modality, int keep, uint16_t *out, int64_t ld_out,
                             int64_t rows_pad, hipStream_t stream);

@@ -12,6 +12,9 @@
 //                     over one workgroup per 32 output columns, all four
 //                     waves streaming weights (weight-bound).
 //  * norm_kernel   -- routed fused add-RMSNorm.
+//  * qk_norm_rope_kernel -- routed per-head QK RMSNorm, then the bf16 rotary
+//                     embedding, in place on the QKV rows.
+//  * transpose_kernel -- bf16 transpose (operands of the routed backward).
 //
 // Numerical contract (RL-Kernel RFC page "[RFC][BAGEL-7B-MoT] WS1/WS2 kernel
 // roadmap", section 3): one fixed fp32 accumulation order per output element,
@@ -1494,6 +1497,69 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
 }
 
 // ============================================================================
+// Routed per-head QK RMSNorm, then the rotary embedding (in place)
+// ============================================================================
+//
+// The "mot_qk_norm_rope" work item (RL-Kernel RFC page, section 5), in the
+// order the page's reference hazards fix: the QK norm in fp32, then the
+// rotation with Q/K in bf16.  One wave per (row, head of 128 columns): lane L
+// holds elements 2L and 2L+1 (lanes 0..31 the head's first half, 32..63 its
+// second), so each element's rotate-half partner (64 columns away) sits in
+// lane L ^ 32.  The head's sum of squares is x0^2 + x1^2 per lane, then an
+// xor-butterfly: one fixed tree.  y = bf16((x * rstd) * w_set) as in the layer
+// norm; then out = bf16(bf16(y * c) -+ bf16(y' * s)), where every product of
+// two bf16 values is exact in fp32 before its rounding.  Rows whose modality
+// byte or position is invalid keep their bytes and raise the error word
+// (atomic maximum, so the larger code wins whatever the order).
+
+constexpr int kErrPosition = 7;  // MOT_ERR_POSITION
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16_rne(float v) { return __uint_as_float(pack2(v, 0.0f) << 16); }
+
+__global__ void set_word_kernel(int32_t *p, int32_t v) {
+    if (threadIdx.x == 0) *p = v;
+}
+
+__global__ void __launch_bounds__(256) qk_norm_rope_kernel(QkArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int H = a.hq + a.hk;
+    const int64_t total = a.T * (int64_t)H;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < total; w += stride) {
+        const int64_t t = w / H;
+        const int h = (int)(w - t * H);
+        const uint32_t m = a.modality[t];
+        const int p = a.positions[t];
+        const bool bad_pos = p < 0 || p >= a.n_pos;
+        if (m > 1 || bad_pos) {
+            if (h == 0 && lane == 0) atomicMax(a.err, bad_pos ? kErrPosition : kErrModality);
+            continue;
+        }
+        uint32_t *const head = (uint32_t *)(a.qkv + t * a.ld + (int64_t)h * 128);
+        const uint32_t v = head[lane];
+        const float x0 = bf16_lo(v), x1 = bf16_hi(v);
+        float ss = x0 * x0 + x1 * x1;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+        const float rstd = 1.0f / sqrtf(ss / 128.0f + a.eps);
+        const uint16_t *wp = h < a.hq ? (m ? a.qw_gen : a.qw_und) : (m ? a.kw_gen : a.kw_und);
+        const uint32_t wv = ((const uint32_t *)wp)[lane];
+        const float y0 = bf16_rne(x0 * rstd * bf16_lo(wv));
+        const float y1 = bf16_rne(x1 * rstd * bf16_hi(wv));
+        const float z0 = __shfl_xor(y0, 32), z1 = __shfl_xor(y1, 32);
+        const int64_t ti = (int64_t)p * 64 + ((2 * lane) & 63);
+        const uint32_t cv = *(const uint32_t *)(a.cos_t + ti), sv = *(const uint32_t *)(a.sin_t + ti);
+        // first half: y*c - y'*s (y' 64 columns later); second half: y*c + y'*s
+        const float sg = lane < 32 ? -1.0f : 1.0f;
+        const float o0 = bf16_rne(bf16_rne(y0 * bf16_lo(cv)) + bf16_rne(sg * (z0 * bf16_lo(sv))));
+        const float o1 = bf16_rne(bf16_rne(y1 * bf16_hi(cv)) + bf16_rne(sg * (z1 * bf16_hi(sv))));
+        head[lane] = pack2(o0, o1);
+    }
+}
+
+// ============================================================================
 // Transpose (backward operands)
 // ============================================================================
 //
@@ -1629,6 +1695,16 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
                    : launch_gemm_t<true, false>(a, inline_route, grid, stream);
     return pro ? launch_gemm_t<false, true>(a, inline_route, grid, stream)
                : launch_gemm_t<false, false>(a, inline_route, grid, stream);
+}
+
+hipError_t launch_qk_norm_rope(const QkArgs &a, hipStream_t stream) {
+    hipLaunchKernelGGL(set_word_kernel, dim3(1), dim3(64), 0, stream, a.err, 0);
+    const int64_t waves = a.T * (int64_t)(a.hq + a.hk);
+    int64_t blocks = (waves + 3) / 4;
+    if (blocks > (1 << 20)) blocks = 1 << 20;  // the kernel strides over the rest
+    if (blocks > 0)
+        hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_transpose(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t cols,

@@ -167,3 +167,35 @@ def test_transpose_fails_closed(kw, code):
     st = mot.lib().mot_transpose_bf16(a["inp"], a["ld_in"], a["rows"], a["cols"], a["m"], a["keep"],
                                       a["out"], a["ld_out"], a["rows_pad"], None)
     assert st == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID),
+    (dict(T=0, qkv=None), OK),                # no-op
+    (dict(eps=0.0), INVALID),
+    (dict(eps=float("nan")), INVALID),
+    (dict(qkv=None), INVALID),
+    (dict(pos=None), INVALID),
+    (dict(kwg=None), INVALID),
+    (dict(hq=0, hk=0), INVALID),
+    (dict(hq=-1), INVALID),
+    (dict(n_pos=0), INVALID),
+    (dict(ld=4096 - 8), INVALID),             # ld shorter than the heads
+    (dict(ld=4612), MISALIGNED),
+    (dict(qkv=A + 4), MISALIGNED),
+    (dict(cos=9 * A + 2), MISALIGNED),
+    (dict(ws=None), WORKSPACE),
+    (dict(wsb=16), WORKSPACE),
+    (dict(ws=12 * A + 8), MISALIGNED),
+    (dict(pos=A + 4096), INVALID),            # positions inside the rows rewritten in place
+    (dict(hq=8192), SHAPE),
+    (dict(T=(1 << 24) + 1), SHAPE),
+])
+def test_qk_norm_rope_fails_closed(kw, code):
+    a = dict(qkv=A, ld=4608, T=64, hq=28, hk=4, m=2 * A, qwu=3 * A, qwg=4 * A, kwu=5 * A, kwg=6 * A,
+             pos=7 * A, cos=8 * A, sin=9 * A, n_pos=4096, eps=1e-6, ws=12 * A, wsb=256)
+    a.update(kw)
+    st = mot.lib().mot_qk_norm_rope(a["qkv"], a["ld"], a["T"], a["hq"], a["hk"], a["m"], a["qwu"], a["qwg"],
+                                    a["kwu"], a["kwg"], a["pos"], a["cos"], a["sin"], a["n_pos"], a["eps"],
+                                    a["ws"], a["wsb"], None)
+    assert st == code
