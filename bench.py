@@ -236,6 +236,23 @@ def main():
             "dw_gen_us": round(s_dw * 1e6, 1), "dw_gen_TFLOP/s": round(f_dw / s_dw / 1e12, 1),
             "dw_gen_rows": n_gen_rows(m)}
         del wt, dyd, dx
+        # routed per-head QK RMSNorm + rotary embedding, in place on the QKV
+        # output (28 q + 4 k heads of 128; rotary tables as data, 4096
+        # positions): HBM-bound, reads and writes the q and k columns
+        qn, kn = W.qk_norm_weights()
+        qn, kn = tuple(t.to(dev) for t in qn), tuple(t.to(dev) for t in kn)
+        cos_t, sin_t, pos = (t.to(dev) for t in W.rope_inputs(T, 4096))
+        qkv_buf = y.clone()
+        wsq = mot.new_workspace(0, dev)
+        s_qk = time_component(lambda: mot.qk_norm_rope(qkv_buf, W.N_Q_HEADS, W.N_K_HEADS, md, qn, kn, pos, cos_t,
+                                                       sin_t, workspace=wsq), iters, stream)
+        if mot.read_device_error(wsq) != 0:
+            raise RuntimeError("qk_norm_rope raised its error word")
+        qk_cols = 128 * (W.N_Q_HEADS + W.N_K_HEADS)
+        nb_qk = 2 * T * qk_cols * 2 + T * (1 + 4 + 2 * 64 * 2)
+        components["qk_norm_rope_T4096"] = {"us": round(s_qk * 1e6, 2), "GB/s": round(nb_qk / s_qk / 1e9, 1),
+                                            "frac_hbm": round(nb_qk / s_qk / 1e9 / PEAK_HBM_GBS, 3)}
+        del qkv_buf
         # context only: the vendor library's dense GEMM of one weight set at
         # the same shape (hipBLASLt via torch.matmul; not batch-invariant,
         # not a target)
@@ -273,9 +290,12 @@ def main():
             act_c = torch.empty((Tc, W.FFN), dtype=torch.bfloat16, device=dev)
             out_c = torch.empty((Tc, K), dtype=torch.bfloat16, device=dev)
             wsc = mot.new_workspace(Tc, dev)
+            cos_c, sin_c, pos_c = (t.to(dev) for t in W.rope_inputs(Tc, 4096, base=5))
             ops = {
                 "norm1": lambda: mot.fused_add_rmsnorm(xc, res_c, nwu, nwg, mcd, out=y1, rstd=None),
                 "qkv": lambda: mot.routed_gemm(y1, wud, wgd, mcd, out=qkv_c, workspace=wsc),
+                "qk_norm_rope": lambda: mot.qk_norm_rope(qkv_c, W.N_Q_HEADS, W.N_K_HEADS, mcd, qn, kn, pos_c, cos_c,
+                                                         sin_c, workspace=wsc),
                 "o": lambda: mot.routed_gemm(qkv_c[:, :W.Q_DIM], ou, og, mcd, out=o_c, workspace=wsc),
                 "norm2": lambda: mot.fused_add_rmsnorm(o_c, res_c, nwu, nwg, mcd, out=y1, rstd=None),
                 "gate_up_swiglu": lambda: mot.routed_gemm_swiglu(y1, gu_u, gu_g, mcd, out=act_c, workspace=wsc),

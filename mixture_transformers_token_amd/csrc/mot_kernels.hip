@@ -1502,21 +1502,29 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
 //
 // The "mot_qk_norm_rope" work item (RL-Kernel RFC page, section 5), in the
 // order the page's reference hazards fix: the QK norm in fp32, then the
-// rotation with Q/K in bf16.  One wave per (row, head of 128 columns): lane L
-// holds elements 2L and 2L+1 (lanes 0..31 the head's first half, 32..63 its
-// second), so each element's rotate-half partner (64 columns away) sits in
-// lane L ^ 32.  The head's sum of squares is x0^2 + x1^2 per lane, then an
-// xor-butterfly: one fixed tree.  y = bf16((x * rstd) * w_set) as in the layer
-// norm; then out = bf16(bf16(y * c) -+ bf16(y' * s)), where every product of
-// two bf16 values is exact in fp32 before its rounding.  Rows whose modality
-// byte or position is invalid keep their bytes and raise the error word
-// (atomic maximum, so the larger code wins whatever the order).
+// rotation with Q/K in bf16.  One wave per row and group of eight heads; a
+// group of 16 lanes covers one head of 128 columns (lane i of the group holds
+// elements 8i .. 8i+7), so one 16-byte load per lane covers four heads, and
+// the wave issues its data loads together with those of the row's modality
+// byte and position.  Each element's rotate-half partner (64
+// columns away) sits in lane i ^ 8 of the same group.  The head's sum of
+// squares is taken per lane over its 8 elements in order, then by an
+// xor-butterfly over the group's 16 lanes: one fixed tree.  y = bf16((x *
+// rstd) * w_set) as in the layer norm; then out = bf16(bf16(y * c) -+
+// bf16(y' * s)), where every product of two bf16 values is exact in fp32
+// before its rounding.  Rows whose modality byte or position is invalid keep
+// their bytes and raise the error word (atomic maximum, so the larger code
+// wins whatever the order).
 
 constexpr int kErrPosition = 7;  // MOT_ERR_POSITION
+constexpr int kQkChunks = 2;     // 4-head chunks per wave (8 heads)
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 __device__ __forceinline__ float bf16_rne(float v) { return __uint_as_float(pack2(v, 0.0f) << 16); }
+__device__ __forceinline__ float bf16_at(const u32x4_t &v, int e) {
+    return (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
+}
 
 __global__ void set_word_kernel(int32_t *p, int32_t v) {
     if (threadIdx.x == 0) *p = v;
@@ -1524,38 +1532,71 @@ __global__ void set_word_kernel(int32_t *p, int32_t v) {
 
 __global__ void __launch_bounds__(256) qk_norm_rope_kernel(QkArgs a) {
     const int lane = threadIdx.x & 63;
+    const int gi = lane & 15, grp = lane >> 4;  // lane in its 16-lane group, group = head within a chunk
     const int H = a.hq + a.hk;
-    const int64_t total = a.T * (int64_t)H;
-    const int64_t stride = (int64_t)gridDim.x * 4;
-    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < total; w += stride) {
-        const int64_t t = w / H;
-        const int h = (int)(w - t * H);
+    const int nch = (H + 3) / 4;                           // 4-head chunks per row
+    const int G = (nch + kQkChunks - 1) / kQkChunks;       // waves per row
+    const int64_t total = a.T * (int64_t)G;
+    for (int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); w < total; w += (int64_t)gridDim.x * 4) {
+        const int64_t t = w / G;
+        const int c0 = (int)(w - t * G) * kQkChunks;
+        uint16_t *const row = a.qkv + t * a.ld;
+        // the row's data first (in bounds whatever the row's byte), so that
+        // its loads overlap those of the modality byte and the position
+        u32x4_t v[kQkChunks];
+#pragma unroll
+        for (int c = 0; c < kQkChunks; ++c) {
+            const int h = 4 * (c0 + c) + grp;
+            if (c0 + c < nch && h < H) v[c] = *(const u32x4_t *)(row + (int64_t)h * 128 + 8 * gi);
+        }
         const uint32_t m = a.modality[t];
         const int p = a.positions[t];
         const bool bad_pos = p < 0 || p >= a.n_pos;
         if (m > 1 || bad_pos) {
-            if (h == 0 && lane == 0) atomicMax(a.err, bad_pos ? kErrPosition : kErrModality);
+            if (lane == 0 && c0 == 0) atomicMax(a.err, bad_pos ? kErrPosition : kErrModality);
             continue;
         }
-        uint32_t *const head = (uint32_t *)(a.qkv + t * a.ld + (int64_t)h * 128);
-        const uint32_t v = head[lane];
-        const float x0 = bf16_lo(v), x1 = bf16_hi(v);
-        float ss = x0 * x0 + x1 * x1;
+        const int64_t ti = (int64_t)p * 64 + 8 * (gi & 7);
+        const u32x4_t cv = *(const u32x4_t *)(a.cos_t + ti), sv = *(const u32x4_t *)(a.sin_t + ti);
+        const u32x4_t wq = *(const u32x4_t *)((m ? a.qw_gen : a.qw_und) + 8 * gi);
+        const u32x4_t wk = *(const u32x4_t *)((m ? a.kw_gen : a.kw_und) + 8 * gi);
+        // the rotation's sign: first half y*c - y'*s, second half y*c + y'*s
+        const float sg = gi < 8 ? -1.0f : 1.0f;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-        const float rstd = 1.0f / sqrtf(ss / 128.0f + a.eps);
-        const uint16_t *wp = h < a.hq ? (m ? a.qw_gen : a.qw_und) : (m ? a.kw_gen : a.kw_und);
-        const uint32_t wv = ((const uint32_t *)wp)[lane];
-        const float y0 = bf16_rne(x0 * rstd * bf16_lo(wv));
-        const float y1 = bf16_rne(x1 * rstd * bf16_hi(wv));
-        const float z0 = __shfl_xor(y0, 32), z1 = __shfl_xor(y1, 32);
-        const int64_t ti = (int64_t)p * 64 + ((2 * lane) & 63);
-        const uint32_t cv = *(const uint32_t *)(a.cos_t + ti), sv = *(const uint32_t *)(a.sin_t + ti);
-        // first half: y*c - y'*s (y' 64 columns later); second half: y*c + y'*s
-        const float sg = lane < 32 ? -1.0f : 1.0f;
-        const float o0 = bf16_rne(bf16_rne(y0 * bf16_lo(cv)) + bf16_rne(sg * (z0 * bf16_lo(sv))));
-        const float o1 = bf16_rne(bf16_rne(y1 * bf16_hi(cv)) + bf16_rne(sg * (z1 * bf16_hi(sv))));
-        head[lane] = pack2(o0, o1);
+        for (int c = 0; c < kQkChunks; ++c) {
+            if (c0 + c >= nch) break;  // wave-uniform
+            const int h = 4 * (c0 + c) + grp;
+            const bool live = h < H;
+            float ss = 0.0f;
+            if (live) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = bf16_at(v[c], e);
+                    ss = e == 0 ? x * x : ss + x * x;
+                }
+            }
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+            const float rstd = 1.0f / sqrtf(ss / 128.0f + a.eps);
+            const u32x4_t &wv = h < a.hq ? wq : wk;
+            u32x4_t y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                y[e] = pack2(bf16_lo(v[c][e]) * rstd * bf16_lo(wv[e]), bf16_hi(v[c][e]) * rstd * bf16_hi(wv[e]));
+            u32x4_t z;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] = (uint32_t)__shfl_xor((int)y[e], 8);
+            u32x4_t o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = bf16_rne(bf16_rne(bf16_lo(y[e]) * bf16_lo(cv[e])) +
+                                          bf16_rne(sg * (bf16_lo(z[e]) * bf16_lo(sv[e]))));
+                const float hi = bf16_rne(bf16_rne(bf16_hi(y[e]) * bf16_hi(cv[e])) +
+                                          bf16_rne(sg * (bf16_hi(z[e]) * bf16_hi(sv[e]))));
+                o[e] = pack2(lo, hi);
+            }
+            if (live) *(u32x4_t *)(row + (int64_t)h * 128 + 8 * gi) = o;
+        }
     }
 }
 
@@ -1699,8 +1740,8 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
 
 hipError_t launch_qk_norm_rope(const QkArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(set_word_kernel, dim3(1), dim3(64), 0, stream, a.err, 0);
-    const int64_t waves = a.T * (int64_t)(a.hq + a.hk);
-    int64_t blocks = (waves + 3) / 4;
+    const int64_t G = ((a.hq + a.hk + 3) / 4 + kQkChunks - 1) / kQkChunks;  // waves per row
+    int64_t blocks = (a.T * G + 3) / 4;
     if (blocks > (1 << 20)) blocks = 1 << 20;  // the kernel strides over the rest
     if (blocks > 0)
         hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);

@@ -26,6 +26,9 @@ HIDDEN = 3584
 Q_DIM = 3584
 KV_DIM = 512
 QKV_DIM = Q_DIM + 2 * KV_DIM  # 4608: q rows, then k rows, then v rows
+HEAD_DIM = 128
+N_Q_HEADS = Q_DIM // HEAD_DIM   # 28
+N_K_HEADS = KV_DIM // HEAD_DIM  # 4
 FFN = 18944
 
 # One BAGEL text-to-image packing unit: 77 prompt rows (und) then a 32x32
