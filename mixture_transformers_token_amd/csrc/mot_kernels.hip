@@ -205,6 +205,7 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
 constexpr int kBigM = 256, kBigN = 256, kSmallM = 128, kSmallN = 128;
+constexpr int kNarrowN = 64;  // weight rows of the narrow tiles (mid-size packs)
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -231,7 +232,8 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 // mode 1: big tiles only; mode 2: small tiles only.
 struct Schedule {
     int U, G;
-    int nwt, nws;  // weight tiles of 256 and of 128 rows
+    int nwt, nws;  // weight tiles of 256 and of sn rows
+    int sn;        // small tiles' weight rows: 128, or 64 (narrow mode)
     int bu, nbr;   // big row blocks: und, und + gen
     int nkeep;     // big tiles run as such
     int nleft;     // big tiles run as four small tiles each
@@ -240,12 +242,14 @@ struct Schedule {
     int ntiles;
 };
 
-__device__ __forceinline__ Schedule make_schedule(int U, int G, int wrows, int grid, int mode) {
+__device__ __forceinline__ Schedule make_schedule(int U, int G, int wrows, int grid, int mode,
+                                                   int sn = kSmallN) {
     Schedule s;
+    s.sn = sn;
     s.U = U;
     s.G = G;
     s.nwt = cdiv(wrows, kBigN);
-    s.nws = cdiv(wrows, kSmallN);
+    s.nws = cdiv(wrows, sn);
     if (mode == 2) {
         s.bu = s.nbr = 0;
     } else if (mode == 1) {
@@ -329,7 +333,7 @@ __device__ __forceinline__ Tile tile_of(const Schedule &s, int t) {
             ti.first = s.U + r0;
             ti.count = min(kSmallM, s.G - r0);
         }
-        ti.wrow0 = n * kSmallN;
+        ti.wrow0 = n * s.sn;
     }
     return ti;
 }
@@ -686,12 +690,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
     // Issue the next k-step's fragment reads over the first MFMAs of this
     // k-step (one read per MFMA), leaving the rest of the k-step to cover
     // their latency.
-    static_assert(NM >= MI + MJ, "more MFMAs than reads per k-step");
+    // (with fewer MFMAs than reads, as in 128x64 tiles, the last reads go
+    // without an MFMA of their own)
     auto interleave_reads = [&]() {
 #pragma unroll
         for (int i = 0; i < MI + MJ; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+            if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         }
         if constexpr (NM > MI + MJ)
             __builtin_amdgcn_sched_group_barrier(0x008, NM - (MI + MJ), 0);
@@ -1024,9 +1029,10 @@ __device__ __forceinline__ uint16_t *prologue_nw_lds() {
 // list and scan scratch; the prologue's big tiles run two stages of A in
 // array 0 or 2 and W in array 1 or 3, and its norm weights take 16 KiB).
 // Small tiles run four stages, one array each.
-template <bool SWIGLU, bool PRO, bool INLINE>
+template <bool SWIGLU, bool PRO, bool INLINE, bool NARROW = false>
 __global__ void __launch_bounds__(kThreads, 1)
 gemm_kernel(GemmArgs a) {
+    static_assert(!NARROW || (!SWIGLU && !PRO), "narrow tiles: plain GEMM only");
     constexpr int kArrayBytes = kBigM * kRowBytes;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kArrayBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kArrayBytes];
@@ -1066,7 +1072,8 @@ gemm_kernel(GemmArgs a) {
     const int wave_id = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     lds_u8 *const eb = (lds_u8 *)(wave_id == 0 ? lds0 : wave_id == 1 ? lds1 : wave_id == 2 ? lds2 : lds3);
     const int grid = (int)gridDim.x;
-    const Schedule sc = make_schedule(U, G, a.wrows, grid, a.tile_mode);
+    const Schedule sc = NARROW ? make_schedule(U, G, a.wrows, grid, 2, kNarrowN)
+                               : make_schedule(U, G, a.wrows, grid, a.tile_mode);
     // Static assignment.  Big tiles go round-robin (whole rounds, or one
     // partial round); small tiles (about a quarter of a big tile's work each)
     // go first to the workgroups that hold no big tile, up to four each, then
@@ -1109,7 +1116,14 @@ gemm_kernel(GemmArgs a) {
             if (ti.wrow0 == 0)
                 for (int i = threadIdx.x; i < ti.count; i += kThreads) a.perm_out[ti.first + i] = s_rows[i];
         }
-        if (ti.big) {
+        if constexpr (NARROW) {
+            // 128 x 64 tiles only (mode 2): twice the small tiles, for packs
+            // whose 128 x 128 tiles would leave most CUs idle
+            constexpr int kHalf = kSmallM * kRowBytes;
+            uint8_t *const xb[4] = {lds0, lds1, lds2, lds3};
+            uint8_t *const wb[4] = {lds0 + kHalf, lds1 + kHalf, lds2 + kHalf, lds3 + kHalf};
+            run_tile<kSmallM, kNarrowN, 4, false, false>(a, ti, xb, wb, eb, s_rows, s_nw, tid);
+        } else if (ti.big) {
             if constexpr (PRO) {
                 uint8_t *const xb[2] = {lds0, lds2}, *const wb[2] = {lds1, lds3};
                 run_tile<kBigM, kBigN, 2, SWIGLU, PRO>(a, ti, xb, wb, eb, s_rows, s_nw, tid);
@@ -1675,6 +1689,14 @@ hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t
 }
 
 namespace {
+hipError_t launch_gemm_narrow(const GemmArgs &a, bool inline_route, int grid, hipStream_t stream) {
+    if (inline_route)
+        hipLaunchKernelGGL((gemm_kernel<false, false, true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_kernel<false, false, false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <bool SWIGLU, bool PRO>
 hipError_t launch_gemm_t(const GemmArgs &a, bool inline_route, int grid, hipStream_t stream) {
     if (inline_route)
@@ -1728,6 +1750,12 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
     if (e != hipSuccess) return e;
     if (ncu <= 0) ncu = 1;
     const bool pro = a.rstd != nullptr;
+    // mid-size pack: when every 128-row block of both sets times 64-row
+    // weight blocks fits one tile per CU, 128 x 64 tiles put twice as many
+    // CUs to work on the weight stream as 128 x 128 ones
+    const int64_t narrow_tiles = ((a.T + kSmallM - 1) / kSmallM + 1) * ((a.wrows + kNarrowN - 1) / kNarrowN);
+    if (!swiglu && !pro && a.tile_mode == 0 && narrow_tiles <= ncu)
+        return launch_gemm_narrow(a, inline_route, (int)narrow_tiles, stream);
     const int64_t bound = gemm_tile_bound(a.T, a.wrows, ncu);
     const int grid = (int)(bound < ncu ? bound : ncu);
     if (grid <= 0) return hipSuccess;

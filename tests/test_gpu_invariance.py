@@ -167,3 +167,20 @@ def test_plan_ready_reuses_the_plan(qkv_setup):
     ws = mot.routing_plan(md)
     y = mot.routed_gemm(dev(s["x_probe"]), s["wu"], s["wg"], md, workspace=ws, plan_ready=True)
     assert raw_equal(y, s["ref"])
+
+
+@pytest.mark.parametrize("T,N", [(65, 4608), (200, 4608), (256, 4608), (300, 192), (1025, 320)])
+def test_narrow_tiles_match_wide_tile_bytes(T, N):
+    """Mid-size packs whose 128-row blocks times 64-row weight blocks fit one
+    tile per CU run 128 x 64 tiles; their bytes equal those of the 128 x 128
+    tiles (forced with a tile flag) row for row."""
+    m = W.pattern(T)
+    m[::3] = 1 - m[::3]
+    x = dev(W.normal_bf16((T, 512), 980 + T))
+    wu = dev(W.normal_bf16((N, 512), 981, 0.02))
+    wg = dev(W.normal_bf16((N, 512), 982, 0.02))
+    md = dev(torch.from_numpy(m))
+    auto = mot.routed_gemm(x, wu, wg, md)
+    wide = mot.routed_gemm(x, wu, wg, md, tile="128x128")
+    assert raw_equal(auto, wide)
+
