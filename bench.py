@@ -100,6 +100,20 @@ def time_calls(fn, iters, stream):
     return start.elapsed_time(end) / iters * 1e-3  # seconds
 
 
+def time_each(fn, n, stream):
+    """Per-launch durations (seconds) of n launches, an event pair around
+    each on the launch stream."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) * 1e-3 for a, b in ev)
+
+
 def time_component(fn, iters, stream, blocks=5, warmup=3):
     """Median over `blocks` blocks of `iters` launches (after `warmup`
     untimed launches) of the per-launch duration, HIP events on the stream."""
@@ -164,6 +178,8 @@ def main():
     # GEMM (segment list built in-kernel), timed with HIP events on its stream
     gemm_s = time_calls(step, max(args.steps, 50), stream)
     achieved = flops / gemm_s / 1e12
+    each = time_each(step, 100, stream)
+    pct = {f"p{q}": round(each[min(len(each) - 1, q * len(each) // 100)] * 1e6, 2) for q in (10, 50, 90)}
     n_und, n_gen = int((m == 0).sum()), int((m == 1).sum())
     traffic = measured_traffic()
     roofline = {
@@ -171,6 +187,7 @@ def main():
         "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
         "avg_kernel_us": round(gemm_s * 1e6, 2),
+        "launch_us_percentiles": pct,
         "flop_per_launch": flops,
         "alg_bytes_per_launch": 2 * (2 * N * K + T * K + T * N) + T,
     }
