@@ -131,7 +131,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
-              "routed projection is row-local and would shard by rows, see DESIGN.md", file=sys.stderr)
+              "routed projection is row-local and would shard by rows", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

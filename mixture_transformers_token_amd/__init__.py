@@ -59,8 +59,8 @@ def lib():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"libmot.so not built at {LIB_PATH}: run __graft_entry__.build() "
-                           "or python mixture_transformers_token_amd/build.py")
+        raise RuntimeError(f"libmot.so not built at {LIB_PATH}: "
+                           "run python mixture_transformers_token_amd/build.py")
     L = ctypes.CDLL(LIB_PATH)
     P, I64, SZ, U = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint
     L.mot_abi_version.restype = ctypes.c_int

@@ -36,7 +36,7 @@ def bits(t: torch.Tensor) -> np.ndarray:
 
 def check_parity(got_bits: np.ndarray, ref: np.ndarray, rne_bits: np.ndarray, what: str,
                  one_step: bool = True):
-    """The spec gate (max-abs / relative Frobenius, elementwise bf16 row
+    """The parity gate (max-abs / relative Frobenius, elementwise bf16 row
     where |ref| >= 8).  one_step additionally requires every output with
     |ref| >= 1/4 to be within one bf16 step of the correctly rounded oracle
     value; it applies to single ops, not to a chain where the oracle carries
