@@ -184,3 +184,19 @@ def test_narrow_tiles_match_wide_tile_bytes(T, N):
     wide = mot.routed_gemm(x, wu, wg, md, tile="128x128")
     assert raw_equal(auto, wide)
 
+
+
+@pytest.mark.parametrize("T", [40, 200])
+def test_plan_ready_small_and_mid_packs(T):
+    """A ready plan reused by the small-pack and the 128 x 64 tile paths
+    gives the bytes of the in-kernel segment list."""
+    m = W.pattern(T)
+    m[::4] = 1 - m[::4]
+    x = dev(W.normal_bf16((T, 512), 990 + T))
+    wu = dev(W.normal_bf16((4608, 512), 991, 0.02))
+    wg = dev(W.normal_bf16((4608, 512), 992, 0.02))
+    md = dev(torch.from_numpy(m))
+    inline = mot.routed_gemm(x, wu, wg, md)
+    ws = mot.routing_plan(md)
+    ready = mot.routed_gemm(x, wu, wg, md, workspace=ws, plan_ready=True)
+    assert raw_equal(ready, inline)
