@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-components", action="store_true")
+    p.add_argument("--only-small-packs", action="store_true",
+                   help="of the components, run only the small packs (for their rocprofv3 profile)")
     p.add_argument("--copy-probe", action="store_true",
                    help="run one 1 GiB device copy first (HBM counter calibration under rocprofv3)")
     p.add_argument("--cpu-rows", type=int, default=4096,
@@ -192,28 +194,9 @@ def main():
         "alg_bytes_per_launch": 2 * (2 * N * K + T * K + T * N) + T,
     }
 
-    # ---- other hot-path steps ------------------------------------------------
-    components = {}
-    if not args.no_components:
-        iters = 30
-        # routed fused add-RMSNorm, T=4096, H=3584 (x, residual in; residual, y out)
-        xs, rs = W.residual_inputs(T, K)
-        nwu, nwg = (t.to(dev) for t in W.norm_weights(K))
-        xsd, rsd = xs.to(dev), rs.to(dev)
-        yn = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
-        rstd = torch.empty(T, dtype=torch.float32, device=dev)
-        s_norm = time_component(lambda: mot.fused_add_rmsnorm(xsd, rsd, nwu, nwg, md, out=yn, rstd=rstd),
-                                iters, stream)
-        nbytes = 4 * T * K * 2 + T * 4 + T
-        components["fused_add_rmsnorm_T4096_H3584"] = {
-            "us": round(s_norm * 1e6, 2), "GB/s": round(nbytes / s_norm / 1e9, 1),
-            "frac_hbm": round(nbytes / s_norm / 1e9 / PEAK_HBM_GBS, 3)}
-        # QKV with the routed-RMSNorm prologue (reads h + rstd instead of y)
-        s_pro = time_component(lambda: mot.routed_gemm(rsd, wud, wgd, md, out=y, workspace=ws,
-                                                       norm=(rstd, nwu, nwg)), iters, stream)
-        components["qkv_prologue_T4096"] = {"us": round(s_pro * 1e6, 2),
-                                            "TFLOP/s": round(flops / s_pro / 1e12, 1)}
-        # small, weight-bound packs (HBM roofline): weights rotated over 8 copies
+    def small_packs(components):
+        """Small, weight-bound packs (HBM roofline) at the QKV shape, weights
+        rotated over four copies so that they come from HBM."""
         for Ts in (1, 64, 256):
             ms = W.pattern(Ts)
             xs_s = W.normal_bf16((Ts, K), 9).to(dev)
@@ -236,6 +219,31 @@ def main():
                                               "frac_hbm": round(nb / s_small / 1e9 / PEAK_HBM_GBS, 3),
                                               "sets": sets}
             del copies
+
+    # ---- other hot-path steps ------------------------------------------------
+    components = {}
+    if args.only_small_packs:
+        small_packs(components)
+    elif not args.no_components:
+        iters = 30
+        # routed fused add-RMSNorm, T=4096, H=3584 (x, residual in; residual, y out)
+        xs, rs = W.residual_inputs(T, K)
+        nwu, nwg = (t.to(dev) for t in W.norm_weights(K))
+        xsd, rsd = xs.to(dev), rs.to(dev)
+        yn = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+        rstd = torch.empty(T, dtype=torch.float32, device=dev)
+        s_norm = time_component(lambda: mot.fused_add_rmsnorm(xsd, rsd, nwu, nwg, md, out=yn, rstd=rstd),
+                                iters, stream)
+        nbytes = 4 * T * K * 2 + T * 4 + T
+        components["fused_add_rmsnorm_T4096_H3584"] = {
+            "us": round(s_norm * 1e6, 2), "GB/s": round(nbytes / s_norm / 1e9, 1),
+            "frac_hbm": round(nbytes / s_norm / 1e9 / PEAK_HBM_GBS, 3)}
+        # QKV with the routed-RMSNorm prologue (reads h + rstd instead of y)
+        s_pro = time_component(lambda: mot.routed_gemm(rsd, wud, wgd, md, out=y, workspace=ws,
+                                                       norm=(rstd, nwu, nwg)), iters, stream)
+        components["qkv_prologue_T4096"] = {"us": round(s_pro * 1e6, 2),
+                                            "TFLOP/s": round(flops / s_pro / 1e12, 1)}
+        small_packs(components)
         # routed backward of the QKV projection: dX = dY W_m on the
         # transposed weights (made once per weight update), and the generation
         # set's dW over its 3788 rows (two transposes + one routed GEMM over T)
