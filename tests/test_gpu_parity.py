@@ -210,6 +210,26 @@ def test_swiglu_small(T, K, F, tile):
     _swiglu_parity(x, wu, wg, m, tile=tile)
 
 
+@pytest.mark.parametrize("T", [1, 8, 20, 33, 64])
+@pytest.mark.parametrize("K", [192, 256])
+def test_swiglu_small_pack_kernel(T, K):
+    """SwiGLU packs of up to 64 rows (the small-pack kernel with 1, 4 or 8
+    A-row groups): parity with the oracle and the bytes of the tiled kernel
+    (forced with a tile flag)."""
+    F = 192
+    m = W.pattern(T)
+    m[::3] = 1 - m[::3]
+    x = W.normal_bf16((T, K), 1400 + T + K)
+    wu = W.normal_bf16((2 * F, K), 1401, 0.05)
+    wg = W.normal_bf16((2 * F, K), 1402, 0.05)
+    _swiglu_parity(x, wu, wg, m)
+    md = dev(torch.from_numpy(m))
+    small = mot.routed_gemm_swiglu(dev(x), dev(wu), dev(wg), md)
+    tiled = mot.routed_gemm_swiglu(dev(x), dev(wu), dev(wg), md, tile="128x128")
+    torch.cuda.synchronize()
+    assert torch.equal(small.view(torch.int16), tiled.view(torch.int16))
+
+
 def test_mlp_full_size_sampled():
     """BAGEL MLP: gate/up K=3584 -> 2x18944 + SwiGLU, then down 18944 -> 3584."""
     T = 4096
