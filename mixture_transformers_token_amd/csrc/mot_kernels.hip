@@ -206,6 +206,7 @@ __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) &
 
 constexpr int kBigM = 256, kBigN = 256, kSmallM = 128, kSmallN = 128;
 constexpr int kNarrowN = 64;  // weight rows of the narrow tiles (mid-size packs)
+constexpr int kPartialBigRows = 160;  // rows from which a partial row block is a big tile
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -228,7 +229,8 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 
 // The tile list, computed identically by every workgroup from the set sizes:
 // [nkeep big tiles][4*nleft quarter tiles][small tiles of the rows past the
-// big row blocks].  mode 0: big tiles for whole rounds, small for the rest;
+// big row blocks].  mode 0: big tiles (full row blocks, and a partial one of
+// at least kPartialBigRows rows) for whole rounds, small for the rest;
 // mode 1: big tiles only; mode 2: small tiles only.
 struct Schedule {
     int U, G;
@@ -256,8 +258,10 @@ __device__ __forceinline__ Schedule make_schedule(int U, int G, int wrows, int g
         s.bu = cdiv(U, kBigM);
         s.nbr = s.bu + cdiv(G, kBigM);
     } else {
-        s.bu = U / kBigM;
-        s.nbr = s.bu + G / kBigM;
+        // a set's partial row block runs as a big tile when it is mostly
+        // full (its 128 x 128 tiles would be as padded and less efficient)
+        s.bu = U / kBigM + (U % kBigM >= kPartialBigRows ? 1 : 0);
+        s.nbr = s.bu + G / kBigM + (G % kBigM >= kPartialBigRows ? 1 : 0);
     }
     const int nbig = s.nbr * s.nwt;
     s.nkeep = (mode == 0 && nbig >= grid) ? (nbig / grid) * grid : nbig;
