@@ -196,19 +196,20 @@ def main():
 
     def small_packs(components):
         """Small, weight-bound packs (HBM roofline) at the QKV shape, weights
-        rotated over four copies so that they come from HBM."""
+        rotated over eight copies of both sets (528 MB, twice the last-level
+        cache) so that they come from HBM."""
         for Ts in (1, 64, 256):
             ms = W.pattern(Ts)
             xs_s = W.normal_bf16((Ts, K), 9).to(dev)
             mds = torch.from_numpy(ms).to(dev)
             copies = [(W.normal_bf16((N, K), 90 + i, 0.02).to(dev), W.normal_bf16((N, K), 190 + i, 0.02).to(dev))
-                      for i in range(4)]
+                      for i in range(8)]
             ys = torch.empty((Ts, N), dtype=torch.bfloat16, device=dev)
             wss = mot.new_workspace(Ts, dev)
             ctr = [0]
 
             def small():
-                a, b = copies[ctr[0] % 4]
+                a, b = copies[ctr[0] % 8]
                 ctr[0] += 1
                 mot.routed_gemm(xs_s, a, b, mds, out=ys, workspace=wss)
             s_small = time_component(small, 40, stream)
