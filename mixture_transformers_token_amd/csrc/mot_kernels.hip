@@ -1268,9 +1268,8 @@ norm_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ residual,
 
 constexpr int kSkThreads = 256;
 constexpr int kSkLdsBytes = 152 * 1024;  // ring budget
-// Ring depth: measured best at 6 stages.  A stage is one 64-wide k-block,
-// or two for packs of up to 8 rows without SwiGLU (measured 10% faster there,
-// slower elsewhere: larger slots leave room for fewer workgroups).  The loads are not what bounds this
+// Ring depth: measured best at 6 stages of one 64-wide k-block (deeper
+// rings, and two-block stages, measured equal or slower).  The loads are not what bounds this
 // kernel (four waves stream the weights at HBM rate with 8 DMA in flight
 // each); the chain is: every output element takes K/16 dependent MFMAs.  A
 // shallower ring leaves LDS for a second workgroup per CU (packs that hold
@@ -1736,11 +1735,9 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
             else
                 hipLaunchKernelGGL((skinny_kernel<true, 8, 1>), grid, block, 0, stream, a, nblk, pub);
         } else {
-            if (a.T <= 8 && (a.K / kBK) % 2 == 0)
-                hipLaunchKernelGGL((skinny_kernel<false, 1, 2>), grid, block, 0, stream, a, nblk, pub);
-            else if (a.T <= 8)
-                hipLaunchKernelGGL((skinny_kernel<false, 1, 1>), grid, block, 0, stream, a, nblk, pub);
-            else if (a.T <= 32)
+            // packs of up to 8 rows measured faster with four A groups (all
+            // four waves loading A) than with one
+            if (a.T <= 32)
                 hipLaunchKernelGGL((skinny_kernel<false, 4, 1>), grid, block, 0, stream, a, nblk, pub);
             else
                 hipLaunchKernelGGL((skinny_kernel<false, 8, 1>), grid, block, 0, stream, a, nblk, pub);

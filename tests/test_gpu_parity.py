@@ -59,10 +59,9 @@ def test_ragged_packs(T):
 @pytest.mark.parametrize("T", [1, 5, 8, 9, 32, 40, 64])
 @pytest.mark.parametrize("K", [64, 128, 192, 320, 448])
 def test_small_pack_stage_sizes(T, K):
-    """Packs of up to 64 rows run the small-pack kernel, whose stages span one
-    or (for up to 8 rows and an even K / 64) two k-blocks: odd and even block
-    counts, parity with the oracle and the bytes of the tiled kernel (forced
-    with a tile flag) for the same rows."""
+    """Packs of up to 64 rows run the small-pack kernel (A-row groups of 4 or
+    8): odd and even k-block counts, parity with the oracle and the bytes of
+    the tiled kernel (forced with a tile flag) for the same rows."""
     m = W.pattern(T)
     m[::3] = 1 - m[::3]
     x, wu, wg, _ = W.gemm_case(T, K, 192, m, base=600 + T + K)
