@@ -11,9 +11,12 @@
  * section 1, item 1).  The numerical contract of the same page (section 3)
  * applies to every call: fixed fp32 accumulator and fixed reduction order, no
  * Split-K / Stream-K / atomics, no fast math, casts only at declared
- * boundaries, fail closed on unsupported geometry.  The three operations are
- * the page's "mot_routed_gemm", "mot_swiglu_mlp" (its gate/up + SwiGLU half)
- * and "mot_fused_add_rmsnorm" work items (section 5).
+ * boundaries, fail closed on unsupported geometry.  The operations are the
+ * page's "mot_routed_gemm", "mot_swiglu_mlp" (its gate/up + SwiGLU half),
+ * "mot_fused_add_rmsnorm" and "mot_qk_norm_rope" work items (section 5), and
+ * the transpose that prepares the routed backward's operands (section 1:
+ * Phase A trains the generation set, the frozen understanding operators still
+ * pass dX back).
  *
  * Conventions shared by every call
  *  - bf16 tensors are passed as uint16_t bit patterns; all tensors are
@@ -29,8 +32,9 @@
  *    the outputs are then untouched.  T == 0 is a no-op returning MOT_OK.
  *  - Calls that share a workspace must be ordered (same stream, or events).
  *
- * Result bytes are batch-invariant: each output row depends only on its own
- * input row, its modality byte and the weights, bit for bit, whatever the
+ * Result bytes of the row-wise calls (GEMMs, norm, QK norm + rotary) are
+ * batch-invariant: each output row depends only on its own input row, its
+ * modality byte (and position) and the weights, bit for bit, whatever the
  * pack's size, order or mix.
  */
 #ifndef MOT_H
