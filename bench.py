@@ -185,7 +185,7 @@ def main():
     n_und, n_gen = int((m == 0).sum()), int((m == 1).sum())
     traffic = measured_traffic()
     roofline = {
-        "kernel": "gemm_kernel<false,false,true,false> (routed QKV GEMM, in-kernel segment list)",
+        "kernel": "gemm_kernel<false,false,true,false,false> (routed QKV GEMM, in-kernel segment list)",
         "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
         "avg_kernel_us": round(gemm_s * 1e6, 2),
@@ -255,12 +255,15 @@ def main():
                               iters, stream)
         s_wt = time_component(lambda: mot.transpose(wgd), iters, stream)
         s_dw = time_component(lambda: mot.grad_w(dyd, xd, md, keep=1), 10, stream)
+        s_dw32 = time_component(lambda: mot.grad_w(dyd, xd, md, keep=1, out_dtype=torch.float32), 10, stream)
         f_dw = 2.0 * n_gen_rows(m) * N * K
         components["qkv_backward_T4096"] = {
             "dx_us": round(s_dx * 1e6, 1), "dx_TFLOP/s": round(flops / s_dx / 1e12, 1),
             "weight_transpose_us": round(s_wt * 1e6, 1),
             "dw_gen_us": round(s_dw * 1e6, 1), "dw_gen_TFLOP/s": round(f_dw / s_dw / 1e12, 1),
-            "dw_gen_rows": n_gen_rows(m)}
+            "dw_gen_fp32_us": round(s_dw32 * 1e6, 1), "dw_gen_fp32_TFLOP/s": round(f_dw / s_dw32 / 1e12, 1),
+            "dw_gen_rows": n_gen_rows(m),
+            "note": "dw_gen times include the two operand transposes (dY over all rows, X with und rows zeroed)"}
         del wt, dyd, dx
         # routed per-head QK RMSNorm + rotary embedding, in place on the QKV
         # output (28 q + 4 k heads of 128; rotary tables as data, 4096

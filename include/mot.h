@@ -13,7 +13,8 @@
  * Split-K / Stream-K / atomics, no fast math, casts only at declared
  * boundaries, fail closed on unsupported geometry.  The operations are the
  * page's "mot_routed_gemm", "mot_swiglu_mlp" (its gate/up + SwiGLU half),
- * "mot_fused_add_rmsnorm" and "mot_qk_norm_rope" work items (section 5), and
+ * "mot_fused_add_rmsnorm" and "mot_qk_norm_rope" work items (section 5), the
+ * routed GEMM's fp32 sums uncast (mot_routed_gemm_f32, for fp32 gradients), and
  * the transpose that prepares the routed backward's operands (section 1:
  * Phase A trains the generation set, the frozen understanding operators still
  * pass dX back).
@@ -47,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 4
+#define MOT_ABI_VERSION 5
 
 typedef enum mot_status {
     MOT_OK = 0,
@@ -132,6 +133,26 @@ int mot_routed_gemm(const uint16_t *x, int64_t ldx,
                     const float *rstd, const uint16_t *nw_und, const uint16_t *nw_gen,
                     void *workspace, size_t workspace_bytes,
                     unsigned flags, void *stream);
+
+/* Routed GEMM with fp32 output: the fp32 sums of mot_routed_gemm, before
+ * their bf16 cast (the bf16 output of mot_routed_gemm is bf16_rne of this
+ * one's, bit for bit).  It serves fp32 weight gradients for a master-weight
+ * optimizer: the RFC page (section 1) trains the generation expert while the
+ * understanding one stays frozen, and the MoE route/combine PR page folds
+ * weight gradients over rows in ascending order in fp32; with the operands of
+ * mot_transpose_bf16 below, this call returns that fp32 fold uncast.
+ *   y      [T][ldy] fp32, columns [0, N) written; ldy >= N, ldy % 8 == 0,
+ *          16-byte aligned; must not overlap x, the weights or the workspace.
+ *   flags  MOT_FLAG_PLAN_READY only (no tile override, no prologue): every
+ *          row block runs as a 256 x 256 tile.
+ * Other arguments and the errors as mot_routed_gemm.  Since ABI 5. */
+int mot_routed_gemm_f32(const uint16_t *x, int64_t ldx,
+                        const uint16_t *w_und, const uint16_t *w_gen,
+                        const uint8_t *modality,
+                        float *y, int64_t ldy,
+                        int64_t T, int64_t K, int64_t N,
+                        void *workspace, size_t workspace_bytes,
+                        unsigned flags, void *stream);
 
 /* Routed gate/up GEMM with the SwiGLU epilogue (the gate/up half of the MLP):
  *   g = sum_k A[t][k] * W_m[j][k],  u = sum_k A[t][k] * W_m[F + j][k]  (fp32),

@@ -6,8 +6,9 @@ provides device memory and the current stream.  There is no fallback: if
 libmot.so is missing or stale, every call raises.
 
 Functions mirror the C ABI:
-  routing_plan, routed_gemm, routed_gemm_swiglu, fused_add_rmsnorm,
-  read_device_error, workspace_bytes, abi_version.
+  routing_plan, routed_gemm, routed_gemm_f32, routed_gemm_swiglu,
+  fused_add_rmsnorm, transpose, qk_norm_rope, read_device_error,
+  workspace_bytes, abi_version; routed_gemm_dx and grad_w compose them.
 """
 from __future__ import annotations
 
@@ -18,12 +19,12 @@ import torch
 
 __all__ = [
     "MotError", "ABI_VERSION", "lib", "abi_version", "workspace_bytes", "new_workspace",
-    "routing_plan", "plan_view", "routed_gemm", "routed_gemm_swiglu", "fused_add_rmsnorm",
+    "routing_plan", "plan_view", "routed_gemm", "routed_gemm_f32", "routed_gemm_swiglu", "fused_add_rmsnorm",
     "transpose", "routed_gemm_dx", "grad_w", "qk_norm_rope",
     "read_device_error", "status_string", "LIB_PATH",
 ]
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
 WS_HEADER_BYTES = 256
 FLAG_PLAN_READY = 1
@@ -35,7 +36,7 @@ TILE_FLAGS = {None: 0x00, "auto": 0x00, "256x256": 0x10, "128x128": 0x20}
 EXPORTS = (
     "mot_abi_version", "mot_status_string", "mot_workspace_bytes", "mot_routing_plan",
     "mot_routed_gemm", "mot_routed_gemm_swiglu", "mot_fused_add_rmsnorm", "mot_read_device_error",
-    "mot_transpose_bf16", "mot_qk_norm_rope",
+    "mot_transpose_bf16", "mot_qk_norm_rope", "mot_routed_gemm_f32",
 )
 
 STATUS = {
@@ -73,6 +74,8 @@ def lib():
     L.mot_routing_plan.argtypes = [P, I64, P, SZ, P]
     L.mot_routed_gemm.restype = ctypes.c_int
     L.mot_routed_gemm.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64, P, P, P, P, SZ, U, P]
+    L.mot_routed_gemm_f32.restype = ctypes.c_int
+    L.mot_routed_gemm_f32.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64, P, SZ, U, P]
     L.mot_routed_gemm_swiglu.restype = ctypes.c_int
     L.mot_routed_gemm_swiglu.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64, P, P, P, P, SZ, U, P]
     L.mot_fused_add_rmsnorm.restype = ctypes.c_int
@@ -158,7 +161,8 @@ def plan_view(workspace: torch.Tensor, T: int):
     return hdr, perm
 
 
-def _routed(fn, name, x, w_und, w_gen, modality, out, norm, workspace, plan_ready, swiglu, tile):
+def _routed(fn, name, x, w_und, w_gen, modality, out, norm, workspace, plan_ready, swiglu, tile,
+            out_dtype=torch.bfloat16):
     _req(x, "x", torch.bfloat16, 2)
     _req(w_und, "w_und", torch.bfloat16, 2)
     _req(w_gen, "w_gen", torch.bfloat16, 2)
@@ -177,8 +181,8 @@ def _routed(fn, name, x, w_und, w_gen, modality, out, norm, workspace, plan_read
         raise ValueError("gate/up weights need an even number of rows")
     N = rows // 2 if swiglu else rows
     if out is None:
-        out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
-    _req(out, "out", torch.bfloat16, 2)
+        out = torch.empty((T, N), dtype=out_dtype, device=x.device)
+    _req(out, "out", out_dtype, 2)
     if tuple(out.shape) != (T, N):
         raise ValueError(f"out must be [{T}, {N}]")
     if workspace is None:
@@ -196,9 +200,16 @@ def _routed(fn, name, x, w_und, w_gen, modality, out, norm, workspace, plan_read
     if tile not in TILE_FLAGS:
         raise ValueError(f"tile must be one of {sorted(k for k in TILE_FLAGS if k)}")
     mod = modality.contiguous()
-    st = fn(_ptr(x), _rows(x, "x"), _ptr(w_und), _ptr(w_gen), _ptr(mod), _ptr(out), _rows(out, "out"),
-            T, K, N, _ptr(rstd), _ptr(nw_u), _ptr(nw_g), _ptr(workspace), workspace.numel(),
-            (FLAG_PLAN_READY if plan_ready else 0) | TILE_FLAGS[tile], _stream(x.device))
+    flags = (FLAG_PLAN_READY if plan_ready else 0) | TILE_FLAGS[tile]
+    if out_dtype == torch.float32:
+        if norm is not None or TILE_FLAGS[tile]:
+            raise ValueError("fp32 output: no prologue and no tile override")
+        st = fn(_ptr(x), _rows(x, "x"), _ptr(w_und), _ptr(w_gen), _ptr(mod), _ptr(out), _rows(out, "out"),
+                T, K, N, _ptr(workspace), workspace.numel(), flags, _stream(x.device))
+    else:
+        st = fn(_ptr(x), _rows(x, "x"), _ptr(w_und), _ptr(w_gen), _ptr(mod), _ptr(out), _rows(out, "out"),
+                T, K, N, _ptr(rstd), _ptr(nw_u), _ptr(nw_g), _ptr(workspace), workspace.numel(),
+                flags, _stream(x.device))
     _check(st, name)
     return out
 
@@ -210,6 +221,13 @@ def routed_gemm(x, w_und, w_gen, modality, out=None, norm=None, workspace=None, 
     tile: None (library's choice) or "256x256" / "128x128" (force one tile shape)."""
     return _routed(lib().mot_routed_gemm, "mot_routed_gemm", x, w_und, w_gen, modality, out, norm,
                    workspace, plan_ready, swiglu=False, tile=tile)
+
+
+def routed_gemm_f32(x, w_und, w_gen, modality, out=None, workspace=None, plan_ready=False):
+    """The routed GEMM's fp32 sums, uncast: y[t] = x[t] @ W_{modality[t]}^T in
+    fp32 (routed_gemm returns bf16_rne of exactly these values)."""
+    return _routed(lib().mot_routed_gemm_f32, "mot_routed_gemm_f32", x, w_und, w_gen, modality, out, None,
+                   workspace, plan_ready, False, None, out_dtype=torch.float32)
 
 
 def routed_gemm_swiglu(x, wgu_und, wgu_gen, modality, out=None, norm=None, workspace=None,
@@ -294,9 +312,10 @@ def routed_gemm_dx(dy, w_und, w_gen, modality, wt=None, out=None, workspace=None
     return routed_gemm(dy, wt[0], wt[1], modality, out=out, workspace=workspace)
 
 
-def grad_w(dy, x, modality, keep=1):
+def grad_w(dy, x, modality, keep=1, out_dtype=torch.bfloat16):
     """dW[n][k] = sum over rows t with modality[t] == keep of dY[t][n] * X[t][k]
-    (fp32, rows folded in ascending order in 16-row chunks), as bf16 [N, K]."""
+    (fp32, rows folded in ascending order in 16-row chunks), as [N, K] in
+    out_dtype: bf16 (one cast) or fp32 (the sums themselves)."""
     _req(dy, "dy", torch.bfloat16, 2)
     _req(x, "x", torch.bfloat16, 2)
     T, N = dy.shape
@@ -306,6 +325,10 @@ def grad_w(dy, x, modality, keep=1):
     dyt = transpose(dy, rows_pad=Tp)
     xt = transpose(x, modality=modality, keep=keep, rows_pad=Tp)
     sets = torch.zeros(N, dtype=torch.uint8, device=dy.device)
+    if out_dtype == torch.float32:
+        return routed_gemm_f32(dyt, xt, xt, sets)
+    if out_dtype != torch.bfloat16:
+        raise ValueError("grad_w: out_dtype must be torch.bfloat16 or torch.float32")
     return routed_gemm(dyt, xt, xt, sets)
 
 

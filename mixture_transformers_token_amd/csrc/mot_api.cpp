@@ -64,7 +64,7 @@ struct RoutedCall {
     int64_t ldx;
     const uint16_t *w_und, *w_gen;
     const uint8_t *modality;
-    uint16_t *y;
+    void *y;
     int64_t ldy;
     int64_t T, K, N;       // N: output columns (F for SwiGLU)
     int64_t w_rows;        // rows of each weight matrix (N, or 2F)
@@ -73,6 +73,7 @@ struct RoutedCall {
     void *workspace;
     size_t workspace_bytes;
     unsigned flags;
+    int out_f32 = 0;       // 1: y is fp32 [T][ldy]
 };
 
 int validate_routed(const RoutedCall &c) {
@@ -90,6 +91,7 @@ int validate_routed(const RoutedCall &c) {
     if (npro != 0 && npro != 3) return MOT_ERR_INVALID_ARG;
     if (npro == 3 && c.K > mot::kMaxPrologueK) return MOT_ERR_UNSUPPORTED_SHAPE;
     if ((c.flags & MOT_FLAG_TILE_MASK) == MOT_FLAG_TILE_MASK) return MOT_ERR_INVALID_ARG;
+    if (c.out_f32 && (npro != 0 || (c.flags & MOT_FLAG_TILE_MASK) != 0)) return MOT_ERR_INVALID_ARG;
     if (!aligned16(c.x) || !aligned16(c.w_und) || !aligned16(c.w_gen) || !aligned16(c.y))
         return MOT_ERR_MISALIGNED;
     if (npro == 3 && (!aligned16(c.nw_und) || !aligned16(c.nw_gen) ||
@@ -98,7 +100,7 @@ int validate_routed(const RoutedCall &c) {
     if (!c.workspace || c.workspace_bytes < ws_bytes(c.T)) return MOT_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(c.workspace) & (kWsAlign - 1)) != 0) return MOT_ERR_MISALIGNED;
     const int64_t x_bytes = ((c.T - 1) * c.ldx + c.K) * 2;
-    const int64_t y_bytes = ((c.T - 1) * c.ldy + c.N) * 2;
+    const int64_t y_bytes = ((c.T - 1) * c.ldy + c.N) * (c.out_f32 ? 4 : 2);
     if (overlaps(c.x, x_bytes, c.y, y_bytes)) return MOT_ERR_INVALID_ARG;
     const int64_t w_bytes = c.w_rows * c.K * 2;
     if (overlaps(c.w_und, w_bytes, c.y, y_bytes) || overlaps(c.w_gen, w_bytes, c.y, y_bytes))
@@ -150,7 +152,8 @@ int run_routed(const RoutedCall &c, bool swiglu, void *stream) {
     }
     a.x_bytes = (uint32_t)(((c.T - 1) * c.ldx + c.K) * 2);
     a.w_bytes = (uint32_t)(c.w_rows * c.K * 2);
-    a.y_bytes = (uint32_t)(((c.T - 1) * c.ldy + c.N) * 2);
+    a.y_bytes = (uint32_t)(((c.T - 1) * c.ldy + c.N) * (c.out_f32 ? 4 : 2));
+    a.out_f32 = c.out_f32;
     if (mot::launch_gemm(a, swiglu, inline_route, s) != hipSuccess) return MOT_ERR_DEVICE;
     return MOT_OK;
 }
@@ -199,6 +202,14 @@ int mot_routed_gemm(const uint16_t *x, int64_t ldx, const uint16_t *w_und, const
                     void *workspace, size_t workspace_bytes, unsigned flags, void *stream) {
     RoutedCall c{x, ldx, w_und, w_gen, modality, y, ldy, T, K, N, N,
                  rstd, nw_und, nw_gen, workspace, workspace_bytes, flags};
+    return run_routed(c, false, stream);
+}
+
+int mot_routed_gemm_f32(const uint16_t *x, int64_t ldx, const uint16_t *w_und, const uint16_t *w_gen,
+                        const uint8_t *modality, float *y, int64_t ldy, int64_t T, int64_t K, int64_t N,
+                        void *workspace, size_t workspace_bytes, unsigned flags, void *stream) {
+    RoutedCall c{x, ldx, w_und, w_gen, modality, y, ldy, T, K, N, N,
+                 nullptr, nullptr, nullptr, workspace, workspace_bytes, flags, 1};
     return run_routed(c, false, stream);
 }
 

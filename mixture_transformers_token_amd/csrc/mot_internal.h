@@ -26,7 +26,7 @@ struct GemmArgs {
     int64_t ldx;
     const uint16_t *w_und;
     const uint16_t *w_gen;
-    uint16_t *y;
+    void *y;              // bf16 output, or fp32 when out_f32
     int64_t ldy;
     const uint8_t *modality;  // [T]; read by the in-kernel segment list
     const int32_t *hdr;   // workspace header: error, n_und, n_gen, T
@@ -45,6 +45,7 @@ struct GemmArgs {
     uint32_t x_bytes;     // extent of x from its base (bytes, < 4 GiB)
     uint32_t w_bytes;     // extent of one weight matrix (bytes, < 4 GiB)
     uint32_t y_bytes;     // extent of y from its base (bytes, < 4 GiB)
+    int out_f32;          // 1: y is fp32 (plain GEMM, 256 x 256 tiles only)
 };
 
 // Routed per-head QK RMSNorm + rotary embedding, in place on QKV rows.

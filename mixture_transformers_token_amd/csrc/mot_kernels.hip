@@ -804,9 +804,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
 // it first.  The epilogue stores straight from the accumulators (8-byte
 // pieces, default cache policy); measured faster here than staging through
 // LDS, which would need the row list rebuilt.
-template <bool SWIGLU>
+template <bool SWIGLU, bool F32 = false>
 __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint8_t *const (&hs)[5],
                                          const int32_t *s_rows, const int tid) {
+    static_assert(!(SWIGLU && F32), "fp32 output: plain GEMM only");
+    constexpr uint32_t kOutBytes = F32 ? 4u : 2u;  // bytes per output element
     constexpr int BM = kBigM, BN = kBigN;
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int MJ = WM / 32, MI = WN / 32;
@@ -854,7 +856,7 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
 #pragma unroll
         for (int j = 0; j < MJ; ++j) {
             const int mloc = wm * WM + j * 32 + rsel;
-            yoff[j] = mloc < ti.count ? (uint32_t)s_rows[mloc] * (uint32_t)a.ldy * 2u : kNoRow;
+            yoff[j] = mloc < ti.count ? (uint32_t)s_rows[mloc] * (uint32_t)a.ldy * kOutBytes : kNoRow;
         }
     }
 
@@ -1002,9 +1004,17 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
                             v[e] = acc[i][j][4 * q + e];
                         }
                     }
-                    const u32x2_t pk = {pack2(v[0], v[1]), pack2(v[2], v[3])};
-                    __builtin_amdgcn_raw_buffer_store_b64(pk, yr, yoff[j] + (uint32_t)(n0 + q * 8 + khalf * 4) * 2u,
-                                                          0, 0);
+                    if constexpr (F32) {
+                        // the fp32 accumulators themselves: 16 bytes per store
+                        const u32x4_t pk = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                            __float_as_uint(v[3])};
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            pk, yr, yoff[j] + (uint32_t)(n0 + q * 8 + khalf * 4) * 4u, 0, 0);
+                    } else {
+                        const u32x2_t pk = {pack2(v[0], v[1]), pack2(v[2], v[3])};
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            pk, yr, yoff[j] + (uint32_t)(n0 + q * 8 + khalf * 4) * 2u, 0, 0);
+                    }
                 }
             }
         }
@@ -1033,10 +1043,11 @@ __device__ __forceinline__ uint16_t *prologue_nw_lds() {
 // list and scan scratch; the prologue's big tiles run two stages of A in
 // array 0 or 2 and W in array 1 or 3, and its norm weights take 16 KiB).
 // Small tiles run four stages, one array each.
-template <bool SWIGLU, bool PRO, bool INLINE, bool NARROW = false>
+template <bool SWIGLU, bool PRO, bool INLINE, bool NARROW = false, bool F32 = false>
 __global__ void __launch_bounds__(kThreads, 1)
 gemm_kernel(GemmArgs a) {
     static_assert(!NARROW || (!SWIGLU && !PRO), "narrow tiles: plain GEMM only");
+    static_assert(!F32 || (!SWIGLU && !PRO && !NARROW), "fp32 output: plain GEMM, big tiles only");
     constexpr int kArrayBytes = kBigM * kRowBytes;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kArrayBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kArrayBytes];
@@ -1076,8 +1087,10 @@ gemm_kernel(GemmArgs a) {
     const int wave_id = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     lds_u8 *const eb = (lds_u8 *)(wave_id == 0 ? lds0 : wave_id == 1 ? lds1 : wave_id == 2 ? lds2 : lds3);
     const int grid = (int)gridDim.x;
+    // fp32 output runs 256 x 256 tiles only (mode 1: every row block,
+    // partial ones included, is a big tile; no small tiles)
     const Schedule sc = NARROW ? make_schedule(U, G, a.wrows, grid, 2, kNarrowN)
-                               : make_schedule(U, G, a.wrows, grid, a.tile_mode);
+                               : make_schedule(U, G, a.wrows, grid, F32 ? 1 : a.tile_mode);
     // Static assignment.  Big tiles go round-robin (whole rounds, or one
     // partial round); small tiles (about a quarter of a big tile's work each)
     // go first to the workgroups that hold no big tile, up to four each, then
@@ -1133,9 +1146,9 @@ gemm_kernel(GemmArgs a) {
                 run_tile<kBigM, kBigN, 2, SWIGLU, PRO>(a, ti, xb, wb, eb, s_rows, s_nw, tid);
             } else {
                 uint8_t *const hs[5] = {lds0, lds1, lds2, lds3, lds4};
-                run_big5<SWIGLU>(a, ti, hs, s_rows, tid);
+                run_big5<SWIGLU, F32>(a, ti, hs, s_rows, tid);
             }
-        } else {
+        } else if constexpr (!F32) {  // (mode 1 schedules no small tiles)
             constexpr int kHalf = kSmallM * kRowBytes;
             uint8_t *const xb[4] = {lds0, lds1, lds2, lds3};
             uint8_t *const wb[4] = {lds0 + kHalf, lds1 + kHalf, lds2 + kHalf, lds3 + kHalf};
@@ -1692,6 +1705,14 @@ hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t
 }
 
 namespace {
+hipError_t launch_gemm_f32(const GemmArgs &a, bool inline_route, int grid, hipStream_t stream) {
+    if (inline_route)
+        hipLaunchKernelGGL((gemm_kernel<false, false, true, false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_kernel<false, false, false, false, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_narrow(const GemmArgs &a, bool inline_route, int grid, hipStream_t stream) {
     if (inline_route)
         hipLaunchKernelGGL((gemm_kernel<false, false, true, true>), dim3(grid), dim3(kThreads), 0, stream, a);
@@ -1721,6 +1742,17 @@ int64_t gemm_tile_bound(int64_t T, int64_t wrows, int ncu) {
 }
 
 hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStream_t stream) {
+    if (a.out_f32) {
+        // fp32 output: 256 x 256 tiles for every row block, one workgroup per CU
+        int dev = 0, ncu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (ncu <= 0) ncu = 1;
+        const int64_t tiles = ((a.T + kBigM - 1) / kBigM + 1) * ((a.wrows + kBigN - 1) / kBigN);
+        return launch_gemm_f32(a, inline_route, (int)(tiles < ncu ? tiles : ncu), stream);
+    }
     if (a.T <= kSkinnyMaxT && a.rstd == nullptr && a.tile_mode == 0) {
         // small pack: weight-bound path, one workgroup per 32 output columns
         // and set; XG = A row groups of 8 that cover the pack

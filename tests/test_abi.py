@@ -97,6 +97,40 @@ def test_gemm_fails_closed(kw, code):
     assert _gemm(**kw) == code
 
 
+def _gemm_f32(**kw):
+    args = dict(x=A, ldx=256, wu=2 * A, wg=3 * A, m=4 * A, y=5 * A, ldy=384, T=64, K=256, N=384,
+                ws=6 * A, wsb=1 << 20, flags=0)
+    args.update(kw)
+    return mot.lib().mot_routed_gemm_f32(args["x"], args["ldx"], args["wu"], args["wg"], args["m"],
+                                         args["y"], args["ldy"], args["T"], args["K"], args["N"],
+                                         args["ws"], args["wsb"], args["flags"], None)
+
+
+G = 1 << 36  # far-apart fake addresses for the large-extent case
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID),
+    (dict(T=0, y=None), OK),
+    (dict(y=None), INVALID),
+    (dict(wu=None), INVALID),
+    (dict(N=96, ldy=128), SHAPE),
+    (dict(ldy=388), MISALIGNED),
+    (dict(y=5 * A + 8), MISALIGNED),
+    (dict(wsb=300), WORKSPACE),
+    (dict(flags=0x10), INVALID),              # no tile override
+    (dict(flags=0x20), INVALID),
+    (dict(flags=2), INVALID),
+    # the fp32 extent (64 rows x 384 x 4 bytes) reaches w_und; half of it would not
+    (dict(y=2 * A - 64 * 384 * 4 + 256), INVALID),
+    # 2^20 rows x 1024 fp32 columns = 4 GiB: past the 32-bit byte offsets
+    (dict(x=G, wu=2 * G, wg=3 * G, m=4 * G, y=5 * G, ws=6 * G, T=1 << 20, N=1024, ldy=1024,
+          wsb=1 << 23), SHAPE),
+])
+def test_gemm_f32_fails_closed(kw, code):
+    assert _gemm_f32(**kw) == code
+
+
 def test_swiglu_fails_closed():
     L = mot.lib()
     # F not a multiple of 64
