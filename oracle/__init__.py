@@ -63,6 +63,9 @@ def lib():
         L.mot_oracle_qk_norm_rope.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, P, P, I64,
                                               ctypes.c_float, P, P, ctypes.c_int]
         L.mot_oracle_qk_norm_rope.restype = ctypes.c_int
+        L.mot_oracle_attention.argtypes = [P, I64, I64, P, I64, P, I64, I64, I64, I64, I64, ctypes.c_int,
+                                           P, I64, P, P, ctypes.c_int]
+        L.mot_oracle_attention.restype = None
         _lib = L
     return _lib
 
@@ -238,3 +241,21 @@ def gate_metrics(got_bits: np.ndarray, ref: np.ndarray) -> dict:
         "max_ref": float(np.max(np.abs(ref))) if ref.size else 0.0,
         "max_ulp_to_rne": int(np.max(ulp_distance(got_bits, rne))) if rne is not None and rne.size else None,
     }
+
+
+def attention(q, k, v, hq, hkv, causal, rows=None, head_dim=128, threads=0):
+    """q [Tq, ldq], k [Tk, ldk], v [Tk, ldv] uint16 (the heads' columns first)
+    -> (ref f64 [n, hq*D], out u16 [n, hq*D]) for the query rows `rows`
+    (default: all): shared joint attention, bottom-right causal when causal."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    Tq, Tk = q.shape[0], k.shape[0]
+    assert v.shape[0] == Tk and hq % hkv == 0
+    assert q.shape[1] >= hq * head_dim and k.shape[1] >= hkv * head_dim and v.shape[1] >= hkv * head_dim
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = Tq if r is None else r.size
+    ref = np.empty((n, hq * head_dim), np.float64)
+    out = np.empty((n, hq * head_dim), np.uint16)
+    if n:
+        lib().mot_oracle_attention(_p(q), q.shape[1], Tq, _p(k), k.shape[1], _p(v), v.shape[1], Tk, hq, hkv,
+                                   head_dim, int(causal), _p(r), n, _p(ref), _p(out), threads)
+    return ref, out

@@ -36,6 +36,11 @@
  *    work item; the RFC page's reference hazards: QK norm in fp32, then the
  *    rotation and Q/K in bf16): see mot_oracle_qk_norm_rope.  Its bf16
  *    roundings are part of the definition, so it rounds where the page does.
+ *  - Shared joint attention (the "gen_joint_attention" work item, same page,
+ *    section 5): softmax(q k^T / sqrt(D)) v over the pack's tokens of both
+ *    modalities, not routed, with grouped kv heads and an optional causal
+ *    mask aligned at the bottom-right corner (the page's reference hazards:
+ *    a cached prefill needs that alignment).  See mot_oracle_attention.
  *
  * Every floating-point step is done in fp64 and rounded to bf16 exactly once,
  * directly from fp64 (no fp32 step), so the oracle is the exact result up to
@@ -44,6 +49,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #ifdef _OPENMP
@@ -364,4 +370,69 @@ int mot_oracle_qk_norm_rope(const uint16_t *qkv, int64_t ld, int64_t T, int64_t 
         }
     }
     return err;
+}
+
+/* ---- shared joint attention ---------------------------------------------- */
+
+/* Attention of query row i, q head h (kv head g = h / (hq / hkv); the heads'
+ * columns are [h*D, (h+1)*D) of q and [g*D, (g+1)*D) of k and v):
+ *   s_j = (sum_d q[i][h*D+d] * k[j][g*D+d]) / sqrt(D)   for each visible key j,
+ *   out[i][h*D+d] = sum_j (exp(s_j - max s) / sum_j' exp(s_j' - max s)) * v[j][g*D+d].
+ * Visible keys: every j < Tk when causal == 0; when causal == 1, the mask is
+ * aligned at the bottom-right corner: query i sees keys j <= i + (Tk - Tq)
+ * (so with Tq == Tk it is the usual causal mask, and the last query sees
+ * every key).  A query that sees no key gets zeros.  fp64 throughout, one
+ * bf16 rounding of the result.
+ * rows (may be NULL = rows 0..nrows-1): the query rows to compute; ref and
+ * out (either may be NULL) are [nrows][hq*D]. */
+void mot_oracle_attention(const uint16_t *q, int64_t ldq, int64_t Tq,
+                          const uint16_t *k, int64_t ldk, const uint16_t *v, int64_t ldv, int64_t Tk,
+                          int64_t hq, int64_t hkv, int64_t D, int causal,
+                          const int64_t *rows, int64_t nrows, double *ref, uint16_t *out, int nthreads)
+{
+    set_threads(nthreads);
+    const double scale = 1.0 / sqrt((double)D);
+    const int64_t group = hq / hkv;
+    const int64_t width = hq * D;
+#pragma omp parallel
+    {
+        double *p = (double *)malloc((size_t)(Tk > 0 ? Tk : 1) * sizeof(double));
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int64_t r = 0; r < nrows; ++r) {
+            for (int64_t h = 0; h < hq; ++h) {
+                const int64_t i = rows ? rows[r] : r;
+                const int64_t g = h / group;
+                int64_t last = causal ? i + (Tk - Tq) : Tk - 1;
+                if (last > Tk - 1)
+                    last = Tk - 1;
+                const uint16_t *qi = q + i * ldq + h * D;
+                double mx = -INFINITY;
+                for (int64_t j = 0; j <= last; ++j) {
+                    const uint16_t *kj = k + j * ldk + g * D;
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d)
+                        dot += bf16_value(qi[d]) * bf16_value(kj[d]);
+                    p[j] = dot * scale;
+                    if (p[j] > mx)
+                        mx = p[j];
+                }
+                double den = 0.0;
+                for (int64_t j = 0; j <= last; ++j) {
+                    p[j] = exp(p[j] - mx);
+                    den += p[j];
+                }
+                for (int64_t d = 0; d < D; ++d) {
+                    double num = 0.0;
+                    for (int64_t j = 0; j <= last; ++j)
+                        num += p[j] * bf16_value(v[j * ldv + g * D + d]);
+                    const double val = last >= 0 ? num / den : 0.0;
+                    if (ref)
+                        ref[r * width + h * D + d] = val;
+                    if (out)
+                        out[r * width + h * D + d] = bf16_round(val);
+                }
+            }
+        }
+        free(p);
+    }
 }

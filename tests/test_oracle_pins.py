@@ -581,3 +581,101 @@ def test_pins_catch_planted_qk_mistakes():
     for kw in (dict(pair=63), dict(swap_tables=True), dict(weights_of_k="q"), dict(whole_row=True),
                dict(cast_first=True)):
         assert not np.array_equal(_torch_qk(case[0], hq, hk, *case[1:], **kw), out), kw
+
+
+# ---- shared joint attention ------------------------------------------------------
+
+
+def _attn_case(Tq, Tk, hq, hkv, base, extra=64, q_std=1.0):
+    D = 128
+    q = _bf((Tq, hq * D + extra), W.seed_of(base, 1), q_std)
+    k = _bf((Tk, hkv * D + extra), W.seed_of(base, 2))
+    v = _bf((Tk, hkv * D + extra), W.seed_of(base, 3))
+    return q, k, v
+
+
+def _torch_attention(q, k, v, hq, hkv, causal, align="bottom_right", kv_map="group", scale=True):
+    """The op from library routines: torch's fp64 scaled_dot_product_attention
+    with an explicit boolean mask and the kv heads repeated per group.  The
+    keyword arguments plant plausible mistakes."""
+    D = 128
+    Tq, Tk = q.shape[0], k.shape[0]
+    Q = torch.from_numpy(oracle.bf16_to_f64(q[:, :hq * D])).view(Tq, hq, D).transpose(0, 1)
+    K = torch.from_numpy(oracle.bf16_to_f64(k[:, :hkv * D])).view(Tk, hkv, D).transpose(0, 1)
+    V = torch.from_numpy(oracle.bf16_to_f64(v[:, :hkv * D])).view(Tk, hkv, D).transpose(0, 1)
+    idx = torch.arange(hq) // (hq // hkv) if kv_map == "group" else torch.arange(hq) % hkv
+    K, V = K[idx], V[idx]
+    i = torch.arange(Tq)[:, None]
+    j = torch.arange(Tk)[None, :]
+    if not causal:
+        mask = torch.ones((Tq, Tk), dtype=torch.bool)
+    elif align == "bottom_right":
+        mask = j <= i + (Tk - Tq)
+    else:
+        mask = j <= i
+    out = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask,
+                                                           scale=None if scale else 1.0)
+    return out.transpose(0, 1).reshape(Tq, hq * D).numpy()
+
+
+@pytest.mark.parametrize("Tq,Tk,causal", [(37, 90, True), (50, 50, True), (50, 50, False), (1, 64, True),
+                                          (70, 33, False)])
+def test_attention_matches_torch_sdpa(Tq, Tk, causal):
+    """Grouped heads (4 q, 2 kv), extra columns past the heads, a cached
+    prefix (Tk > Tq): the oracle equals torch's fp64 attention to rounding,
+    and its bf16 output is the RNE rounding of its fp64 result."""
+    q, k, v = _attn_case(Tq, Tk, 4, 2, base=900 + Tq)
+    ref, out = oracle.attention(q, k, v, 4, 2, causal)
+    want = _torch_attention(q, k, v, 4, 2, causal)
+    assert np.abs(ref - want).max() <= 1e-12
+    rows = [0, Tq - 1]
+    for r in rows:
+        for c in (0, 129, 511):
+            assert out[r, c] == oracle.bf16_round(ref[r, c])
+
+
+def test_attention_closed_forms():
+    """q = 0: uniform weights, so each row is the mean of the V rows it sees.
+    The first row of a square causal pack sees key 0 only: V's row 0 exactly.
+    Rows that see no key (Tq > Tk, causal) are zero.  A key whose score
+    dwarfs the others takes all the weight."""
+    D = 128
+    Tq, Tk = 6, 9
+    q = np.zeros((Tq, 2 * D), np.uint16)
+    k = _bf((Tk, D), 911)
+    v = _bf((Tk, D), 912)
+    ref, _ = oracle.attention(q, k, v, 2, 1, True)
+    V = oracle.bf16_to_f64(v)
+    for i in range(Tq):
+        want = V[:i + Tk - Tq + 1].mean(0)
+        assert np.abs(ref[i, :D] - want).max() <= 1e-14 and np.abs(ref[i, D:] - want).max() <= 1e-14
+    q2, k2, v2 = _attn_case(8, 8, 1, 1, base=913)
+    _, out2 = oracle.attention(q2, k2, v2, 1, 1, True)
+    assert np.array_equal(out2[0], v2[0, :D])
+    # Tq = 5 queries over 3 keys, bottom-right: rows 0 and 1 see nothing
+    q3, k3, v3 = _attn_case(5, 3, 1, 1, base=914)
+    ref3, out3 = oracle.attention(q3, k3, v3, 1, 1, True)
+    assert not ref3[:2].any() and not out3[:2].any()
+    assert np.array_equal(out3[2], v3[0, :D])
+    # dominance: the query is 8x key 1 and keys 0 and 2 are zero, so key 1's
+    # score exceeds theirs by about 90 and their weights are below 1e-38
+    K4 = torch.from_numpy(oracle.bf16_to_f64(k3[:, :D]))
+    qd = np.zeros((1, D), np.uint16)
+    qd[0] = W.bits((8 * K4[1]).to(torch.bfloat16)[None])[0]
+    kb = k3.copy()
+    kb[0, :D] = 0
+    kb[2, :D] = 0
+    refd, _ = oracle.attention(qd, kb, v3, 1, 1, False)
+    assert np.abs(refd[0] - oracle.bf16_to_f64(v3[1, :D])).max() <= 1e-9
+
+
+def test_pins_catch_planted_attention_mistakes():
+    """Plausible mistakes, planted in the torch pin on the CPU, move it far
+    from the oracle: a top-left aligned causal mask, kv heads taken round
+    robin instead of in groups, no 1/sqrt(D) scale, no mask at all."""
+    q, k, v = _attn_case(24, 56, 4, 2, base=920)
+    ref, _ = oracle.attention(q, k, v, 4, 2, True)
+    assert np.abs(ref - _torch_attention(q, k, v, 4, 2, True)).max() <= 1e-12
+    for kw in (dict(align="top_left"), dict(kv_map="round_robin"), dict(scale=False)):
+        assert np.abs(ref - _torch_attention(q, k, v, 4, 2, True, **kw)).max() > 1e-2, kw
+    assert np.abs(ref - _torch_attention(q, k, v, 4, 2, False)).max() > 1e-2
