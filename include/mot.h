@@ -14,7 +14,8 @@
  * boundaries, fail closed on unsupported geometry.  The operations are the
  * page's "mot_routed_gemm", "mot_swiglu_mlp" (its gate/up + SwiGLU half),
  * "mot_fused_add_rmsnorm" and "mot_qk_norm_rope" work items (section 5), the
- * routed GEMM's fp32 sums uncast (mot_routed_gemm_f32, for fp32 gradients), and
+ * routed GEMM's fp32 sums uncast (mot_routed_gemm_f32, for fp32 gradients), the
+ * shared attention of both sets ("gen_joint_attention", section 5), and
  * the transpose that prepares the routed backward's operands (section 1:
  * Phase A trains the generation set, the frozen understanding operators still
  * pass dX back).
@@ -48,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 5
+#define MOT_ABI_VERSION 6
 
 typedef enum mot_status {
     MOT_OK = 0,
@@ -250,6 +251,44 @@ int mot_qk_norm_rope(uint16_t *qkv, int64_t ld, int64_t T, int64_t n_q_heads, in
  * MOT_OK, MOT_ERR_MODALITY, MOT_ERR_POSITION, or MOT_ERR_DEVICE if the copy
  * fails. */
 int mot_read_device_error(const void *workspace, void *stream);
+
+/* Workspace bytes of mot_joint_attention: the transposed V of the kv heads,
+ * n_kv_heads * 128 rows of round_up(Tk, 64) bf16 (0 when Tk == 0).  Since
+ * ABI 6. */
+size_t mot_attention_workspace_bytes(int64_t Tk, int64_t n_kv_heads);
+
+/* Shared joint attention: the "gen_joint_attention" work item of the RFC
+ * page (section 5).  Both weight sets share it, so it is not routed: every
+ * query row of the pack attends over the same keys, of both modalities.
+ * For query row i and q head h, with kv head g = h / (n_q_heads / n_kv_heads):
+ *   s_j = fp32 sum_d q[i][128h+d] * k[j][128g+d], times the fp32 rounding of
+ *         1/sqrt(128), for each key j that row i sees;
+ *   out[i][128h+d] = bf16_rne( sum_j p_j v[j][128g+d] / sum_j p_j ),
+ *         p_j = expf(s_j - max s), accumulated over blocks of 64 keys from
+ *         key 0 upwards with an online (running max) softmax in fp32; the
+ *         p_j enter the products with v as bf16.
+ * Visible keys: all Tk when causal == 0.  With causal == 1 the mask is
+ * aligned at the bottom-right corner, as the same page's reference hazards
+ * require for a cached prefill: row i sees keys j <= i + (Tk - Tq).  A row
+ * that sees no key gets zeros.  One accumulation order per element, no
+ * split over keys (the page's section 3); a row's bytes depend only on its
+ * q row, the keys it sees and the v rows, not on the other rows of the pack.
+ *   q   [Tq][ldq] bf16, heads at columns [0, 128*n_q_heads); ldq % 8 == 0.
+ *   k, v [Tk][ldk], [Tk][ldv] bf16, kv heads at columns [0, 128*n_kv_heads)
+ *        (q, k and v may be column ranges of one QKV buffer).
+ *   out [Tq][ldo] bf16, columns [0, 128*n_q_heads) written; must not overlap
+ *        q, k, v or the workspace.
+ *   head_dim == 128; n_q_heads % n_kv_heads == 0; n_q_heads <= 256;
+ *   Tq, Tk <= MOT_MAX_T; causal 0 or 1; pointers 16-byte aligned.
+ *   workspace: >= mot_attention_workspace_bytes(Tk, n_kv_heads) bytes,
+ *        16-byte aligned, overwritten (not needed when Tk == 0).
+ * Errors: MOT_ERR_INVALID_ARG, MOT_ERR_UNSUPPORTED_SHAPE, MOT_ERR_MISALIGNED,
+ * MOT_ERR_WORKSPACE, MOT_ERR_DEVICE.  Tq == 0 is a no-op.  Since ABI 6. */
+int mot_joint_attention(const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk,
+                        const uint16_t *v, int64_t ldv, uint16_t *out, int64_t ldo,
+                        int64_t Tq, int64_t Tk, int64_t n_q_heads, int64_t n_kv_heads,
+                        int64_t head_dim, int causal, void *workspace, size_t workspace_bytes,
+                        void *stream);
 
 #ifdef __cplusplus
 }

@@ -7,7 +7,7 @@ libmot.so is missing or stale, every call raises.
 
 Functions mirror the C ABI:
   routing_plan, routed_gemm, routed_gemm_f32, routed_gemm_swiglu,
-  fused_add_rmsnorm, transpose, qk_norm_rope, read_device_error,
+  fused_add_rmsnorm, transpose, qk_norm_rope, joint_attention, read_device_error,
   workspace_bytes, abi_version; routed_gemm_dx and grad_w compose them.
 """
 from __future__ import annotations
@@ -20,11 +20,12 @@ import torch
 __all__ = [
     "MotError", "ABI_VERSION", "lib", "abi_version", "workspace_bytes", "new_workspace",
     "routing_plan", "plan_view", "routed_gemm", "routed_gemm_f32", "routed_gemm_swiglu", "fused_add_rmsnorm",
-    "transpose", "routed_gemm_dx", "grad_w", "qk_norm_rope",
+    "transpose", "routed_gemm_dx", "grad_w", "qk_norm_rope", "joint_attention",
+    "attention_workspace_bytes",
     "read_device_error", "status_string", "LIB_PATH",
 ]
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
 WS_HEADER_BYTES = 256
 FLAG_PLAN_READY = 1
@@ -36,7 +37,8 @@ TILE_FLAGS = {None: 0x00, "auto": 0x00, "256x256": 0x10, "128x128": 0x20}
 EXPORTS = (
     "mot_abi_version", "mot_status_string", "mot_workspace_bytes", "mot_routing_plan",
     "mot_routed_gemm", "mot_routed_gemm_swiglu", "mot_fused_add_rmsnorm", "mot_read_device_error",
-    "mot_transpose_bf16", "mot_qk_norm_rope", "mot_routed_gemm_f32",
+    "mot_transpose_bf16", "mot_qk_norm_rope", "mot_routed_gemm_f32", "mot_attention_workspace_bytes",
+    "mot_joint_attention",
 )
 
 STATUS = {
@@ -86,6 +88,11 @@ def lib():
     L.mot_transpose_bf16.argtypes = [P, I64, I64, I64, P, ctypes.c_int, P, I64, I64, P]
     L.mot_qk_norm_rope.restype = ctypes.c_int
     L.mot_qk_norm_rope.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, P, P, I64, ctypes.c_float, P, SZ, P]
+    L.mot_attention_workspace_bytes.restype = SZ
+    L.mot_attention_workspace_bytes.argtypes = [I64, I64]
+    L.mot_joint_attention.restype = ctypes.c_int
+    L.mot_joint_attention.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, I64, I64, ctypes.c_int, P,
+                                      SZ, P]
     v = L.mot_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"stale libmot.so: ABI {v}, binding expects {ABI_VERSION}; rebuild it")
@@ -361,3 +368,38 @@ def qk_norm_rope(qkv, n_q_heads, n_k_heads, modality, q_norm, k_norm, positions,
                                 ws.numel(), _stream(qkv.device))
     _check(st, "mot_qk_norm_rope")
     return qkv
+
+
+def attention_workspace_bytes(Tk: int, n_kv_heads: int) -> int:
+    return int(lib().mot_attention_workspace_bytes(int(Tk), int(n_kv_heads)))
+
+
+def joint_attention(q, k, v, n_q_heads, n_kv_heads, causal=True, out=None, workspace=None):
+    """Shared joint attention over the pack (both modalities, not routed):
+    out[i] = softmax(q_i k^T / sqrt(128)) v per q head, kv heads shared by
+    groups of n_q_heads / n_kv_heads; causal: row i sees keys
+    j <= i + (Tk - Tq) (bottom-right aligned).  q [Tq, >= 128 hq], k and v
+    [Tk, >= 128 hkv] bf16 row-major views (column ranges of one QKV buffer
+    are fine).  Returns out [Tq, 128 hq] bf16."""
+    _req(q, "q", torch.bfloat16, 2)
+    _req(k, "k", torch.bfloat16, 2)
+    _req(v, "v", torch.bfloat16, 2)
+    Tq, Tk = q.shape[0], k.shape[0]
+    if v.shape[0] != Tk:
+        raise ValueError("k and v must have the same rows")
+    width = 128 * int(n_q_heads)
+    if q.shape[1] < width or k.shape[1] < 128 * int(n_kv_heads) or v.shape[1] < 128 * int(n_kv_heads):
+        raise ValueError("q, k or v narrower than its heads")
+    if out is None:
+        out = torch.empty((Tq, width), dtype=torch.bfloat16, device=q.device)
+    _req(out, "out", torch.bfloat16, 2)
+    if out.shape[0] != Tq or out.shape[1] < width:
+        raise ValueError(f"out must be [{Tq}, >= {width}]")
+    if workspace is None:
+        workspace = torch.empty(max(attention_workspace_bytes(Tk, n_kv_heads), 16), dtype=torch.uint8,
+                                device=q.device)
+    st = lib().mot_joint_attention(_ptr(q), _rows(q, "q"), _ptr(k), _rows(k, "k"), _ptr(v), _rows(v, "v"),
+                                   _ptr(out), _rows(out, "out"), Tq, Tk, int(n_q_heads), int(n_kv_heads), 128,
+                                   1 if causal else 0, _ptr(workspace), workspace.numel(), _stream(q.device))
+    _check(st, "mot_joint_attention")
+    return out

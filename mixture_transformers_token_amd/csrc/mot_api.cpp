@@ -55,6 +55,14 @@ class DeviceGuard {
     bool switched_ = false;
 };
 
+constexpr int64_t kAttnHeadDim = 128;
+constexpr int64_t kAttnMaxHeads = 256;
+
+size_t attn_ws_bytes(int64_t Tk, int64_t hkv) {
+    if (Tk <= 0 || hkv <= 0) return 0;
+    return (size_t)(hkv * kAttnHeadDim * round_up(Tk, 64) * 2);
+}
+
 size_t ws_bytes(int64_t T) {
     return (size_t)(MOT_WS_HEADER_BYTES + round_up(4 * (T > 0 ? T : 0), kWsAlign));
 }
@@ -273,6 +281,63 @@ int mot_transpose_bf16(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t 
     return mot::launch_transpose(in, ld_in, rows, cols, modality, keep, out, ld_out, rows_pad, s) == hipSuccess
                ? MOT_OK
                : MOT_ERR_DEVICE;
+}
+
+size_t mot_attention_workspace_bytes(int64_t Tk, int64_t n_kv_heads) {
+    return attn_ws_bytes(Tk, n_kv_heads);
+}
+
+int mot_joint_attention(const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk, const uint16_t *v,
+                        int64_t ldv, uint16_t *out, int64_t ldo, int64_t Tq, int64_t Tk, int64_t n_q_heads,
+                        int64_t n_kv_heads, int64_t head_dim, int causal, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    if (Tq < 0 || Tk < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads)
+        return MOT_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return MOT_ERR_INVALID_ARG;
+    if (Tq == 0) return MOT_OK;
+    if (head_dim != kAttnHeadDim || n_q_heads > kAttnMaxHeads) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (Tq > MOT_MAX_T || Tk > MOT_MAX_T) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (!q || !out || (Tk > 0 && (!k || !v))) return MOT_ERR_INVALID_ARG;
+    const int64_t qw = n_q_heads * kAttnHeadDim, kw = n_kv_heads * kAttnHeadDim;
+    if (ldq < qw || ldo < qw || (Tk > 0 && (ldk < kw || ldv < kw))) return MOT_ERR_INVALID_ARG;
+    if (ldq % 8 || ldo % 8 || (Tk > 0 && (ldk % 8 || ldv % 8))) return MOT_ERR_MISALIGNED;
+    if (!aligned16(q) || !aligned16(out) || (Tk > 0 && (!aligned16(k) || !aligned16(v))))
+        return MOT_ERR_MISALIGNED;
+    const size_t wsb = attn_ws_bytes(Tk, n_kv_heads);
+    if (Tk > 0 && (!workspace || workspace_bytes < wsb)) return MOT_ERR_WORKSPACE;
+    if (Tk > 0 && !aligned16(workspace)) return MOT_ERR_MISALIGNED;
+    const int64_t q_bytes = ((Tq - 1) * ldq + qw) * 2, o_bytes = ((Tq - 1) * ldo + qw) * 2;
+    if (overlaps(out, o_bytes, q, q_bytes)) return MOT_ERR_INVALID_ARG;
+    if (Tk > 0) {
+        const int64_t k_bytes = ((Tk - 1) * ldk + kw) * 2, v_bytes = ((Tk - 1) * ldv + kw) * 2;
+        if (overlaps(out, o_bytes, k, k_bytes) || overlaps(out, o_bytes, v, v_bytes) ||
+            overlaps(out, o_bytes, workspace, (int64_t)wsb) || overlaps(workspace, (int64_t)wsb, q, q_bytes) ||
+            overlaps(workspace, (int64_t)wsb, k, k_bytes) || overlaps(workspace, (int64_t)wsb, v, v_bytes))
+            return MOT_ERR_INVALID_ARG;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(s);
+    if (!guard.ok()) return MOT_ERR_DEVICE;
+    const int64_t tk_pad = round_up(Tk, 64);
+    uint16_t *vt = static_cast<uint16_t *>(workspace);
+    if (Tk > 0 && mot::launch_transpose(v, ldv, Tk, kw, nullptr, 1, vt, tk_pad, tk_pad, s) != hipSuccess)
+        return MOT_ERR_DEVICE;
+    mot::AttnArgs a;
+    a.q = q;
+    a.ldq = ldq;
+    a.k = k;
+    a.ldk = ldk;
+    a.vt = vt;
+    a.ldvt = tk_pad;
+    a.out = out;
+    a.ldo = ldo;
+    a.Tq = Tq;
+    a.Tk = Tk;
+    a.hq = (int)n_q_heads;
+    a.hkv = (int)n_kv_heads;
+    a.causal = causal;
+    a.scale = (float)(1.0 / sqrt((double)kAttnHeadDim));
+    return mot::launch_attention(a, s) == hipSuccess ? MOT_OK : MOT_ERR_DEVICE;
 }
 
 int mot_qk_norm_rope(uint16_t *qkv, int64_t ld, int64_t T, int64_t n_q_heads, int64_t n_k_heads,

@@ -1,0 +1,222 @@
+// Shared joint attention (gfx950): the attention that the two weight sets
+// share.  The RL-Kernel RFC page "[RFC][BAGEL-7B-MoT][CUDA/ROCm] WS1/WS2
+// kernel roadmap and integration plan" lists it as the "gen_joint_attention"
+// work item (section 5); its reference hazards (section 2) note that a
+// cached prefill needs a causal mask aligned at the bottom-right corner, and
+// its numerical contract (section 3) rules out split-KV and unordered merges.
+//
+// out[i][h] = softmax_j(q_i . k_j / sqrt(128)) v_j over the keys j that query
+// i sees: all Tk keys, or with the causal mask j <= i + (Tk - Tq).  q head h
+// reads kv head h / (hq / hkv).  Head dimension 128.
+//
+// Workgroup: 4 waves, 128 query rows of one q head (32 per wave).  Keys go in
+// blocks of 64, from key 0 upwards, one block at a time through LDS; each
+// query keeps an online softmax (running max and sum, in fp32) and its fp32
+// output accumulators.  No block is split across workgroups, so every output
+// element sees one accumulation order, fixed by the key blocks -- which start
+// at key 0 whatever the pack -- and the row's bytes do not depend on the
+// other queries of the pack.  Blocks past a query's last visible key (the
+// workgroup runs to its last query's) change nothing: their scores are -inf,
+// so the rescale factor is exactly 1 and the weights exactly 0.
+//
+// MFMA (v_mfma_f32_32x32x16_bf16, D[i][j] = sum_k a_i[k] b_j[k], lane l
+// holding a_i, b_j for i, j = l & 31 at k = 8 (l >> 5) + 0..7, and D[i][j]
+// for j = l & 31, i = 8 (r >> 2) + 4 (l >> 5) + (r & 3) in register r):
+//   scores  S^T[key][q] = sum_d K[key][d] Q[q][d]       (a = K row, b = Q row)
+//   output  O^T[d][q]   = sum_key V^T[d][key] P[q][key]  (a = V^T row, b = P)
+// so a lane holds its query's scores for 16 of each 32 keys, and its half-
+// wave partner (lane ^ 32) the other 16; the P operand is the lane's own
+// scores in register order, and the V^T operand lists the same keys in the
+// same slots (keys 4h..4h+3, then 8+4h..8+4h+3 of each 16).  V^T comes from
+// the library's transpose into the workspace ([hkv*128][Tk rounded up to 64],
+// zero past Tk).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mot_internal.h"
+
+namespace mot {
+namespace {
+
+typedef __bf16 at_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 at_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float at_f32x2_t __attribute__((ext_vector_type(2)));
+typedef float at_f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t at_u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t at_u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;            // head dimension
+constexpr int kBQ = 128;           // query rows per workgroup
+constexpr int kBK = 64;            // keys per block
+constexpr int kKRow = kD * 2 + 16;   // bytes per staged K row (16 bytes of padding)
+constexpr int kVRow = kBK * 2 + 16;  // bytes per staged V^T row
+constexpr int kThreads = 256;
+
+// fp32 -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t at_pack2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((at_f32x2_t){lo, hi}, at_bf16x2_t));
+}
+
+__global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t ks[kBK * kKRow];
+    __shared__ __attribute__((aligned(16))) uint8_t vs[kD * kVRow];
+
+    const int tid = (int)threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lq = lane & 31, hh = lane >> 5;
+    const int h = (int)blockIdx.y;
+    const int kvh = h / (a.hq / a.hkv);
+    const int64_t q0 = (int64_t)blockIdx.x * kBQ;
+    const int64_t qrow = q0 + wave * 32 + lq;
+    const int64_t shift = a.Tk - a.Tq;  // bottom-right alignment of the causal mask
+
+    // this query's last visible key, and the keys the workgroup needs
+    int64_t last = a.causal ? qrow + shift : a.Tk - 1;
+    if (last > a.Tk - 1) last = a.Tk - 1;
+    const int64_t qlast = (q0 + kBQ - 1 < a.Tq - 1) ? q0 + kBQ - 1 : a.Tq - 1;
+    int64_t kend = a.causal ? qlast + shift + 1 : a.Tk;
+    if (kend > a.Tk) kend = a.Tk;
+    const int nkb = kend > 0 ? (int)((kend + kBK - 1) / kBK) : 0;
+
+    // Q fragments: row qrow (clamped; rows past Tq are never stored), columns
+    // h*128 + 16 s + 8 hh .. +8
+    at_bf16x8_t qf[8];
+    {
+        const int64_t qr = qrow < a.Tq ? qrow : a.Tq - 1;
+        const uint16_t *qp = a.q + qr * a.ldq + h * kD + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qf[s] = *(const at_bf16x8_t *)(qp + 16 * s);
+    }
+
+    // staging: 1024 16-byte chunks of K (64 rows x 16) and of V^T (128 rows
+    // x 8) per block, four of each per thread
+    const uint16_t *kbase = a.k + kvh * kD;
+    const uint16_t *vbase = a.vt + (int64_t)kvh * kD * a.ldvt;
+    at_u32x4_t kr[4], vr[4];
+    auto load_block = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + kThreads * i;
+            const int r = idx >> 4, c = idx & 15;
+            const int64_t key = (int64_t)kb * kBK + r;
+            kr[i] = key < a.Tk ? *(const at_u32x4_t *)(kbase + key * a.ldk + c * 8) : (at_u32x4_t){0, 0, 0, 0};
+            const int d = idx >> 3, c2 = idx & 7;
+            vr[i] = *(const at_u32x4_t *)(vbase + (int64_t)d * a.ldvt + (int64_t)kb * kBK + c2 * 8);
+        }
+    };
+    auto store_block = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + kThreads * i;
+            *(at_u32x4_t *)(ks + (idx >> 4) * kKRow + (idx & 15) * 16) = kr[i];
+            *(at_u32x4_t *)(vs + (idx >> 3) * kVRow + (idx & 7) * 16) = vr[i];
+        }
+    };
+
+    at_f32x16_t oacc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) oacc[t] = (at_f32x16_t){};
+    float m_run = -INFINITY, l_run = 0.0f;
+    const float scale = a.scale;
+
+    if (nkb > 0) load_block(0);
+    for (int kb = 0; kb < nkb; ++kb) {
+        __syncthreads();  // the previous block's LDS reads are done
+        store_block();
+        __syncthreads();
+        if (kb + 1 < nkb) load_block(kb + 1);
+
+        // scores of keys kb*64 + [0, 64)
+        at_f32x16_t sacc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            sacc[kt] = (at_f32x16_t){};
+            const uint8_t *row = ks + (kt * 32 + lq) * kKRow + 16 * hh;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const at_bf16x8_t kf = *(const at_bf16x8_t *)(row + 32 * s);
+                sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kt], 0, 0, 0);
+            }
+        }
+        // scale, mask, block maximum
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t key = (int64_t)kb * kBK + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const float x = key <= last ? sacc[kt][r] * scale : -INFINITY;
+                sacc[kt][r] = x;
+                mx = fmaxf(mx, x);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;  // no key seen yet: weights 0
+        const float alpha = expf(m_run - m_use);
+        float psum = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = expf(sacc[kt][r] - m_use);
+                sacc[kt][r] = p;
+                psum += p;
+            }
+        }
+        psum += __shfl_xor(psum, 32);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) oacc[t] *= alpha;
+
+        // P as bf16 operands: k-step s2 covers registers 8 (s2 & 1) .. +8 of
+        // score tile s2 >> 1
+        at_bf16x8_t pf[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const int kt = s2 >> 1, r0 = 8 * (s2 & 1);
+            const at_u32x4_t pk = {at_pack2(sacc[kt][r0 + 0], sacc[kt][r0 + 1]),
+                                   at_pack2(sacc[kt][r0 + 2], sacc[kt][r0 + 3]),
+                                   at_pack2(sacc[kt][r0 + 4], sacc[kt][r0 + 5]),
+                                   at_pack2(sacc[kt][r0 + 6], sacc[kt][r0 + 7])};
+            pf[s2] = __builtin_bit_cast(at_bf16x8_t, pk);
+        }
+        // O^T += V^T P^T, keys in ascending 16-key steps
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const uint8_t *row = vs + (dt * 32 + lq) * kVRow;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const at_u32x2_t lo = *(const at_u32x2_t *)(row + (s2 * 16 + 4 * hh) * 2);
+                const at_u32x2_t hi = *(const at_u32x2_t *)(row + (s2 * 16 + 8 + 4 * hh) * 2);
+                const at_u32x4_t vv = {lo.x, lo.y, hi.x, hi.y};
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(at_bf16x8_t, vv), pf[s2],
+                                                                   oacc[dt], 0, 0, 0);
+            }
+        }
+    }
+
+    if (qrow >= a.Tq) return;
+    uint16_t *op = a.out + qrow * a.ldo + h * kD + 4 * hh;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = l_run > 0.0f ? oacc[dt][4 * j + e] / l_run : 0.0f;
+            *(at_u32x2_t *)(op + dt * 32 + 8 * j) = (at_u32x2_t){at_pack2(v[0], v[1]), at_pack2(v[2], v[3])};
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.Tq + kBQ - 1) / kBQ), (unsigned)a.hq);
+    hipLaunchKernelGGL(attention_kernel, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace mot

@@ -63,6 +63,24 @@ struct QkArgs {
     int32_t *err;         // error word (cleared by the launch)
 };
 
+// Shared joint attention, head dimension 128 (mot_attention.hip).
+struct AttnArgs {
+    const uint16_t *q;    // [Tq][ldq] bf16: q heads of 128 columns
+    int64_t ldq;
+    const uint16_t *k;    // [Tk][ldk] bf16: kv heads of 128 columns
+    int64_t ldk;
+    const uint16_t *vt;   // [hkv*128][ldvt] bf16: V transposed, zero past Tk
+    int64_t ldvt;         // multiple of 64, >= Tk
+    uint16_t *out;        // [Tq][ldo] bf16
+    int64_t ldo;
+    int64_t Tq, Tk;
+    int hq, hkv;          // hq % hkv == 0
+    int causal;           // 1: query i sees keys j <= i + (Tk - Tq)
+    float scale;          // fp32 rounding of 1/sqrt(128)
+};
+
+hipError_t launch_attention(const AttnArgs &a, hipStream_t stream);
+
 hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t *perm,
                        hipStream_t stream);
 // Launches the persistent routed GEMM (one workgroup per CU at most).  With

@@ -233,3 +233,48 @@ def test_qk_norm_rope_fails_closed(kw, code):
                                     a["kwu"], a["kwg"], a["pos"], a["cos"], a["sin"], a["n_pos"], a["eps"],
                                     a["ws"], a["wsb"], None)
     assert st == code
+
+
+def _attn(**kw):
+    args = dict(q=A, ldq=512, k=2 * A, ldk=256, v=3 * A, ldv=256, out=4 * A, ldo=512, Tq=64, Tk=100, hq=4,
+                hkv=2, D=128, causal=1, ws=6 * A, wsb=1 << 20)
+    args.update(kw)
+    return mot.lib().mot_joint_attention(args["q"], args["ldq"], args["k"], args["ldk"], args["v"], args["ldv"],
+                                         args["out"], args["ldo"], args["Tq"], args["Tk"], args["hq"],
+                                         args["hkv"], args["D"], args["causal"], args["ws"], args["wsb"], None)
+
+
+def test_attention_workspace_bytes():
+    assert mot.attention_workspace_bytes(0, 4) == 0
+    assert mot.attention_workspace_bytes(1, 4) == 4 * 128 * 64 * 2
+    assert mot.attention_workspace_bytes(4096, 4) == 4 * 128 * 4096 * 2
+    assert mot.attention_workspace_bytes(4097, 1) == 128 * 4160 * 2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Tq=-1), INVALID),
+    (dict(Tk=-1), INVALID),
+    (dict(Tq=0, q=None), OK),                 # Tq == 0 is a no-op
+    (dict(hq=3), INVALID),                    # hq % hkv != 0
+    (dict(hkv=0), INVALID),
+    (dict(causal=2), INVALID),
+    (dict(D=64), SHAPE),                      # head dimension 128 only
+    (dict(hq=512, hkv=2, ldq=512 * 128, ldo=512 * 128), SHAPE),
+    (dict(Tq=(1 << 24) + 1), SHAPE),
+    (dict(q=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(k=None), INVALID),
+    (dict(ldq=384), INVALID),                 # narrower than the q heads
+    (dict(ldo=384), INVALID),
+    (dict(ldk=128), INVALID),
+    (dict(ldq=516), MISALIGNED),
+    (dict(v=3 * A + 8), MISALIGNED),
+    (dict(ws=None), WORKSPACE),
+    (dict(wsb=2 * 128 * 128 * 2 - 2), WORKSPACE),
+    (dict(ws=6 * A + 8), MISALIGNED),
+    (dict(out=A + 1024), INVALID),            # out overlaps q
+    (dict(out=2 * A), INVALID),               # out overlaps k
+    (dict(ws=3 * A + 512), INVALID),          # workspace overlaps v
+])
+def test_attention_fails_closed(kw, code):
+    assert _attn(**kw) == code

@@ -1,0 +1,114 @@
+"""GPU parity of the shared joint attention (the RFC page's
+"gen_joint_attention" work item: one attention over the pack's tokens of both
+modalities, grouped kv heads, causal mask aligned at the bottom-right corner
+for a cached prefill) against the CPU oracle, and its batch invariance.
+
+Parity bar: the gate of the other parity tests (max-abs 2e-2, relative
+Frobenius 5e-3) against the oracle's exact fp64 result.  The one-step check
+does not apply: the kernel feeds the softmax weights to the second product
+as bf16 (a declared cast), so its result is not the rounding of the exact
+value.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_transformers_token_amd as mot
+import oracle
+import workloads as W
+from helpers import bits, check_parity, dev
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def _inputs(Tq, Tk, hq, hkv, base, extra=0):
+    q = W.normal_bf16((Tq, hq * D + extra), W.seed_of(base, 1))
+    k = W.normal_bf16((Tk, hkv * D + extra), W.seed_of(base, 2))
+    v = W.normal_bf16((Tk, hkv * D + extra), W.seed_of(base, 3))
+    return q, k, v
+
+
+def _parity(q, k, v, hq, hkv, causal, what, rows=None, out=None):
+    got = mot.joint_attention(dev(q) if not q.is_cuda else q, dev(k) if not k.is_cuda else k,
+                              dev(v) if not v.is_cuda else v, hq, hkv, causal=causal, out=out)
+    torch.cuda.synchronize()
+    gb = bits(got)
+    sel = np.arange(q.shape[0]) if rows is None else rows
+    ref, rne = oracle.attention(W.bits(q.cpu()), W.bits(k.cpu()), W.bits(v.cpu()), hq, hkv, causal, rows=sel)
+    check_parity(gb[sel][:, :hq * D], ref, rne, what, one_step=False)
+    return got
+
+
+@pytest.mark.parametrize("Tq,Tk,hq,hkv,causal", [
+    (1, 1, 1, 1, True), (37, 90, 4, 2, True), (128, 128, 2, 1, True), (128, 128, 2, 1, False),
+    (200, 333, 7, 1, True), (300, 300, 4, 4, False), (129, 700, 4, 2, True), (65, 64, 2, 2, False)])
+def test_attention_small(Tq, Tk, hq, hkv, causal):
+    q, k, v = _inputs(Tq, Tk, hq, hkv, base=1000 + Tq + Tk, extra=64)
+    _parity(q, k, v, hq, hkv, causal, f"attn Tq={Tq} Tk={Tk} hq={hq} hkv={hkv} causal={causal}")
+
+
+def test_attention_rows_without_keys():
+    """Tq > Tk with the bottom-right causal mask: the first Tq - Tk rows see
+    no key and are zero; the rest match the oracle."""
+    q, k, v = _inputs(333, 200, 2, 1, base=1010)
+    got = _parity(q, k, v, 2, 1, True, "attn Tq>Tk")
+    assert not bits(got)[:133].any()
+
+
+def test_attention_no_keys():
+    q = W.normal_bf16((70, 256), 1011)
+    k = torch.empty((0, 128), dtype=torch.bfloat16)
+    out = mot.joint_attention(dev(q), dev(k), dev(k), 2, 1, causal=False)
+    torch.cuda.synchronize()
+    assert not bits(out).any()
+    e = mot.joint_attention(dev(q[:0]), dev(k), dev(k), 2, 1)
+    assert tuple(e.shape) == (0, 256)
+
+
+def test_attention_qkv_layout_sampled():
+    """The BAGEL layer's shape: 28 q heads and 4 kv heads of 128 read from one
+    [4096, 4608] QKV buffer (q, k, v as column ranges), causal over the
+    4096-row pack, 40 sampled rows checked against the oracle."""
+    T = 4096
+    qkv = W.normal_bf16((T, W.QKV_DIM), 1012)
+    qkv_d = dev(qkv)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, T - 1],
+                                     np.random.default_rng(15).integers(0, T, 33)]))
+    got = mot.joint_attention(qkv_d[:, :W.Q_DIM], qkv_d[:, W.Q_DIM:W.Q_DIM + W.KV_DIM],
+                              qkv_d[:, W.Q_DIM + W.KV_DIM:], W.N_Q_HEADS, W.N_K_HEADS, causal=True)
+    torch.cuda.synchronize()
+    qb = W.bits(qkv)
+    ref, rne = oracle.attention(qb[:, :W.Q_DIM], qb[:, W.Q_DIM:W.Q_DIM + W.KV_DIM], qb[:, W.Q_DIM + W.KV_DIM:],
+                                W.N_Q_HEADS, W.N_K_HEADS, True, rows=rows)
+    check_parity(bits(got)[rows], ref, rne, "attn QKV T=4096", one_step=False)
+
+
+def test_attention_cached_prefill_sampled():
+    """A cached prefill: 1000 new rows over 4096 keys (3096 cached), the mask
+    aligned at the bottom-right corner; sampled rows."""
+    q, k, v = _inputs(1000, 4096, W.N_Q_HEADS, W.N_K_HEADS, base=1013)
+    rows = np.unique(np.concatenate([[0, 999], np.random.default_rng(16).integers(0, 1000, 14)]))
+    _parity(q, k, v, W.N_Q_HEADS, W.N_K_HEADS, True, "attn prefill 1000/4096", rows=rows)
+
+
+def test_attention_rows_batch_invariant():
+    """A row's bytes depend only on its q row and the keys it sees: the last
+    300 rows of a 1000-row causal pack, run as a pack of their own over the
+    same keys (the bottom-right alignment keeps what each row sees), give the
+    same bytes; without the mask, permuting the rows permutes the output
+    rows bit for bit."""
+    q, k, v = _inputs(1000, 1500, 4, 2, base=1014)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    full = mot.joint_attention(qd, kd, vd, 4, 2, causal=True)
+    tail = mot.joint_attention(qd[700:].contiguous(), kd, vd, 4, 2, causal=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(full)[700:], bits(tail))
+    perm = W.permutation(1000, 17).to("cuda")
+    a = mot.joint_attention(qd, kd, vd, 4, 2, causal=False)
+    b = mot.joint_attention(qd[perm].contiguous(), kd, vd, 4, 2, causal=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(a)[perm.cpu().numpy()], bits(b))
