@@ -336,7 +336,7 @@ int mot_joint_attention(const uint16_t *q, int64_t ldq, const uint16_t *k, int64
     a.hq = (int)n_q_heads;
     a.hkv = (int)n_kv_heads;
     a.causal = causal;
-    a.scale = (float)(1.0 / sqrt((double)kAttnHeadDim));
+    a.scale_log2e = (float)(1.4426950408889634074 / sqrt((double)kAttnHeadDim));
     return mot::launch_attention(a, s) == hipSuccess ? MOT_OK : MOT_ERR_DEVICE;
 }
 

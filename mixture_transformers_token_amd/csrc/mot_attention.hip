@@ -64,15 +64,21 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int lq = lane & 31, hh = lane >> 5;
-    const int h = (int)blockIdx.y;
+    // heads vary fastest and the query blocks run from the last one down, so
+    // that under the causal mask the longest workgroups start first
+    const int nqb = (int)((a.Tq + kBQ - 1) / kBQ);
+    const int h = (int)(blockIdx.x % (unsigned)a.hq);
     const int kvh = h / (a.hq / a.hkv);
-    const int64_t q0 = (int64_t)blockIdx.x * kBQ;
+    const int64_t q0 = (int64_t)(nqb - 1 - (int)(blockIdx.x / (unsigned)a.hq)) * kBQ;
     const int64_t qrow = q0 + wave * 32 + lq;
     const int64_t shift = a.Tk - a.Tq;  // bottom-right alignment of the causal mask
 
     // this query's last visible key, and the keys the workgroup needs
     int64_t last = a.causal ? qrow + shift : a.Tk - 1;
     if (last > a.Tk - 1) last = a.Tk - 1;
+    // the wave's smallest last visible key: blocks up to it need no mask
+    int64_t wlast = a.causal ? q0 + wave * 32 + shift : a.Tk - 1;
+    if (wlast > a.Tk - 1) wlast = a.Tk - 1;
     const int64_t qlast = (q0 + kBQ - 1 < a.Tq - 1) ? q0 + kBQ - 1 : a.Tq - 1;
     int64_t kend = a.causal ? qlast + shift + 1 : a.Tk;
     if (kend > a.Tk) kend = a.Tk;
@@ -99,7 +105,9 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
             const int idx = tid + kThreads * i;
             const int r = idx >> 4, c = idx & 15;
             const int64_t key = (int64_t)kb * kBK + r;
-            kr[i] = key < a.Tk ? *(const at_u32x4_t *)(kbase + key * a.ldk + c * 8) : (at_u32x4_t){0, 0, 0, 0};
+            // rows past Tk: load the last row, then zero it (no branch)
+            const at_u32x4_t kv = *(const at_u32x4_t *)(kbase + (key < a.Tk ? key : a.Tk - 1) * a.ldk + c * 8);
+            kr[i] = key < a.Tk ? kv : (at_u32x4_t){0, 0, 0, 0};
             const int d = idx >> 3, c2 = idx & 7;
             vr[i] = *(const at_u32x4_t *)(vbase + (int64_t)d * a.ldvt + (int64_t)kb * kBK + c2 * 8);
         }
@@ -116,8 +124,11 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
     at_f32x16_t oacc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) oacc[t] = (at_f32x16_t){};
+    // scores in the base-2 domain: s * (1/sqrt(128)) * log2(e), one fp32
+    // multiply by a constant rounded once; the weights are then exp2 of
+    // differences (v_exp_f32)
     float m_run = -INFINITY, l_run = 0.0f;
-    const float scale = a.scale;
+    const float scale = a.scale_log2e;
 
     if (nkb > 0) load_block(0);
     for (int kb = 0; kb < nkb; ++kb) {
@@ -138,28 +149,39 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
                 sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kt], 0, 0, 0);
             }
         }
-        // scale, mask, block maximum
+        // scale, mask (only where the block reaches past the wave's first
+        // row's last visible key), block maximum
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) sacc[kt] *= scale;
+        if ((int64_t)kb * kBK + kBK - 1 > wlast) {
+            const int rel = (int)(last - (int64_t)kb * kBK);  // last visible key, block-relative
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (key > rel) sacc[kt][r] = -INFINITY;
+                }
+            }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t key = (int64_t)kb * kBK + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const float x = key <= last ? sacc[kt][r] * scale : -INFINITY;
-                sacc[kt][r] = x;
-                mx = fmaxf(mx, x);
-            }
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;  // no key seen yet: weights 0
-        const float alpha = expf(m_run - m_use);
+        // exactly 1 while the running max holds (blocks past a row's last
+        // visible key then leave its state bit for bit as it was)
+        const float alpha = m_run == m_use ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_use);
         float psum = 0.0f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = expf(sacc[kt][r] - m_use);
+                const float p = __builtin_amdgcn_exp2f(sacc[kt][r] - m_use);
                 sacc[kt][r] = p;
                 psum += p;
             }
@@ -167,8 +189,12 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
         psum += __shfl_xor(psum, 32);
         l_run = l_run * alpha + psum;
         m_run = m_new;
+        // alpha is exactly 1 while the running max holds: skip the rescale
+        // when it holds for the whole wave (same bytes either way)
+        if (__any(alpha != 1.0f)) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) oacc[t] *= alpha;
+            for (int t = 0; t < 4; ++t) oacc[t] *= alpha;
+        }
 
         // P as bf16 operands: k-step s2 covers registers 8 (s2 & 1) .. +8 of
         // score tile s2 >> 1
@@ -214,7 +240,7 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.Tq + kBQ - 1) / kBQ), (unsigned)a.hq);
+    const dim3 grid((unsigned)(a.hq * ((a.Tq + kBQ - 1) / kBQ)));
     hipLaunchKernelGGL(attention_kernel, grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

@@ -76,7 +76,7 @@ struct AttnArgs {
     int64_t Tq, Tk;
     int hq, hkv;          // hq % hkv == 0
     int causal;           // 1: query i sees keys j <= i + (Tk - Tq)
-    float scale;          // fp32 rounding of 1/sqrt(128)
+    float scale_log2e;    // fp32 rounding of log2(e)/sqrt(128)
 };
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream);
