@@ -310,6 +310,10 @@ int mot_joint_attention(const uint16_t *q, int64_t ldq, const uint16_t *k, int64
     if (overlaps(out, o_bytes, q, q_bytes)) return MOT_ERR_INVALID_ARG;
     if (Tk > 0) {
         const int64_t k_bytes = ((Tk - 1) * ldk + kw) * 2, v_bytes = ((Tk - 1) * ldv + kw) * 2;
+        // the kernel addresses K (up to its last key block's end) and the
+        // transposed V with 32-bit byte offsets
+        if ((round_up(Tk, 64) * ldk + kw) * 2 >= (int64_t(1) << 32) || (int64_t)wsb >= (int64_t(1) << 32))
+            return MOT_ERR_UNSUPPORTED_SHAPE;
         if (overlaps(out, o_bytes, k, k_bytes) || overlaps(out, o_bytes, v, v_bytes) ||
             overlaps(out, o_bytes, workspace, (int64_t)wsb) || overlaps(workspace, (int64_t)wsb, q, q_bytes) ||
             overlaps(workspace, (int64_t)wsb, k, k_bytes) || overlaps(workspace, (int64_t)wsb, v, v_bytes))

@@ -44,6 +44,7 @@ typedef float at_f32x2_t __attribute__((ext_vector_type(2)));
 typedef float at_f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t at_u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t at_u32x4_t __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t at_rsrc_t;
 
 constexpr int kD = 128;            // head dimension
 constexpr int kBQ = 128;           // query rows per workgroup
@@ -51,6 +52,11 @@ constexpr int kBK = 64;            // keys per block
 constexpr int kKRow = kD * 2 + 16;   // bytes per staged K row (16 bytes of padding)
 constexpr int kVRow = kBK * 2 + 16;  // bytes per staged V^T row
 constexpr int kThreads = 256;
+
+// Raw buffer over [base, base + bytes): a load past the end reads zeros.
+__device__ __forceinline__ at_rsrc_t at_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
 
 // fp32 -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t at_pack2(float lo, float hi) {
@@ -95,21 +101,24 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
     }
 
     // staging: 1024 16-byte chunks of K (64 rows x 16) and of V^T (128 rows
-    // x 8) per block, four of each per thread
-    const uint16_t *kbase = a.k + kvh * kD;
-    const uint16_t *vbase = a.vt + (int64_t)kvh * kD * a.ldvt;
+    // x 8) per block, four of each per thread, through raw buffers (32-bit
+    // offsets; K rows past Tk lie past the K buffer's end and read zeros)
+    const at_rsrc_t kres = at_rsrc(a.k + kvh * kD, (uint32_t)(((a.Tk - 1) * a.ldk + (a.hkv - kvh) * kD) * 2));
+    const at_rsrc_t vres = at_rsrc(a.vt + (int64_t)kvh * kD * a.ldvt, (uint32_t)(kD * a.ldvt * 2));
+    uint32_t koff[4], voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + kThreads * i;
+        koff[i] = (uint32_t)(idx >> 4) * (uint32_t)a.ldk * 2u + (uint32_t)(idx & 15) * 16u;
+        voff[i] = (uint32_t)(idx >> 3) * (uint32_t)a.ldvt * 2u + (uint32_t)(idx & 7) * 16u;
+    }
     at_u32x4_t kr[4], vr[4];
     auto load_block = [&](int kb) {
+        const uint32_t ks0 = (uint32_t)kb * kBK * (uint32_t)a.ldk * 2u, vs0 = (uint32_t)kb * kBK * 2u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int idx = tid + kThreads * i;
-            const int r = idx >> 4, c = idx & 15;
-            const int64_t key = (int64_t)kb * kBK + r;
-            // rows past Tk: load the last row, then zero it (no branch)
-            const at_u32x4_t kv = *(const at_u32x4_t *)(kbase + (key < a.Tk ? key : a.Tk - 1) * a.ldk + c * 8);
-            kr[i] = key < a.Tk ? kv : (at_u32x4_t){0, 0, 0, 0};
-            const int d = idx >> 3, c2 = idx & 7;
-            vr[i] = *(const at_u32x4_t *)(vbase + (int64_t)d * a.ldvt + (int64_t)kb * kBK + c2 * 8);
+            kr[i] = __builtin_amdgcn_raw_buffer_load_b128(kres, (int)koff[i], (int)ks0, 0);
+            vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, (int)voff[i], (int)vs0, 0);
         }
     };
     auto store_block = [&]() {
@@ -124,9 +133,8 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
     at_f32x16_t oacc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) oacc[t] = (at_f32x16_t){};
-    // scores in the base-2 domain: s * (1/sqrt(128)) * log2(e), one fp32
-    // multiply by a constant rounded once; the weights are then exp2 of
-    // differences (v_exp_f32)
+    // running max of the raw scores; the weights are 2^(c (s - m)) with the
+    // constant c = log2(e)/sqrt(128) rounded once to fp32 (v_exp_f32)
     float m_run = -INFINITY, l_run = 0.0f;
     const float scale = a.scale_log2e;
 
@@ -149,10 +157,8 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
                 sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kt], 0, 0, 0);
             }
         }
-        // scale, mask (only where the block reaches past the wave's first
-        // row's last visible key), block maximum
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) sacc[kt] *= scale;
+        // mask (only where the block reaches past the wave's first row's
+        // last visible key), block maximum of the raw scores
         if ((int64_t)kb * kBK + kBK - 1 > wlast) {
             const int rel = (int)(last - (int64_t)kb * kBK);  // last visible key, block-relative
 #pragma unroll
@@ -173,15 +179,17 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;  // no key seen yet: weights 0
+        // weight = 2^(s c - m c), c = log2(e)/sqrt(128): one fma per score
+        const float mc = m_use * scale;
         // exactly 1 while the running max holds (blocks past a row's last
         // visible key then leave its state bit for bit as it was)
-        const float alpha = m_run == m_use ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_use);
+        const float alpha = m_run == m_use ? 1.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(m_run, scale, -mc));
         float psum = 0.0f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(sacc[kt][r] - m_use);
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], scale, -mc));
                 sacc[kt][r] = p;
                 psum += p;
             }
