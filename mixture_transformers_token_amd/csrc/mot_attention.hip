@@ -50,12 +50,23 @@ constexpr int kD = 128;            // head dimension
 constexpr int kBQ = 128;           // query rows per workgroup
 constexpr int kBK = 64;            // keys per block
 constexpr int kKRow = kD * 2 + 16;   // bytes per staged K row (16 bytes of padding)
-constexpr int kVRow = kBK * 2 + 16;  // bytes per staged V^T row
+// bytes per staged V^T row: 34 dwords, so the 8-byte fragment reads of 16
+// consecutive rows fall on distinct banks
+constexpr int kVRow = kBK * 2 + 8;
 constexpr int kThreads = 256;
+constexpr float kLazy = 8.0f;        // log2 headroom of the softmax reference max
 
 // Raw buffer over [base, base + bytes): a load past the end reads zeros.
 __device__ __forceinline__ at_rsrc_t at_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// {x of lane l, x of lane l ^ 32} in every lane (v_permlane32_swap), lower
+// half's value first
+__device__ __forceinline__ void at_halves(float x, float &lo, float &hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
 }
 
 // fp32 -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
@@ -126,7 +137,9 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
         for (int i = 0; i < 4; ++i) {
             const int idx = tid + kThreads * i;
             *(at_u32x4_t *)(ks + (idx >> 4) * kKRow + (idx & 15) * 16) = kr[i];
-            *(at_u32x4_t *)(vs + (idx >> 3) * kVRow + (idx & 7) * 16) = vr[i];
+            uint8_t *vp = vs + (idx >> 3) * kVRow + (idx & 7) * 16;  // 8-byte aligned rows
+            *(at_u32x2_t *)vp = (at_u32x2_t){vr[i].x, vr[i].y};
+            *(at_u32x2_t *)(vp + 8) = (at_u32x2_t){vr[i].z, vr[i].w};
         }
     };
 
@@ -170,31 +183,44 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
                 }
             }
         }
-        float mx = -INFINITY;
+        // pairwise trees (short dependency chains), then the two half-waves
+        float t16[16];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int r = 0; r < 16; ++r) t16[r] = fmaxf(sacc[0][r], sacc[1][r]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+        for (int w = 8; w >= 1; w >>= 1) {
+#pragma unroll
+            for (int r = 0; r < w; ++r) t16[r] = fmaxf(t16[r], t16[r + w]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
+        float mlo, mhi;
+        at_halves(t16[0], mlo, mhi);
+        const float mx = fmaxf(mlo, mhi);
+        // The reference max moves only when a score exceeds it by more than
+        // kLazy / c (weights then stay below 2^kLazy, far inside fp32 and
+        // bf16 range): most blocks keep it, so the output needs no rescale.
+        // The rule looks at the row's own scores only.
+        const float m_new = (m_run == -INFINITY || (mx - m_run) * scale > kLazy) ? mx : m_run;
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;  // no key seen yet: weights 0
         // weight = 2^(s c - m c), c = log2(e)/sqrt(128): one fma per score
         const float mc = m_use * scale;
         // exactly 1 while the running max holds (blocks past a row's last
         // visible key then leave its state bit for bit as it was)
         const float alpha = m_run == m_use ? 1.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(m_run, scale, -mc));
-        float psum = 0.0f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], scale, -mc));
-                sacc[kt][r] = p;
-                psum += p;
-            }
+            for (int r = 0; r < 16; ++r) sacc[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], scale, -mc));
         }
-        psum += __shfl_xor(psum, 32);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t16[r] = sacc[0][r] + sacc[1][r];
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1) {
+#pragma unroll
+            for (int r = 0; r < w; ++r) t16[r] = t16[r] + t16[r + w];
+        }
+        float slo, shi;
+        at_halves(t16[0], slo, shi);
+        const float psum = slo + shi;  // same operands, same order, in both halves
         l_run = l_run * alpha + psum;
         m_run = m_new;
         // alpha is exactly 1 while the running max holds: skip the rescale
