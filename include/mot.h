@@ -261,12 +261,15 @@ size_t mot_attention_workspace_bytes(int64_t Tk, int64_t n_kv_heads);
  * page (section 5).  Both weight sets share it, so it is not routed: every
  * query row of the pack attends over the same keys, of both modalities.
  * For query row i and q head h, with kv head g = h / (n_q_heads / n_kv_heads):
- *   s_j = fp32 sum_d q[i][128h+d] * k[j][128g+d], times the fp32 rounding of
- *         1/sqrt(128), for each key j that row i sees;
+ *   s_j = fp32 sum_d q[i][128h+d] * k[j][128g+d] for each key j that row i
+ *         sees (the softmax of s_j / sqrt(128));
  *   out[i][128h+d] = bf16_rne( sum_j p_j v[j][128g+d] / sum_j p_j ),
- *         p_j = expf(s_j - max s), accumulated over blocks of 64 keys from
- *         key 0 upwards with an online (running max) softmax in fp32; the
- *         p_j enter the products with v as bf16.
+ *         p_j = 2^(c s_j - c m) (hardware exp2), c = log2(e)/sqrt(128)
+ *         rounded once to fp32, m a per-row reference that follows the
+ *         running maximum of the scores and moves only when a block's
+ *         maximum exceeds it by more than 8/c (so p_j <= 2^8); keys in blocks
+ *         of 64 from key 0 upwards, the sums and the rescale by 2^(c m_old -
+ *         c m_new) in fp32; the p_j enter the products with v as bf16.
  * Visible keys: all Tk when causal == 0.  With causal == 1 the mask is
  * aligned at the bottom-right corner, as the same page's reference hazards
  * require for a cached prefill: row i sees keys j <= i + (Tk - Tq).  A row

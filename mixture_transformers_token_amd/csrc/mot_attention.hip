@@ -199,7 +199,9 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
         // kLazy / c (weights then stay below 2^kLazy, far inside fp32 and
         // bf16 range): most blocks keep it, so the output needs no rescale.
         // The rule looks at the row's own scores only.
-        const float m_new = (m_run == -INFINITY || (mx - m_run) * scale > kLazy) ? mx : m_run;
+        // (no key seen yet: m_run = -inf makes d +inf or NaN, so the max is taken)
+        const float d = (mx - m_run) * scale;
+        const float m_new = d <= kLazy ? m_run : mx;
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;  // no key seen yet: weights 0
         // weight = 2^(s c - m c), c = log2(e)/sqrt(128): one fma per score
         const float mc = m_use * scale;
