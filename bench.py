@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--no-components", action="store_true")
     p.add_argument("--only-small-packs", action="store_true",
                    help="of the components, run only the small packs (for their rocprofv3 profile)")
+    p.add_argument("--only-attention", action="store_true",
+                   help="of the components, run only the joint attention (for its rocprofv3 profile)")
     p.add_argument("--copy-probe", action="store_true",
                    help="run one 1 GiB device copy first (HBM counter calibration under rocprofv3)")
     p.add_argument("--cpu-rows", type=int, default=4096,
@@ -221,10 +223,28 @@ def main():
                                               "sets": sets}
             del copies
 
+    def joint_attention(components, qkv_buf, iters):
+        # shared joint attention over QKV rows (28 q / 4 kv heads, causal,
+        # bottom-right aligned; q, k, v read as column ranges of the buffer):
+        # MFMA-bound; useful flops count only the visible keys
+        q_v, k_v = qkv_buf[:, :W.Q_DIM], qkv_buf[:, W.Q_DIM:W.Q_DIM + W.KV_DIM]
+        v_v = qkv_buf[:, W.Q_DIM + W.KV_DIM:]
+        att = torch.empty((T, W.Q_DIM), dtype=torch.bfloat16, device=dev)
+        ws_att = torch.empty(mot.attention_workspace_bytes(T, W.N_K_HEADS), dtype=torch.uint8, device=dev)
+        s_att = time_component(lambda: mot.joint_attention(q_v, k_v, v_v, W.N_Q_HEADS, W.N_K_HEADS, causal=True,
+                                                           out=att, workspace=ws_att), iters, stream)
+        f_att = 4.0 * W.N_Q_HEADS * 128 * T * (T + 1) / 2
+        components["joint_attention_causal_T4096"] = {
+            "us": round(s_att * 1e6, 1), "TFLOP/s": round(f_att / s_att / 1e12, 1),
+            "frac_mfma": round(f_att / s_att / 1e12 / PEAK_BF16_TFLOPS, 3),
+            "note": "includes the V transpose into the workspace; flops of visible keys only"}
+
     # ---- other hot-path steps ------------------------------------------------
     components = {}
     if args.only_small_packs:
         small_packs(components)
+    elif args.only_attention:
+        joint_attention(components, y.clone(), 30)
     elif not args.no_components:
         iters = 30
         # routed fused add-RMSNorm, T=4096, H=3584 (x, residual in; residual, y out)
@@ -281,21 +301,8 @@ def main():
         nb_qk = 2 * T * qk_cols * 2 + T * (1 + 4 + 2 * 64 * 2)
         components["qk_norm_rope_T4096"] = {"us": round(s_qk * 1e6, 2), "GB/s": round(nb_qk / s_qk / 1e9, 1),
                                             "frac_hbm": round(nb_qk / s_qk / 1e9 / PEAK_HBM_GBS, 3)}
-        # shared joint attention over the same QKV rows (28 q / 4 kv heads,
-        # causal, bottom-right aligned; q, k, v read as column ranges of the
-        # buffer): MFMA-bound; useful flops count only the visible keys
-        q_v, k_v = qkv_buf[:, :W.Q_DIM], qkv_buf[:, W.Q_DIM:W.Q_DIM + W.KV_DIM]
-        v_v = qkv_buf[:, W.Q_DIM + W.KV_DIM:]
-        att = torch.empty((T, W.Q_DIM), dtype=torch.bfloat16, device=dev)
-        ws_att = torch.empty(mot.attention_workspace_bytes(T, W.N_K_HEADS), dtype=torch.uint8, device=dev)
-        s_att = time_component(lambda: mot.joint_attention(q_v, k_v, v_v, W.N_Q_HEADS, W.N_K_HEADS, causal=True,
-                                                           out=att, workspace=ws_att), iters, stream)
-        f_att = 4.0 * W.N_Q_HEADS * 128 * T * (T + 1) / 2
-        components["joint_attention_causal_T4096"] = {
-            "us": round(s_att * 1e6, 1), "TFLOP/s": round(f_att / s_att / 1e12, 1),
-            "frac_mfma": round(f_att / s_att / 1e12 / PEAK_BF16_TFLOPS, 3),
-            "note": "includes the V transpose into the workspace; flops of visible keys only"}
-        del qkv_buf, att, ws_att
+        joint_attention(components, qkv_buf, iters)
+        del qkv_buf
         # context only: the vendor library's dense GEMM of one weight set at
         # the same shape (hipBLASLt via torch.matmul; not batch-invariant,
         # not a target)
