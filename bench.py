@@ -323,10 +323,12 @@ def main():
         components["gate_up_swiglu_T4096"] = {"us": round(s_gu * 1e6, 1),
                                               "TFLOP/s": round(f_gu / s_gu / 1e12, 1)}
         components["down_T4096"] = {"us": round(s_dn * 1e6, 1), "TFLOP/s": round(f_dn / s_dn / 1e12, 1)}
-        # per-layer routed linear chain: fused add-RMSNorm -> QKV -> O (q slice
-        # standing in for attention) -> fused add-RMSNorm -> gate/up+SwiGLU ->
-        # down, on the three-branch CFG pack and on a 16384-row pack; FLOPs
-        # count real rows only (the CFG pack's 562 padding rows excluded)
+        # per-layer chain: fused add-RMSNorm -> QKV -> QK norm + rotary ->
+        # shared joint attention (causal, the pack as one sequence) -> O ->
+        # fused add-RMSNorm -> gate/up+SwiGLU -> down, on the three-branch CFG
+        # pack and on a 16384-row pack; "TFLOP/s" counts the routed linear
+        # steps over real rows only (the CFG pack's 562 padding rows
+        # excluded), the attention's time is in the layer time
         ou, og = (t.to(dev) for t in W.o_weights())
         for name, mc, real in (("cfg_pack_T4096", W.cfg_pack_modality(), 3534),
                                ("pack_T16384", W.pattern(16384), 16384)):
@@ -337,6 +339,8 @@ def main():
             y1 = torch.empty((Tc, K), dtype=torch.bfloat16, device=dev)
             qkv_c = torch.empty((Tc, N), dtype=torch.bfloat16, device=dev)
             o_c = torch.empty((Tc, K), dtype=torch.bfloat16, device=dev)
+            att_c = torch.empty((Tc, W.Q_DIM), dtype=torch.bfloat16, device=dev)
+            ws_att_c = torch.empty(mot.attention_workspace_bytes(Tc, W.N_K_HEADS), dtype=torch.uint8, device=dev)
             act_c = torch.empty((Tc, W.FFN), dtype=torch.bfloat16, device=dev)
             out_c = torch.empty((Tc, K), dtype=torch.bfloat16, device=dev)
             wsc = mot.new_workspace(Tc, dev)
@@ -346,7 +350,10 @@ def main():
                 "qkv": lambda: mot.routed_gemm(y1, wud, wgd, mcd, out=qkv_c, workspace=wsc),
                 "qk_norm_rope": lambda: mot.qk_norm_rope(qkv_c, W.N_Q_HEADS, W.N_K_HEADS, mcd, qn, kn, pos_c, cos_c,
                                                          sin_c, workspace=wsc),
-                "o": lambda: mot.routed_gemm(qkv_c[:, :W.Q_DIM], ou, og, mcd, out=o_c, workspace=wsc),
+                "attention": lambda: mot.joint_attention(qkv_c[:, :W.Q_DIM], qkv_c[:, W.Q_DIM:W.Q_DIM + W.KV_DIM],
+                                                         qkv_c[:, W.Q_DIM + W.KV_DIM:], W.N_Q_HEADS, W.N_K_HEADS,
+                                                         causal=True, out=att_c, workspace=ws_att_c),
+                "o": lambda: mot.routed_gemm(att_c, ou, og, mcd, out=o_c, workspace=wsc),
                 "norm2": lambda: mot.fused_add_rmsnorm(o_c, res_c, nwu, nwg, mcd, out=y1, rstd=None),
                 "gate_up_swiglu": lambda: mot.routed_gemm_swiglu(y1, gu_u, gu_g, mcd, out=act_c, workspace=wsc),
                 "down": lambda: mot.routed_gemm(act_c, dn_u, dn_g, mcd, out=out_c, workspace=wsc),
@@ -361,7 +368,7 @@ def main():
             components[f"layer_chain_{name}"] = {"us": round(s_layer * 1e6, 1),
                                                  "TFLOP/s": round(f_layer / s_layer / 1e12, 1),
                                                  "real_rows": real, "per_op_us": per_op}
-            del act_c
+            del act_c, att_c, ws_att_c
         del gu_u, gu_g, dn_u, dn_g
 
     # ---- CPU oracle baseline on a bounded row sample -------------------------

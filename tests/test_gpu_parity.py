@@ -248,10 +248,10 @@ def test_mlp_full_size_sampled():
 
 
 def _layer_chain_gpu(x, r, m, wts, rope):
-    """fused add-RMSNorm -> QKV -> QK norm + rotary -> O (on the q slice,
-    standing in for the shared attention) -> fused add-RMSNorm -> gate/up +
-    SwiGLU -> down, every step routed by the same modality bytes.  Returns
-    {step: (input, output)}."""
+    """fused add-RMSNorm -> QKV -> QK norm + rotary -> shared joint attention
+    (causal over the whole pack) -> O -> fused add-RMSNorm -> gate/up +
+    SwiGLU -> down, every routed step routed by the same modality bytes.
+    Returns {step: (input, output)}."""
     (n1u, n1g), (qu, qg), (ou, og), (n2u, n2g), (gu, gg), (du, dg), (qn, kn) = wts
     cos_t, sin_t, pos = rope
     md = dev(torch.from_numpy(m))
@@ -263,33 +263,41 @@ def _layer_chain_gpu(x, r, m, wts, rope):
     mot.qk_norm_rope(qkv, W.N_Q_HEADS, W.N_K_HEADS, md, tuple(dev(t) for t in qn), tuple(dev(t) for t in kn),
                      dev(pos), dev(cos_t), dev(sin_t), workspace=ws)
     assert mot.read_device_error(ws) == 0
-    o = mot.routed_gemm(qkv[:, :W.Q_DIM], dev(ou), dev(og), md)
+    att = mot.joint_attention(qkv[:, :W.Q_DIM], qkv[:, W.Q_DIM:W.Q_DIM + W.KV_DIM], qkv[:, W.Q_DIM + W.KV_DIM:],
+                              W.N_Q_HEADS, W.N_K_HEADS, causal=True)
+    o = mot.routed_gemm(att, dev(ou), dev(og), md)
     y2, _ = mot.fused_add_rmsnorm(o, res, dev(n2u), dev(n2g), md)
     act = mot.routed_gemm_swiglu(y2, dev(gu), dev(gg), md)
     out = mot.routed_gemm(act, dev(du), dev(dg), md)
     torch.cuda.synchronize()
-    return {"qkv": (y1, qkv0), "qk": (qkv0, qkv), "o": (qkv[:, :W.Q_DIM], o), "act": (y2, act),
+    return {"qkv": (y1, qkv0), "qk": (qkv0, qkv), "att": (qkv, att), "o": (att, o), "act": (y2, act),
             "out": (act, out)}
 
 
 def _layer_chain_oracle(x, r, m, wts, rope, rows):
-    """The same chain in the oracle, carrying its own bf16 intermediates, on
-    the sampled rows.  Returns {step: (input bits, (ref, rne))}."""
+    """The same chain in the oracle, carrying its own bf16 intermediates.
+    The steps up to the QK norm run on every row (the attention of a sampled
+    row reads every row's k and v); the rest on the sampled rows.  Returns
+    {step: (input bits, (ref, rne))} on the sampled rows."""
     (n1u, n1g), (qu, qg), (ou, og), (n2u, n2g), (gu, gg), (du, dg), (qn, kn) = wts
     cos_t, sin_t, pos = rope
     B = W.bits
+    Q, KV = W.Q_DIM, W.KV_DIM
     s1 = oracle.fused_add_rmsnorm(x, r, B(n1u), B(n1g), m)
-    qkv = oracle.routed_gemm(s1["out"], B(qu), B(qg), m)
-    ref_q, out_q, err = oracle.qk_norm_rope(qkv[1], W.N_Q_HEADS, W.N_K_HEADS, m, tuple(B(t) for t in qn),
-                                            tuple(B(t) for t in kn), pos.numpy()[rows], B(cos_t), B(sin_t))
+    _, qkv_all = oracle.routed_gemm(s1["out"], B(qu), B(qg), m, want_ref=False)
+    qkv = oracle.routed_gemm(s1["out"][rows], B(qu), B(qg), m[rows])
+    assert np.array_equal(qkv[1], qkv_all[rows])
+    ref_q, out_q, err = oracle.qk_norm_rope(qkv_all, W.N_Q_HEADS, W.N_K_HEADS, m, tuple(B(t) for t in qn),
+                                            tuple(B(t) for t in kn), pos.numpy(), B(cos_t), B(sin_t))
     assert err == 0
-    q = np.ascontiguousarray(out_q[:, :W.Q_DIM])
-    o = oracle.routed_gemm(q, B(ou), B(og), m)
-    s2 = oracle.fused_add_rmsnorm(o[1], s1["h"], B(n2u), B(n2g), m)
-    act = oracle.routed_gemm_swiglu(s2["out"], B(gu), B(gg), m)
-    out = oracle.routed_gemm(act[1], B(du), B(dg), m)
-    return {"qkv": (s1["out"], qkv), "qk": (qkv[1], (ref_q, out_q)), "o": (q, o), "act": (s2["out"], act),
-            "out": (act[1], out)}
+    att = oracle.attention(out_q[:, :Q], out_q[:, Q:Q + KV], out_q[:, Q + KV:], W.N_Q_HEADS, W.N_K_HEADS, True,
+                           rows=rows)
+    o = oracle.routed_gemm(att[1], B(ou), B(og), m[rows])
+    s2 = oracle.fused_add_rmsnorm(o[1], s1["h"][rows], B(n2u), B(n2g), m[rows])
+    act = oracle.routed_gemm_swiglu(s2["out"], B(gu), B(gg), m[rows])
+    out = oracle.routed_gemm(act[1], B(du), B(dg), m[rows])
+    return {"qkv": (s1["out"][rows], qkv), "qk": (qkv[1], (ref_q[rows], out_q[rows])), "att": (out_q, att),
+            "o": (att[1], o), "act": (s2["out"], act), "out": (act[1], out)}
 
 
 @pytest.fixture(scope="module")
@@ -304,10 +312,13 @@ def layer_weights():
 
 @pytest.mark.parametrize("which", ["cfg_pack", "large_pack"])
 def test_layer_chain_sampled(layer_weights, which):
-    """The per-layer routed linear chain on the three-branch CFG pack
-    (3534 rows padded to 4096) and on the 16384-row mixed pack, against the
-    oracle's own chain on a seeded row sample holding every segment boundary
-    (every step is row-local, so the sample is an exact restriction).
+    """The per-layer chain (routed linear steps and the shared joint
+    attention, causal over the whole pack taken as one sequence) on the
+    three-branch CFG pack (3534 rows padded to 4096) and on the 16384-row
+    mixed pack, against the oracle's own chain on a seeded row sample holding
+    every segment boundary (every step but the attention is row-local, so
+    the sample is an exact restriction; the oracle's attention of a sampled
+    row reads every row's k and v).
 
     Where a step's input bytes are the same in both chains, the step is held
     to the full per-op bar.  Past the first step the chains round their bf16
@@ -325,17 +336,21 @@ def test_layer_chain_sampled(layer_weights, which):
     rope = W.rope_inputs(T, 4096, base=96)
     got = _layer_chain_gpu(x, r, m, layer_weights, rope)
     rows = W.sample_rows(m, 16, seed=9)
-    want = _layer_chain_oracle(W.bits(x)[rows], W.bits(r)[rows], m[rows], layer_weights, rope, rows)
-    for step in ("qkv", "qk", "o", "act", "out"):
+    want = _layer_chain_oracle(W.bits(x), W.bits(r), m, layer_weights, rope, rows)
+    for step in ("qkv", "qk", "att", "o", "act", "out"):
         gin, gout = got[step]
         win, (ref, rne) = want[step]
-        same_input = np.array_equal(bits(gin)[rows], win)
+        # the attention's input is every row's q, k and v
+        same_input = (np.array_equal(bits(gin), win) if step == "att" else
+                      np.array_equal(bits(gin)[rows], win))
         metrics = oracle.gate_metrics(bits(gout)[rows], ref)
         assert np.isfinite(oracle.bf16_to_f64(bits(gout)[rows])).all(), (which, step)
         assert metrics["rel_fro"] <= 5e-3, (which, step, metrics)
         if same_input:
-            # the QK step rounds a bf16 intermediate of its own: no one-step check
-            check_parity(bits(gout)[rows], ref, rne, f"layer chain {which}: {step}", one_step=step != "qk")
+            # the QK step rounds a bf16 intermediate of its own, the attention
+            # casts its weights to bf16: no one-step check for either
+            check_parity(bits(gout)[rows], ref, rne, f"layer chain {which}: {step}",
+                         one_step=step not in ("qk", "att"))
     # the first step's inputs come from the norm, which is exact up to the
     # rounding of (h*rstd)*w: the QKV step is held to the full bar
     check_parity(bits(got["qkv"][1])[rows], *want["qkv"][1], f"layer chain {which}: qkv",
