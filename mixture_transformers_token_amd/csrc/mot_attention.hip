@@ -159,14 +159,14 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
         if (kb + 1 < nkb) load_block(kb + 1);
 
         // scores of keys kb*64 + [0, 64)
-        at_f32x16_t sacc[2];
+        // (the two tiles' chains alternate, so no MFMA waits on the one
+        // just issued; each tile's k order is unchanged)
+        at_f32x16_t sacc[2] = {(at_f32x16_t){}, (at_f32x16_t){}};
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            sacc[kt] = (at_f32x16_t){};
-            const uint8_t *row = ks + (kt * 32 + lq) * kKRow + 16 * hh;
+        for (int s = 0; s < 8; ++s) {
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const at_bf16x8_t kf = *(const at_bf16x8_t *)(row + 32 * s);
+            for (int kt = 0; kt < 2; ++kt) {
+                const at_bf16x8_t kf = *(const at_bf16x8_t *)(ks + (kt * 32 + lq) * kKRow + 16 * hh + 32 * s);
                 sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kt], 0, 0, 0);
             }
         }
@@ -244,12 +244,13 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
                                    at_pack2(sacc[kt][r0 + 6], sacc[kt][r0 + 7])};
             pf[s2] = __builtin_bit_cast(at_bf16x8_t, pk);
         }
-        // O^T += V^T P^T, keys in ascending 16-key steps
+        // O^T += V^T P^T, keys in ascending 16-key steps (the four output
+        // tiles' chains alternate)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-            const uint8_t *row = vs + (dt * 32 + lq) * kVRow;
+        for (int s2 = 0; s2 < 4; ++s2) {
 #pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
+            for (int dt = 0; dt < 4; ++dt) {
+                const uint8_t *row = vs + (dt * 32 + lq) * kVRow;
                 const at_u32x2_t lo = *(const at_u32x2_t *)(row + (s2 * 16 + 4 * hh) * 2);
                 const at_u32x2_t hi = *(const at_u32x2_t *)(row + (s2 * 16 + 8 + 4 * hh) * 2);
                 const at_u32x4_t vv = {lo.x, lo.y, hi.x, hi.y};
