@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 6
+#define MOT_ABI_VERSION 7
 
 typedef enum mot_status {
     MOT_OK = 0,
@@ -59,7 +59,8 @@ typedef enum mot_status {
     MOT_ERR_WORKSPACE = 4,         /* workspace missing or smaller than mot_workspace_bytes(T) */
     MOT_ERR_DEVICE = 5,            /* a HIP runtime call or a kernel launch failed */
     MOT_ERR_MODALITY = 6,          /* a modality byte was neither 0 nor 1 (reported by mot_read_device_error) */
-    MOT_ERR_POSITION = 7           /* a rotary position outside its table (reported by mot_read_device_error) */
+    MOT_ERR_POSITION = 7,          /* a rotary position outside its table (reported by mot_read_device_error) */
+    MOT_ERR_SEQLENS = 8            /* packed sequence lengths invalid (reported by mot_read_device_error) */
 } mot_status;
 
 /* Limits checked on the host. */
@@ -248,7 +249,7 @@ int mot_qk_norm_rope(uint16_t *qkv, int64_t ld, int64_t T, int64_t n_q_heads, in
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Synchronises `stream` and returns the workspace's device error word:
- * MOT_OK, MOT_ERR_MODALITY, MOT_ERR_POSITION, or MOT_ERR_DEVICE if the copy
+ * MOT_OK, MOT_ERR_MODALITY, MOT_ERR_POSITION, MOT_ERR_SEQLENS, or MOT_ERR_DEVICE if the copy
  * fails. */
 int mot_read_device_error(const void *workspace, void *stream);
 
@@ -292,6 +293,38 @@ int mot_joint_attention(const uint16_t *q, int64_t ldq, const uint16_t *k, int64
                         int64_t Tq, int64_t Tk, int64_t n_q_heads, int64_t n_kv_heads,
                         int64_t head_dim, int causal, void *workspace, size_t workspace_bytes,
                         void *stream);
+
+/* Workspace bytes of mot_joint_attention_varlen: a MOT_WS_HEADER_BYTES
+ * header (its first int32 is the error word), then the transposed V of the
+ * kv heads, n_kv_heads * 128 rows of round_up(Tk + 63 * n_seqs, 64) bf16.
+ * 0 for invalid sizes.  Since ABI 7. */
+size_t mot_attention_varlen_workspace_bytes(int64_t Tk, int64_t n_seqs, int64_t n_kv_heads);
+
+/* mot_joint_attention over packed sequences: sequence b has the query rows
+ * [cu_q[b], cu_q[b+1]) and the keys [cu_k[b], cu_k[b+1]); each row attends
+ * only over its own sequence's keys, with the causal mask aligned at the
+ * bottom-right corner of that sequence (row i of a sequence of Lq rows and
+ * Lk keys sees its keys j <= i + Lk - Lq).  Several requests (the branches of
+ * a CFG step, prompts of a batch) then share one call, and a row's bytes are
+ * those it gets when its sequence runs alone: the softmax order is fixed per
+ * sequence, from its first key.
+ *   cu_q, cu_k [n_seqs + 1] int32 device arrays: 0 = cu[0] <= ... <=
+ *        cu[n_seqs] = Tq (resp. Tk); no sequence longer than max_q rows.
+ *        They are checked on the device; if they break these rules nothing is
+ *        written and the workspace's error word is MOT_ERR_SEQLENS (read it
+ *        with mot_read_device_error; it is 0 after a valid call).
+ *   max_q: an upper bound on the rows of one sequence (host value; the grid
+ *        is n_seqs x ceil(max_q / 128) x n_q_heads workgroups).
+ *   workspace: >= mot_attention_varlen_workspace_bytes(Tk, n_seqs,
+ *        n_kv_heads) bytes, 256-byte aligned, overwritten.
+ * Other arguments, the arithmetic and the errors as mot_joint_attention.
+ * Tq == 0 is a no-op.  Since ABI 7. */
+int mot_joint_attention_varlen(const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk,
+                               const uint16_t *v, int64_t ldv, uint16_t *out, int64_t ldo,
+                               const int32_t *cu_q, const int32_t *cu_k, int64_t n_seqs,
+                               int64_t Tq, int64_t Tk, int64_t max_q,
+                               int64_t n_q_heads, int64_t n_kv_heads, int64_t head_dim, int causal,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

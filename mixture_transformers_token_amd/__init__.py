@@ -21,11 +21,11 @@ __all__ = [
     "MotError", "ABI_VERSION", "lib", "abi_version", "workspace_bytes", "new_workspace",
     "routing_plan", "plan_view", "routed_gemm", "routed_gemm_f32", "routed_gemm_swiglu", "fused_add_rmsnorm",
     "transpose", "routed_gemm_dx", "grad_w", "qk_norm_rope", "joint_attention",
-    "attention_workspace_bytes",
+    "attention_workspace_bytes", "joint_attention_varlen", "attention_varlen_workspace_bytes",
     "read_device_error", "status_string", "LIB_PATH",
 ]
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
 WS_HEADER_BYTES = 256
 FLAG_PLAN_READY = 1
@@ -38,12 +38,13 @@ EXPORTS = (
     "mot_abi_version", "mot_status_string", "mot_workspace_bytes", "mot_routing_plan",
     "mot_routed_gemm", "mot_routed_gemm_swiglu", "mot_fused_add_rmsnorm", "mot_read_device_error",
     "mot_transpose_bf16", "mot_qk_norm_rope", "mot_routed_gemm_f32", "mot_attention_workspace_bytes",
-    "mot_joint_attention",
+    "mot_joint_attention", "mot_attention_varlen_workspace_bytes", "mot_joint_attention_varlen",
 )
 
 STATUS = {
     0: "MOT_OK", 1: "MOT_ERR_INVALID_ARG", 2: "MOT_ERR_UNSUPPORTED_SHAPE", 3: "MOT_ERR_MISALIGNED",
     4: "MOT_ERR_WORKSPACE", 5: "MOT_ERR_DEVICE", 6: "MOT_ERR_MODALITY", 7: "MOT_ERR_POSITION",
+    8: "MOT_ERR_SEQLENS",
 }
 
 
@@ -93,6 +94,11 @@ def lib():
     L.mot_joint_attention.restype = ctypes.c_int
     L.mot_joint_attention.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, I64, I64, ctypes.c_int, P,
                                       SZ, P]
+    L.mot_attention_varlen_workspace_bytes.restype = SZ
+    L.mot_attention_varlen_workspace_bytes.argtypes = [I64, I64, I64]
+    L.mot_joint_attention_varlen.restype = ctypes.c_int
+    L.mot_joint_attention_varlen.argtypes = [P, I64, P, I64, P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I64, I64,
+                                             ctypes.c_int, P, SZ, P]
     v = L.mot_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"stale libmot.so: ABI {v}, binding expects {ABI_VERSION}; rebuild it")
@@ -403,3 +409,43 @@ def joint_attention(q, k, v, n_q_heads, n_kv_heads, causal=True, out=None, works
                                    1 if causal else 0, _ptr(workspace), workspace.numel(), _stream(q.device))
     _check(st, "mot_joint_attention")
     return out
+
+
+def attention_varlen_workspace_bytes(Tk: int, n_seqs: int, n_kv_heads: int) -> int:
+    return int(lib().mot_attention_varlen_workspace_bytes(int(Tk), int(n_seqs), int(n_kv_heads)))
+
+
+def joint_attention_varlen(q, k, v, cu_q, cu_k, max_q, n_q_heads, n_kv_heads, causal=True, out=None,
+                           workspace=None):
+    """joint_attention over packed sequences: sequence b has the q rows
+    [cu_q[b], cu_q[b+1]) and the keys [cu_k[b], cu_k[b+1]) (int32 GPU
+    tensors of n_seqs + 1 entries, checked on the device; max_q bounds one
+    sequence's rows).  Returns (out, workspace); mot_read_device_error on the
+    workspace reports MOT_ERR_SEQLENS for invalid lengths."""
+    _req(q, "q", torch.bfloat16, 2)
+    _req(k, "k", torch.bfloat16, 2)
+    _req(v, "v", torch.bfloat16, 2)
+    _req(cu_q, "cu_q", torch.int32, 1)
+    _req(cu_k, "cu_k", torch.int32, 1)
+    if cu_q.shape != cu_k.shape or cu_q.shape[0] < 1:
+        raise ValueError("cu_q and cu_k must both hold n_seqs + 1 entries")
+    n_seqs = cu_q.shape[0] - 1
+    Tq, Tk = q.shape[0], k.shape[0]
+    if v.shape[0] != Tk:
+        raise ValueError("k and v must have the same rows")
+    width = 128 * int(n_q_heads)
+    if out is None:
+        out = torch.empty((Tq, width), dtype=torch.bfloat16, device=q.device)
+    _req(out, "out", torch.bfloat16, 2)
+    if out.shape[0] != Tq or out.shape[1] < width:
+        raise ValueError(f"out must be [{Tq}, >= {width}]")
+    if workspace is None:
+        workspace = torch.empty(max(attention_varlen_workspace_bytes(Tk, max(n_seqs, 1), n_kv_heads), 256),
+                                dtype=torch.uint8, device=q.device)
+    cq, ck = cu_q.contiguous(), cu_k.contiguous()
+    st = lib().mot_joint_attention_varlen(_ptr(q), _rows(q, "q"), _ptr(k), _rows(k, "k"), _ptr(v), _rows(v, "v"),
+                                          _ptr(out), _rows(out, "out"), _ptr(cq), _ptr(ck), n_seqs, Tq, Tk,
+                                          int(max_q), int(n_q_heads), int(n_kv_heads), 128, 1 if causal else 0,
+                                          _ptr(workspace), workspace.numel(), _stream(q.device))
+    _check(st, "mot_joint_attention_varlen")
+    return out, workspace

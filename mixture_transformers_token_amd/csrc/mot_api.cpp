@@ -63,6 +63,15 @@ size_t attn_ws_bytes(int64_t Tk, int64_t hkv) {
     return (size_t)(hkv * kAttnHeadDim * round_up(Tk, 64) * 2);
 }
 
+// packed sequences: V^T row pitch (columns), enough for every sequence's keys
+// rounded up to 64
+int64_t attn_varlen_ldvt(int64_t Tk, int64_t n_seqs) { return round_up(Tk + 63 * n_seqs, 64); }
+
+size_t attn_varlen_ws_bytes(int64_t Tk, int64_t n_seqs, int64_t hkv) {
+    if (Tk < 0 || n_seqs <= 0 || hkv <= 0) return 0;
+    return (size_t)(MOT_WS_HEADER_BYTES + hkv * kAttnHeadDim * attn_varlen_ldvt(Tk, n_seqs) * 2);
+}
+
 size_t ws_bytes(int64_t T) {
     return (size_t)(MOT_WS_HEADER_BYTES + round_up(4 * (T > 0 ? T : 0), kWsAlign));
 }
@@ -182,6 +191,7 @@ const char *mot_status_string(int status) {
     case MOT_ERR_DEVICE: return "MOT_ERR_DEVICE: HIP runtime or launch failure";
     case MOT_ERR_MODALITY: return "MOT_ERR_MODALITY: modality byte not 0 or 1";
     case MOT_ERR_POSITION: return "MOT_ERR_POSITION: position outside the rotary table";
+    case MOT_ERR_SEQLENS: return "MOT_ERR_SEQLENS: packed sequence lengths invalid";
     default: return "unknown mot_status";
     }
 }
@@ -341,6 +351,78 @@ int mot_joint_attention(const uint16_t *q, int64_t ldq, const uint16_t *k, int64
     a.hkv = (int)n_kv_heads;
     a.causal = causal;
     a.scale_log2e = (float)(1.4426950408889634074 / sqrt((double)kAttnHeadDim));
+    return mot::launch_attention(a, s) == hipSuccess ? MOT_OK : MOT_ERR_DEVICE;
+}
+
+size_t mot_attention_varlen_workspace_bytes(int64_t Tk, int64_t n_seqs, int64_t n_kv_heads) {
+    return attn_varlen_ws_bytes(Tk, n_seqs, n_kv_heads);
+}
+
+int mot_joint_attention_varlen(const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk, const uint16_t *v,
+                               int64_t ldv, uint16_t *out, int64_t ldo, const int32_t *cu_q, const int32_t *cu_k,
+                               int64_t n_seqs, int64_t Tq, int64_t Tk, int64_t max_q, int64_t n_q_heads,
+                               int64_t n_kv_heads, int64_t head_dim, int causal, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    if (Tq < 0 || Tk < 0 || n_seqs < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads)
+        return MOT_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return MOT_ERR_INVALID_ARG;
+    if (Tq == 0) return MOT_OK;
+    if (n_seqs == 0 || max_q < 1) return MOT_ERR_INVALID_ARG;
+    if (head_dim != kAttnHeadDim || n_q_heads > kAttnMaxHeads) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (Tq > MOT_MAX_T || Tk > MOT_MAX_T || max_q > MOT_MAX_T || n_seqs > 65536) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (n_seqs * n_q_heads * ((max_q + 127) / 128) >= (int64_t(1) << 31)) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (!q || !out || !cu_q || !cu_k || (Tk > 0 && (!k || !v))) return MOT_ERR_INVALID_ARG;
+    const int64_t qw = n_q_heads * kAttnHeadDim, kw = n_kv_heads * kAttnHeadDim;
+    if (ldq < qw || ldo < qw || (Tk > 0 && (ldk < kw || ldv < kw))) return MOT_ERR_INVALID_ARG;
+    if (ldq % 8 || ldo % 8 || (Tk > 0 && (ldk % 8 || ldv % 8))) return MOT_ERR_MISALIGNED;
+    if (!aligned16(q) || !aligned16(out) || (Tk > 0 && (!aligned16(k) || !aligned16(v))) ||
+        (reinterpret_cast<uintptr_t>(cu_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_k) & 3u))
+        return MOT_ERR_MISALIGNED;
+    const size_t wsb = attn_varlen_ws_bytes(Tk, n_seqs, n_kv_heads);
+    if (!workspace || workspace_bytes < wsb) return MOT_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kWsAlign - 1)) != 0) return MOT_ERR_MISALIGNED;
+    const int64_t q_bytes = ((Tq - 1) * ldq + qw) * 2, o_bytes = ((Tq - 1) * ldo + qw) * 2;
+    if (overlaps(out, o_bytes, q, q_bytes) || overlaps(out, o_bytes, workspace, (int64_t)wsb) ||
+        overlaps(workspace, (int64_t)wsb, q, q_bytes))
+        return MOT_ERR_INVALID_ARG;
+    if (Tk > 0) {
+        const int64_t k_bytes = ((Tk - 1) * ldk + kw) * 2, v_bytes = ((Tk - 1) * ldv + kw) * 2;
+        if ((round_up(Tk, 64) * ldk + kw) * 2 >= (int64_t(1) << 32)) return MOT_ERR_UNSUPPORTED_SHAPE;
+        if (overlaps(out, o_bytes, k, k_bytes) || overlaps(out, o_bytes, v, v_bytes) ||
+            overlaps(workspace, (int64_t)wsb, k, k_bytes) || overlaps(workspace, (int64_t)wsb, v, v_bytes))
+            return MOT_ERR_INVALID_ARG;
+    }
+    if ((int64_t)wsb >= (int64_t(1) << 32)) return MOT_ERR_UNSUPPORTED_SHAPE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(s);
+    if (!guard.ok()) return MOT_ERR_DEVICE;
+    int32_t *err = static_cast<int32_t *>(workspace);
+    uint16_t *vt = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + MOT_WS_HEADER_BYTES);
+    const int64_t ldvt = attn_varlen_ldvt(Tk, n_seqs);
+    if (mot::launch_seqlens_check(cu_q, cu_k, (int)n_seqs, Tq, Tk, max_q, err, s) != hipSuccess)
+        return MOT_ERR_DEVICE;
+    if (mot::launch_vt_packed(v, ldv, (int)kw, cu_k, (int)n_seqs, vt, ldvt, err, s) != hipSuccess)
+        return MOT_ERR_DEVICE;
+    mot::AttnArgs a;
+    a.q = q;
+    a.ldq = ldq;
+    a.k = k;
+    a.ldk = ldk;
+    a.vt = vt;
+    a.ldvt = ldvt;
+    a.out = out;
+    a.ldo = ldo;
+    a.Tq = Tq;
+    a.Tk = Tk;
+    a.hq = (int)n_q_heads;
+    a.hkv = (int)n_kv_heads;
+    a.causal = causal;
+    a.scale_log2e = (float)(1.4426950408889634074 / sqrt((double)kAttnHeadDim));
+    a.cu_q = cu_q;
+    a.cu_k = cu_k;
+    a.nseq = (int)n_seqs;
+    a.nqb = (int)((max_q + 127) / 128);
+    a.err = err;
     return mot::launch_attention(a, s) == hipSuccess ? MOT_OK : MOT_ERR_DEVICE;
 }
 

@@ -81,32 +81,53 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int lq = lane & 31, hh = lane >> 5;
+    // Sequence of this workgroup: one sequence, or (packed sequences) the
+    // block's share of nqb query blocks x hq heads of sequence b, whose rows
+    // are [cu_q[b], cu_q[b+1]) and keys [cu_k[b], cu_k[b+1]), and whose V^T
+    // columns start at the sum of the earlier sequences' key counts rounded
+    // up to 64.
+    int64_t Tq = a.Tq, Tk = a.Tk, qs = 0, ks0 = 0, vcol = 0;
+    unsigned rem = blockIdx.x;
+    if (a.cu_q) {
+        if (__builtin_amdgcn_readfirstlane(*(volatile const int32_t *)a.err) != 0) return;  // lengths invalid
+        const int b = (int)(blockIdx.x / (unsigned)(a.nqb * a.hq));
+        rem = blockIdx.x % (unsigned)(a.nqb * a.hq);
+        qs = a.cu_q[b];
+        Tq = a.cu_q[b + 1] - qs;
+        ks0 = a.cu_k[b];
+        Tk = a.cu_k[b + 1] - ks0;
+        for (int j = 0; j < b; ++j) vcol += ((int64_t)(a.cu_k[j + 1] - a.cu_k[j]) + kBK - 1) / kBK * kBK;
+    }
     // heads vary fastest and the query blocks run from the last one down, so
     // that under the causal mask the longest workgroups start first
-    const int nqb = (int)((a.Tq + kBQ - 1) / kBQ);
-    const int h = (int)(blockIdx.x % (unsigned)a.hq);
+    const int nqb = a.cu_q ? a.nqb : (int)((Tq + kBQ - 1) / kBQ);
+    const int h = (int)(rem % (unsigned)a.hq);
     const int kvh = h / (a.hq / a.hkv);
-    const int64_t q0 = (int64_t)(nqb - 1 - (int)(blockIdx.x / (unsigned)a.hq)) * kBQ;
+    const int64_t q0 = (int64_t)(nqb - 1 - (int)(rem / (unsigned)a.hq)) * kBQ;
+    if (q0 >= Tq) return;  // (packed sequences shorter than the longest)
     const int64_t qrow = q0 + wave * 32 + lq;
-    const int64_t shift = a.Tk - a.Tq;  // bottom-right alignment of the causal mask
+    const int64_t shift = Tk - Tq;  // bottom-right alignment of the causal mask
+    const uint16_t *qbase = a.q + qs * a.ldq;
+    const uint16_t *kbase0 = a.k + ks0 * a.ldk;
+    uint16_t *obase = a.out + qs * a.ldo;
 
     // this query's last visible key, and the keys the workgroup needs
-    int64_t last = a.causal ? qrow + shift : a.Tk - 1;
-    if (last > a.Tk - 1) last = a.Tk - 1;
+    int64_t last = a.causal ? qrow + shift : Tk - 1;
+    if (last > Tk - 1) last = Tk - 1;
     // the wave's smallest last visible key: blocks up to it need no mask
-    int64_t wlast = a.causal ? q0 + wave * 32 + shift : a.Tk - 1;
-    if (wlast > a.Tk - 1) wlast = a.Tk - 1;
-    const int64_t qlast = (q0 + kBQ - 1 < a.Tq - 1) ? q0 + kBQ - 1 : a.Tq - 1;
-    int64_t kend = a.causal ? qlast + shift + 1 : a.Tk;
-    if (kend > a.Tk) kend = a.Tk;
+    int64_t wlast = a.causal ? q0 + wave * 32 + shift : Tk - 1;
+    if (wlast > Tk - 1) wlast = Tk - 1;
+    const int64_t qlast = (q0 + kBQ - 1 < Tq - 1) ? q0 + kBQ - 1 : Tq - 1;
+    int64_t kend = a.causal ? qlast + shift + 1 : Tk;
+    if (kend > Tk) kend = Tk;
     const int nkb = kend > 0 ? (int)((kend + kBK - 1) / kBK) : 0;
 
     // Q fragments: row qrow (clamped; rows past Tq are never stored), columns
     // h*128 + 16 s + 8 hh .. +8
     at_bf16x8_t qf[8];
     {
-        const int64_t qr = qrow < a.Tq ? qrow : a.Tq - 1;
-        const uint16_t *qp = a.q + qr * a.ldq + h * kD + 8 * hh;
+        const int64_t qr = qrow < Tq ? qrow : Tq - 1;
+        const uint16_t *qp = qbase + qr * a.ldq + h * kD + 8 * hh;
 #pragma unroll
         for (int s = 0; s < 8; ++s) qf[s] = *(const at_bf16x8_t *)(qp + 16 * s);
     }
@@ -114,8 +135,9 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
     // staging: 1024 16-byte chunks of K (64 rows x 16) and of V^T (128 rows
     // x 8) per block, four of each per thread, through raw buffers (32-bit
     // offsets; K rows past Tk lie past the K buffer's end and read zeros)
-    const at_rsrc_t kres = at_rsrc(a.k + kvh * kD, (uint32_t)(((a.Tk - 1) * a.ldk + (a.hkv - kvh) * kD) * 2));
-    const at_rsrc_t vres = at_rsrc(a.vt + (int64_t)kvh * kD * a.ldvt, (uint32_t)(kD * a.ldvt * 2));
+    const at_rsrc_t kres =
+        at_rsrc(kbase0 + kvh * kD, Tk > 0 ? (uint32_t)(((Tk - 1) * a.ldk + (a.hkv - kvh) * kD) * 2) : 0u);
+    const at_rsrc_t vres = at_rsrc(a.vt + (int64_t)kvh * kD * a.ldvt + vcol, (uint32_t)((kD * a.ldvt - vcol) * 2));
     uint32_t koff[4], voff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -260,8 +282,8 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
         }
     }
 
-    if (qrow >= a.Tq) return;
-    uint16_t *op = a.out + qrow * a.ldo + h * kD + 4 * hh;
+    if (qrow >= Tq) return;
+    uint16_t *op = obase + qrow * a.ldo + h * kD + 4 * hh;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -274,11 +296,95 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
     }
 }
 
+// Checks the packed sequences' cumulative lengths and writes the error word
+// (0, or kErrSeqlens): cu_q and cu_k start at 0, never decrease, end at Tq
+// and Tk, and no sequence has more than max_q rows.  One workgroup.
+constexpr int kErrSeqlens = 8;  // MOT_ERR_SEQLENS
+
+__global__ void __launch_bounds__(256) seqlens_check_kernel(const int32_t *cu_q, const int32_t *cu_k, int n,
+                                                            int64_t Tq, int64_t Tk, int64_t max_q, int32_t *err) {
+    __shared__ int bad;
+    if (threadIdx.x == 0) bad = (cu_q[0] != 0 || cu_k[0] != 0 || cu_q[n] != Tq || cu_k[n] != Tk) ? 1 : 0;
+    __syncthreads();
+    for (int b = (int)threadIdx.x; b < n; b += (int)blockDim.x) {
+        const int64_t lq = (int64_t)cu_q[b + 1] - cu_q[b], lk = (int64_t)cu_k[b + 1] - cu_k[b];
+        if (lq < 0 || lk < 0 || lq > max_q) atomicOr(&bad, 1);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) *err = bad ? kErrSeqlens : 0;
+}
+
+// V^T of packed sequences: out[d][col] for the hkv*128 columns d of v; the
+// columns of sequence b start at off_b = sum over b' < b of its key count
+// rounded up to 64, and hold its keys in order, then zeros up to the next
+// multiple of 64 (and zeros past the last sequence, up to ldo).  One
+// workgroup per 64 output columns (all inside one sequence's range) and 64
+// rows d; LDS tile transpose, 16-byte loads and stores.
+__global__ void __launch_bounds__(256) vt_packed_kernel(const uint16_t *v, int64_t ldv, const int32_t *cu_k, int n,
+                                                        uint16_t *out, int64_t ldo, const int32_t *err) {
+    if (__builtin_amdgcn_readfirstlane(*(volatile const int32_t *)err) != 0) return;
+    __shared__ uint16_t tile[64][72];
+    const int64_t c0 = (int64_t)blockIdx.x * 64;
+    const int d0 = (int)blockIdx.y * 64;
+    // the sequence whose range holds c0
+    int64_t off = 0, ks = 0, len = 0;
+    bool found = false;
+    for (int b = 0; b < n; ++b) {
+        const int64_t l = (int64_t)cu_k[b + 1] - cu_k[b];
+        const int64_t span = (l + 63) / 64 * 64;
+        if (c0 < off + span) {
+            ks = cu_k[b];
+            len = l;
+            found = true;
+            break;
+        }
+        off += span;
+    }
+    const int t = (int)threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int ch = t + 256 * i;          // 512 chunks: 64 keys x 8 chunks of 8 d
+        const int kk = ch >> 3, dc = ch & 7;
+        const int64_t j = c0 - off + kk;     // key within the sequence
+        at_u32x4_t val = {0, 0, 0, 0};
+        if (found && j < len) val = *(const at_u32x4_t *)(v + (ks + j) * ldv + d0 + dc * 8);
+        const uint16_t *e = (const uint16_t *)&val;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) tile[dc * 8 + q][kk] = e[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int ch = t + 256 * i;          // 512 chunks: 64 rows d x 8 chunks of 8 columns
+        const int dd = ch >> 3, cc = ch & 7;
+        at_u32x4_t val;
+        uint16_t *e = (uint16_t *)&val;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[q] = tile[dd][cc * 8 + q];
+        *(at_u32x4_t *)(out + (int64_t)(d0 + dd) * ldo + c0 + cc * 8) = val;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.hq * ((a.Tq + kBQ - 1) / kBQ)));
+    const int64_t nqb = a.cu_q ? a.nqb : (a.Tq + kBQ - 1) / kBQ;
+    const int64_t nseq = a.cu_q ? a.nseq : 1;
+    const dim3 grid((unsigned)(nseq * a.hq * nqb));
     hipLaunchKernelGGL(attention_kernel, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_seqlens_check(const int32_t *cu_q, const int32_t *cu_k, int n, int64_t Tq, int64_t Tk,
+                                int64_t max_q, int32_t *err, hipStream_t stream) {
+    hipLaunchKernelGGL(seqlens_check_kernel, dim3(1), dim3(256), 0, stream, cu_q, cu_k, n, Tq, Tk, max_q, err);
+    return hipGetLastError();
+}
+
+hipError_t launch_vt_packed(const uint16_t *v, int64_t ldv, int kv_cols, const int32_t *cu_k, int n, uint16_t *out,
+                            int64_t ldo, const int32_t *err, hipStream_t stream) {
+    const dim3 grid((unsigned)(ldo / 64), (unsigned)(kv_cols / 64));
+    hipLaunchKernelGGL(vt_packed_kernel, grid, dim3(256), 0, stream, v, ldv, cu_k, n, out, ldo, err);
     return hipGetLastError();
 }
 

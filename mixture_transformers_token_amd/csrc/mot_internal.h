@@ -77,9 +77,18 @@ struct AttnArgs {
     int hq, hkv;          // hq % hkv == 0
     int causal;           // 1: query i sees keys j <= i + (Tk - Tq)
     float scale_log2e;    // fp32 rounding of log2(e)/sqrt(128)
+    // packed sequences (cu_q == nullptr: one sequence of Tq rows, Tk keys)
+    const int32_t *cu_q = nullptr, *cu_k = nullptr;  // [nseq + 1] cumulative rows / keys
+    int nseq = 0;
+    int nqb = 0;                   // query blocks of 128 per sequence (longest)
+    const int32_t *err = nullptr;  // lengths check result; the kernel exits if non-zero
 };
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_seqlens_check(const int32_t *cu_q, const int32_t *cu_k, int n, int64_t Tq, int64_t Tk,
+                                int64_t max_q, int32_t *err, hipStream_t stream);
+hipError_t launch_vt_packed(const uint16_t *v, int64_t ldv, int kv_cols, const int32_t *cu_k, int n, uint16_t *out,
+                            int64_t ldo, const int32_t *err, hipStream_t stream);
 
 hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t *perm,
                        hipStream_t stream);

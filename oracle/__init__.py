@@ -259,3 +259,18 @@ def attention(q, k, v, hq, hkv, causal, rows=None, head_dim=128, threads=0):
         lib().mot_oracle_attention(_p(q), q.shape[1], Tq, _p(k), k.shape[1], _p(v), v.shape[1], Tk, hq, hkv,
                                    head_dim, int(causal), _p(r), n, _p(ref), _p(out), threads)
     return ref, out
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, hq, hkv, causal, head_dim=128, threads=0):
+    """Packed sequences: sequence b is q rows [cu_q[b], cu_q[b+1]) over keys
+    [cu_k[b], cu_k[b+1]), each by attention() -> (ref f64 [Tq, hq*D], out u16)."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    ref = np.zeros((q.shape[0], hq * head_dim), np.float64)
+    out = np.zeros((q.shape[0], hq * head_dim), np.uint16)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 == q0:
+            continue
+        r, o = attention(q[q0:q1], k[k0:k1], v[k0:k1], hq, hkv, causal, head_dim=head_dim, threads=threads)
+        ref[q0:q1], out[q0:q1] = r, o
+    return ref, out

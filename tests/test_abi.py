@@ -278,3 +278,38 @@ def test_attention_workspace_bytes():
 ])
 def test_attention_fails_closed(kw, code):
     assert _attn(**kw) == code
+
+
+def _attn_varlen(**kw):
+    args = dict(q=A, ldq=512, k=2 * A, ldk=256, v=3 * A, ldv=256, out=4 * A, ldo=512, cq=5 * A, ck=5 * A + 64,
+                n=3, Tq=64, Tk=100, maxq=64, hq=4, hkv=2, D=128, causal=1, ws=6 * A, wsb=1 << 20)
+    args.update(kw)
+    return mot.lib().mot_joint_attention_varlen(
+        args["q"], args["ldq"], args["k"], args["ldk"], args["v"], args["ldv"], args["out"], args["ldo"],
+        args["cq"], args["ck"], args["n"], args["Tq"], args["Tk"], args["maxq"], args["hq"], args["hkv"], args["D"],
+        args["causal"], args["ws"], args["wsb"], None)
+
+
+def test_attention_varlen_workspace_bytes():
+    assert mot.attention_varlen_workspace_bytes(100, 0, 2) == 0
+    assert mot.attention_varlen_workspace_bytes(100, 3, 2) == 256 + 2 * 128 * 320 * 2
+    assert mot.attention_varlen_workspace_bytes(0, 1, 1) == 256 + 128 * 64 * 2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Tq=0, q=None), OK),
+    (dict(n=0), INVALID),
+    (dict(maxq=0), INVALID),
+    (dict(cq=None), INVALID),
+    (dict(ck=5 * A + 2), MISALIGNED),
+    (dict(hq=3), INVALID),
+    (dict(D=64), SHAPE),
+    (dict(n=65537), SHAPE),
+    (dict(ws=None), WORKSPACE),
+    (dict(wsb=256 + 2 * 128 * 320 * 2 - 2), WORKSPACE),
+    (dict(ws=6 * A + 16), MISALIGNED),
+    (dict(out=A + 1024), INVALID),
+    (dict(ws=3 * A + 512), INVALID),
+])
+def test_attention_varlen_fails_closed(kw, code):
+    assert _attn_varlen(**kw) == code

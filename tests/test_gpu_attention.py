@@ -112,3 +112,76 @@ def test_attention_rows_batch_invariant():
     b = mot.joint_attention(qd[perm].contiguous(), kd, vd, 4, 2, causal=False)
     torch.cuda.synchronize()
     assert np.array_equal(bits(a)[perm.cpu().numpy()], bits(b))
+
+
+# ---- packed sequences ------------------------------------------------------------
+
+
+def _cu(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_varlen_small(causal):
+    """Five packed sequences of ragged lengths (one with no rows, one with
+    more keys than rows, one with more rows than keys): each row matches the
+    oracle run on its own sequence, and has the bytes of its sequence run
+    alone through the single-sequence call."""
+    lq = [37, 0, 130, 64, 5]
+    lk = [90, 20, 130, 30, 200]
+    cq, ck = _cu(lq), _cu(lk)
+    q, k, v = _inputs(int(cq[-1]), int(ck[-1]), 4, 2, base=1020 + causal, extra=64)
+    got, ws = mot.joint_attention_varlen(dev(q), dev(k), dev(v), dev(torch.from_numpy(cq)),
+                                         dev(torch.from_numpy(ck)), max(lq), 4, 2, causal=causal)
+    assert mot.read_device_error(ws) == 0
+    gb = bits(got)
+    ref, rne = oracle.attention_varlen(W.bits(q), W.bits(k), W.bits(v), cq, ck, 4, 2, causal)
+    check_parity(gb[:, :4 * D], ref, rne, f"attn varlen causal={causal}", one_step=False)
+    for b in range(len(lq)):
+        if lq[b] == 0:
+            continue
+        alone = mot.joint_attention(dev(q[cq[b]:cq[b + 1]]), dev(k[ck[b]:ck[b + 1]]), dev(v[ck[b]:ck[b + 1]]), 4, 2,
+                                    causal=causal)
+        torch.cuda.synchronize()
+        assert np.array_equal(gb[cq[b]:cq[b + 1]], bits(alone)), b
+
+
+def test_attention_varlen_cfg_pack_sampled():
+    """The three-branch CFG pack as three requests and a prompt-only tail
+    (28 q / 4 kv heads): the branches' rows never see each other, sampled
+    rows against the oracle."""
+    lq = [1101, 1101, 1101, 77, 77, 77, 562]
+    cq = _cu(lq)
+    T = int(cq[-1])
+    q, k, v = _inputs(T, T, W.N_Q_HEADS, W.N_K_HEADS, base=1030)
+    got, ws = mot.joint_attention_varlen(dev(q), dev(k), dev(v), dev(torch.from_numpy(cq)),
+                                         dev(torch.from_numpy(cq)), max(lq), W.N_Q_HEADS, W.N_K_HEADS, causal=True)
+    assert mot.read_device_error(ws) == 0
+    gb = bits(got)
+    for b in (0, 2, 5, 6):
+        rows = np.unique(np.r_[0, lq[b] - 1, np.random.default_rng(20 + b).integers(0, lq[b], 4)])
+        ref, rne = oracle.attention(W.bits(q)[cq[b]:cq[b + 1]], W.bits(k)[cq[b]:cq[b + 1]],
+                                    W.bits(v)[cq[b]:cq[b + 1]], W.N_Q_HEADS, W.N_K_HEADS, True, rows=rows)
+        check_parity(gb[cq[b] + rows], ref, rne, f"attn varlen cfg branch {b}", one_step=False)
+
+
+@pytest.mark.parametrize("bad", ["decreasing", "wrong_total", "too_long"])
+def test_attention_varlen_rejects_bad_lengths(bad):
+    """Lengths that break the rules raise MOT_ERR_SEQLENS on the device and
+    leave the output untouched."""
+    lq, lk = [40, 30], [50, 20]
+    cq, ck = _cu(lq), _cu(lk)
+    q, k, v = _inputs(70, 70, 2, 1, base=1040)
+    max_q = 40
+    if bad == "decreasing":
+        cq = np.array([0, 50, 40, 70], np.int32)[[0, 1, 3]]
+        cq[1] = 80  # 0, 80, 70: the second sequence has a negative length
+    elif bad == "wrong_total":
+        ck = np.array([0, 50, 69], np.int32)
+    else:
+        max_q = 30
+    out = torch.full((70, 256), 7.0, dtype=torch.bfloat16, device="cuda")
+    _, ws = mot.joint_attention_varlen(dev(q), dev(k), dev(v), dev(torch.from_numpy(cq)), dev(torch.from_numpy(ck)),
+                                       max_q, 2, 1, causal=True, out=out)
+    assert mot.read_device_error(ws) == 8  # MOT_ERR_SEQLENS
+    assert bool((out == 7.0).all())
