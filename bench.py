@@ -324,14 +324,15 @@ def main():
                                               "TFLOP/s": round(f_gu / s_gu / 1e12, 1)}
         components["down_T4096"] = {"us": round(s_dn * 1e6, 1), "TFLOP/s": round(f_dn / s_dn / 1e12, 1)}
         # per-layer chain: fused add-RMSNorm -> QKV -> QK norm + rotary ->
-        # shared joint attention (causal, the pack as one sequence) -> O ->
+        # shared joint attention (causal within each request: the CFG pack's
+        # seven, the 16384-row pack as one) -> O ->
         # fused add-RMSNorm -> gate/up+SwiGLU -> down, on the three-branch CFG
         # pack and on a 16384-row pack; "TFLOP/s" counts the routed linear
         # steps over real rows only (the CFG pack's 562 padding rows
         # excluded), the attention's time is in the layer time
         ou, og = (t.to(dev) for t in W.o_weights())
-        for name, mc, real in (("cfg_pack_T4096", W.cfg_pack_modality(), 3534),
-                               ("pack_T16384", W.pattern(16384), 16384)):
+        for name, mc, real, lens in (("cfg_pack_T4096", W.cfg_pack_modality(), 3534, W.cfg_pack_lengths()),
+                                     ("pack_T16384", W.pattern(16384), 16384, [16384])):
             Tc = mc.size
             mcd = torch.from_numpy(mc).to(dev)
             xc, rc = (t.to(dev) for t in W.residual_inputs(Tc, K, base=5))
@@ -340,7 +341,9 @@ def main():
             qkv_c = torch.empty((Tc, N), dtype=torch.bfloat16, device=dev)
             o_c = torch.empty((Tc, K), dtype=torch.bfloat16, device=dev)
             att_c = torch.empty((Tc, W.Q_DIM), dtype=torch.bfloat16, device=dev)
-            ws_att_c = torch.empty(mot.attention_workspace_bytes(Tc, W.N_K_HEADS), dtype=torch.uint8, device=dev)
+            cu_c = torch.from_numpy(W.cu_lengths(lens)).to(dev)
+            ws_att_c = torch.empty(mot.attention_varlen_workspace_bytes(Tc, len(lens), W.N_K_HEADS),
+                                   dtype=torch.uint8, device=dev)
             act_c = torch.empty((Tc, W.FFN), dtype=torch.bfloat16, device=dev)
             out_c = torch.empty((Tc, K), dtype=torch.bfloat16, device=dev)
             wsc = mot.new_workspace(Tc, dev)
@@ -350,9 +353,9 @@ def main():
                 "qkv": lambda: mot.routed_gemm(y1, wud, wgd, mcd, out=qkv_c, workspace=wsc),
                 "qk_norm_rope": lambda: mot.qk_norm_rope(qkv_c, W.N_Q_HEADS, W.N_K_HEADS, mcd, qn, kn, pos_c, cos_c,
                                                          sin_c, workspace=wsc),
-                "attention": lambda: mot.joint_attention(qkv_c[:, :W.Q_DIM], qkv_c[:, W.Q_DIM:W.Q_DIM + W.KV_DIM],
-                                                         qkv_c[:, W.Q_DIM + W.KV_DIM:], W.N_Q_HEADS, W.N_K_HEADS,
-                                                         causal=True, out=att_c, workspace=ws_att_c),
+                "attention": lambda: mot.joint_attention_varlen(
+                    qkv_c[:, :W.Q_DIM], qkv_c[:, W.Q_DIM:W.Q_DIM + W.KV_DIM], qkv_c[:, W.Q_DIM + W.KV_DIM:], cu_c,
+                    cu_c, max(lens), W.N_Q_HEADS, W.N_K_HEADS, causal=True, out=att_c, workspace=ws_att_c),
                 "o": lambda: mot.routed_gemm(att_c, ou, og, mcd, out=o_c, workspace=wsc),
                 "norm2": lambda: mot.fused_add_rmsnorm(o_c, res_c, nwu, nwg, mcd, out=y1, rstd=None),
                 "gate_up_swiglu": lambda: mot.routed_gemm_swiglu(y1, gu_u, gu_g, mcd, out=act_c, workspace=wsc),

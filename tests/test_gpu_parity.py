@@ -247,11 +247,11 @@ def test_mlp_full_size_sampled():
     check_parity(bits(y)[rows], ref2, rne2, "mlp down (oracle chain)", one_step=False)
 
 
-def _layer_chain_gpu(x, r, m, wts, rope):
+def _layer_chain_gpu(x, r, m, wts, rope, lengths):
     """fused add-RMSNorm -> QKV -> QK norm + rotary -> shared joint attention
-    (causal over the whole pack) -> O -> fused add-RMSNorm -> gate/up +
-    SwiGLU -> down, every routed step routed by the same modality bytes.
-    Returns {step: (input, output)}."""
+    (causal within each request of `lengths`) -> O -> fused add-RMSNorm ->
+    gate/up + SwiGLU -> down, every routed step routed by the same modality
+    bytes.  Returns {step: (input, output)}."""
     (n1u, n1g), (qu, qg), (ou, og), (n2u, n2g), (gu, gg), (du, dg), (qn, kn) = wts
     cos_t, sin_t, pos = rope
     md = dev(torch.from_numpy(m))
@@ -263,8 +263,11 @@ def _layer_chain_gpu(x, r, m, wts, rope):
     mot.qk_norm_rope(qkv, W.N_Q_HEADS, W.N_K_HEADS, md, tuple(dev(t) for t in qn), tuple(dev(t) for t in kn),
                      dev(pos), dev(cos_t), dev(sin_t), workspace=ws)
     assert mot.read_device_error(ws) == 0
-    att = mot.joint_attention(qkv[:, :W.Q_DIM], qkv[:, W.Q_DIM:W.Q_DIM + W.KV_DIM], qkv[:, W.Q_DIM + W.KV_DIM:],
-                              W.N_Q_HEADS, W.N_K_HEADS, causal=True)
+    cu = dev(torch.from_numpy(W.cu_lengths(lengths)))
+    att, ws_att = mot.joint_attention_varlen(qkv[:, :W.Q_DIM], qkv[:, W.Q_DIM:W.Q_DIM + W.KV_DIM],
+                                             qkv[:, W.Q_DIM + W.KV_DIM:], cu, cu, max(lengths), W.N_Q_HEADS,
+                                             W.N_K_HEADS, causal=True)
+    assert mot.read_device_error(ws_att) == 0
     o = mot.routed_gemm(att, dev(ou), dev(og), md)
     y2, _ = mot.fused_add_rmsnorm(o, res, dev(n2u), dev(n2g), md)
     act = mot.routed_gemm_swiglu(y2, dev(gu), dev(gg), md)
@@ -274,7 +277,7 @@ def _layer_chain_gpu(x, r, m, wts, rope):
             "out": (act, out)}
 
 
-def _layer_chain_oracle(x, r, m, wts, rope, rows):
+def _layer_chain_oracle(x, r, m, wts, rope, rows, lengths):
     """The same chain in the oracle, carrying its own bf16 intermediates.
     The steps up to the QK norm run on every row (the attention of a sampled
     row reads every row's k and v); the rest on the sampled rows.  Returns
@@ -290,8 +293,17 @@ def _layer_chain_oracle(x, r, m, wts, rope, rows):
     ref_q, out_q, err = oracle.qk_norm_rope(qkv_all, W.N_Q_HEADS, W.N_K_HEADS, m, tuple(B(t) for t in qn),
                                             tuple(B(t) for t in kn), pos.numpy(), B(cos_t), B(sin_t))
     assert err == 0
-    att = oracle.attention(out_q[:, :Q], out_q[:, Q:Q + KV], out_q[:, Q + KV:], W.N_Q_HEADS, W.N_K_HEADS, True,
-                           rows=rows)
+    # each sampled row attends within its own request
+    cu = W.cu_lengths(lengths)
+    att_ref = np.empty((rows.size, Q))
+    att_out = np.empty((rows.size, Q), np.uint16)
+    for b in range(len(lengths)):
+        sel = np.nonzero((rows >= cu[b]) & (rows < cu[b + 1]))[0]
+        if sel.size:
+            seq = slice(cu[b], cu[b + 1])
+            att_ref[sel], att_out[sel] = oracle.attention(out_q[seq, :Q], out_q[seq, Q:Q + KV], out_q[seq, Q + KV:],
+                                                          W.N_Q_HEADS, W.N_K_HEADS, True, rows=rows[sel] - cu[b])
+    att = (att_ref, att_out)
     o = oracle.routed_gemm(att[1], B(ou), B(og), m[rows])
     s2 = oracle.fused_add_rmsnorm(o[1], s1["h"][rows], B(n2u), B(n2g), m[rows])
     act = oracle.routed_gemm_swiglu(s2["out"], B(gu), B(gg), m[rows])
@@ -313,9 +325,9 @@ def layer_weights():
 @pytest.mark.parametrize("which", ["cfg_pack", "large_pack"])
 def test_layer_chain_sampled(layer_weights, which):
     """The per-layer chain (routed linear steps and the shared joint
-    attention, causal over the whole pack taken as one sequence) on the
-    three-branch CFG pack (3534 rows padded to 4096) and on the 16384-row
-    mixed pack, against the oracle's own chain on a seeded row sample holding
+    attention, causal within each request: the CFG pack's seven requests,
+    the 16384-row pack as one) on the three-branch CFG pack (3534 rows padded
+    to 4096) and on the 16384-row mixed pack, against the oracle's own chain on a seeded row sample holding
     every segment boundary (every step but the attention is row-local, so
     the sample is an exact restriction; the oracle's attention of a sampled
     row reads every row's k and v).
@@ -329,14 +341,16 @@ def test_layer_chain_sampled(layer_weights, which):
     residual, set or weights) fails by orders of magnitude."""
     if which == "cfg_pack":
         m = W.cfg_pack_modality()
+        lengths = W.cfg_pack_lengths()
     else:
         m = W.pattern(16384)
+        lengths = [16384]
     T = m.size
     x, r = W.residual_inputs(T, W.HIDDEN, base=95)
     rope = W.rope_inputs(T, 4096, base=96)
-    got = _layer_chain_gpu(x, r, m, layer_weights, rope)
+    got = _layer_chain_gpu(x, r, m, layer_weights, rope, lengths)
     rows = W.sample_rows(m, 16, seed=9)
-    want = _layer_chain_oracle(W.bits(x), W.bits(r), m, layer_weights, rope, rows)
+    want = _layer_chain_oracle(W.bits(x), W.bits(r), m, layer_weights, rope, rows, lengths)
     for step in ("qkv", "qk", "att", "o", "act", "out"):
         gin, gout = got[step]
         win, (ref, rne) = want[step]

@@ -81,6 +81,17 @@ def cfg_pack_modality() -> np.ndarray:
     return np.concatenate([body, np.zeros(4096 - 3534, np.uint8)])
 
 
+def cfg_pack_lengths() -> list:
+    """Rows per request of the CFG pack: the three branches, the three
+    prompt-only branches and the padding rows, each its own sequence."""
+    return [1101, 1101, 1101, 77, 77, 77, 4096 - 3534]
+
+
+def cu_lengths(lengths) -> np.ndarray:
+    """Cumulative row counts [0, l0, l0 + l1, ...] as int32."""
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """Raw uint16 view of a CPU bf16 tensor (for the oracle)."""
     assert t.dtype == torch.bfloat16
