@@ -7,7 +7,8 @@ libmot.so is missing or stale, every call raises.
 
 Functions mirror the C ABI:
   routing_plan, routed_gemm, routed_gemm_f32, routed_gemm_swiglu,
-  fused_add_rmsnorm, transpose, qk_norm_rope, joint_attention, read_device_error,
+  fused_add_rmsnorm, transpose, qk_norm_rope, joint_attention,
+  joint_attention_varlen, read_device_error,
   workspace_bytes, abi_version; routed_gemm_dx and grad_w compose them.
 """
 from __future__ import annotations
