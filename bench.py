@@ -133,8 +133,8 @@ def n_gen_rows(m):
 
 def main():
     args = parse()
+    if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the "
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the "
               "routed projection is row-local and would shard by rows", file=sys.stderr)
         sys.exit(2)
     import numpy as np
