@@ -54,6 +54,10 @@ constexpr int kKRow = kD * 2 + 16;   // bytes per staged K row (16 bytes of padd
 // consecutive rows fall on distinct banks
 constexpr int kVRow = kBK * 2 + 8;
 constexpr int kThreads = 256;
+// LDS fragment reads kept this many reads ahead of the MFMAs that use them
+// (scores: K fragments; output: V^T fragments).  The compiler's own order ran
+// them one or two ahead; six measured 2-4% faster (same bytes).
+constexpr int KPF = 6, VPF = 6;
 constexpr float kLazy = 8.0f;        // log2 headroom of the softmax reference max
 
 // Raw buffer over [base, base + bytes): a load past the end reads zeros.
@@ -192,6 +196,13 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
                 sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kt], 0, 0, 0);
             }
         }
+        // K fragment reads KPF ahead of the score MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, KPF, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i + KPF < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
         // mask (only where the block reaches past the wave's first row's
         // last visible key), block maximum of the raw scores
         if ((int64_t)kb * kBK + kBK - 1 > wlast) {
@@ -279,6 +290,12 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
                 oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(at_bf16x8_t, vv), pf[s2],
                                                                    oacc[dt], 0, 0, 0);
             }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, VPF, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i + VPF < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
     }
 
