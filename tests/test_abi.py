@@ -275,6 +275,8 @@ def test_attention_workspace_bytes():
     (dict(out=A + 1024), INVALID),            # out overlaps q
     (dict(out=2 * A), INVALID),               # out overlaps k
     (dict(ws=3 * A + 512), INVALID),          # workspace overlaps v
+    # 2^20 keys at a 4096-column pitch: K past the 32-bit byte offsets
+    (dict(q=G, k=2 * G, v=3 * G, out=4 * G, ws=5 * G, Tk=1 << 20, ldk=4096, ldv=4096, wsb=1 << 32), SHAPE),
 ])
 def test_attention_fails_closed(kw, code):
     assert _attn(**kw) == code
