@@ -187,6 +187,11 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
         // scores of keys kb*64 + [0, 64)
         // (the two tiles' chains alternate, so no MFMA waits on the one
         // just issued; each tile's k order is unchanged)
+        // The MFMA stretches run at raised wave priority: the two waves that
+        // share a SIMD then drift out of phase, one issuing MFMAs while the
+        // other does its softmax arithmetic (measured 4-7% faster, same
+        // bytes).
+        __builtin_amdgcn_s_setprio(1);
         at_f32x16_t sacc[2] = {(at_f32x16_t){}, (at_f32x16_t){}};
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
@@ -203,6 +208,7 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (i + KPF < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
         // mask (only where the block reaches past the wave's first row's
         // last visible key), block maximum of the raw scores
         if ((int64_t)kb * kBK + kBK - 1 > wlast) {
@@ -277,6 +283,7 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
                                    at_pack2(sacc[kt][r0 + 6], sacc[kt][r0 + 7])};
             pf[s2] = __builtin_bit_cast(at_bf16x8_t, pk);
         }
+        __builtin_amdgcn_s_setprio(1);
         // O^T += V^T P^T, keys in ascending 16-key steps (the four output
         // tiles' chains alternate)
 #pragma unroll
@@ -297,6 +304,7 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (i + VPF < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
     }
 
     if (qrow >= Tq) return;
