@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 7
+#define MOT_ABI_VERSION 8
 
 typedef enum mot_status {
     MOT_OK = 0,
@@ -60,7 +60,11 @@ typedef enum mot_status {
     MOT_ERR_DEVICE = 5,            /* a HIP runtime call or a kernel launch failed */
     MOT_ERR_MODALITY = 6,          /* a modality byte was neither 0 nor 1 (reported by mot_read_device_error) */
     MOT_ERR_POSITION = 7,          /* a rotary position outside its table (reported by mot_read_device_error) */
-    MOT_ERR_SEQLENS = 8            /* packed sequence lengths invalid (reported by mot_read_device_error) */
+    MOT_ERR_SEQLENS = 8,           /* packed sequence lengths invalid (reported by mot_read_device_error) */
+    MOT_ERR_PLAN = 9,              /* a plan passed with MOT_FLAG_PLAN_READY does not describe the call's
+                                      T rows (reported by mot_read_device_error; since ABI 8) */
+    MOT_ERR_INDEX_SET = 10         /* a row in neither index set, in both, or twice in one; or an index
+                                      outside [0, T) (reported by mot_read_device_error; since ABI 8) */
 } mot_status;
 
 /* Limits checked on the host. */
@@ -69,7 +73,8 @@ typedef enum mot_status {
 
 /* Workspace layout (device memory, 256-byte aligned, caller-owned):
  *   bytes [0, 16)      int32 header[4] = { error, n_und, n_gen, T }
- *                      error is MOT_OK or MOT_ERR_MODALITY; on error n_und = n_gen = 0.
+ *                      error is MOT_OK or MOT_ERR_MODALITY (MOT_ERR_PLAN, MOT_ERR_INDEX_SET:
+ *                      see below); on error n_und = n_gen = 0.
  *   bytes [256, 256+4T) int32 perm[T]: the rows with modality 0 in ascending
  *                      order, then the rows with modality 1 in ascending order.
  * This stable partition is the pack's segment list: routed kernels cut it into
@@ -95,9 +100,39 @@ size_t mot_workspace_bytes(int64_t T);
 int mot_routing_plan(const uint8_t *modality, int64_t T,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* Modality bytes from the pack's two index sets.  The RFC page (section 1,
+ * item 1) selects each row's weight set by a fixed index set: the rows of
+ * the understanding branch and those of the generation branch.  This call
+ * turns the two lists into the per-row byte the routed calls read:
+ *   modality[und_idx[i]] = 0,  modality[gen_idx[i]] = 1.
+ *   und_idx [n_und], gen_idx [n_gen]: int32 device arrays of row indices, in
+ *        any order; modality [T] uint8 device array, written.
+ *   Every row must appear exactly once over the two lists: n_und + n_gen
+ *   must equal T (checked on the host: MOT_ERR_INVALID_ARG).  On the device,
+ *   a row that is in neither list, in both or twice in one, and any index
+ *   outside [0, T), raise MOT_ERR_INDEX_SET in the workspace's error word
+ *   (read it with mot_read_device_error; it is cleared by the call); such
+ *   rows get the invalid byte 0xFF, so a routed call on these bytes writes
+ *   nothing and reports MOT_ERR_MODALITY.  The result does not depend on the
+ *   lists' order.
+ *   workspace: >= mot_workspace_bytes(T) bytes, 256-byte aligned; its plan
+ *   (header and perm) is overwritten (per-row counts), so build the plan
+ *   afterwards.  No argument may overlap another.
+ * Errors: MOT_ERR_INVALID_ARG, MOT_ERR_UNSUPPORTED_SHAPE, MOT_ERR_MISALIGNED,
+ * MOT_ERR_WORKSPACE, MOT_ERR_DEVICE.  T == 0 (with empty lists) is a no-op.
+ * Since ABI 8. */
+int mot_modality_from_index_sets(const int32_t *und_idx, int64_t n_und, const int32_t *gen_idx, int64_t n_gen,
+                                 uint8_t *modality, int64_t T, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
 /* Flags of the routed GEMM calls. */
 #define MOT_FLAG_PLAN_READY 1u /* workspace already holds the plan of this `modality`,
-                                  built earlier in stream order; skip rebuilding it */
+                                  built earlier in stream order; skip rebuilding it.
+                                  A plan whose header does not describe T rows makes the
+                                  call write nothing and raise MOT_ERR_PLAN (since ABI 8);
+                                  a plan whose error word is set makes it write nothing.
+                                  (Packs of at most 64 rows rebuild their segment list
+                                  from `modality` whatever this flag says.) */
 /* Tile shapes (token rows x weight rows per workgroup).  By default the
  * kernel runs 256x256 tiles for whole rounds of the GPU and 128x128 tiles for
  * the rest, chosen on the device from the pack's set sizes; these flags force
@@ -249,8 +284,8 @@ int mot_qk_norm_rope(uint16_t *qkv, int64_t ld, int64_t T, int64_t n_q_heads, in
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Synchronises `stream` and returns the workspace's device error word:
- * MOT_OK, MOT_ERR_MODALITY, MOT_ERR_POSITION, MOT_ERR_SEQLENS, or MOT_ERR_DEVICE if the copy
- * fails. */
+ * MOT_OK, MOT_ERR_MODALITY, MOT_ERR_POSITION, MOT_ERR_SEQLENS, MOT_ERR_PLAN,
+ * MOT_ERR_INDEX_SET, or MOT_ERR_DEVICE if the copy fails. */
 int mot_read_device_error(const void *workspace, void *stream);
 
 /* Workspace bytes of mot_joint_attention: the transposed V of the kv heads,

@@ -6,7 +6,7 @@ provides device memory and the current stream.  There is no fallback: if
 libmot.so is missing or stale, every call raises.
 
 Functions mirror the C ABI:
-  routing_plan, routed_gemm, routed_gemm_f32, routed_gemm_swiglu,
+  modality_from_index_sets, routing_plan, routed_gemm, routed_gemm_f32, routed_gemm_swiglu,
   fused_add_rmsnorm, transpose, qk_norm_rope, joint_attention,
   joint_attention_varlen, read_device_error,
   workspace_bytes, abi_version; routed_gemm_dx and grad_w compose them.
@@ -20,13 +20,13 @@ import torch
 
 __all__ = [
     "MotError", "ABI_VERSION", "lib", "abi_version", "workspace_bytes", "new_workspace",
-    "routing_plan", "plan_view", "routed_gemm", "routed_gemm_f32", "routed_gemm_swiglu", "fused_add_rmsnorm",
+    "routing_plan", "modality_from_index_sets", "plan_view", "routed_gemm", "routed_gemm_f32", "routed_gemm_swiglu", "fused_add_rmsnorm",
     "transpose", "routed_gemm_dx", "grad_w", "qk_norm_rope", "joint_attention",
     "attention_workspace_bytes", "joint_attention_varlen", "attention_varlen_workspace_bytes",
     "read_device_error", "status_string", "LIB_PATH",
 ]
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
 WS_HEADER_BYTES = 256
 FLAG_PLAN_READY = 1
@@ -40,12 +40,13 @@ EXPORTS = (
     "mot_routed_gemm", "mot_routed_gemm_swiglu", "mot_fused_add_rmsnorm", "mot_read_device_error",
     "mot_transpose_bf16", "mot_qk_norm_rope", "mot_routed_gemm_f32", "mot_attention_workspace_bytes",
     "mot_joint_attention", "mot_attention_varlen_workspace_bytes", "mot_joint_attention_varlen",
+    "mot_modality_from_index_sets",
 )
 
 STATUS = {
     0: "MOT_OK", 1: "MOT_ERR_INVALID_ARG", 2: "MOT_ERR_UNSUPPORTED_SHAPE", 3: "MOT_ERR_MISALIGNED",
     4: "MOT_ERR_WORKSPACE", 5: "MOT_ERR_DEVICE", 6: "MOT_ERR_MODALITY", 7: "MOT_ERR_POSITION",
-    8: "MOT_ERR_SEQLENS",
+    8: "MOT_ERR_SEQLENS", 9: "MOT_ERR_PLAN", 10: "MOT_ERR_INDEX_SET",
 }
 
 
@@ -100,6 +101,8 @@ def lib():
     L.mot_joint_attention_varlen.restype = ctypes.c_int
     L.mot_joint_attention_varlen.argtypes = [P, I64, P, I64, P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I64, I64,
                                              ctypes.c_int, P, SZ, P]
+    L.mot_modality_from_index_sets.restype = ctypes.c_int
+    L.mot_modality_from_index_sets.argtypes = [P, I64, P, I64, P, I64, P, SZ, P]
     v = L.mot_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"stale libmot.so: ABI {v}, binding expects {ABI_VERSION}; rebuild it")
@@ -166,6 +169,30 @@ def routing_plan(modality: torch.Tensor, workspace: torch.Tensor | None = None) 
     _check(lib().mot_routing_plan(_ptr(modality.contiguous()), T, _ptr(workspace),
                                   workspace.numel(), _stream(modality.device)), "mot_routing_plan")
     return workspace
+
+
+def modality_from_index_sets(und_idx: torch.Tensor, gen_idx: torch.Tensor, T: int, out=None,
+                             workspace: torch.Tensor | None = None):
+    """Per-row modality bytes [T] uint8 from the understanding and generation
+    row index lists (int32 GPU tensors, any order).  Every row must be in
+    exactly one list once; otherwise the device raises MOT_ERR_INDEX_SET in
+    the workspace's error word (read_device_error) and marks those rows with
+    the invalid byte 0xFF.  Returns (modality, workspace)."""
+    _req(und_idx, "und_idx", torch.int32, 1)
+    _req(gen_idx, "gen_idx", torch.int32, 1)
+    T = int(T)
+    if out is None:
+        out = torch.empty(T, dtype=torch.uint8, device=und_idx.device)
+    _req(out, "out", torch.uint8, 1)
+    if out.shape[0] != T or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{T}] uint8 tensor")
+    if workspace is None:
+        workspace = new_workspace(T, und_idx.device)
+    u, g = und_idx.contiguous(), gen_idx.contiguous()
+    st = lib().mot_modality_from_index_sets(_ptr(u), u.shape[0], _ptr(g), g.shape[0], _ptr(out), T,
+                                            _ptr(workspace), workspace.numel(), _stream(und_idx.device))
+    _check(st, "mot_modality_from_index_sets")
+    return out, workspace
 
 
 def plan_view(workspace: torch.Tensor, T: int):

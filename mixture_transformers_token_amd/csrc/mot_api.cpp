@@ -192,6 +192,8 @@ const char *mot_status_string(int status) {
     case MOT_ERR_MODALITY: return "MOT_ERR_MODALITY: modality byte not 0 or 1";
     case MOT_ERR_POSITION: return "MOT_ERR_POSITION: position outside the rotary table";
     case MOT_ERR_SEQLENS: return "MOT_ERR_SEQLENS: packed sequence lengths invalid";
+    case MOT_ERR_PLAN: return "MOT_ERR_PLAN: the ready plan does not describe this pack";
+    case MOT_ERR_INDEX_SET: return "MOT_ERR_INDEX_SET: a row is not in exactly one index set, or an index is out of range";
     default: return "unknown mot_status";
     }
 }
@@ -212,6 +214,34 @@ int mot_routing_plan(const uint8_t *modality, int64_t T, void *workspace, size_t
     int32_t *hdr = static_cast<int32_t *>(workspace);
     int32_t *perm = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + MOT_WS_HEADER_BYTES);
     return mot::launch_plan(modality, T, hdr, perm, s) == hipSuccess ? MOT_OK : MOT_ERR_DEVICE;
+}
+
+int mot_modality_from_index_sets(const int32_t *und_idx, int64_t n_und, const int32_t *gen_idx, int64_t n_gen,
+                                 uint8_t *modality, int64_t T, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+    if (T < 0 || n_und < 0 || n_gen < 0) return MOT_ERR_INVALID_ARG;
+    if (T > MOT_MAX_T) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (n_und + n_gen != T) return MOT_ERR_INVALID_ARG;  // some row is in neither list, or in more than one
+    if (T == 0) return MOT_OK;
+    if (!modality || (n_und > 0 && !und_idx) || (n_gen > 0 && !gen_idx)) return MOT_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(und_idx) & 3u) || (reinterpret_cast<uintptr_t>(gen_idx) & 3u))
+        return MOT_ERR_MISALIGNED;
+    if (!workspace || workspace_bytes < ws_bytes(T)) return MOT_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kWsAlign - 1)) != 0) return MOT_ERR_MISALIGNED;
+    const int64_t wsb = (int64_t)ws_bytes(T);
+    if (overlaps(modality, T, workspace, wsb) || (n_und > 0 && overlaps(modality, T, und_idx, 4 * n_und)) ||
+        (n_gen > 0 && overlaps(modality, T, gen_idx, 4 * n_gen)) ||
+        (n_und > 0 && overlaps(workspace, wsb, und_idx, 4 * n_und)) ||
+        (n_gen > 0 && overlaps(workspace, wsb, gen_idx, 4 * n_gen)))
+        return MOT_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(s);
+    if (!guard.ok()) return MOT_ERR_DEVICE;
+    int32_t *err = static_cast<int32_t *>(workspace);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + MOT_WS_HEADER_BYTES);
+    return mot::launch_index_sets(und_idx, n_und, gen_idx, n_gen, modality, T, err, cnt, s) == hipSuccess
+               ? MOT_OK
+               : MOT_ERR_DEVICE;
 }
 
 int mot_routed_gemm(const uint16_t *x, int64_t ldx, const uint16_t *w_und, const uint16_t *w_gen,

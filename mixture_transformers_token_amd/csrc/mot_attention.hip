@@ -60,7 +60,8 @@ constexpr int kThreads = 256;
 constexpr int KPF = 6, VPF = 6;
 constexpr float kLazy = 8.0f;        // log2 headroom of the softmax reference max
 
-// Raw buffer over [base, base + bytes): a load past the end reads zeros.
+// Raw buffer over [base, base + bytes): a load whose per-lane offset lies
+// past the end reads zeros (the wave-uniform offset is not range-checked).
 __device__ __forceinline__ at_rsrc_t at_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -137,8 +138,15 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
     }
 
     // staging: 1024 16-byte chunks of K (64 rows x 16) and of V^T (128 rows
-    // x 8) per block, four of each per thread, through raw buffers (32-bit
-    // offsets; K rows past Tk lie past the K buffer's end and read zeros)
+    // x 8) per block, four of each per thread, through raw buffers with
+    // 32-bit offsets.  The K chunk's whole offset (block row and key row) is
+    // the per-lane offset: only that part of a buffer address is checked
+    // against the buffer's size (the wave-uniform offset is not), so the
+    // rows of a last, partial block that lie past key Tk - 1 start at or
+    // beyond the buffer's end and read zeros instead of memory past the K
+    // view.  V^T offsets stay inside the rows of the workspace (its columns
+    // are padded to a multiple of 64 keys), so its block offset can be the
+    // wave-uniform part.
     const at_rsrc_t kres =
         at_rsrc(kbase0 + kvh * kD, Tk > 0 ? (uint32_t)(((Tk - 1) * a.ldk + (a.hkv - kvh) * kD) * 2) : 0u);
     const at_rsrc_t vres = at_rsrc(a.vt + (int64_t)kvh * kD * a.ldvt + vcol, (uint32_t)((kD * a.ldvt - vcol) * 2));
@@ -151,10 +159,10 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
     }
     at_u32x4_t kr[4], vr[4];
     auto load_block = [&](int kb) {
-        const uint32_t ks0 = (uint32_t)kb * kBK * (uint32_t)a.ldk * 2u, vs0 = (uint32_t)kb * kBK * 2u;
+        const uint32_t kblk = (uint32_t)kb * kBK * (uint32_t)a.ldk * 2u, vs0 = (uint32_t)kb * kBK * 2u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            kr[i] = __builtin_amdgcn_raw_buffer_load_b128(kres, (int)koff[i], (int)ks0, 0);
+            kr[i] = __builtin_amdgcn_raw_buffer_load_b128(kres, (int)(koff[i] + kblk), 0, 0);
             vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, (int)voff[i], (int)vs0, 0);
         }
     };

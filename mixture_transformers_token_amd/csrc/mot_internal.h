@@ -92,6 +92,9 @@ hipError_t launch_vt_packed(const uint16_t *v, int64_t ldv, int kv_cols, const i
 
 hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t *perm,
                        hipStream_t stream);
+// Modality bytes from the und / gen index lists; cnt: T words of scratch.
+hipError_t launch_index_sets(const int32_t *und_idx, int64_t n_und, const int32_t *gen_idx, int64_t n_gen,
+                             uint8_t *modality, int64_t T, int32_t *err, uint32_t *cnt, hipStream_t stream);
 // Launches the persistent routed GEMM (one workgroup per CU at most).  With
 // inline_route the kernel builds (and publishes) the segment list itself.
 hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStream_t stream);

@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -43,6 +44,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kErrModality = 6;  // MOT_ERR_MODALITY
+constexpr int kErrPlan = 9;      // MOT_ERR_PLAN
 
 // ---- bf16 helpers (format definition: upper 16 bits of an IEEE binary32) ----
 
@@ -157,6 +159,63 @@ plan_kernel(const uint8_t *__restrict__ modality, int T, int32_t *__restrict__ h
         hdr[2] = T - n_und;
         hdr[3] = T;
     }
+}
+
+// ============================================================================
+// Modality bytes from the two index sets
+// ============================================================================
+//
+// The pack's rows come as two index lists (understanding rows, generation
+// rows).  Every row must be in exactly one list, once.  Per row, a word of
+// the workspace counts the row's appearances in its low 30 bits (at most
+// n_und + n_gen = T <= 2^24, so it never carries) and every generation-list
+// appearance also adds 2^30; the adds are integer adds, so the result does
+// not depend on their order.  A count of exactly 1 gives the row's byte: 0,
+// or 1 when that one appearance was in the generation list.  Any other
+// count (a row in neither list, in both, or twice in one) gives 0xFF, an
+// invalid byte, and raises MOT_ERR_INDEX_SET (a routed call on those bytes
+// then writes nothing).  An index outside [0, T) raises the same error.
+
+constexpr int kErrIndexSet = 10;  // MOT_ERR_INDEX_SET
+constexpr uint32_t kGenFlag = 1u << 30;
+constexpr uint32_t kCountMask = kGenFlag - 1u;
+
+__global__ void __launch_bounds__(256)
+index_clear_kernel(uint32_t *__restrict__ cnt, int T, int32_t *__restrict__ err) {
+    const int stride = (int)(gridDim.x * blockDim.x);
+    for (int t = (int)(blockIdx.x * blockDim.x + threadIdx.x); t < T; t += stride) cnt[t] = 0u;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
+}
+
+__global__ void __launch_bounds__(256)
+index_count_kernel(const int32_t *__restrict__ und_idx, int n_und, const int32_t *__restrict__ gen_idx,
+                   int n_gen, uint32_t *__restrict__ cnt, int T, int32_t *__restrict__ err) {
+    const int stride = (int)(gridDim.x * blockDim.x);
+    bool bad = false;
+    for (int i = (int)(blockIdx.x * blockDim.x + threadIdx.x); i < n_und + n_gen; i += stride) {
+        const bool is_gen = i >= n_und;
+        const int r = is_gen ? gen_idx[i - n_und] : und_idx[i];
+        if (r < 0 || r >= T) {
+            bad = true;
+            continue;
+        }
+        atomicAdd(cnt + r, is_gen ? kGenFlag + 1u : 1u);
+    }
+    if (bad) atomicMax(err, kErrIndexSet);
+}
+
+__global__ void __launch_bounds__(256)
+index_finish_kernel(const uint32_t *__restrict__ cnt, int T, uint8_t *__restrict__ modality,
+                    int32_t *__restrict__ err) {
+    const int stride = (int)(gridDim.x * blockDim.x);
+    bool bad = false;
+    for (int t = (int)(blockIdx.x * blockDim.x + threadIdx.x); t < T; t += stride) {
+        const uint32_t c = cnt[t];
+        const uint8_t m = (c & kCountMask) == 1u ? (uint8_t)(c >> 30) : (uint8_t)0xFF;
+        bad |= m == 0xFF;
+        modality[t] = m;
+    }
+    if (bad) atomicMax(err, kErrIndexSet);
 }
 
 // ============================================================================
@@ -446,9 +505,14 @@ typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 // Direct global->LDS 16-byte buffer load: lane L's 16 bytes land at
-// lds + 16*L.  The buffer resource covers exactly one operand, so an offset
-// past its end reads zeros instead of faulting; `voff` is the lane's byte
-// offset, `soff` the wave-uniform k offset.  Operands are limited to 4 GiB.
+// lds + 16*L.  `voff` is the lane's byte offset (a row start plus a 16-byte
+// chunk of the row's first 64 columns), `soff` the wave-uniform k offset
+// (k-block * 128 bytes, below the row's K columns).  The GEMMs stage only
+// valid rows (rows past a tile's end repeat a valid row, weight rows are
+// clamped to the last one), so voff + soff always lies inside the operand;
+// only voff is checked against the resource's size by the hardware, which
+// is why the kernels never rely on that check.  Operands are limited to
+// 4 GiB (32-bit offsets).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer, gfx9 data format word
 
@@ -1077,11 +1141,21 @@ gemm_kernel(GemmArgs a) {
         if (bad) return;  // the pack holds an invalid byte: write nothing
     } else {
         const int32_t *hdr = a.hdr;
+        const int e0 = hdr[0];
         U = hdr[1];
         G = hdr[2];
-        // a plan that does not describe exactly T rows (error, or a stale plan
-        // passed with MOT_FLAG_PLAN_READY) makes every workgroup exit
-        if (hdr[0] != 0 || hdr[3] != T || U < 0 || G < 0 || U + G != T) return;
+        // A plan whose error word is set makes every workgroup exit (the word
+        // already reports why).  A plan that does not describe exactly T rows
+        // (a stale plan, or one of another pack, passed with
+        // MOT_FLAG_PLAN_READY) fails closed too: nothing is written and
+        // workgroup 0 raises MOT_ERR_PLAN in the error word, after every
+        // workgroup has read the header (the others see the same header, so
+        // they exit as well).
+        if (e0 != 0) return;
+        if (hdr[3] != T || U < 0 || G < 0 || U + G != T) {
+            if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr_out[0] = kErrPlan;
+            return;
+        }
     }
     // per-wave epilogue staging: array `wave` of the first four
     const int wave_id = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -1512,7 +1586,12 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
             a.perm_out[(m ? U : 0) + rank] = lane;
         }
     }
-    if (bad) return;  // the pack holds an invalid byte: write nothing (all waves)
+    if (bad) {
+        // the pack holds an invalid byte: write nothing (all waves), and
+        // raise the error word also when a ready plan was passed
+        if (!publish && blockIdx.x == 0 && threadIdx.x == 0) a.hdr_out[0] = kErrModality;
+        return;
+    }
     const uint64_t mine = set ? gen : und;
     const int count = __popcll(mine);
     if (count == 0) return;  // all waves
@@ -1696,6 +1775,18 @@ transpose_kernel(const uint16_t *__restrict__ in, int64_t ld_in, int rows, int c
 // ============================================================================
 // Launchers
 // ============================================================================
+
+hipError_t launch_index_sets(const int32_t *und_idx, int64_t n_und, const int32_t *gen_idx, int64_t n_gen,
+                             uint8_t *modality, int64_t T, int32_t *err, uint32_t *cnt, hipStream_t stream) {
+    const auto blocks = [](int64_t n) { return dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 4096))); };
+    hipLaunchKernelGGL(index_clear_kernel, blocks(T), dim3(256), 0, stream, cnt, (int)T, err);
+    if (n_und + n_gen > 0)
+        hipLaunchKernelGGL(index_count_kernel, blocks(n_und + n_gen), dim3(256), 0, stream, und_idx, (int)n_und,
+                           gen_idx, (int)n_gen, cnt, (int)T, err);
+    hipLaunchKernelGGL(index_finish_kernel, blocks(T), dim3(256), 0, stream, (const uint32_t *)cnt, (int)T,
+                       modality, err);
+    return hipGetLastError();
+}
 
 hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t *perm,
                        hipStream_t stream) {

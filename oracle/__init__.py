@@ -111,6 +111,37 @@ def routing_plan(modality: np.ndarray):
     return perm, int(nu[0]), int(ng[0])
 
 
+ERR_INDEX_SET = 10  # a row not in exactly one index set, or an index outside [0, T)
+
+
+def modality_from_index_sets(und_idx, gen_idx, T):
+    """Per-row modality bytes from the two index sets (RL-Kernel RFC page,
+    section 1, item 1: each row's weight set is fixed by an index set).  A
+    row listed exactly once, in the understanding list, gets 0; exactly once,
+    in the generation list, 1; any other row (in neither list, in both, or
+    twice in one) gets the invalid byte 0xFF and the call reports
+    ERR_INDEX_SET, as does an index outside [0, T) (which marks no row).
+    Plain loops over the lists.  Returns (modality uint8 [T], error)."""
+    count = [0] * T
+    in_gen = [False] * T
+    err = 0
+    for lst, is_gen in ((und_idx, False), (gen_idx, True)):
+        for r in np.asarray(lst).tolist():
+            if not 0 <= r < T:
+                err = ERR_INDEX_SET
+                continue
+            count[r] += 1
+            in_gen[r] = in_gen[r] or is_gen
+    m = np.empty(T, np.uint8)
+    for t in range(T):
+        if count[t] == 1:
+            m[t] = 1 if in_gen[t] else 0
+        else:
+            m[t] = 0xFF
+            err = ERR_INDEX_SET
+    return m, err
+
+
 def routed_gemm(x, w_und, w_gen, modality, want_ref=True, want_out=True, threads=0):
     """x [T,K] uint16, w_* [N,K] uint16, modality [T] uint8 -> (ref f64 [T,N], out u16 [T,N])."""
     x = _u16(x)

@@ -315,3 +315,30 @@ def test_attention_varlen_workspace_bytes():
 ])
 def test_attention_varlen_fails_closed(kw, code):
     assert _attn_varlen(**kw) == code
+
+
+def _index_sets(**kw):
+    args = dict(u=A, nu=24, g=2 * A, ng=40, m=3 * A, T=64, ws=4 * A, wsb=1 << 20)
+    args.update(kw)
+    return mot.lib().mot_modality_from_index_sets(args["u"], args["nu"], args["g"], args["ng"], args["m"],
+                                                  args["T"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID),
+    (dict(nu=-1, ng=65), INVALID),
+    (dict(nu=24, ng=41), INVALID),            # n_und + n_gen != T: some row in neither or in both
+    (dict(nu=0, ng=0, T=0, u=None, g=None, m=None), OK),  # empty pack
+    (dict(m=None), INVALID),
+    (dict(u=None), INVALID),
+    (dict(g=None), INVALID),
+    (dict(u=A + 2), MISALIGNED),
+    (dict(ws=None), WORKSPACE),
+    (dict(wsb=300), WORKSPACE),
+    (dict(ws=4 * A + 16), MISALIGNED),
+    (dict(m=A + 8), INVALID),                 # modality overlaps the und list
+    (dict(ws=3 * A), INVALID),                # workspace overlaps modality
+    (dict(T=(1 << 24) + 1, nu=(1 << 24) + 1, ng=0), SHAPE),
+])
+def test_index_sets_fail_closed(kw, code):
+    assert _index_sets(**kw) == code

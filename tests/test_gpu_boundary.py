@@ -1,0 +1,148 @@
+"""Boundary behaviour on the GPU, through the C ABI: the modality bytes built
+from the two index sets (RL-Kernel RFC page, section 1, item 1: the weight
+set of a row is fixed by an index set), and a ready plan that does not
+describe the pack (the same page's section 3: fail closed)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_transformers_token_amd as mot
+import oracle
+import workloads as W
+from helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+ERR_MODALITY, ERR_PLAN, ERR_INDEX_SET = 6, 9, 10
+
+
+def _lists(m, seed):
+    rng = np.random.default_rng(seed)
+    und = np.flatnonzero(m == 0).astype(np.int32)
+    gen = np.flatnonzero(m == 1).astype(np.int32)
+    return rng.permutation(und).astype(np.int32), rng.permutation(gen).astype(np.int32)
+
+
+def _run_index_sets(und, gen, T):
+    out = torch.full((max(T, 1),), 0x5A, dtype=torch.uint8, device="cuda")[:T]
+    m, ws = mot.modality_from_index_sets(dev(torch.from_numpy(und)), dev(torch.from_numpy(gen)), T, out=out)
+    return m.cpu().numpy(), mot.read_device_error(ws), ws
+
+
+@pytest.mark.parametrize("T", [1, 77, 1101, 4096, 16384, 40000])
+def test_index_sets_give_the_modality_bytes(T):
+    m_want = W.pattern(T) if T % 2 == 0 else np.random.default_rng(T).integers(0, 2, T).astype(np.uint8)
+    und, gen = _lists(m_want, T)
+    m, err, _ = _run_index_sets(und, gen, T)
+    m_or, err_or = oracle.modality_from_index_sets(und, gen, T)
+    assert err == err_or == 0
+    assert np.array_equal(m, m_or) and np.array_equal(m, m_want)
+    # the segment list built from those bytes is the two lists, each sorted
+    perm, nu, ng = oracle.routing_plan(m)
+    ws = mot.routing_plan(dev(torch.from_numpy(m)))
+    hdr, gperm = mot.plan_view(ws, T)
+    assert list(hdr.cpu().numpy()) == [0, nu, ng, T]
+    assert np.array_equal(gperm.cpu().numpy(), np.concatenate([np.sort(und), np.sort(gen)]))
+
+
+@pytest.mark.parametrize("case", ["both_and_neither", "twice_in_und", "out_of_range", "negative", "all_gen"])
+def test_index_set_errors_match_the_oracle(case):
+    T = 1101
+    m0 = W.pattern(T)
+    und, gen = _lists(m0, 5)
+    if case == "both_and_neither":
+        gen = gen.copy()
+        gen[10] = und[3]          # und[3]'s row in both lists, gen[10]'s old row in neither
+    elif case == "twice_in_und":
+        und = und.copy()
+        und[1] = und[0]
+    elif case == "out_of_range":
+        gen = gen.copy()
+        gen[0] = T
+    elif case == "negative":
+        und = und.copy()
+        und[-1] = -1
+    elif case == "all_gen":
+        und, gen = np.zeros(0, np.int32), np.random.default_rng(1).permutation(T).astype(np.int32)
+    m, err, _ = _run_index_sets(und, gen, T)
+    m_or, err_or = oracle.modality_from_index_sets(und, gen, T)
+    assert err == err_or
+    assert np.array_equal(m, m_or)
+    if case == "all_gen":
+        assert err == 0 and np.all(m == 1)
+    else:
+        assert err == ERR_INDEX_SET and np.any(m == 0xFF)
+
+
+def test_index_set_error_makes_the_gemm_write_nothing():
+    T, K, N = 300, 128, 128
+    und, gen = _lists(W.pattern(T), 9)
+    gen = gen.copy()
+    gen[2] = und[2]
+    m, err, _ = _run_index_sets(und, gen, T)
+    assert err == ERR_INDEX_SET
+    x, wu, wg, _ = W.gemm_case(T, K, N, np.zeros(T, np.uint8), base=63)
+    ws = mot.new_workspace(T, "cuda")
+    y = torch.full((T, N), 5.0, dtype=torch.bfloat16, device="cuda")
+    mot.routed_gemm(dev(x), dev(wu), dev(wg), dev(torch.from_numpy(m)), out=y, workspace=ws)
+    assert mot.read_device_error(ws) == ERR_MODALITY
+    assert torch.all(y == 5.0)
+
+
+def test_index_sets_clear_a_previous_error():
+    T = 100
+    und, gen = _lists(W.pattern(T), 2)
+    bad = gen.copy()
+    bad[0] = T + 5
+    _, err, ws = _run_index_sets(und, bad, T)
+    assert err == ERR_INDEX_SET
+    m, _ = mot.modality_from_index_sets(dev(torch.from_numpy(und)), dev(torch.from_numpy(gen)), T, workspace=ws)
+    assert mot.read_device_error(ws) == 0
+    assert np.array_equal(m.cpu().numpy(), W.pattern(T))
+
+
+@pytest.mark.parametrize("T_plan,T", [(100, 200), (4000, 4096), (4096, 4000), (9000, 9001)])
+def test_stale_ready_plan_fails_closed(T_plan, T):
+    """A plan built for another pack size, passed with plan_ready, makes the
+    GEMM write nothing and raise MOT_ERR_PLAN."""
+    K, N = 128, 384
+    ws = mot.new_workspace(max(T, T_plan), "cuda")
+    mot.routing_plan(dev(torch.from_numpy(W.pattern(T_plan))), workspace=ws)
+    assert mot.read_device_error(ws) == 0
+    m = W.pattern(T)
+    x, wu, wg, _ = W.gemm_case(T, K, N, m, base=64)
+    y = torch.full((T, N), 5.0, dtype=torch.bfloat16, device="cuda")
+    mot.routed_gemm(dev(x), dev(wu), dev(wg), dev(torch.from_numpy(m)), out=y, workspace=ws, plan_ready=True)
+    assert mot.read_device_error(ws) == ERR_PLAN
+    assert torch.all(y == 5.0)
+    act = torch.full((T, N // 2), 5.0, dtype=torch.bfloat16, device="cuda")
+    mot.routing_plan(dev(torch.from_numpy(W.pattern(T_plan))), workspace=ws)
+    mot.routed_gemm_swiglu(dev(x), dev(wu), dev(wg), dev(torch.from_numpy(m)), out=act, workspace=ws,
+                           plan_ready=True)
+    assert mot.read_device_error(ws) == ERR_PLAN
+    assert torch.all(act == 5.0)
+    # the matching plan through the same workspace computes the pack
+    mot.routing_plan(dev(torch.from_numpy(m)), workspace=ws)
+    mot.routed_gemm(dev(x), dev(wu), dev(wg), dev(torch.from_numpy(m)), out=y, workspace=ws, plan_ready=True)
+    assert mot.read_device_error(ws) == 0
+    ref = mot.routed_gemm(dev(x), dev(wu), dev(wg), dev(torch.from_numpy(m)))
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+
+
+def test_small_pack_with_ready_plan_reports_bad_bytes():
+    """Packs of at most 64 rows rebuild their segment list from the bytes; an
+    invalid byte still writes nothing and raises the error word when a ready
+    plan was passed."""
+    T, K, N = 40, 128, 128
+    m = W.pattern(T)
+    ws = mot.routing_plan(dev(torch.from_numpy(m)))
+    m_bad = m.copy()
+    m_bad[7] = 4
+    x, wu, wg, _ = W.gemm_case(T, K, N, m, base=65)
+    y = torch.full((T, N), 5.0, dtype=torch.bfloat16, device="cuda")
+    mot.routed_gemm(dev(x), dev(wu), dev(wg), dev(torch.from_numpy(m_bad)), out=y, workspace=ws, plan_ready=True)
+    assert mot.read_device_error(ws) == ERR_MODALITY
+    assert torch.all(y == 5.0)

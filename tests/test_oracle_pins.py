@@ -679,3 +679,195 @@ def test_pins_catch_planted_attention_mistakes():
     for kw in (dict(align="top_left"), dict(kv_map="round_robin"), dict(scale=False)):
         assert np.abs(ref - _torch_attention(q, k, v, 4, 2, True, **kw)).max() > 1e-2, kw
     assert np.abs(ref - _torch_attention(q, k, v, 4, 2, False)).max() > 1e-2
+
+
+# ---- packed sequences (attention over several requests in one pack) ---------
+
+def _torch_attention_packed(q, k, v, cu_q, cu_k, hq, hkv, causal, keys_by="cu_k", align="per_seq"):
+    """The packed op as ONE torch fp64 attention over the whole pack with a
+    block-diagonal mask: query row i of sequence b sees key j of sequence b
+    (and, causal, j - cu_k[b] <= (i - cu_q[b]) + Lk - Lq).  Rows that see no
+    key are zero.  keys_by / align plant mistakes: keys cut by the query
+    offsets, or the causal mask aligned at the whole pack's corner."""
+    D = 128
+    Tq, Tk = q.shape[0], k.shape[0]
+    Q = torch.from_numpy(oracle.bf16_to_f64(q[:, :hq * D])).view(Tq, hq, D).transpose(0, 1)
+    K = torch.from_numpy(oracle.bf16_to_f64(k[:, :hkv * D])).view(Tk, hkv, D).transpose(0, 1)
+    V = torch.from_numpy(oracle.bf16_to_f64(v[:, :hkv * D])).view(Tk, hkv, D).transpose(0, 1)
+    idx = torch.arange(hq) // (hq // hkv)
+    K, V = K[idx], V[idx]
+    ck = list(cu_q) if keys_by == "cu_q" else list(cu_k)
+    mask = torch.zeros((Tq, Tk), dtype=torch.bool)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(ck[b]), int(ck[b + 1])
+        for i in range(q0, q1):
+            for j in range(k0, min(k1, Tk)):
+                if not causal:
+                    ok = True
+                elif align == "per_seq":
+                    ok = (j - k0) <= (i - q0) + (k1 - k0) - (q1 - q0)
+                else:
+                    ok = j <= i + (Tk - Tq)
+                mask[i, j] = ok
+    out = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask)
+    out = out.transpose(0, 1).reshape(Tq, hq * D)
+    seen = mask.any(1)
+    out[~seen] = 0.0
+    return out.numpy()
+
+
+# ragged requests: one empty, one with more keys than rows (a cached prefix),
+# one with more rows than keys (its first rows see nothing when causal)
+_PACKS = [([0, 17, 17, 40, 71, 72], [0, 30, 31, 40, 90, 92]),
+          ([0, 64, 130], [0, 64, 129])]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("pack", range(len(_PACKS)))
+def test_attention_varlen_matches_block_diagonal_torch(pack, causal):
+    cu_q, cu_k = _PACKS[pack]
+    q, k, v = _attn_case(cu_q[-1], cu_k[-1], 4, 2, base=930 + pack)
+    ref, out = oracle.attention_varlen(q, k, v, cu_q, cu_k, 4, 2, causal)
+    want = _torch_attention_packed(q, k, v, cu_q, cu_k, 4, 2, causal)
+    assert np.abs(ref - want).max() <= 1e-12
+    for r in (0, cu_q[-1] - 1):
+        for c in (0, 300):
+            assert out[r, c] == oracle.bf16_round(ref[r, c])
+
+
+def _varlen_mutant(q, k, v, cu_q, cu_k, hq, hkv, causal, mistake):
+    """oracle.attention_varlen with a planted mistake, on the CPU."""
+    ref = np.zeros((q.shape[0], hq * 128))
+    for b in range(len(cu_q) - 1):
+        q0, q1 = cu_q[b], cu_q[b + 1]
+        k0, k1 = (cu_q[b], cu_q[b + 1]) if mistake == "keys_by_cu_q" else (cu_k[b], cu_k[b + 1])
+        if mistake == "keys_from_zero":
+            k0 = 0
+        if q1 == q0:
+            continue
+        r, _ = oracle.attention(q[q0:q1], k[k0:k1], v[k0:k1], hq, hkv, causal)
+        ref[q0:q1] = r
+    return ref
+
+
+def test_pins_catch_planted_varlen_mistakes():
+    cu_q, cu_k = _PACKS[0]
+    q, k, v = _attn_case(cu_q[-1], cu_k[-1], 4, 2, base=940)
+    want = _torch_attention_packed(q, k, v, cu_q, cu_k, 4, 2, True)
+    assert np.abs(_varlen_mutant(q, k, v, cu_q, cu_k, 4, 2, True, None) - want).max() <= 1e-12
+    for mistake in ("keys_by_cu_q", "keys_from_zero"):
+        assert np.abs(_varlen_mutant(q, k, v, cu_q, cu_k, 4, 2, True, mistake) - want).max() > 1e-2, mistake
+    # the pin itself tells the per-sequence alignment from the pack's corner
+    assert np.abs(_torch_attention_packed(q, k, v, cu_q, cu_k, 4, 2, True, align="pack") - want).max() > 1e-2
+
+
+# ---- the gate's metrics and the bf16 step distance ----------------------------
+
+def _all_finite_bf16():
+    """Every finite bf16 pattern, and its rank among the distinct finite
+    values in increasing order (+0 and -0 share a rank)."""
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.bf16_to_f64(pats)
+    fin = np.isfinite(vals)
+    pats, vals = pats[fin], vals[fin]
+    distinct = np.unique(vals)
+    rank = np.searchsorted(distinct, vals)
+    return pats, vals, dict(zip(pats.tolist(), rank.tolist()))
+
+
+def test_ulp_distance_is_rank_difference():
+    """The bf16 step distance equals the difference of the two values' ranks
+    among all distinct finite bf16 values -- checked on the sign boundary,
+    the subnormals, the largest values and random pairs."""
+    pats, _, rank = _all_finite_bf16()
+    rng = np.random.default_rng(3)
+    edge = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x807F, 0x8080, 0x3F80, 0xBF80,
+                     0x7F7F, 0xFF7F, 0x7F7E, 0x3F7F], np.uint16)
+    a = np.concatenate([np.repeat(edge, edge.size), rng.choice(pats, 20000)])
+    b = np.concatenate([np.tile(edge, edge.size), rng.choice(pats, 20000)])
+    want = np.abs(np.array([rank[x] for x in a.tolist()]) - np.array([rank[x] for x in b.tolist()]))
+    assert np.array_equal(oracle.ulp_distance(a, b), want)
+    # a count of raw patterns, without the sign handling, is wrong across zero
+    raw = np.abs(a.astype(np.int64) - b.astype(np.int64))
+    assert not np.array_equal(raw, want)
+
+
+def test_gate_metrics_hand_worked():
+    """A hand-worked case: ref = (3, -4, 0, 0.5); got = bf16 (3, -4.03125,
+    0.0078125, 0.5).  Differences (0, -1/32, 1/128, 0): max-abs 1/32,
+    ||d|| = sqrt(1/1024 + 1/16384) = sqrt(17)/128, ||ref|| = sqrt(25.25),
+    elementwise excess max(|d| - (2e-2 + 1.6e-2|ref|)) over (-0.068,
+    -0.05275, -0.0121875, -0.028) at the third entry: 1/128 - 2e-2; bf16 step
+    distance to RNE(ref): 0, 1, 0x3C00 patterns up from 0 (1/128 = 2^-7:
+    biased exponent 120, so 120*128 = 15360), 0."""
+    ref = np.array([3.0, -4.0, 0.0, 0.5])
+    got = np.array([0x4040, 0xC081, 0x3C00, 0x3F00], np.uint16)
+    assert list(oracle.bf16_to_f64(got)) == [3.0, -4.03125, 0.0078125, 0.5]
+    m = oracle.gate_metrics(got, ref)
+    assert m["max_abs"] == 1 / 32
+    assert math.isclose(m["rel_fro"], math.sqrt(17) / 128 / math.sqrt(25.25), rel_tol=1e-14)
+    assert math.isclose(m["elem_excess"], 1 / 128 - 2e-2, rel_tol=1e-14)
+    assert m["max_ref"] == 4.0
+    assert m["max_ulp_to_rne"] == 15360
+
+
+def test_gate_metrics_against_fsum_and_planted_mistakes():
+    """The metrics against a plain re-derivation with math.fsum on random
+    data, and two plausible mistakes that the re-derivation tells apart:
+    the Frobenius error relative to the GPU result's norm instead of the
+    reference's, and the max-abs error taken without the absolute value."""
+    rng = np.random.default_rng(11)
+    ref = rng.standard_normal(500) * 3
+    got = np.array([oracle.bf16_round(v + 0.01 * rng.standard_normal()) for v in ref], np.uint16)
+    g = oracle.bf16_to_f64(got)
+    d = [gi - ri for gi, ri in zip(g.tolist(), ref.tolist())]
+    want_rel = math.sqrt(math.fsum(x * x for x in d)) / math.sqrt(math.fsum(x * x for x in ref.tolist()))
+    want_max = max(abs(x) for x in d)
+    want_exc = max(abs(x) - (2e-2 + 1.6e-2 * abs(r)) for x, r in zip(d, ref.tolist()))
+    m = oracle.gate_metrics(got, ref)
+    assert math.isclose(m["rel_fro"], want_rel, rel_tol=1e-12)
+    assert m["max_abs"] == want_max and math.isclose(m["elem_excess"], want_exc, rel_tol=1e-12, abs_tol=1e-15)
+    wrong_rel = math.sqrt(math.fsum(x * x for x in d)) / math.sqrt(math.fsum(x * x for x in g.tolist()))
+    assert not math.isclose(wrong_rel, want_rel, rel_tol=1e-9)
+    assert max(d) != want_max or min(d) > -want_max
+
+
+# ---- modality bytes from the two index sets -----------------------------------
+
+def test_index_sets_brute_force():
+    """Every way of listing the rows of a pack of up to 3 rows, each row
+    placed 0, 1 or 2 times in each list (plus an out-of-range index): the
+    byte is 0 or 1 exactly for the rows listed once overall, and the error
+    is raised exactly when some row is not, or an index is out of range."""
+    import itertools
+    for T in range(0, 4):
+        for placing in itertools.product(range(9), repeat=T):
+            und, gen = [], []
+            for r, p in enumerate(placing):
+                und += [r] * (p % 3)
+                gen += [r] * (p // 3)
+            for extra in ((), (T,)):
+                m, err = oracle.modality_from_index_sets(np.array(und, np.int64),
+                                                         np.array(gen + list(extra), np.int64), T)
+                ok = True
+                for r, p in enumerate(placing):
+                    nu, ng = p % 3, p // 3
+                    if nu + ng == 1:
+                        assert m[r] == (1 if ng else 0)
+                    else:
+                        assert m[r] == 0xFF
+                        ok = False
+                assert (err == 0) == (ok and not extra)
+
+
+def test_index_sets_round_trip_to_the_segment_list():
+    """For a valid split the bytes are the pack's modality, and the routing
+    plan of those bytes lists each index set in ascending order."""
+    m0 = W.pattern(2202)
+    rng = np.random.default_rng(4)
+    und = rng.permutation(np.flatnonzero(m0 == 0))
+    gen = rng.permutation(np.flatnonzero(m0 == 1))
+    m, err = oracle.modality_from_index_sets(und, gen, m0.size)
+    assert err == 0 and np.array_equal(m, m0)
+    perm, nu, ng = oracle.routing_plan(m)
+    assert np.array_equal(perm, np.concatenate([np.sort(und), np.sort(gen)])) and (nu, ng) == (und.size, gen.size)
