@@ -60,6 +60,8 @@ def lib():
         L.mot_oracle_fused_add_rmsnorm.argtypes = [P, P, P, P, P, ctypes.c_float, I64, I64,
                                                    P, P, P, P, ctypes.c_int]
         L.mot_oracle_fused_add_rmsnorm.restype = None
+        L.mot_oracle_rmsnorm_apply.argtypes = [P, P, P, P, P, I64, I64, P, P, ctypes.c_int]
+        L.mot_oracle_rmsnorm_apply.restype = None
         L.mot_oracle_qk_norm_rope.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P, P, P, P, I64,
                                               ctypes.c_float, P, P, ctypes.c_int]
         L.mot_oracle_qk_norm_rope.restype = ctypes.c_int
@@ -221,6 +223,24 @@ def fused_add_rmsnorm(x, r, w_und, w_gen, modality, eps=1e-6, threads=0):
     lib().mot_oracle_fused_add_rmsnorm(_p(x), _p(rr), _p(wu), _p(wg), _p(m), float(eps), T, H,
                                        _p(h), _p(rstd), _p(ref), _p(out), threads)
     return {"h": h, "rstd": rstd, "ref": ref, "out": out}
+
+
+def rmsnorm_apply(h, rstd, w_und, w_gen, modality, threads=0):
+    """The routed RMSNorm's output for a given per-row rstd (fp32 values):
+    h [T,H] uint16, rstd [T] -> (ref f64 [T,H] = h*rstd*w_m exactly, out u16
+    [T,H] = its bf16 rounding).  This is the A operand of the GEMM's
+    routed-RMSNorm prologue."""
+    h = _u16(h)
+    T, H = h.shape
+    rs = np.ascontiguousarray(np.asarray(rstd, np.float32).astype(np.float64))
+    assert rs.shape == (T,)
+    wu, wg = _u16(w_und, (H,)), _u16(w_gen, (H,))
+    m = np.ascontiguousarray(modality, dtype=np.uint8)
+    assert m.shape == (T,)
+    ref = np.empty((T, H), np.float64)
+    out = np.empty((T, H), np.uint16)
+    lib().mot_oracle_rmsnorm_apply(_p(h), _p(rs), _p(wu), _p(wg), _p(m), T, H, _p(ref), _p(out), threads)
+    return ref, out
 
 
 def qk_norm_rope(qkv, n_q_heads, n_k_heads, modality, q_norm, k_norm, positions, cos_t, sin_t,

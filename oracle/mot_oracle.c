@@ -298,6 +298,33 @@ void mot_oracle_fused_add_rmsnorm(const uint16_t *x, const uint16_t *r,
     }
 }
 
+/* The second half of the routed RMSNorm for a given rstd: the A operand of
+ * the GEMM's routed-RMSNorm prologue ("fused routed RMSNorm-prologue" of
+ * the routed projection; the convention of the MoE PR page's RMSNorm
+ * commits: the weight multiply in full precision, one trailing cast).
+ * h: [T, H] bf16; rstd: [T] (an fp32 value, passed as a double);
+ * ref (may be NULL): [T, H] fp64 h * rstd * w_{m(t)}; out (may be NULL):
+ * [T, H] bf16 = bf16_round(ref).  (The product of a bf16, an fp32 and a bf16
+ * value has at most 40 significant bits, so ref is exact.) */
+void mot_oracle_rmsnorm_apply(const uint16_t *h, const double *rstd,
+                              const uint16_t *w_und, const uint16_t *w_gen,
+                              const uint8_t *modality, int64_t T, int64_t H,
+                              double *ref, uint16_t *out, int nthreads)
+{
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *w = modality[t] ? w_gen : w_und;
+        for (int64_t k = 0; k < H; ++k) {
+            double y = bf16_value(h[t * H + k]) * rstd[t] * bf16_value(w[k]);
+            if (ref)
+                ref[t * H + k] = y;
+            if (out)
+                out[t * H + k] = bf16_round(y);
+        }
+    }
+}
+
 /* ---- routed per-head QK RMSNorm, then rotary position embedding -------------- */
 
 /* The "mot_qk_norm_rope" work item of the RFC page (section 5), with the

@@ -200,3 +200,59 @@ def test_plan_ready_small_and_mid_packs(T):
     ws = mot.routing_plan(md)
     ready = mot.routed_gemm(x, wu, wg, md, workspace=ws, plan_ready=True)
     assert raw_equal(ready, inline)
+
+
+# ---- the same sweep on the MLP's routed GEMMs --------------------------------
+
+@pytest.fixture(scope="module")
+def mlp_setup():
+    """BAGEL MLP weights at full size: gate/up K=3584 -> 2 x 18944 (SwiGLU)
+    and down K=18944 -> 3584; probe and filler rows for both."""
+    gu_u, gu_g, dn_u, dn_g = (dev(t) for t in W.mlp_weights(base=7))
+    probe_m = W.pattern(1024)
+    xg_probe = W.normal_bf16((1024, K), W.seed_of(7, 20))
+    xg_fill = W.normal_bf16((3072, K), W.seed_of(7, 21))
+    xd_probe = W.normal_bf16((1024, W.FFN), W.seed_of(7, 22))
+    xd_fill = W.normal_bf16((3072, W.FFN), W.seed_of(7, 23))
+    md = dev(torch.from_numpy(probe_m))
+    ref_g = mot.routed_gemm_swiglu(dev(xg_probe), gu_u, gu_g, md)
+    ref_d = mot.routed_gemm(dev(xd_probe), dn_u, dn_g, md)
+    torch.cuda.synchronize()
+    return dict(probe_m=probe_m, swiglu=(xg_probe, xg_fill, lambda x, m: mot.routed_gemm_swiglu(x, gu_u, gu_g, m),
+                                         ref_g),
+                down=(xd_probe, xd_fill, lambda x, m: mot.routed_gemm(x, dn_u, dn_g, m), ref_d))
+
+
+# a subset of the QKV sweep's packs: the probe alone, one extra row of each
+# set, and 512 / 3072 extra rows at 0%, 50% and 100% gen, permuted
+MLP_PACKS = [(0, "0%"), (1, "0%"), (1, "1 token"), (512, "50%"), (3072, "0%"), (3072, "50%"), (3072, "100%")]
+
+
+@pytest.mark.parametrize("op", ["swiglu", "down"])
+@pytest.mark.parametrize("n,frac", MLP_PACKS)
+def test_mlp_probe_rows_bitwise_invariant(mlp_setup, op, n, frac):
+    s = mlp_setup
+    x_probe, x_fill, run, ref = s[op]
+    fm = _fill_modality(n, frac)
+    x = torch.cat([x_probe, x_fill[:n]])
+    m = np.concatenate([s["probe_m"], fm])
+    T = x.shape[0]
+    perm = W.permutation(T, 300 + n).numpy()
+    y = run(dev(x[perm]), dev(torch.from_numpy(m[perm])))
+    pos = np.empty(T, np.int64)
+    pos[perm] = np.arange(T)
+    got = y[torch.from_numpy(pos[:1024]).cuda()]
+    torch.cuda.synchronize()
+    assert raw_equal(got, ref), f"{op}: probe rows changed in pack n={n} frac={frac}"
+
+
+@pytest.mark.parametrize("op", ["swiglu", "down"])
+def test_mlp_small_packs_match_large_pack_bytes(mlp_setup, op):
+    """Packs of 1, 33 and 64 rows (the small-pack kernel) give each row the
+    bytes it has in the 1024-row pack, for the MLP shapes too."""
+    s = mlp_setup
+    x_probe, _, run, ref = s[op]
+    for T in (1, 33, 64):
+        rows = np.random.default_rng(50 + T).permutation(1024)[:T]
+        y = run(dev(x_probe[rows]), dev(torch.from_numpy(s["probe_m"][rows].copy())))
+        assert raw_equal(y, ref[torch.from_numpy(rows).cuda()]), (op, T)

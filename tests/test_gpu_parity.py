@@ -485,3 +485,75 @@ def test_bad_modality_sets_error_and_writes_nothing():
     mot.routed_gemm(dev(x2), dev(wu2), dev(wg2), dev(torch.from_numpy(m2)), out=y2, workspace=ws2)
     assert mot.read_device_error(ws2) == 6
     assert torch.all(y2 == 5.0)
+
+
+# ---- routed-RMSNorm prologue -------------------------------------------------
+
+def _prologue_case(T, K, base, exact_rstd=True):
+    """h (the residual stream), the routed norm weights and a per-row rstd.
+    With exact_rstd the rstd of each row (the oracle's) is rounded to 8
+    significant bits: then (h * rstd) * w is exact in fp32 and both sides
+    round the same exact value once, so the prologue's A operand equals the
+    oracle's bit for bit and the GEMM can be held to the single-op bar."""
+    m = W.pattern(T)
+    m[::7] = 1 - m[::7]
+    h, _ = W.residual_inputs(T, K, base=base)
+    nwu, nwg = W.norm_weights(K, base=base)
+    rstd = oracle.fused_add_rmsnorm(W.bits(h), None, W.bits(nwu), W.bits(nwg), m)["rstd"]
+    if exact_rstd:
+        rstd = np.array([oracle.bf16_value(oracle.bf16_round(v)) for v in rstd])
+    return m, h, nwu, nwg, rstd.astype(np.float32)
+
+
+@pytest.mark.parametrize("T,K,N,rows", [(4096, W.HIDDEN, W.QKV_DIM, 40), (1, 3584, 4608, None),
+                                        (17, 3584, 4608, None), (64, 512, 384, None), (300, 256, 320, None)])
+def test_prologue_against_oracle(T, K, N, rows):
+    """The GEMM's routed-RMSNorm prologue, A = bf16((h * rstd) * w_set),
+    against the oracle's norm application followed by its GEMM: the full QKV
+    shape on sampled rows, and packs of at most 64 rows (which take the tiled
+    kernel when the prologue is on)."""
+    m, h, nwu, nwg, rstd = _prologue_case(T, K, base=1700 + T)
+    wu = W.normal_bf16((N, K), 1701, 0.02)
+    wg = W.normal_bf16((N, K), 1702, 0.02)
+    y = mot.routed_gemm(dev(h), dev(wu), dev(wg), dev(torch.from_numpy(m)),
+                        norm=(dev(torch.from_numpy(rstd)), dev(nwu), dev(nwg)))
+    torch.cuda.synchronize()
+    sel = np.arange(T) if rows is None else W.sample_rows(m, rows, seed=13)
+    _, a = oracle.rmsnorm_apply(W.bits(h)[sel], rstd[sel], W.bits(nwu), W.bits(nwg), m[sel])
+    args = (a, W.bits(wu), W.bits(wg), m[sel])
+    ref, rne = oracle.routed_gemm(*args)
+    check_parity(bits(y)[sel], ref, rne, f"prologue T={T} K={K} N={N}", bound=gemm_bound(*args))
+
+
+@pytest.mark.parametrize("T", [1, 40, 600])
+def test_prologue_swiglu_against_oracle(T):
+    K, F = 512, 192
+    m, h, nwu, nwg, rstd = _prologue_case(T, K, base=1750 + T)
+    wu = W.normal_bf16((2 * F, K), 1751, 0.05)
+    wg = W.normal_bf16((2 * F, K), 1752, 0.05)
+    act = mot.routed_gemm_swiglu(dev(h), dev(wu), dev(wg), dev(torch.from_numpy(m)),
+                                 norm=(dev(torch.from_numpy(rstd)), dev(nwu), dev(nwg)))
+    torch.cuda.synchronize()
+    _, a = oracle.rmsnorm_apply(W.bits(h), rstd, W.bits(nwu), W.bits(nwg), m)
+    args = (a, W.bits(wu), W.bits(wg), m)
+    ref, rne = oracle.routed_gemm_swiglu(*args)
+    check_parity(bits(act), ref, rne, f"prologue swiglu T={T}", bound=swiglu_bound(*args))
+
+
+def test_prologue_with_the_norms_own_rstd():
+    """The prologue fed the norm kernel's fp32 rstd (any fp32 value): the
+    product (h * rstd) rounds in fp32 before the weight multiply, so the
+    A operand can sit one bf16 step from the oracle's exact rounding in a
+    few elements; the output is held to the gate (max-abs, relative
+    Frobenius), as a two-step chain."""
+    T, K, N = 4096, W.HIDDEN, W.QKV_DIM
+    m, h, nwu, nwg, rstd = _prologue_case(T, K, base=1760, exact_rstd=False)
+    wu = W.normal_bf16((N, K), 1761, 0.02)
+    wg = W.normal_bf16((N, K), 1762, 0.02)
+    y = mot.routed_gemm(dev(h), dev(wu), dev(wg), dev(torch.from_numpy(m)),
+                        norm=(dev(torch.from_numpy(rstd)), dev(nwu), dev(nwg)))
+    torch.cuda.synchronize()
+    sel = W.sample_rows(m, 24, seed=14)
+    _, a = oracle.rmsnorm_apply(W.bits(h)[sel], rstd[sel], W.bits(nwu), W.bits(nwg), m[sel])
+    ref, rne = oracle.routed_gemm(a, W.bits(wu), W.bits(wg), m[sel])
+    check_parity(bits(y)[sel], ref, rne, "prologue with fp32 rstd", one_step=False)

@@ -871,3 +871,27 @@ def test_index_sets_round_trip_to_the_segment_list():
     assert err == 0 and np.array_equal(m, m0)
     perm, nu, ng = oracle.routing_plan(m)
     assert np.array_equal(perm, np.concatenate([np.sort(und), np.sort(gen)])) and (nu, ng) == (und.size, gen.size)
+
+
+def test_rmsnorm_apply_exact_by_rationals():
+    """The norm application for a given fp32 rstd, element by element
+    against exact rational arithmetic: ref == h * rstd * w_{m(t)} exactly, and
+    out is its correct bf16 rounding; rows pick their own set's weights."""
+    T, H = 6, 64
+    m = np.array([0, 1, 1, 0, 1, 0], np.uint8)
+    h = W.bits(W.normal_bf16((T, H), 960))
+    wu, wg = (W.bits(t) for t in W.norm_weights(H, base=96))
+    rstd = np.float32(np.random.default_rng(9).uniform(0.5, 2.0, T))
+    ref, out = oracle.rmsnorm_apply(h, rstd, wu, wg, m)
+    hv, wuv, wgv = oracle.bf16_to_f64(h), oracle.bf16_to_f64(wu), oracle.bf16_to_f64(wg)
+    for t in range(T):
+        w = wgv if m[t] else wuv
+        for k in range(H):
+            q = Fraction(float(hv[t, k])) * Fraction(float(rstd[t])) * Fraction(float(w[k]))
+            assert Fraction(float(ref[t, k])) == q
+            assert out[t, k] == rne_bf16_exact(q)
+    # with rstd from the norm itself (rounded to fp32) it reproduces the
+    # norm's outputs but for the few elements the fp32 rounding of rstd moves
+    full = oracle.fused_add_rmsnorm(h, None, wu, wg, m)
+    _, out2 = oracle.rmsnorm_apply(h, np.float32(full["rstd"]), wu, wg, m)
+    assert (out2 == full["out"]).mean() >= 0.99
