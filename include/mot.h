@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 8
+#define MOT_ABI_VERSION 9
 
 typedef enum mot_status {
     MOT_OK = 0,
@@ -170,6 +170,33 @@ int mot_routed_gemm(const uint16_t *x, int64_t ldx,
                     const float *rstd, const uint16_t *nw_und, const uint16_t *nw_gen,
                     void *workspace, size_t workspace_bytes,
                     unsigned flags, void *stream);
+
+/* Largest pack of mot_routed_gemm_noalloc. */
+#define MOT_NOALLOC_MAX_T 65536
+
+/* mot_routed_gemm without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The call's workspace (the
+ * routing header and segment list, MOT_WS_HEADER_BYTES + 4 * T bytes) lives
+ * in a static device array of the library, sized for MOT_NOALLOC_MAX_T rows
+ * (256 KiB + 256 bytes), one copy per GPU, held until the process ends.  The
+ * call allocates nothing.  Every call on one GPU shares that GPU's array and
+ * leaves its contents there: calls that overlap on one GPU (other streams,
+ * other threads) race and must be ordered by the caller.
+ *   error_out: NULL, or a device int32 that receives the call's device error
+ *        word in stream order (MOT_OK, or MOT_ERR_MODALITY if a modality byte
+ *        was invalid, in which case nothing was written to y).
+ *   flags: tile-shape flags only; MOT_FLAG_PLAN_READY is MOT_ERR_INVALID_ARG.
+ * Other arguments, the result bytes (identical to mot_routed_gemm's) and the
+ * errors as mot_routed_gemm, plus MOT_ERR_UNSUPPORTED_SHAPE for
+ * T > MOT_NOALLOC_MAX_T.  Since ABI 9. */
+int mot_routed_gemm_noalloc(const uint16_t *x, int64_t ldx,
+                            const uint16_t *w_und, const uint16_t *w_gen,
+                            const uint8_t *modality,
+                            uint16_t *y, int64_t ldy,
+                            int64_t T, int64_t K, int64_t N,
+                            const float *rstd, const uint16_t *nw_und, const uint16_t *nw_gen,
+                            int32_t *error_out, unsigned flags, void *stream);
 
 /* Routed GEMM with fp32 output: the fp32 sums of mot_routed_gemm, before
  * their bf16 cast (the bf16 output of mot_routed_gemm is bf16_rne of this

@@ -20,13 +20,13 @@ import torch
 
 __all__ = [
     "MotError", "ABI_VERSION", "lib", "abi_version", "workspace_bytes", "new_workspace",
-    "routing_plan", "modality_from_index_sets", "plan_view", "routed_gemm", "routed_gemm_f32", "routed_gemm_swiglu", "fused_add_rmsnorm",
+    "routing_plan", "modality_from_index_sets", "routed_gemm_noalloc", "NOALLOC_MAX_T", "plan_view", "routed_gemm", "routed_gemm_f32", "routed_gemm_swiglu", "fused_add_rmsnorm",
     "transpose", "routed_gemm_dx", "grad_w", "qk_norm_rope", "joint_attention",
     "attention_workspace_bytes", "joint_attention_varlen", "attention_varlen_workspace_bytes",
     "read_device_error", "status_string", "LIB_PATH",
 ]
 
-ABI_VERSION = 8
+ABI_VERSION = 9
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
 WS_HEADER_BYTES = 256
 FLAG_PLAN_READY = 1
@@ -40,7 +40,7 @@ EXPORTS = (
     "mot_routed_gemm", "mot_routed_gemm_swiglu", "mot_fused_add_rmsnorm", "mot_read_device_error",
     "mot_transpose_bf16", "mot_qk_norm_rope", "mot_routed_gemm_f32", "mot_attention_workspace_bytes",
     "mot_joint_attention", "mot_attention_varlen_workspace_bytes", "mot_joint_attention_varlen",
-    "mot_modality_from_index_sets",
+    "mot_modality_from_index_sets", "mot_routed_gemm_noalloc",
 )
 
 STATUS = {
@@ -101,6 +101,8 @@ def lib():
     L.mot_joint_attention_varlen.restype = ctypes.c_int
     L.mot_joint_attention_varlen.argtypes = [P, I64, P, I64, P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I64, I64,
                                              ctypes.c_int, P, SZ, P]
+    L.mot_routed_gemm_noalloc.restype = ctypes.c_int
+    L.mot_routed_gemm_noalloc.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64, P, P, P, P, U, P]
     L.mot_modality_from_index_sets.restype = ctypes.c_int
     L.mot_modality_from_index_sets.argtypes = [P, I64, P, I64, P, I64, P, SZ, P]
     v = L.mot_abi_version()
@@ -262,6 +264,42 @@ def routed_gemm(x, w_und, w_gen, modality, out=None, norm=None, workspace=None, 
     tile: None (library's choice) or "256x256" / "128x128" (force one tile shape)."""
     return _routed(lib().mot_routed_gemm, "mot_routed_gemm", x, w_und, w_gen, modality, out, norm,
                    workspace, plan_ready, swiglu=False, tile=tile)
+
+
+NOALLOC_MAX_T = 65536
+
+
+def routed_gemm_noalloc(x, w_und, w_gen, modality, out, norm=None, error_out=None, tile=None):
+    """routed_gemm without a workspace: the library's own per-GPU scratch
+    holds the segment list (packs of up to NOALLOC_MAX_T rows), so the call
+    allocates nothing; `out` must be given.  error_out: None or an int32 GPU
+    tensor of one element that receives the device error word.  Calls that
+    overlap on one GPU share the scratch and must be ordered."""
+    _req(x, "x", torch.bfloat16, 2)
+    _req(w_und, "w_und", torch.bfloat16, 2)
+    _req(w_gen, "w_gen", torch.bfloat16, 2)
+    _req(modality, "modality", torch.uint8, 1)
+    _req(out, "out", torch.bfloat16, 2)
+    if w_und.shape != w_gen.shape or not (w_und.is_contiguous() and w_gen.is_contiguous()):
+        raise ValueError("w_und and w_gen must be contiguous and of the same shape")
+    T, K = x.shape
+    N = w_und.shape[0]
+    if w_und.shape[1] != K or modality.shape[0] != T or tuple(out.shape) != (T, N):
+        raise ValueError("shapes: x [T, K], weights [N, K], modality [T], out [T, N]")
+    if not modality.is_contiguous():
+        raise ValueError("modality must be contiguous (no copy is made)")
+    rstd = nw_u = nw_g = None
+    if norm is not None:
+        rstd, nw_u, nw_g = norm
+    if error_out is not None:
+        _req(error_out, "error_out", torch.int32, 1)
+    if tile not in TILE_FLAGS:
+        raise ValueError(f"tile must be one of {sorted(k for k in TILE_FLAGS if k)}")
+    st = lib().mot_routed_gemm_noalloc(_ptr(x), _rows(x, "x"), _ptr(w_und), _ptr(w_gen), _ptr(modality),
+                                       _ptr(out), _rows(out, "out"), T, K, N, _ptr(rstd), _ptr(nw_u), _ptr(nw_g),
+                                       _ptr(error_out), TILE_FLAGS[tile], _stream(x.device))
+    _check(st, "mot_routed_gemm_noalloc")
+    return out
 
 
 def routed_gemm_f32(x, w_und, w_gen, modality, out=None, workspace=None, plan_ready=False):

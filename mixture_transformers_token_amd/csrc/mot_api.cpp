@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/mot.h"
 #include "mot_internal.h"
 
@@ -175,9 +177,60 @@ int run_routed(const RoutedCall &c, bool swiglu, void *stream) {
     return MOT_OK;
 }
 
+// ---- allocation-free routed GEMM --------------------------------------------
+//
+// The scratch of mot_routed_gemm_noalloc: one routed workspace (header and
+// segment list) for packs of up to MOT_NOALLOC_MAX_T rows, in device memory
+// that the library holds from load to process end, one copy per GPU.  In host
+// code `scratch` names a host-side stand-in, not the device address: the
+// address is taken once per device with hipGetSymbolAddress (that device
+// current) and only that pointer is ever passed to kernels.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[MOT_WS_HEADER_BYTES + 4 * (size_t)MOT_NOALLOC_MAX_T];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (nullptr on failure).
+void *device_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
+
+int mot_routed_gemm_noalloc(const uint16_t *x, int64_t ldx, const uint16_t *w_und, const uint16_t *w_gen,
+                            const uint8_t *modality, uint16_t *y, int64_t ldy, int64_t T, int64_t K, int64_t N,
+                            const float *rstd, const uint16_t *nw_und, const uint16_t *nw_gen,
+                            int32_t *error_out, unsigned flags, void *stream) {
+    if (T < 0) return MOT_ERR_INVALID_ARG;
+    if (T > MOT_NOALLOC_MAX_T) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (flags & MOT_FLAG_PLAN_READY) return MOT_ERR_INVALID_ARG;  // the scratch holds no caller's plan
+    if (reinterpret_cast<uintptr_t>(error_out) & 3u) return MOT_ERR_MISALIGNED;
+    if (error_out && y && T > 0 && overlaps(error_out, 4, y, ((T - 1) * ldy + N) * 2)) return MOT_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(s);
+    if (!guard.ok()) return MOT_ERR_DEVICE;
+    void *ws = device_scratch();
+    if (ws == nullptr) return MOT_ERR_DEVICE;
+    RoutedCall c{x, ldx, w_und, w_gen, modality, y, ldy, T, K, N, N,
+                 rstd, nw_und, nw_gen, ws, sizeof(scratch), flags};
+    const int v = validate_routed(c);
+    if (v != MOT_OK || T == 0) return v;
+    const int st = run_routed(c, false, stream);
+    if (st != MOT_OK || error_out == nullptr) return st;
+    return mot::launch_copy_word(static_cast<const int32_t *>(ws), error_out, s) == hipSuccess ? MOT_OK
+                                                                                              : MOT_ERR_DEVICE;
+}
 
 int mot_abi_version(void) { return MOT_ABI_VERSION; }
 

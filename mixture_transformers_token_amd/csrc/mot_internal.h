@@ -99,6 +99,8 @@ hipError_t launch_index_sets(const int32_t *und_idx, int64_t n_und, const int32_
 // inline_route the kernel builds (and publishes) the segment list itself.
 hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStream_t stream);
 hipError_t launch_qk_norm_rope(const QkArgs &a, hipStream_t stream);
+// *dst = *src on the device (one thread), in stream order.
+hipError_t launch_copy_word(const int32_t *src, int32_t *dst, hipStream_t stream);
 hipError_t launch_transpose(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t cols,
                             const uint8_t *modality, int keep, uint16_t *out, int64_t ld_out,
                             int64_t rows_pad, hipStream_t stream);

@@ -1639,6 +1639,10 @@ __global__ void set_word_kernel(int32_t *p, int32_t v) {
     if (threadIdx.x == 0) *p = v;
 }
 
+__global__ void copy_word_kernel(const int32_t *src, int32_t *dst) {
+    if (threadIdx.x == 0) *dst = *src;
+}
+
 __global__ void __launch_bounds__(256) qk_norm_rope_kernel(QkArgs a) {
     const int lane = threadIdx.x & 63;
     const int gi = lane & 15, grp = lane >> 4;  // lane in its 16-lane group, group = head within a chunk
@@ -1888,6 +1892,11 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
                    : launch_gemm_t<true, false>(a, inline_route, grid, stream);
     return pro ? launch_gemm_t<false, true>(a, inline_route, grid, stream)
                : launch_gemm_t<false, false>(a, inline_route, grid, stream);
+}
+
+hipError_t launch_copy_word(const int32_t *src, int32_t *dst, hipStream_t stream) {
+    hipLaunchKernelGGL(copy_word_kernel, dim3(1), dim3(64), 0, stream, src, dst);
+    return hipGetLastError();
 }
 
 hipError_t launch_qk_norm_rope(const QkArgs &a, hipStream_t stream) {
