@@ -11,6 +11,7 @@ tests/test_oracle_pins.py.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -325,3 +326,105 @@ def attention_varlen(q, k, v, cu_q, cu_k, hq, hkv, causal, head_dim=128, threads
         r, o = attention(q[q0:q1], k[k0:k1], v[k0:k1], hq, hkv, causal, head_dim=head_dim, threads=threads)
         ref[q0:q1], out[q0:q1] = r, o
     return ref, out
+
+
+# ---- latent step: three-branch renormalised CFG, and the flow SDE step -------
+#
+# The RL-Kernel RFC page lists both as work items ("cfg_combine_renorm" and
+# "flow_sde_step_logp", section 5) and fixes their contract, not their
+# formulas: up to three branches, two scales, a timestep window and a
+# norm-ratio rescale with a minimum, renormalised per request (section 1,
+# item 3; section 3, "BAGEL-specific rules"); the SDE step and its log
+# probability in fp32 with sigma = t and dt = t_i - t_{i+1} > 0, the
+# log-probability summed over all latent elements of a request (section 3).
+# The formulas below are this project's readings of that contract; the SDE is
+# the Euler-Maruyama step of the rectified flow's reverse SDE published with
+# Flow-GRPO (arXiv 2505.05470, cited on the RFC page).  Plain fp64 per request.
+
+RENORM_NONE, RENORM_GLOBAL, RENORM_CHANNEL = 0, 1, 2
+
+
+def _f32(v):
+    return float(np.float32(v))
+
+
+def cfg_combine_renorm(v_cond, v_text_uncond, v_img_uncond, cu_rows, t, s_text, s_img, t_lo, t_hi,
+                       renorm_min, renorm_type):
+    """Guided velocity of each request b (rows [cu_rows[b], cu_rows[b+1])),
+    inputs fp32 [R, C] (v_img_uncond None: two branches):
+      inside the window t_lo < t[b] <= t_hi (fp32 comparisons):
+        g = v_tu + s_text (v_c - v_tu);  three branches: g = v_iu + s_img (g - v_iu)
+        global renorm: r = clamp(||v_c||_2 / ||g||_2, renorm_min, 1) over the
+          request's elements (r = 1 when ||g|| = 0); out = r g
+        channel renorm: the same ratio per row (over its C channels)
+        none: out = g
+      outside the window: out = v_c.
+    Returns the fp64 result [R, C]."""
+    vc = np.asarray(v_cond, np.float32).astype(np.float64)
+    vt = np.asarray(v_text_uncond, np.float32).astype(np.float64)
+    vi = None if v_img_uncond is None else np.asarray(v_img_uncond, np.float32).astype(np.float64)
+    s1, s2, lo, hi, rmin = (_f32(a) for a in (s_text, s_img, t_lo, t_hi, renorm_min))
+    out = np.zeros_like(vc)
+    for b in range(len(cu_rows) - 1):
+        r0, r1 = int(cu_rows[b]), int(cu_rows[b + 1])
+        tb = _f32(t[b])
+        if not (lo < tb <= hi):
+            out[r0:r1] = vc[r0:r1]
+            continue
+        g = vt[r0:r1] + s1 * (vc[r0:r1] - vt[r0:r1])
+        if vi is not None:
+            g = vi[r0:r1] + s2 * (g - vi[r0:r1])
+        if renorm_type == RENORM_GLOBAL:
+            ng = math.sqrt(math.fsum((g * g).ravel().tolist()))
+            nc = math.sqrt(math.fsum((vc[r0:r1] ** 2).ravel().tolist()))
+            r = 1.0 if ng == 0.0 else min(1.0, max(rmin, nc / ng))
+            out[r0:r1] = g * r
+        elif renorm_type == RENORM_CHANNEL:
+            for i in range(r1 - r0):
+                ng = math.sqrt(math.fsum((g[i] * g[i]).tolist()))
+                nc = math.sqrt(math.fsum((vc[r0 + i] ** 2).tolist()))
+                r = 1.0 if ng == 0.0 else min(1.0, max(rmin, nc / ng))
+                out[r0 + i] = g[i] * r
+        else:
+            out[r0:r1] = g
+    return out
+
+
+def sde_scale(t, t_next, eta):
+    """Diffusion scale of the step from t to t_next: s = eta sqrt(t / (1 - t)),
+    with 1 - t_next in the denominator at the first step t = 1."""
+    t, tn, e = _f32(t), _f32(t_next), _f32(eta)
+    den = 1.0 - (t if t < 1.0 else tn)
+    return e * math.sqrt(t / den)
+
+
+def flow_sde_step_logp(x, v, cu_rows, t_cur, t_next, eta, noise=None, x_next=None):
+    """One step of request b from t = t_cur[b] down to t_next[b]
+    (dt = t - t_next > 0), x_t = (1 - t) x_0 + t eps and v = dx/dt:
+      s  = sde_scale(t, t_next, eta)
+      mu = x - dt (v + s^2 / (2 t) (x + (1 - t) v))
+      x_next = mu + s sqrt(dt) noise              (when noise is given)
+      logp_b = sum over the request's elements of
+               -(x_next - mu)^2 / (2 s^2 dt) - log(s sqrt(dt)) - log(2 pi) / 2
+    x, v, noise, x_next: fp32 [R, C].  Returns (mu, x_next, logp) in fp64."""
+    xx = np.asarray(x, np.float32).astype(np.float64)
+    vv = np.asarray(v, np.float32).astype(np.float64)
+    mu = np.zeros_like(xx)
+    xn = np.zeros_like(xx)
+    logp = np.zeros(len(cu_rows) - 1)
+    for b in range(len(cu_rows) - 1):
+        r0, r1 = int(cu_rows[b]), int(cu_rows[b + 1])
+        t, tn = _f32(t_cur[b]), _f32(t_next[b])
+        dt = t - tn
+        s = sde_scale(t, tn, eta)
+        m = xx[r0:r1] - dt * (vv[r0:r1] + (s * s / (2.0 * t)) * (xx[r0:r1] + (1.0 - t) * vv[r0:r1]))
+        std = s * math.sqrt(dt)
+        if noise is not None:
+            xb = m + std * np.asarray(noise, np.float32)[r0:r1].astype(np.float64)
+        else:
+            xb = np.asarray(x_next, np.float32)[r0:r1].astype(np.float64)
+        d = (xb - m).ravel().tolist()
+        n = len(d)
+        logp[b] = -math.fsum(di * di for di in d) / (2.0 * std * std) - n * (math.log(std) + 0.5 * math.log(2 * math.pi))
+        mu[r0:r1], xn[r0:r1] = m, xb
+    return mu, xn, logp
