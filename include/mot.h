@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 9
+#define MOT_ABI_VERSION 10
 
 typedef enum mot_status {
     MOT_OK = 0,
@@ -63,8 +63,10 @@ typedef enum mot_status {
     MOT_ERR_SEQLENS = 8,           /* packed sequence lengths invalid (reported by mot_read_device_error) */
     MOT_ERR_PLAN = 9,              /* a plan passed with MOT_FLAG_PLAN_READY does not describe the call's
                                       T rows (reported by mot_read_device_error; since ABI 8) */
-    MOT_ERR_INDEX_SET = 10         /* a row in neither index set, in both, or twice in one; or an index
+    MOT_ERR_INDEX_SET = 10,        /* a row in neither index set, in both, or twice in one; or an index
                                       outside [0, T) (reported by mot_read_device_error; since ABI 8) */
+    MOT_ERR_SCHEDULE = 11          /* a latent step's timesteps break 0 <= t_next < t <= 1, or a CFG t is
+                                      not finite (reported by mot_read_device_error; since ABI 10) */
 } mot_status;
 
 /* Limits checked on the host. */
@@ -312,7 +314,7 @@ int mot_qk_norm_rope(uint16_t *qkv, int64_t ld, int64_t T, int64_t n_q_heads, in
 
 /* Synchronises `stream` and returns the workspace's device error word:
  * MOT_OK, MOT_ERR_MODALITY, MOT_ERR_POSITION, MOT_ERR_SEQLENS, MOT_ERR_PLAN,
- * MOT_ERR_INDEX_SET, or MOT_ERR_DEVICE if the copy fails. */
+ * MOT_ERR_INDEX_SET, MOT_ERR_SCHEDULE, or MOT_ERR_DEVICE if the copy fails. */
 int mot_read_device_error(const void *workspace, void *stream);
 
 /* Workspace bytes of mot_joint_attention: the transposed V of the kv heads,
@@ -387,6 +389,75 @@ int mot_joint_attention_varlen(const uint16_t *q, int64_t ldq, const uint16_t *k
                                int64_t Tq, int64_t Tk, int64_t max_q,
                                int64_t n_q_heads, int64_t n_kv_heads, int64_t head_dim, int causal,
                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- latent step: renormalised CFG and the flow SDE step (since ABI 10) ----
+ *
+ * The "cfg_combine_renorm" and "flow_sde_step_logp" work items of the RFC
+ * page (section 5).  The page fixes their contract, not their formulas (its
+ * section 1, item 3, and section 3, "BAGEL-specific rules"): up to three CFG
+ * branches, two scales, a timestep window compared on fp32 t, a norm-ratio
+ * rescale with a minimum, renormalised per request (never over the packed
+ * batch); the SDE step and its log-probability in fp32, with sigma = t
+ * (x_t = (1 - t) x_0 + t noise) and dt = t_i - t_{i+1} > 0, the
+ * log-probability summed over the request's latent elements in a fixed
+ * order.  The formulas below are this library's readings of that contract.
+ *
+ * Layout: fp32 [rows][C] arrays, C % 4 == 0, C <= 4096, packed by request:
+ * request b owns rows [cu_rows[b], cu_rows[b+1]) (cu_rows: int32 device
+ * array of n_req + 1 entries, 0 = cu[0] <= ... <= cu[n_req] = rows, no
+ * request longer than max_rows; checked on the device, and a violation
+ * writes nothing and raises MOT_ERR_SEQLENS).  Work goes in chunks of 64 rows
+ * of one request; request-wide sums add the chunks' fp32 sums in ascending
+ * order, so a request's results do not depend on the other requests of the
+ * pack.  workspace: >= mot_latent_workspace_bytes(n_req, max_rows) bytes,
+ * 256-byte aligned; its error word is set by every call. */
+size_t mot_latent_workspace_bytes(int64_t n_req, int64_t max_rows);
+
+#define MOT_RENORM_NONE 0
+#define MOT_RENORM_GLOBAL 1   /* one ratio per request, over all its elements */
+#define MOT_RENORM_CHANNEL 2  /* one ratio per latent row, over its C channels */
+
+/* Guided velocity of each request b, in fp32:
+ *   inside the window t_lo < t[b] <= t_hi:
+ *     g = v_tu + s_text (v_c - v_tu);  three branches: g = v_iu + s_img (g - v_iu)
+ *     r = min(1, max(renorm_min, ||v_c|| / ||g||)) over the request (GLOBAL)
+ *         or over each row (CHANNEL), r = 1 when ||g|| = 0; r = 1 (NONE)
+ *     out = r g
+ *   outside the window: out = v_c.
+ *   v_cond, v_text_uncond: [rows][C] fp32; v_img_uncond: [rows][C] or NULL
+ *   (two branches); out [rows][C], overlapping no input; t [n_req] fp32
+ *   device array (finite, else MOT_ERR_SCHEDULE and nothing written);
+ *   scales and window finite, 0 <= renorm_min <= 1.
+ * Errors: MOT_ERR_INVALID_ARG, MOT_ERR_UNSUPPORTED_SHAPE, MOT_ERR_MISALIGNED
+ * (16-byte aligned arrays, 4-byte aligned cu_rows and t), MOT_ERR_WORKSPACE,
+ * MOT_ERR_DEVICE.  n_req == 0 with rows == 0 is a no-op. */
+int mot_cfg_combine_renorm(const float *v_cond, const float *v_text_uncond, const float *v_img_uncond, float *out,
+                           const int32_t *cu_rows, int64_t n_req, int64_t rows, int64_t C, int64_t max_rows,
+                           const float *t, float s_text, float s_img, float t_lo, float t_hi, float renorm_min,
+                           int renorm_type, void *workspace, size_t workspace_bytes, void *stream);
+
+/* One SDE step of each request b from t = t_cur[b] down to t_next[b], in
+ * fp32 (the Euler-Maruyama step of rectified flow's reverse SDE published
+ * with Flow-GRPO; v is the model's velocity dx/dt):
+ *   dt = t - t_next > 0,  s = eta sqrt(t / (1 - t)) (1 - t_next in the
+ *   denominator at the first step t = 1),  k = s^2 / (2 t)
+ *   mu = x - dt (v + k (x + (1 - t) v)),  sd = s sqrt(dt)
+ *   sampling (noise != NULL):  x_next_out = mu + sd noise
+ *   either mode, with x_next the sample or x_next_in:
+ *     logp[b] = -q / (2 sd^2) - n (log(sd) + log(2 pi) / 2),
+ *     q = sum over the request's n = rows_b * C elements of (x_next - mu)^2
+ *   (the same arithmetic in both modes, so evaluating a sample's x_next gives
+ *   the sampling call's logp bit for bit).
+ *   x, v, noise, x_next_in, x_next_out: [rows][C] fp32; exactly one mode:
+ *   noise and x_next_out non-NULL with x_next_in NULL, or x_next_in alone.
+ *   logp [n_req] fp32; t_cur, t_next [n_req] fp32 device arrays with
+ *   0 <= t_next < t_cur <= 1 (else MOT_ERR_SCHEDULE, nothing written);
+ *   eta > 0 and finite.  Outputs overlap no input.
+ * Errors as mot_cfg_combine_renorm. */
+int mot_flow_sde_step_logp(const float *x, const float *v, const float *noise, const float *x_next_in,
+                           float *x_next_out, float *logp, const int32_t *cu_rows, int64_t n_req, int64_t rows,
+                           int64_t C, int64_t max_rows, const float *t_cur, const float *t_next, float eta,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -23,10 +23,11 @@ __all__ = [
     "routing_plan", "modality_from_index_sets", "routed_gemm_noalloc", "NOALLOC_MAX_T", "plan_view", "routed_gemm", "routed_gemm_f32", "routed_gemm_swiglu", "fused_add_rmsnorm",
     "transpose", "routed_gemm_dx", "grad_w", "qk_norm_rope", "joint_attention",
     "attention_workspace_bytes", "joint_attention_varlen", "attention_varlen_workspace_bytes",
-    "read_device_error", "status_string", "LIB_PATH",
+    "read_device_error", "status_string", "LIB_PATH", "latent_workspace_bytes", "cfg_combine_renorm",
+    "flow_sde_step_logp", "RENORM",
 ]
 
-ABI_VERSION = 9
+ABI_VERSION = 10
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
 WS_HEADER_BYTES = 256
 FLAG_PLAN_READY = 1
@@ -40,13 +41,14 @@ EXPORTS = (
     "mot_routed_gemm", "mot_routed_gemm_swiglu", "mot_fused_add_rmsnorm", "mot_read_device_error",
     "mot_transpose_bf16", "mot_qk_norm_rope", "mot_routed_gemm_f32", "mot_attention_workspace_bytes",
     "mot_joint_attention", "mot_attention_varlen_workspace_bytes", "mot_joint_attention_varlen",
-    "mot_modality_from_index_sets", "mot_routed_gemm_noalloc",
+    "mot_modality_from_index_sets", "mot_routed_gemm_noalloc", "mot_latent_workspace_bytes",
+    "mot_cfg_combine_renorm", "mot_flow_sde_step_logp",
 )
 
 STATUS = {
     0: "MOT_OK", 1: "MOT_ERR_INVALID_ARG", 2: "MOT_ERR_UNSUPPORTED_SHAPE", 3: "MOT_ERR_MISALIGNED",
     4: "MOT_ERR_WORKSPACE", 5: "MOT_ERR_DEVICE", 6: "MOT_ERR_MODALITY", 7: "MOT_ERR_POSITION",
-    8: "MOT_ERR_SEQLENS", 9: "MOT_ERR_PLAN", 10: "MOT_ERR_INDEX_SET",
+    8: "MOT_ERR_SEQLENS", 9: "MOT_ERR_PLAN", 10: "MOT_ERR_INDEX_SET", 11: "MOT_ERR_SCHEDULE",
 }
 
 
@@ -101,6 +103,13 @@ def lib():
     L.mot_joint_attention_varlen.restype = ctypes.c_int
     L.mot_joint_attention_varlen.argtypes = [P, I64, P, I64, P, I64, P, I64, P, P, I64, I64, I64, I64, I64, I64, I64,
                                              ctypes.c_int, P, SZ, P]
+    F = ctypes.c_float
+    L.mot_latent_workspace_bytes.restype = SZ
+    L.mot_latent_workspace_bytes.argtypes = [I64, I64]
+    L.mot_cfg_combine_renorm.restype = ctypes.c_int
+    L.mot_cfg_combine_renorm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, F, F, F, F, F, ctypes.c_int, P, SZ, P]
+    L.mot_flow_sde_step_logp.restype = ctypes.c_int
+    L.mot_flow_sde_step_logp.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, P, P, F, P, SZ, P]
     L.mot_routed_gemm_noalloc.restype = ctypes.c_int
     L.mot_routed_gemm_noalloc.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64, P, P, P, P, U, P]
     L.mot_modality_from_index_sets.restype = ctypes.c_int
@@ -515,3 +524,82 @@ def joint_attention_varlen(q, k, v, cu_q, cu_k, max_q, n_q_heads, n_kv_heads, ca
                                           _ptr(workspace), workspace.numel(), _stream(q.device))
     _check(st, "mot_joint_attention_varlen")
     return out, workspace
+
+
+# ---- latent step: renormalised CFG combine, flow SDE step ---------------------
+
+RENORM = {"none": 0, "global": 1, "channel": 2}
+
+
+def latent_workspace_bytes(n_req: int, max_rows: int) -> int:
+    return int(lib().mot_latent_workspace_bytes(int(n_req), int(max_rows)))
+
+
+def _latent_common(arrs, cu_rows, name):
+    for a, nm in arrs:
+        if a is not None:
+            _req(a, nm, torch.float32, 2)
+            if not a.is_contiguous():
+                raise ValueError(f"{nm} must be contiguous [rows, C]")
+    _req(cu_rows, "cu_rows", torch.int32, 1)
+    if cu_rows.shape[0] < 1:
+        raise ValueError("cu_rows must hold n_req + 1 entries")
+    return cu_rows.contiguous()
+
+
+def cfg_combine_renorm(v_cond, v_text_uncond, v_img_uncond, cu_rows, max_rows, t, s_text, s_img, t_lo, t_hi,
+                       renorm_min=0.0, renorm="global", out=None, workspace=None):
+    """Guided velocity per request (rows [cu_rows[b], cu_rows[b+1]) of the
+    fp32 [rows, C] branches; v_img_uncond None for two branches), inside the
+    window t_lo < t[b] <= t_hi, with the norm-ratio rescale clamped to
+    [renorm_min, 1] per request ("global"), per row ("channel") or none.
+    t: fp32 [n_req] GPU tensor.  Returns (out, workspace)."""
+    cu = _latent_common(((v_cond, "v_cond"), (v_text_uncond, "v_text_uncond"), (v_img_uncond, "v_img_uncond")),
+                        cu_rows, "cfg")
+    rows, C = v_cond.shape
+    for a in (v_text_uncond, v_img_uncond):
+        if a is not None and a.shape != v_cond.shape:
+            raise ValueError("the branches must have the same shape")
+    _req(t, "t", torch.float32, 1)
+    n = cu.shape[0] - 1
+    if renorm not in RENORM:
+        raise ValueError(f"renorm must be one of {sorted(RENORM)}")
+    if out is None:
+        out = torch.empty_like(v_cond)
+    if workspace is None:
+        workspace = torch.empty(max(latent_workspace_bytes(n, max_rows), 256), dtype=torch.uint8,
+                                device=v_cond.device)
+    st = lib().mot_cfg_combine_renorm(_ptr(v_cond), _ptr(v_text_uncond), _ptr(v_img_uncond), _ptr(out), _ptr(cu), n,
+                                      rows, C, int(max_rows), _ptr(t.contiguous()), float(s_text), float(s_img),
+                                      float(t_lo), float(t_hi), float(renorm_min), RENORM[renorm], _ptr(workspace),
+                                      workspace.numel(), _stream(v_cond.device))
+    _check(st, "mot_cfg_combine_renorm")
+    return out, workspace
+
+
+def flow_sde_step_logp(x, v, cu_rows, max_rows, t_cur, t_next, eta, noise=None, x_next=None, out=None, logp=None,
+                       workspace=None):
+    """One flow SDE step per request from t_cur[b] to t_next[b] (fp32 [n_req]
+    GPU tensors): with noise, sample x_next (returned in `out`); with x_next,
+    evaluate it.  Either way returns (x_next or None, logp [n_req] fp32,
+    workspace)."""
+    cu = _latent_common(((x, "x"), (v, "v"), (noise, "noise"), (x_next, "x_next")), cu_rows, "sde")
+    rows, C = x.shape
+    _req(t_cur, "t_cur", torch.float32, 1)
+    _req(t_next, "t_next", torch.float32, 1)
+    n = cu.shape[0] - 1
+    if (noise is None) == (x_next is None):
+        raise ValueError("give exactly one of noise (sampling) and x_next (evaluation)")
+    if noise is not None and out is None:
+        out = torch.empty_like(x)
+    if logp is None:
+        logp = torch.empty(n, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(latent_workspace_bytes(n, max_rows), 256), dtype=torch.uint8, device=x.device)
+    st = lib().mot_flow_sde_step_logp(_ptr(x), _ptr(v), _ptr(noise), _ptr(x_next), _ptr(out if noise is not None
+                                                                                         else None),
+                                      _ptr(logp), _ptr(cu), n, rows, C, int(max_rows), _ptr(t_cur.contiguous()),
+                                      _ptr(t_next.contiguous()), float(eta), _ptr(workspace), workspace.numel(),
+                                      _stream(x.device))
+    _check(st, "mot_flow_sde_step_logp")
+    return (out if noise is not None else None), logp, workspace

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmot.so")
 SOURCES = [os.path.join(CSRC, "mot_kernels.hip"), os.path.join(CSRC, "mot_attention.hip"),
-           os.path.join(CSRC, "mot_api.cpp")]
+           os.path.join(CSRC, "mot_latent.hip"), os.path.join(CSRC, "mot_api.cpp")]
 HEADERS = [os.path.join(CSRC, "mot_internal.h"),
            os.path.join(os.path.dirname(HERE), "include", "mot.h")]
 

@@ -74,6 +74,27 @@ size_t attn_varlen_ws_bytes(int64_t Tk, int64_t n_seqs, int64_t hkv) {
     return (size_t)(MOT_WS_HEADER_BYTES + hkv * kAttnHeadDim * attn_varlen_ldvt(Tk, n_seqs) * 2);
 }
 
+constexpr int64_t kLatentMaxC = 4096;
+
+size_t latent_ws_bytes(int64_t n_req, int64_t max_rows) {
+    if (n_req <= 0 || max_rows <= 0 || n_req > MOT_MAX_T || max_rows > MOT_MAX_T) return 0;
+    return (size_t)(MOT_WS_HEADER_BYTES + n_req * (int64_t)mot::latent_chunks(max_rows) * 2 * 4);
+}
+
+// Checks shared by the latent-step calls; 0 if fine.
+int validate_latent(int64_t n_req, int64_t rows, int64_t C, int64_t max_rows, const int32_t *cu,
+                    void *workspace, size_t workspace_bytes) {
+    if (n_req < 0 || rows < 0 || C <= 0 || max_rows < 1) return MOT_ERR_INVALID_ARG;
+    if (C % 4 || C > kLatentMaxC || rows > MOT_MAX_T || n_req > MOT_MAX_T || max_rows > MOT_MAX_T)
+        return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (n_req * (int64_t)mot::latent_chunks(max_rows) >= (int64_t(1) << 31)) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (!cu) return MOT_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(cu) & 3u) return MOT_ERR_MISALIGNED;
+    if (!workspace || workspace_bytes < latent_ws_bytes(n_req, max_rows)) return MOT_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kWsAlign - 1)) != 0) return MOT_ERR_MISALIGNED;
+    return MOT_OK;
+}
+
 size_t ws_bytes(int64_t T) {
     return (size_t)(MOT_WS_HEADER_BYTES + round_up(4 * (T > 0 ? T : 0), kWsAlign));
 }
@@ -246,6 +267,7 @@ const char *mot_status_string(int status) {
     case MOT_ERR_POSITION: return "MOT_ERR_POSITION: position outside the rotary table";
     case MOT_ERR_SEQLENS: return "MOT_ERR_SEQLENS: packed sequence lengths invalid";
     case MOT_ERR_PLAN: return "MOT_ERR_PLAN: the ready plan does not describe this pack";
+    case MOT_ERR_SCHEDULE: return "MOT_ERR_SCHEDULE: a step's timesteps are outside 0 <= t_next < t <= 1 (or t not finite)";
     case MOT_ERR_INDEX_SET: return "MOT_ERR_INDEX_SET: a row is not in exactly one index set, or an index is out of range";
     default: return "unknown mot_status";
     }
@@ -558,6 +580,82 @@ int mot_qk_norm_rope(uint16_t *qkv, int64_t ld, int64_t T, int64_t n_q_heads, in
     a.eps = eps;
     a.err = static_cast<int32_t *>(workspace);
     return mot::launch_qk_norm_rope(a, s) == hipSuccess ? MOT_OK : MOT_ERR_DEVICE;
+}
+
+size_t mot_latent_workspace_bytes(int64_t n_req, int64_t max_rows) { return latent_ws_bytes(n_req, max_rows); }
+
+int mot_cfg_combine_renorm(const float *v_cond, const float *v_text_uncond, const float *v_img_uncond, float *out,
+                           const int32_t *cu_rows, int64_t n_req, int64_t rows, int64_t C, int64_t max_rows,
+                           const float *t, float s_text, float s_img, float t_lo, float t_hi, float renorm_min,
+                           int renorm_type, void *workspace, size_t workspace_bytes, void *stream) {
+    if (n_req == 0 && rows == 0 && C > 0) return MOT_OK;
+    const int v = validate_latent(n_req, rows, C, max_rows, cu_rows, workspace, workspace_bytes);
+    if (v != MOT_OK) return v;
+    if (n_req == 0) return MOT_ERR_INVALID_ARG;  // rows without requests
+    if (!v_cond || !v_text_uncond || !out || !t) return MOT_ERR_INVALID_ARG;
+    if (renorm_type < 0 || renorm_type > 2) return MOT_ERR_INVALID_ARG;
+    if (!isfinite(s_text) || !isfinite(s_img) || !isfinite(t_lo) || !isfinite(t_hi) ||
+        !(renorm_min >= 0.0f && renorm_min <= 1.0f))
+        return MOT_ERR_INVALID_ARG;
+    if (!aligned16(v_cond) || !aligned16(v_text_uncond) || (v_img_uncond && !aligned16(v_img_uncond)) ||
+        !aligned16(out) || (reinterpret_cast<uintptr_t>(t) & 3u))
+        return MOT_ERR_MISALIGNED;
+    const int64_t bytes = rows * C * 4;
+    const int64_t wsb = (int64_t)latent_ws_bytes(n_req, max_rows);
+    const void *ins[] = {v_cond, v_text_uncond, v_img_uncond, cu_rows, t, workspace};
+    const int64_t in_bytes[] = {bytes, bytes, bytes, 4 * (n_req + 1), 4 * n_req, wsb};
+    for (int i = 0; i < 6; ++i)
+        if (ins[i] && overlaps(out, bytes, ins[i], in_bytes[i])) return MOT_ERR_INVALID_ARG;
+    for (int i = 0; i < 5; ++i)
+        if (ins[i] && overlaps(workspace, wsb, ins[i], in_bytes[i])) return MOT_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(s);
+    if (!guard.ok()) return MOT_ERR_DEVICE;
+    int32_t *err = static_cast<int32_t *>(workspace);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(workspace) + MOT_WS_HEADER_BYTES);
+    return mot::launch_cfg_combine(v_cond, v_text_uncond, v_img_uncond, out, cu_rows, (int)n_req, rows, (int)C,
+                                   max_rows, t, s_text, s_img, t_lo, t_hi, renorm_min, renorm_type, err, part,
+                                   s) == hipSuccess
+               ? MOT_OK
+               : MOT_ERR_DEVICE;
+}
+
+int mot_flow_sde_step_logp(const float *x, const float *v, const float *noise, const float *x_next_in,
+                           float *x_next_out, float *logp, const int32_t *cu_rows, int64_t n_req, int64_t rows,
+                           int64_t C, int64_t max_rows, const float *t_cur, const float *t_next, float eta,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    if (n_req == 0 && rows == 0 && C > 0) return MOT_OK;
+    const int vs = validate_latent(n_req, rows, C, max_rows, cu_rows, workspace, workspace_bytes);
+    if (vs != MOT_OK) return vs;
+    if (n_req == 0) return MOT_ERR_INVALID_ARG;
+    if (!x || !v || !logp || !t_cur || !t_next) return MOT_ERR_INVALID_ARG;
+    const bool sample = noise != nullptr;
+    if (sample ? (!x_next_out || x_next_in) : (!x_next_in || x_next_out)) return MOT_ERR_INVALID_ARG;
+    if (!(eta > 0.0f) || !isfinite(eta)) return MOT_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(v) || (noise && !aligned16(noise)) || (x_next_in && !aligned16(x_next_in)) ||
+        (x_next_out && !aligned16(x_next_out)) || (reinterpret_cast<uintptr_t>(logp) & 3u) ||
+        (reinterpret_cast<uintptr_t>(t_cur) & 3u) || (reinterpret_cast<uintptr_t>(t_next) & 3u))
+        return MOT_ERR_MISALIGNED;
+    const int64_t bytes = rows * C * 4;
+    const int64_t wsb = (int64_t)latent_ws_bytes(n_req, max_rows);
+    const void *ins[] = {x, v, noise, x_next_in, cu_rows, t_cur, t_next, workspace};
+    const int64_t in_bytes[] = {bytes, bytes, bytes, bytes, 4 * (n_req + 1), 4 * n_req, 4 * n_req, wsb};
+    for (int i = 0; i < 8; ++i) {
+        if (!ins[i]) continue;
+        if (x_next_out && overlaps(x_next_out, bytes, ins[i], in_bytes[i])) return MOT_ERR_INVALID_ARG;
+        if (overlaps(logp, 4 * n_req, ins[i], in_bytes[i])) return MOT_ERR_INVALID_ARG;
+        if (i < 7 && overlaps(workspace, wsb, ins[i], in_bytes[i])) return MOT_ERR_INVALID_ARG;
+    }
+    if (x_next_out && overlaps(x_next_out, bytes, logp, 4 * n_req)) return MOT_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(s);
+    if (!guard.ok()) return MOT_ERR_DEVICE;
+    int32_t *err = static_cast<int32_t *>(workspace);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(workspace) + MOT_WS_HEADER_BYTES);
+    return mot::launch_sde_step(x, v, noise, x_next_in, x_next_out, logp, cu_rows, (int)n_req, rows, (int)C, max_rows,
+                                t_cur, t_next, eta, err, part, s) == hipSuccess
+               ? MOT_OK
+               : MOT_ERR_DEVICE;
 }
 
 int mot_read_device_error(const void *workspace, void *stream) {

@@ -90,6 +90,17 @@ hipError_t launch_seqlens_check(const int32_t *cu_q, const int32_t *cu_k, int n,
 hipError_t launch_vt_packed(const uint16_t *v, int64_t ldv, int kv_cols, const int32_t *cu_k, int n, uint16_t *out,
                             int64_t ldo, const int32_t *err, hipStream_t stream);
 
+// Latent step (mot_latent.hip): chunk slots of one request, and the launches.
+int latent_chunks(int64_t max_rows);
+hipError_t launch_cfg_combine(const float *vc, const float *vt, const float *vi, float *out, const int32_t *cu,
+                              int n, int64_t rows, int C, int64_t max_rows, const float *t, float s_text, float s_img,
+                              float t_lo, float t_hi, float rmin, int type, int32_t *err, float *part,
+                              hipStream_t stream);
+hipError_t launch_sde_step(const float *x, const float *v, const float *noise, const float *xn_in, float *xn_out,
+                           float *logp, const int32_t *cu, int n, int64_t rows, int C, int64_t max_rows,
+                           const float *t_cur, const float *t_next, float eta, int32_t *err, float *part,
+                           hipStream_t stream);
+
 hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t *perm,
                        hipStream_t stream);
 // Modality bytes from the und / gen index lists; cnt: T words of scratch.

@@ -342,3 +342,77 @@ def _index_sets(**kw):
 ])
 def test_index_sets_fail_closed(kw, code):
     assert _index_sets(**kw) == code
+
+
+def _cfg(**kw):
+    F = ctypes.c_float
+    args = dict(vc=A, vt=2 * A, vi=3 * A, out=4 * A, cu=5 * A, n=2, rows=100, C=64, maxr=64, t=6 * A, s1=4.0, s2=1.5,
+                lo=0.0, hi=1.0, rmin=0.0, kind=1, ws=7 * A, wsb=1 << 20)
+    args.update(kw)
+    return mot.lib().mot_cfg_combine_renorm(args["vc"], args["vt"], args["vi"], args["out"], args["cu"], args["n"],
+                                            args["rows"], args["C"], args["maxr"], args["t"], args["s1"], args["s2"],
+                                            args["lo"], args["hi"], args["rmin"], args["kind"], args["ws"], args["wsb"],
+                                            None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0, rows=0), OK),
+    (dict(n=-1), INVALID),
+    (dict(C=0), INVALID),
+    (dict(C=66), SHAPE),
+    (dict(C=8192), SHAPE),
+    (dict(maxr=0), INVALID),
+    (dict(vc=None), INVALID),
+    (dict(vt=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(t=None), INVALID),
+    (dict(cu=None), INVALID),
+    (dict(kind=3), INVALID),
+    (dict(rmin=1.5), INVALID),
+    (dict(s1=float("inf")), INVALID),
+    (dict(vc=A + 4), MISALIGNED),
+    (dict(cu=5 * A + 2), MISALIGNED),
+    (dict(ws=None), WORKSPACE),
+    (dict(wsb=200), WORKSPACE),
+    (dict(ws=7 * A + 16), MISALIGNED),
+    (dict(out=A + 1024), INVALID),            # out overlaps v_cond
+    (dict(n=0), INVALID),                      # rows without requests
+])
+def test_cfg_fails_closed(kw, code):
+    assert _cfg(**kw) == code
+
+
+def _sde(**kw):
+    args = dict(x=A, v=2 * A, z=3 * A, xin=None, xout=4 * A, lp=5 * A, cu=6 * A, n=2, rows=100, C=64, maxr=64,
+                tc=7 * A, tn=8 * A, eta=0.7, ws=9 * A, wsb=1 << 20)
+    args.update(kw)
+    return mot.lib().mot_flow_sde_step_logp(args["x"], args["v"], args["z"], args["xin"], args["xout"], args["lp"],
+                                            args["cu"], args["n"], args["rows"], args["C"], args["maxr"], args["tc"],
+                                            args["tn"], args["eta"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0, rows=0), OK),
+    (dict(x=None), INVALID),
+    (dict(lp=None), INVALID),
+    (dict(tn=None), INVALID),
+    (dict(xout=None), INVALID),                   # sampling needs x_next_out
+    (dict(xin=10 * A), INVALID),                  # both modes at once
+    (dict(z=None, xout=None), INVALID),           # neither mode
+    (dict(eta=0.0), INVALID),
+    (dict(eta=float("nan")), INVALID),
+    (dict(C=30), SHAPE),
+    (dict(xout=4 * A + 8), MISALIGNED),
+    (dict(lp=5 * A + 2), MISALIGNED),
+    (dict(wsb=100), WORKSPACE),
+    (dict(xout=A + 512), INVALID),                # x_next_out overlaps x
+    (dict(lp=2 * A + 64), INVALID),               # logp overlaps v
+])
+def test_sde_fails_closed(kw, code):
+    assert _sde(**kw) == code
+
+
+def test_latent_workspace_bytes():
+    assert mot.latent_workspace_bytes(0, 64) == 0
+    assert mot.latent_workspace_bytes(3, 1024) == 256 + 3 * 16 * 8
+    assert mot.latent_workspace_bytes(1, 65) == 256 + 2 * 8
