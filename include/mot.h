@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 10
+#define MOT_ABI_VERSION 11
 
 typedef enum mot_status {
     MOT_OK = 0,
@@ -172,6 +172,30 @@ int mot_routed_gemm(const uint16_t *x, int64_t ldx,
                     const float *rstd, const uint16_t *nw_und, const uint16_t *nw_gen,
                     void *workspace, size_t workspace_bytes,
                     unsigned flags, void *stream);
+
+/* The QKV projection with the per-head routed QK RMSNorm and rotary
+ * embedding in its epilogue: the "mot_qk_norm_rope" work item of the RFC page
+ * (section 5) fused into "mot_routed_gemm", in the order of the page's
+ * reference hazards (QK norm in fp32, then the rotation with Q/K in bf16).
+ * The output bytes are those of mot_routed_gemm followed by mot_qk_norm_rope
+ * on its rows (same arithmetic, bit for bit), without writing and re-reading
+ * the q and k columns in between.
+ *   Arguments of mot_routed_gemm (no prologue) and of mot_qk_norm_rope:
+ *   y [T][ldy] with N >= 128 * (n_q_heads + n_k_heads): q heads at columns
+ *   [0, 128 n_q_heads), k heads next, the rest (v) stored as the GEMM's
+ *   bytes.  flags: tile-shape flags only (MOT_FLAG_PLAN_READY is
+ *   MOT_ERR_INVALID_ARG: the call builds its plan, whose error word it
+ *   uses).  Rows whose position is outside the table keep the GEMM's bytes and
+ *   raise MOT_ERR_POSITION in the workspace's error word; an invalid modality
+ *   byte makes the call write nothing and raises MOT_ERR_MODALITY (the larger
+ *   code wins).
+ * Errors: those of both calls.  Since ABI 11. */
+int mot_routed_gemm_qk_norm_rope(const uint16_t *x, int64_t ldx, const uint16_t *w_und, const uint16_t *w_gen,
+                                 const uint8_t *modality, uint16_t *y, int64_t ldy, int64_t T, int64_t K, int64_t N,
+                                 int64_t n_q_heads, int64_t n_k_heads, const uint16_t *qw_und, const uint16_t *qw_gen,
+                                 const uint16_t *kw_und, const uint16_t *kw_gen, const int32_t *positions,
+                                 const uint16_t *cos_table, const uint16_t *sin_table, int64_t n_pos, float eps,
+                                 void *workspace, size_t workspace_bytes, unsigned flags, void *stream);
 
 /* Largest pack of mot_routed_gemm_noalloc. */
 #define MOT_NOALLOC_MAX_T 65536

@@ -24,10 +24,10 @@ __all__ = [
     "transpose", "routed_gemm_dx", "grad_w", "qk_norm_rope", "joint_attention",
     "attention_workspace_bytes", "joint_attention_varlen", "attention_varlen_workspace_bytes",
     "read_device_error", "status_string", "LIB_PATH", "latent_workspace_bytes", "cfg_combine_renorm",
-    "flow_sde_step_logp", "RENORM",
+    "flow_sde_step_logp", "RENORM", "routed_gemm_qk_norm_rope",
 ]
 
-ABI_VERSION = 10
+ABI_VERSION = 11
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
 WS_HEADER_BYTES = 256
 FLAG_PLAN_READY = 1
@@ -42,7 +42,7 @@ EXPORTS = (
     "mot_transpose_bf16", "mot_qk_norm_rope", "mot_routed_gemm_f32", "mot_attention_workspace_bytes",
     "mot_joint_attention", "mot_attention_varlen_workspace_bytes", "mot_joint_attention_varlen",
     "mot_modality_from_index_sets", "mot_routed_gemm_noalloc", "mot_latent_workspace_bytes",
-    "mot_cfg_combine_renorm", "mot_flow_sde_step_logp",
+    "mot_cfg_combine_renorm", "mot_flow_sde_step_logp", "mot_routed_gemm_qk_norm_rope",
 )
 
 STATUS = {
@@ -110,6 +110,9 @@ def lib():
     L.mot_cfg_combine_renorm.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, F, F, F, F, F, ctypes.c_int, P, SZ, P]
     L.mot_flow_sde_step_logp.restype = ctypes.c_int
     L.mot_flow_sde_step_logp.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, P, P, F, P, SZ, P]
+    L.mot_routed_gemm_qk_norm_rope.restype = ctypes.c_int
+    L.mot_routed_gemm_qk_norm_rope.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, P,
+                                               I64, ctypes.c_float, P, SZ, U, P]
     L.mot_routed_gemm_noalloc.restype = ctypes.c_int
     L.mot_routed_gemm_noalloc.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64, P, P, P, P, U, P]
     L.mot_modality_from_index_sets.restype = ctypes.c_int
@@ -308,6 +311,49 @@ def routed_gemm_noalloc(x, w_und, w_gen, modality, out, norm=None, error_out=Non
                                        _ptr(out), _rows(out, "out"), T, K, N, _ptr(rstd), _ptr(nw_u), _ptr(nw_g),
                                        _ptr(error_out), TILE_FLAGS[tile], _stream(x.device))
     _check(st, "mot_routed_gemm_noalloc")
+    return out
+
+
+def routed_gemm_qk_norm_rope(x, w_und, w_gen, modality, n_q_heads, n_k_heads, q_norm, k_norm, positions,
+                             cos_table, sin_table, eps=1e-6, out=None, workspace=None, tile=None):
+    """The QKV projection with the per-head QK RMSNorm and rotary embedding in
+    its epilogue: the bytes of routed_gemm followed by qk_norm_rope on its
+    output, in one call.  q_norm, k_norm: (und, gen) pairs of [128] bf16;
+    positions [T] int32; cos_table, sin_table [n_pos, 64] bf16.  Rows whose
+    position is outside the table keep the GEMM's bytes and raise the
+    workspace's error word (MOT_ERR_POSITION).  Returns out [T, N]."""
+    _req(x, "x", torch.bfloat16, 2)
+    _req(w_und, "w_und", torch.bfloat16, 2)
+    _req(w_gen, "w_gen", torch.bfloat16, 2)
+    _req(modality, "modality", torch.uint8, 1)
+    _req(positions, "positions", torch.int32, 1)
+    for t, name in ((cos_table, "cos_table"), (sin_table, "sin_table")):
+        _req(t, name, torch.bfloat16, 2)
+    if w_und.shape != w_gen.shape or not (w_und.is_contiguous() and w_gen.is_contiguous()):
+        raise ValueError("w_und and w_gen must be contiguous and of the same shape")
+    T, K = x.shape
+    N = w_und.shape[0]
+    if modality.shape[0] != T or positions.shape[0] != T or w_und.shape[1] != K:
+        raise ValueError("shapes: x [T, K], weights [N, K], modality and positions [T]")
+    if cos_table.shape != sin_table.shape or cos_table.shape[1] != 64:
+        raise ValueError("cos_table and sin_table must both be [n_pos, 64]")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    _req(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (T, N):
+        raise ValueError(f"out must be [{T}, {N}]")
+    if workspace is None:
+        workspace = new_workspace(T, x.device)
+    if tile not in TILE_FLAGS:
+        raise ValueError(f"tile must be one of {sorted(k for k in TILE_FLAGS if k)}")
+    tensors = [*(w.contiguous() for w in (*q_norm, *k_norm)), positions.contiguous(), cos_table.contiguous(),
+               sin_table.contiguous()]
+    st = lib().mot_routed_gemm_qk_norm_rope(_ptr(x), _rows(x, "x"), _ptr(w_und), _ptr(w_gen),
+                                            _ptr(modality.contiguous()), _ptr(out), _rows(out, "out"), T, K, N,
+                                            int(n_q_heads), int(n_k_heads), *(_ptr(t) for t in tensors),
+                                            cos_table.shape[0], float(eps), _ptr(workspace), workspace.numel(),
+                                            TILE_FLAGS[tile], _stream(x.device))
+    _check(st, "mot_routed_gemm_qk_norm_rope")
     return out
 
 

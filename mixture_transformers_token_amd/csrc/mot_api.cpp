@@ -114,6 +114,7 @@ struct RoutedCall {
     size_t workspace_bytes;
     unsigned flags;
     int out_f32 = 0;       // 1: y is fp32 [T][ldy]
+    const mot::QkArgs *qk = nullptr;  // fused QK norm + rotary epilogue (qkv, ld, T unused)
 };
 
 int validate_routed(const RoutedCall &c) {
@@ -194,6 +195,35 @@ int run_routed(const RoutedCall &c, bool swiglu, void *stream) {
     a.w_bytes = (uint32_t)(c.w_rows * c.K * 2);
     a.y_bytes = (uint32_t)(((c.T - 1) * c.ldy + c.N) * (c.out_f32 ? 4 : 2));
     a.out_f32 = c.out_f32;
+    if (c.qk != nullptr && c.T <= mot::kSkinnyMaxT && a.tile_mode == 0) {
+        // small pack: the weight-bound GEMM (its 32-column slabs split heads),
+        // then the standalone QK kernel on its rows, which does nothing if
+        // the GEMM's error word is set
+        if (mot::launch_gemm(a, false, inline_route, s) != hipSuccess) return MOT_ERR_DEVICE;
+        mot::QkArgs q = *c.qk;
+        q.qkv = static_cast<uint16_t *>(c.y);
+        q.ld = c.ldy;
+        q.T = c.T;
+        q.err = hdr;
+        q.after_gemm = 1;
+        return mot::launch_qk_norm_rope(q, s) == hipSuccess ? MOT_OK : MOT_ERR_DEVICE;
+    }
+    if (c.qk != nullptr) {
+        a.qk_heads = c.qk->hq + c.qk->hk;
+        a.qk_hq = c.qk->hq;
+        a.qw_und = c.qk->qw_und;
+        a.qw_gen = c.qk->qw_gen;
+        a.kw_und = c.qk->kw_und;
+        a.kw_gen = c.qk->kw_gen;
+        a.positions = c.qk->positions;
+        a.cos_t = c.qk->cos_t;
+        a.sin_t = c.qk->sin_t;
+        a.n_pos = c.qk->n_pos;
+        a.qk_eps = c.qk->eps;
+        // the in-kernel segment list raises errors by atomic maximum in a
+        // cleared word (the plan kernel writes the word itself)
+        if (inline_route && mot::launch_set_word(hdr, 0, s) != hipSuccess) return MOT_ERR_DEVICE;
+    }
     if (mot::launch_gemm(a, swiglu, inline_route, s) != hipSuccess) return MOT_ERR_DEVICE;
     return MOT_OK;
 }
@@ -325,6 +355,48 @@ int mot_routed_gemm(const uint16_t *x, int64_t ldx, const uint16_t *w_und, const
                     void *workspace, size_t workspace_bytes, unsigned flags, void *stream) {
     RoutedCall c{x, ldx, w_und, w_gen, modality, y, ldy, T, K, N, N,
                  rstd, nw_und, nw_gen, workspace, workspace_bytes, flags};
+    return run_routed(c, false, stream);
+}
+
+int mot_routed_gemm_qk_norm_rope(const uint16_t *x, int64_t ldx, const uint16_t *w_und, const uint16_t *w_gen,
+                                 const uint8_t *modality, uint16_t *y, int64_t ldy, int64_t T, int64_t K, int64_t N,
+                                 int64_t n_q_heads, int64_t n_k_heads, const uint16_t *qw_und, const uint16_t *qw_gen,
+                                 const uint16_t *kw_und, const uint16_t *kw_gen, const int32_t *positions,
+                                 const uint16_t *cos_table, const uint16_t *sin_table, int64_t n_pos, float eps,
+                                 void *workspace, size_t workspace_bytes, unsigned flags, void *stream) {
+    if (n_q_heads < 0 || n_k_heads < 0 || n_q_heads + n_k_heads == 0) return MOT_ERR_INVALID_ARG;
+    if (!(eps > 0.0f) || !isfinite(eps)) return MOT_ERR_INVALID_ARG;
+    if (flags & MOT_FLAG_PLAN_READY) return MOT_ERR_INVALID_ARG;  // the call raises errors in its own plan's word
+    RoutedCall c{x, ldx, w_und, w_gen, modality, y, ldy, T, K, N, N,
+                 nullptr, nullptr, nullptr, workspace, workspace_bytes, flags};
+    const int v = validate_routed(c);
+    if (v != MOT_OK || T == 0) return v;
+    if (128 * (n_q_heads + n_k_heads) > N) return MOT_ERR_INVALID_ARG;
+    if (!qw_und || !qw_gen || !kw_und || !kw_gen || !positions || !cos_table || !sin_table || n_pos <= 0)
+        return MOT_ERR_INVALID_ARG;
+    if (n_pos > MOT_MAX_T) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (!aligned16(qw_und) || !aligned16(qw_gen) || !aligned16(kw_und) || !aligned16(kw_gen) || !aligned16(positions) ||
+        !aligned16(cos_table) || !aligned16(sin_table))
+        return MOT_ERR_MISALIGNED;
+    const int64_t y_bytes = ((T - 1) * ldy + N) * 2;
+    const void *ins[] = {qw_und, qw_gen, kw_und, kw_gen, positions, cos_table, sin_table};
+    const int64_t in_bytes[] = {256, 256, 256, 256, 4 * T, 128 * n_pos, 128 * n_pos};
+    for (int i = 0; i < 7; ++i)
+        if (overlaps(y, y_bytes, ins[i], in_bytes[i])) return MOT_ERR_INVALID_ARG;
+    mot::QkArgs q;
+    q.hq = (int)n_q_heads;
+    q.hk = (int)n_k_heads;
+    q.modality = modality;
+    q.qw_und = qw_und;
+    q.qw_gen = qw_gen;
+    q.kw_und = kw_und;
+    q.kw_gen = kw_gen;
+    q.positions = positions;
+    q.cos_t = cos_table;
+    q.sin_t = sin_table;
+    q.n_pos = (int)n_pos;
+    q.eps = eps;
+    c.qk = &q;
     return run_routed(c, false, stream);
 }
 

@@ -46,6 +46,18 @@ struct GemmArgs {
     uint32_t w_bytes;     // extent of one weight matrix (bytes, < 4 GiB)
     uint32_t y_bytes;     // extent of y from its base (bytes, < 4 GiB)
     int out_f32;          // 1: y is fp32 (plain GEMM, 256 x 256 tiles only)
+    // Fused per-head QK RMSNorm + rotary epilogue (the QKV projection's
+    // mot_qk_norm_rope step inside the GEMM; qk_heads == 0: none).  Heads are
+    // 128 output columns from column 0: qk_hq q heads, then k heads, up to
+    // qk_heads; later columns (v) are stored plain.  Position errors raise
+    // MOT_ERR_POSITION in hdr_out[0] by atomic maximum.
+    int qk_heads = 0;
+    int qk_hq = 0;
+    const uint16_t *qw_und = nullptr, *qw_gen = nullptr, *kw_und = nullptr, *kw_gen = nullptr;
+    const int32_t *positions = nullptr;
+    const uint16_t *cos_t = nullptr, *sin_t = nullptr;  // [n_pos][64] bf16
+    int n_pos = 0;
+    float qk_eps = 0.0f;
 };
 
 // Routed per-head QK RMSNorm + rotary embedding, in place on QKV rows.
@@ -60,7 +72,9 @@ struct QkArgs {
     const uint16_t *cos_t, *sin_t;                      // [n_pos][64] bf16
     int n_pos;
     float eps;
-    int32_t *err;         // error word (cleared by the launch)
+    int32_t *err;         // error word (cleared by the launch, unless after_gemm)
+    int after_gemm = 0;   // 1: runs after the routed GEMM that wrote these rows: the word
+                          // holds the GEMM's result; if set, nothing is done
 };
 
 // Shared joint attention, head dimension 128 (mot_attention.hip).
@@ -110,6 +124,8 @@ hipError_t launch_index_sets(const int32_t *und_idx, int64_t n_und, const int32_
 // inline_route the kernel builds (and publishes) the segment list itself.
 hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStream_t stream);
 hipError_t launch_qk_norm_rope(const QkArgs &a, hipStream_t stream);
+// *dst = v on the device (one thread), in stream order.
+hipError_t launch_set_word(int32_t *dst, int32_t v, hipStream_t stream);
 // *dst = *src on the device (one thread), in stream order.
 hipError_t launch_copy_word(const int32_t *src, int32_t *dst, hipStream_t stream);
 hipError_t launch_transpose(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t cols,

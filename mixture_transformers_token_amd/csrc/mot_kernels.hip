@@ -60,6 +60,60 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
+// ---- per-head QK RMSNorm + rotary helpers (standalone kernel and fused epilogue) ----
+
+constexpr int kErrPosition = 7;  // MOT_ERR_POSITION
+constexpr int kQkChunks = 2;     // 4-head chunks per wave (8 heads)
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16_rne(float v) { return __uint_as_float(pack2(v, 0.0f) << 16); }
+__device__ __forceinline__ float bf16_at(const u32x4_t &v, int e) {
+    return (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
+}
+
+// One head of one row, as 16 lanes hold it (lane gi of the group: elements
+// 8 gi .. 8 gi + 7 in v): the head's RMSNorm (sum of squares per lane in
+// element order, then the xor-butterfly over the group: one fixed tree),
+// y = bf16((x * rstd) * w), then the rotate-half rotation with the
+// partner 64 columns away in lane gi ^ 8.  `live` lanes hold a real head;
+// every lane of the wave must call it (it shuffles).  Shared by the
+// standalone kernel and the QKV GEMM's fused epilogue, so both give the same
+// bytes.
+__device__ __forceinline__ u32x4_t qk_head(const u32x4_t &v, bool live, int gi, float eps, const u32x4_t &wv,
+                                           const u32x4_t &cv, const u32x4_t &sv) {
+    float ss = 0.0f;
+    if (live) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = bf16_at(v, e);
+            ss = e == 0 ? x * x : ss + x * x;
+        }
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    const float rstd = 1.0f / sqrtf(ss / 128.0f + eps);
+    u32x4_t y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        y[e] = pack2(bf16_lo(v[e]) * rstd * bf16_lo(wv[e]), bf16_hi(v[e]) * rstd * bf16_hi(wv[e]));
+    u32x4_t z;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = (uint32_t)__shfl_xor((int)y[e], 8);
+    // the rotation's sign: first half y*c - y'*s, second half y*c + y'*s
+    const float sg = gi < 8 ? -1.0f : 1.0f;
+    u32x4_t o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_rne(bf16_rne(bf16_lo(y[e]) * bf16_lo(cv[e])) +
+                                  bf16_rne(sg * (bf16_lo(z[e]) * bf16_lo(sv[e]))));
+        const float hi = bf16_rne(bf16_rne(bf16_hi(y[e]) * bf16_hi(cv[e])) +
+                                  bf16_rne(sg * (bf16_hi(z[e]) * bf16_hi(sv[e]))));
+        o[e] = pack2(lo, hi);
+    }
+    return o;
+}
+
 // ============================================================================
 // Routing plan
 // ============================================================================
@@ -533,6 +587,109 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
+// ---- fused QK norm + rotary epilogue (QKV projection) ------------------------
+//
+// The "mot_qk_norm_rope" step (RL-Kernel RFC page, section 5) inside the QKV
+// GEMM.  A head is 128 output columns, and both tile shapes that run it (256 x
+// 256 and 128 x 128) start on a head boundary.  The tile's bf16 outputs (the
+// plain GEMM's bytes) are staged in LDS one head at a time, the rotary table
+// rows of the tile's positions are staged beside them by LDS-DMA, and each
+// 16-lane group runs qk_head on one (row, head) exactly as the standalone
+// kernel's groups hold it: the result is that kernel's, bit for bit.  Staged
+// head rows are 256 bytes, their 16-byte chunks XOR-swizzled by the row.
+
+constexpr int kQkRowBytes = 256;
+
+__device__ __forceinline__ uint32_t qk_chunk_off(int r, int c) {
+    return (uint32_t)(r * kQkRowBytes + ((c ^ (r & 15)) << 4));
+}
+
+// Positions of the tile's rows into p_rows: -1 for a position outside the
+// table (which raises MOT_ERR_POSITION; the row keeps the GEMM's bytes), 0
+// for the slots past the tile's rows.
+__device__ __forceinline__ void qk_positions(const GemmArgs &a, const Tile &ti, const int32_t *s_rows,
+                                             int32_t *p_rows, int bm) {
+    for (int i = (int)threadIdx.x; i < bm; i += kThreads) {
+        int p = 0;
+        if (i < ti.count) {
+            p = a.positions[s_rows[i]];
+            if (p < 0 || p >= a.n_pos) {
+                atomicMax(a.hdr_out, kErrPosition);
+                p = -1;
+            }
+        }
+        p_rows[i] = p;
+    }
+}
+
+// The rotary table rows (128 bytes of cos into cs, of sin into sn) of the
+// tile's rows, by LDS-DMA: each instruction fills eight rows.  A bad or
+// padding row reads table row 0 (its result is not stored).
+template <int BM>
+__device__ __forceinline__ void qk_tables(const GemmArgs &a, const int32_t *p_rows, uint8_t *cs, uint8_t *sn,
+                                          int wave, int lane) {
+    const rsrc_t cr = make_rsrc(a.cos_t, (uint32_t)a.n_pos * 128u);
+    const rsrc_t sr = make_rsrc(a.sin_t, (uint32_t)a.n_pos * 128u);
+#pragma unroll
+    for (int r0 = wave * 8; r0 < BM; r0 += 32) {
+        const int p = max(p_rows[r0 + (lane >> 3)], 0);
+        const uint32_t off = (uint32_t)p * 128u + (uint32_t)(lane & 7) * 16u;
+        dma16(cr, off, 0, cs + r0 * 128);
+        dma16(sr, off, 0, sn + r0 * 128);
+    }
+}
+
+// A wave's MI x MJ accumulator blocks as bf16 into a head's staging rows:
+// token row row0 + 32 j + (lane & 31), head column col0 + 32 i + 8 q +
+// 4 (lane >> 5) .. +3 (the plain epilogue's rounding of the same values).
+template <int MI, int MJ>
+__device__ __forceinline__ void qk_stage(const f32x16_t (&acc)[MI][MJ], uint8_t *st, int row0, int col0, int lane) {
+    const int rsel = lane & 31, khalf = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < MJ; ++j)
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = row0 + 32 * j + rsel;
+                const int c = col0 + 32 * i + 8 * q + 4 * khalf;
+                const u32x2_t pk = {pack2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                    pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+                *(lds_u32x2 *)((lds_u8 *)st + qk_chunk_off(r, c >> 3) + (c & 7) * 2) = pk;
+            }
+}
+
+// One staged head (tile rows [0, BM): rows below 128 in st_lo, the rest in
+// st_hi; output columns col0 .. col0 + 127): group g of the wave takes rows
+// 4 wave + g, + 16, ...  Heads past the q and k heads (v) are stored as they
+// are.
+template <int BM>
+__device__ __forceinline__ void qk_head_rows(const GemmArgs &a, const Tile &ti, int col0, const uint8_t *st_lo,
+                                             const uint8_t *st_hi, const uint8_t *cs, const uint8_t *sn,
+                                             const int32_t *s_rows, const int32_t *p_rows, int wave, int lane) {
+    if (col0 >= a.N) return;  // uniform
+    const int gi = lane & 15, g = lane >> 4;
+    const int hg = col0 >> 7;
+    const bool qk = hg < a.qk_heads;
+    const uint16_t *w = hg < a.qk_hq ? (ti.set ? a.qw_gen : a.qw_und) : (ti.set ? a.kw_gen : a.kw_und);
+    u32x4_t wv = {0u, 0u, 0u, 0u};
+    if (qk) wv = *(const u32x4_t *)(w + 8 * gi);
+    const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+    const uint32_t ldy_bytes = (uint32_t)a.ldy * 2u;
+    for (int r = wave * 4 + g; r < BM; r += 16) {
+        const uint8_t *st = (BM > 128 && r >= 128) ? st_hi : st_lo;
+        const u32x4_t v = *(const lds_u32x4 *)((const lds_u8 *)st + qk_chunk_off(r & 127, gi));
+        const u32x4_t cv = *(const lds_u32x4 *)((const lds_u8 *)cs + r * 128 + (gi & 7) * 16);
+        const u32x4_t sv = *(const lds_u32x4 *)((const lds_u8 *)sn + r * 128 + (gi & 7) * 16);
+        const u32x4_t o = qk_head(v, true, gi, a.qk_eps, wv, cv, sv);
+        if (r < ti.count && col0 + 8 * gi < a.N) {  // (a last head may end at a 64-column edge)
+            const u32x4_t out = (qk && p_rows[r] >= 0) ? o : v;
+            __builtin_amdgcn_raw_buffer_store_b128(out, yr, (uint32_t)s_rows[r] * ldy_bytes + (uint32_t)(col0 + 8 * gi) * 2u,
+                                                   0, 0);
+        }
+    }
+}
+
 // Rows per epilogue pass: the largest multiple of 32 that divides the wave's
 // rows and whose padded rows fit one 32 KiB LDS array.
 constexpr int ep_rows(int wm, int rs) {
@@ -622,10 +779,13 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs &a, const Tile &t
 // refill (re-reading the final k-block when it runs past the end), so the
 // number of DMA instructions in flight is a compile-time constant.
 // s_rows (the tile's A rows) is filled and published by the caller.
-template <int BM, int BN, int NS, bool SWIGLU, bool PRO>
+template <int BM, int BN, int NS, bool SWIGLU, bool PRO, bool QK = false>
 __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint8_t *const (&xb)[NS],
                                          uint8_t *const (&wb)[NS], lds_u8 *const eb,
-                                         const int32_t *s_rows, uint16_t *s_nw, const int tid) {
+                                         const int32_t *s_rows, uint16_t *s_nw, const int tid,
+                                         int32_t *qk_p = nullptr) {
+    static_assert(!QK || (BM == 128 && BN == 128 && NS >= 2 && !SWIGLU && !PRO),
+                  "fused QK epilogue: plain 128 x 128 tiles");
     constexpr int WM = BM / 2, WN = BN / 2;   // wave tile: tokens x weight rows
     constexpr int MJ = WM / 32, MI = WN / 32; // MFMA blocks per wave
     constexpr int NM = MI * MJ;               // MFMAs per k-step
@@ -847,6 +1007,20 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
 
     // Epilogue.
     __syncthreads();  // every wave is done reading the last stage
+    if constexpr (QK) {
+        if (ti.wrow0 < a.qk_heads * 128) {
+            // the tile is one head: staged in array 0, the rotary rows in
+            // array 1 (cos, then sin)
+            qk_positions(a, ti, s_rows, qk_p, BM);
+            __syncthreads();
+            qk_tables<BM>(a, qk_p, xb[1], xb[1] + BM * 128, wave, lane);
+            qk_stage<MI, MJ>(acc, xb[0], wm * WM, wn * WN, lane);
+            wait_vm_lgkm0<0>();
+            __syncthreads();
+            qk_head_rows<BM>(a, ti, ti.wrow0, xb[0], xb[0], xb[1], xb[1] + BM * 128, s_rows, qk_p, wave, lane);
+            return;
+        }
+    }
     epilogue_staged<WM, WN, MI, MJ, SWIGLU>(a, ti, acc, eb, s_rows, lane, wm, wn);
 }
 
@@ -868,10 +1042,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
 // it first.  The epilogue stores straight from the accumulators (8-byte
 // pieces, default cache policy); measured faster here than staging through
 // LDS, which would need the row list rebuilt.
-template <bool SWIGLU, bool F32 = false>
+template <bool SWIGLU, bool F32 = false, bool QK = false, typename FillRows = int>
 __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint8_t *const (&hs)[5],
-                                         const int32_t *s_rows, const int tid) {
+                                         const int32_t *s_rows, const int tid, const FillRows &fill_rows = 0,
+                                         int32_t *qk_p = nullptr) {
     static_assert(!(SWIGLU && F32), "fp32 output: plain GEMM only");
+    static_assert(!QK || (!SWIGLU && !F32), "fused QK epilogue: plain bf16 GEMM only");
     constexpr uint32_t kOutBytes = F32 ? 4u : 2u;  // bytes per output element
     constexpr int BM = kBigM, BN = kBigN;
     constexpr int WM = BM / 2, WN = BN / 2;
@@ -1041,6 +1217,30 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
     if (kt + 3 < nk) stage(std::integral_constant<int, 3>{}, kt + 3);
     wait_vm_lgkm0<0>();  // no DMA may still be writing LDS when the tile ends
 
+    if constexpr (QK) {
+        if (ti.wrow0 < a.qk_heads * 128) {
+            // Two heads per tile, one after the other: the head of the waves
+            // with wn = h is staged in slots 0 (rows 0-127) and 1 (rows
+            // 128-255); the rotary rows go to slots 2 (cos) and 3 (sin); the
+            // row list, which the ring overwrote, is rebuilt in slot 4.
+            __syncthreads();  // every wave is done with the ring
+            fill_rows();
+            __syncthreads();
+            qk_positions(a, ti, s_rows, qk_p, BM);
+            __syncthreads();
+            qk_tables<BM>(a, qk_p, hs[2], hs[3], wave, lane);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (wn == h) qk_stage<MI, MJ>(acc, wm ? hs[1] : hs[0], 0, 0, lane);
+                wait_vm_lgkm0<0>();
+                __syncthreads();
+                qk_head_rows<BM>(a, ti, ti.wrow0 + 128 * h, hs[0], hs[1], hs[2], hs[3], s_rows, qk_p, wave, lane);
+                __syncthreads();  // the staging slots are read before the next head overwrites them
+            }
+            return;
+        }
+    }
+
     // Epilogue: lane holds, for token row m = lane&31 of each block, four
     // consecutive output columns per register quad (SwiGLU: the act of each
     // gate/up pair).
@@ -1107,11 +1307,12 @@ __device__ __forceinline__ uint16_t *prologue_nw_lds() {
 // list and scan scratch; the prologue's big tiles run two stages of A in
 // array 0 or 2 and W in array 1 or 3, and its norm weights take 16 KiB).
 // Small tiles run four stages, one array each.
-template <bool SWIGLU, bool PRO, bool INLINE, bool NARROW = false, bool F32 = false>
+template <bool SWIGLU, bool PRO, bool INLINE, bool NARROW = false, bool F32 = false, bool QK = false>
 __global__ void __launch_bounds__(kThreads, 1)
 gemm_kernel(GemmArgs a) {
     static_assert(!NARROW || (!SWIGLU && !PRO), "narrow tiles: plain GEMM only");
     static_assert(!F32 || (!SWIGLU && !PRO && !NARROW), "fp32 output: plain GEMM, big tiles only");
+    static_assert(!QK || (!SWIGLU && !PRO && !NARROW && !F32), "fused QK epilogue: plain bf16 GEMM only");
     constexpr int kArrayBytes = kBigM * kRowBytes;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kArrayBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kArrayBytes];
@@ -1120,6 +1321,7 @@ gemm_kernel(GemmArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds4[PRO ? 2048 : kArrayBytes];
     int32_t *const s_rows = (int32_t *)lds4;            // kBigM entries
     int *const s_red = (int *)(lds4 + kBigM * 4);       // block-scan scratch
+    int32_t *const qk_p = QK ? (int32_t *)(lds4 + 2048) : nullptr;  // fused QK epilogue: row positions
     uint16_t *const s_nw = prologue_nw_lds<PRO>();
 
     const int T = (int)a.T;
@@ -1133,7 +1335,13 @@ gemm_kernel(GemmArgs a) {
         U = __builtin_amdgcn_readfirstlane(U);
         G = T - U;
         if (blockIdx.x == 0 && threadIdx.x == 0) {
-            a.hdr_out[0] = bad ? kErrModality : 0;
+            // (with the fused QK epilogue the word is cleared before the
+            // launch and other workgroups may raise position errors in it)
+            if constexpr (QK) {
+                if (bad) atomicMax(a.hdr_out, kErrModality);
+            } else {
+                a.hdr_out[0] = bad ? kErrModality : 0;
+            }
             a.hdr_out[1] = bad ? 0 : U;
             a.hdr_out[2] = bad ? 0 : G;
             a.hdr_out[3] = T;
@@ -1151,7 +1359,9 @@ gemm_kernel(GemmArgs a) {
         // workgroup 0 raises MOT_ERR_PLAN in the error word, after every
         // workgroup has read the header (the others see the same header, so
         // they exit as well).
-        if (e0 != 0) return;
+        // (with the fused QK epilogue another workgroup may already have
+        // raised a position error; only the plan's own error stops the call)
+        if (QK ? e0 == kErrModality : e0 != 0) return;
         if (hdr[3] != T || U < 0 || G < 0 || U + G != T) {
             if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr_out[0] = kErrPlan;
             return;
@@ -1194,12 +1404,15 @@ gemm_kernel(GemmArgs a) {
         asm volatile("" : "+v"(tid));
         __syncthreads();  // every wave is done with the previous tile's LDS
         // the tile's rows into s_rows
-        if constexpr (INLINE) {
-            route_gather(rb, ti.set, ti.first - (ti.set ? U : 0), ti.count, bm, s_rows, s_red);
-        } else {
-            for (int i = threadIdx.x; i < bm; i += kThreads)
-                s_rows[i] = i < ti.count ? min(max(a.perm[ti.first + i], 0), T - 1) : 0;
-        }
+        auto fill_rows = [&]() {
+            if constexpr (INLINE) {
+                route_gather(rb, ti.set, ti.first - (ti.set ? U : 0), ti.count, bm, s_rows, s_red);
+            } else {
+                for (int i = threadIdx.x; i < bm; i += kThreads)
+                    s_rows[i] = i < ti.count ? min(max(a.perm[ti.first + i], 0), T - 1) : 0;
+            }
+        };
+        fill_rows();
         __syncthreads();
         if constexpr (INLINE) {
             // the tiles of weight rows [0, ...) cover every row once: they
@@ -1220,13 +1433,13 @@ gemm_kernel(GemmArgs a) {
                 run_tile<kBigM, kBigN, 2, SWIGLU, PRO>(a, ti, xb, wb, eb, s_rows, s_nw, tid);
             } else {
                 uint8_t *const hs[5] = {lds0, lds1, lds2, lds3, lds4};
-                run_big5<SWIGLU, F32>(a, ti, hs, s_rows, tid);
+                run_big5<SWIGLU, F32, QK>(a, ti, hs, s_rows, tid, fill_rows, qk_p);
             }
         } else if constexpr (!F32) {  // (mode 1 schedules no small tiles)
             constexpr int kHalf = kSmallM * kRowBytes;
             uint8_t *const xb[4] = {lds0, lds1, lds2, lds3};
             uint8_t *const wb[4] = {lds0 + kHalf, lds1 + kHalf, lds2 + kHalf, lds3 + kHalf};
-            run_tile<kSmallM, kSmallN, 4, SWIGLU, PRO>(a, ti, xb, wb, eb, s_rows, s_nw, tid);
+            run_tile<kSmallM, kSmallN, 4, SWIGLU, PRO, QK>(a, ti, xb, wb, eb, s_rows, s_nw, tid, qk_p);
         }
     }
 }
@@ -1625,16 +1838,6 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
 // their bytes and raise the error word (atomic maximum, so the larger code
 // wins whatever the order).
 
-constexpr int kErrPosition = 7;  // MOT_ERR_POSITION
-constexpr int kQkChunks = 2;     // 4-head chunks per wave (8 heads)
-
-__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
-__device__ __forceinline__ float bf16_rne(float v) { return __uint_as_float(pack2(v, 0.0f) << 16); }
-__device__ __forceinline__ float bf16_at(const u32x4_t &v, int e) {
-    return (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
-}
-
 __global__ void set_word_kernel(int32_t *p, int32_t v) {
     if (threadIdx.x == 0) *p = v;
 }
@@ -1644,6 +1847,7 @@ __global__ void copy_word_kernel(const int32_t *src, int32_t *dst) {
 }
 
 __global__ void __launch_bounds__(256) qk_norm_rope_kernel(QkArgs a) {
+    if (a.after_gemm && __builtin_amdgcn_readfirstlane(*(volatile const int32_t *)a.err) != 0) return;
     const int lane = threadIdx.x & 63;
     const int gi = lane & 15, grp = lane >> 4;  // lane in its 16-lane group, group = head within a chunk
     const int H = a.hq + a.hk;
@@ -1673,41 +1877,12 @@ __global__ void __launch_bounds__(256) qk_norm_rope_kernel(QkArgs a) {
         const u32x4_t cv = *(const u32x4_t *)(a.cos_t + ti), sv = *(const u32x4_t *)(a.sin_t + ti);
         const u32x4_t wq = *(const u32x4_t *)((m ? a.qw_gen : a.qw_und) + 8 * gi);
         const u32x4_t wk = *(const u32x4_t *)((m ? a.kw_gen : a.kw_und) + 8 * gi);
-        // the rotation's sign: first half y*c - y'*s, second half y*c + y'*s
-        const float sg = gi < 8 ? -1.0f : 1.0f;
 #pragma unroll
         for (int c = 0; c < kQkChunks; ++c) {
             if (c0 + c >= nch) break;  // wave-uniform
             const int h = 4 * (c0 + c) + grp;
             const bool live = h < H;
-            float ss = 0.0f;
-            if (live) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = bf16_at(v[c], e);
-                    ss = e == 0 ? x * x : ss + x * x;
-                }
-            }
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-            const float rstd = 1.0f / sqrtf(ss / 128.0f + a.eps);
-            const u32x4_t &wv = h < a.hq ? wq : wk;
-            u32x4_t y;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                y[e] = pack2(bf16_lo(v[c][e]) * rstd * bf16_lo(wv[e]), bf16_hi(v[c][e]) * rstd * bf16_hi(wv[e]));
-            u32x4_t z;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z[e] = (uint32_t)__shfl_xor((int)y[e], 8);
-            u32x4_t o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float lo = bf16_rne(bf16_rne(bf16_lo(y[e]) * bf16_lo(cv[e])) +
-                                          bf16_rne(sg * (bf16_lo(z[e]) * bf16_lo(sv[e]))));
-                const float hi = bf16_rne(bf16_rne(bf16_hi(y[e]) * bf16_hi(cv[e])) +
-                                          bf16_rne(sg * (bf16_hi(z[e]) * bf16_hi(sv[e]))));
-                o[e] = pack2(lo, hi);
-            }
+            const u32x4_t o = qk_head(v[c], live, gi, a.eps, h < a.hq ? wq : wk, cv, sv);
             if (live) *(u32x4_t *)(row + (int64_t)h * 128 + 8 * gi) = o;
         }
     }
@@ -1816,6 +1991,16 @@ hipError_t launch_gemm_narrow(const GemmArgs &a, bool inline_route, int grid, hi
     return hipGetLastError();
 }
 
+hipError_t launch_gemm_qk(const GemmArgs &a, bool inline_route, int grid, hipStream_t stream) {
+    if (inline_route)
+        hipLaunchKernelGGL((gemm_kernel<false, false, true, false, false, true>), dim3(grid), dim3(kThreads), 0, stream,
+                           a);
+    else
+        hipLaunchKernelGGL((gemm_kernel<false, false, false, false, false, true>), dim3(grid), dim3(kThreads), 0,
+                           stream, a);
+    return hipGetLastError();
+}
+
 template <bool SWIGLU, bool PRO>
 hipError_t launch_gemm_t(const GemmArgs &a, bool inline_route, int grid, hipStream_t stream) {
     if (inline_route)
@@ -1848,7 +2033,7 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
         const int64_t tiles = ((a.T + kBigM - 1) / kBigM + 1) * ((a.wrows + kBigN - 1) / kBigN);
         return launch_gemm_f32(a, inline_route, (int)(tiles < ncu ? tiles : ncu), stream);
     }
-    if (a.T <= kSkinnyMaxT && a.rstd == nullptr && a.tile_mode == 0) {
+    if (a.T <= kSkinnyMaxT && a.rstd == nullptr && a.tile_mode == 0 && a.qk_heads == 0) {
         // small pack: weight-bound path, one workgroup per 32 output columns
         // and set; XG = A row groups of 8 that cover the pack
         const int nblk = a.N / 32;
@@ -1882,16 +2067,22 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
     // weight blocks fits one tile per CU, 128 x 64 tiles put twice as many
     // CUs to work on the weight stream as 128 x 128 ones
     const int64_t narrow_tiles = ((a.T + kSmallM - 1) / kSmallM + 1) * ((a.wrows + kNarrowN - 1) / kNarrowN);
-    if (!swiglu && !pro && a.tile_mode == 0 && narrow_tiles <= ncu)
+    if (!swiglu && !pro && a.qk_heads == 0 && a.tile_mode == 0 && narrow_tiles <= ncu)
         return launch_gemm_narrow(a, inline_route, (int)narrow_tiles, stream);
     const int64_t bound = gemm_tile_bound(a.T, a.wrows, ncu);
     const int grid = (int)(bound < ncu ? bound : ncu);
     if (grid <= 0) return hipSuccess;
+    if (a.qk_heads > 0) return launch_gemm_qk(a, inline_route, grid, stream);
     if (swiglu)
         return pro ? launch_gemm_t<true, true>(a, inline_route, grid, stream)
                    : launch_gemm_t<true, false>(a, inline_route, grid, stream);
     return pro ? launch_gemm_t<false, true>(a, inline_route, grid, stream)
                : launch_gemm_t<false, false>(a, inline_route, grid, stream);
+}
+
+hipError_t launch_set_word(int32_t *dst, int32_t v, hipStream_t stream) {
+    hipLaunchKernelGGL(set_word_kernel, dim3(1), dim3(64), 0, stream, dst, v);
+    return hipGetLastError();
 }
 
 hipError_t launch_copy_word(const int32_t *src, int32_t *dst, hipStream_t stream) {
@@ -1900,7 +2091,7 @@ hipError_t launch_copy_word(const int32_t *src, int32_t *dst, hipStream_t stream
 }
 
 hipError_t launch_qk_norm_rope(const QkArgs &a, hipStream_t stream) {
-    hipLaunchKernelGGL(set_word_kernel, dim3(1), dim3(64), 0, stream, a.err, 0);
+    if (!a.after_gemm) hipLaunchKernelGGL(set_word_kernel, dim3(1), dim3(64), 0, stream, a.err, 0);
     const int64_t G = ((a.hq + a.hk + 3) / 4 + kQkChunks - 1) / kQkChunks;  // waves per row
     int64_t blocks = (a.T * G + 3) / 4;
     if (blocks > (1 << 20)) blocks = 1 << 20;  // the kernel strides over the rest
