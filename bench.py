@@ -212,29 +212,31 @@ def main():
     def small_packs(components):
         """Small, weight-bound packs (HBM roofline) at the QKV shape, weights
         rotated over eight copies of both sets (528 MB, twice the last-level
-        cache) so that they come from HBM."""
-        for Ts in (1, 64, 256):
-            ms = W.pattern(Ts)
-            xs_s = W.normal_bf16((Ts, K), 9).to(dev)
-            mds = torch.from_numpy(ms).to(dev)
-            copies = [(W.normal_bf16((N, K), 90 + i, 0.02).to(dev), W.normal_bf16((N, K), 190 + i, 0.02).to(dev))
-                      for i in range(8)]
-            ys = torch.empty((Ts, N), dtype=torch.bfloat16, device=dev)
-            wss = mot.new_workspace(Ts, dev)
-            ctr = [0]
+        cache) so that they come from HBM.  Two variants per size: the BAGEL
+        pattern's prefix (a prompt of 77 und rows, then latents) and a pack of
+        generation rows only."""
+        copies = [(W.normal_bf16((N, K), 90 + i, 0.02).to(dev), W.normal_bf16((N, K), 190 + i, 0.02).to(dev))
+                  for i in range(8)]
+        for Ts in (1, 8, 64, 77, 128, 256):
+            for variant in ("prefix", "gen"):
+                ms = W.pattern(Ts) if variant == "prefix" else np.ones(Ts, np.uint8)
+                xs_s = W.normal_bf16((Ts, K), 9).to(dev)
+                mds = torch.from_numpy(ms).to(dev)
+                ys = torch.empty((Ts, N), dtype=torch.bfloat16, device=dev)
+                wss = mot.new_workspace(Ts, dev)
+                ctr = [0]
 
-            def small():
-                a, b = copies[ctr[0] % 8]
-                ctr[0] += 1
-                mot.routed_gemm(xs_s, a, b, mds, out=ys, workspace=wss)
-            s_small = time_component(small, 40, stream)
-            sets = int((ms == 0).any()) + int((ms == 1).any())
-            nb = sets * N * K * 2 + Ts * K * 2 + Ts * N * 2 + Ts
-            components[f"qkv_small_T{Ts}"] = {"us": round(s_small * 1e6, 2),
-                                              "GB/s": round(nb / s_small / 1e9, 1),
-                                              "frac_hbm": round(nb / s_small / 1e9 / PEAK_HBM_GBS, 3),
-                                              "sets": sets}
-            del copies
+                def small():
+                    a, b = copies[ctr[0] % 8]
+                    ctr[0] += 1
+                    mot.routed_gemm(xs_s, a, b, mds, out=ys, workspace=wss)
+                s_small = time_component(small, 40, stream)
+                sets = int((ms == 0).any()) + int((ms == 1).any())
+                nb = sets * N * K * 2 + Ts * K * 2 + Ts * N * 2 + Ts
+                components[f"qkv_small_T{Ts}_{variant}"] = {
+                    "us": round(s_small * 1e6, 2), "GB/s": round(nb / s_small / 1e9, 1),
+                    "frac_hbm": round(nb / s_small / 1e9 / PEAK_HBM_GBS, 3), "sets": sets}
+        del copies
 
     def joint_attention(components, qkv_buf, iters):
         # shared joint attention over QKV rows (28 q / 4 kv heads, causal,
@@ -266,12 +268,25 @@ def main():
         xsd, rsd = xs.to(dev), rs.to(dev)
         yn = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
         rstd = torch.empty(T, dtype=torch.float32, device=dev)
-        s_norm = time_component(lambda: mot.fused_add_rmsnorm(xsd, rsd, nwu, nwg, md, out=yn, rstd=rstd),
-                                iters, stream)
+        # eight input copies rotated (x, residual, out: 8 x 3 x 29 MB, above
+        # the 256 MB last-level cache), so every byte comes from HBM
+        norm_sets = [(xsd.clone(), rsd.clone(), torch.empty_like(yn)) for _ in range(8)]
+        nctr = [0]
+
+        def norm_rot():
+            xa, ra, ya = norm_sets[nctr[0] % 8]
+            nctr[0] += 1
+            mot.fused_add_rmsnorm(xa, ra, nwu, nwg, md, out=ya, rstd=rstd)
+        s_norm = time_component(norm_rot, iters, stream)
+        s_norm_hot = time_component(lambda: mot.fused_add_rmsnorm(xsd, rsd, nwu, nwg, md, out=yn, rstd=rstd),
+                                    iters, stream)
+        del norm_sets
         nbytes = 4 * T * K * 2 + T * 4 + T
         components["fused_add_rmsnorm_T4096_H3584"] = {
             "us": round(s_norm * 1e6, 2), "GB/s": round(nbytes / s_norm / 1e9, 1),
-            "frac_hbm": round(nbytes / s_norm / 1e9 / PEAK_HBM_GBS, 3)}
+            "frac_hbm": round(nbytes / s_norm / 1e9 / PEAK_HBM_GBS, 3),
+            "us_same_inputs": round(s_norm_hot * 1e6, 2),
+            "note": "inputs rotated over eight copies (from HBM); us_same_inputs reuses one set (cache-served)"}
         # QKV with the routed-RMSNorm prologue (reads h + rstd instead of y)
         s_pro = time_component(lambda: mot.routed_gemm(rsd, wud, wgd, md, out=y, workspace=ws,
                                                        norm=(rstd, nwu, nwg)), iters, stream)
@@ -314,6 +329,21 @@ def main():
         nb_qk = 2 * T * qk_cols * 2 + T * (1 + 4 + 2 * 64 * 2)
         components["qk_norm_rope_T4096"] = {"us": round(s_qk * 1e6, 2), "GB/s": round(nb_qk / s_qk / 1e9, 1),
                                             "frac_hbm": round(nb_qk / s_qk / 1e9 / PEAK_HBM_GBS, 3)}
+        # the QKV GEMM with the QK norm + rotary in its epilogue, against the
+        # two calls (same bytes)
+        yq = torch.empty_like(y)
+        s_fused = time_component(lambda: mot.routed_gemm_qk_norm_rope(xd, wud, wgd, md, W.N_Q_HEADS, W.N_K_HEADS, qn,
+                                                                       kn, pos, cos_t, sin_t, out=yq, workspace=ws),
+                                 iters, stream)
+
+        def two_calls():
+            mot.routed_gemm(xd, wud, wgd, md, out=yq, workspace=ws)
+            mot.qk_norm_rope(yq, W.N_Q_HEADS, W.N_K_HEADS, md, qn, kn, pos, cos_t, sin_t, workspace=wsq)
+        s_two = time_component(two_calls, iters, stream)
+        components["qkv_qk_norm_rope_fused_T4096"] = {
+            "us": round(s_fused * 1e6, 2), "TFLOP/s": round(flops / s_fused / 1e12, 1),
+            "two_calls_us": round(s_two * 1e6, 2)}
+        del yq
         joint_attention(components, qkv_buf, iters)
         del qkv_buf
         # context only: the vendor library's dense GEMM of one weight set at
@@ -336,6 +366,27 @@ def main():
         components["gate_up_swiglu_T4096"] = {"us": round(s_gu * 1e6, 1),
                                               "TFLOP/s": round(f_gu / s_gu / 1e12, 1)}
         components["down_T4096"] = {"us": round(s_dn * 1e6, 1), "TFLOP/s": round(f_dn / s_dn / 1e12, 1)}
+        # one GPU's share under 4-way tensor parallelism (28 q / 4 kv heads:
+        # TP2 and TP4 are valid, TP8 is not): column-parallel QKV and gate/up
+        # (N / 4 of both sets), row-parallel O and down (K / 4); the partial
+        # sums' reduction across GPUs is not part of this measurement
+        tp = {}
+        for name, (Kt, Nt, sw) in {"qkv_tp4": (K, N // 4, False), "o_tp4": (W.Q_DIM // 4, K, False),
+                                   "gate_up_swiglu_tp4": (K, W.FFN // 4, True),
+                                   "down_tp4": (W.FFN // 4, K, False)}.items():
+            xt = W.normal_bf16((T, Kt), 31).to(dev)
+            rows_w = 2 * Nt if sw else Nt
+            wa = W.normal_bf16((rows_w, Kt), 32, 0.02).to(dev)
+            wb = W.normal_bf16((rows_w, Kt), 33, 0.02).to(dev)
+            yt = torch.empty((T, Nt), dtype=torch.bfloat16, device=dev)
+            fn = (lambda: mot.routed_gemm_swiglu(xt, wa, wb, md, out=yt, workspace=ws)) if sw else \
+                 (lambda: mot.routed_gemm(xt, wa, wb, md, out=yt, workspace=ws))
+            st = time_component(fn, 10, stream)
+            ft = 2.0 * T * Kt * rows_w
+            tp[name] = {"K": Kt, "N": Nt, "us": round(st * 1e6, 1), "TFLOP/s": round(ft / st / 1e12, 1),
+                        "frac_mfma": round(ft / st / 1e12 / PEAK_BF16_TFLOPS, 3)}
+            del xt, wa, wb, yt
+        components["tp4_shard_shapes_T4096"] = tp
         # per-layer chain: fused add-RMSNorm -> QKV -> QK norm + rotary ->
         # shared joint attention (causal within each request: the CFG pack's
         # seven, the 16384-row pack as one) -> O ->
@@ -363,9 +414,9 @@ def main():
             cos_c, sin_c, pos_c = (t.to(dev) for t in W.rope_inputs(Tc, 4096, base=5))
             ops = {
                 "norm1": lambda: mot.fused_add_rmsnorm(xc, res_c, nwu, nwg, mcd, out=y1, rstd=None),
-                "qkv": lambda: mot.routed_gemm(y1, wud, wgd, mcd, out=qkv_c, workspace=wsc),
-                "qk_norm_rope": lambda: mot.qk_norm_rope(qkv_c, W.N_Q_HEADS, W.N_K_HEADS, mcd, qn, kn, pos_c, cos_c,
-                                                         sin_c, workspace=wsc),
+                "qkv_qk_norm_rope": lambda: mot.routed_gemm_qk_norm_rope(y1, wud, wgd, mcd, W.N_Q_HEADS, W.N_K_HEADS,
+                                                                         qn, kn, pos_c, cos_c, sin_c, out=qkv_c,
+                                                                         workspace=wsc),
                 "attention": lambda: mot.joint_attention_varlen(
                     qkv_c[:, :W.Q_DIM], qkv_c[:, W.Q_DIM:W.Q_DIM + W.KV_DIM], qkv_c[:, W.Q_DIM + W.KV_DIM:], cu_c,
                     cu_c, max(lens), W.N_Q_HEADS, W.N_K_HEADS, causal=True, out=att_c, workspace=ws_att_c),
@@ -380,6 +431,22 @@ def main():
                     f()
             s_layer = time_component(layer, 2, stream)
             per_op = {k: round(time_component(f, 3, stream) * 1e6, 1) for k, f in ops.items()}
+            if name == "cfg_pack_T4096":
+                # the generation step's attention: each branch's 1024 latent
+                # rows query its 77 prompt rows and its latents without a mask
+                # (the prompt's keys and values come from the cache in a real
+                # step; here they are the pack's own rows)
+                def gen_step_attention():
+                    for b in range(3):
+                        r0 = 1101 * b
+                        mot.joint_attention(qkv_c[r0 + 77:r0 + 1101, :W.Q_DIM],
+                                            qkv_c[r0:r0 + 1101, W.Q_DIM:W.Q_DIM + W.KV_DIM],
+                                            qkv_c[r0:r0 + 1101, W.Q_DIM + W.KV_DIM:], W.N_Q_HEADS, W.N_K_HEADS,
+                                            causal=False, out=att_c[r0 + 77:r0 + 1101], workspace=ws_att_c)
+                s_gen = time_component(gen_step_attention, 3, stream)
+                f_gen = 3 * 4.0 * W.N_Q_HEADS * 128 * 1024 * 1101
+                per_op["attention_gen_step_3x1024_over_1101"] = round(s_gen * 1e6, 1)
+                per_op["attention_gen_step_TFLOP/s"] = round(f_gen / s_gen / 1e12, 1)
             f_layer = 2.0 * real * (K * N + W.Q_DIM * K + K * 2 * W.FFN + W.FFN * K)
             components[f"layer_chain_{name}"] = {"us": round(s_layer * 1e6, 1),
                                                  "TFLOP/s": round(f_layer / s_layer / 1e12, 1),

@@ -604,21 +604,36 @@ __device__ __forceinline__ uint32_t qk_chunk_off(int r, int c) {
     return (uint32_t)(r * kQkRowBytes + ((c ^ (r & 15)) << 4));
 }
 
-// Positions of the tile's rows into p_rows: -1 for a position outside the
-// table (which raises MOT_ERR_POSITION; the row keeps the GEMM's bytes), 0
-// for the slots past the tile's rows.
-__device__ __forceinline__ void qk_positions(const GemmArgs &a, const Tile &ti, const int32_t *s_rows,
+// Row r = threadIdx.x of the tile (one row per thread: tiles have at most
+// 256 rows): its output row and its position, loaded before the tile's main
+// loop so that their latency hides under it (two registers through the loop).
+struct QkRow {
+    int row;  // output row (0 for the slots past the tile's rows)
+    int pos;  // position
+};
+
+__device__ __forceinline__ QkRow qk_row_load(const GemmArgs &a, const Tile &ti, const int32_t *s_rows, int bm) {
+    QkRow q{0, 0};
+    const int i = (int)threadIdx.x;
+    if (i < bm) q.row = s_rows[i];
+    if (i < ti.count) q.pos = a.positions[q.row];
+    return q;
+}
+
+// After the main loop: the row list and the positions into LDS (p_rows: -1
+// for a position outside the table, which raises MOT_ERR_POSITION; the row
+// keeps the GEMM's bytes).
+__device__ __forceinline__ void qk_row_store(const GemmArgs &a, const Tile &ti, const QkRow &q, int32_t *s_rows,
                                              int32_t *p_rows, int bm) {
-    for (int i = (int)threadIdx.x; i < bm; i += kThreads) {
-        int p = 0;
-        if (i < ti.count) {
-            p = a.positions[s_rows[i]];
-            if (p < 0 || p >= a.n_pos) {
-                atomicMax(a.hdr_out, kErrPosition);
-                p = -1;
-            }
+    const int i = (int)threadIdx.x;
+    if (i < bm) {
+        int p = q.pos;
+        if (i < ti.count && (p < 0 || p >= a.n_pos)) {
+            atomicMax(a.hdr_out, kErrPosition);
+            p = -1;
         }
-        p_rows[i] = p;
+        s_rows[i] = q.row;
+        p_rows[i] = i < ti.count ? p : 0;
     }
 }
 
@@ -676,16 +691,32 @@ __device__ __forceinline__ void qk_head_rows(const GemmArgs &a, const Tile &ti, 
     if (qk) wv = *(const u32x4_t *)(w + 8 * gi);
     const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
     const uint32_t ldy_bytes = (uint32_t)a.ldy * 2u;
-    for (int r = wave * 4 + g; r < BM; r += 16) {
-        const uint8_t *st = (BM > 128 && r >= 128) ? st_hi : st_lo;
-        const u32x4_t v = *(const lds_u32x4 *)((const lds_u8 *)st + qk_chunk_off(r & 127, gi));
-        const u32x4_t cv = *(const lds_u32x4 *)((const lds_u8 *)cs + r * 128 + (gi & 7) * 16);
-        const u32x4_t sv = *(const lds_u32x4 *)((const lds_u8 *)sn + r * 128 + (gi & 7) * 16);
-        const u32x4_t o = qk_head(v, true, gi, a.qk_eps, wv, cv, sv);
-        if (r < ti.count && col0 + 8 * gi < a.N) {  // (a last head may end at a 64-column edge)
-            const u32x4_t out = (qk && p_rows[r] >= 0) ? o : v;
-            __builtin_amdgcn_raw_buffer_store_b128(out, yr, (uint32_t)s_rows[r] * ldy_bytes + (uint32_t)(col0 + 8 * gi) * 2u,
-                                                   0, 0);
+    const bool col_ok = col0 + 8 * gi < a.N;  // (a last head may end at a 64-column edge)
+    // four rows per group at a time (r, r + 16, r + 32, r + 48): their LDS
+    // reads are issued together and their arithmetic interleaves
+    constexpr int U = 4;
+    static_assert(BM % (16 * U) == 0, "rows per pass");
+    for (int r0 = wave * 4 + g; r0 < BM; r0 += 16 * U) {
+        u32x4_t v[U], cv[U], sv[U], o[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = r0 + 16 * u;
+            const uint8_t *st = (BM > 128 && r >= 128) ? st_hi : st_lo;
+            v[u] = *(const lds_u32x4 *)((const lds_u8 *)st + qk_chunk_off(r & 127, gi));
+            cv[u] = *(const lds_u32x4 *)((const lds_u8 *)cs + r * 128 + (gi & 7) * 16);
+            sv[u] = *(const lds_u32x4 *)((const lds_u8 *)sn + r * 128 + (gi & 7) * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) o[u] = qk_head(v[u], true, gi, a.qk_eps, wv, cv[u], sv[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = r0 + 16 * u;
+            if (r < ti.count && col_ok) {
+                const u32x4_t out = (qk && p_rows[r] >= 0) ? o[u] : v[u];
+                __builtin_amdgcn_raw_buffer_store_b128(out, yr,
+                                                       (uint32_t)s_rows[r] * ldy_bytes + (uint32_t)(col0 + 8 * gi) * 2u,
+                                                       0, 0);
+            }
         }
     }
 }
@@ -851,6 +882,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
     };
     auto issue_all = [&](int kt, int s) { issue(kt, s, 0, PER_STAGE); };
 
+    QkRow qkr{0, 0};
+    if constexpr (QK) {
+        if (ti.wrow0 < a.qk_heads * 128) qkr = qk_row_load(a, ti, s_rows, BM);
+    }
+
     float rs[MJ];
     if constexpr (PRO) {
 #pragma unroll
@@ -1011,7 +1047,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
         if (ti.wrow0 < a.qk_heads * 128) {
             // the tile is one head: staged in array 0, the rotary rows in
             // array 1 (cos, then sin)
-            qk_positions(a, ti, s_rows, qk_p, BM);
+            qk_row_store(a, ti, qkr, const_cast<int32_t *>(s_rows), qk_p, BM);
             __syncthreads();
             qk_tables<BM>(a, qk_p, xb[1], xb[1] + BM * 128, wave, lane);
             qk_stage<MI, MJ>(acc, xb[0], wm * WM, wn * WN, lane);
@@ -1042,10 +1078,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
 // it first.  The epilogue stores straight from the accumulators (8-byte
 // pieces, default cache policy); measured faster here than staging through
 // LDS, which would need the row list rebuilt.
-template <bool SWIGLU, bool F32 = false, bool QK = false, typename FillRows = int>
+template <bool SWIGLU, bool F32 = false, bool QK = false>
 __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint8_t *const (&hs)[5],
-                                         const int32_t *s_rows, const int tid, const FillRows &fill_rows = 0,
-                                         int32_t *qk_p = nullptr) {
+                                         const int32_t *s_rows, const int tid, int32_t *qk_p = nullptr) {
     static_assert(!(SWIGLU && F32), "fp32 output: plain GEMM only");
     static_assert(!QK || (!SWIGLU && !F32), "fused QK epilogue: plain bf16 GEMM only");
     constexpr uint32_t kOutBytes = F32 ? 4u : 2u;  // bytes per output element
@@ -1085,6 +1120,12 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
             wrow = min(ti.wrow0 + r, a.N - 1);
         }
         woff[j] = (uint32_t)wrow * (uint32_t)(K * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+    }
+    // the fused QK epilogue's row and position (the ring overwrites the
+    // row list during the main loop)
+    QkRow qkr{0, 0};
+    if constexpr (QK) {
+        if (ti.wrow0 < a.qk_heads * 128) qkr = qk_row_load(a, ti, s_rows, BM);
     }
     // byte offsets of this lane's four output rows (below 4 GiB), kNoRow
     // past the tile's rows (odd, so never a row's offset)
@@ -1224,9 +1265,7 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
             // 128-255); the rotary rows go to slots 2 (cos) and 3 (sin); the
             // row list, which the ring overwrote, is rebuilt in slot 4.
             __syncthreads();  // every wave is done with the ring
-            fill_rows();
-            __syncthreads();
-            qk_positions(a, ti, s_rows, qk_p, BM);
+            qk_row_store(a, ti, qkr, const_cast<int32_t *>(s_rows), qk_p, BM);
             __syncthreads();
             qk_tables<BM>(a, qk_p, hs[2], hs[3], wave, lane);
 #pragma unroll
@@ -1404,15 +1443,12 @@ gemm_kernel(GemmArgs a) {
         asm volatile("" : "+v"(tid));
         __syncthreads();  // every wave is done with the previous tile's LDS
         // the tile's rows into s_rows
-        auto fill_rows = [&]() {
-            if constexpr (INLINE) {
-                route_gather(rb, ti.set, ti.first - (ti.set ? U : 0), ti.count, bm, s_rows, s_red);
-            } else {
-                for (int i = threadIdx.x; i < bm; i += kThreads)
-                    s_rows[i] = i < ti.count ? min(max(a.perm[ti.first + i], 0), T - 1) : 0;
-            }
-        };
-        fill_rows();
+        if constexpr (INLINE) {
+            route_gather(rb, ti.set, ti.first - (ti.set ? U : 0), ti.count, bm, s_rows, s_red);
+        } else {
+            for (int i = threadIdx.x; i < bm; i += kThreads)
+                s_rows[i] = i < ti.count ? min(max(a.perm[ti.first + i], 0), T - 1) : 0;
+        }
         __syncthreads();
         if constexpr (INLINE) {
             // the tiles of weight rows [0, ...) cover every row once: they
@@ -1433,7 +1469,7 @@ gemm_kernel(GemmArgs a) {
                 run_tile<kBigM, kBigN, 2, SWIGLU, PRO>(a, ti, xb, wb, eb, s_rows, s_nw, tid);
             } else {
                 uint8_t *const hs[5] = {lds0, lds1, lds2, lds3, lds4};
-                run_big5<SWIGLU, F32, QK>(a, ti, hs, s_rows, tid, fill_rows, qk_p);
+                run_big5<SWIGLU, F32, QK>(a, ti, hs, s_rows, tid, qk_p);
             }
         } else if constexpr (!F32) {  // (mode 1 schedules no small tiles)
             constexpr int kHalf = kSmallM * kRowBytes;
