@@ -377,7 +377,14 @@ __device__ __forceinline__ Schedule make_schedule(int U, int G, int wrows, int g
         s.nbr = s.bu + G / kBigM + (G % kBigM >= kPartialBigRows ? 1 : 0);
     }
     const int nbig = s.nbr * s.nwt;
-    s.nkeep = (mode == 0 && nbig >= grid) ? (nbig / grid) * grid : nbig;
+    if (mode == 0 && 2 * nbig <= grid) {
+        // big tiles would leave at least half of the machine idle through a
+        // whole big-tile time: their quarters (at most two rounds of small
+        // tiles, each about a third of a big tile's time) finish sooner
+        s.nkeep = 0;
+    } else {
+        s.nkeep = (mode == 0 && nbig >= grid) ? (nbig / grid) * grid : nbig;
+    }
     s.nleft = nbig - s.nkeep;
     s.ru = min(s.bu * kBigM, U);
     s.rg = min((s.nbr - s.bu) * kBigM, G);
@@ -494,19 +501,44 @@ __device__ __forceinline__ int block_excl_scan(int v, int *s_red, int &total) {
 
 struct RouteBits {
     uint32_t bits[2];  // [set]: bit 16p + i <=> row p*kRoutePass + 16*tid + i is in the set
+    int base[2][2];    // [set][pass]: rank, among the set's rows, of this thread's first row of the pass
 };
 
 // Reads the pack's modality bytes once (all loads issued before any is
-// used); returns true if some byte is neither 0 nor 1.  U = und rows.
+// used); returns true if some byte is neither 0 nor 1.  U = und rows.  The
+// ranks of this thread's rows among each set's rows come from one pair of
+// workgroup scans here, so that a tile's rows need no scan later.
 __device__ bool route_count(const uint8_t *__restrict__ mod, int T, int *s_red, int &U, RouteBits &rb) {
     uint32_t v[kRoutePasses * kRouteRows];
+    if ((reinterpret_cast<uintptr_t>(mod) & 15u) == 0 && T >= kRouteRows) {
+        // 16 bytes per pass and thread in one load (the last full 16-byte
+        // piece of the pack for a thread past its end: masked below)
 #pragma unroll
-    for (int p = 0; p < kRoutePasses; ++p)
+        for (int p = 0; p < kRoutePasses; ++p) {
+            const int r0 = min(p * kRoutePass + (int)threadIdx.x * kRouteRows, (T & ~(kRouteRows - 1)) - kRouteRows);
+            const uint4 q = *(const uint4 *)(mod + r0);
+            const int sh = p * kRoutePass + (int)threadIdx.x * kRouteRows - r0;  // 0 unless clamped
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-        for (int i = 0; i < kRouteRows; ++i) {
-            const int r = p * kRoutePass + (int)threadIdx.x * kRouteRows + i;
-            v[p * kRouteRows + i] = mod[min(r, T - 1)];
+            for (int i = 0; i < kRouteRows; ++i) v[p * kRouteRows + i] = (w[i >> 2] >> (8 * (i & 3))) & 0xffu;
+            if (sh != 0) {
+                // rows past the last full piece: byte loads
+#pragma unroll
+                for (int i = 0; i < kRouteRows; ++i) {
+                    const int r = p * kRoutePass + (int)threadIdx.x * kRouteRows + i;
+                    v[p * kRouteRows + i] = mod[min(r, T - 1)];
+                }
+            }
         }
+    } else {
+#pragma unroll
+        for (int p = 0; p < kRoutePasses; ++p)
+#pragma unroll
+            for (int i = 0; i < kRouteRows; ++i) {
+                const int r = p * kRoutePass + (int)threadIdx.x * kRouteRows + i;
+                v[p * kRouteRows + i] = mod[min(r, T - 1)];
+            }
+    }
     uint32_t und = 0, gen = 0, bad = 0;
 #pragma unroll
     for (int p = 0; p < kRoutePasses; ++p)
@@ -522,26 +554,37 @@ __device__ bool route_count(const uint8_t *__restrict__ mod, int T, int *s_red, 
         }
     rb.bits[0] = und;
     rb.bits[1] = gen;
-    // und count (at most kInlineRouteMaxT < 2^20) and bad-byte flags in one
-    // scan; no other LDS is used (the GEMM's stage arrays fill the LDS)
-    int tot;
-    (void)block_excl_scan(__popc(und) | ((int)bad << 20), s_red, tot);
-    U = tot & 0xfffff;
-    return (tot >> 20) != 0;
+    // Per-pass counts of each set, two to a word (each total <= 4096 < 2^16:
+    // kInlineRouteMaxT = 2 passes of 4096 rows).  No other LDS is used (the
+    // GEMM's stage arrays fill the LDS).
+    const int cu = __popc(und & 0xffffu) | (__popc(und >> 16) << 16);
+    const int cg = __popc(gen & 0xffffu) | (__popc(gen >> 16) << 16);
+    int tu, tg;
+    const int eu = block_excl_scan(cu, s_red, tu);
+    const int eg = block_excl_scan(cg, s_red, tg);
+    const int tu0 = tu & 0xffff, tg0 = tg & 0xffff;
+    rb.base[0][0] = eu & 0xffff;
+    rb.base[0][1] = tu0 + (eu >> 16);
+    rb.base[1][0] = eg & 0xffff;
+    rb.base[1][1] = tg0 + (eg >> 16);
+    U = tu0 + (tu >> 16);
+    int tb;
+    (void)block_excl_scan((int)bad, s_red, tb);
+    return tb != 0;
 }
 
 // s_rows[i] = the row of rank f + i among the pack's rows of `set` (i < count),
-// row 0 for the slots past count.
+// row 0 for the slots past count.  No workgroup-wide step: each thread
+// writes its own rows whose rank falls in the tile's window.
 __device__ void route_gather(const RouteBits &rb, int set, int f, int count, int bm, int32_t *s_rows,
-                             int *s_red) {
+                             int * /*s_red*/) {
     for (int i = count + (int)threadIdx.x; i < bm; i += kThreads) s_rows[i] = 0;
     const uint32_t all = set ? rb.bits[1] : rb.bits[0];
-    int base_rank = 0;
 #pragma unroll
     for (int p = 0; p < kRoutePasses; ++p) {
         uint32_t mask = (all >> (16 * p)) & 0xffffu;
-        int tot;
-        int rank = base_rank + block_excl_scan(__popc(mask), s_red, tot);
+        int rank = set ? rb.base[1][p] : rb.base[0][p];
+        if (rank >= f + count || rank + __popc(mask) <= f) continue;
         const int r0 = p * kRoutePass + (int)threadIdx.x * kRouteRows;
         while (mask != 0 && rank < f + count) {
             const int i = __ffs(mask) - 1;
@@ -549,7 +592,6 @@ __device__ void route_gather(const RouteBits &rb, int set, int f, int count, int
             if (rank >= f) s_rows[rank - f] = r0 + i;
             ++rank;
         }
-        base_rank += tot;
     }
 }
 
