@@ -557,3 +557,24 @@ def test_prologue_with_the_norms_own_rstd():
     _, a = oracle.rmsnorm_apply(W.bits(h)[sel], rstd[sel], W.bits(nwu), W.bits(nwg), m[sel])
     ref, rne = oracle.routed_gemm(a, W.bits(wu), W.bits(wg), m[sel])
     check_parity(bits(y)[sel], ref, rne, "prologue with fp32 rstd", one_step=False)
+
+
+@pytest.mark.parametrize("T", [1, 8, 9, 16, 17])
+def test_small_packs_at_bagel_k(T):
+    """Packs of 1 to 17 rows at the BAGEL hidden size (K=3584, 56 k-blocks):
+    parity with the oracle and the tiled kernel's bytes, plain and SwiGLU."""
+    m = W.pattern(T)
+    m[::2] = 1 - m[::2]
+    x, wu, wg, _ = W.gemm_case(T, W.HIDDEN, 512, m, base=1800 + T)
+    _gemm_parity(x, wu, wg, m)
+    md = dev(torch.from_numpy(m))
+    small = mot.routed_gemm(dev(x), dev(wu), dev(wg), md)
+    tiled = mot.routed_gemm(dev(x), dev(wu), dev(wg), md, tile="128x128")
+    torch.cuda.synchronize()
+    assert torch.equal(small.view(torch.int16), tiled.view(torch.int16))
+    wgu_u = W.normal_bf16((1024, W.HIDDEN), 1810 + T, 0.02)
+    wgu_g = W.normal_bf16((1024, W.HIDDEN), 1820 + T, 0.02)
+    a1 = mot.routed_gemm_swiglu(dev(x), dev(wgu_u), dev(wgu_g), md)
+    a2 = mot.routed_gemm_swiglu(dev(x), dev(wgu_u), dev(wgu_g), md, tile="128x128")
+    torch.cuda.synchronize()
+    assert torch.equal(a1.view(torch.int16), a2.view(torch.int16))
