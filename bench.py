@@ -49,6 +49,8 @@ def parse():
                    help="of the components, run only the small packs (for their rocprofv3 profile)")
     p.add_argument("--only-attention", action="store_true",
                    help="of the components, run only the joint attention (for its rocprofv3 profile)")
+    p.add_argument("--only-latent", action="store_true",
+                   help="of the components, run only the latent step (for its rocprofv3 profile)")
     p.add_argument("--copy-probe", action="store_true",
                    help="run one 1 GiB device copy first (HBM counter calibration under rocprofv3)")
     p.add_argument("--cpu-rows", type=int, default=4096,
@@ -286,12 +288,46 @@ def main():
             "frac_mfma": round(f_att / s_att / 1e12 / PEAK_BF16_TFLOPS, 3),
             "note": "includes the V transpose into the workspace; flops of visible keys only"}
 
+    def latent_step(components):
+        """The per-step latent work of a batch of 16 rollouts of 1024 latent
+        rows x 64 fp32 channels (512x512 images): the three-branch CFG
+        combine with the per-request norm-ratio rescale, then the SDE step
+        sampling x_next with its log-probability, and the evaluation of a
+        given x_next.  HBM-bound, small: timed from HIP-graph replays."""
+        B, R, Cl = 16, 1024, 64
+        g = torch.Generator().manual_seed(77)
+        br = [torch.randn((B * R, Cl), generator=g).to(dev) for _ in range(6)]
+        vc, vt, vi, xl, nz, xn = br
+        cul = torch.arange(0, B * R + 1, R, dtype=torch.int32).to(dev)
+        tl = torch.full((B,), 0.6, dtype=torch.float32, device=dev)
+        tn = torch.full((B,), 0.55, dtype=torch.float32, device=dev)
+        vg = torch.empty_like(vc)
+        xo = torch.empty_like(vc)
+        lp = torch.empty(B, dtype=torch.float32, device=dev)
+        wsl = torch.empty(mot.latent_workspace_bytes(B, R), dtype=torch.uint8, device=dev)
+        cfg = lambda: mot.cfg_combine_renorm(vc, vt, vi, cul, R, tl, 4.0, 1.5, 0.0, 1.0, 0.0, "global", out=vg,
+                                             workspace=wsl)
+        sde = lambda: mot.flow_sde_step_logp(xl, vg, cul, R, tl, tn, 1.0, noise=nz, out=xo, logp=lp, workspace=wsl)
+        ev = lambda: mot.flow_sde_step_logp(xl, vg, cul, R, tl, tn, 1.0, x_next=xn, logp=lp, workspace=wsl)
+        ent = {}
+        for nm, fn, arrays in (("cfg_combine_renorm", cfg, 4), ("sde_step_sample_logp", sde, 4),
+                               ("sde_step_eval_logp", ev, 3)):
+            st = time_component_graph(fn, 16, stream)
+            nb = arrays * B * R * Cl * 4
+            ent[nm] = {"us": round(st * 1e6, 2), "GB/s": round(nb / st / 1e9, 1),
+                       "frac_hbm": round(nb / st / 1e9 / PEAK_HBM_GBS, 3)}
+        if mot.read_device_error(wsl) != 0:
+            raise RuntimeError("latent step raised its error word")
+        components["latent_step_16x1024x64_fp32"] = ent
+
     # ---- other hot-path steps ------------------------------------------------
     components = {}
     if args.only_small_packs:
         small_packs(components)
     elif args.only_attention:
         joint_attention(components, y.clone(), 30)
+    elif args.only_latent:
+        latent_step(components)
     elif not args.no_components:
         iters = 30
         # routed fused add-RMSNorm, T=4096, H=3584 (x, residual in; residual, y out)
@@ -468,13 +504,16 @@ def main():
                 # rows query its 77 prompt rows and its latents without a mask
                 # (the prompt's keys and values come from the cache in a real
                 # step; here they are the pack's own rows)
+                # One packed call over the three branches (their prompt
+                # rows ride along as queries: 7% more work, not counted)
+                cu_gen = torch.from_numpy(W.cu_lengths([1101, 1101, 1101])).to(dev)
+                ws_gen = torch.empty(mot.attention_varlen_workspace_bytes(3303, 3, W.N_K_HEADS), dtype=torch.uint8,
+                                     device=dev)
+
                 def gen_step_attention():
-                    for b in range(3):
-                        r0 = 1101 * b
-                        mot.joint_attention(qkv_c[r0 + 77:r0 + 1101, :W.Q_DIM],
-                                            qkv_c[r0:r0 + 1101, W.Q_DIM:W.Q_DIM + W.KV_DIM],
-                                            qkv_c[r0:r0 + 1101, W.Q_DIM + W.KV_DIM:], W.N_Q_HEADS, W.N_K_HEADS,
-                                            causal=False, out=att_c[r0 + 77:r0 + 1101], workspace=ws_att_c)
+                    mot.joint_attention_varlen(qkv_c[:3303, :W.Q_DIM], qkv_c[:3303, W.Q_DIM:W.Q_DIM + W.KV_DIM],
+                                               qkv_c[:3303, W.Q_DIM + W.KV_DIM:], cu_gen, cu_gen, 1101, W.N_Q_HEADS,
+                                               W.N_K_HEADS, causal=False, out=att_c[:3303], workspace=ws_gen)
                 s_gen = time_component(gen_step_attention, 3, stream)
                 f_gen = 3 * 4.0 * W.N_Q_HEADS * 128 * 1024 * 1101
                 per_op["attention_gen_step_3x1024_over_1101"] = round(s_gen * 1e6, 1)
@@ -485,6 +524,7 @@ def main():
                                                  "real_rows": real, "per_op_us": per_op}
             del act_c, att_c, ws_att_c
         del gu_u, gu_g, dn_u, dn_g
+        latent_step(components)
 
     # ---- CPU oracle baseline on a bounded row sample -------------------------
     cpu = None

@@ -165,6 +165,31 @@ def test_attention_varlen_cfg_pack_sampled():
         check_parity(gb[cq[b] + rows], ref, rne, f"attn varlen cfg branch {b}", one_step=False)
 
 
+def test_attention_varlen_gen_step_sampled():
+    """One denoising step of the three-branch pack: every row of a branch
+    sees all 1101 keys of its branch (no causal mask: the latent queries
+    attend to the prompt and to each other), sampled rows against the oracle,
+    and a branch's bytes equal its own single-sequence call."""
+    lq = [1101, 1101, 1101]
+    cq = _cu(lq)
+    T = int(cq[-1])
+    q, k, v = _inputs(T, T, W.N_Q_HEADS, W.N_K_HEADS, base=1040)
+    got, ws = mot.joint_attention_varlen(dev(q), dev(k), dev(v), dev(torch.from_numpy(cq)),
+                                         dev(torch.from_numpy(cq)), max(lq), W.N_Q_HEADS, W.N_K_HEADS, causal=False)
+    assert mot.read_device_error(ws) == 0
+    gb = bits(got)
+    for b in range(3):
+        rows = np.unique(np.r_[0, 76, 77, lq[b] - 1, np.random.default_rng(30 + b).integers(77, lq[b], 4)])
+        ref, rne = oracle.attention(W.bits(q)[cq[b]:cq[b + 1]], W.bits(k)[cq[b]:cq[b + 1]],
+                                    W.bits(v)[cq[b]:cq[b + 1]], W.N_Q_HEADS, W.N_K_HEADS, False, rows=rows)
+        check_parity(gb[cq[b] + rows], ref, rne, f"attn gen step branch {b}", one_step=False)
+    b = 1
+    alone = mot.joint_attention(dev(q[cq[b]:cq[b + 1]]), dev(k[cq[b]:cq[b + 1]]), dev(v[cq[b]:cq[b + 1]]),
+                                W.N_Q_HEADS, W.N_K_HEADS, causal=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(gb[cq[b]:cq[b + 1]], bits(alone))
+
+
 @pytest.mark.parametrize("bad", ["decreasing", "wrong_total", "too_long"])
 def test_attention_varlen_rejects_bad_lengths(bad):
     """Lengths that break the rules raise MOT_ERR_SEQLENS on the device and
