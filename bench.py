@@ -12,9 +12,15 @@ Beside it, on the same line:
   roofline      dominant kernel (the routed GEMM) against the bf16 MFMA peak,
                 its average duration from HIP events on the launch stream;
   cpu_baseline  the CPU oracle timed on a bounded row sample on this host;
-  components    the other hot-path steps: routed fused add-RMSNorm (GB/s),
-                the routed-RMSNorm prologue variant, the MLP gate/up+SwiGLU and
-                down projections, a small-pack HBM-bound case.
+  components    the other hot-path steps, each against its own roofline:
+                routed fused add-RMSNorm and the QK norm + rotary (GB/s), the
+                routed-RMSNorm prologue, small weight-bound packs, the
+                backward's dX and dW, the QKV GEMM with the QK norm + rotary
+                in its epilogue, shared joint attention, the MLP, one GPU's
+                share under 4-way tensor parallelism, a whole layer on the
+                CFG pack and on a 16384-row pack, and the latent step (CFG
+                combine, SDE step with its log-probability).  --only picks
+                some of them (one rocprofv3 run per kernel family).
 
 Inputs are synthetic and seeded (CPU generators, then copied to the GPU).
 """
@@ -45,12 +51,10 @@ def parse():
                    help="seconds of untimed launches before the warm-up (clock settling)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-components", action="store_true")
-    p.add_argument("--only-small-packs", action="store_true",
-                   help="of the components, run only the small packs (for their rocprofv3 profile)")
-    p.add_argument("--only-attention", action="store_true",
-                   help="of the components, run only the joint attention (for its rocprofv3 profile)")
-    p.add_argument("--only-latent", action="store_true",
-                   help="of the components, run only the latent step (for its rocprofv3 profile)")
+    p.add_argument("--only", default="",
+                   help="comma-separated components to run (for one rocprofv3 run per kernel family): norm, "
+                        "prologue, small_packs, backward, qk_norm_rope, qkv_qk_fused, attention, context_blas, "
+                        "mlp, tp4, layer_chain, latent")
     p.add_argument("--copy-probe", action="store_true",
                    help="run one 1 GiB device copy first (HBM counter calibration under rocprofv3)")
     p.add_argument("--cpu-rows", type=int, default=4096,
@@ -321,23 +325,22 @@ def main():
         components["latent_step_16x1024x64_fp32"] = ent
 
     # ---- other hot-path steps ------------------------------------------------
-    components = {}
-    if args.only_small_packs:
-        small_packs(components)
-    elif args.only_attention:
-        joint_attention(components, y.clone(), 30)
-    elif args.only_latent:
-        latent_step(components)
-    elif not args.no_components:
-        iters = 30
-        # routed fused add-RMSNorm, T=4096, H=3584 (x, residual in; residual, y out)
-        xs, rs = W.residual_inputs(T, K)
-        nwu, nwg = (t.to(dev) for t in W.norm_weights(K))
-        xsd, rsd = xs.to(dev), rs.to(dev)
+    # Each component is a function of the dict it fills; --only picks some
+    # (one rocprofv3 run per kernel family), --no-components none.
+    iters = 30
+    nwu, nwg = (t.to(dev) for t in W.norm_weights(K))
+    qn, kn = W.qk_norm_weights()
+    qn, kn = tuple(t.to(dev) for t in qn), tuple(t.to(dev) for t in kn)
+    cos_t, sin_t, pos = (t.to(dev) for t in W.rope_inputs(T, 4096))
+    xs, rs = W.residual_inputs(T, K)
+    xsd, rsd = xs.to(dev), rs.to(dev)
+
+    def c_norm(components):
+        # routed fused add-RMSNorm, T=4096, H=3584 (x, residual in; residual,
+        # y out); eight input copies rotated (x, residual, out: 8 x 3 x 29 MB,
+        # above the 256 MB last-level cache), so every byte comes from HBM
         yn = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
         rstd = torch.empty(T, dtype=torch.float32, device=dev)
-        # eight input copies rotated (x, residual, out: 8 x 3 x 29 MB, above
-        # the 256 MB last-level cache), so every byte comes from HBM
         norm_sets = [(xsd.clone(), rsd.clone(), torch.empty_like(yn)) for _ in range(8)]
         nctr = [0]
 
@@ -348,19 +351,25 @@ def main():
         s_norm = time_component(norm_rot, iters, stream)
         s_norm_hot = time_component(lambda: mot.fused_add_rmsnorm(xsd, rsd, nwu, nwg, md, out=yn, rstd=rstd),
                                     iters, stream)
-        del norm_sets
         nbytes = 4 * T * K * 2 + T * 4 + T
         components["fused_add_rmsnorm_T4096_H3584"] = {
             "us": round(s_norm * 1e6, 2), "GB/s": round(nbytes / s_norm / 1e9, 1),
             "frac_hbm": round(nbytes / s_norm / 1e9 / PEAK_HBM_GBS, 3),
             "us_same_inputs": round(s_norm_hot * 1e6, 2),
             "note": "inputs rotated over eight copies (from HBM); us_same_inputs reuses one set (cache-served)"}
+
+    def c_prologue(components):
         # QKV with the routed-RMSNorm prologue (reads h + rstd instead of y)
-        s_pro = time_component(lambda: mot.routed_gemm(rsd, wud, wgd, md, out=y, workspace=ws,
+        rstd = torch.empty(T, dtype=torch.float32, device=dev)
+        yn = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+        h = rsd.clone()
+        mot.fused_add_rmsnorm(xsd, h, nwu, nwg, md, out=yn, rstd=rstd)
+        s_pro = time_component(lambda: mot.routed_gemm(h, wud, wgd, md, out=y, workspace=ws,
                                                        norm=(rstd, nwu, nwg)), iters, stream)
         components["qkv_prologue_T4096"] = {"us": round(s_pro * 1e6, 2),
                                             "TFLOP/s": round(flops / s_pro / 1e12, 1)}
-        small_packs(components)
+
+    def c_backward(components):
         # routed backward of the QKV projection: dX = dY W_m on the
         # transposed weights (made once per weight update), and the generation
         # set's dW over its 3788 rows (two transposes + one routed GEMM over T)
@@ -380,15 +389,14 @@ def main():
             "dw_gen_fp32_us": round(s_dw32 * 1e6, 1), "dw_gen_fp32_TFLOP/s": round(f_dw / s_dw32 / 1e12, 1),
             "dw_gen_rows": n_gen_rows(m),
             "note": "dw_gen times include the two operand transposes (dY over all rows, X with und rows zeroed)"}
-        del wt, dyd, dx
+
+    wsq = mot.new_workspace(0, dev)
+
+    def c_qk_norm_rope(components):
         # routed per-head QK RMSNorm + rotary embedding, in place on the QKV
         # output (28 q + 4 k heads of 128; rotary tables as data, 4096
         # positions): HBM-bound, reads and writes the q and k columns
-        qn, kn = W.qk_norm_weights()
-        qn, kn = tuple(t.to(dev) for t in qn), tuple(t.to(dev) for t in kn)
-        cos_t, sin_t, pos = (t.to(dev) for t in W.rope_inputs(T, 4096))
         qkv_buf = y.clone()
-        wsq = mot.new_workspace(0, dev)
         s_qk = time_component(lambda: mot.qk_norm_rope(qkv_buf, W.N_Q_HEADS, W.N_K_HEADS, md, qn, kn, pos, cos_t,
                                                        sin_t, workspace=wsq), iters, stream)
         if mot.read_device_error(wsq) != 0:
@@ -397,6 +405,8 @@ def main():
         nb_qk = 2 * T * qk_cols * 2 + T * (1 + 4 + 2 * 64 * 2)
         components["qk_norm_rope_T4096"] = {"us": round(s_qk * 1e6, 2), "GB/s": round(nb_qk / s_qk / 1e9, 1),
                                             "frac_hbm": round(nb_qk / s_qk / 1e9 / PEAK_HBM_GBS, 3)}
+
+    def c_qkv_qk_fused(components):
         # the QKV GEMM with the QK norm + rotary in its epilogue, against the
         # two calls (same bytes)
         yq = torch.empty_like(y)
@@ -412,8 +422,11 @@ def main():
             "us": round(s_fused * 1e6, 2), "TFLOP/s": round(flops / s_fused / 1e12, 1),
             "two_calls_us": round(s_two * 1e6, 2)}
         del yq
-        joint_attention(components, qkv_buf, iters)
-        del qkv_buf
+
+    def c_attention(components):
+        joint_attention(components, y.clone(), iters)
+
+    def c_context_blas(components):
         # context only: the vendor library's dense GEMM of one weight set at
         # the same shape (hipBLASLt via torch.matmul; not batch-invariant,
         # not a target)
@@ -422,8 +435,17 @@ def main():
         components["context_dense_one_set_torch_matmul_T4096"] = {
             "us": round(s_blas * 1e6, 1), "TFLOP/s": round(flops / s_blas / 1e12, 1),
             "note": "hipBLASLt dense x @ W_gen^T, one set, for context; not batch-invariant"}
+
+    mlp_w = []
+
+    def mlp_dev():
+        if not mlp_w:
+            mlp_w.extend(t.to(dev) for t in W.mlp_weights())
+        return mlp_w
+
+    def c_mlp(components):
         # MLP: gate/up+SwiGLU 3584 -> 2x18944, down 18944 -> 3584
-        gu_u, gu_g, dn_u, dn_g = (t.to(dev) for t in W.mlp_weights())
+        gu_u, gu_g, dn_u, dn_g = mlp_dev()
         act = torch.empty((T, W.FFN), dtype=torch.bfloat16, device=dev)
         yd = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
         s_gu = time_component(lambda: mot.routed_gemm_swiglu(xd, gu_u, gu_g, md, out=act, workspace=ws),
@@ -434,6 +456,8 @@ def main():
         components["gate_up_swiglu_T4096"] = {"us": round(s_gu * 1e6, 1),
                                               "TFLOP/s": round(f_gu / s_gu / 1e12, 1)}
         components["down_T4096"] = {"us": round(s_dn * 1e6, 1), "TFLOP/s": round(f_dn / s_dn / 1e12, 1)}
+
+    def c_tp4(components):
         # one GPU's share under 4-way tensor parallelism (28 q / 4 kv heads:
         # TP2 and TP4 are valid, TP8 is not): column-parallel QKV and gate/up
         # (N / 4 of both sets), row-parallel O and down (K / 4); the partial
@@ -455,6 +479,9 @@ def main():
                         "frac_mfma": round(ft / st / 1e12 / PEAK_BF16_TFLOPS, 3)}
             del xt, wa, wb, yt
         components["tp4_shard_shapes_T4096"] = tp
+
+    def c_layer_chain(components):
+        gu_u, gu_g, dn_u, dn_g = mlp_dev()
         # per-layer chain: fused add-RMSNorm -> QKV -> QK norm + rotary ->
         # shared joint attention (causal within each request: the CFG pack's
         # seven, the 16384-row pack as one) -> O ->
@@ -523,8 +550,26 @@ def main():
                                                  "TFLOP/s": round(f_layer / s_layer / 1e12, 1),
                                                  "real_rows": real, "per_op_us": per_op}
             del act_c, att_c, ws_att_c
-        del gu_u, gu_g, dn_u, dn_g
-        latent_step(components)
+
+    registry = {"norm": c_norm, "prologue": c_prologue, "small_packs": small_packs, "backward": c_backward,
+                "qk_norm_rope": c_qk_norm_rope, "qkv_qk_fused": c_qkv_qk_fused, "attention": c_attention,
+                "context_blas": c_context_blas, "mlp": c_mlp, "tp4": c_tp4, "layer_chain": c_layer_chain,
+                "latent": latent_step}
+    if args.no_components:
+        chosen = []
+    elif args.only:
+        chosen = args.only.split(",")
+        unknown = [c for c in chosen if c not in registry]
+        if unknown:
+            raise SystemExit(f"unknown component(s) {unknown}; known: {sorted(registry)}")
+    else:
+        chosen = list(registry)
+    components = {}
+    for cname in chosen:
+        registry[cname](components)
+        torch.cuda.synchronize()
+        print(f"[bench] component {cname} done", file=sys.stderr, flush=True)
+    mlp_w.clear()
 
     # ---- CPU oracle baseline on a bounded row sample -------------------------
     cpu = None
