@@ -3,15 +3,16 @@
  * token-routed projection.
  *
  * The method: BAGEL-7B-MoT's Qwen2.5-7B-shaped decoder holds two full weight
- * sets, "understanding" (und) and "generation" (gen), that share attention;
- * every GEMM and every norm picks the weight set of each packed token row by a
- * fixed per-row index set, not by a learned router, and a row's output bytes
- * must not depend on the modality mix of the pack (RL-Kernel RFC page
- * "[RFC][BAGEL-7B-MoT][CUDA/ROCm] WS1/WS2 kernel roadmap and integration plan",
- * section 1, item 1).  The numerical contract of the same page (section 3)
- * applies to every call: fixed fp32 accumulator and fixed reduction order, no
- * Split-K / Stream-K / atomics, no fast math, casts only at declared
- * boundaries, fail closed on unsupported geometry.  The operations are the
+ * sets, "understanding" (und) and "generation" (gen), that share attention.
+ * In every GEMM and norm each packed token row is routed to one set by a
+ * per-row modality index (there is no learned router), and an output row's
+ * bytes may not change with the other rows packed beside it (RL-Kernel RFC
+ * page "[RFC][BAGEL-7B-MoT][CUDA/ROCm] WS1/WS2 kernel roadmap and integration
+ * plan", section 1, item 1).  Every call keeps that page's numerical rules
+ * (section 3): one fp32 accumulation order per output element, no reduction
+ * split across workgroups and no atomics, no fast math, rounding only where
+ * the interface declares it, and an error status instead of a guess for a
+ * shape it does not support.  The operations are the
  * page's "mot_routed_gemm", "mot_swiglu_mlp" (its gate/up + SwiGLU half),
  * "mot_fused_add_rmsnorm" and "mot_qk_norm_rope" work items (section 5), the
  * routed GEMM's fp32 sums uncast (mot_routed_gemm_f32, for fp32 gradients), the
@@ -268,8 +269,9 @@ int mot_routed_gemm_swiglu(const uint16_t *x, int64_t ldx,
  *          and sqrt, one fixed reduction tree per row that does not depend on T
  *   out[t][k] = bf16_rne((h_k * rstd) * w_m[k])   fp32, one cast
  *   rstd_out[t] = rstd
- * (RMSNorm convention of the RL-Kernel MoE route/combine PR page: fp32
- * weight multiply, single trailing cast, row reduction fixed for a fixed H.)
+ * (RMSNorm convention of the RL-Kernel MoE route/combine PR page: the weight
+ * is applied in fp32, the result is rounded once, and a row's reduction order
+ * depends on H alone.)
  *   x, residual, out: [T][H] bf16, contiguous; out may be NULL (prologue mode:
  *   the routed GEMMs then read h and rstd); rstd_out [T] fp32 or NULL; at least
  *   one of out / rstd_out non-NULL.  w_und, w_gen [H] bf16.
@@ -417,14 +419,15 @@ int mot_joint_attention_varlen(const uint16_t *q, int64_t ldq, const uint16_t *k
 /* ---- latent step: renormalised CFG and the flow SDE step (since ABI 10) ----
  *
  * The "cfg_combine_renorm" and "flow_sde_step_logp" work items of the RFC
- * page (section 5).  The page fixes their contract, not their formulas (its
- * section 1, item 3, and section 3, "BAGEL-specific rules"): up to three CFG
- * branches, two scales, a timestep window compared on fp32 t, a norm-ratio
- * rescale with a minimum, renormalised per request (never over the packed
- * batch); the SDE step and its log-probability in fp32, with sigma = t
- * (x_t = (1 - t) x_0 + t noise) and dt = t_i - t_{i+1} > 0, the
- * log-probability summed over the request's latent elements in a fixed
- * order.  The formulas below are this library's readings of that contract.
+ * page (section 5).  The page gives the rules they keep, not their formulas
+ * (section 1, item 3; section 3, its rules for BAGEL): the combine takes up to
+ * three branches and two guidance scales, guides only inside a window of t
+ * tested in fp32, and rescales by a clamped ratio of norms taken for each
+ * request on its own, never across the pack; the step and its
+ * log-probability are fp32, sigma equals t (the path x_t = (1 - t) x_0 +
+ * t noise), the step goes down from t_i to t_{i+1} (a positive dt), and the
+ * log-probability adds up the request's latent elements in an order fixed in
+ * advance.  The formulas below are this library's readings of those rules.
  *
  * Layout: fp32 [rows][C] arrays, C % 4 == 0, C <= 4096, packed by request:
  * request b owns rows [cu_rows[b], cu_rows[b+1]) (cu_rows: int32 device

@@ -2,12 +2,13 @@
 // the flow SDE step with its log-probability, the "cfg_combine_renorm" and
 // "flow_sde_step_logp" work items of the RL-Kernel RFC page "[RFC][BAGEL-
 // 7B-MoT][CUDA/ROCm] WS1/WS2 kernel roadmap and integration plan" (section
-// 5).  The page fixes their contract (section 1, item 3; section 3,
-// "BAGEL-specific rules"): up to three branches, two scales, a timestep
-// window compared on fp32 t, a norm-ratio rescale with a minimum, taken per
-// request; the step and its log-probability in fp32 with sigma = t and
-// dt = t_i - t_{i+1} > 0, the log-probability summed over the request's
-// latent elements in a fixed order.  The formulas are the library's readings
+// 5).  The page gives their rules, not their formulas (section 1, item 3;
+// section 3, its rules for BAGEL): at most three branches and two guidance
+// scales, guidance only inside a window of t tested in fp32, a clamped
+// rescale by a ratio of norms taken for each request alone; the step and its
+// log-probability in fp32, sigma equal to t, a step down in t (positive dt),
+// and the log-probability added up over the request's latent elements in an
+// order fixed in advance.  The formulas are the library's readings
 // of that contract (mot.h states them); the SDE is the Euler-Maruyama step of
 // rectified flow's reverse SDE as published with Flow-GRPO.
 //

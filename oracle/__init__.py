@@ -331,12 +331,12 @@ def attention_varlen(q, k, v, cu_q, cu_k, hq, hkv, causal, head_dim=128, threads
 # ---- latent step: three-branch renormalised CFG, and the flow SDE step -------
 #
 # The RL-Kernel RFC page lists both as work items ("cfg_combine_renorm" and
-# "flow_sde_step_logp", section 5) and fixes their contract, not their
-# formulas: up to three branches, two scales, a timestep window and a
-# norm-ratio rescale with a minimum, renormalised per request (section 1,
-# item 3; section 3, "BAGEL-specific rules"); the SDE step and its log
-# probability in fp32 with sigma = t and dt = t_i - t_{i+1} > 0, the
-# log-probability summed over all latent elements of a request (section 3).
+# "flow_sde_step_logp", section 5) and gives their rules, not their formulas
+# (section 1, item 3; section 3, its rules for BAGEL): at most three branches
+# and two guidance scales, guidance only inside a window of t, a rescale by a
+# clamped ratio of norms taken for each request alone; the step and its
+# log-probability in fp32, sigma equal to t, a step down in t (positive dt),
+# and the log-probability added up over every latent element of a request.
 # The formulas below are this project's readings of that contract; the SDE is
 # the Euler-Maruyama step of the rectified flow's reverse SDE published with
 # Flow-GRPO (arXiv 2505.05470, cited on the RFC page).  Plain fp64 per request.

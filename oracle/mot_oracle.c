@@ -10,8 +10,8 @@
  *
  *  - Routing.  The RL-Kernel RFC page "[RFC][BAGEL-7B-MoT][CUDA/ROCm] WS1/WS2
  *    kernel roadmap and integration plan", section 1 (Motivation, item 1):
- *    one decoder holds two weight sets; every GEMM and norm picks its weight
- *    set per token by a fixed index set, with no learned router.  Here the
+ *    one decoder holds two weight sets, and in each GEMM and norm a token
+ *    row's set is given by a per-row index, not a learned router.  Here the
  *    index set is a byte per row: 0 = understanding set, 1 = generation set.
  *  - Routed GEMM (the "mot_routed_gemm" work item, same page, section 5):
  *    out[t,n] = bf16_rne( sum_k x[t,k] * W_{m(t)}[n,k] ), W stored [N,K].

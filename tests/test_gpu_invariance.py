@@ -1,9 +1,9 @@
 """Bitwise batch invariance on the GPU (raw-bit identity, +0/-0 distinct).
 
-The pages require that a row's bytes not depend on the modality mix of the
-pack (RL-Kernel RFC page "[RFC][BAGEL-7B-MoT] WS1/WS2 kernel roadmap",
-section 1), and that both weight sets and the modality-mix test are present
-before a routed row is claimed (section 6).  The sweep follows the
+An output row's bytes may not change with the other rows packed beside it
+(RL-Kernel RFC page "[RFC][BAGEL-7B-MoT] WS1/WS2 kernel roadmap", section 1),
+and a routed row counts only with both weight sets exercised and a test of
+mixed-modality packs (section 6).  The sweep follows the
 batch-invariance workload: a fixed 1024-row probe block (77 und then 947 gen
 rows, so both sets are probed) repacked with 0, 1, 512 and 3072 other rows at
 gen fractions 0%, one token, 50% and 100%, each pack row-permuted with three

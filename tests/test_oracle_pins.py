@@ -4,8 +4,9 @@ Every check here is independent of the oracle's own code: exact integer /
 rational arithmetic written in this file, library routines (torch fp64
 matmul, torch silu), closed forms, brute force on tiny shapes, and structural
 invariants of the routing definition (RL-Kernel RFC page "[RFC][BAGEL-7B-MoT]
-WS1/WS2 kernel roadmap", section 1: a row picks its weight set by a fixed
-index set, and a row's bytes must not depend on the modality mix of the pack).
+WS1/WS2 kernel roadmap", section 1: a per-row index, not a router, gives each
+row its weight set, and an output row's bytes may not change with the other
+rows of the pack).
 
 The mutation tests at the end plant typical mistakes (swapped weight sets, a
 dropped k term, a transposed operand, a wrong SiLU sign, a norm without the

@@ -7,9 +7,9 @@ draws only -- none of the method's arithmetic lives here.
 Modality follows the BAGEL Mixture-of-Transformers description on the
 RL-Kernel RFC page ("[RFC][BAGEL-7B-MoT] WS1/WS2 kernel roadmap", section 1):
 text and ViT rows use the understanding weight set (modality 0), VAE-latent
-rows use the generation set (modality 1).  Random draws use one explicit CPU
-generator per tensor, following the same page's numerical contract (section 3,
-explicit per-sample generator with fixed device, dtype and consumption order).
+rows use the generation set (modality 1).  Random draws use one seeded CPU
+generator per tensor, with the device, dtype and order of the draws fixed, as
+the same page's numerical rules ask of the sampling noise (section 3).
 """
 from __future__ import annotations
 
