@@ -18,7 +18,7 @@ constexpr int64_t kInlineRouteMaxT = 8192;
 
 // Packs of at most this many rows (without the norm prologue, with the
 // library's own tile choice) take the weight-bound small-pack kernel.
-constexpr int64_t kSkinnyMaxT = 64;
+constexpr int64_t kSkinnyMaxT = 128;
 
 // Arguments of one routed GEMM launch.  Sizes are validated by the caller.
 struct GemmArgs {

@@ -8,7 +8,7 @@
 //                     LDS ring, 128x128 tiles for the rest); in-kernel
 //                     segment list; optional routed-RMSNorm prologue on the A
 //                     operand; optional SwiGLU epilogue (gate/up pairs).
-//  * skinny_kernel -- the same GEMM for packs of at most 64 rows, spread
+//  * skinny_kernel -- the same GEMM for packs of at most 128 rows, spread
 //                     over one workgroup per 32 output columns, all four
 //                     waves streaming weights (weight-bound).
 //  * norm_kernel   -- routed fused add-RMSNorm.
@@ -1639,10 +1639,15 @@ norm_kernel(const uint16_t *__restrict__ x, uint16_t *__restrict__ residual,
 // so that the LDS latency hides under the MFMAs.  The chain is the one of the
 // big and small tiles (v_mfma_f32_32x32x16_bf16, D[n][m] = sum_k W[n][k]
 // A[m][k], k ascending), so every output element gets the same bytes; its
-// K/16 dependent MFMAs, not the weight loads, set the kernel's time.  Only
-// the pack's A rows are loaded (XG groups of 8); a fragment of an unloaded row
-// reads other bytes of the same slot, which only reach output rows that are
-// never stored.
+// K/16 dependent MFMAs (44 cycles each when dependent, measured), not the
+// weight loads, set the kernel's time.  Only the pack's A row groups are
+// loaded (XG groups of 8: 1 to 16, so up to four compute waves); a fragment
+// of an unloaded row reads other bytes of the same slot, which only reach
+// output rows that are never stored.  With XG of 12 or 16 a workgroup's ring
+// fills most of the LDS, so a pack holding both sets (twice as many
+// workgroups as weight blocks) runs its extra workgroups in a second wave
+// of the grid; packs of one set, the usual case (a prompt, a decode batch),
+// use one workgroup per CU.
 
 constexpr int kSkThreads = 256;
 constexpr int kSkLdsBytes = 152 * 1024;  // ring budget
@@ -1657,7 +1662,7 @@ constexpr int kSkMaxStages = 6;
 template <int MI, int XG, int KSUB_>
 struct SkinnyCfg {
     static constexpr int KSUB = KSUB_;                          // 64-wide k-blocks per stage
-    static constexpr int JMAX = XG > 4 ? 2 : 1;                 // row blocks of 32
+    static constexpr int JMAX = XG >= 8 ? XG / 4 : 1;           // row blocks of 32
     static constexpr int AB = XG * 8 * kRowBytes;               // A rows' bytes of a k-block
     static constexpr int SUB = AB + MI * 32 * kRowBytes;        // + the weight rows
     static constexpr int SLOT = KSUB * SUB;
@@ -1702,7 +1707,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs &a, int set, int blk,
 #pragma unroll
     for (int g = 0; g < XW; ++g) {
         const int r = (wave + 4 * g) * 8 + (lane >> 3);
-        xoff[g] = (uint32_t)s_rows[r < 64 ? r : 0] * (uint32_t)(a.ldx * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+        xoff[g] = (uint32_t)s_rows[r] * (uint32_t)(a.ldx * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
     }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -1739,7 +1744,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs &a, int set, int blk,
         }
     };
 
-    const int mj = count > 32 ? 2 : 1;
+    const int mj = (count + 31) / 32;
     const bool computes = wave < mj;
     f32x16_t acc[MI];
 #pragma unroll
@@ -1748,7 +1753,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs &a, int set, int blk,
         for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
     const int rsel = lane & 31, khalf = lane >> 5;
     const int lsw = swz(lane & 15);
-    const int arow = (wave & 1) * 32 + rsel;  // this wave's token row of the slot (compute waves)
+    const int arow = wave * 32 + rsel;  // this wave's token row of the slot (compute waves)
 
     // Fragments are read one stage ahead, so that the LDS latency hides
     // under the MFMAs: iteration kt waits for stage kt+1, passes the barrier
@@ -1850,20 +1855,35 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs &a, int set, int blk,
 // pack's segment list itself (every wave from the same ballots: lane l owns
 // row l); workgroup 0 publishes it (and the error word) to the workspace
 // unless the caller passed a ready plan.
+// nblk: output column blocks of 32 (N / 32, or F / 32 for SwiGLU); XG: A row
+// groups of 8 staged per k-block (at least the pack's rows / 8); KS: k-blocks
+// of 64 per stage (dividing K / 64).  Builds the pack's segment list itself
+// (every wave from the same ballots: lane l owns rows l and, for packs of more
+// than 64 rows, l + 64); workgroup 0 publishes it (and the error word) to the
+// workspace unless the caller passed a ready plan.
 template <bool SWIGLU, int XG, int KS>
 __global__ void __launch_bounds__(kSkThreads)
 skinny_kernel(GemmArgs a, int nblk, int publish) {
     using C = SkinnyCfg<SWIGLU ? 2 : 1, XG, KS>;
-    __shared__ int32_t s_rows[64];
+    constexpr int RW = XG > 8 ? 2 : 1;  // rows per lane
+    __shared__ int32_t s_rows[64 * RW];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int T = (int)a.T;
     const int set = (int)blockIdx.x / nblk, blk = (int)blockIdx.x % nblk;
-    const uint32_t m = lane < T ? (uint32_t)a.modality[lane] : 0u;
-    const uint64_t valid = lane < T ? 1ull : 0ull;
-    const uint64_t bad = __ballot(valid && m > 1);
-    const uint64_t und = __ballot(valid && m == 0), gen = __ballot(valid && m == 1);
-    const int U = __popcll(und);
+    uint32_t m[RW];
+    uint64_t und[RW], gen[RW], bad = 0;
+    int U = 0;
+#pragma unroll
+    for (int h = 0; h < RW; ++h) {
+        const int r = lane + 64 * h;
+        m[h] = r < T ? (uint32_t)a.modality[r] : 0u;
+        bad |= __ballot(r < T && m[h] > 1);
+        und[h] = __ballot(r < T && m[h] == 0);
+        gen[h] = __ballot(r < T && m[h] == 1);
+        U += __popcll(und[h]);
+    }
+    const uint64_t below = (1ull << lane) - 1;
     if (publish && blockIdx.x == 0 && wave == 0) {
         if (lane == 0) {
             a.hdr_out[0] = bad ? kErrModality : 0;
@@ -1871,10 +1891,18 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
             a.hdr_out[2] = bad ? 0 : T - U;
             a.hdr_out[3] = T;
         }
-        if (!bad && lane < T) {
-            const uint64_t mine = m ? gen : und;
-            const int rank = __popcll(mine & ((1ull << lane) - 1));
-            a.perm_out[(m ? U : 0) + rank] = lane;
+        if (!bad) {
+            int base_u = 0, base_g = U;
+#pragma unroll
+            for (int h = 0; h < RW; ++h) {
+                const int r = lane + 64 * h;
+                if (r < T) {
+                    const uint64_t mine = m[h] ? gen[h] : und[h];
+                    a.perm_out[(m[h] ? base_g : base_u) + __popcll(mine & below)] = r;
+                }
+                base_u += __popcll(und[h]);
+                base_g += __popcll(gen[h]);
+            }
         }
     }
     if (bad) {
@@ -1883,12 +1911,25 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
         if (!publish && blockIdx.x == 0 && threadIdx.x == 0) a.hdr_out[0] = kErrModality;
         return;
     }
-    const uint64_t mine = set ? gen : und;
-    const int count = __popcll(mine);
+    int count = 0, first = -1;
+#pragma unroll
+    for (int h = 0; h < RW; ++h) {
+        const uint64_t mine = set ? gen[h] : und[h];
+        if (first < 0 && mine) first = 64 * h + __ffsll((unsigned long long)mine) - 1;
+        count += __popcll(mine);
+    }
     if (count == 0) return;  // all waves
     if (wave == 0) {
-        if (lane < T && ((mine >> lane) & 1ull)) s_rows[__popcll(mine & ((1ull << lane) - 1))] = lane;
-        if (lane >= count) s_rows[lane] = __ffsll((unsigned long long)mine) - 1;  // padding: a row of the set
+        int base = 0;
+#pragma unroll
+        for (int h = 0; h < RW; ++h) {
+            const uint64_t mine = set ? gen[h] : und[h];
+            if ((mine >> lane) & 1ull) s_rows[base + __popcll(mine & below)] = lane + 64 * h;
+            base += __popcll(mine);
+        }
+#pragma unroll
+        for (int h = 0; h < RW; ++h)
+            if (lane + 64 * h >= count) s_rows[lane + 64 * h] = first;  // padding: a row of the set
     }
     __syncthreads();
     uint8_t *sl[C::S];
@@ -2122,15 +2163,23 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
                 hipLaunchKernelGGL((skinny_kernel<true, 1, 1>), grid, block, 0, stream, a, nblk, pub);
             else if (a.T <= 32)
                 hipLaunchKernelGGL((skinny_kernel<true, 4, 1>), grid, block, 0, stream, a, nblk, pub);
-            else
+            else if (a.T <= 64)
                 hipLaunchKernelGGL((skinny_kernel<true, 8, 1>), grid, block, 0, stream, a, nblk, pub);
+            else if (a.T <= 96)
+                hipLaunchKernelGGL((skinny_kernel<true, 12, 1>), grid, block, 0, stream, a, nblk, pub);
+            else
+                hipLaunchKernelGGL((skinny_kernel<true, 16, 1>), grid, block, 0, stream, a, nblk, pub);
         } else {
             // packs of up to 8 rows measured faster with four A groups (all
             // four waves loading A) than with one
             if (a.T <= 32)
                 hipLaunchKernelGGL((skinny_kernel<false, 4, 1>), grid, block, 0, stream, a, nblk, pub);
-            else
+            else if (a.T <= 64)
                 hipLaunchKernelGGL((skinny_kernel<false, 8, 1>), grid, block, 0, stream, a, nblk, pub);
+            else if (a.T <= 96)
+                hipLaunchKernelGGL((skinny_kernel<false, 12, 1>), grid, block, 0, stream, a, nblk, pub);
+            else
+                hipLaunchKernelGGL((skinny_kernel<false, 16, 1>), grid, block, 0, stream, a, nblk, pub);
         }
         return hipGetLastError();
     }

@@ -133,7 +133,7 @@ def test_stale_ready_plan_fails_closed(T_plan, T):
 
 
 def test_small_pack_with_ready_plan_reports_bad_bytes():
-    """Packs of at most 64 rows rebuild their segment list from the bytes; an
+    """Packs of at most 128 rows rebuild their segment list from the bytes; an
     invalid byte still writes nothing and raises the error word when a ready
     plan was passed."""
     T, K, N = 40, 128, 128

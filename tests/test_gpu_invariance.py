@@ -102,10 +102,11 @@ def test_tile_shape_does_not_change_bytes(qkv_setup, tile):
     assert raw_equal(y, s["ref"])
 
 
-@pytest.mark.parametrize("T", [1, 7, 32, 33, 64, 65])
+@pytest.mark.parametrize("T", [1, 7, 32, 33, 64, 65, 96, 97, 128, 129])
 def test_small_packs_match_large_pack_bytes(qkv_setup, T):
-    """Packs of up to 64 rows run the weight-bound small-pack kernel (65 rows
-    the tiled kernel): each row's bytes equal those of the 1024-row pack."""
+    """Packs of up to 128 rows run the weight-bound small-pack kernel (8, 12
+    or 16 row groups; 129 rows the tiled kernel): each row's bytes equal
+    those of the 1024-row pack."""
     s = qkv_setup
     rows = np.random.default_rng(T).permutation(1024)[:T]
     y = mot.routed_gemm(dev(s["x_probe"][rows]), s["wu"], s["wg"],
@@ -186,7 +187,7 @@ def test_narrow_tiles_match_wide_tile_bytes(T, N):
 
 
 
-@pytest.mark.parametrize("T", [40, 200])
+@pytest.mark.parametrize("T", [40, 100, 200])
 def test_plan_ready_small_and_mid_packs(T):
     """A ready plan reused by the small-pack and the 128 x 64 tile paths
     gives the bytes of the in-kernel segment list."""
@@ -248,11 +249,11 @@ def test_mlp_probe_rows_bitwise_invariant(mlp_setup, op, n, frac):
 
 @pytest.mark.parametrize("op", ["swiglu", "down"])
 def test_mlp_small_packs_match_large_pack_bytes(mlp_setup, op):
-    """Packs of 1, 33 and 64 rows (the small-pack kernel) give each row the
-    bytes it has in the 1024-row pack, for the MLP shapes too."""
+    """Packs of 1, 33, 64, 100 and 128 rows (the small-pack kernel) give each
+    row the bytes it has in the 1024-row pack, for the MLP shapes too."""
     s = mlp_setup
     x_probe, _, run, ref = s[op]
-    for T in (1, 33, 64):
+    for T in (1, 33, 64, 100, 128):
         rows = np.random.default_rng(50 + T).permutation(1024)[:T]
         y = run(dev(x_probe[rows]), dev(torch.from_numpy(s["probe_m"][rows].copy())))
         assert raw_equal(y, ref[torch.from_numpy(rows).cuda()]), (op, T)

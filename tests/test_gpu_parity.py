@@ -57,12 +57,12 @@ def test_ragged_packs(T):
     _gemm_parity(x, wu, wg, m)
 
 
-@pytest.mark.parametrize("T", [1, 5, 8, 9, 32, 40, 64])
+@pytest.mark.parametrize("T", [1, 5, 8, 9, 32, 40, 64, 65, 96, 97, 128])
 @pytest.mark.parametrize("K", [64, 128, 192, 320, 448])
 def test_small_pack_stage_sizes(T, K):
-    """Packs of up to 64 rows run the small-pack kernel (A-row groups of 4 or
-    8): odd and even k-block counts, parity with the oracle and the bytes of
-    the tiled kernel (forced with a tile flag) for the same rows."""
+    """Packs of up to 128 rows run the small-pack kernel (A-row groups of 4,
+    8, 12 or 16): odd and even k-block counts, parity with the oracle and the
+    bytes of the tiled kernel (forced with a tile flag) for the same rows."""
     m = W.pattern(T)
     m[::3] = 1 - m[::3]
     x, wu, wg, _ = W.gemm_case(T, K, 192, m, base=600 + T + K)
@@ -213,12 +213,12 @@ def test_swiglu_small(T, K, F, tile):
     _swiglu_parity(x, wu, wg, m, tile=tile)
 
 
-@pytest.mark.parametrize("T", [1, 8, 20, 33, 64])
+@pytest.mark.parametrize("T", [1, 8, 20, 33, 64, 90, 128])
 @pytest.mark.parametrize("K", [192, 256])
 def test_swiglu_small_pack_kernel(T, K):
-    """SwiGLU packs of up to 64 rows (the small-pack kernel with 1, 4 or 8
-    A-row groups): parity with the oracle and the bytes of the tiled kernel
-    (forced with a tile flag)."""
+    """SwiGLU packs of up to 128 rows (the small-pack kernel with 1, 4, 8, 12
+    or 16 A-row groups): parity with the oracle and the bytes of the tiled
+    kernel (forced with a tile flag)."""
     F = 192
     m = W.pattern(T)
     m[::3] = 1 - m[::3]
@@ -510,7 +510,7 @@ def _prologue_case(T, K, base, exact_rstd=True):
 def test_prologue_against_oracle(T, K, N, rows):
     """The GEMM's routed-RMSNorm prologue, A = bf16((h * rstd) * w_set),
     against the oracle's norm application followed by its GEMM: the full QKV
-    shape on sampled rows, and packs of at most 64 rows (which take the tiled
+    shape on sampled rows, and packs of at most 128 rows (which take the tiled
     kernel when the prologue is on)."""
     m, h, nwu, nwg, rstd = _prologue_case(T, K, base=1700 + T)
     wu = W.normal_bf16((N, K), 1701, 0.02)
@@ -559,9 +559,9 @@ def test_prologue_with_the_norms_own_rstd():
     check_parity(bits(y)[sel], ref, rne, "prologue with fp32 rstd", one_step=False)
 
 
-@pytest.mark.parametrize("T", [1, 8, 9, 16, 17])
+@pytest.mark.parametrize("T", [1, 8, 9, 16, 17, 77, 100, 128])
 def test_small_packs_at_bagel_k(T):
-    """Packs of 1 to 17 rows at the BAGEL hidden size (K=3584, 56 k-blocks):
+    """Packs of 1 to 128 rows at the BAGEL hidden size (K=3584, 56 k-blocks):
     parity with the oracle and the tiled kernel's bytes, plain and SwiGLU."""
     m = W.pattern(T)
     m[::2] = 1 - m[::2]

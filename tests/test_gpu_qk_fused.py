@@ -50,9 +50,9 @@ def _fused(m, x, wu, wg, qn, kn, cos_t, sin_t, pos, hq, hk, tile=None, out=None)
     return y, mot.read_device_error(ws)
 
 
-@pytest.mark.parametrize("T", [1, 40, 64, 65, 200, 1101, 4096, 9001])
+@pytest.mark.parametrize("T", [1, 40, 64, 65, 128, 129, 200, 1101, 4096, 9001])
 def test_fused_equals_two_kernel_path(T):
-    """Packs of at most 64 rows (the small-pack GEMM, then the QK kernel),
+    """Packs of at most 128 rows (the small-pack GEMM, then the QK kernel),
     mid-size packs (128 x 128 tiles), 256 x 256 tiles with a partial round,
     and a pack above the in-kernel segment list's limit (plan kernel)."""
     args = _inputs(T, 512 if T != 4096 else W.HIDDEN, W.QKV_DIM, base=700 + T)
