@@ -554,23 +554,30 @@ __device__ bool route_count(const uint8_t *__restrict__ mod, int T, int *s_red, 
         }
     rb.bits[0] = und;
     rb.bits[1] = gen;
-    // Per-pass counts of each set, two to a word (each total <= 4096 < 2^16:
-    // kInlineRouteMaxT = 2 passes of 4096 rows).  No other LDS is used (the
-    // GEMM's stage arrays fill the LDS).
+    // Per-pass und counts, two to a word (each total <= 4096 < 2^16:
+    // kInlineRouteMaxT = 2 passes of 4096 rows), in one workgroup scan.  Each
+    // wave's "some byte is invalid" flag goes beside the scan's per-wave sums
+    // and is published by its first barrier.  A gen rank needs no scan of its
+    // own: when every byte is valid, the rows before a thread's first row of
+    // a pass are und or gen, so its gen rank is their number minus its und
+    // rank.  No other LDS is used (the GEMM's stage arrays fill the LDS).
     const int cu = __popc(und & 0xffffu) | (__popc(und >> 16) << 16);
-    const int cg = __popc(gen & 0xffffu) | (__popc(gen >> 16) << 16);
-    int tu, tg;
+    const int nw = kThreads / 64;
+    const bool wave_bad = __ballot(bad != 0) != 0;
+    if ((threadIdx.x & 63) == 0) s_red[nw + (threadIdx.x >> 6)] = wave_bad ? 1 : 0;
+    int tu;
     const int eu = block_excl_scan(cu, s_red, tu);
-    const int eg = block_excl_scan(cg, s_red, tg);
-    const int tu0 = tu & 0xffff, tg0 = tg & 0xffff;
+    const int tu0 = tu & 0xffff;
     rb.base[0][0] = eu & 0xffff;
     rb.base[0][1] = tu0 + (eu >> 16);
-    rb.base[1][0] = eg & 0xffff;
-    rb.base[1][1] = tg0 + (eg >> 16);
+#pragma unroll
+    for (int p = 0; p < kRoutePasses; ++p)
+        rb.base[1][p] = min(p * kRoutePass + (int)threadIdx.x * kRouteRows, T) - rb.base[0][p];
     U = tu0 + (tu >> 16);
-    int tb;
-    (void)block_excl_scan((int)bad, s_red, tb);
-    return tb != 0;
+    int any_bad = 0;
+#pragma unroll
+    for (int w = 0; w < nw; ++w) any_bad |= s_red[nw + w];
+    return any_bad != 0;
 }
 
 // s_rows[i] = the row of rank f + i among the pack's rows of `set` (i < count),
