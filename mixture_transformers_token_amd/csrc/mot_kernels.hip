@@ -318,6 +318,11 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
 constexpr int kBigM = 256, kBigN = 256, kSmallM = 128, kSmallN = 128;
+// Wide-round big tiles: 256 token rows x 224 weight rows (four waves of 64 x
+// 224), for plain GEMMs whose weight rows split into 224-row tiles that fill
+// whole rounds better than 256-row ones (O and down at N = 3584: 16 x 16 =
+// 256 tiles at T = 4096, one per CU, against 16 x 14 = 224).
+constexpr int kWideN = 224;
 constexpr int kNarrowN = 64;  // weight rows of the narrow tiles (mid-size packs)
 constexpr int kPartialBigRows = 160;  // rows from which a partial row block is a big tile
 
@@ -347,7 +352,8 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 // mode 1: big tiles only; mode 2: small tiles only.
 struct Schedule {
     int U, G;
-    int nwt, nws;  // weight tiles of 256 and of sn rows
+    int bn;        // big tiles' weight rows: kBigN, or kWideN
+    int nwt, nws;  // weight tiles of bn and of sn rows
     int sn;        // small tiles' weight rows: 128, or 64 (narrow mode)
     int bu, nbr;   // big row blocks: und, und + gen
     int nkeep;     // big tiles run as such
@@ -358,11 +364,12 @@ struct Schedule {
 };
 
 __device__ __forceinline__ Schedule make_schedule(int U, int G, int wrows, int grid, int mode,
-                                                   int sn = kSmallN) {
+                                                   int sn = kSmallN, bool allow_wide = false) {
     Schedule s;
     s.sn = sn;
     s.U = U;
     s.G = G;
+    s.bn = kBigN;
     s.nwt = cdiv(wrows, kBigN);
     s.nws = cdiv(wrows, sn);
     if (mode == 2) {
@@ -376,8 +383,25 @@ __device__ __forceinline__ Schedule make_schedule(int U, int G, int wrows, int g
         s.bu = U / kBigM + (U % kBigM >= kPartialBigRows ? 1 : 0);
         s.nbr = s.bu + G / kBigM + (G % kBigM >= kPartialBigRows ? 1 : 0);
     }
+    if (allow_wide && mode == 0 && wrows % kWideN == 0) {
+        // 224-row weight tiles when their rounds (a partial round counted
+        // whole) take less big-tile time than the 256-row tiles', they fill
+        // more than half of the grid, and the small tiles of the partial row
+        // blocks fit the idle workgroups of their last round (two each);
+        // wide tiles always run whole
+        const int nw = s.nbr * (wrows / kWideN), nn = s.nbr * s.nwt;
+        const int rw = cdiv(nw, grid);
+        const int ns = (cdiv(U - min(s.bu * kBigM, U), kSmallM) + cdiv(G - min((s.nbr - s.bu) * kBigM, G), kSmallM)) *
+                       cdiv(wrows, sn);
+        if (2 * nw > grid && rw * kWideN < cdiv(nn, grid) * kBigN && ns <= 2 * (rw * grid - nw)) {
+            s.bn = kWideN;
+            s.nwt = wrows / kWideN;
+        }
+    }
     const int nbig = s.nbr * s.nwt;
-    if (mode == 0 && 2 * nbig <= grid) {
+    if (s.bn == kWideN) {
+        s.nkeep = nbig;
+    } else if (mode == 0 && 2 * nbig <= grid) {
         // big tiles would leave at least half of the machine idle through a
         // whole big-tile time: their quarters (at most two rounds of small
         // tiles, each about a third of a big tile's time) finish sooner
@@ -427,7 +451,7 @@ __device__ __forceinline__ Tile tile_of(const Schedule &s, int t) {
         int mb, nb;
         big_tile(s, t, mb, nb);
         block_rows(s, mb, ti);
-        ti.wrow0 = nb * kBigN;
+        ti.wrow0 = nb * s.bn;
         ti.big = true;
         return ti;
     }
@@ -1127,23 +1151,27 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
 // it first.  The epilogue stores straight from the accumulators (8-byte
 // pieces, default cache policy); measured faster here than staging through
 // LDS, which would need the row list rebuilt.
-template <bool SWIGLU, bool F32 = false, bool QK = false>
+template <bool SWIGLU, bool F32 = false, bool QK = false, int BN = kBigN>
 __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint8_t *const (&hs)[5],
                                          const int32_t *s_rows, const int tid, int32_t *qk_p = nullptr) {
     static_assert(!(SWIGLU && F32), "fp32 output: plain GEMM only");
     static_assert(!QK || (!SWIGLU && !F32), "fused QK epilogue: plain bf16 GEMM only");
     constexpr uint32_t kOutBytes = F32 ? 4u : 2u;  // bytes per output element
-    constexpr int BM = kBigM, BN = kBigN;
-    constexpr int WM = BM / 2, WN = BN / 2;
+    static_assert(BN == kBigN || (BN == kWideN && !SWIGLU && !F32 && !QK), "wide tiles: plain bf16 GEMM only");
+    // 256 x 256: waves in a 2 x 2 grid of 128 x 128; 256 x 224: four waves
+    // of 64 token rows x all 224 weight rows
+    constexpr int BM = kBigM;
+    constexpr int WAVES_N = BN == kBigN ? 2 : 1;
+    constexpr int WM = BM / (4 / WAVES_N), WN = BN / WAVES_N;
     constexpr int MJ = WM / 32, MI = WN / 32;
     constexpr int NM = MI * MJ;
     constexpr int XL = BM / 32, WL = BN / 32;  // DMA instructions per wave per operand and stage
     constexpr int HX = XL / 2, HW = WL / 2;
-    static_assert(XL == 8 && WL == 8 && NM == 16, "big tile");
+    static_assert(XL == 8 && ((WL == 8 && NM == 16) || (WL == 7 && NM == 14)), "big tile");
 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = WAVES_N == 2 ? wave >> 1 : wave, wn = WAVES_N == 2 ? (wave & 1) : 0;
     const int K = a.K;
     const int nk = K / kBK;
 
@@ -1395,12 +1423,17 @@ __device__ __forceinline__ uint16_t *prologue_nw_lds() {
 // list and scan scratch; the prologue's big tiles run two stages of A in
 // array 0 or 2 and W in array 1 or 3, and its norm weights take 16 KiB).
 // Small tiles run four stages, one array each.
-template <bool SWIGLU, bool PRO, bool INLINE, bool NARROW = false, bool F32 = false, bool QK = false>
+// WIDE: the schedule may pick 256 x 224 big tiles (plain GEMMs whose weight
+// rows are a multiple of 224; a separate instantiation, so that the other
+// GEMMs keep their register allocation).
+template <bool SWIGLU, bool PRO, bool INLINE, bool NARROW = false, bool F32 = false, bool QK = false,
+          bool WIDE = false>
 __global__ void __launch_bounds__(kThreads, 1)
 gemm_kernel(GemmArgs a) {
     static_assert(!NARROW || (!SWIGLU && !PRO), "narrow tiles: plain GEMM only");
     static_assert(!F32 || (!SWIGLU && !PRO && !NARROW), "fp32 output: plain GEMM, big tiles only");
     static_assert(!QK || (!SWIGLU && !PRO && !NARROW && !F32), "fused QK epilogue: plain bf16 GEMM only");
+    static_assert(!WIDE || (!SWIGLU && !PRO && !NARROW && !F32 && !QK), "wide tiles: plain bf16 GEMM only");
     constexpr int kArrayBytes = kBigM * kRowBytes;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kArrayBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kArrayBytes];
@@ -1462,7 +1495,7 @@ gemm_kernel(GemmArgs a) {
     // fp32 output runs 256 x 256 tiles only (mode 1: every row block,
     // partial ones included, is a big tile; no small tiles)
     const Schedule sc = NARROW ? make_schedule(U, G, a.wrows, grid, 2, kNarrowN)
-                               : make_schedule(U, G, a.wrows, grid, F32 ? 1 : a.tile_mode);
+                               : make_schedule(U, G, a.wrows, grid, F32 ? 1 : a.tile_mode, kSmallN, WIDE);
     // Static assignment.  Big tiles go round-robin (whole rounds, or one
     // partial round); small tiles (about a quarter of a big tile's work each)
     // go first to the workgroups that hold no big tile, up to four each, then
@@ -1518,7 +1551,14 @@ gemm_kernel(GemmArgs a) {
                 run_tile<kBigM, kBigN, 2, SWIGLU, PRO>(a, ti, xb, wb, eb, s_rows, s_nw, tid);
             } else {
                 uint8_t *const hs[5] = {lds0, lds1, lds2, lds3, lds4};
-                run_big5<SWIGLU, F32, QK>(a, ti, hs, s_rows, tid, qk_p);
+                if constexpr (WIDE) {
+                    if (sc.bn == kWideN)
+                        run_big5<false, false, false, kWideN>(a, ti, hs, s_rows, tid, qk_p);
+                    else
+                        run_big5<false, false, false>(a, ti, hs, s_rows, tid, qk_p);
+                } else {
+                    run_big5<SWIGLU, F32, QK>(a, ti, hs, s_rows, tid, qk_p);
+                }
             }
         } else if constexpr (!F32) {  // (mode 1 schedules no small tiles)
             constexpr int kHalf = kSmallM * kRowBytes;
@@ -2129,6 +2169,17 @@ hipError_t launch_gemm_qk(const GemmArgs &a, bool inline_route, int grid, hipStr
 
 template <bool SWIGLU, bool PRO>
 hipError_t launch_gemm_t(const GemmArgs &a, bool inline_route, int grid, hipStream_t stream) {
+    if constexpr (!SWIGLU && !PRO) {
+        if (a.tile_mode == 0 && a.wrows % kWideN == 0) {
+            if (inline_route)
+                hipLaunchKernelGGL((gemm_kernel<false, false, true, false, false, false, true>), dim3(grid),
+                                   dim3(kThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL((gemm_kernel<false, false, false, false, false, false, true>), dim3(grid),
+                                   dim3(kThreads), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
     if (inline_route)
         hipLaunchKernelGGL((gemm_kernel<SWIGLU, PRO, true>), dim3(grid), dim3(kThreads), 0, stream, a);
     else

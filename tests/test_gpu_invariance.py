@@ -92,6 +92,30 @@ def test_repeatable_and_strided_output(qkv_setup):
     assert raw_equal(big[:, 32:32 + N].contiguous(), s["ref"])
 
 
+@pytest.mark.parametrize("n_und,n_gen,N", [(1024, 3072, 3584), (512, 2048, 3584), (1024, 3072, 448)])
+def test_wide_tiles_give_the_bytes_of_the_other_shapes(n_und, n_gen, N):
+    """Packs whose weight rows split into 224-row tiles that fill the rounds
+    better (O and down at N = 3584 on a pack of whole 256-row blocks: 256
+    tiles of 256 x 224 in one round, or a partial round of 160) run the wide
+    tiles; their bytes equal those of forced 256 x 256 and 128 x 128 tiles.
+    N = 448 is a shape the wide tiles do not take (too few tiles)."""
+    T = n_und + n_gen
+    m = np.concatenate([np.zeros(n_und, np.uint8), np.ones(n_gen, np.uint8)])
+    m = m[W.permutation(T, 5).numpy()].copy()
+    x = dev(W.normal_bf16((T, 512), 930))
+    wu = dev(W.normal_bf16((N, 512), 931, 0.02))
+    wg = dev(W.normal_bf16((N, 512), 932, 0.02))
+    md = dev(torch.from_numpy(m))
+    auto = mot.routed_gemm(x, wu, wg, md)
+    ws = mot.routing_plan(md)
+    ready = mot.routed_gemm(x, wu, wg, md, workspace=ws, plan_ready=True)
+    for tile in ("256x256", "128x128"):
+        forced = mot.routed_gemm(x, wu, wg, md, tile=tile)
+        torch.cuda.synchronize()
+        assert raw_equal(auto, forced), tile
+    assert raw_equal(auto, ready)
+
+
 @pytest.mark.parametrize("tile", ["256x256", "128x128"])
 def test_tile_shape_does_not_change_bytes(qkv_setup, tile):
     """Every tile shape runs the same per-element k order: forcing one shape

@@ -265,6 +265,17 @@ def test_down_full_k_per_op():
     _gemm_parity(a, dn_u, dn_g, m, rows=rows)
 
 
+def test_down_cfg_pack_wide_tiles():
+    """The down projection on the three-branch CFG pack (1024 und and 3072
+    gen rows, whole 256-row blocks), which runs 256 x 224 tiles in one round:
+    the single-op bar against the oracle on sampled rows."""
+    m = W.cfg_pack_modality()
+    a = W.normal_bf16((m.size, W.FFN), 1910)
+    _, _, dn_u, dn_g = W.mlp_weights()
+    rows = W.sample_rows(m, 24, seed=13)
+    _gemm_parity(a, dn_u, dn_g, m, rows=rows)
+
+
 def _layer_chain_gpu(x, r, m, wts, rope, lengths):
     """fused add-RMSNorm -> QKV -> QK norm + rotary -> shared joint attention
     (causal within each request of `lengths`) -> O -> fused add-RMSNorm ->
