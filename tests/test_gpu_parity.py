@@ -109,6 +109,22 @@ def test_qkv_full_size_sampled():
     _gemm_parity(x, wu, wg, m, rows=rows)
 
 
+def test_qkv_after_routed_rmsnorm_full_size():
+    """The QKV workload as configured: X is the routed RMSNorm of a seeded
+    residual stream (the oracle's norm of generator rows, so the GEMM's
+    input bytes are the same on both sides), T=4096, K=3584, N=4608, in the
+    benchmark's launch configuration; the single-op bar on sampled rows."""
+    T = 4096
+    m = W.pattern(T)
+    xr, r = W.residual_inputs(T, W.HIDDEN, base=77)
+    nwu, nwg = W.norm_weights(W.HIDDEN, base=77)
+    normed = oracle.fused_add_rmsnorm(W.bits(xr), W.bits(r), W.bits(nwu), W.bits(nwg), m)["out"]
+    x = W.from_bits(normed)
+    _, wu, wg, _ = W.qkv(T)
+    rows = W.sample_rows(m, 32, seed=3)
+    _gemm_parity(x, wu, wg, m, rows=rows)
+
+
 def _bf16_bits(sign, exp, mant):
     """bf16 bit patterns of (-1)^sign * (1 + mant/128) * 2^exp."""
     return ((sign.astype(np.uint16) << 15) | ((exp + 127).astype(np.uint16) << 7) |
