@@ -432,7 +432,8 @@ int mot_joint_attention_varlen(const uint16_t *q, int64_t ldq, const uint16_t *k
  * Layout: fp32 [rows][C] arrays, C % 4 == 0, C <= 4096, packed by request:
  * request b owns rows [cu_rows[b], cu_rows[b+1]) (cu_rows: int32 device
  * array of n_req + 1 entries, 0 = cu[0] <= ... <= cu[n_req] = rows, no
- * request longer than max_rows; checked on the device, and a violation
+ * request longer than max_rows >= 1, n_req >= 1; empty requests are allowed,
+ * and their log-probability is 0; checked on the device, and a violation
  * writes nothing and raises MOT_ERR_SEQLENS).  Work goes in chunks of 64 rows
  * of one request; request-wide sums add the chunks' fp32 sums in ascending
  * order, so a request's results do not depend on the other requests of the

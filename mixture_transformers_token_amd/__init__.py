@@ -171,7 +171,10 @@ def _rows(t, name):
 
 
 def new_workspace(T: int, device) -> torch.Tensor:
-    return torch.empty(workspace_bytes(T), dtype=torch.uint8, device=device)
+    """A routed workspace for packs of up to T rows, zero-filled (so that its
+    error word reads 0 until a call writes it: calls on an empty pack are
+    no-ops that leave the workspace untouched)."""
+    return torch.zeros(workspace_bytes(T), dtype=torch.uint8, device=device)
 
 
 def routing_plan(modality: torch.Tensor, workspace: torch.Tensor | None = None) -> torch.Tensor:

@@ -20,6 +20,7 @@ int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes) {
+    if (a_bytes <= 0 || b_bytes <= 0) return false;  // an empty range overlaps nothing
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
     return a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
 }
@@ -664,7 +665,8 @@ int mot_cfg_combine_renorm(const float *v_cond, const float *v_text_uncond, cons
     const int v = validate_latent(n_req, rows, C, max_rows, cu_rows, workspace, workspace_bytes);
     if (v != MOT_OK) return v;
     if (n_req == 0) return MOT_ERR_INVALID_ARG;  // rows without requests
-    if (!v_cond || !v_text_uncond || !out || !t) return MOT_ERR_INVALID_ARG;
+    // (with no rows the row arrays are not read and may be NULL)
+    if ((rows > 0 && (!v_cond || !v_text_uncond || !out)) || !t) return MOT_ERR_INVALID_ARG;
     if (renorm_type < 0 || renorm_type > 2) return MOT_ERR_INVALID_ARG;
     if (!isfinite(s_text) || !isfinite(s_img) || !isfinite(t_lo) || !isfinite(t_hi) ||
         !(renorm_min >= 0.0f && renorm_min <= 1.0f))
@@ -700,9 +702,11 @@ int mot_flow_sde_step_logp(const float *x, const float *v, const float *noise, c
     const int vs = validate_latent(n_req, rows, C, max_rows, cu_rows, workspace, workspace_bytes);
     if (vs != MOT_OK) return vs;
     if (n_req == 0) return MOT_ERR_INVALID_ARG;
-    if (!x || !v || !logp || !t_cur || !t_next) return MOT_ERR_INVALID_ARG;
+    // (with no rows the row arrays are not read and may be NULL: every
+    // request is empty and its log-probability is 0)
+    if ((rows > 0 && (!x || !v)) || !logp || !t_cur || !t_next) return MOT_ERR_INVALID_ARG;
     const bool sample = noise != nullptr;
-    if (sample ? (!x_next_out || x_next_in) : (!x_next_in || x_next_out)) return MOT_ERR_INVALID_ARG;
+    if (rows > 0 && (sample ? (!x_next_out || x_next_in) : (!x_next_in || x_next_out))) return MOT_ERR_INVALID_ARG;
     if (!(eta > 0.0f) || !isfinite(eta)) return MOT_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(v) || (noise && !aligned16(noise)) || (x_next_in && !aligned16(x_next_in)) ||
         (x_next_out && !aligned16(x_next_out)) || (reinterpret_cast<uintptr_t>(logp) & 3u) ||
