@@ -97,3 +97,83 @@ def test_joint_attention_graph():
     _replays_match(lambda: mot.joint_attention_varlen(q, k, v, cu, cu, 323, W.N_Q_HEADS, W.N_K_HEADS, causal=True,
                                                       out=out2, workspace=ws2), out2, ref2)
     assert mot.read_device_error(ws2) == 0
+
+
+def test_fused_qk_and_wide_gemm_graph():
+    """The QKV GEMM with the QK norm + rotary epilogue (its error-word clear
+    is a kernel, not a memset), and a down-shaped GEMM that runs 256 x 224
+    tiles on a pack of whole row blocks."""
+    T = 1024
+    m = np.concatenate([np.zeros(256, np.uint8), np.ones(768, np.uint8)])
+    x = dev(W.normal_bf16((T, 512), 1401))
+    wu, wg = dev(W.normal_bf16((W.QKV_DIM, 512), 1402, 0.02)), dev(W.normal_bf16((W.QKV_DIM, 512), 1403, 0.02))
+    md = dev(torch.from_numpy(m))
+    qn, kn = W.qk_norm_weights(base=1404)
+    qn, kn = tuple(dev(t) for t in qn), tuple(dev(t) for t in kn)
+    c, s, pos = (dev(t) for t in W.rope_inputs(T, 2048, base=1404))
+    ref = mot.routed_gemm_qk_norm_rope(x, wu, wg, md, W.N_Q_HEADS, W.N_K_HEADS, qn, kn, pos, c, s)
+    out = torch.empty_like(ref)
+    ws = mot.new_workspace(T, x.device)
+    _replays_match(lambda: mot.routed_gemm_qk_norm_rope(x, wu, wg, md, W.N_Q_HEADS, W.N_K_HEADS, qn, kn, pos, c,
+                                                         s, out=out, workspace=ws), out, ref)
+    assert mot.read_device_error(ws) == 0
+    T2 = 4096
+    m2 = np.concatenate([np.zeros(1024, np.uint8), np.ones(3072, np.uint8)])
+    x2 = dev(W.normal_bf16((T2, 256), 1405))
+    du, dg = dev(W.normal_bf16((3584, 256), 1406, 0.02)), dev(W.normal_bf16((3584, 256), 1407, 0.02))
+    md2 = dev(torch.from_numpy(m2))
+    ref2 = mot.routed_gemm(x2, du, dg, md2)
+    out2 = torch.empty_like(ref2)
+    ws2 = mot.new_workspace(T2, x2.device)
+    _replays_match(lambda: mot.routed_gemm(x2, du, dg, md2, out=out2, workspace=ws2), out2, ref2)
+
+
+def test_noalloc_and_index_sets_graph():
+    """The allocation-free GEMM (its scratch is the library's) and the
+    index-set conversion, captured together."""
+    T = 300
+    m = W.pattern(T)
+    und = dev(torch.from_numpy(np.flatnonzero(m == 0).astype(np.int32)[::-1].copy()))
+    gen = dev(torch.from_numpy(np.flatnonzero(m == 1).astype(np.int32)))
+    x = dev(W.normal_bf16((T, 256), 1411))
+    wu, wg = dev(W.normal_bf16((384, 256), 1412, 0.02)), dev(W.normal_bf16((384, 256), 1413, 0.02))
+    md = torch.empty(T, dtype=torch.uint8, device="cuda")
+    wsi = mot.new_workspace(T, x.device)
+    mot.modality_from_index_sets(und, gen, T, out=md, workspace=wsi)
+    ref = mot.routed_gemm(x, wu, wg, md)
+    out = torch.empty_like(ref)
+
+    def run():
+        mot.modality_from_index_sets(und, gen, T, out=md, workspace=wsi)
+        mot.routed_gemm_noalloc(x, wu, wg, md, out)
+
+    _replays_match(run, out, ref)
+    assert mot.read_device_error(wsi) == 0
+
+
+def test_latent_step_graph():
+    """The CFG combine and the SDE step (their check kernels clear the error
+    word), captured and replayed."""
+    C, lens = 64, [300, 0, 77]
+    cu = dev(torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32))
+    rows = int(sum(lens))
+    g = torch.Generator().manual_seed(9)
+    vc, vt, vi, xl, z = (dev(torch.randn((rows, C), generator=g)) for _ in range(5))
+    t = dev(torch.tensor([0.7, 0.5, 1.0], dtype=torch.float32))
+    tn = dev(torch.tensor([0.6, 0.4, 0.95], dtype=torch.float32))
+    ref, _ = mot.cfg_combine_renorm(vc, vt, vi, cu, 300, t, 4.0, 1.5, 0.0, 1.0, 0.2, "global")
+    xref, lref, _ = mot.flow_sde_step_logp(xl, ref, cu, 300, t, tn, 0.7, noise=z)
+    out = torch.empty_like(ref)
+    xo = torch.empty_like(xref)
+    lp = torch.empty_like(lref)
+    ws = torch.zeros(mot.latent_workspace_bytes(3, 300), dtype=torch.uint8, device="cuda")
+    both = torch.empty((rows * C + rows * C + 3,), dtype=torch.float32, device="cuda")
+    refs = torch.cat([ref.view(-1), xref.view(-1), lref.view(-1)])
+
+    def run():
+        mot.cfg_combine_renorm(vc, vt, vi, cu, 300, t, 4.0, 1.5, 0.0, 1.0, 0.2, "global", out=out, workspace=ws)
+        mot.flow_sde_step_logp(xl, out, cu, 300, t, tn, 0.7, noise=z, out=xo, logp=lp, workspace=ws)
+        torch.cat([out.view(-1), xo.view(-1), lp.view(-1)], out=both)
+
+    _replays_match(run, both, refs)
+    assert mot.read_device_error(ws) == 0
