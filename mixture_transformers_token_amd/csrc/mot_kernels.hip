@@ -406,8 +406,15 @@ __device__ __forceinline__ Schedule make_schedule(int U, int G, int wrows, int g
         // whole big-tile time: their quarters (at most two rounds of small
         // tiles, each about a third of a big tile's time) finish sooner
         s.nkeep = 0;
+    } else if (mode == 0 && nbig >= grid) {
+        // whole rounds as big tiles; a partial last round stays big when it
+        // fills more than half of the grid (its quarters would take more
+        // than two rounds of small tiles, each over a third of a big tile's
+        // time), else it runs as quarters
+        const int left = nbig % grid;
+        s.nkeep = 2 * left > grid ? nbig : nbig - left;
     } else {
-        s.nkeep = (mode == 0 && nbig >= grid) ? (nbig / grid) * grid : nbig;
+        s.nkeep = nbig;
     }
     s.nleft = nbig - s.nkeep;
     s.ru = min(s.bu * kBigM, U);
@@ -1502,17 +1509,20 @@ gemm_kernel(GemmArgs a) {
     // round-robin over all workgroups.
     const int w = xcd_remap((int)blockIdx.x, grid);
     const int nsm = sc.ntiles - sc.nkeep;
-    const int idle = sc.nkeep < grid ? grid - sc.nkeep : 0;
+    // workgroups w < fill run one big tile more than the others (the last,
+    // partial round); the others are idle then and take small tiles first
+    const int fill = sc.nkeep % grid;
+    const int idle = fill > 0 ? grid - fill : (sc.nkeep == 0 ? grid : 0);
     const int cap = min(nsm, 4 * idle);
     const int n_big = w < sc.nkeep ? cdiv(sc.nkeep - w, grid) : 0;
-    const int n_idle = (idle > 0 && w >= sc.nkeep && w - sc.nkeep < cap) ? cdiv(cap - (w - sc.nkeep), idle) : 0;
+    const int n_idle = (idle > 0 && w >= fill && w - fill < cap) ? cdiv(cap - (w - fill), idle) : 0;
     const int n_rr = cap + w < nsm ? cdiv(nsm - cap - w, grid) : 0;
     for (int it = 0; it < n_big + n_idle + n_rr; ++it) {
         int t;
         if (it < n_big)
             t = w + it * grid;
         else if (it < n_big + n_idle)
-            t = sc.nkeep + (w - sc.nkeep) + (it - n_big) * idle;
+            t = sc.nkeep + (w - fill) + (it - n_big) * idle;
         else
             t = sc.nkeep + cap + w + (it - n_big - n_idle) * grid;
         const Tile ti = tile_of(sc, t);

@@ -92,6 +92,26 @@ def test_repeatable_and_strided_output(qkv_setup):
     assert raw_equal(big[:, 32:32 + N].contiguous(), s["ref"])
 
 
+@pytest.mark.parametrize("n_und,n_gen,N", [(0, 3072, 8448), (100, 2972, 8448), (0, 3072, 4352)])
+def test_partial_round_of_big_tiles_gives_the_same_bytes(n_und, n_gen, N):
+    """A last round of big tiles more than half full runs as big tiles (12 x
+    33 = 396 tiles: 140 in the second round), with the partial row blocks'
+    small tiles on the workgroups idle in it; N = 4352 (12 x 17 = 204, under
+    one round) as a reference.  Bytes equal those of forced tile shapes."""
+    T = n_und + n_gen
+    m = np.concatenate([np.zeros(n_und, np.uint8), np.ones(n_gen, np.uint8)])
+    m = m[W.permutation(T, 6).numpy()].copy()
+    x = dev(W.normal_bf16((T, 128), 940))
+    wu = dev(W.normal_bf16((N, 128), 941, 0.02))
+    wg = dev(W.normal_bf16((N, 128), 942, 0.02))
+    md = dev(torch.from_numpy(m))
+    auto = mot.routed_gemm(x, wu, wg, md)
+    for tile in ("256x256", "128x128"):
+        forced = mot.routed_gemm(x, wu, wg, md, tile=tile)
+        torch.cuda.synchronize()
+        assert raw_equal(auto, forced), tile
+
+
 @pytest.mark.parametrize("n_und,n_gen,N", [(1024, 3072, 3584), (512, 2048, 3584), (1024, 3072, 448)])
 def test_wide_tiles_give_the_bytes_of_the_other_shapes(n_und, n_gen, N):
     """Packs whose weight rows split into 224-row tiles that fill the rounds
