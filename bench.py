@@ -56,7 +56,7 @@ def parse():
     p.add_argument("--only", default="",
                    help="comma-separated components to run (for one rocprofv3 run per kernel family): norm, "
                         "prologue, small_packs, backward, qk_norm_rope, qkv_qk_fused, attention, context_blas, "
-                        "mlp, tp4, layer_chain, latent")
+                        "mlp, tp4, layer_chain, gen_step, latent")
     p.add_argument("--copy-probe", action="store_true",
                    help="run one 1 GiB device copy first (HBM counter calibration under rocprofv3)")
     p.add_argument("--cpu-rows", type=int, default=4096,
@@ -563,10 +563,62 @@ def main():
                                                  "real_rows": real, "per_op_us": per_op}
             del act_c, att_c, ws_att_c
 
+    def c_gen_step(components):
+        """One decoder layer of a denoising step: the three CFG branches'
+        latent rows only (3 x 1024 generation rows), the prompts' keys and
+        values coming from a cache: norm -> QKV + QK norm/rotary -> attention
+        of each branch's latents over its 77 cached prompt keys and its 1024
+        latent keys (no mask) -> O -> norm -> gate/up + SwiGLU -> down.  The
+        cache is a separate [3 x 1101, 4608] buffer (its latent rows stand
+        for this step's keys and values; timing does not depend on values)."""
+        gu_u, gu_g, dn_u, dn_g = mlp_dev()
+        ou, og = (t.to(dev) for t in W.o_weights())
+        Tg = 3 * 1024
+        mg = torch.ones(Tg, dtype=torch.uint8, device=dev)
+        xg, rg = (t.to(dev) for t in W.residual_inputs(Tg, K, base=9))
+        y1 = torch.empty((Tg, K), dtype=torch.bfloat16, device=dev)
+        qkv_g = torch.empty((Tg, N), dtype=torch.bfloat16, device=dev)
+        kv = W.normal_bf16((3 * 1101, N), 10).to(dev)
+        att = torch.empty((Tg, W.Q_DIM), dtype=torch.bfloat16, device=dev)
+        o_g = torch.empty((Tg, K), dtype=torch.bfloat16, device=dev)
+        act_g = torch.empty((Tg, W.FFN), dtype=torch.bfloat16, device=dev)
+        out_g = torch.empty((Tg, K), dtype=torch.bfloat16, device=dev)
+        wsg = mot.new_workspace(Tg, dev)
+        cu_q = torch.from_numpy(W.cu_lengths([1024] * 3)).to(dev)
+        cu_k = torch.from_numpy(W.cu_lengths([1101] * 3)).to(dev)
+        ws_a = torch.empty(mot.attention_varlen_workspace_bytes(3 * 1101, 3, W.N_K_HEADS), dtype=torch.uint8,
+                           device=dev)
+        cos_g, sin_g, pos_g = (t.to(dev) for t in W.rope_inputs(Tg, 4096, base=9))
+        ops = {
+            "norm1": lambda: mot.fused_add_rmsnorm(xg, rg, nwu, nwg, mg, out=y1, rstd=None),
+            "qkv_qk_norm_rope": lambda: mot.routed_gemm_qk_norm_rope(y1, wud, wgd, mg, W.N_Q_HEADS, W.N_K_HEADS, qn,
+                                                                     kn, pos_g, cos_g, sin_g, out=qkv_g,
+                                                                     workspace=wsg),
+            "attention": lambda: mot.joint_attention_varlen(
+                qkv_g[:, :W.Q_DIM], kv[:, W.Q_DIM:W.Q_DIM + W.KV_DIM], kv[:, W.Q_DIM + W.KV_DIM:], cu_q, cu_k, 1024,
+                W.N_Q_HEADS, W.N_K_HEADS, causal=False, out=att, workspace=ws_a),
+            "o": lambda: mot.routed_gemm(att, ou, og, mg, out=o_g, workspace=wsg),
+            "norm2": lambda: mot.fused_add_rmsnorm(o_g, rg, nwu, nwg, mg, out=y1, rstd=None),
+            "gate_up_swiglu": lambda: mot.routed_gemm_swiglu(y1, gu_u, gu_g, mg, out=act_g, workspace=wsg),
+            "down": lambda: mot.routed_gemm(act_g, dn_u, dn_g, mg, out=out_g, workspace=wsg),
+        }
+
+        def layer():
+            for f in ops.values():
+                f()
+        s_layer = time_component(layer, 2, stream)
+        per_op = {k: round(time_component(f, 3, stream) * 1e6, 1) for k, f in ops.items()}
+        f_lin = 2.0 * Tg * (K * N + W.Q_DIM * K + K * 2 * W.FFN + W.FFN * K)
+        f_att = 4.0 * W.N_Q_HEADS * 128 * Tg * 1101
+        components["layer_gen_step_3x1024_latents"] = {
+            "us": round(s_layer * 1e6, 1), "TFLOP/s": round((f_lin + f_att) / s_layer / 1e12, 1),
+            "rows": Tg, "per_op_us": per_op,
+            "note": "flops: the routed linear steps and the attention (1101 keys per latent row)"}
+
     registry = {"norm": c_norm, "prologue": c_prologue, "small_packs": small_packs, "backward": c_backward,
                 "qk_norm_rope": c_qk_norm_rope, "qkv_qk_fused": c_qkv_qk_fused, "attention": c_attention,
                 "context_blas": c_context_blas, "mlp": c_mlp, "tp4": c_tp4, "layer_chain": c_layer_chain,
-                "latent": latent_step}
+                "gen_step": c_gen_step, "latent": latent_step}
     if args.no_components:
         chosen = []
     elif args.only:
