@@ -532,7 +532,9 @@ __device__ __forceinline__ int block_excl_scan(int v, int *s_red, int &total) {
 
 struct RouteBits {
     uint32_t bits[2];  // [set]: bit 16p + i <=> row p*kRoutePass + 16*tid + i is in the set
-    int base[2][2];    // [set][pass]: rank, among the set's rows, of this thread's first row of the pass
+    uint32_t ubase;    // rank among the und rows of this thread's first row of pass 0 (low
+                       // half) and pass 1 (high half); its gen rank is the rows before it
+                       // minus this (every byte is valid whenever ranks are used)
 };
 
 // Reads the pack's modality bytes once (all loads issued before any is
@@ -599,11 +601,7 @@ __device__ bool route_count(const uint8_t *__restrict__ mod, int T, int *s_red, 
     int tu;
     const int eu = block_excl_scan(cu, s_red, tu);
     const int tu0 = tu & 0xffff;
-    rb.base[0][0] = eu & 0xffff;
-    rb.base[0][1] = tu0 + (eu >> 16);
-#pragma unroll
-    for (int p = 0; p < kRoutePasses; ++p)
-        rb.base[1][p] = min(p * kRoutePass + (int)threadIdx.x * kRouteRows, T) - rb.base[0][p];
+    rb.ubase = (uint32_t)(eu & 0xffff) | ((uint32_t)(tu0 + (eu >> 16)) << 16);
     U = tu0 + (tu >> 16);
     int any_bad = 0;
 #pragma unroll
@@ -614,16 +612,16 @@ __device__ bool route_count(const uint8_t *__restrict__ mod, int T, int *s_red, 
 // s_rows[i] = the row of rank f + i among the pack's rows of `set` (i < count),
 // row 0 for the slots past count.  No workgroup-wide step: each thread
 // writes its own rows whose rank falls in the tile's window.
-__device__ void route_gather(const RouteBits &rb, int set, int f, int count, int bm, int32_t *s_rows,
-                             int * /*s_red*/) {
+__device__ void route_gather(const RouteBits &rb, int T, int set, int f, int count, int bm, int32_t *s_rows) {
     for (int i = count + (int)threadIdx.x; i < bm; i += kThreads) s_rows[i] = 0;
     const uint32_t all = set ? rb.bits[1] : rb.bits[0];
 #pragma unroll
     for (int p = 0; p < kRoutePasses; ++p) {
         uint32_t mask = (all >> (16 * p)) & 0xffffu;
-        int rank = set ? rb.base[1][p] : rb.base[0][p];
-        if (rank >= f + count || rank + __popc(mask) <= f) continue;
         const int r0 = p * kRoutePass + (int)threadIdx.x * kRouteRows;
+        const int ub = (int)((rb.ubase >> (16 * p)) & 0xffffu);
+        int rank = set ? min(r0, T) - ub : ub;
+        if (rank >= f + count || rank + __popc(mask) <= f) continue;
         while (mask != 0 && rank < f + count) {
             const int i = __ffs(mask) - 1;
             mask &= mask - 1;
@@ -821,8 +819,10 @@ constexpr int kStoreAux = 0x11;
 // per register quad.  The bf16 results (SwiGLU: act of each gate/up pair) go
 // through a wave-private LDS region (rows padded by 16 bytes) so that every
 // global store writes whole 16-byte chunks of contiguous row segments.  The
-// caller has synchronised the workgroup after the main loop.
-template <int WM, int WN, int MI, int MJ, bool SWIGLU>
+// caller has synchronised the workgroup after the main loop.  SEQ: one
+// 32 x 32 block at a time (a scheduling barrier after each block's LDS
+// writes), so that the accumulators are not all copied out to VGPRs first.
+template <int WM, int WN, int MI, int MJ, bool SWIGLU, bool SEQ = false>
 __device__ __forceinline__ void epilogue_staged(const GemmArgs &a, const Tile &ti, f32x16_t (&acc)[MI][MJ],
                                                 lds_u8 *const eb, const int32_t *s_rows, int lane, int wm,
                                                 int wn) {
@@ -867,6 +867,7 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs &a, const Tile &t
                     const u32x2_t pk = {pack2(v[0], v[1]), pack2(v[2], v[3])};
                     *(lds_u32x2 *)(wp + jj * 32 * RS + (i * 32 + q * 8) * 2) = pk;
                 }
+                if constexpr (SEQ) __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
@@ -1154,13 +1155,19 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
 // At the barrier of stage j, A(j+1) and W(j+1) must have landed; only the
 // eight instructions of A(j+2) may still be in flight.
 // The row list lives in slot 4 until the prologue's barrier: each lane
-// takes its DMA offsets and the byte offsets of its four output rows from
-// it first.  The epilogue stores straight from the accumulators (8-byte
-// pieces, default cache policy); measured faster here than staging through
-// LDS, which would need the row list rebuilt.
+// takes its DMA offsets and the token rows of its four output rows from it
+// first.  Epilogue of the 256 x 256 bf16 tiles: the row list, which the ring
+// overwrote, is rebuilt in slot 4 from those rows, and each wave writes its
+// results through its own array (epilogue_staged), so that every store
+// instruction covers whole 256-byte (SwiGLU: 128-byte) row segments.  The
+// accumulators' own layout gives 16 contiguous bytes per row and store
+// instruction, which takes the memory system about twice as long to absorb
+// when every workgroup stores its tile at the same time.  fp32 output and
+// 224-row tiles store straight from the accumulators.
 template <bool SWIGLU, bool F32 = false, bool QK = false, int BN = kBigN>
 __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint8_t *const (&hs)[5],
-                                         const int32_t *s_rows, const int tid, int32_t *qk_p = nullptr) {
+                                         const int32_t *s_rows, const int tid, lds_u8 *const eb,
+                                         int32_t *qk_p = nullptr) {
     static_assert(!(SWIGLU && F32), "fp32 output: plain GEMM only");
     static_assert(!QK || (!SWIGLU && !F32), "fused QK epilogue: plain bf16 GEMM only");
     constexpr uint32_t kOutBytes = F32 ? 4u : 2u;  // bytes per output element
@@ -1211,18 +1218,14 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
     if constexpr (QK) {
         if (ti.wrow0 < a.qk_heads * 128) qkr = qk_row_load(a, ti, s_rows, BM);
     }
-    // byte offsets of this lane's four output rows (below 4 GiB), kNoRow
-    // past the tile's rows (odd, so never a row's offset)
-    constexpr uint32_t kNoRow = 0xffffffffu;
+    // token rows of this lane's four output rows, -1 past the tile's rows
     const int rsel = lane & 31;
     const int khalf = lane >> 5;
-    uint32_t yoff[MJ];
-    {
+    int32_t yrow[MJ];
 #pragma unroll
-        for (int j = 0; j < MJ; ++j) {
-            const int mloc = wm * WM + j * 32 + rsel;
-            yoff[j] = mloc < ti.count ? (uint32_t)s_rows[mloc] * (uint32_t)a.ldy * kOutBytes : kNoRow;
-        }
+    for (int j = 0; j < MJ; ++j) {
+        const int mloc = wm * WM + j * 32 + rsel;
+        yrow[j] = mloc < ti.count ? s_rows[mloc] : -1;
     }
 
     // operand o (0 = A, 1 = W) of k-block kb into slot s, instructions [lo, hi)
@@ -1364,6 +1367,23 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
         }
     }
 
+    if constexpr (!F32 && BN == kBigN) {
+        int32_t *const rows = const_cast<int32_t *>(s_rows);
+        __syncthreads();  // every wave is done with the ring
+        if (wn == 0 && khalf == 0) {
+#pragma unroll
+            for (int j = 0; j < MJ; ++j) rows[wm * WM + j * 32 + rsel] = yrow[j];
+        }
+        __syncthreads();
+        // (the lane index made opaque: the epilogue's LDS and column
+        // offsets are then computed here, not before the main loop, where
+        // they would be kept, or spilled, through it)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        epilogue_staged<WM, WN, MI, MJ, SWIGLU, true>(a, ti, acc, eb, rows, ln, wm, wn);
+        return;
+    }
+
     // Epilogue: lane holds, for token row m = lane&31 of each block, four
     // consecutive output columns per register quad (SwiGLU: the act of each
     // gate/up pair).
@@ -1373,7 +1393,8 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
         const int col0 = SWIGLU ? ti.wrow0 / 2 + wn * (BN / 4) : ti.wrow0 + wn * WN;
 #pragma unroll
         for (int j = 0; j < MJ; ++j) {
-            if (yoff[j] == kNoRow) continue;
+            if (yrow[j] < 0) continue;
+            const uint32_t yoff = (uint32_t)yrow[j] * (uint32_t)a.ldy * kOutBytes;  // below 4 GiB
 #pragma unroll
             for (int i = 0; i < OI; ++i) {
                 const int n0 = col0 + i * 32;
@@ -1396,11 +1417,11 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
                         const u32x4_t pk = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
                                             __float_as_uint(v[3])};
                         __builtin_amdgcn_raw_buffer_store_b128(
-                            pk, yr, yoff[j] + (uint32_t)(n0 + q * 8 + khalf * 4) * 4u, 0, 0);
+                            pk, yr, yoff + (uint32_t)(n0 + q * 8 + khalf * 4) * 4u, 0, 0);
                     } else {
                         const u32x2_t pk = {pack2(v[0], v[1]), pack2(v[2], v[3])};
                         __builtin_amdgcn_raw_buffer_store_b64(
-                            pk, yr, yoff[j] + (uint32_t)(n0 + q * 8 + khalf * 4) * 2u, 0, 0);
+                            pk, yr, yoff + (uint32_t)(n0 + q * 8 + khalf * 4) * 2u, 0, 0);
                     }
                 }
             }
@@ -1536,7 +1557,12 @@ gemm_kernel(GemmArgs a) {
         __syncthreads();  // every wave is done with the previous tile's LDS
         // the tile's rows into s_rows
         if constexpr (INLINE) {
-            route_gather(rb, ti.set, ti.first - (ti.set ? U : 0), ti.count, bm, s_rows, s_red);
+            // (the route words made opaque per tile as well: the ranks
+            // derived from them are then not hoisted out of this loop, where
+            // they would be kept, or spilled, through the whole tile)
+            RouteBits rt = rb;
+            if constexpr (!PRO) asm volatile("" : "+v"(rt.bits[0]), "+v"(rt.bits[1]), "+v"(rt.ubase));
+            route_gather(rt, T, ti.set, ti.first - (ti.set ? U : 0), ti.count, bm, s_rows);
         } else {
             for (int i = threadIdx.x; i < bm; i += kThreads)
                 s_rows[i] = i < ti.count ? min(max(a.perm[ti.first + i], 0), T - 1) : 0;
@@ -1563,11 +1589,11 @@ gemm_kernel(GemmArgs a) {
                 uint8_t *const hs[5] = {lds0, lds1, lds2, lds3, lds4};
                 if constexpr (WIDE) {
                     if (sc.bn == kWideN)
-                        run_big5<false, false, false, kWideN>(a, ti, hs, s_rows, tid, qk_p);
+                        run_big5<false, false, false, kWideN>(a, ti, hs, s_rows, tid, eb, qk_p);
                     else
-                        run_big5<false, false, false>(a, ti, hs, s_rows, tid, qk_p);
+                        run_big5<false, false, false>(a, ti, hs, s_rows, tid, eb, qk_p);
                 } else {
-                    run_big5<SWIGLU, F32, QK>(a, ti, hs, s_rows, tid, qk_p);
+                    run_big5<SWIGLU, F32, QK>(a, ti, hs, s_rows, tid, eb, qk_p);
                 }
             }
         } else if constexpr (!F32) {  // (mode 1 schedules no small tiles)
