@@ -610,15 +610,16 @@ __device__ bool route_count(const uint8_t *__restrict__ mod, int T, int *s_red, 
 }
 
 // s_rows[i] = the row of rank f + i among the pack's rows of `set` (i < count),
-// row 0 for the slots past count.  No workgroup-wide step: each thread
+// row 0 for the slots past count.  tid: the thread index.  No workgroup-wide step: each thread
 // writes its own rows whose rank falls in the tile's window.
-__device__ void route_gather(const RouteBits &rb, int T, int set, int f, int count, int bm, int32_t *s_rows) {
-    for (int i = count + (int)threadIdx.x; i < bm; i += kThreads) s_rows[i] = 0;
+__device__ void route_gather(const RouteBits &rb, int T, int set, int f, int count, int bm, int32_t *s_rows,
+                             int tid) {
+    for (int i = count + tid; i < bm; i += kThreads) s_rows[i] = 0;
     const uint32_t all = set ? rb.bits[1] : rb.bits[0];
 #pragma unroll
     for (int p = 0; p < kRoutePasses; ++p) {
         uint32_t mask = (all >> (16 * p)) & 0xffffu;
-        const int r0 = p * kRoutePass + (int)threadIdx.x * kRouteRows;
+        const int r0 = p * kRoutePass + tid * kRouteRows;
         const int ub = (int)((rb.ubase >> (16 * p)) & 0xffffu);
         int rank = set ? min(r0, T) - ub : ub;
         if (rank >= f + count || rank + __popc(mask) <= f) continue;
@@ -819,9 +820,11 @@ constexpr int kStoreAux = 0x11;
 // per register quad.  The bf16 results (SwiGLU: act of each gate/up pair) go
 // through a wave-private LDS region (rows padded by 16 bytes) so that every
 // global store writes whole 16-byte chunks of contiguous row segments.  The
-// caller has synchronised the workgroup after the main loop.  SEQ: one
+// caller has synchronised the workgroup after the main loop.  SEQ (big
+// tiles, whose accumulators fill the register file): passes of 32 rows, one
 // 32 x 32 block at a time (a scheduling barrier after each block's LDS
-// writes), so that the accumulators are not all copied out to VGPRs first.
+// writes), so that the accumulators are not all copied out to VGPRs first,
+// and at most eight row read-backs at a time.
 template <int WM, int WN, int MI, int MJ, bool SWIGLU, bool SEQ = false>
 __device__ __forceinline__ void epilogue_staged(const GemmArgs &a, const Tile &ti, f32x16_t (&acc)[MI][MJ],
                                                 lds_u8 *const eb, const int32_t *s_rows, int lane, int wm,
@@ -831,19 +834,22 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs &a, const Tile &t
     constexpr int OC = SWIGLU ? WN / 2 : WN;  // output columns per wave
     constexpr int OI = OC / 32;               // output column blocks
     constexpr int RS = OC * 2 + 16;           // LDS row stride, bytes
-    constexpr int RH = ep_rows(WM, RS);       // rows per pass
-    constexpr int LPR = OC / 8;               // lanes per row (16 bytes each)
-    constexpr int RPI = 64 / LPR;             // rows per store instruction
-    static_assert(RH % 32 == 0 && WM % RH == 0 && 64 % LPR == 0 && RH % RPI == 0, "epilogue");
+    constexpr int RH = SEQ ? 32 : ep_rows(WM, RS);  // rows per pass
+    constexpr int LPR = OC / 8;               // lanes holding a row's 16-byte pieces
+    constexpr int LPP = LPR <= 8 ? 8 : LPR <= 16 ? 16 : 32;  // lanes per row (a power of two)
+    constexpr int RPI = 64 / LPP;             // rows per store instruction
+    static_assert(RH % 32 == 0 && WM % RH == 0 && LPR <= LPP && RH % RPI == 0, "epilogue");
+    // (lanes LPR..LPP-1 of a row, if any, read padding or the next row and store nothing)
+    static_assert((RH - RPI + 63 / LPP) * RS + LPP * 16 <= 32768, "epilogue read-back stays in the array");
     const int col0 = SWIGLU ? ti.wrow0 / 2 + wn * (BN / 4) : ti.wrow0 + wn * WN;
     // one LDS base per lane for the writes and one for the read-back; the
     // rest are immediate offsets
     lds_u8 *const wp = eb + rsel * RS + khalf * 8;
-    lds_u8 *const rp = eb + (lane / LPR) * RS + (lane % LPR) * 16;
+    lds_u8 *const rp = eb + (lane / LPP) * RS + (lane % LPP) * 16;
     const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
     const uint32_t ldy_bytes = (uint32_t)a.ldy * 2u;
-    const int col = col0 + (lane % LPR) * 8;
-    const bool col_ok = col < a.N;
+    const int col = col0 + (lane % LPP) * 8;
+    const bool col_ok = lane % LPP < LPR && col < a.N;
 #pragma unroll
     for (int jp = 0; jp < MJ; jp += RH / 32) {
 #pragma unroll
@@ -873,11 +879,15 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs &a, const Tile &t
 #pragma unroll
         for (int r = 0; r < RH; r += RPI) {
             const u32x4_t v = *(const lds_u32x4 *)(rp + r * RS);
-            const int mloc = wm * WM + jp * 32 + r + lane / LPR;
+            const int mloc = wm * WM + jp * 32 + r + lane / LPP;
             if (col_ok && mloc < ti.count)
                 __builtin_amdgcn_raw_buffer_store_b128(
                     v, yr,
                     (uint32_t)s_rows[mloc] * ldy_bytes + (uint32_t)col * 2u, 0, kStoreAux);
+            // (at most eight read-backs in flight: not all of a pass's rows
+            // are loaded into VGPRs before the first store)
+            if constexpr (SEQ)
+                if ((r / RPI) % 8 == 7) __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
@@ -1367,7 +1377,7 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
         }
     }
 
-    if constexpr (!F32 && BN == kBigN) {
+    if constexpr (!F32) {
         int32_t *const rows = const_cast<int32_t *>(s_rows);
         __syncthreads();  // every wave is done with the ring
         if (wn == 0 && khalf == 0) {
@@ -1562,7 +1572,8 @@ gemm_kernel(GemmArgs a) {
             // they would be kept, or spilled, through the whole tile)
             RouteBits rt = rb;
             if constexpr (!PRO) asm volatile("" : "+v"(rt.bits[0]), "+v"(rt.bits[1]), "+v"(rt.ubase));
-            route_gather(rt, T, ti.set, ti.first - (ti.set ? U : 0), ti.count, bm, s_rows);
+            route_gather(rt, T, ti.set, ti.first - (ti.set ? U : 0), ti.count, bm, s_rows,
+                         PRO ? (int)threadIdx.x : tid);
         } else {
             for (int i = threadIdx.x; i < bm; i += kThreads)
                 s_rows[i] = i < ti.count ? min(max(a.perm[ti.first + i], 0), T - 1) : 0;
