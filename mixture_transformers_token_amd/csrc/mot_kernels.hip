@@ -426,17 +426,21 @@ __device__ __forceinline__ Schedule make_schedule(int U, int G, int wrows, int g
 }
 
 // Big tile b: 256-row block mb of the concatenated blocks [und..., gen...] by
-// weight tile nb, ordered in groups of 4 row blocks (consecutive tiles share
-// A rows or weight rows).
+// weight tile nb, ordered in groups of 4 weight tiles, all row blocks of a
+// group before the next group (consecutive tiles share A rows or weight
+// rows).  An XCD's 32 consecutive tiles then cover 8 row blocks by 4 weight
+// tiles, fewer distinct operand panels than the row-grouped order gave with
+// 18 weight tiles (the QKV projection), so more of its operand reads hit the
+// XCD's L2: about 1% faster on the QKV, O, down and gate/up GEMMs.
 __device__ __forceinline__ void big_tile(const Schedule &s, int b, int &mb, int &nb) {
-    constexpr int GM = 4;
-    const int width = GM * s.nwt;
-    const int g = b / width;
-    const int first_m = g * GM;
-    const int gm = min(s.nbr - first_m, GM);
-    const int in = b - g * width;
-    mb = first_m + in % gm;
-    nb = in / gm;
+    constexpr int GN = 4;
+    const int height = GN * s.nbr;
+    const int g = b / height;
+    const int first_n = g * GN;
+    const int gn = min(s.nwt - first_n, GN);
+    const int in = b - g * height;
+    mb = in / gn;
+    nb = first_n + in % gn;
 }
 
 __device__ __forceinline__ void block_rows(const Schedule &s, int mb, Tile &ti) {
