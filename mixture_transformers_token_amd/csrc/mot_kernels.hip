@@ -72,14 +72,25 @@ __device__ __forceinline__ float bf16_at(const u32x4_t &v, int e) {
     return (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
 }
 
+// The value v holds in lane (i + N) mod 16 of this lane's 16-lane row (a DPP
+// row rotation: no LDS round trip).
+template <int N>
+__device__ __forceinline__ uint32_t row_rot(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x120 + N, 0xf, 0xf, false);
+}
+
 // One head of one row, as 16 lanes hold it (lane gi of the group: elements
-// 8 gi .. 8 gi + 7 in v): the head's RMSNorm (sum of squares per lane in
-// element order, then the xor-butterfly over the group: one fixed tree),
-// y = bf16((x * rstd) * w), then the rotate-half rotation with the
-// partner 64 columns away in lane gi ^ 8.  `live` lanes hold a real head;
-// every lane of the wave must call it (it shuffles).  Shared by the
-// standalone kernel and the QKV GEMM's fused epilogue, so both give the same
-// bytes.
+// 8 gi .. 8 gi + 7 in v; the groups are DPP rows): the head's RMSNorm (sum of
+// squares per lane in element order, then the xor-butterfly over the group:
+// one fixed tree), y = bf16((x * rstd) * w), then the rotate-half rotation
+// with the partner 64 columns away in lane gi ^ 8.  The butterfly's partners
+// come from row rotations by 8, 4, 2, 1: once a value is the same in lanes
+// i and i ^ 8 (and i ^ 4 ...), lane (i + 4) mod 16 holds the value of lane
+// i ^ 4, and so on, so each lane adds exactly the xor partner's value (the
+// same sums, bit for bit, as an exchange by lane xor).  `live` lanes hold a
+// real head; every lane of the wave must call it with all lanes active.
+// Shared by the standalone kernel and the QKV GEMM's fused epilogue, so both
+// give the same bytes.
 __device__ __forceinline__ u32x4_t qk_head(const u32x4_t &v, bool live, int gi, float eps, const u32x4_t &wv,
                                            const u32x4_t &cv, const u32x4_t &sv) {
     float ss = 0.0f;
@@ -90,8 +101,10 @@ __device__ __forceinline__ u32x4_t qk_head(const u32x4_t &v, bool live, int gi, 
             ss = e == 0 ? x * x : ss + x * x;
         }
     }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+    ss += __uint_as_float(row_rot<8>(__float_as_uint(ss)));
+    ss += __uint_as_float(row_rot<4>(__float_as_uint(ss)));
+    ss += __uint_as_float(row_rot<2>(__float_as_uint(ss)));
+    ss += __uint_as_float(row_rot<1>(__float_as_uint(ss)));
     const float rstd = 1.0f / sqrtf(ss / 128.0f + eps);
     u32x4_t y;
 #pragma unroll
@@ -99,7 +112,7 @@ __device__ __forceinline__ u32x4_t qk_head(const u32x4_t &v, bool live, int gi, 
         y[e] = pack2(bf16_lo(v[e]) * rstd * bf16_lo(wv[e]), bf16_hi(v[e]) * rstd * bf16_hi(wv[e]));
     u32x4_t z;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) z[e] = (uint32_t)__shfl_xor((int)y[e], 8);
+    for (int e = 0; e < 4; ++e) z[e] = row_rot<8>(y[e]);
     // the rotation's sign: first half y*c - y'*s, second half y*c + y'*s
     const float sg = gi < 8 ? -1.0f : 1.0f;
     u32x4_t o;
@@ -687,17 +700,19 @@ __device__ __forceinline__ uint32_t qk_chunk_off(int r, int c) {
     return (uint32_t)(r * kQkRowBytes + ((c ^ (r & 15)) << 4));
 }
 
-// Row r = threadIdx.x of the tile (one row per thread: tiles have at most
-// 256 rows): its output row and its position, loaded before the tile's main
-// loop so that their latency hides under it (two registers through the loop).
+// Row r = thread i of the tile (one row per thread: tiles have at most 256
+// rows): its output row and its position, loaded before the tile's main loop
+// so that their latency hides under it (two registers through the loop).
+// i is the thread index the tile loop made opaque, so that no address
+// derived from it is hoisted out of that loop (and spilled).
 struct QkRow {
     int row;  // output row (0 for the slots past the tile's rows)
     int pos;  // position
 };
 
-__device__ __forceinline__ QkRow qk_row_load(const GemmArgs &a, const Tile &ti, const int32_t *s_rows, int bm) {
+__device__ __forceinline__ QkRow qk_row_load(const GemmArgs &a, const Tile &ti, const int32_t *s_rows, int bm,
+                                             int i) {
     QkRow q{0, 0};
-    const int i = (int)threadIdx.x;
     if (i < bm) q.row = s_rows[i];
     if (i < ti.count) q.pos = a.positions[q.row];
     return q;
@@ -707,8 +722,7 @@ __device__ __forceinline__ QkRow qk_row_load(const GemmArgs &a, const Tile &ti, 
 // for a position outside the table, which raises MOT_ERR_POSITION; the row
 // keeps the GEMM's bytes).
 __device__ __forceinline__ void qk_row_store(const GemmArgs &a, const Tile &ti, const QkRow &q, int32_t *s_rows,
-                                             int32_t *p_rows, int bm) {
-    const int i = (int)threadIdx.x;
+                                             int32_t *p_rows, int bm, int i) {
     if (i < bm) {
         int p = q.pos;
         if (i < ti.count && (p < 0 || p >= a.n_pos)) {
@@ -777,7 +791,7 @@ __device__ __forceinline__ void qk_head_rows(const GemmArgs &a, const Tile &ti, 
     const bool col_ok = col0 + 8 * gi < a.N;  // (a last head may end at a 64-column edge)
     // four rows per group at a time (r, r + 16, r + 32, r + 48): their LDS
     // reads are issued together and their arithmetic interleaves
-    constexpr int U = 4;
+    constexpr int U = BM > 128 ? 2 : 4;
     static_assert(BM % (16 * U) == 0, "rows per pass");
     for (int r0 = wave * 4 + g; r0 < BM; r0 += 16 * U) {
         u32x4_t v[U], cv[U], sv[U], o[U];
@@ -979,7 +993,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
 
     QkRow qkr{0, 0};
     if constexpr (QK) {
-        if (ti.wrow0 < a.qk_heads * 128) qkr = qk_row_load(a, ti, s_rows, BM);
+        if (ti.wrow0 < a.qk_heads * 128) qkr = qk_row_load(a, ti, s_rows, BM, tid);
     }
 
     float rs[MJ];
@@ -1142,7 +1156,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
         if (ti.wrow0 < a.qk_heads * 128) {
             // the tile is one head: staged in array 0, the rotary rows in
             // array 1 (cos, then sin)
-            qk_row_store(a, ti, qkr, const_cast<int32_t *>(s_rows), qk_p, BM);
+            qk_row_store(a, ti, qkr, const_cast<int32_t *>(s_rows), qk_p, BM, tid);
             __syncthreads();
             qk_tables<BM>(a, qk_p, xb[1], xb[1] + BM * 128, wave, lane);
             qk_stage<MI, MJ>(acc, xb[0], wm * WM, wn * WN, lane);
@@ -1230,7 +1244,7 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
     // row list during the main loop)
     QkRow qkr{0, 0};
     if constexpr (QK) {
-        if (ti.wrow0 < a.qk_heads * 128) qkr = qk_row_load(a, ti, s_rows, BM);
+        if (ti.wrow0 < a.qk_heads * 128) qkr = qk_row_load(a, ti, s_rows, BM, tid);
     }
     // token rows of this lane's four output rows, -1 past the tile's rows
     const int rsel = lane & 31;
@@ -1366,7 +1380,7 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
             // 128-255); the rotary rows go to slots 2 (cos) and 3 (sin); the
             // row list, which the ring overwrote, is rebuilt in slot 4.
             __syncthreads();  // every wave is done with the ring
-            qk_row_store(a, ti, qkr, const_cast<int32_t *>(s_rows), qk_p, BM);
+            qk_row_store(a, ti, qkr, const_cast<int32_t *>(s_rows), qk_p, BM, tid);
             __syncthreads();
             qk_tables<BM>(a, qk_p, hs[2], hs[3], wave, lane);
 #pragma unroll
