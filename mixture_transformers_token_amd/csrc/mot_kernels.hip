@@ -336,10 +336,67 @@ constexpr int kBigM = 256, kBigN = 256, kSmallM = 128, kSmallN = 128;
 // whole rounds better than 256-row ones (O and down at N = 3584: 16 x 16 =
 // 256 tiles at T = 4096, one per CU, against 16 x 14 = 224).
 constexpr int kWideN = 224;
+// Short big tiles: 192 token rows x 256 weight rows (four waves of 96 x 128),
+// in the same instantiation, for packs whose 192-row blocks fill whole rounds
+// better (O and down on a generation step's 3072 latent rows: 16 x 14 = 224
+// tiles of 48 MFMA blocks, against 12 x 16 = 192 wide tiles of 56).
+constexpr int kShortM = 192;
 constexpr int kNarrowN = 64;  // weight rows of the narrow tiles (mid-size packs)
-constexpr int kPartialBigRows = 160;  // rows from which a partial row block is a big tile
+constexpr int kPartialBigRows = 160;    // rows from which a partial row block is a big tile
+constexpr int kPartialShortRows = 120;  // the same for 192-row blocks
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Shape of the big tiles of a plain GEMM's schedule (U und and G gen rows,
+// wrows weight rows, grid workgroups, small tiles of sn weight rows).
+// Besides 256 x 256 the candidates are 256 x 224 (allow_wide, weight rows a
+// multiple of 224) and 192 x 256 (allow_short), which always run whole.
+// Each is priced at its rounds of big tiles (a partial round counted whole)
+// times the tile's area; a candidate must fill more than half of the grid
+// and leave the small tiles of its partial row blocks room in the idle
+// workgroups of its last round (two each).  Short tiles must also beat
+// 256 x 256 priced as the schedule runs it: a partial round at most half
+// full as rounds of quarters, each a third of a big tile's time (the QKV
+// projection at T = 4096: one round and a quarter round, where short tiles
+// would need two rounds).  The cheapest wins; ties keep 256 x 256.  Shared
+// by the kernels' schedule and the host's choice of instantiation.
+__host__ __device__ inline void big_shape(int U, int G, int wrows, int grid, int sn, bool allow_wide,
+                                          bool allow_short, int &bm, int &bn) {
+    auto up = [](int a, int b) { return (a + b - 1) / b; };
+    auto blocks = [](int n, int b, int partial) { return n / b + (n % b >= partial ? 1 : 0); };
+    auto small_tiles = [&](int bu, int bg, int b) {
+        const int ru = bu * b < U ? bu * b : U, rg = bg * b < G ? bg * b : G;
+        return (up(U - ru, kSmallM) + up(G - rg, kSmallM)) * up(wrows, sn);
+    };
+    const int bu = blocks(U, kBigM, kPartialBigRows), bg = blocks(G, kBigM, kPartialBigRows);
+    bm = kBigM;
+    bn = kBigN;
+    int best = up((bu + bg) * up(wrows, kBigN), grid) * kBigM * kBigN;
+    if (allow_wide && wrows % kWideN == 0) {
+        const int nw = (bu + bg) * (wrows / kWideN);
+        const int rw = up(nw, grid);
+        if (2 * nw > grid && rw * kBigM * kWideN < best && small_tiles(bu, bg, kBigM) <= 2 * (rw * grid - nw)) {
+            best = rw * kBigM * kWideN;
+            bn = kWideN;
+        }
+    }
+    if (allow_short) {
+        const int nn = (bu + bg) * up(wrows, kBigN), left = nn % grid;
+        int base = up(nn, grid) * kBigM * kBigN;
+        if (2 * nn <= grid)
+            base = up(4 * nn, grid) * kBigM * kBigN / 3;
+        else if (nn > grid && left > 0 && 2 * left <= grid)
+            base = (nn / grid) * kBigM * kBigN + up(4 * left, grid) * kBigM * kBigN / 3;
+        const int su = blocks(U, kShortM, kPartialShortRows), sg = blocks(G, kShortM, kPartialShortRows);
+        const int nsh = (su + sg) * up(wrows, kBigN);
+        const int rs = up(nsh, grid);
+        if (2 * nsh > grid && rs * kShortM * kBigN < (best < base ? best : base) &&
+            small_tiles(su, sg, kShortM) <= 2 * (rs * grid - nsh)) {
+            bm = kShortM;
+            bn = kBigN;
+        }
+    }
+}
 
 struct Tile {
     int set;    // 0 = und, 1 = gen
@@ -365,6 +422,7 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
 // mode 1: big tiles only; mode 2: small tiles only.
 struct Schedule {
     int U, G;
+    int bm;        // big tiles' token rows: kBigM, or kShortM
     int bn;        // big tiles' weight rows: kBigN, or kWideN
     int nwt, nws;  // weight tiles of bn and of sn rows
     int sn;        // small tiles' weight rows: 128, or 64 (narrow mode)
@@ -376,15 +434,24 @@ struct Schedule {
     int ntiles;
 };
 
+// allow_wide: 256 x 224 big tiles where the cost model prefers them;
+// short: 192 x 256 big tiles always (the host launched the short-tile
+// instantiation because the cost model prefers them for the pack's size).
 __device__ __forceinline__ Schedule make_schedule(int U, int G, int wrows, int grid, int mode,
-                                                   int sn = kSmallN, bool allow_wide = false) {
+                                                   int sn = kSmallN, bool allow_wide = false,
+                                                   bool short_tiles = false) {
     Schedule s;
     s.sn = sn;
     s.U = U;
     s.G = G;
+    s.bm = kBigM;
     s.bn = kBigN;
-    s.nwt = cdiv(wrows, kBigN);
     s.nws = cdiv(wrows, sn);
+    if (mode == 0 && short_tiles)
+        s.bm = kShortM;
+    else if (mode == 0 && allow_wide)
+        big_shape(U, G, wrows, grid, sn, true, false, s.bm, s.bn);
+    s.nwt = cdiv(wrows, s.bn);
     if (mode == 2) {
         s.bu = s.nbr = 0;
     } else if (mode == 1) {
@@ -393,26 +460,12 @@ __device__ __forceinline__ Schedule make_schedule(int U, int G, int wrows, int g
     } else {
         // a set's partial row block runs as a big tile when it is mostly
         // full (its 128 x 128 tiles would be as padded and less efficient)
-        s.bu = U / kBigM + (U % kBigM >= kPartialBigRows ? 1 : 0);
-        s.nbr = s.bu + G / kBigM + (G % kBigM >= kPartialBigRows ? 1 : 0);
-    }
-    if (allow_wide && mode == 0 && wrows % kWideN == 0) {
-        // 224-row weight tiles when their rounds (a partial round counted
-        // whole) take less big-tile time than the 256-row tiles', they fill
-        // more than half of the grid, and the small tiles of the partial row
-        // blocks fit the idle workgroups of their last round (two each);
-        // wide tiles always run whole
-        const int nw = s.nbr * (wrows / kWideN), nn = s.nbr * s.nwt;
-        const int rw = cdiv(nw, grid);
-        const int ns = (cdiv(U - min(s.bu * kBigM, U), kSmallM) + cdiv(G - min((s.nbr - s.bu) * kBigM, G), kSmallM)) *
-                       cdiv(wrows, sn);
-        if (2 * nw > grid && rw * kWideN < cdiv(nn, grid) * kBigN && ns <= 2 * (rw * grid - nw)) {
-            s.bn = kWideN;
-            s.nwt = wrows / kWideN;
-        }
+        const int partial = s.bm == kShortM ? kPartialShortRows : kPartialBigRows;
+        s.bu = U / s.bm + (U % s.bm >= partial ? 1 : 0);
+        s.nbr = s.bu + G / s.bm + (G % s.bm >= partial ? 1 : 0);
     }
     const int nbig = s.nbr * s.nwt;
-    if (s.bn == kWideN) {
+    if (s.bn == kWideN || s.bm == kShortM) {
         s.nkeep = nbig;
     } else if (mode == 0 && 2 * nbig <= grid) {
         // big tiles would leave at least half of the machine idle through a
@@ -430,8 +483,8 @@ __device__ __forceinline__ Schedule make_schedule(int U, int G, int wrows, int g
         s.nkeep = nbig;
     }
     s.nleft = nbig - s.nkeep;
-    s.ru = min(s.bu * kBigM, U);
-    s.rg = min((s.nbr - s.bu) * kBigM, G);
+    s.ru = min(s.bu * s.bm, U);
+    s.rg = min((s.nbr - s.bu) * s.bm, G);
     s.su = cdiv(U - s.ru, kSmallM);
     s.sg = cdiv(G - s.rg, kSmallM);
     s.ntiles = s.nkeep + 4 * s.nleft + (s.su + s.sg) * s.nws;
@@ -459,13 +512,13 @@ __device__ __forceinline__ void big_tile(const Schedule &s, int b, int &mb, int 
 __device__ __forceinline__ void block_rows(const Schedule &s, int mb, Tile &ti) {
     if (mb < s.bu) {
         ti.set = 0;
-        ti.first = mb * kBigM;
-        ti.count = min(kBigM, s.U - ti.first);
+        ti.first = mb * s.bm;
+        ti.count = min(s.bm, s.U - ti.first);
     } else {
-        const int off = (mb - s.bu) * kBigM;
+        const int off = (mb - s.bu) * s.bm;
         ti.set = 1;
         ti.first = s.U + off;
-        ti.count = min(kBigM, s.G - off);
+        ti.count = min(s.bm, s.G - off);
     }
 }
 
@@ -1192,7 +1245,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
 // instruction, which takes the memory system about twice as long to absorb
 // when every workgroup stores its tile at the same time.  fp32 output and
 // 224-row tiles store straight from the accumulators.
-template <bool SWIGLU, bool F32 = false, bool QK = false, int BN = kBigN>
+template <bool SWIGLU, bool F32 = false, bool QK = false, int BN = kBigN, int BM = kBigM>
 __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint8_t *const (&hs)[5],
                                          const int32_t *s_rows, const int tid, lds_u8 *const eb,
                                          int32_t *qk_p = nullptr) {
@@ -1200,16 +1253,21 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
     static_assert(!QK || (!SWIGLU && !F32), "fused QK epilogue: plain bf16 GEMM only");
     constexpr uint32_t kOutBytes = F32 ? 4u : 2u;  // bytes per output element
     static_assert(BN == kBigN || (BN == kWideN && !SWIGLU && !F32 && !QK), "wide tiles: plain bf16 GEMM only");
-    // 256 x 256: waves in a 2 x 2 grid of 128 x 128; 256 x 224: four waves
-    // of 64 token rows x all 224 weight rows
-    constexpr int BM = kBigM;
+    static_assert(BM == kBigM || (BM == kShortM && BN == kBigN && !SWIGLU && !F32 && !QK),
+                  "short tiles: plain bf16 GEMM only");
+    // 256 x 256: waves in a 2 x 2 grid of 128 x 128; 192 x 256: a 2 x 2 grid
+    // of 96 x 128; 256 x 224: four waves of 64 token rows x all 224 weight
+    // rows
     constexpr int WAVES_N = BN == kBigN ? 2 : 1;
     constexpr int WM = BM / (4 / WAVES_N), WN = BN / WAVES_N;
     constexpr int MJ = WM / 32, MI = WN / 32;
     constexpr int NM = MI * MJ;
     constexpr int XL = BM / 32, WL = BN / 32;  // DMA instructions per wave per operand and stage
     constexpr int HX = XL / 2, HW = WL / 2;
-    static_assert(XL == 8 && ((WL == 8 && NM == 16) || (WL == 7 && NM == 14)), "big tile");
+    static_assert((XL == 8 && ((WL == 8 && NM == 16) || (WL == 7 && NM == 14))) ||
+                      (XL == 6 && WL == 8 && NM == 12),
+                  "big tile");
+    constexpr int DL = XL > WL ? XL : WL;
 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1259,12 +1317,15 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
     // operand o (0 = A, 1 = W) of k-block kb into slot s, instructions [lo, hi)
     auto issue = [&](int o, int kb, int s, int lo, int hi) {
 #pragma unroll
-        for (int j = 0; j < XL; ++j) {
+        for (int j = 0; j < DL; ++j) {
             if (j < lo || j >= hi) continue;
-            if (o == 0)
-                dma16(xr, xoff[j], (uint32_t)kb * kRowBytes, hs[s] + (wave * (BM / 4) + j * 8) * kRowBytes);
-            else
-                dma16(wr, woff[j], (uint32_t)kb * kRowBytes, hs[s] + (wave * (BN / 4) + j * 8) * kRowBytes);
+            if (o == 0) {
+                if (j < XL)
+                    dma16(xr, xoff[j], (uint32_t)kb * kRowBytes, hs[s] + (wave * (BM / 4) + j * 8) * kRowBytes);
+            } else {
+                if (j < WL)
+                    dma16(wr, woff[j], (uint32_t)kb * kRowBytes, hs[s] + (wave * (BN / 4) + j * 8) * kRowBytes);
+            }
         }
     };
 
@@ -1480,16 +1541,18 @@ __device__ __forceinline__ uint16_t *prologue_nw_lds() {
 // array 0 or 2 and W in array 1 or 3, and its norm weights take 16 KiB).
 // Small tiles run four stages, one array each.
 // WIDE: the schedule may pick 256 x 224 big tiles (plain GEMMs whose weight
-// rows are a multiple of 224; a separate instantiation, so that the other
-// GEMMs keep their register allocation).
+// rows are a multiple of 224); SHORT: its big tiles are 192 x 256.
+// Separate instantiations, so that the other GEMMs keep their register
+// allocation (a kernel with the 192-row and the 256-row paths spills).
 template <bool SWIGLU, bool PRO, bool INLINE, bool NARROW = false, bool F32 = false, bool QK = false,
-          bool WIDE = false>
+          bool WIDE = false, bool SHORT = false>
 __global__ void __launch_bounds__(kThreads, 1)
 gemm_kernel(GemmArgs a) {
     static_assert(!NARROW || (!SWIGLU && !PRO), "narrow tiles: plain GEMM only");
     static_assert(!F32 || (!SWIGLU && !PRO && !NARROW), "fp32 output: plain GEMM, big tiles only");
     static_assert(!QK || (!SWIGLU && !PRO && !NARROW && !F32), "fused QK epilogue: plain bf16 GEMM only");
     static_assert(!WIDE || (!SWIGLU && !PRO && !NARROW && !F32 && !QK), "wide tiles: plain bf16 GEMM only");
+    static_assert(!SHORT || (!SWIGLU && !PRO && !NARROW && !F32 && !QK && !WIDE), "short tiles: plain bf16 GEMM only");
     constexpr int kArrayBytes = kBigM * kRowBytes;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kArrayBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kArrayBytes];
@@ -1551,7 +1614,7 @@ gemm_kernel(GemmArgs a) {
     // fp32 output runs 256 x 256 tiles only (mode 1: every row block,
     // partial ones included, is a big tile; no small tiles)
     const Schedule sc = NARROW ? make_schedule(U, G, a.wrows, grid, 2, kNarrowN)
-                               : make_schedule(U, G, a.wrows, grid, F32 ? 1 : a.tile_mode, kSmallN, WIDE);
+                               : make_schedule(U, G, a.wrows, grid, F32 ? 1 : a.tile_mode, kSmallN, WIDE, SHORT);
     // Static assignment.  Big tiles go round-robin (whole rounds, or one
     // partial round); small tiles (about a quarter of a big tile's work each)
     // go first to the workgroups that hold no big tile, up to four each, then
@@ -1576,7 +1639,7 @@ gemm_kernel(GemmArgs a) {
             t = sc.nkeep + cap + w + (it - n_big - n_idle) * grid;
         const Tile ti = tile_of(sc, t);
         if (ti.count <= 0 || ti.wrow0 >= a.wrows) continue;  // uniform: nothing to compute
-        const int bm = ti.big ? kBigM : kSmallM;
+        const int bm = ti.big ? sc.bm : kSmallM;
         // The thread index, made opaque per tile: per-lane offsets are then
         // recomputed in each tile instead of being hoisted out of this loop
         // and spilled (a spill reload waits on vmcnt, i.e. on in-flight DMA).
@@ -1621,6 +1684,8 @@ gemm_kernel(GemmArgs a) {
                         run_big5<false, false, false, kWideN>(a, ti, hs, s_rows, tid, eb, qk_p);
                     else
                         run_big5<false, false, false>(a, ti, hs, s_rows, tid, eb, qk_p);
+                } else if constexpr (SHORT) {
+                    run_big5<false, false, false, kBigN, kShortM>(a, ti, hs, s_rows, tid, eb, qk_p);
                 } else {
                     run_big5<SWIGLU, F32, QK>(a, ti, hs, s_rows, tid, eb, qk_p);
                 }
@@ -2235,6 +2300,24 @@ hipError_t launch_gemm_qk(const GemmArgs &a, bool inline_route, int grid, hipStr
 template <bool SWIGLU, bool PRO>
 hipError_t launch_gemm_t(const GemmArgs &a, bool inline_route, int grid, hipStream_t stream) {
     if constexpr (!SWIGLU && !PRO) {
+        // The host does not know the pack's split into the two sets before
+        // an in-kernel segment list is built: it picks the instantiation from
+        // the cost model with every row in one set.  The short-tile kernel
+        // then runs 192-row big tiles for the real split (same bytes as any
+        // other shape); the wide-tile kernel chooses between 256 x 224 and
+        // 256 x 256 for it.
+        int bm = kBigM, bn = kBigN;
+        if (a.tile_mode == 0 && a.T <= (1 << 30))
+            big_shape(0, (int)a.T, (int)a.wrows, grid, kSmallN, true, true, bm, bn);
+        if (a.tile_mode == 0 && bm == kShortM) {
+            if (inline_route)
+                hipLaunchKernelGGL((gemm_kernel<false, false, true, false, false, false, false, true>), dim3(grid),
+                                   dim3(kThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL((gemm_kernel<false, false, false, false, false, false, false, true>), dim3(grid),
+                                   dim3(kThreads), 0, stream, a);
+            return hipGetLastError();
+        }
         if (a.tile_mode == 0 && a.wrows % kWideN == 0) {
             if (inline_route)
                 hipLaunchKernelGGL((gemm_kernel<false, false, true, false, false, false, true>), dim3(grid),

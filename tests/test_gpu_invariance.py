@@ -136,6 +136,32 @@ def test_wide_tiles_give_the_bytes_of_the_other_shapes(n_und, n_gen, N):
     assert raw_equal(auto, ready)
 
 
+@pytest.mark.parametrize("n_und,n_gen,N", [(0, 3072, 3584), (100, 2972, 3584), (0, 3072, 1024)])
+def test_short_tiles_give_the_bytes_of_the_other_shapes(n_und, n_gen, N):
+    """A pack whose 192-row blocks fill the rounds better (O and down on a
+    generation step's 3072 latent rows: 16 x 14 = 224 tiles of 192 x 256,
+    against 192 of 256 x 224) runs the short-tile kernel, also when some rows
+    belong to the other set (the host chooses from the pack's size alone);
+    bytes equal those of forced 256 x 256 and 128 x 128 tiles, with the
+    in-kernel segment list and with a ready plan.  N = 1024 is a shape the
+    short tiles do not take (too few tiles)."""
+    T = n_und + n_gen
+    m = np.concatenate([np.zeros(n_und, np.uint8), np.ones(n_gen, np.uint8)])
+    m = m[W.permutation(T, 7).numpy()].copy()
+    x = dev(W.normal_bf16((T, 512), 950))
+    wu = dev(W.normal_bf16((N, 512), 951, 0.02))
+    wg = dev(W.normal_bf16((N, 512), 952, 0.02))
+    md = dev(torch.from_numpy(m))
+    auto = mot.routed_gemm(x, wu, wg, md)
+    ws = mot.routing_plan(md)
+    ready = mot.routed_gemm(x, wu, wg, md, workspace=ws, plan_ready=True)
+    for tile in ("256x256", "128x128"):
+        forced = mot.routed_gemm(x, wu, wg, md, tile=tile)
+        torch.cuda.synchronize()
+        assert raw_equal(auto, forced), tile
+    assert raw_equal(auto, ready)
+
+
 @pytest.mark.parametrize("tile", ["256x256", "128x128"])
 def test_tile_shape_does_not_change_bytes(qkv_setup, tile):
     """Every tile shape runs the same per-element k order: forcing one shape

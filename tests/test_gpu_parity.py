@@ -292,6 +292,17 @@ def test_down_cfg_pack_wide_tiles():
     _gemm_parity(a, dn_u, dn_g, m, rows=rows)
 
 
+def test_down_generation_step_short_tiles():
+    """The down projection of a generation step (3072 latent rows, all in
+    the generation set), which runs 192 x 256 tiles (16 x 14 = 224, one
+    round): the single-op bar against the oracle on sampled rows."""
+    m = np.ones(3072, np.uint8)
+    a = W.normal_bf16((m.size, W.FFN), 1920)
+    _, _, dn_u, dn_g = W.mlp_weights()
+    rows = W.sample_rows(m, 24, seed=14)
+    _gemm_parity(a, dn_u, dn_g, m, rows=rows)
+
+
 def _layer_chain_gpu(x, r, m, wts, rope, lengths):
     """fused add-RMSNorm -> QKV -> QK norm + rotary -> shared joint attention
     (causal within each request of `lengths`) -> O -> fused add-RMSNorm ->
