@@ -246,7 +246,7 @@ def main():
     n_und, n_gen = int((m == 0).sum()), int((m == 1).sum())
     traffic = measured_traffic()
     roofline = {
-        "kernel": "gemm_kernel<false,false,true,false,false,false,false> (routed QKV GEMM, in-kernel segment list)",
+        "kernel": "gemm_kernel<false,false,true,false,false,false,false,false> (routed QKV GEMM, in-kernel segment list)",
         "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
         "avg_kernel_us": round(gemm_s * 1e6, 2),
