@@ -371,26 +371,29 @@ __host__ __device__ inline void big_shape(int U, int G, int wrows, int grid, int
     const int bu = blocks(U, kBigM, kPartialBigRows), bg = blocks(G, kBigM, kPartialBigRows);
     bm = kBigM;
     bn = kBigN;
-    int best = up((bu + bg) * up(wrows, kBigN), grid) * kBigM * kBigN;
+    // costs in 64 bits: rounds times a tile's area overflows 32 bits for
+    // the largest packs
+    const int64_t area = (int64_t)kBigM * kBigN;
+    int64_t best = up((bu + bg) * up(wrows, kBigN), grid) * area;
     if (allow_wide && wrows % kWideN == 0) {
         const int nw = (bu + bg) * (wrows / kWideN);
         const int rw = up(nw, grid);
-        if (2 * nw > grid && rw * kBigM * kWideN < best && small_tiles(bu, bg, kBigM) <= 2 * (rw * grid - nw)) {
-            best = rw * kBigM * kWideN;
+        if (2 * nw > grid && rw * (int64_t)kBigM * kWideN < best && small_tiles(bu, bg, kBigM) <= 2 * (rw * grid - nw)) {
+            best = rw * (int64_t)kBigM * kWideN;
             bn = kWideN;
         }
     }
     if (allow_short) {
         const int nn = (bu + bg) * up(wrows, kBigN), left = nn % grid;
-        int base = up(nn, grid) * kBigM * kBigN;
+        int64_t base = up(nn, grid) * area;
         if (2 * nn <= grid)
-            base = up(4 * nn, grid) * kBigM * kBigN / 3;
+            base = up(4 * nn, grid) * area / 3;
         else if (nn > grid && left > 0 && 2 * left <= grid)
-            base = (nn / grid) * kBigM * kBigN + up(4 * left, grid) * kBigM * kBigN / 3;
+            base = (nn / grid) * area + up(4 * left, grid) * area / 3;
         const int su = blocks(U, kShortM, kPartialShortRows), sg = blocks(G, kShortM, kPartialShortRows);
         const int nsh = (su + sg) * up(wrows, kBigN);
         const int rs = up(nsh, grid);
-        if (2 * nsh > grid && rs * kShortM * kBigN < (best < base ? best : base) &&
+        if (2 * nsh > grid && rs * (int64_t)kShortM * kBigN < (best < base ? best : base) &&
             small_tiles(su, sg, kShortM) <= 2 * (rs * grid - nsh)) {
             bm = kShortM;
             bn = kBigN;
