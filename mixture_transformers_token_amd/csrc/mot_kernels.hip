@@ -67,7 +67,6 @@ constexpr int kQkChunks = 2;     // 4-head chunks per wave (8 heads)
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
-__device__ __forceinline__ float bf16_rne(float v) { return __uint_as_float(pack2(v, 0.0f) << 16); }
 __device__ __forceinline__ float bf16_at(const u32x4_t &v, int e) {
     return (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
 }
@@ -113,16 +112,20 @@ __device__ __forceinline__ u32x4_t qk_head(const u32x4_t &v, bool live, int gi, 
     u32x4_t z;
 #pragma unroll
     for (int e = 0; e < 4; ++e) z[e] = row_rot<8>(y[e]);
-    // the rotation's sign: first half y*c - y'*s, second half y*c + y'*s
-    const float sg = gi < 8 ? -1.0f : 1.0f;
+    // out = bf16(bf16(y c) + bf16(sg (y' s))), sg = -1 in the first half of
+    // the head (y c - y' s), +1 in the second.  The sign goes into the sine's
+    // sign bits (negating a factor negates the product exactly, zeros
+    // included), each pair of roundings is one packed conversion, and the
+    // sum is rounded once by the final pack (rounding a bf16 value again
+    // leaves it as it is): the same bits, fewer instructions.
+    const uint32_t sflip = gi < 8 ? 0x80008000u : 0u;
     u32x4_t o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const float lo = bf16_rne(bf16_rne(bf16_lo(y[e]) * bf16_lo(cv[e])) +
-                                  bf16_rne(sg * (bf16_lo(z[e]) * bf16_lo(sv[e]))));
-        const float hi = bf16_rne(bf16_rne(bf16_hi(y[e]) * bf16_hi(cv[e])) +
-                                  bf16_rne(sg * (bf16_hi(z[e]) * bf16_hi(sv[e]))));
-        o[e] = pack2(lo, hi);
+        const uint32_t c = pack2(bf16_lo(y[e]) * bf16_lo(cv[e]), bf16_hi(y[e]) * bf16_hi(cv[e]));
+        const uint32_t sw = sv[e] ^ sflip;
+        const uint32_t t = pack2(bf16_lo(z[e]) * bf16_lo(sw), bf16_hi(z[e]) * bf16_hi(sw));
+        o[e] = pack2(bf16_lo(c) + bf16_lo(t), bf16_hi(c) + bf16_hi(t));
     }
     return o;
 }
