@@ -1634,7 +1634,18 @@ gemm_kernel(GemmArgs a) {
     const int cap = min(nsm, 4 * idle);
     const int n_big = w < sc.nkeep ? cdiv(sc.nkeep - w, grid) : 0;
     const int n_idle = (idle > 0 && w >= fill && w - fill < cap) ? cdiv(cap - (w - fill), idle) : 0;
-    const int n_rr = cap + w < nsm ? cdiv(nsm - cap - w, grid) : 0;
+    // Round-robin small tiles that fit in one round go in chunks of four
+    // consecutive tiles (a big tile's quarters, or neighbours in a row block:
+    // they share operand panels) dealt to the XCDs in turn.  Contiguous
+    // ranges per XCD would crowd such a round onto the first few XCDs, whose
+    // L2s and fabric links then carry all of its operand traffic (QKV at
+    // T=4096: 164 small tiles on five XCDs; dealt out, 3% faster).
+    int wsm = w;
+    if ((grid & 31) == 0 && nsm - cap <= grid) {
+        const int id = (int)blockIdx.x, local = id >> 3;
+        wsm = (local >> 2) * 32 + (id & 7) * 4 + (local & 3);
+    }
+    const int n_rr = cap + wsm < nsm ? cdiv(nsm - cap - wsm, grid) : 0;
     for (int it = 0; it < n_big + n_idle + n_rr; ++it) {
         int t;
         if (it < n_big)
@@ -1642,7 +1653,7 @@ gemm_kernel(GemmArgs a) {
         else if (it < n_big + n_idle)
             t = sc.nkeep + (w - fill) + (it - n_big) * idle;
         else
-            t = sc.nkeep + cap + w + (it - n_big - n_idle) * grid;
+            t = sc.nkeep + cap + wsm + (it - n_big - n_idle) * grid;
         const Tile ti = tile_of(sc, t);
         if (ti.count <= 0 || ti.wrow0 >= a.wrows) continue;  // uniform: nothing to compute
         const int bm = ti.big ? sc.bm : kSmallM;
