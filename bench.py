@@ -295,14 +295,13 @@ def main():
         q_v, k_v = qkv_buf[:, :W.Q_DIM], qkv_buf[:, W.Q_DIM:W.Q_DIM + W.KV_DIM]
         v_v = qkv_buf[:, W.Q_DIM + W.KV_DIM:]
         att = torch.empty((T, W.Q_DIM), dtype=torch.bfloat16, device=dev)
-        ws_att = torch.empty(mot.attention_workspace_bytes(T, W.N_K_HEADS), dtype=torch.uint8, device=dev)
         s_att = time_component(lambda: mot.joint_attention(q_v, k_v, v_v, W.N_Q_HEADS, W.N_K_HEADS, causal=True,
-                                                           out=att, workspace=ws_att), iters, stream)
+                                                           out=att), iters, stream)
         f_att = 4.0 * W.N_Q_HEADS * 128 * T * (T + 1) / 2
         components["joint_attention_causal_T4096"] = {
             "us": round(s_att * 1e6, 1), "TFLOP/s": round(f_att / s_att / 1e12, 1),
             "frac_mfma": round(f_att / s_att / 1e12 / PEAK_BF16_TFLOPS, 3),
-            "note": "includes the V transpose into the workspace; flops of visible keys only"}
+            "note": "one kernel (V read in place); flops of visible keys only"}
 
     def latent_step(components):
         """The per-step latent work of a batch of 16 rollouts of 1024 latent

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 11
+#define MOT_ABI_VERSION 12
 
 typedef enum mot_status {
     MOT_OK = 0,
@@ -343,9 +343,8 @@ int mot_qk_norm_rope(uint16_t *qkv, int64_t ld, int64_t T, int64_t n_q_heads, in
  * MOT_ERR_INDEX_SET, MOT_ERR_SCHEDULE, or MOT_ERR_DEVICE if the copy fails. */
 int mot_read_device_error(const void *workspace, void *stream);
 
-/* Workspace bytes of mot_joint_attention: the transposed V of the kv heads,
- * n_kv_heads * 128 rows of round_up(Tk, 64) bf16 (0 when Tk == 0).  Since
- * ABI 6. */
+/* Workspace bytes of mot_joint_attention: 0 (V is read in place; until
+ * ABI 11 the call kept a transposed copy of V there).  Since ABI 6. */
 size_t mot_attention_workspace_bytes(int64_t Tk, int64_t n_kv_heads);
 
 /* Shared joint attention: the "gen_joint_attention" work item of the RFC
@@ -374,20 +373,21 @@ size_t mot_attention_workspace_bytes(int64_t Tk, int64_t n_kv_heads);
  *        q, k, v or the workspace.
  *   head_dim == 128; n_q_heads % n_kv_heads == 0; n_q_heads <= 256;
  *   Tq, Tk <= MOT_MAX_T; causal 0 or 1; pointers 16-byte aligned.
- *   workspace: >= mot_attention_workspace_bytes(Tk, n_kv_heads) bytes,
- *        16-byte aligned, overwritten (not needed when Tk == 0).
+ *   workspace, workspace_bytes: unused (may be NULL, 0); kept for callers
+ *        that size one with mot_attention_workspace_bytes.
+ *   The kernel addresses K and V with 32-bit byte offsets: (round_up(Tk, 64)
+ *        * ldk + 128 * n_kv_heads) * 2 and the same with ldv stay below 2^32.
  * Errors: MOT_ERR_INVALID_ARG, MOT_ERR_UNSUPPORTED_SHAPE, MOT_ERR_MISALIGNED,
- * MOT_ERR_WORKSPACE, MOT_ERR_DEVICE.  Tq == 0 is a no-op.  Since ABI 6. */
+ * MOT_ERR_DEVICE.  Tq == 0 is a no-op.  Since ABI 6. */
 int mot_joint_attention(const uint16_t *q, int64_t ldq, const uint16_t *k, int64_t ldk,
                         const uint16_t *v, int64_t ldv, uint16_t *out, int64_t ldo,
                         int64_t Tq, int64_t Tk, int64_t n_q_heads, int64_t n_kv_heads,
                         int64_t head_dim, int causal, void *workspace, size_t workspace_bytes,
                         void *stream);
 
-/* Workspace bytes of mot_joint_attention_varlen: a MOT_WS_HEADER_BYTES
- * header (its first int32 is the error word), then the transposed V of the
- * kv heads, n_kv_heads * 128 rows of round_up(Tk + 63 * n_seqs, 64) bf16.
- * 0 for invalid sizes.  Since ABI 7. */
+/* Workspace bytes of mot_joint_attention_varlen: MOT_WS_HEADER_BYTES, the
+ * header whose first int32 is the lengths check's error word (until ABI 11
+ * a transposed copy of V followed it).  0 for invalid sizes.  Since ABI 7. */
 size_t mot_attention_varlen_workspace_bytes(int64_t Tk, int64_t n_seqs, int64_t n_kv_heads);
 
 /* mot_joint_attention over packed sequences: sequence b has the query rows

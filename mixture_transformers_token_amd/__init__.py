@@ -27,7 +27,7 @@ __all__ = [
     "flow_sde_step_logp", "RENORM", "routed_gemm_qk_norm_rope",
 ]
 
-ABI_VERSION = 11
+ABI_VERSION = 12
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
 WS_HEADER_BYTES = 256
 FLAG_PLAN_READY = 1
@@ -525,12 +525,11 @@ def joint_attention(q, k, v, n_q_heads, n_kv_heads, causal=True, out=None, works
     _req(out, "out", torch.bfloat16, 2)
     if out.shape[0] != Tq or out.shape[1] < width:
         raise ValueError(f"out must be [{Tq}, >= {width}]")
-    if workspace is None:
-        workspace = torch.empty(max(attention_workspace_bytes(Tk, n_kv_heads), 16), dtype=torch.uint8,
-                                device=q.device)
+    # (the call reads V in place and needs no workspace; one passed in is unused)
     st = lib().mot_joint_attention(_ptr(q), _rows(q, "q"), _ptr(k), _rows(k, "k"), _ptr(v), _rows(v, "v"),
                                    _ptr(out), _rows(out, "out"), Tq, Tk, int(n_q_heads), int(n_kv_heads), 128,
-                                   1 if causal else 0, _ptr(workspace), workspace.numel(), _stream(q.device))
+                                   1 if causal else 0, _ptr(workspace),
+                                   0 if workspace is None else workspace.numel(), _stream(q.device))
     _check(st, "mot_joint_attention")
     return out
 

@@ -61,18 +61,13 @@ class DeviceGuard {
 constexpr int64_t kAttnHeadDim = 128;
 constexpr int64_t kAttnMaxHeads = 256;
 
-size_t attn_ws_bytes(int64_t Tk, int64_t hkv) {
-    if (Tk <= 0 || hkv <= 0) return 0;
-    return (size_t)(hkv * kAttnHeadDim * round_up(Tk, 64) * 2);
-}
-
-// packed sequences: V^T row pitch (columns), enough for every sequence's keys
-// rounded up to 64
-int64_t attn_varlen_ldvt(int64_t Tk, int64_t n_seqs) { return round_up(Tk + 63 * n_seqs, 64); }
+// the attention reads V in place: one sequence needs no workspace, packed
+// sequences only the header with the lengths check's error word
+size_t attn_ws_bytes(int64_t, int64_t) { return 0; }
 
 size_t attn_varlen_ws_bytes(int64_t Tk, int64_t n_seqs, int64_t hkv) {
     if (Tk < 0 || n_seqs <= 0 || hkv <= 0) return 0;
-    return (size_t)(MOT_WS_HEADER_BYTES + hkv * kAttnHeadDim * attn_varlen_ldvt(Tk, n_seqs) * 2);
+    return (size_t)MOT_WS_HEADER_BYTES;
 }
 
 constexpr int64_t kLatentMaxC = 4096;
@@ -491,36 +486,29 @@ int mot_joint_attention(const uint16_t *q, int64_t ldq, const uint16_t *k, int64
     if (ldq % 8 || ldo % 8 || (Tk > 0 && (ldk % 8 || ldv % 8))) return MOT_ERR_MISALIGNED;
     if (!aligned16(q) || !aligned16(out) || (Tk > 0 && (!aligned16(k) || !aligned16(v))))
         return MOT_ERR_MISALIGNED;
-    const size_t wsb = attn_ws_bytes(Tk, n_kv_heads);
-    if (Tk > 0 && (!workspace || workspace_bytes < wsb)) return MOT_ERR_WORKSPACE;
-    if (Tk > 0 && !aligned16(workspace)) return MOT_ERR_MISALIGNED;
+    (void)workspace;
+    (void)workspace_bytes;
     const int64_t q_bytes = ((Tq - 1) * ldq + qw) * 2, o_bytes = ((Tq - 1) * ldo + qw) * 2;
     if (overlaps(out, o_bytes, q, q_bytes)) return MOT_ERR_INVALID_ARG;
     if (Tk > 0) {
         const int64_t k_bytes = ((Tk - 1) * ldk + kw) * 2, v_bytes = ((Tk - 1) * ldv + kw) * 2;
-        // the kernel addresses K (up to its last key block's end) and the
-        // transposed V with 32-bit byte offsets
-        if ((round_up(Tk, 64) * ldk + kw) * 2 >= (int64_t(1) << 32) || (int64_t)wsb >= (int64_t(1) << 32))
+        // the kernel addresses K and V (up to their last key block's end)
+        // with 32-bit byte offsets
+        if ((round_up(Tk, 64) * ldk + kw) * 2 >= (int64_t(1) << 32) ||
+            (round_up(Tk, 64) * ldv + kw) * 2 >= (int64_t(1) << 32))
             return MOT_ERR_UNSUPPORTED_SHAPE;
-        if (overlaps(out, o_bytes, k, k_bytes) || overlaps(out, o_bytes, v, v_bytes) ||
-            overlaps(out, o_bytes, workspace, (int64_t)wsb) || overlaps(workspace, (int64_t)wsb, q, q_bytes) ||
-            overlaps(workspace, (int64_t)wsb, k, k_bytes) || overlaps(workspace, (int64_t)wsb, v, v_bytes))
-            return MOT_ERR_INVALID_ARG;
+        if (overlaps(out, o_bytes, k, k_bytes) || overlaps(out, o_bytes, v, v_bytes)) return MOT_ERR_INVALID_ARG;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     DeviceGuard guard(s);
     if (!guard.ok()) return MOT_ERR_DEVICE;
-    const int64_t tk_pad = round_up(Tk, 64);
-    uint16_t *vt = static_cast<uint16_t *>(workspace);
-    if (Tk > 0 && mot::launch_transpose(v, ldv, Tk, kw, nullptr, 1, vt, tk_pad, tk_pad, s) != hipSuccess)
-        return MOT_ERR_DEVICE;
     mot::AttnArgs a;
     a.q = q;
     a.ldq = ldq;
     a.k = k;
     a.ldk = ldk;
-    a.vt = vt;
-    a.ldvt = tk_pad;
+    a.v = v;
+    a.ldv = ldv;
     a.out = out;
     a.ldo = ldo;
     a.Tq = Tq;
@@ -565,29 +553,26 @@ int mot_joint_attention_varlen(const uint16_t *q, int64_t ldq, const uint16_t *k
         return MOT_ERR_INVALID_ARG;
     if (Tk > 0) {
         const int64_t k_bytes = ((Tk - 1) * ldk + kw) * 2, v_bytes = ((Tk - 1) * ldv + kw) * 2;
-        if ((round_up(Tk, 64) * ldk + kw) * 2 >= (int64_t(1) << 32)) return MOT_ERR_UNSUPPORTED_SHAPE;
+        if ((round_up(Tk, 64) * ldk + kw) * 2 >= (int64_t(1) << 32) ||
+            (round_up(Tk, 64) * ldv + kw) * 2 >= (int64_t(1) << 32))
+            return MOT_ERR_UNSUPPORTED_SHAPE;
         if (overlaps(out, o_bytes, k, k_bytes) || overlaps(out, o_bytes, v, v_bytes) ||
             overlaps(workspace, (int64_t)wsb, k, k_bytes) || overlaps(workspace, (int64_t)wsb, v, v_bytes))
             return MOT_ERR_INVALID_ARG;
     }
-    if ((int64_t)wsb >= (int64_t(1) << 32)) return MOT_ERR_UNSUPPORTED_SHAPE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     DeviceGuard guard(s);
     if (!guard.ok()) return MOT_ERR_DEVICE;
     int32_t *err = static_cast<int32_t *>(workspace);
-    uint16_t *vt = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + MOT_WS_HEADER_BYTES);
-    const int64_t ldvt = attn_varlen_ldvt(Tk, n_seqs);
     if (mot::launch_seqlens_check(cu_q, cu_k, (int)n_seqs, Tq, Tk, max_q, err, s) != hipSuccess)
-        return MOT_ERR_DEVICE;
-    if (mot::launch_vt_packed(v, ldv, (int)kw, cu_k, (int)n_seqs, vt, ldvt, err, s) != hipSuccess)
         return MOT_ERR_DEVICE;
     mot::AttnArgs a;
     a.q = q;
     a.ldq = ldq;
     a.k = k;
     a.ldk = ldk;
-    a.vt = vt;
-    a.ldvt = ldvt;
+    a.v = v;
+    a.ldv = ldv;
     a.out = out;
     a.ldo = ldo;
     a.Tq = Tq;

@@ -27,9 +27,11 @@
 // so a lane holds its query's scores for 16 of each 32 keys, and its half-
 // wave partner (lane ^ 32) the other 16; the P operand is the lane's own
 // scores in register order, and the V^T operand lists the same keys in the
-// same slots (keys 4h..4h+3, then 8+4h..8+4h+3 of each 16).  V^T comes from
-// the library's transpose into the workspace ([hkv*128][Tk rounded up to 64],
-// zero past Tk).
+// same slots (keys 4h..4h+3, then 8+4h..8+4h+3 of each 16).  V is staged as
+// it lies in memory, one key per LDS row, and the V^T operand comes from
+// two transposing LDS reads (ds_read_b64_tr_b16: within each 16-lane group,
+// element e of lane 4a+b is element b of the 4-value chunk that lane 4e+a
+// addresses), so no transposed copy of V is made.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -50,14 +52,17 @@ constexpr int kD = 128;            // head dimension
 constexpr int kBQ = 128;           // query rows per workgroup
 constexpr int kBK = 64;            // keys per block
 constexpr int kKRow = kD * 2 + 16;   // bytes per staged K row (16 bytes of padding)
-// bytes per staged V^T row: 34 dwords, so the 8-byte fragment reads of 16
-// consecutive rows fall on distinct banks
-constexpr int kVRow = kBK * 2 + 8;
+// bytes per staged V row (one key): no padding; its eight 32-byte granules
+// are permuted by the row's index mod 4 (v_swz), so that the transposing
+// reads of four consecutive keys by 16 lanes, and of the two 16-column halves
+// by 32 lanes, fall on distinct banks
+constexpr int kVRow = kD * 2;
 constexpr int kThreads = 256;
-// LDS fragment reads kept this many reads ahead of the MFMAs that use them
-// (scores: K fragments; output: V^T fragments).  The compiler's own order ran
-// them one or two ahead; six measured 2-4% faster (same bytes).
-constexpr int KPF = 6, VPF = 6;
+// LDS fragments kept this many MFMAs ahead of the MFMAs that use them
+// (scores: K fragments, one read each; output: V^T fragments, two
+// transposing reads each).  The compiler's own order ran them one or two
+// ahead; six K and ten V^T fragments measured fastest (same bytes).
+constexpr int KPF = 6, VPF = 10;
 constexpr float kLazy = 8.0f;        // log2 headroom of the softmax reference max
 
 // Raw buffer over [base, base + bytes): a load whose per-lane offset lies
@@ -74,6 +79,14 @@ __device__ __forceinline__ void at_halves(float x, float &lo, float &hi) {
     hi = __uint_as_float(r[1]);
 }
 
+// granule permutation of staged V row r: granule g is stored at g ^ v_swz(r)
+// (0, 5, 2, 7 for r mod 4 = 0..3: distinct mod 4, and with their neighbours
+// g ^ 1 they cover all eight granules)
+__device__ __forceinline__ int v_swz(int r) { return ((r & 1) ? 5 : 0) ^ (r & 2); }
+
+typedef short at_i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) at_i16x4_t lds_i16x4_t;
+
 // fp32 -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t at_pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((at_f32x2_t){lo, hi}, at_bf16x2_t));
@@ -81,17 +94,15 @@ __device__ __forceinline__ uint32_t at_pack2(float lo, float hi) {
 
 __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t ks[kBK * kKRow];
-    __shared__ __attribute__((aligned(16))) uint8_t vs[kD * kVRow];
+    __shared__ __attribute__((aligned(16))) uint8_t vs[kBK * kVRow];
 
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int lq = lane & 31, hh = lane >> 5;
     // Sequence of this workgroup: one sequence, or (packed sequences) the
     // block's share of nqb query blocks x hq heads of sequence b, whose rows
-    // are [cu_q[b], cu_q[b+1]) and keys [cu_k[b], cu_k[b+1]), and whose V^T
-    // columns start at the sum of the earlier sequences' key counts rounded
-    // up to 64.
-    int64_t Tq = a.Tq, Tk = a.Tk, qs = 0, ks0 = 0, vcol = 0;
+    // are [cu_q[b], cu_q[b+1]) and keys [cu_k[b], cu_k[b+1]).
+    int64_t Tq = a.Tq, Tk = a.Tk, qs = 0, ks0 = 0;
     unsigned rem = blockIdx.x;
     if (a.cu_q) {
         if (__builtin_amdgcn_readfirstlane(*(volatile const int32_t *)a.err) != 0) return;  // lengths invalid
@@ -101,7 +112,6 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
         Tq = a.cu_q[b + 1] - qs;
         ks0 = a.cu_k[b];
         Tk = a.cu_k[b + 1] - ks0;
-        for (int j = 0; j < b; ++j) vcol += ((int64_t)(a.cu_k[j + 1] - a.cu_k[j]) + kBK - 1) / kBK * kBK;
     }
     // heads vary fastest and the query blocks run from the last one down, so
     // that under the causal mask the longest workgroups start first
@@ -114,6 +124,7 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
     const int64_t shift = Tk - Tq;  // bottom-right alignment of the causal mask
     const uint16_t *qbase = a.q + qs * a.ldq;
     const uint16_t *kbase0 = a.k + ks0 * a.ldk;
+    const uint16_t *vbase0 = a.v + ks0 * a.ldv;
     uint16_t *obase = a.out + qs * a.ldo;
 
     // this query's last visible key, and the keys the workgroup needs
@@ -137,45 +148,56 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
         for (int s = 0; s < 8; ++s) qf[s] = *(const at_bf16x8_t *)(qp + 16 * s);
     }
 
-    // staging: 1024 16-byte chunks of K (64 rows x 16) and of V^T (128 rows
-    // x 8) per block, four of each per thread, through raw buffers with
-    // 32-bit offsets.  The K chunk's whole offset (block row and key row) is
-    // the per-lane offset: only that part of a buffer address is checked
-    // against the buffer's size (the wave-uniform offset is not), so the
-    // rows of a last, partial block that lie past key Tk - 1 start at or
-    // beyond the buffer's end and read zeros instead of memory past the K
-    // view.  V^T offsets stay inside the rows of the workspace (its columns
-    // are padded to a multiple of 64 keys), so its block offset can be the
-    // wave-uniform part.
+    // staging: 1024 16-byte chunks of K and of V (64 key rows x 16 each)
+    // per block, four of each per thread, through raw buffers with 32-bit
+    // offsets.  A chunk's whole offset (block row and key row) is the
+    // per-lane offset: only that part of a buffer address is checked against
+    // the buffer's size (the wave-uniform offset is not), so the rows of a
+    // last, partial block that lie past key Tk - 1 start at or beyond the
+    // buffer's end and read zeros instead of memory past the K and V views
+    // (zero V rows keep the masked keys' products exactly 0).
     const at_rsrc_t kres =
         at_rsrc(kbase0 + kvh * kD, Tk > 0 ? (uint32_t)(((Tk - 1) * a.ldk + (a.hkv - kvh) * kD) * 2) : 0u);
-    const at_rsrc_t vres = at_rsrc(a.vt + (int64_t)kvh * kD * a.ldvt + vcol, (uint32_t)((kD * a.ldvt - vcol) * 2));
+    const at_rsrc_t vres =
+        at_rsrc(vbase0 + kvh * kD, Tk > 0 ? (uint32_t)(((Tk - 1) * a.ldv + (a.hkv - kvh) * kD) * 2) : 0u);
     uint32_t koff[4], voff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int idx = tid + kThreads * i;
         koff[i] = (uint32_t)(idx >> 4) * (uint32_t)a.ldk * 2u + (uint32_t)(idx & 15) * 16u;
-        voff[i] = (uint32_t)(idx >> 3) * (uint32_t)a.ldvt * 2u + (uint32_t)(idx & 7) * 16u;
+        voff[i] = (uint32_t)(idx >> 4) * (uint32_t)a.ldv * 2u + (uint32_t)(idx & 15) * 16u;
     }
     at_u32x4_t kr[4], vr[4];
     auto load_block = [&](int kb) {
-        const uint32_t kblk = (uint32_t)kb * kBK * (uint32_t)a.ldk * 2u, vs0 = (uint32_t)kb * kBK * 2u;
+        const uint32_t kblk = (uint32_t)kb * kBK * (uint32_t)a.ldk * 2u;
+        const uint32_t vblk = (uint32_t)kb * kBK * (uint32_t)a.ldv * 2u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             kr[i] = __builtin_amdgcn_raw_buffer_load_b128(kres, (int)(koff[i] + kblk), 0, 0);
-            vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, (int)voff[i], (int)vs0, 0);
+            vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, (int)(voff[i] + vblk), 0, 0);
         }
     };
     auto store_block = [&]() {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int idx = tid + kThreads * i;
-            *(at_u32x4_t *)(ks + (idx >> 4) * kKRow + (idx & 15) * 16) = kr[i];
-            uint8_t *vp = vs + (idx >> 3) * kVRow + (idx & 7) * 16;  // 8-byte aligned rows
-            *(at_u32x2_t *)vp = (at_u32x2_t){vr[i].x, vr[i].y};
-            *(at_u32x2_t *)(vp + 8) = (at_u32x2_t){vr[i].z, vr[i].w};
+            const int r = idx >> 4, c = idx & 15;  // key row, 16-byte chunk
+            *(at_u32x4_t *)(ks + r * kKRow + c * 16) = kr[i];
+            *(at_u32x4_t *)(vs + r * kVRow + (((c >> 1) ^ v_swz(r)) << 5) + ((c & 1) << 4)) = vr[i];
         }
     };
+    // V^T fragment addresses: lane l (16-lane group position L = l & 15)
+    // addresses key row 4 (l >> 5) + (L >> 2) of each 8-key group and the
+    // four values d = 32 dt + 16 ((l >> 4) & 1) + 4 (L & 3) + 0..3, so that it
+    // receives d = 32 dt + (l & 31) for four consecutive keys
+    uint32_t vrd[4];
+    {
+        const int L = lane & 15;
+        const int r = 4 * hh + (L >> 2);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            vrd[dt] = (uint32_t)(r * kVRow + (((2 * dt + ((lane >> 4) & 1)) ^ v_swz(r)) << 5) + 8 * (L & 3));
+    }
 
     at_f32x16_t oacc[4];
 #pragma unroll
@@ -298,19 +320,24 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
         for (int s2 = 0; s2 < 4; ++s2) {
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const uint8_t *row = vs + (dt * 32 + lq) * kVRow;
-                const at_u32x2_t lo = *(const at_u32x2_t *)(row + (s2 * 16 + 4 * hh) * 2);
-                const at_u32x2_t hi = *(const at_u32x2_t *)(row + (s2 * 16 + 8 + 4 * hh) * 2);
+                // keys 16 s2 + 4 hh + 0..3, then 16 s2 + 8 + 4 hh + 0..3
+                const at_u32x2_t lo = __builtin_bit_cast(
+                    at_u32x2_t,
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vs + vrd[dt] + s2 * 16 * kVRow)));
+                const at_u32x2_t hi = __builtin_bit_cast(
+                    at_u32x2_t,
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vs + vrd[dt] + (s2 * 16 + 8) * kVRow)));
                 const at_u32x4_t vv = {lo.x, lo.y, hi.x, hi.y};
                 oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(at_bf16x8_t, vv), pf[s2],
                                                                    oacc[dt], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, VPF, 0);
+        // (two transposing reads per V^T fragment)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * VPF, 0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (i + VPF < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (i + VPF < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_s_setprio(0);
     }
@@ -347,57 +374,6 @@ __global__ void __launch_bounds__(256) seqlens_check_kernel(const int32_t *cu_q,
     if (threadIdx.x == 0) *err = bad ? kErrSeqlens : 0;
 }
 
-// V^T of packed sequences: out[d][col] for the hkv*128 columns d of v; the
-// columns of sequence b start at off_b = sum over b' < b of its key count
-// rounded up to 64, and hold its keys in order, then zeros up to the next
-// multiple of 64 (and zeros past the last sequence, up to ldo).  One
-// workgroup per 64 output columns (all inside one sequence's range) and 64
-// rows d; LDS tile transpose, 16-byte loads and stores.
-__global__ void __launch_bounds__(256) vt_packed_kernel(const uint16_t *v, int64_t ldv, const int32_t *cu_k, int n,
-                                                        uint16_t *out, int64_t ldo, const int32_t *err) {
-    if (__builtin_amdgcn_readfirstlane(*(volatile const int32_t *)err) != 0) return;
-    __shared__ uint16_t tile[64][72];
-    const int64_t c0 = (int64_t)blockIdx.x * 64;
-    const int d0 = (int)blockIdx.y * 64;
-    // the sequence whose range holds c0
-    int64_t off = 0, ks = 0, len = 0;
-    bool found = false;
-    for (int b = 0; b < n; ++b) {
-        const int64_t l = (int64_t)cu_k[b + 1] - cu_k[b];
-        const int64_t span = (l + 63) / 64 * 64;
-        if (c0 < off + span) {
-            ks = cu_k[b];
-            len = l;
-            found = true;
-            break;
-        }
-        off += span;
-    }
-    const int t = (int)threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int ch = t + 256 * i;          // 512 chunks: 64 keys x 8 chunks of 8 d
-        const int kk = ch >> 3, dc = ch & 7;
-        const int64_t j = c0 - off + kk;     // key within the sequence
-        at_u32x4_t val = {0, 0, 0, 0};
-        if (found && j < len) val = *(const at_u32x4_t *)(v + (ks + j) * ldv + d0 + dc * 8);
-        const uint16_t *e = (const uint16_t *)&val;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) tile[dc * 8 + q][kk] = e[q];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int ch = t + 256 * i;          // 512 chunks: 64 rows d x 8 chunks of 8 columns
-        const int dd = ch >> 3, cc = ch & 7;
-        at_u32x4_t val;
-        uint16_t *e = (uint16_t *)&val;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) e[q] = tile[dd][cc * 8 + q];
-        *(at_u32x4_t *)(out + (int64_t)(d0 + dd) * ldo + c0 + cc * 8) = val;
-    }
-}
-
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
@@ -411,13 +387,6 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t stream) {
 hipError_t launch_seqlens_check(const int32_t *cu_q, const int32_t *cu_k, int n, int64_t Tq, int64_t Tk,
                                 int64_t max_q, int32_t *err, hipStream_t stream) {
     hipLaunchKernelGGL(seqlens_check_kernel, dim3(1), dim3(256), 0, stream, cu_q, cu_k, n, Tq, Tk, max_q, err);
-    return hipGetLastError();
-}
-
-hipError_t launch_vt_packed(const uint16_t *v, int64_t ldv, int kv_cols, const int32_t *cu_k, int n, uint16_t *out,
-                            int64_t ldo, const int32_t *err, hipStream_t stream) {
-    const dim3 grid((unsigned)(ldo / 64), (unsigned)(kv_cols / 64));
-    hipLaunchKernelGGL(vt_packed_kernel, grid, dim3(256), 0, stream, v, ldv, cu_k, n, out, ldo, err);
     return hipGetLastError();
 }
 

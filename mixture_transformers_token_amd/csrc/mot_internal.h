@@ -83,8 +83,8 @@ struct AttnArgs {
     int64_t ldq;
     const uint16_t *k;    // [Tk][ldk] bf16: kv heads of 128 columns
     int64_t ldk;
-    const uint16_t *vt;   // [hkv*128][ldvt] bf16: V transposed, zero past Tk
-    int64_t ldvt;         // multiple of 64, >= Tk
+    const uint16_t *v;    // [Tk][ldv] bf16: kv heads of 128 columns
+    int64_t ldv;
     uint16_t *out;        // [Tq][ldo] bf16
     int64_t ldo;
     int64_t Tq, Tk;
@@ -101,8 +101,6 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_seqlens_check(const int32_t *cu_q, const int32_t *cu_k, int n, int64_t Tq, int64_t Tk,
                                 int64_t max_q, int32_t *err, hipStream_t stream);
-hipError_t launch_vt_packed(const uint16_t *v, int64_t ldv, int kv_cols, const int32_t *cu_k, int n, uint16_t *out,
-                            int64_t ldo, const int32_t *err, hipStream_t stream);
 
 // Latent step (mot_latent.hip): chunk slots of one request, and the launches.
 int latent_chunks(int64_t max_rows);

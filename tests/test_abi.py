@@ -245,10 +245,9 @@ def _attn(**kw):
 
 
 def test_attention_workspace_bytes():
-    assert mot.attention_workspace_bytes(0, 4) == 0
-    assert mot.attention_workspace_bytes(1, 4) == 4 * 128 * 64 * 2
-    assert mot.attention_workspace_bytes(4096, 4) == 4 * 128 * 4096 * 2
-    assert mot.attention_workspace_bytes(4097, 1) == 128 * 4160 * 2
+    # V is read in place: the single-sequence call needs no workspace
+    for tk, hkv in ((0, 4), (1, 4), (4096, 4), (4097, 1)):
+        assert mot.attention_workspace_bytes(tk, hkv) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -269,14 +268,13 @@ def test_attention_workspace_bytes():
     (dict(ldk=128), INVALID),
     (dict(ldq=516), MISALIGNED),
     (dict(v=3 * A + 8), MISALIGNED),
-    (dict(ws=None), WORKSPACE),
-    (dict(wsb=2 * 128 * 128 * 2 - 2), WORKSPACE),
-    (dict(ws=6 * A + 8), MISALIGNED),
     (dict(out=A + 1024), INVALID),            # out overlaps q
     (dict(out=2 * A), INVALID),               # out overlaps k
-    (dict(ws=3 * A + 512), INVALID),          # workspace overlaps v
+    (dict(out=3 * A + 512), INVALID),         # out overlaps v
     # 2^20 keys at a 4096-column pitch: K past the 32-bit byte offsets
-    (dict(q=G, k=2 * G, v=3 * G, out=4 * G, ws=5 * G, Tk=1 << 20, ldk=4096, ldv=4096, wsb=1 << 32), SHAPE),
+    (dict(q=G, k=2 * G, v=3 * G, out=4 * G, Tk=1 << 20, ldk=4096, ldv=4096), SHAPE),
+    # the same for V alone (K at a 256-column pitch fits)
+    (dict(q=G, k=2 * G, v=3 * G, out=4 * G, Tk=1 << 20, ldk=256, ldv=4096), SHAPE),
 ])
 def test_attention_fails_closed(kw, code):
     assert _attn(**kw) == code
@@ -293,9 +291,10 @@ def _attn_varlen(**kw):
 
 
 def test_attention_varlen_workspace_bytes():
+    # the header with the lengths check's error word only (V is read in place)
     assert mot.attention_varlen_workspace_bytes(100, 0, 2) == 0
-    assert mot.attention_varlen_workspace_bytes(100, 3, 2) == 256 + 2 * 128 * 320 * 2
-    assert mot.attention_varlen_workspace_bytes(0, 1, 1) == 256 + 128 * 64 * 2
+    assert mot.attention_varlen_workspace_bytes(100, 3, 2) == 256
+    assert mot.attention_varlen_workspace_bytes(0, 1, 1) == 256
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -308,10 +307,10 @@ def test_attention_varlen_workspace_bytes():
     (dict(D=64), SHAPE),
     (dict(n=65537), SHAPE),
     (dict(ws=None), WORKSPACE),
-    (dict(wsb=256 + 2 * 128 * 320 * 2 - 2), WORKSPACE),
+    (dict(wsb=255), WORKSPACE),
     (dict(ws=6 * A + 16), MISALIGNED),
     (dict(out=A + 1024), INVALID),
-    (dict(ws=3 * A + 512), INVALID),
+    (dict(ws=3 * A + 256), INVALID),          # workspace overlaps v
 ])
 def test_attention_varlen_fails_closed(kw, code):
     assert _attn_varlen(**kw) == code

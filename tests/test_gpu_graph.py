@@ -80,16 +80,14 @@ def test_qk_norm_rope_graph():
 
 
 def test_joint_attention_graph():
-    """Both attention calls (V transpose + attention; the packed form with
-    its lengths check and packed V transpose) replay to the eager bytes."""
+    """Both attention calls (the packed form with its lengths check) replay
+    to the eager bytes."""
     T = 700
     qkv = dev(W.normal_bf16((T, W.QKV_DIM), 1320))
     q, k, v = qkv[:, :W.Q_DIM], qkv[:, W.Q_DIM:W.Q_DIM + W.KV_DIM], qkv[:, W.Q_DIM + W.KV_DIM:]
     ref = mot.joint_attention(q, k, v, W.N_Q_HEADS, W.N_K_HEADS, causal=True)
     out = torch.empty_like(ref)
-    ws = torch.empty(mot.attention_workspace_bytes(T, W.N_K_HEADS), dtype=torch.uint8, device="cuda")
-    _replays_match(lambda: mot.joint_attention(q, k, v, W.N_Q_HEADS, W.N_K_HEADS, causal=True, out=out,
-                                               workspace=ws), out, ref)
+    _replays_match(lambda: mot.joint_attention(q, k, v, W.N_Q_HEADS, W.N_K_HEADS, causal=True, out=out), out, ref)
     cu = dev(torch.from_numpy(W.cu_lengths([300, 0, 77, 323])))
     ref2, _ = mot.joint_attention_varlen(q, k, v, cu, cu, 323, W.N_Q_HEADS, W.N_K_HEADS, causal=True)
     out2 = torch.empty_like(ref2)
