@@ -383,7 +383,8 @@ def main():
     def c_backward(components):
         # routed backward of the QKV projection: dX = dY W_m on the
         # transposed weights (made once per weight update), and the generation
-        # set's dW over its 3788 rows (two transposes + one routed GEMM over T)
+        # set's dW over its 3788 rows (one kernel over dY and X as they lie;
+        # the contraction runs over all T rows, the und rows read as zeros)
         dyd = W.normal_bf16((T, N), 11).to(dev)
         wt = (mot.transpose(wud), mot.transpose(wgd))
         dx = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
@@ -399,7 +400,7 @@ def main():
             "dw_gen_us": round(s_dw * 1e6, 1), "dw_gen_TFLOP/s": round(f_dw / s_dw / 1e12, 1),
             "dw_gen_fp32_us": round(s_dw32 * 1e6, 1), "dw_gen_fp32_TFLOP/s": round(f_dw / s_dw32 / 1e12, 1),
             "dw_gen_rows": n_gen_rows(m),
-            "note": "dw_gen times include the two operand transposes (dY over all rows, X with und rows zeroed)"}
+            "note": "dw_gen: one mot_grad_w call (token-major operands, no transposes); flops count the gen rows"}
 
     wsq = mot.new_workspace(0, dev)
 

@@ -17,9 +17,9 @@
  * "mot_fused_add_rmsnorm" and "mot_qk_norm_rope" work items (section 5), the
  * routed GEMM's fp32 sums uncast (mot_routed_gemm_f32, for fp32 gradients), the
  * shared attention of both sets ("gen_joint_attention", section 5), and
- * the transpose that prepares the routed backward's operands (section 1:
- * Phase A trains the generation set, the frozen understanding operators still
- * pass dX back).
+ * the routed backward (section 1: Phase A trains the generation set, the
+ * frozen understanding operators still pass dX back): the transpose that
+ * prepares its operands and the weight gradient over token rows.
  *
  * Conventions shared by every call
  *  - bf16 tensors are passed as uint16_t bit patterns; all tensors are
@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 12
+#define MOT_ABI_VERSION 13
 
 typedef enum mot_status {
     MOT_OK = 0,
@@ -310,6 +310,32 @@ int mot_fused_add_rmsnorm(const uint16_t *x, uint16_t *residual,
 int mot_transpose_bf16(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t cols,
                        const uint8_t *modality, int keep, uint16_t *out, int64_t ld_out,
                        int64_t rows_pad, void *stream);
+
+/* Weight gradient of one set, from the operands as they lie in memory (no
+ * transposed copies): the generation-set dW of the routed backward (the RFC
+ * page, section 1: Phase A trains the generation expert), or the other set's
+ * with keep = 0.
+ *   out[n][k] = sum over rows t < T with modality[t] == keep of
+ *               dy[t][n] * x[t][k]
+ * in fp32, the rows folded in ascending order in 16-row MFMA steps over all
+ * T rows (rows of the other set, or with any other byte, count as zero rows,
+ * so the fold is the one mot_routed_gemm gives on mot_transpose_bf16's
+ * operands above, bit for bit), stored as bf16 (round to nearest even once)
+ * or, with out_f32 = 1, as the fp32 sums.
+ *   dy  [T][lddy] bf16, columns [0, N);  x [T][ldx] bf16, columns [0, K);
+ *   modality [T] bytes;  out [N][ldo] bf16 (fp32 when out_f32), columns
+ *   [0, K) written; must not overlap dy, x or modality.
+ *   K % 64 == 0, K <= MOT_MAX_DIM, N <= MOT_MAX_T, T <= MOT_MAX_T; lddy >= N,
+ *   ldx >= K, ldo >= K, all % 8 == 0; dy, x, out 16-byte aligned; keep and
+ *   out_f32 0 or 1.  The kernel addresses dy and x (their rows up to T
+ *   rounded up to 64, 256-column tiles) and out with 32-bit byte offsets:
+ *   larger extents are MOT_ERR_UNSUPPORTED_SHAPE.
+ * Errors: MOT_ERR_INVALID_ARG, MOT_ERR_UNSUPPORTED_SHAPE, MOT_ERR_MISALIGNED,
+ * MOT_ERR_DEVICE.  N == 0 or K == 0 is a no-op; T == 0 writes zeros (dy, x
+ * and modality may then be NULL).  Since ABI 13. */
+int mot_grad_w(const uint16_t *dy, int64_t lddy, const uint16_t *x, int64_t ldx,
+               const uint8_t *modality, int keep, int64_t T, int64_t N, int64_t K,
+               void *out, int64_t ldo, int out_f32, void *stream);
 
 /* Routed per-head QK RMSNorm, then the rotary embedding, in place on the
  * rows of the QKV projection's output: the "mot_qk_norm_rope" work item of

@@ -27,7 +27,7 @@ __all__ = [
     "flow_sde_step_logp", "RENORM", "routed_gemm_qk_norm_rope",
 ]
 
-ABI_VERSION = 12
+ABI_VERSION = 13
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
 WS_HEADER_BYTES = 256
 FLAG_PLAN_READY = 1
@@ -40,7 +40,7 @@ EXPORTS = (
     "mot_abi_version", "mot_status_string", "mot_workspace_bytes", "mot_routing_plan",
     "mot_routed_gemm", "mot_routed_gemm_swiglu", "mot_fused_add_rmsnorm", "mot_read_device_error",
     "mot_transpose_bf16", "mot_qk_norm_rope", "mot_routed_gemm_f32", "mot_attention_workspace_bytes",
-    "mot_joint_attention", "mot_attention_varlen_workspace_bytes", "mot_joint_attention_varlen",
+    "mot_joint_attention", "mot_attention_varlen_workspace_bytes", "mot_joint_attention_varlen", "mot_grad_w",
     "mot_modality_from_index_sets", "mot_routed_gemm_noalloc", "mot_latent_workspace_bytes",
     "mot_cfg_combine_renorm", "mot_flow_sde_step_logp", "mot_routed_gemm_qk_norm_rope",
 )
@@ -98,6 +98,8 @@ def lib():
     L.mot_joint_attention.restype = ctypes.c_int
     L.mot_joint_attention.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, I64, I64, ctypes.c_int, P,
                                       SZ, P]
+    L.mot_grad_w.restype = ctypes.c_int
+    L.mot_grad_w.argtypes = [P, I64, P, I64, P, ctypes.c_int, I64, I64, I64, P, I64, ctypes.c_int, P]
     L.mot_attention_varlen_workspace_bytes.restype = SZ
     L.mot_attention_varlen_workspace_bytes.argtypes = [I64, I64, I64]
     L.mot_joint_attention_varlen.restype = ctypes.c_int
@@ -452,21 +454,24 @@ def routed_gemm_dx(dy, w_und, w_gen, modality, wt=None, out=None, workspace=None
 def grad_w(dy, x, modality, keep=1, out_dtype=torch.bfloat16):
     """dW[n][k] = sum over rows t with modality[t] == keep of dY[t][n] * X[t][k]
     (fp32, rows folded in ascending order in 16-row chunks), as [N, K] in
-    out_dtype: bf16 (one cast) or fp32 (the sums themselves)."""
+    out_dtype: bf16 (one cast) or fp32 (the sums themselves).  One kernel
+    reads dy and x as they lie (mot_grad_w); the same bytes as routed_gemm on
+    their transposes (transpose, with x's other-set rows zeroed)."""
     _req(dy, "dy", torch.bfloat16, 2)
     _req(x, "x", torch.bfloat16, 2)
+    _req(modality, "modality", torch.uint8, 1)
     T, N = dy.shape
-    if x.shape[0] != T:
-        raise ValueError("dy and x must have the same rows")
-    Tp = _pad64(max(T, 1))
-    dyt = transpose(dy, rows_pad=Tp)
-    xt = transpose(x, modality=modality, keep=keep, rows_pad=Tp)
-    sets = torch.zeros(N, dtype=torch.uint8, device=dy.device)
-    if out_dtype == torch.float32:
-        return routed_gemm_f32(dyt, xt, xt, sets)
-    if out_dtype != torch.bfloat16:
+    K = x.shape[1]
+    if x.shape[0] != T or modality.shape[0] != T:
+        raise ValueError("dy, x and modality must have the same rows")
+    if out_dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("grad_w: out_dtype must be torch.bfloat16 or torch.float32")
-    return routed_gemm(dyt, xt, xt, sets)
+    f32 = out_dtype == torch.float32
+    out = torch.empty((N, K), dtype=out_dtype, device=dy.device)
+    st = lib().mot_grad_w(_ptr(dy), _rows(dy, "dy"), _ptr(x), _rows(x, "x"), _ptr(modality.contiguous()),
+                          int(keep), T, N, K, _ptr(out), _rows(out, "out"), 1 if f32 else 0, _stream(dy.device))
+    _check(st, "mot_grad_w")
+    return out
 
 
 def qk_norm_rope(qkv, n_q_heads, n_k_heads, modality, q_norm, k_norm, positions, cos_table, sin_table,

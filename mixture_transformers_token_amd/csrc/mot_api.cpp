@@ -466,6 +466,57 @@ int mot_transpose_bf16(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t 
                : MOT_ERR_DEVICE;
 }
 
+int mot_grad_w(const uint16_t *dy, int64_t lddy, const uint16_t *x, int64_t ldx, const uint8_t *modality,
+               int keep, int64_t T, int64_t N, int64_t K, void *out, int64_t ldo, int out_f32, void *stream) {
+    if (T < 0 || N < 0 || K < 0 || (keep != 0 && keep != 1) || (out_f32 != 0 && out_f32 != 1))
+        return MOT_ERR_INVALID_ARG;
+    if (N == 0 || K == 0) return MOT_OK;
+    if (!out || (T > 0 && (!dy || !x || !modality))) return MOT_ERR_INVALID_ARG;
+    if (T > MOT_MAX_T || N > MOT_MAX_T || K % 64 || K > MOT_MAX_DIM) return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (lddy < N || ldx < K || ldo < K) return MOT_ERR_INVALID_ARG;
+    if (lddy % 8 || ldx % 8 || ldo % 8) return MOT_ERR_MISALIGNED;
+    if (!aligned16(dy) || !aligned16(x) || !aligned16(out)) return MOT_ERR_MISALIGNED;
+    const int64_t esz = out_f32 ? 4 : 2;
+    if (T == 0) dy = x = nullptr, modality = nullptr;  // nothing is read
+    const int64_t dy_bytes = T > 0 ? ((T - 1) * lddy + N) * 2 : 0;
+    const int64_t x_bytes = T > 0 ? ((T - 1) * ldx + K) * 2 : 0;
+    const int64_t o_bytes = ((N - 1) * ldo + K) * esz;
+    // byte offsets the kernel forms: token rows up to T rounded up to 64,
+    // columns up to the last 256-column tile's end (and an out-of-range
+    // sentinel just below 2^32 for the rows it drops)
+    const int64_t tp = round_up(T > 0 ? T : 1, 64);
+    const int64_t lim = (int64_t(1) << 32) - 256;
+    if ((tp * lddy + round_up(N, 256)) * 2 >= lim || (tp * ldx + round_up(K, 256)) * 2 >= lim ||
+        o_bytes >= (int64_t(1) << 32))
+        return MOT_ERR_UNSUPPORTED_SHAPE;
+    if (overlaps(out, o_bytes, dy, dy_bytes) || overlaps(out, o_bytes, x, x_bytes) ||
+        overlaps(out, o_bytes, modality, T))
+        return MOT_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(s);
+    if (!guard.ok()) return MOT_ERR_DEVICE;
+    mot::GemmArgs a;
+    a.x = dy;
+    a.ldx = lddy;
+    a.w_und = x;
+    a.w_gen = x;
+    a.ldw = ldx;
+    a.y = out;
+    a.ldy = ldo;
+    a.modality = modality;
+    a.keep = keep;
+    a.t_tok = (int)T;
+    a.T = N;
+    a.K = (int)tp;
+    a.N = (int)K;
+    a.wrows = (int)K;
+    a.x_bytes = (uint32_t)dy_bytes;
+    a.w_bytes = (uint32_t)x_bytes;
+    a.y_bytes = (uint32_t)o_bytes;
+    a.out_f32 = out_f32;
+    return mot::launch_grad_w(a, s) == hipSuccess ? MOT_OK : MOT_ERR_DEVICE;
+}
+
 size_t mot_attention_workspace_bytes(int64_t Tk, int64_t n_kv_heads) {
     return attn_ws_bytes(Tk, n_kv_heads);
 }

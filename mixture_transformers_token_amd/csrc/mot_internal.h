@@ -58,6 +58,12 @@ struct GemmArgs {
     const uint16_t *cos_t = nullptr, *sin_t = nullptr;  // [n_pos][64] bf16
     int n_pos = 0;
     float qk_eps = 0.0f;
+    // Weight gradient (launch_grad_w): token-major operands, x = dY [t_tok][ldx]
+    // and the weight side X [t_tok][ldw]; X rows whose modality byte is not
+    // keep count as zeros; K = t_tok rounded up to 64.
+    int64_t ldw = 0;
+    int keep = 1;
+    int t_tok = 0;
 };
 
 // Routed per-head QK RMSNorm + rotary embedding, in place on QKV rows.
@@ -97,6 +103,11 @@ struct AttnArgs {
     int nqb = 0;                   // query blocks of 128 per sequence (longest)
     const int32_t *err = nullptr;  // lengths check result; the kernel exits if non-zero
 };
+
+// dW[n][k] = sum over token rows t with modality[t] == keep of dY[t][n] X[t][k]
+// (GemmArgs: x = dY, w_und = X, y = dW, T = rows n, K = tokens rounded up to
+// 64, N = wrows = columns k; out_f32 as for the GEMM).
+hipError_t launch_grad_w(const GemmArgs &a, hipStream_t stream);
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_seqlens_check(const int32_t *cu_q, const int32_t *cu_k, int n, int64_t Tq, int64_t Tk,

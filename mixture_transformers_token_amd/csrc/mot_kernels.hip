@@ -1251,11 +1251,28 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
 // instruction, which takes the memory system about twice as long to absorb
 // when every workgroup stores its tile at the same time.  fp32 output and
 // 224-row tiles store straight from the accumulators.
-template <bool SWIGLU, bool F32 = false, bool QK = false, int BN = kBigN, int BM = kBigM>
+// TOK: token-major operands (the weight gradient): the contraction runs over
+// token rows, both operands are read as they lie in memory ([token][column],
+// a.x = dY with pitch a.ldx, the weight side = X with pitch a.ldw), and the
+// tile's rows are the output rows of the x side (its row list the identity).
+// A stage slot then holds 64 token rows of 256 columns (512 bytes each, their
+// 32-byte granules permuted by the row index mod 4: granule g at
+// g ^ tok_swz(r)), filled by LDS-DMA two token rows per instruction, and a
+// fragment (eight consecutive tokens of one column) is two transposing reads
+// (ds_read_b64_tr_b16: within each 16-lane group, element e of lane 4a+b is
+// element b of the 4-value chunk that lane 4e+a addresses).  The k order and
+// the MFMA operands are those of the same product on transposed copies.
+// Weight-side token rows whose modality byte is not a.keep, and rows past
+// a.t_tok, read as zeros (out-of-range buffer offsets).
+__device__ __forceinline__ int tok_swz(int r) { return ((r & 1) ? 5 : 0) ^ (r & 2); }
+constexpr int kTokRowBytes = 2 * kBigN;  // 256 bf16 columns
+
+template <bool SWIGLU, bool F32 = false, bool QK = false, int BN = kBigN, int BM = kBigM, bool TOK = false>
 __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint8_t *const (&hs)[5],
                                          const int32_t *s_rows, const int tid, lds_u8 *const eb,
                                          int32_t *qk_p = nullptr) {
     static_assert(!(SWIGLU && F32), "fp32 output: plain GEMM only");
+    static_assert(!TOK || (!SWIGLU && !QK && BN == kBigN && BM == kBigM), "token-major operands: plain 256 x 256");
     static_assert(!QK || (!SWIGLU && !F32), "fused QK epilogue: plain bf16 GEMM only");
     constexpr uint32_t kOutBytes = F32 ? 4u : 2u;  // bytes per output element
     static_assert(BN == kBigN || (BN == kWideN && !SWIGLU && !F32 && !QK), "wide tiles: plain bf16 GEMM only");
@@ -1285,6 +1302,19 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
     const rsrc_t wr = make_rsrc(ti.set ? a.w_gen : a.w_und, a.w_bytes);
 
     uint32_t xoff[XL], woff[WL];
+    if constexpr (TOK) {
+        // instruction j: token row r = 16 wave + 2 j + (lane >> 5) of the
+        // stage; the lane's 16-byte position p = lane & 31 holds the row's
+        // chunk p ^ 2 tok_swz(r), columns ti.first (x) or ti.wrow0 (w) +
+        // 8 (p ^ 2 tok_swz(r))
+#pragma unroll
+        for (int j = 0; j < XL; ++j) {
+            const int r = wave * 16 + 2 * j + (lane >> 5);
+            const uint32_t c = (uint32_t)((lane & 31) ^ (tok_swz(r) << 1));
+            xoff[j] = (uint32_t)r * (uint32_t)(a.ldx * 2) + ((uint32_t)ti.first + 8u * c) * 2u;
+            woff[j] = (uint32_t)r * (uint32_t)(a.ldw * 2) + ((uint32_t)ti.wrow0 + 8u * c) * 2u;
+        }
+    } else {
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
         const int r = wave * (BM / 4) + j * 8 + (lane >> 3);
@@ -1304,6 +1334,24 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
         }
         woff[j] = (uint32_t)wrow * (uint32_t)(K * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
     }
+    }
+    // TOK: the weight-side rows' modality bytes, one 16-row group per wave
+    // and stage (lane l reads row 16 wave + (l & 15) of the stage): loaded at
+    // the start of a stage for the stage two ahead, turned into a row mask
+    // (bit q: row 16 wave + q is kept) after that stage's barrier, by which
+    // the load has landed (the DMA issued after it is what remains in flight)
+    const rsrc_t mr = make_rsrc(a.modality, TOK ? (uint32_t)a.t_tok : 0u);
+    uint32_t tflag = 0;
+    uint32_t tmask = 0;
+    auto flag_load = [&](int kb) {
+        if constexpr (TOK)
+            tflag = __builtin_amdgcn_raw_buffer_load_b8(
+                mr, (int)((uint32_t)kb * kBK + (uint32_t)(wave * 16 + (lane & 15))), 0, 0);
+    };
+    auto flag_mask = [&]() {
+        if constexpr (TOK)
+            tmask = (uint32_t)__builtin_amdgcn_ballot_w64(tflag == (uint32_t)a.keep) & 0xffffu;
+    };
     // the fused QK epilogue's row and position (the ring overwrites the
     // row list during the main loop)
     QkRow qkr{0, 0};
@@ -1322,6 +1370,23 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
 
     // operand o (0 = A, 1 = W) of k-block kb into slot s, instructions [lo, hi)
     auto issue = [&](int o, int kb, int s, int lo, int hi) {
+        if constexpr (TOK) {
+            const uint32_t tb = (uint32_t)kb * kBK;  // first token row of the stage
+#pragma unroll
+            for (int j = 0; j < DL; ++j) {
+                if (j < lo || j >= hi) continue;
+                uint8_t *dst = hs[s] + (wave * 16 + 2 * j) * kTokRowBytes;
+                if (o == 0) {
+                    dma16(xr, xoff[j] + tb * (uint32_t)(a.ldx * 2), 0, dst);
+                } else {
+                    // a dropped row reads an offset past the buffer's end
+                    // (zeros; the extents stay below 2^32 - 256)
+                    const bool kept = (tmask >> (2 * j + (lane >> 5))) & 1u;
+                    dma16(wr, kept ? woff[j] + tb * (uint32_t)(a.ldw * 2) : 0xffffff00u, 0, dst);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < DL; ++j) {
             if (j < lo || j >= hi) continue;
@@ -1345,15 +1410,52 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
 
     const int lsw = swz(lane & 15);
     uint32_t xq[4], wq[4];
+    if constexpr (TOK) {
+        // 32-column block cb of the tile: lane l (L = l & 15) addresses token
+        // row 8 (l >> 5) + (L >> 2) (+ 16 q, + 4 for the second half) and the
+        // four columns 32 cb + 16 ((l >> 4) & 1) + 4 (L & 3), and receives
+        // column 32 cb + (l & 31) of four consecutive token rows
+        const int L = lane & 15;
+        const int tr = 8 * khalf + (L >> 2);
+        const int gs = ((lane >> 4) & 1) ^ tok_swz(tr);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t base = (uint32_t)(tr * kTokRowBytes + 8 * (L & 3));
+            xq[q] = base + (uint32_t)(((2 * (wm * MJ + q)) ^ gs) << 5);
+            wq[q] = base + (uint32_t)(((2 * (wn * MI + q)) ^ gs) << 5);
+        }
+    } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const uint32_t pos = (uint32_t)(((2 * q + khalf) ^ lsw) * 16);
         xq[q] = (uint32_t)((wm * WM + rsel) * kRowBytes) + pos;
         wq[q] = (uint32_t)((wn * WN + rsel) * kRowBytes) + pos;
     }
+    }
+    // TOK: eight consecutive token rows of one column block (xq / wq index
+    // the block, q the 16-row k-step)
+    auto tok_frag = [&](const uint8_t *sl, uint32_t off, int q) -> bf16x8_t {
+        typedef short i16x4_t __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+        const u32x2_t lo = __builtin_bit_cast(
+            u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(sl + off + q * 16 * kTokRowBytes)));
+        const u32x2_t hi = __builtin_bit_cast(
+            u32x2_t,
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(sl + off + (q * 16 + 4) * kTokRowBytes)));
+        return __builtin_bit_cast(bf16x8_t, (u32x4_t){lo.x, lo.y, hi.x, hi.y});
+    };
     // fragments of k-step q of the stage whose A rows are in slot sa and W rows in sw
     auto load_frags = [&](int sa, int sw, int q, bf16x8_t (&fa)[MI], bf16x8_t (&fb)[MJ]) {
         const uint8_t *xs = hs[sa], *ws = hs[sw];
+        if constexpr (TOK) {
+            static_assert(!TOK || (MI == 4 && MJ == 4), "token-major tiles: 4 x 4 blocks per wave");
+            fa[0] = tok_frag(ws, wq[0], q);
+#pragma unroll
+            for (int j = 0; j < MJ; ++j) fb[j] = tok_frag(xs, xq[j], q);
+#pragma unroll
+            for (int i = 1; i < MI; ++i) fa[i] = tok_frag(ws, wq[i], q);
+            return;
+        }
         fa[0] = *(const bf16x8_t *)(ws + wq[q]);
 #pragma unroll
         for (int j = 0; j < MJ; ++j) fb[j] = *(const bf16x8_t *)(xs + xq[q] + j * 32 * kRowBytes);
@@ -1372,7 +1474,7 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
     auto interleave = [&]() {
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
-            if (i < MI + MJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            if (i < MI + MJ) __builtin_amdgcn_sched_group_barrier(0x100, TOK ? 2 : 1, 0);  // DS read
             if (i % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (DMA)
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
         }
@@ -1387,6 +1489,7 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
         constexpr int sa = (2 * jm) % 5, sw = (2 * jm + 1) % 5;            // this stage
         constexpr int na = (2 * jm + 2) % 5, nw = (2 * jm + 3) % 5;        // next stage
         constexpr int a2 = (2 * jm + 4) % 5, w2 = (2 * jm + 5) % 5;        // A(j+2), W(j+2)
+        flag_load(min(kt + 2, nk - 1));             // TOK: modality of stage j+2
         load_frags(sa, sw, 1, fa1, fb1);
         issue(1, min(kt + 1, nk - 1), nw, HW, WL);  // W(j+1), second half
         mfmas(fa0, fb0);
@@ -1406,6 +1509,7 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
         wait_vm_lgkm0<XL>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
+        flag_mask();
         // Past the end the refills re-read the final k-block into freed
         // slots, and the first fragments of a stage that does not exist are
         // read from a stale, in-bounds slot.
@@ -1418,8 +1522,18 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
 
     // prologue: A0, W0, A1, W1 into slots 0..3 (slot 4 holds the row list
     // until every wave has passed the barrier below)
+    if constexpr (TOK) {
+        flag_load(0);
+        wait_vm_lgkm0<0>();
+        flag_mask();
+    }
     issue(0, 0, 0, 0, XL);
     issue(1, 0, 1, 0, WL);
+    if constexpr (TOK) {
+        flag_load(min(1, nk - 1));
+        wait_vm_lgkm0<0>();
+        flag_mask();
+    }
     issue(0, min(1, nk - 1), 2, 0, XL);
     issue(1, min(1, nk - 1), 3, 0, WL);
     wait_vm_lgkm0<XL + WL>();
@@ -1714,6 +1828,50 @@ gemm_kernel(GemmArgs a) {
             run_tile<kSmallM, kSmallN, 4, SWIGLU, PRO, QK>(a, ti, xb, wb, eb, s_rows, s_nw, tid, qk_p);
         }
     }
+}
+
+// ============================================================================
+// Weight gradient over token-major operands
+// ============================================================================
+//
+// dW_set[n][k] = sum over the pack's rows t of that set of dY[t][n] X[t][k]:
+// one 256 x 256 output tile per workgroup (n rows from dY's columns, k
+// columns from X's), the contraction over all token rows in blocks of 64
+// (the rows of the other set read as zeros), fp32 accumulation in ascending
+// 16-row MFMA steps, stored as bf16 (one rounding) or as the fp32 sums.  The
+// big-tile ring with token-major staging (run_big5<..., TOK>): the operands
+// are read where they lie, with no transposed copies.  Tiles are numbered
+// in groups of four k tiles over all n tiles (as the GEMM's big tiles), and
+// the XCD remap gives each XCD a contiguous range of them.
+template <bool F32>
+__global__ void __launch_bounds__(kThreads, 1) grad_w_kernel(GemmArgs a) {
+    constexpr int kArrayBytes = kBigM * kRowBytes;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kArrayBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kArrayBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[kArrayBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[kArrayBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds4[kArrayBytes];
+    int32_t *const s_rows = (int32_t *)lds4;
+    const int grid = (int)gridDim.x;
+    const int t = xcd_remap((int)blockIdx.x, grid);
+    const int nmb = cdiv((int)a.T, kBigM), nwt = cdiv(a.wrows, kBigN);
+    constexpr int GN = 4;
+    const int g = t / (GN * nmb);
+    const int gn = min(nwt - g * GN, GN);
+    const int in = t - g * GN * nmb;
+    Tile ti;
+    ti.set = 0;
+    ti.first = (in / gn) * kBigM;
+    ti.count = min(kBigM, (int)a.T - ti.first);
+    ti.wrow0 = (g * GN + in % gn) * kBigN;
+    ti.big = true;
+    if (ti.count <= 0 || ti.wrow0 >= a.wrows) return;  // uniform (grid = whole tiles)
+    for (int i = (int)threadIdx.x; i < kBigM; i += kThreads) s_rows[i] = ti.first + i;
+    const int wave_id = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    lds_u8 *const eb = (lds_u8 *)(wave_id == 0 ? lds0 : wave_id == 1 ? lds1 : wave_id == 2 ? lds2 : lds3);
+    uint8_t *const hs[5] = {lds0, lds1, lds2, lds3, lds4};
+    __syncthreads();
+    run_big5<false, F32, false, kBigN, kBigM, true>(a, ti, hs, s_rows, (int)threadIdx.x, eb);
 }
 
 // ============================================================================
@@ -2284,6 +2442,16 @@ hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t
                        hipStream_t stream) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, modality, (int)T,
                        hdr, perm);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_w(const GemmArgs &a, hipStream_t stream) {
+    const int64_t tiles = (a.T + kBigM - 1) / kBigM * ((a.wrows + kBigN - 1) / kBigN);
+    if (tiles <= 0) return hipSuccess;
+    if (a.out_f32)
+        hipLaunchKernelGGL(grad_w_kernel<true>, dim3((unsigned)tiles), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(grad_w_kernel<false>, dim3((unsigned)tiles), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

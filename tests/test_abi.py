@@ -280,6 +280,39 @@ def test_attention_fails_closed(kw, code):
     assert _attn(**kw) == code
 
 
+def _grad_w(**kw):
+    args = dict(dy=A, lddy=256, x=2 * A, ldx=128, m=3 * A, keep=1, T=100, N=256, K=128, out=4 * A, ldo=128,
+                f32=0)
+    args.update(kw)
+    return mot.lib().mot_grad_w(args["dy"], args["lddy"], args["x"], args["ldx"], args["m"], args["keep"],
+                                args["T"], args["N"], args["K"], args["out"], args["ldo"], args["f32"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID),
+    (dict(N=-1), INVALID),
+    (dict(keep=2), INVALID),
+    (dict(f32=2), INVALID),
+    (dict(N=0, dy=None, x=None, m=None, out=None), OK),   # empty output: a no-op
+    (dict(K=0), OK),
+    (dict(out=None), INVALID),
+    (dict(dy=None), INVALID),
+    (dict(m=None), INVALID),
+    (dict(K=96, ldx=96, ldo=96), SHAPE),                  # K % 64 != 0
+    (dict(T=(1 << 24) + 1), SHAPE),
+    (dict(lddy=128), INVALID),                            # narrower than N
+    (dict(ldo=64), INVALID),
+    (dict(lddy=260), MISALIGNED),
+    (dict(x=2 * A + 8), MISALIGNED),
+    (dict(out=2 * A + 1024), INVALID),                    # out overlaps x
+    (dict(out=3 * A), INVALID),                           # out overlaps modality
+    # 2^20 rows at a 4096-column pitch: dY past the 32-bit byte offsets
+    (dict(dy=G, x=2 * G, m=3 * G, out=4 * G, T=1 << 20, lddy=4096), SHAPE),
+])
+def test_grad_w_fails_closed(kw, code):
+    assert _grad_w(**kw) == code
+
+
 def _attn_varlen(**kw):
     args = dict(q=A, ldq=512, k=2 * A, ldk=256, v=3 * A, ldv=256, out=4 * A, ldo=512, cq=5 * A, ck=5 * A + 64,
                 n=3, Tq=64, Tk=100, maxq=64, hq=4, hkv=2, D=128, causal=1, ws=6 * A, wsb=1 << 20)

@@ -96,6 +96,42 @@ def test_grad_w_qkv_shape_sampled():
     _grad_parity(4096, W.QKV_DIM, W.HIDDEN, m, base=540, cols=np.sort(cols))
 
 
+def _grad_w_transposed(dy, x, m, keep, f32):
+    """The same weight gradient as a routed GEMM over the tokens, on
+    transposed copies (x's other-set rows zeroed, both padded to 64 rows)."""
+    T, N = dy.shape
+    Tp = max(64, (T + 63) // 64 * 64)
+    dyt = mot.transpose(dy, rows_pad=Tp)
+    xt = mot.transpose(x, modality=m, keep=keep, rows_pad=Tp)
+    sets = torch.zeros(N, dtype=torch.uint8, device=dy.device)
+    return (mot.routed_gemm_f32 if f32 else mot.routed_gemm)(dyt, xt, xt, sets)
+
+
+@pytest.mark.parametrize("T,N,K,keep,pitch", [(0, 64, 64, 1, 0), (1, 64, 64, 1, 0), (63, 200, 64, 1, 8),
+                                              (100, 256, 320, 0, 0), (333, 300, 256, 1, 4),
+                                              (1101, 520, 192, 1, 0), (4096, 4608, 3584, 1, 0)])
+@pytest.mark.parametrize("f32", [False, True])
+def test_grad_w_is_the_transposed_product(T, N, K, keep, pitch, f32):
+    """mot_grad_w reads dY and X where they lie (token-major tiles, transposing
+    LDS reads) and gives, bit for bit, the routed GEMM's bytes on their
+    transposes: the same 16-row MFMA steps in the same order, the other
+    set's rows zero.  Ragged row counts, padded row pitches, keep = 0 and
+    invalid modality bytes (dropped like the other set's rows) included."""
+    base = 560 + T + N
+    dyb = W.normal_bf16((T, N + pitch), W.seed_of(base, 1))
+    x = W.normal_bf16((T, K), W.seed_of(base, 4))
+    m = W.pattern(T) if T else np.zeros(0, np.uint8)
+    if T > 7:
+        m[3::7] = 9  # neither set: dropped by both forms
+    dy_d, x_d, m_d = dev(dyb)[:, :N], dev(x), dev(torch.from_numpy(m))
+    got = mot.grad_w(dy_d, x_d, m_d, keep=keep, out_dtype=torch.float32 if f32 else torch.bfloat16)
+    want = _grad_w_transposed(dy_d, x_d, m_d, keep, f32)
+    torch.cuda.synchronize()
+    assert tuple(got.shape) == (N, K)
+    view = torch.int32 if f32 else torch.int16
+    assert torch.equal(got.view(view), want.view(view)), f"T={T} N={N} K={K} keep={keep} f32={f32}"
+
+
 def test_dx_rows_batch_invariant():
     """dX runs the forward's routed GEMM: a row's bytes do not depend on the
     pack around it (probe rows alone, inside a larger mixed pack, permuted)."""
