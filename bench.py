@@ -246,7 +246,7 @@ def main():
     n_und, n_gen = int((m == 0).sum()), int((m == 1).sum())
     traffic = measured_traffic()
     roofline = {
-        "kernel": "gemm_kernel<false,false,true,false,false,false,false,false> (routed QKV GEMM, in-kernel segment list)",
+        "kernel": "gemm_kernel<false,false,true,false,false,false,false,false,false> (routed QKV GEMM, in-kernel segment list)",
         "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
         "avg_kernel_us": round(gemm_s * 1e6, 2),
@@ -381,21 +381,24 @@ def main():
                                             "TFLOP/s": round(flops / s_pro / 1e12, 1)}
 
     def c_backward(components):
-        # routed backward of the QKV projection: dX = dY W_m on the
-        # transposed weights (made once per weight update), and the generation
+        # routed backward of the QKV projection: dX = dY W_m with the weights
+        # read as they lie (and, for comparison, on transposed weights made
+        # once per weight update), and the generation
         # set's dW over its 3788 rows (one kernel over dY and X as they lie;
         # the contraction runs over all T rows, the und rows read as zeros)
         dyd = W.normal_bf16((T, N), 11).to(dev)
         wt = (mot.transpose(wud), mot.transpose(wgd))
         dx = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
-        s_dx = time_component(lambda: mot.routed_gemm_dx(dyd, wud, wgd, md, wt=wt, out=dx, workspace=ws),
-                              iters, stream)
+        s_dx = time_component(lambda: mot.routed_gemm_dx(dyd, wud, wgd, md, out=dx, workspace=ws), iters, stream)
+        s_dx_wt = time_component(lambda: mot.routed_gemm_dx(dyd, wud, wgd, md, wt=wt, out=dx, workspace=ws),
+                                 iters, stream)
         s_wt = time_component(lambda: mot.transpose(wgd), iters, stream)
         s_dw = time_component(lambda: mot.grad_w(dyd, xd, md, keep=1), 10, stream)
         s_dw32 = time_component(lambda: mot.grad_w(dyd, xd, md, keep=1, out_dtype=torch.float32), 10, stream)
         f_dw = 2.0 * n_gen_rows(m) * N * K
         components["qkv_backward_T4096"] = {
             "dx_us": round(s_dx * 1e6, 1), "dx_TFLOP/s": round(flops / s_dx / 1e12, 1),
+            "dx_pretransposed_weights_us": round(s_dx_wt * 1e6, 1),
             "weight_transpose_us": round(s_wt * 1e6, 1),
             "dw_gen_us": round(s_dw * 1e6, 1), "dw_gen_TFLOP/s": round(f_dw / s_dw / 1e12, 1),
             "dw_gen_fp32_us": round(s_dw32 * 1e6, 1), "dw_gen_fp32_TFLOP/s": round(f_dw / s_dw32 / 1e12, 1),

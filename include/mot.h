@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 13
+#define MOT_ABI_VERSION 14
 
 typedef enum mot_status {
     MOT_OK = 0,
@@ -310,6 +310,24 @@ int mot_fused_add_rmsnorm(const uint16_t *x, uint16_t *residual,
 int mot_transpose_bf16(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t cols,
                        const uint8_t *modality, int keep, uint16_t *out, int64_t ld_out,
                        int64_t rows_pad, void *stream);
+
+/* Routed input gradient with the forward's weights as they lie: the dX of
+ * the routed backward (the RFC page, section 1: the frozen understanding
+ * operators still pass dX back), with no transposed copy of either set.
+ *   dx[t][k] = bf16_rne( fp32 sum over n of dy[t][n] * W_{modality[t]}[n][k] )
+ * the n in ascending 16-step MFMA chunks: the k order, and so the bytes, of
+ * mot_routed_gemm(dy, W_und^T, W_gen^T) (W^T from mot_transpose_bf16).
+ *   dy [T][lddy] bf16, columns [0, N); w_und, w_gen [N][K] bf16 (nn.Linear
+ *   layout of the forward y = x W^T, pitch K); dx [T][lddx] bf16, columns
+ *   [0, K) written; N % 64 == 0, K % 64 == 0.
+ *   flags: MOT_FLAG_PLAN_READY only.  Every row block runs as a 256 x 256
+ *   tile (partial blocks included).
+ * Modality bytes, workspace, plan, error word and the other errors as
+ * mot_routed_gemm (with its K the contraction length N here and its N the
+ * output width K).  Since ABI 14. */
+int mot_routed_gemm_dx(const uint16_t *dy, int64_t lddy, const uint16_t *w_und, const uint16_t *w_gen,
+                       const uint8_t *modality, uint16_t *dx, int64_t lddx, int64_t T, int64_t N, int64_t K,
+                       void *workspace, size_t workspace_bytes, unsigned flags, void *stream);
 
 /* Weight gradient of one set, from the operands as they lie in memory (no
  * transposed copies): the generation-set dW of the routed backward (the RFC

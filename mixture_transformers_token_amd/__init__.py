@@ -9,7 +9,7 @@ Functions mirror the C ABI:
   modality_from_index_sets, routing_plan, routed_gemm, routed_gemm_f32, routed_gemm_swiglu,
   fused_add_rmsnorm, transpose, qk_norm_rope, joint_attention,
   joint_attention_varlen, read_device_error,
-  workspace_bytes, abi_version; routed_gemm_dx and grad_w compose them.
+  workspace_bytes, abi_version, routed_gemm_dx, grad_w.
 """
 from __future__ import annotations
 
@@ -27,7 +27,7 @@ __all__ = [
     "flow_sde_step_logp", "RENORM", "routed_gemm_qk_norm_rope",
 ]
 
-ABI_VERSION = 13
+ABI_VERSION = 14
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmot.so")
 WS_HEADER_BYTES = 256
 FLAG_PLAN_READY = 1
@@ -41,6 +41,7 @@ EXPORTS = (
     "mot_routed_gemm", "mot_routed_gemm_swiglu", "mot_fused_add_rmsnorm", "mot_read_device_error",
     "mot_transpose_bf16", "mot_qk_norm_rope", "mot_routed_gemm_f32", "mot_attention_workspace_bytes",
     "mot_joint_attention", "mot_attention_varlen_workspace_bytes", "mot_joint_attention_varlen", "mot_grad_w",
+    "mot_routed_gemm_dx",
     "mot_modality_from_index_sets", "mot_routed_gemm_noalloc", "mot_latent_workspace_bytes",
     "mot_cfg_combine_renorm", "mot_flow_sde_step_logp", "mot_routed_gemm_qk_norm_rope",
 )
@@ -98,6 +99,8 @@ def lib():
     L.mot_joint_attention.restype = ctypes.c_int
     L.mot_joint_attention.argtypes = [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, I64, I64, ctypes.c_int, P,
                                       SZ, P]
+    L.mot_routed_gemm_dx.restype = ctypes.c_int
+    L.mot_routed_gemm_dx.argtypes = [P, I64, P, P, P, P, I64, I64, I64, I64, P, SZ, U, P]
     L.mot_grad_w.restype = ctypes.c_int
     L.mot_grad_w.argtypes = [P, I64, P, I64, P, ctypes.c_int, I64, I64, I64, P, I64, ctypes.c_int, P]
     L.mot_attention_varlen_workspace_bytes.restype = SZ
@@ -442,13 +445,38 @@ def transpose(x, modality=None, keep=1, rows_pad=None):
     return out
 
 
-def routed_gemm_dx(dy, w_und, w_gen, modality, wt=None, out=None, workspace=None):
+def routed_gemm_dx(dy, w_und, w_gen, modality, wt=None, out=None, workspace=None, plan_ready=False):
     """dX[t] = dY[t] @ W_{modality[t]} (the routed backward for the inputs);
-    W_* are the forward's [N, K] weights.  wt = (W_und^T, W_gen^T) from
-    transpose() may be passed to reuse them."""
-    if wt is None:
-        wt = (transpose(w_und), transpose(w_gen))
-    return routed_gemm(dy, wt[0], wt[1], modality, out=out, workspace=workspace)
+    W_* are the forward's [N, K] weights, read as they lie (mot_routed_gemm_dx,
+    256 x 256 tiles).  wt = (W_und^T, W_gen^T) from transpose() runs the
+    routed GEMM on them instead (its tile choice, small packs included); both
+    forms give the same bytes."""
+    if wt is not None:
+        return routed_gemm(dy, wt[0], wt[1], modality, out=out, workspace=workspace, plan_ready=plan_ready)
+    _req(dy, "dy", torch.bfloat16, 2)
+    _req(w_und, "w_und", torch.bfloat16, 2)
+    _req(w_gen, "w_gen", torch.bfloat16, 2)
+    _req(modality, "modality", torch.uint8, 1)
+    if w_und.shape != w_gen.shape or not (w_und.is_contiguous() and w_gen.is_contiguous()):
+        raise ValueError("w_und and w_gen must be contiguous and of the same shape [N, K]")
+    T, N = dy.shape
+    if w_und.shape[0] != N or modality.shape[0] != T:
+        raise ValueError("shapes: dy [T, N], weights [N, K], modality [T]")
+    K = w_und.shape[1]
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.bfloat16, device=dy.device)
+    _req(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (T, K):
+        raise ValueError(f"out must be [{T}, {K}]")
+    if workspace is None:
+        if plan_ready:
+            raise ValueError("plan_ready needs the workspace that holds the plan")
+        workspace = new_workspace(T, dy.device)
+    st = lib().mot_routed_gemm_dx(_ptr(dy), _rows(dy, "dy"), _ptr(w_und), _ptr(w_gen), _ptr(modality.contiguous()),
+                                  _ptr(out), _rows(out, "out"), T, N, K, _ptr(workspace), workspace.numel(),
+                                  FLAG_PLAN_READY if plan_ready else 0, _stream(dy.device))
+    _check(st, "mot_routed_gemm_dx")
+    return out
 
 
 def grad_w(dy, x, modality, keep=1, out_dtype=torch.bfloat16):

@@ -111,6 +111,9 @@ struct RoutedCall {
     unsigned flags;
     int out_f32 = 0;       // 1: y is fp32 [T][ldy]
     const mot::QkArgs *qk = nullptr;  // fused QK norm + rotary epilogue (qkv, ld, T unused)
+    // 1: the weights are contraction-major, [K][N] with pitch N (the forward's
+    // weights of dX = dY W): big tiles only, no prologue, bf16 output
+    int wtok = 0;
 };
 
 int validate_routed(const RoutedCall &c) {
@@ -219,6 +222,11 @@ int run_routed(const RoutedCall &c, bool swiglu, void *stream) {
         // the in-kernel segment list raises errors by atomic maximum in a
         // cleared word (the plan kernel writes the word itself)
         if (inline_route && mot::launch_set_word(hdr, 0, s) != hipSuccess) return MOT_ERR_DEVICE;
+    }
+    if (c.wtok) {
+        a.ldw = c.N;
+        a.tile_mode = 1;
+        return mot::launch_gemm_wtok(a, inline_route, s) == hipSuccess ? MOT_OK : MOT_ERR_DEVICE;
     }
     if (mot::launch_gemm(a, swiglu, inline_route, s) != hipSuccess) return MOT_ERR_DEVICE;
     return MOT_OK;
@@ -464,6 +472,23 @@ int mot_transpose_bf16(const uint16_t *in, int64_t ld_in, int64_t rows, int64_t 
     return mot::launch_transpose(in, ld_in, rows, cols, modality, keep, out, ld_out, rows_pad, s) == hipSuccess
                ? MOT_OK
                : MOT_ERR_DEVICE;
+}
+
+int mot_routed_gemm_dx(const uint16_t *dy, int64_t lddy, const uint16_t *w_und, const uint16_t *w_gen,
+                       const uint8_t *modality, uint16_t *dx, int64_t lddx, int64_t T, int64_t N, int64_t K,
+                       void *workspace, size_t workspace_bytes, unsigned flags, void *stream) {
+    if ((flags & ~MOT_FLAG_PLAN_READY) != 0) return MOT_ERR_INVALID_ARG;
+    // the routed GEMM's contract with the contraction over N and K output
+    // columns; the weights [N][K] are the same bytes as its [K][N] operand's
+    // transpose
+    RoutedCall c{dy, lddy, w_und, w_gen, modality, dx, lddx, T, N, K, K,
+                 nullptr, nullptr, nullptr, workspace, workspace_bytes, flags};
+    c.wtok = 1;
+    const int v = validate_routed(c);
+    if (v != MOT_OK || T == 0) return v;
+    // the last 256-column tile reads up to 256 columns past K in W's rows
+    if ((N * K + 256) * 2 >= (int64_t(1) << 32)) return MOT_ERR_UNSUPPORTED_SHAPE;
+    return run_routed(c, false, stream);
 }
 
 int mot_grad_w(const uint16_t *dy, int64_t lddy, const uint16_t *x, int64_t ldx, const uint8_t *modality,

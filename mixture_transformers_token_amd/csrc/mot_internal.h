@@ -109,6 +109,11 @@ struct AttnArgs {
 // 64, N = wrows = columns k; out_f32 as for the GEMM).
 hipError_t launch_grad_w(const GemmArgs &a, hipStream_t stream);
 
+// Routed GEMM whose weights are contraction-major (W [K][ldw], the x side
+// [T][ldx] as usual): dX = dY W with the forward's [N][K] weights read as they
+// lie.  Big tiles only (a.tile_mode must be 1).
+hipError_t launch_gemm_wtok(const GemmArgs &a, bool inline_route, hipStream_t stream);
+
 hipError_t launch_attention(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_seqlens_check(const int32_t *cu_q, const int32_t *cu_k, int n, int64_t Tq, int64_t Tk,
                                 int64_t max_q, int32_t *err, hipStream_t stream);

@@ -1267,12 +1267,19 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Tile &ti, uint
 __device__ __forceinline__ int tok_swz(int r) { return ((r & 1) ? 5 : 0) ^ (r & 2); }
 constexpr int kTokRowBytes = 2 * kBigN;  // 256 bf16 columns
 
-template <bool SWIGLU, bool F32 = false, bool QK = false, int BN = kBigN, int BM = kBigM, bool TOK = false>
+// WTOK: only the weight side is contraction-major: W [contraction][ldw]
+// (the forward's [N][K] weights read as they lie, for dX = dY W: the
+// contraction runs over W's rows), staged and read as TOK stages it; the x
+// side is the routed token rows as usual.  All W rows count.
+template <bool SWIGLU, bool F32 = false, bool QK = false, int BN = kBigN, int BM = kBigM, bool TOK = false,
+          bool WTOK = false>
 __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint8_t *const (&hs)[5],
                                          const int32_t *s_rows, const int tid, lds_u8 *const eb,
                                          int32_t *qk_p = nullptr) {
     static_assert(!(SWIGLU && F32), "fp32 output: plain GEMM only");
     static_assert(!TOK || (!SWIGLU && !QK && BN == kBigN && BM == kBigM), "token-major operands: plain 256 x 256");
+    static_assert(!WTOK || (!TOK && !SWIGLU && !QK && !F32 && BN == kBigN && BM == kBigM),
+                  "contraction-major weights: plain bf16 256 x 256");
     static_assert(!QK || (!SWIGLU && !F32), "fused QK epilogue: plain bf16 GEMM only");
     constexpr uint32_t kOutBytes = F32 ? 4u : 2u;  // bytes per output element
     static_assert(BN == kBigN || (BN == kWideN && !SWIGLU && !F32 && !QK), "wide tiles: plain bf16 GEMM only");
@@ -1322,6 +1329,14 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
     }
 #pragma unroll
     for (int j = 0; j < WL; ++j) {
+        if constexpr (WTOK) {
+            // as TOK's weight side: W row r of the stage, chunk position
+            // lane & 31, columns ti.wrow0 + 8 (p ^ 2 tok_swz(r))
+            const int r = wave * 16 + 2 * j + (lane >> 5);
+            const uint32_t c = (uint32_t)((lane & 31) ^ (tok_swz(r) << 1));
+            woff[j] = (uint32_t)r * (uint32_t)(a.ldw * 2) + ((uint32_t)ti.wrow0 + 8u * c) * 2u;
+            continue;
+        }
         const int r = wave * (BN / 4) + j * 8 + (lane >> 3);
         int wrow;
         if constexpr (SWIGLU) {
@@ -1390,6 +1405,11 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
 #pragma unroll
         for (int j = 0; j < DL; ++j) {
             if (j < lo || j >= hi) continue;
+            if (WTOK && o == 1) {
+                dma16(wr, woff[j] + (uint32_t)kb * kBK * (uint32_t)(a.ldw * 2), 0,
+                      hs[s] + (wave * 16 + 2 * j) * kTokRowBytes);
+                continue;
+            }
             if (o == 0) {
                 if (j < XL)
                     dma16(xr, xoff[j], (uint32_t)kb * kRowBytes, hs[s] + (wave * (BM / 4) + j * 8) * kRowBytes);
@@ -1429,7 +1449,15 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
     for (int q = 0; q < 4; ++q) {
         const uint32_t pos = (uint32_t)(((2 * q + khalf) ^ lsw) * 16);
         xq[q] = (uint32_t)((wm * WM + rsel) * kRowBytes) + pos;
-        wq[q] = (uint32_t)((wn * WN + rsel) * kRowBytes) + pos;
+        if constexpr (WTOK) {
+            // (as TOK's: q indexes the wave's 32-column block of W)
+            const int L = lane & 15;
+            const int tr = 8 * khalf + (L >> 2);
+            const int gs = ((lane >> 4) & 1) ^ tok_swz(tr);
+            wq[q] = (uint32_t)(tr * kTokRowBytes + 8 * (L & 3)) + (uint32_t)(((2 * (wn * MI + q)) ^ gs) << 5);
+        } else {
+            wq[q] = (uint32_t)((wn * WN + rsel) * kRowBytes) + pos;
+        }
     }
     }
     // TOK: eight consecutive token rows of one column block (xq / wq index
@@ -1456,6 +1484,15 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
             for (int i = 1; i < MI; ++i) fa[i] = tok_frag(ws, wq[i], q);
             return;
         }
+        if constexpr (WTOK) {
+            static_assert(!WTOK || MI == 4, "contraction-major weights: 4 column blocks per wave");
+            fa[0] = tok_frag(ws, wq[0], q);
+#pragma unroll
+            for (int j = 0; j < MJ; ++j) fb[j] = *(const bf16x8_t *)(xs + xq[q] + j * 32 * kRowBytes);
+#pragma unroll
+            for (int i = 1; i < MI; ++i) fa[i] = tok_frag(ws, wq[i], q);
+            return;
+        }
         fa[0] = *(const bf16x8_t *)(ws + wq[q]);
 #pragma unroll
         for (int j = 0; j < MJ; ++j) fb[j] = *(const bf16x8_t *)(xs + xq[q] + j * 32 * kRowBytes);
@@ -1474,7 +1511,8 @@ __device__ __forceinline__ void run_big5(const GemmArgs &a, const Tile &ti, uint
     auto interleave = [&]() {
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
-            if (i < MI + MJ) __builtin_amdgcn_sched_group_barrier(0x100, TOK ? 2 : 1, 0);  // DS read
+            if (WTOK ? i < 2 * MI + MJ : i < MI + MJ)
+                __builtin_amdgcn_sched_group_barrier(0x100, TOK ? 2 : 1, 0);  // DS read
             if (i % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM (DMA)
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
         }
@@ -1665,7 +1703,7 @@ __device__ __forceinline__ uint16_t *prologue_nw_lds() {
 // Separate instantiations, so that the other GEMMs keep their register
 // allocation (a kernel with the 192-row and the 256-row paths spills).
 template <bool SWIGLU, bool PRO, bool INLINE, bool NARROW = false, bool F32 = false, bool QK = false,
-          bool WIDE = false, bool SHORT = false>
+          bool WIDE = false, bool SHORT = false, bool WTOK = false>
 __global__ void __launch_bounds__(kThreads, 1)
 gemm_kernel(GemmArgs a) {
     static_assert(!NARROW || (!SWIGLU && !PRO), "narrow tiles: plain GEMM only");
@@ -1673,6 +1711,8 @@ gemm_kernel(GemmArgs a) {
     static_assert(!QK || (!SWIGLU && !PRO && !NARROW && !F32), "fused QK epilogue: plain bf16 GEMM only");
     static_assert(!WIDE || (!SWIGLU && !PRO && !NARROW && !F32 && !QK), "wide tiles: plain bf16 GEMM only");
     static_assert(!SHORT || (!SWIGLU && !PRO && !NARROW && !F32 && !QK && !WIDE), "short tiles: plain bf16 GEMM only");
+    static_assert(!WTOK || (!SWIGLU && !PRO && !NARROW && !F32 && !QK && !WIDE && !SHORT),
+                  "contraction-major weights: plain bf16 GEMM, big tiles only (mode 1)");
     constexpr int kArrayBytes = kBigM * kRowBytes;
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kArrayBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kArrayBytes];
@@ -1817,11 +1857,13 @@ gemm_kernel(GemmArgs a) {
                         run_big5<false, false, false>(a, ti, hs, s_rows, tid, eb, qk_p);
                 } else if constexpr (SHORT) {
                     run_big5<false, false, false, kBigN, kShortM>(a, ti, hs, s_rows, tid, eb, qk_p);
+                } else if constexpr (WTOK) {
+                    run_big5<false, false, false, kBigN, kBigM, false, true>(a, ti, hs, s_rows, tid, eb);
                 } else {
                     run_big5<SWIGLU, F32, QK>(a, ti, hs, s_rows, tid, eb, qk_p);
                 }
             }
-        } else if constexpr (!F32) {  // (mode 1 schedules no small tiles)
+        } else if constexpr (!F32 && !WTOK) {  // (mode 1 schedules no small tiles)
             constexpr int kHalf = kSmallM * kRowBytes;
             uint8_t *const xb[4] = {lds0, lds1, lds2, lds3};
             uint8_t *const wb[4] = {lds0 + kHalf, lds1 + kHalf, lds2 + kHalf, lds3 + kHalf};
@@ -2442,6 +2484,27 @@ hipError_t launch_plan(const uint8_t *modality, int64_t T, int32_t *hdr, int32_t
                        hipStream_t stream) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, modality, (int)T,
                        hdr, perm);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_wtok(const GemmArgs &a, bool inline_route, hipStream_t stream) {
+    int dev = 0, ncu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (ncu <= 0) ncu = 1;
+    // mode 1: at most (row blocks of T, plus one for the two sets' partial
+    // blocks) x weight tiles big tiles
+    const int64_t tiles = ((a.T + kBigM - 1) / kBigM + 1) * ((a.wrows + kBigN - 1) / kBigN);
+    const int grid = (int)(tiles < ncu ? tiles : ncu);
+    if (grid <= 0) return hipSuccess;
+    if (inline_route)
+        hipLaunchKernelGGL((gemm_kernel<false, false, true, false, false, false, false, false, true>), dim3(grid),
+                           dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_kernel<false, false, false, false, false, false, false, false, true>),
+                           dim3(grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

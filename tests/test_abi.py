@@ -280,6 +280,34 @@ def test_attention_fails_closed(kw, code):
     assert _attn(**kw) == code
 
 
+def _dx(**kw):
+    args = dict(dy=A, lddy=256, wu=2 * A, wg=3 * A, m=4 * A, dx=5 * A, lddx=128, T=100, N=256, K=128, ws=6 * A,
+                wsb=1 << 20, flags=0)
+    args.update(kw)
+    return mot.lib().mot_routed_gemm_dx(args["dy"], args["lddy"], args["wu"], args["wg"], args["m"], args["dx"],
+                                        args["lddx"], args["T"], args["N"], args["K"], args["ws"], args["wsb"],
+                                        args["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), INVALID),
+    (dict(T=0), OK),                                      # empty pack: a no-op
+    (dict(flags=0x10), INVALID),                          # no tile override (256 x 256 tiles only)
+    (dict(wg=None), INVALID),
+    (dict(m=None), INVALID),
+    (dict(N=100, lddy=104), SHAPE),                       # contraction % 64 != 0
+    (dict(K=96, lddx=96), SHAPE),                         # output width % 64 != 0
+    (dict(lddy=128), INVALID),                            # narrower than N
+    (dict(lddx=64), INVALID),
+    (dict(lddx=132), MISALIGNED),
+    (dict(wu=2 * A + 8), MISALIGNED),
+    (dict(ws=None), WORKSPACE),
+    (dict(dx=2 * A + 1024), INVALID),                     # dx overlaps w_und
+])
+def test_dx_fails_closed(kw, code):
+    assert _dx(**kw) == code
+
+
 def _grad_w(**kw):
     args = dict(dy=A, lddy=256, x=2 * A, ldx=128, m=3 * A, keep=1, T=100, N=256, K=128, out=4 * A, ldo=128,
                 f32=0)

@@ -96,6 +96,50 @@ def test_grad_w_qkv_shape_sampled():
     _grad_parity(4096, W.QKV_DIM, W.HIDDEN, m, base=540, cols=np.sort(cols))
 
 
+@pytest.mark.parametrize("T,N,K", [(1, 64, 64), (77, 128, 192), (300, 320, 256), (1101, 448, 320),
+                                   (4096, 4608, 3584)])
+def test_dx_weights_as_they_lie_equal_the_transposed_product(T, N, K):
+    """mot_routed_gemm_dx reads the forward's [N, K] weights where they lie
+    (contraction-major weight stages, transposing LDS reads) and gives, bit
+    for bit, the routed GEMM's bytes on the transposed weights, whatever
+    tile shapes that call picks (256 x 256 big tiles here, small tiles or the
+    small-pack kernel there): same MFMA chain, same k order."""
+    base = 600 + T
+    dy = dev(W.normal_bf16((T, N), W.seed_of(base, 1)))
+    wu = dev(W.normal_bf16((N, K), W.seed_of(base, 2), 0.02))
+    wg = dev(W.normal_bf16((N, K), W.seed_of(base, 3), 0.02))
+    m = W.pattern(T)
+    m[::5] = 1 - m[::5]
+    md = dev(torch.from_numpy(m))
+    got = mot.routed_gemm_dx(dy, wu, wg, md)
+    want = mot.routed_gemm_dx(dy, wu, wg, md, wt=(mot.transpose(wu), mot.transpose(wg)))
+    torch.cuda.synchronize()
+    assert raw_equal(got, want), f"T={T} N={N} K={K}"
+
+
+def test_dx_weights_as_they_lie_plan_ready_and_bad_bytes():
+    """The ready-plan form gives the same bytes; an invalid modality byte
+    makes the call write nothing and raises the error word."""
+    T, N, K = 500, 256, 192
+    dy = dev(W.normal_bf16((T, N), 620))
+    wu = dev(W.normal_bf16((N, K), 621, 0.02))
+    wg = dev(W.normal_bf16((N, K), 622, 0.02))
+    md = dev(torch.from_numpy(W.pattern(T)))
+    ws = mot.new_workspace(T, dy.device)
+    mot.routing_plan(md, workspace=ws)
+    a = mot.routed_gemm_dx(dy, wu, wg, md, workspace=ws, plan_ready=True)
+    b = mot.routed_gemm_dx(dy, wu, wg, md)
+    torch.cuda.synchronize()
+    assert raw_equal(a, b)
+    bad = W.pattern(T)
+    bad[123] = 7
+    out = torch.full((T, K), 3.0, dtype=torch.bfloat16, device="cuda")
+    ws2 = mot.new_workspace(T, dy.device)
+    mot.routed_gemm_dx(dy, wu, wg, dev(torch.from_numpy(bad)), out=out, workspace=ws2)
+    assert mot.read_device_error(ws2) == 6  # MOT_ERR_MODALITY
+    assert bool((out == 3.0).all())
+
+
 def _grad_w_transposed(dy, x, m, keep, f32):
     """The same weight gradient as a routed GEMM over the tokens, on
     transposed copies (x's other-set rows zeroed, both padded to 64 rows)."""
