@@ -1788,16 +1788,17 @@ gemm_kernel(GemmArgs a) {
     const int cap = min(nsm, 4 * idle);
     const int n_big = w < sc.nkeep ? cdiv(sc.nkeep - w, grid) : 0;
     const int n_idle = (idle > 0 && w >= fill && w - fill < cap) ? cdiv(cap - (w - fill), idle) : 0;
-    // Round-robin small tiles that fit in one round go in chunks of four
-    // consecutive tiles (a big tile's quarters, or neighbours in a row block:
-    // they share operand panels) dealt to the XCDs in turn.  Contiguous
-    // ranges per XCD would crowd such a round onto the first few XCDs, whose
-    // L2s and fabric links then carry all of its operand traffic (QKV at
-    // T=4096: 164 small tiles on five XCDs; dealt out, 3% faster).
+    // Round-robin small tiles that fit in one round go in chunks of eight
+    // consecutive tiles (two neighbouring big tiles' quarters, or neighbours
+    // in a row block: they share operand panels) dealt to the XCDs in turn.
+    // Contiguous ranges per XCD would crowd such a round onto the first few
+    // XCDs, whose L2s and fabric links then carry all of its operand traffic
+    // (QKV at T=4096: 164 small tiles on five XCDs; dealt out, 3% faster;
+    // chunks of eight fetch less than chunks of four in the same time).
     int wsm = w;
-    if ((grid & 31) == 0 && nsm - cap <= grid) {
+    if ((grid & 63) == 0 && nsm - cap <= grid) {
         const int id = (int)blockIdx.x, local = id >> 3;
-        wsm = (local >> 2) * 32 + (id & 7) * 4 + (local & 3);
+        wsm = (local >> 3) * 64 + (id & 7) * 8 + (local & 7);
     }
     const int n_rr = cap + wsm < nsm ? cdiv(nsm - cap - wsm, grid) : 0;
     for (int it = 0; it < n_big + n_idle + n_rr; ++it) {
