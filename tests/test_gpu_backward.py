@@ -97,13 +97,14 @@ def test_grad_w_qkv_shape_sampled():
 
 
 @pytest.mark.parametrize("T,N,K", [(1, 64, 64), (77, 128, 192), (300, 320, 256), (1101, 448, 320),
-                                   (4096, 4608, 3584)])
+                                   (4096, 4608, 3584), (9000, 256, 192)])
 def test_dx_weights_as_they_lie_equal_the_transposed_product(T, N, K):
     """mot_routed_gemm_dx reads the forward's [N, K] weights where they lie
     (contraction-major weight stages, transposing LDS reads) and gives, bit
     for bit, the routed GEMM's bytes on the transposed weights, whatever
     tile shapes that call picks (256 x 256 big tiles here, small tiles or the
-    small-pack kernel there): same MFMA chain, same k order."""
+    small-pack kernel there): same MFMA chain, same k order.  T = 9000 takes
+    the segment list from the plan kernel instead of building it in-kernel."""
     base = 600 + T
     dy = dev(W.normal_bf16((T, N), W.seed_of(base, 1)))
     wu = dev(W.normal_bf16((N, K), W.seed_of(base, 2), 0.02))
