@@ -87,6 +87,20 @@ __device__ __forceinline__ int v_swz(int r) { return ((r & 1) ? 5 : 0) ^ (r & 2)
 typedef short at_i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) at_i16x4_t lds_i16x4_t;
 
+// max(a, b, c) and max(a, b) of finite or infinite scores in one instruction
+// each (written out: the compiler's fmaxf first quiets every input with a
+// v_max x, x of its own, which doubles the instruction count of a max tree)
+__device__ __forceinline__ float at_max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float at_max2(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // fp32 -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t at_pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((at_f32x2_t){lo, hi}, at_bf16x2_t));
@@ -252,18 +266,28 @@ __global__ void __launch_bounds__(kThreads, 2) attention_kernel(AttnArgs a) {
                 }
             }
         }
-        // pairwise trees (short dependency chains), then the two half-waves
-        float t16[16];
+        // the lane's 32 scores by a three-input tree (16 instructions; the
+        // maximum does not depend on the grouping), then the two half-waves
+        float mx;
+        {
+            float v32[32], w12[12], x4[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) t16[r] = fmaxf(sacc[0][r], sacc[1][r]);
+            for (int r = 0; r < 16; ++r) {
+                v32[r] = sacc[0][r];
+                v32[16 + r] = sacc[1][r];
+            }
 #pragma unroll
-        for (int w = 8; w >= 1; w >>= 1) {
+            for (int i = 0; i < 10; ++i) w12[i] = at_max3(v32[3 * i], v32[3 * i + 1], v32[3 * i + 2]);
+            w12[10] = v32[30];
+            w12[11] = v32[31];
 #pragma unroll
-            for (int r = 0; r < w; ++r) t16[r] = fmaxf(t16[r], t16[r + w]);
+            for (int i = 0; i < 4; ++i) x4[i] = at_max3(w12[3 * i], w12[3 * i + 1], w12[3 * i + 2]);
+            const float lane_max = at_max2(at_max3(x4[0], x4[1], x4[2]), x4[3]);
+            float mlo, mhi;
+            at_halves(lane_max, mlo, mhi);
+            mx = at_max2(mlo, mhi);
         }
-        float mlo, mhi;
-        at_halves(t16[0], mlo, mhi);
-        const float mx = fmaxf(mlo, mhi);
+        float t16[16];
         // The reference max moves only when a score exceeds it by more than
         // kLazy / c (weights then stay below 2^kLazy, far inside fp32 and
         // bf16 range): most blocks keep it, so the output needs no rescale.
