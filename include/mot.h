@@ -288,7 +288,9 @@ int mot_fused_add_rmsnorm(const uint16_t *x, uint16_t *residual,
                           int64_t T, int64_t H,
                           void *workspace, void *stream);
 
-/* bf16 transpose, the operand preparation of the routed backward.  The RFC
+/* bf16 transpose, the operand preparation of the routed backward on
+ * transposed copies (mot_routed_gemm_dx and mot_grad_w below compute the same
+ * products, with the same bytes, from the operands as they lie).  The RFC
  * page (section 1) trains only the generation expert in Phase A while the
  * frozen understanding operators still need dX, and the MoE route/combine PR
  * page folds weight gradients over rows in ascending order in fp32.  With it:
