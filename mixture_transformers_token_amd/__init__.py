@@ -479,7 +479,7 @@ def routed_gemm_dx(dy, w_und, w_gen, modality, wt=None, out=None, workspace=None
     return out
 
 
-def grad_w(dy, x, modality, keep=1, out_dtype=torch.bfloat16):
+def grad_w(dy, x, modality, keep=1, out_dtype=torch.bfloat16, out=None):
     """dW[n][k] = sum over rows t with modality[t] == keep of dY[t][n] * X[t][k]
     (fp32, rows folded in ascending order in 16-row chunks), as [N, K] in
     out_dtype: bf16 (one cast) or fp32 (the sums themselves).  One kernel
@@ -495,7 +495,11 @@ def grad_w(dy, x, modality, keep=1, out_dtype=torch.bfloat16):
     if out_dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("grad_w: out_dtype must be torch.bfloat16 or torch.float32")
     f32 = out_dtype == torch.float32
-    out = torch.empty((N, K), dtype=out_dtype, device=dy.device)
+    if out is None:
+        out = torch.empty((N, K), dtype=out_dtype, device=dy.device)
+    _req(out, "out", out_dtype, 2)
+    if tuple(out.shape) != (N, K):
+        raise ValueError(f"out must be [{N}, {K}]")
     st = lib().mot_grad_w(_ptr(dy), _rows(dy, "dy"), _ptr(x), _rows(x, "x"), _ptr(modality.contiguous()),
                           int(keep), T, N, K, _ptr(out), _rows(out, "out"), 1 if f32 else 0, _stream(dy.device))
     _check(st, "mot_grad_w")

@@ -57,6 +57,27 @@ def test_swiglu_graph():
     _replays_match(lambda: mot.routed_gemm_swiglu(x, wu, wg, md, out=out, workspace=ws), out, ref)
 
 
+@pytest.mark.parametrize("f32", [False, True])
+def test_backward_graph(f32):
+    """dX with the weights as they lie and dW over token-major operands
+    replay to the eager bytes."""
+    T, N, K = 700, 512, 384
+    m = W.pattern(T)
+    dy = dev(W.normal_bf16((T, N), 1340))
+    x = dev(W.normal_bf16((T, K), 1341))
+    wu = dev(W.normal_bf16((N, K), 1342, 0.05))
+    wg = dev(W.normal_bf16((N, K), 1343, 0.05))
+    md = dev(torch.from_numpy(m))
+    ref = mot.routed_gemm_dx(dy, wu, wg, md)
+    out = torch.empty_like(ref)
+    ws = mot.new_workspace(T, dy.device)
+    _replays_match(lambda: mot.routed_gemm_dx(dy, wu, wg, md, out=out, workspace=ws), out, ref)
+    dt = torch.float32 if f32 else torch.bfloat16
+    ref_w = mot.grad_w(dy, x, md, keep=1, out_dtype=dt)
+    out_w = torch.empty_like(ref_w)
+    _replays_match(lambda: mot.grad_w(dy, x, md, keep=1, out_dtype=dt, out=out_w), out_w, ref_w)
+
+
 def test_qk_norm_rope_graph():
     """The in-place op, captured with the copy that restores its input."""
     T = 512
