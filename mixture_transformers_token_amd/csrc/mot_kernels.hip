@@ -2244,6 +2244,165 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs &a, int set, int blk,
     }
 }
 
+// skinny_tile for a plain GEMM whose workgroup takes two adjacent 32-row
+// weight blocks (64 output columns; blk counts them in 64s) and the rows the
+// caller gives it (at most 64): the same stages, fragments and MFMA chain per
+// output element.  A separate function, so that the other instantiations'
+// code is not touched.
+template <int XG, int KS>
+__device__ __forceinline__ void skinny_pair_tile(const GemmArgs &a, int set, int blk, int count,
+                                                 uint8_t *const (&sl)[SkinnyCfg<2, XG, KS>::S],
+                                                 const int32_t *s_rows, const int wave, const int lane) {
+    constexpr bool SWIGLU = false;
+    constexpr int MI = 2;
+    using C = SkinnyCfg<MI, XG, KS>;
+    constexpr int S = C::S, AB = C::AB, XW = C::XW, KSUB = C::KSUB, SUB = C::SUB;
+    const int K = a.K;
+    const int nk = K / kBK / KSUB;  // stages (the launch makes KSUB divide K / 64)
+    const rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+    const rsrc_t wr = make_rsrc(set ? a.w_gen : a.w_und, a.w_bytes);
+    // this wave's DMA of a stage: A groups wave + 4g (g < XW; with XG < 4
+    // only waves 0 .. XG-1 load one), weight groups wave + 4i (i < MI)
+    const bool loads_a = XG >= 4 || wave < XG;
+    uint32_t xoff[XW], woff[MI];
+#pragma unroll
+    for (int g = 0; g < XW; ++g) {
+        const int r = (wave + 4 * g) * 8 + (lane >> 3);
+        xoff[g] = (uint32_t)s_rows[r] * (uint32_t)(a.ldx * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+        const int r = (wave + 4 * i) * 8 + (lane >> 3);  // staged W row: [0,32) gate (or plain), [32,64) up
+        const int wrow = blk * 64 + r;
+        woff[i] = (uint32_t)wrow * (uint32_t)(K * 2) + (uint32_t)(((lane & 7) ^ swz(r)) * 16);
+    }
+    auto issue = [&](int kt, int s) {
+#pragma unroll
+        for (int u = 0; u < KSUB; ++u) {
+            const uint32_t koff = (uint32_t)(kt * KSUB + u) * kRowBytes;
+            if (loads_a) {
+#pragma unroll
+                for (int g = 0; g < XW; ++g)
+                    dma16(xr, xoff[g], koff, sl[s] + u * SUB + (wave + 4 * g) * 8 * kRowBytes);
+            }
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                dma16(wr, woff[i], koff, sl[s] + u * SUB + AB + (wave + 4 * i) * 8 * kRowBytes);
+        }
+    };
+    // a stage has landed for this wave once at most Y younger stages are in
+    // flight (counts differ between waves that load A and those that do
+    // not, each a wave-uniform branch)
+    auto wait_stage = [&](auto y_c) {
+        constexpr int Y = decltype(y_c)::value;
+        if constexpr (XG >= 4) {
+            wait_vm_lgkm0<Y * (MI + XW) * KSUB>();
+        } else {
+            if (loads_a)
+                wait_vm_lgkm0<Y * (MI + 1) * KSUB>();
+            else
+                wait_vm_lgkm0<Y * MI * KSUB>();
+        }
+    };
+
+    const int mj = (count + 31) / 32;
+    const bool computes = wave < mj;
+    f32x16_t acc[MI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+    const int rsel = lane & 31, khalf = lane >> 5;
+    const int lsw = swz(lane & 15);
+    const int arow = wave * 32 + rsel;  // this wave's token row of the slot (compute waves)
+
+    // Fragments are read one stage ahead, so that the LDS latency hides
+    // under the MFMAs: iteration kt waits for stage kt+1, passes the barrier
+    // (which also tells every wave that stage kt's slot, read in the
+    // previous iteration, is free), refills that slot with k-block kt+S (the
+    // final k-block again past the end, into a slot that is not read again),
+    // reads stage kt+1's fragments and runs stage kt's four k-steps.
+    constexpr int NQ = 4 * KSUB;  // k-steps of 16 per stage, ascending
+    bf16x8_t fa0[NQ][MI], fb0[NQ], fa1[NQ][MI], fb1[NQ];
+    auto read_stage = [&](int s, bf16x8_t (&fa)[NQ][MI], bf16x8_t (&fb)[NQ]) {
+#pragma unroll
+        for (int t = 0; t < NQ; ++t) {
+            const int u = t / 4, q = t % 4;
+            const uint32_t pos = (uint32_t)(((2 * q + khalf) ^ lsw) * 16);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                fa[t][i] = *(const bf16x8_t *)(sl[s] + u * SUB + AB + (i * 32 + rsel) * kRowBytes + pos);
+            fb[t] = *(const bf16x8_t *)(sl[s] + u * SUB + arow * kRowBytes + pos);
+        }
+    };
+    auto mfma_stage = [&](const bf16x8_t (&fa)[NQ][MI], const bf16x8_t (&fb)[NQ]) {
+#pragma unroll
+        for (int t = 0; t < NQ; ++t)
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[t][i], fb[t], acc[i], 0, 0, 0);
+    };
+    // stage kt sits in slot s; its fragments are in (fa0, fb0) when the
+    // parity p is 0, else in (fa1, fb1)
+    auto stage = [&](int kt, int s, auto p_c) {
+        wait_stage(std::integral_constant<int, S - 2>{});
+        __builtin_amdgcn_s_barrier();
+        issue(min(kt + S, nk - 1), s);
+        if (computes) {
+            if constexpr (decltype(p_c)::value == 0) {
+                read_stage((s + 1) % S, fa1, fb1);
+                mfma_stage(fa0, fb0);
+            } else {
+                read_stage((s + 1) % S, fa0, fb0);
+                mfma_stage(fa1, fb1);
+            }
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < S; ++s) issue(min(s, nk - 1), s);
+    wait_stage(std::integral_constant<int, S - 1>{});
+    __builtin_amdgcn_s_barrier();
+    if (computes) read_stage(0, fa0, fb0);
+    // unrolled by 2S so that both the slot and the register parity of every
+    // stage are compile-time constants
+    int kt = 0;
+    for (; kt + 2 * S - 1 < nk; kt += 2 * S) {
+#pragma unroll
+        for (int s = 0; s < 2 * S; ++s) {
+            if (s % 2 == 0)
+                stage(kt + s, s % S, std::integral_constant<int, 0>{});
+            else
+                stage(kt + s, s % S, std::integral_constant<int, 1>{});
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < 2 * S - 1; ++s) {
+        if (kt + s < nk) {
+            if (s % 2 == 0)
+                stage(kt + s, s % S, std::integral_constant<int, 0>{});
+            else
+                stage(kt + s, s % S, std::integral_constant<int, 1>{});
+        }
+    }
+    wait_vm_lgkm0<0>();  // no DMA may still be writing LDS when the workgroup ends
+    if (!computes) return;
+
+    const rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+    const int col0 = blk * 64;
+    const int mloc = wave * 32 + rsel;
+    if (mloc >= count) return;
+    const uint32_t yrow = (uint32_t)s_rows[mloc] * (uint32_t)a.ldy * 2u;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x2_t pk = {pack2(acc[i][4 * q], acc[i][4 * q + 1]), pack2(acc[i][4 * q + 2], acc[i][4 * q + 3])};
+            __builtin_amdgcn_raw_buffer_store_b64(pk, yr, yrow + (uint32_t)(col0 + 32 * i + q * 8 + khalf * 4) * 2u, 0,
+                                                  0);
+        }
+}
+
+
 // nblk: output column blocks of 32 (N / 32, or F / 32 for SwiGLU); XG: A row
 // groups of 8 staged per k-block (at least the pack's rows / 8); KS: k-blocks
 // of 64 per stage (dividing K / 64).  Builds the
@@ -2330,6 +2489,96 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
     uint8_t *sl[C::S];
     sk_slots<C::SLOT>(sl, std::make_integer_sequence<int, C::S>{});
     skinny_tile<SWIGLU, XG, KS>(a, set, blk, count, sl, s_rows, wave, lane);
+}
+
+// Packs of 97-128 rows (plain GEMM).  Workgroups b % nblk = 2j and 2j + 1
+// share the 64 output columns of block j.  Where the set has more than 64
+// rows, workgroup 2j + h takes the 64-row half h of them (in ascending order)
+// and all 64 columns, so that each stages 64 A rows and 64 weight rows per
+// k-block instead of 128 and 32 (a fifth fewer bytes per CU); where it has
+// at most 64, each takes all of them and the 32 columns of block 2j + h.
+// Every output element keeps its MFMA chain either way.  nblk = N / 32 (even:
+// N is a multiple of 64).  Segment list and error word as skinny_kernel.
+template <int XG, int KS>
+__global__ void __launch_bounds__(kSkThreads)
+skinny_pair_kernel(GemmArgs a, int nblk, int publish) {
+    using C = SkinnyCfg<2, XG, KS>;
+    constexpr int RW = 2;  // rows per lane (packs of up to 128 rows)
+    __shared__ int32_t s_rows[64 * RW];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int T = (int)a.T;
+    const int set = (int)blockIdx.x / nblk;
+    const int blk = ((int)blockIdx.x % nblk) >> 1;
+    const int half = ((int)blockIdx.x % nblk) & 1;
+    uint32_t m[RW];
+    uint64_t und[RW], gen[RW], bad = 0;
+    int U = 0;
+#pragma unroll
+    for (int h = 0; h < RW; ++h) {
+        const int r = lane + 64 * h;
+        m[h] = r < T ? (uint32_t)a.modality[r] : 0u;
+        bad |= __ballot(r < T && m[h] > 1);
+        und[h] = __ballot(r < T && m[h] == 0);
+        gen[h] = __ballot(r < T && m[h] == 1);
+        U += __popcll(und[h]);
+    }
+    const uint64_t below = (1ull << lane) - 1;
+    if (publish && blockIdx.x == 0 && wave == 0) {
+        if (lane == 0) {
+            a.hdr_out[0] = bad ? kErrModality : 0;
+            a.hdr_out[1] = bad ? 0 : U;
+            a.hdr_out[2] = bad ? 0 : T - U;
+            a.hdr_out[3] = T;
+        }
+        if (!bad) {
+            int base_u = 0, base_g = U;
+#pragma unroll
+            for (int h = 0; h < RW; ++h) {
+                const int r = lane + 64 * h;
+                if (r < T) {
+                    const uint64_t mine = m[h] ? gen[h] : und[h];
+                    a.perm_out[(m[h] ? base_g : base_u) + __popcll(mine & below)] = r;
+                }
+                base_u += __popcll(und[h]);
+                base_g += __popcll(gen[h]);
+            }
+        }
+    }
+    if (bad) {
+        // the pack holds an invalid byte: write nothing (all waves), and
+        // raise the error word also when a ready plan was passed
+        if (!publish && blockIdx.x == 0 && threadIdx.x == 0) a.hdr_out[0] = kErrModality;
+        return;
+    }
+    int total = 0;
+#pragma unroll
+    for (int h = 0; h < RW; ++h) total += __popcll(set ? gen[h] : und[h]);
+    const bool split = total <= 64;          // one 32-column block each
+    const int lo = split ? 0 : 64 * half;    // first sorted row of this workgroup
+    const int count = min(total - lo, 64);
+    if (count <= 0) return;  // all waves
+    if (wave == 0) {
+        int base = 0;
+#pragma unroll
+        for (int h = 0; h < RW; ++h) {
+            const uint64_t mine = set ? gen[h] : und[h];
+            const int p = base + __popcll(mine & below);
+            if (((mine >> lane) & 1ull) && p >= lo && p < lo + 64) s_rows[p - lo] = lane + 64 * h;
+            base += __popcll(mine);
+        }
+    }
+    __syncthreads();
+    if (wave == 0 && lane >= count) s_rows[lane] = s_rows[0];  // padding: a row of the half
+    __syncthreads();
+    // one ring serves both tiles: the 32-column stages fit in the slots
+    static_assert(SkinnyCfg<1, XG, KS>::S == C::S && SkinnyCfg<1, XG, KS>::SLOT <= C::SLOT, "shared ring");
+    uint8_t *sl[C::S];
+    sk_slots<C::SLOT>(sl, std::make_integer_sequence<int, C::S>{});
+    if (split)
+        skinny_tile<false, XG, KS>(a, set, 2 * blk + half, count, sl, s_rows, wave, lane);
+    else
+        skinny_pair_tile<XG, KS>(a, set, blk, count, sl, s_rows, wave, lane);
 }
 
 // ============================================================================
@@ -2634,7 +2883,8 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
             else if (a.T <= 96)
                 hipLaunchKernelGGL((skinny_kernel<false, 12, 1>), grid, block, 0, stream, a, nblk, pub);
             else
-                hipLaunchKernelGGL((skinny_kernel<false, 16, 1>), grid, block, 0, stream, a, nblk, pub);
+                // 97-128 rows: halves of each set's rows by 64 output columns
+                hipLaunchKernelGGL((skinny_pair_kernel<8, 1>), grid, block, 0, stream, a, nblk, pub);
         }
         return hipGetLastError();
     }

@@ -184,6 +184,25 @@ def test_small_packs_match_large_pack_bytes(qkv_setup, T):
     assert raw_equal(y, s["ref"][torch.from_numpy(rows).cuda()])
 
 
+@pytest.mark.parametrize("T,N,n_und", [(100, 192, 70), (120, 64, 30), (128, 256, 64), (128, 128, 65),
+                                       (97, 4608, 97)])
+def test_small_packs_paired_columns(T, N, n_und):
+    """Packs of 97-128 rows: a set of more than 64 rows is split in halves of
+    64 over workgroups of 64 output columns, a set of at most 64 rows over
+    workgroups of 32 columns.  The bytes of forced 128 x 128 tiles, for sets
+    of 65 (a half of one row), 64 and fewer rows, and an empty set."""
+    m = np.zeros(T, np.uint8)
+    m[n_und:] = 1
+    m = m[np.random.default_rng(T + N).permutation(T)]
+    x = dev(W.normal_bf16((T, 512), 960 + T))
+    wu = dev(W.normal_bf16((N, 512), 961, 0.02))
+    wg = dev(W.normal_bf16((N, 512), 962, 0.02))
+    md = dev(torch.from_numpy(m))
+    small = mot.routed_gemm(x, wu, wg, md)
+    tiled = mot.routed_gemm(x, wu, wg, md, tile="128x128")
+    assert raw_equal(small, tiled)
+
+
 def test_mixed_equals_per_set_dense(qkv_setup):
     """Mixed pack == each set's rows run as a single-set pack (gathered)."""
     s = qkv_setup
