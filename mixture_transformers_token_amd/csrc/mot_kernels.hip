@@ -2491,10 +2491,10 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
     skinny_tile<SWIGLU, XG, KS>(a, set, blk, count, sl, s_rows, wave, lane);
 }
 
-// Packs of 97-128 rows (plain GEMM).  Workgroups b % nblk = 2j and 2j + 1
-// share the 64 output columns of block j.  Where the set has more than 64
-// rows, workgroup 2j + h takes the 64-row half h of them (in ascending order)
-// and all 64 columns, so that each stages 64 A rows and 64 weight rows per
+// Packs of 97-128 rows (plain GEMM).  Two workgroups, h = 0 and 1, share
+// the 64 output columns of each block j.  Where the set has more than 64
+// rows, workgroup h takes the 64-row half h of them (in ascending order) and
+// all 64 columns, so that each stages 64 A rows and 64 weight rows per
 // k-block instead of 128 and 32 (a fifth fewer bytes per CU); where it has
 // at most 64, each takes all of them and the 32 columns of block 2j + h.
 // Every output element keeps its MFMA chain either way.  nblk = N / 32 (even:
@@ -2509,8 +2509,12 @@ skinny_pair_kernel(GemmArgs a, int nblk, int publish) {
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int T = (int)a.T;
     const int set = (int)blockIdx.x / nblk;
-    const int blk = ((int)blockIdx.x % nblk) >> 1;
-    const int half = ((int)blockIdx.x % nblk) & 1;
+    // partners sit 8 apart in groups of 16 (the tail of fewer than 16:
+    // adjacent), so that both land on one XCD and read the pair's weight
+    // rows through one L2
+    const int bb = (int)blockIdx.x % nblk, g16 = bb >> 4, full = nblk >> 4;
+    const int blk = g16 < full ? g16 * 8 + (bb & 7) : full * 8 + ((bb - 16 * full) >> 1);
+    const int half = g16 < full ? (bb >> 3) & 1 : bb & 1;
     uint32_t m[RW];
     uint64_t und[RW], gen[RW], bad = 0;
     int U = 0;
