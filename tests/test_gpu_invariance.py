@@ -276,6 +276,21 @@ def test_narrow_tiles_match_wide_tile_bytes(T, N):
 
 
 
+@pytest.mark.parametrize("T,N", [(256, 4608), (160, 4480), (129, 64), (200, 192)])
+def test_narrow_tiles_one_set(T, N):
+    """Mid-size packs of one set, whose tiles are dealt to the XCDs by
+    weight tile (weight tile counts that are and are not multiples of 8,
+    and a single weight tile): the bytes of 128 x 128 tiles."""
+    m = np.ones(T, np.uint8)
+    x = dev(W.normal_bf16((T, 512), 985 + T))
+    wu = dev(W.normal_bf16((N, 512), 986, 0.02))
+    wg = dev(W.normal_bf16((N, 512), 987, 0.02))
+    md = dev(torch.from_numpy(m))
+    auto = mot.routed_gemm(x, wu, wg, md)
+    wide = mot.routed_gemm(x, wu, wg, md, tile="128x128")
+    assert raw_equal(auto, wide)
+
+
 @pytest.mark.parametrize("T", [40, 100, 200])
 def test_plan_ready_small_and_mid_packs(T):
     """A ready plan reused by the small-pack and the 128 x 64 tile paths
