@@ -2491,30 +2491,41 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
     skinny_tile<SWIGLU, XG, KS>(a, set, blk, count, sl, s_rows, wave, lane);
 }
 
-// Packs of 97-128 rows (plain GEMM).  Two workgroups, h = 0 and 1, share
-// the 64 output columns of each block j.  Where the set has more than 64
-// rows, workgroup h takes the 64-row half h of them (in ascending order) and
-// all 64 columns, so that each stages 64 A rows and 64 weight rows per
-// k-block instead of 128 and 32 (a fifth fewer bytes per CU); where it has
-// at most 64, each takes all of them and the 32 columns of block 2j + h.
-// Every output element keeps its MFMA chain either way.  nblk = N / 32 (even:
-// N is a multiple of 64).  Segment list and error word as skinny_kernel.
-template <int XG, int KS>
+// Plain GEMM packs of up to two halves of HR = 8 XG rows (HR = 64: packs of
+// 97-128 rows; HR = 128: 129-256).  The 64 output columns of block j have
+// four workgroup slots; each set takes c of them in turn (und first):
+//   - more than HR rows: c = 2, slot h runs the HR-row half h of the set's
+//     rows (in ascending order) by all 64 columns;
+//   - at most HR rows, the other set empty: c = 2, slot h runs all of them
+//     by the 32 columns of block 2j + h;
+//   - at most HR rows, the other set not empty: c = 1, all of them by all
+//     64 columns;
+//   - no rows: c = 0;
+// and slots past both sets' share exit.  A mixed pack then keeps at most
+// three workgroups per block busy (one wave of the grid on 256 CUs where
+// four per block, at one workgroup per CU, took two), and a workgroup
+// stages HR A rows and 64 weight rows per k-block instead of all the rows
+// and 32.  Every output element keeps its MFMA chain in every case.  nblk =
+// N / 32 (even: N is a multiple of 64); the grid is 2 nblk.  Segment list
+// and error word as skinny_kernel.
+template <int XG, int KS, int RW>
 __global__ void __launch_bounds__(kSkThreads)
 skinny_pair_kernel(GemmArgs a, int nblk, int publish) {
     using C = SkinnyCfg<2, XG, KS>;
-    constexpr int RW = 2;  // rows per lane (packs of up to 128 rows)
-    __shared__ int32_t s_rows[64 * RW];
+    constexpr int HR = XG * 8;  // rows of a half
+    static_assert(64 * RW == 2 * HR, "a pack of up to two halves, RW rows per lane");
+    __shared__ int32_t s_rows[HR];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int T = (int)a.T;
-    const int set = (int)blockIdx.x / nblk;
-    // partners sit 8 apart in groups of 16 (the tail of fewer than 16:
-    // adjacent), so that both land on one XCD and read the pair's weight
-    // rows through one L2
-    const int bb = (int)blockIdx.x % nblk, g16 = bb >> 4, full = nblk >> 4;
-    const int blk = g16 < full ? g16 * 8 + (bb & 7) : full * 8 + ((bb - 16 * full) >> 1);
-    const int half = g16 < full ? (bb >> 3) & 1 : bb & 1;
+    // slot-major: the busy slots (the low ones) are consecutive workgroups,
+    // spread evenly over the XCDs and their shader engines, and a block's
+    // slots sit nblk / 2 apart (one XCD, one L2 for its weight rows, when
+    // that is a multiple of 8).  Slots interleaved with the block index at a
+    // stride of 8 ran packs of one set at half the busy CUs' count per
+    // engine and left a second wave: 17.9 -> 30.2 us at T = 100.
+    const int npair = nblk >> 1;
+    const int slot = (int)blockIdx.x / npair, blk = (int)blockIdx.x % npair;
     uint32_t m[RW];
     uint64_t und[RW], gen[RW], bad = 0;
     int U = 0;
@@ -2555,32 +2566,36 @@ skinny_pair_kernel(GemmArgs a, int nblk, int publish) {
         if (!publish && blockIdx.x == 0 && threadIdx.x == 0) a.hdr_out[0] = kErrModality;
         return;
     }
-    int total = 0;
-#pragma unroll
-    for (int h = 0; h < RW; ++h) total += __popcll(set ? gen[h] : und[h]);
-    const bool split = total <= 64;          // one 32-column block each
-    const int lo = split ? 0 : 64 * half;    // first sorted row of this workgroup
-    const int count = min(total - lo, 64);
-    if (count <= 0) return;  // all waves
+    const int G = T - U;
+    const int c0 = U == 0 ? 0 : (U > HR || G == 0) ? 2 : 1;
+    const int c1 = G == 0 ? 0 : (G > HR || U == 0) ? 2 : 1;
+    if (slot >= c0 + c1) return;  // all waves
+    const int set = slot < c0 ? 0 : 1;
+    const int part = slot < c0 ? slot : slot - c0;
+    const int total = set ? G : U;
+    const bool split = total <= HR && (set ? c1 : c0) == 2;  // one 32-column block each
+    const int lo = total > HR ? HR * part : 0;               // first sorted row of this workgroup
+    const int count = min(total - lo, HR);                    // > 0
     if (wave == 0) {
         int base = 0;
 #pragma unroll
         for (int h = 0; h < RW; ++h) {
             const uint64_t mine = set ? gen[h] : und[h];
             const int p = base + __popcll(mine & below);
-            if (((mine >> lane) & 1ull) && p >= lo && p < lo + 64) s_rows[p - lo] = lane + 64 * h;
+            if (((mine >> lane) & 1ull) && p >= lo && p < lo + HR) s_rows[p - lo] = lane + 64 * h;
             base += __popcll(mine);
         }
     }
     __syncthreads();
-    if (wave == 0 && lane >= count) s_rows[lane] = s_rows[0];  // padding: a row of the half
+    for (int i = (int)threadIdx.x; i < HR; i += kSkThreads)
+        if (i >= count) s_rows[i] = s_rows[0];  // padding: a row of the half
     __syncthreads();
     // one ring serves both tiles: the 32-column stages fit in the slots
     static_assert(SkinnyCfg<1, XG, KS>::S == C::S && SkinnyCfg<1, XG, KS>::SLOT <= C::SLOT, "shared ring");
     uint8_t *sl[C::S];
     sk_slots<C::SLOT>(sl, std::make_integer_sequence<int, C::S>{});
     if (split)
-        skinny_tile<false, XG, KS>(a, set, 2 * blk + half, count, sl, s_rows, wave, lane);
+        skinny_tile<false, XG, KS>(a, set, 2 * blk + part, count, sl, s_rows, wave, lane);
     else
         skinny_pair_tile<XG, KS>(a, set, blk, count, sl, s_rows, wave, lane);
 }
@@ -2888,7 +2903,7 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
                 hipLaunchKernelGGL((skinny_kernel<false, 12, 1>), grid, block, 0, stream, a, nblk, pub);
             else
                 // 97-128 rows: halves of each set's rows by 64 output columns
-                hipLaunchKernelGGL((skinny_pair_kernel<8, 1>), grid, block, 0, stream, a, nblk, pub);
+                hipLaunchKernelGGL((skinny_pair_kernel<8, 1, 2>), grid, block, 0, stream, a, nblk, pub);
         }
         return hipGetLastError();
     }
@@ -2899,6 +2914,13 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
     if (e != hipSuccess) return e;
     if (ncu <= 0) ncu = 1;
     const bool pro = a.rstd != nullptr;
+    if (!swiglu && !pro && a.T <= 2 * kSkinnyMaxT && a.tile_mode == 0 && a.qk_heads == 0) {
+        // 129-256 rows: halves of 128 of each set's rows by 64 output columns
+        const int nblk = a.N / 32;
+        hipLaunchKernelGGL((skinny_pair_kernel<16, 1, 4>), dim3(2 * nblk), dim3(kSkThreads), 0, stream, a, nblk,
+                           inline_route ? 1 : 0);
+        return hipGetLastError();
+    }
     // mid-size pack: when every 128-row block of both sets times 64-row
     // weight blocks fits one tile per CU, 128 x 64 tiles put twice as many
     // CUs to work on the weight stream as 128 x 128 ones
