@@ -134,8 +134,10 @@ int mot_modality_from_index_sets(const int32_t *und_idx, int64_t n_und, const in
                                   A plan whose header does not describe T rows makes the
                                   call write nothing and raise MOT_ERR_PLAN (since ABI 8);
                                   a plan whose error word is set makes it write nothing.
-                                  (Packs of at most 128 rows rebuild their segment list
-                                  from `modality` whatever this flag says.) */
+                                  (Plain GEMM packs of at most 256 rows and SwiGLU packs
+                                  of at most 128 rebuild their segment list from
+                                  `modality` whatever this flag says; above 128 rows
+                                  they still check the plan's header as above.) */
 /* Tile shapes (token rows x weight rows per workgroup).  By default the
  * kernel runs 256x256 tiles for whole rounds of the GPU and 128x128 tiles for
  * the rest, chosen on the device from the pack's set sizes; these flags force

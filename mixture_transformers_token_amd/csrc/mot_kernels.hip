@@ -2492,7 +2492,7 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
 }
 
 // Plain GEMM packs of up to two halves of HR = 8 XG rows (HR = 64: packs of
-// 97-128 rows; HR = 128: 129-256).  The 64 output columns of block j have
+// 33-128 rows; HR = 128: 129-256).  The 64 output columns of block j have
 // four workgroup slots; each set takes c of them in turn (und first):
 //   - more than HR rows: c = 2, slot h runs the HR-row half h of the set's
 //     rows (in ascending order) by all 64 columns;
@@ -2565,6 +2565,20 @@ skinny_pair_kernel(GemmArgs a, int nblk, int publish) {
         // raise the error word also when a ready plan was passed
         if (!publish && blockIdx.x == 0 && threadIdx.x == 0) a.hdr_out[0] = kErrModality;
         return;
+    }
+    if (!publish && T > 128) {
+        // above 128 rows a ready plan is checked as the tiled kernel checks
+        // it (the segment list itself is still rebuilt from the bytes): a
+        // plan whose error word is set, or whose header does not describe T
+        // rows, makes every workgroup exit, and workgroup 0 raises
+        // MOT_ERR_PLAN for the latter (a workgroup that reads the header
+        // after that write sees the error word and exits too)
+        const int e0 = a.hdr[0], pu = a.hdr[1], pg = a.hdr[2];
+        if (e0 != 0) return;
+        if (a.hdr[3] != T || pu < 0 || pg < 0 || pu + pg != T) {
+            if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr_out[0] = kErrPlan;
+            return;
+        }
     }
     const int G = T - U;
     const int c0 = U == 0 ? 0 : (U > HR || G == 0) ? 2 : 1;
@@ -2897,12 +2911,8 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
             // four waves loading A) than with one
             if (a.T <= 32)
                 hipLaunchKernelGGL((skinny_kernel<false, 4, 1>), grid, block, 0, stream, a, nblk, pub);
-            else if (a.T <= 64)
-                hipLaunchKernelGGL((skinny_kernel<false, 8, 1>), grid, block, 0, stream, a, nblk, pub);
-            else if (a.T <= 96)
-                hipLaunchKernelGGL((skinny_kernel<false, 12, 1>), grid, block, 0, stream, a, nblk, pub);
             else
-                // 97-128 rows: halves of each set's rows by 64 output columns
+                // 33-128 rows: halves of each set's rows by 64 output columns
                 hipLaunchKernelGGL((skinny_pair_kernel<8, 1, 2>), grid, block, 0, stream, a, nblk, pub);
         }
         return hipGetLastError();

@@ -103,7 +103,7 @@ def test_index_sets_clear_a_previous_error():
     assert np.array_equal(m.cpu().numpy(), W.pattern(T))
 
 
-@pytest.mark.parametrize("T_plan,T", [(100, 200), (4000, 4096), (4096, 4000), (9000, 9001)])
+@pytest.mark.parametrize("T_plan,T", [(100, 200), (256, 129), (4000, 4096), (4096, 4000), (9000, 9001)])
 def test_stale_ready_plan_fails_closed(T_plan, T):
     """A plan built for another pack size, passed with plan_ready, makes the
     GEMM write nothing and raise MOT_ERR_PLAN."""
