@@ -293,6 +293,28 @@ def test_narrow_tiles_one_set(T, N):
     assert raw_equal(auto, wide)
 
 
+@pytest.mark.parametrize("T,K,N,n_und", [(40, 64, 128, 20), (150, 64, 192, 150), (256, 18944, 3584, 100),
+                                         (100, 18944, 3584, 0), (33, 3584, 64, 32)])
+def test_small_packs_paired_strides_and_depths(T, K, N, n_und):
+    """Packs of 33-256 rows at the shortest contraction (one k-block) and at
+    the down projection's (296 k-blocks), reading x and writing y through
+    row strides wider than the rows: the bytes of forced 128 x 128 tiles on
+    contiguous copies, and the columns past N of y's rows left as they were."""
+    m = np.zeros(T, np.uint8)
+    m[n_und:] = 1
+    m = m[np.random.default_rng(T + K).permutation(T)]
+    xb = dev(W.normal_bf16((T, K + 64), 970 + T))
+    x = xb[:, :K]
+    wu = dev(W.normal_bf16((N, K), 971, 0.02))
+    wg = dev(W.normal_bf16((N, K), 972, 0.02))
+    md = dev(torch.from_numpy(m))
+    yb = torch.full((T, N + 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    mot.routed_gemm(x, wu, wg, md, out=yb[:, :N])
+    tiled = mot.routed_gemm(x.contiguous(), wu, wg, md, tile="128x128")
+    assert raw_equal(yb[:, :N].contiguous(), tiled)
+    assert torch.all(yb[:, N:] == 3.0)
+
+
 @pytest.mark.parametrize("T", [40, 100, 200])
 def test_plan_ready_small_and_mid_packs(T):
     """A ready plan reused by the small-pack and the 128 x 64 tile paths

@@ -57,12 +57,13 @@ def test_ragged_packs(T):
     _gemm_parity(x, wu, wg, m)
 
 
-@pytest.mark.parametrize("T", [1, 5, 8, 9, 32, 40, 64, 65, 96, 97, 128])
+@pytest.mark.parametrize("T", [1, 5, 8, 9, 32, 40, 64, 65, 96, 97, 128, 129, 200, 256])
 @pytest.mark.parametrize("K", [64, 128, 192, 320, 448])
 def test_small_pack_stage_sizes(T, K):
-    """Packs of up to 128 rows run the small-pack kernel (A-row groups of 4,
-    8, 12 or 16): odd and even k-block counts, parity with the oracle and the
-    bytes of the tiled kernel (forced with a tile flag) for the same rows."""
+    """Packs of up to 256 rows run the small-pack kernels (A-row groups of 4
+    up to 32 rows, halves of 64 or 128 rows above): odd and even k-block
+    counts, parity with the oracle and the bytes of the tiled kernel (forced
+    with a tile flag) for the same rows."""
     m = W.pattern(T)
     m[::3] = 1 - m[::3]
     x, wu, wg, _ = W.gemm_case(T, K, 192, m, base=600 + T + K)
