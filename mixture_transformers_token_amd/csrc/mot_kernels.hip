@@ -2499,18 +2499,20 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
 //   - at most HR rows, the other set empty: c = 2, slot h runs all of them
 //     by the 32 columns of block 2j + h;
 //   - at most HR rows, the other set not empty: c = 1, all of them by all
-//     64 columns;
+//     64 columns, when the grid (2 nblk) is larger than the CU count
+//     (`spread` = 0); else c = 2 as for a lone set;
 //   - no rows: c = 0;
-// and slots past both sets' share exit.  A mixed pack then keeps at most
-// three workgroups per block busy (one wave of the grid on 256 CUs where
-// four per block, at one workgroup per CU, took two), and a workgroup
+// and slots past both sets' share exit.  A mixed pack of many blocks then
+// keeps at most three workgroups per block busy (one wave of the grid on
+// 256 CUs where four per block, at one workgroup per CU, took two), one of
+// few blocks keeps every CU it can busy, and a workgroup
 // stages HR A rows and 64 weight rows per k-block instead of all the rows
 // and 32.  Every output element keeps its MFMA chain in every case.  nblk =
 // N / 32 (even: N is a multiple of 64); the grid is 2 nblk.  Segment list
 // and error word as skinny_kernel.
 template <int XG, int KS, int RW>
 __global__ void __launch_bounds__(kSkThreads)
-skinny_pair_kernel(GemmArgs a, int nblk, int publish) {
+skinny_pair_kernel(GemmArgs a, int nblk, int publish, int spread) {
     using C = SkinnyCfg<2, XG, KS>;
     constexpr int HR = XG * 8;  // rows of a half
     static_assert(64 * RW == 2 * HR, "a pack of up to two halves, RW rows per lane");
@@ -2581,8 +2583,8 @@ skinny_pair_kernel(GemmArgs a, int nblk, int publish) {
         }
     }
     const int G = T - U;
-    const int c0 = U == 0 ? 0 : (U > HR || G == 0) ? 2 : 1;
-    const int c1 = G == 0 ? 0 : (G > HR || U == 0) ? 2 : 1;
+    const int c0 = U == 0 ? 0 : (U > HR || G == 0 || spread) ? 2 : 1;
+    const int c1 = G == 0 ? 0 : (G > HR || U == 0 || spread) ? 2 : 1;
     if (slot >= c0 + c1) return;  // all waves
     const int set = slot < c0 ? 0 : 1;
     const int part = slot < c0 ? slot : slot - c0;
@@ -2877,6 +2879,16 @@ int64_t gemm_tile_bound(int64_t T, int64_t wrows, int ncu) {
     return small_only > big_first ? small_only : big_first;
 }
 
+// 1 when the paired small-pack grid (2 nblk workgroups) fits the device's
+// CUs: every non-empty set then takes two slots per column block.
+int skinny_spread(int nblk) {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return 2 * nblk <= ncu ? 1 : 0;
+}
+
 hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStream_t stream) {
     if (a.out_f32) {
         // fp32 output: 256 x 256 tiles for every row block, one workgroup per CU
@@ -2913,7 +2925,8 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
                 hipLaunchKernelGGL((skinny_kernel<false, 4, 1>), grid, block, 0, stream, a, nblk, pub);
             else
                 // 33-128 rows: halves of each set's rows by 64 output columns
-                hipLaunchKernelGGL((skinny_pair_kernel<8, 1, 2>), grid, block, 0, stream, a, nblk, pub);
+                hipLaunchKernelGGL((skinny_pair_kernel<8, 1, 2>), grid, block, 0, stream, a, nblk, pub,
+                                   skinny_spread(nblk));
         }
         return hipGetLastError();
     }
@@ -2928,7 +2941,7 @@ hipError_t launch_gemm(const GemmArgs &a, bool swiglu, bool inline_route, hipStr
         // 129-256 rows: halves of 128 of each set's rows by 64 output columns
         const int nblk = a.N / 32;
         hipLaunchKernelGGL((skinny_pair_kernel<16, 1, 4>), dim3(2 * nblk), dim3(kSkThreads), 0, stream, a, nblk,
-                           inline_route ? 1 : 0);
+                           inline_route ? 1 : 0, skinny_spread(nblk));
         return hipGetLastError();
     }
     // mid-size pack: when every 128-row block of both sets times 64-row

@@ -187,7 +187,8 @@ def test_small_packs_match_large_pack_bytes(qkv_setup, T):
 @pytest.mark.parametrize("T,N,n_und", [(100, 192, 70), (120, 64, 30), (128, 256, 64), (128, 128, 65),
                                        (97, 4608, 97), (256, 192, 128), (256, 128, 129), (200, 4608, 200),
                                        (129, 64, 0), (160, 320, 31), (48, 192, 24), (33, 64, 0),
-                                       (64, 4608, 1), (77, 128, 40)])
+                                       (64, 4608, 1), (77, 128, 40), (150, 4608, 140), (64, 3584, 32),
+                                       (256, 3584, 100)])
 def test_small_packs_paired_columns(T, N, n_und):
     """Packs of 33-128 (129-256) rows: a set of more than 64 (128) rows is
     split in halves of 64 (128) over workgroups of 64 output columns, a
