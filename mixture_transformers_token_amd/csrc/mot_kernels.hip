@@ -2501,6 +2501,8 @@ skinny_kernel(GemmArgs a, int nblk, int publish) {
 //   - at most HR rows, the other set not empty: c = 1, all of them by all
 //     64 columns, when the grid (2 nblk) is larger than the CU count
 //     (`spread` = 0); else c = 2 as for a lone set;
+//   - more than HR rows, the other set empty, `spread` = 1: c = 4, slot p
+//     runs half p / 2 of the rows by the 32 columns of block 2j + p % 2;
 //   - no rows: c = 0;
 // and slots past both sets' share exit.  A mixed pack of many blocks then
 // keeps at most three workgroups per block busy (one wave of the grid on
@@ -2583,14 +2585,17 @@ skinny_pair_kernel(GemmArgs a, int nblk, int publish, int spread) {
         }
     }
     const int G = T - U;
-    const int c0 = U == 0 ? 0 : (U > HR || G == 0 || spread) ? 2 : 1;
-    const int c1 = G == 0 ? 0 : (G > HR || U == 0 || spread) ? 2 : 1;
+    const int c0 = U == 0 ? 0 : (spread && G == 0 && U > HR) ? 4 : (U > HR || G == 0 || spread) ? 2 : 1;
+    const int c1 = G == 0 ? 0 : (spread && U == 0 && G > HR) ? 4 : (G > HR || U == 0 || spread) ? 2 : 1;
     if (slot >= c0 + c1) return;  // all waves
     const int set = slot < c0 ? 0 : 1;
     const int part = slot < c0 ? slot : slot - c0;
     const int total = set ? G : U;
-    const bool split = total <= HR && (set ? c1 : c0) == 2;  // one 32-column block each
-    const int lo = total > HR ? HR * part : 0;               // first sorted row of this workgroup
+    const int cs = set ? c1 : c0;
+    const bool split = cs == 4 || (total <= HR && cs == 2);  // one 32-column block each
+    const int half = cs == 4 ? part >> 1 : part;
+    const int col = cs == 4 ? part & 1 : part;               // 32-column block 2 blk + col (split)
+    const int lo = total > HR ? HR * half : 0;               // first sorted row of this workgroup
     const int count = min(total - lo, HR);                    // > 0
     if (wave == 0) {
         int base = 0;
@@ -2611,7 +2616,7 @@ skinny_pair_kernel(GemmArgs a, int nblk, int publish, int spread) {
     uint8_t *sl[C::S];
     sk_slots<C::SLOT>(sl, std::make_integer_sequence<int, C::S>{});
     if (split)
-        skinny_tile<false, XG, KS>(a, set, 2 * blk + part, count, sl, s_rows, wave, lane);
+        skinny_tile<false, XG, KS>(a, set, 2 * blk + col, count, sl, s_rows, wave, lane);
     else
         skinny_pair_tile<XG, KS>(a, set, blk, count, sl, s_rows, wave, lane);
 }

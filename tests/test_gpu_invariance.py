@@ -188,7 +188,7 @@ def test_small_packs_match_large_pack_bytes(qkv_setup, T):
                                        (97, 4608, 97), (256, 192, 128), (256, 128, 129), (200, 4608, 200),
                                        (129, 64, 0), (160, 320, 31), (48, 192, 24), (33, 64, 0),
                                        (64, 4608, 1), (77, 128, 40), (150, 4608, 140), (64, 3584, 32),
-                                       (256, 3584, 100)])
+                                       (256, 3584, 100), (100, 3584, 100), (256, 3584, 0), (65, 192, 0)])
 def test_small_packs_paired_columns(T, N, n_und):
     """Packs of 33-128 (129-256) rows: a set of more than 64 (128) rows is
     split in halves of 64 (128) over workgroups of 64 output columns, a
