@@ -55,7 +55,8 @@ def parse():
     p.add_argument("--no-components", action="store_true")
     p.add_argument("--only", default="",
                    help="comma-separated components to run (for one rocprofv3 run per kernel family): norm, "
-                        "prologue, small_packs, backward, qk_norm_rope, qkv_qk_fused, attention, context_blas, "
+                        "prologue, small_packs, down_small_packs, backward, qk_norm_rope, qkv_qk_fused, attention, "
+                        "context_blas, "
                         "mlp, tp4, layer_chain, gen_step, latent")
     p.add_argument("--copy-probe", action="store_true",
                    help="run one 1 GiB device copy first (HBM counter calibration under rocprofv3)")
@@ -286,6 +287,36 @@ def main():
                     "us": round(s_small * 1e6, 2), "GB/s": round(nb / s_small / 1e9, 1),
                     "frac_hbm": round(nb / s_small / 1e9 / PEAK_HBM_GBS, 3), "sets": sets,
                     "eager_us": round(s_eager * 1e6, 2)}
+        del copies
+
+    def down_small_packs(components):
+        """Small packs at the down projection's shape (K = 18944 -> N = 3584):
+        a chain of 1184 dependent MFMAs per output element and only 112
+        32-column blocks, so the paired small-pack kernel spreads a set's rows
+        over all four slots of a block.  Weights rotated over two copies of
+        both sets (543 MB, twice the last-level cache); HIP-graph timed."""
+        Kd, Nd = W.FFN, W.HIDDEN
+        copies = [(W.normal_bf16((Nd, Kd), 290 + i, 0.02).to(dev), W.normal_bf16((Nd, Kd), 390 + i, 0.02).to(dev))
+                  for i in range(2)]
+        for Ts in (1, 64, 128, 256):
+            for variant in ("prefix", "gen"):
+                ms = W.pattern(Ts) if variant == "prefix" else np.ones(Ts, np.uint8)
+                xs_d = W.normal_bf16((Ts, Kd), 19).to(dev)
+                mds = torch.from_numpy(ms).to(dev)
+                ys = torch.empty((Ts, Nd), dtype=torch.bfloat16, device=dev)
+                wss = mot.new_workspace(Ts, dev)
+                ctr = [0]
+
+                def small():
+                    a, b = copies[ctr[0] % 2]
+                    ctr[0] += 1
+                    mot.routed_gemm(xs_d, a, b, mds, out=ys, workspace=wss)
+                s_small = time_component_graph(small, 16, stream)
+                sets = int((ms == 0).any()) + int((ms == 1).any())
+                nb = sets * Nd * Kd * 2 + Ts * Kd * 2 + Ts * Nd * 2 + Ts
+                components[f"down_small_T{Ts}_{variant}"] = {
+                    "us": round(s_small * 1e6, 2), "GB/s": round(nb / s_small / 1e9, 1),
+                    "frac_hbm": round(nb / s_small / 1e9 / PEAK_HBM_GBS, 3), "sets": sets}
         del copies
 
     def joint_attention(components, qkv_buf, iters):
@@ -618,7 +649,8 @@ def main():
             "rows": Tg, "per_op_us": per_op,
             "note": "flops: the routed linear steps and the attention (1101 keys per latent row)"}
 
-    registry = {"norm": c_norm, "prologue": c_prologue, "small_packs": small_packs, "backward": c_backward,
+    registry = {"norm": c_norm, "prologue": c_prologue, "small_packs": small_packs,
+                "down_small_packs": down_small_packs, "backward": c_backward,
                 "qk_norm_rope": c_qk_norm_rope, "qkv_qk_fused": c_qkv_qk_fused, "attention": c_attention,
                 "context_blas": c_context_blas, "mlp": c_mlp, "tp4": c_tp4, "layer_chain": c_layer_chain,
                 "gen_step": c_gen_step, "latent": latent_step}
